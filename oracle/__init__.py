@@ -1,0 +1,205 @@
+"""CPU oracle for grouped affine dequantization and the quantized matmul (MLX layout).
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product library never imports it, and the two share no
+code: this is a ctypes wrapper over ``oracle.c`` (plain C, built with gcc, no HIP).
+
+Every function takes and returns host numpy arrays. bf16 values travel as ``uint16`` bit
+patterns. What each function computes, and the page passage it follows, is documented in
+``oracle.c``:
+
+* ``unpack_codes`` / ``pack_codes`` -- the row's little-endian bit stream, one bit at a time
+  (nuvec_core ``quantized.rs`` module documentation; rlx-moshi ``mlx_dequant.rs``, doc comment of
+  ``dequantize_affine``).
+* ``dequantize`` -- ``w = scale * code + bias`` per group, float32 product then float32 sum
+  (rlx-moshi ``dequantize_affine``; spark_runtime ``mlx_int8.rs`` module formula), optionally
+  rounded to bf16 (nearest, ties to even).
+* ``dequant_rows`` -- the gathered-row lookup (maya2_mlx ``quant.py``, ``rows``).
+* ``qmm`` -- ``x . dequantize(W)^T`` summed in double precision (nuvec_core ``quantized_matmul``;
+  maya2_mlx ``mm``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (always recompiles)."""
+    cmd = ["gcc", *CFLAGS, "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    global _lib
+    _lib = None
+    return _LIB
+
+
+_lib = None
+
+_u32p = np.ctypeslib.ndpointer(np.uint32, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    lib.orc_version.restype = _int
+    lib.orc_unpack_codes.argtypes = [_u32p, _i64, _i64, _int, _u8p]
+    lib.orc_pack_codes.argtypes = [_u8p, _i64, _i64, _int, _u32p]
+    lib.orc_bf16_to_f32.argtypes = [_u16p, _i64, _f32p]
+    lib.orc_f32_to_bf16.argtypes = [_f32p, _i64, _u16p]
+    lib.orc_dequantize.argtypes = [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _f32p, _int]
+    lib.orc_dequant_rows.argtypes = [_u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _u32p, _i64,
+                                     _f32p, _int]
+    lib.orc_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
+                            _int, _f64p, _int]
+    for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
+                 "orc_qmm"):
+        getattr(lib, name).restype = _int
+    for name in ("orc_bf16_to_f32", "orc_f32_to_bf16"):
+        getattr(lib, name).restype = None
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid parameters (rc={rc})")
+
+
+def unpack_codes(packed: np.ndarray, cols: int, bits: int) -> np.ndarray:
+    packed = _c(np.atleast_2d(packed), np.uint32)
+    rows = packed.shape[0]
+    out = np.empty((rows, cols), np.uint8)
+    _check(_load().orc_unpack_codes(packed, rows, cols, bits, out), "unpack_codes")
+    return out
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    codes = _c(np.atleast_2d(codes), np.uint8)
+    rows, cols = codes.shape
+    if (cols * bits) % 32:
+        raise ValueError("cols * bits must be a multiple of 32")
+    out = np.empty((rows, cols * bits // 32), np.uint32)
+    _check(_load().orc_pack_codes(codes, rows, cols, bits, out), "pack_codes")
+    return out
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _load().orc_bf16_to_f32(h.reshape(-1), h.size, out.reshape(-1))
+    return out
+
+
+def f32_to_bf16(a: np.ndarray) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_f32_to_bf16(a.reshape(-1), a.size, out.reshape(-1))
+    return out
+
+
+def dequantize(packed, scales, biases, group_size: int, bits: int, out: str = "f32",
+               cols: int | None = None, threads: int | None = None) -> np.ndarray:
+    """Dense [rows, cols] float32 (``out="f32"``) or bf16 bits (``out="bf16"``)."""
+    packed = _c(np.atleast_2d(packed), np.uint32)
+    scales = _c(np.atleast_2d(scales), np.uint16)
+    biases = _c(np.atleast_2d(biases), np.uint16)
+    rows = packed.shape[0]
+    cols = packed.shape[1] * 32 // bits if cols is None else cols
+    res = np.empty((rows, cols), np.float32)
+    _check(_load().orc_dequantize(packed, scales, biases, rows, cols, group_size, bits, res,
+                                  threads or default_threads()), "dequantize")
+    if out == "f32":
+        return res
+    if out == "bf16":
+        return f32_to_bf16(res)
+    raise ValueError(out)
+
+
+def dequant_rows(packed, scales, biases, indices, group_size: int, bits: int, out: str = "f32",
+                 threads: int | None = None) -> np.ndarray:
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    biases = _c(biases, np.uint16)
+    idx = _c(indices, np.uint32).reshape(-1)
+    rows = packed.shape[0]
+    cols = packed.shape[1] * 32 // bits
+    res = np.empty((idx.size, cols), np.float32)
+    _check(_load().orc_dequant_rows(packed, scales, biases, rows, cols, group_size, bits, idx,
+                                    idx.size, res, threads or default_threads()), "dequant_rows")
+    if out == "f32":
+        return res
+    if out == "bf16":
+        return f32_to_bf16(res)
+    raise ValueError(out)
+
+
+def qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: int,
+        threads: int | None = None) -> np.ndarray:
+    """y = x . dequantize(W)^T in float64, shape [m, n]. ``x_dtype`` is "f32" (x float32) or
+    "bf16" (x uint16 bit patterns)."""
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    biases = _c(biases, np.uint16)
+    if x_dtype == "bf16":
+        xa = _c(np.atleast_2d(x), np.uint16)
+    elif x_dtype == "f32":
+        xa = _c(np.atleast_2d(x), np.float32)
+    else:
+        raise ValueError(x_dtype)
+    m, k = xa.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 32 != k * bits:
+        raise ValueError("x columns do not match the packed width")
+    out = np.empty((m, n), np.float64)
+    _check(_load().orc_qmm(xa.ctypes.data, 1 if x_dtype == "bf16" else 0, m, packed, scales, biases,
+                           n, k, group_size, bits, out, threads or default_threads()), "qmm")
+    return out
+
+
+def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    """The matmul comparison: for each output row, the largest |y - ref| divided by the largest
+    |ref| of that row (the absolute error where that row of ref is all zero); the result is the
+    worst row. Elementwise relative error is meaningless for sums that can land near zero."""
+    y = np.asarray(y, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if y.shape != ref.shape:
+        raise ValueError(f"shape mismatch {y.shape} vs {ref.shape}")
+    if y.size == 0:
+        return 0.0
+    err = np.abs(y - ref).max(axis=-1)
+    scale = np.abs(ref).max(axis=-1)
+    rel = np.where(scale > 0, err / np.where(scale > 0, scale, 1.0), err)
+    return float(rel.max())

@@ -1,0 +1,279 @@
+/*
+ * CPU oracle for MLX-style grouped affine quantization:
+ *   - dequantize:        w[n,k] = scale[n,k/G] * code[n,k] + bias[n,k/G]
+ *   - gathered rows:     out[i,:] = dequantize(table)[idx[i], :]
+ *   - quantized matmul:  y[m,n] = sum_k x[m,k] * w[n,k]      (y = x . dequantize(W)^T)
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library. The HIP library never calls it and shares no code, header, table or
+ * helper with it.
+ *
+ * It is plain and slow on purpose, so that it can be checked against the pages by eye:
+ *   - a code is read one bit at a time out of the row's bit stream;
+ *   - a weight is formed by the affine rule exactly as written: float32 product, then float32 sum;
+ *   - matmul sums run sequentially over k in double precision, with no blocking or reordering.
+ * Build with gcc -O2 -ffp-contract=off (no -ffast-math), so the compiler fuses nothing.
+ *
+ * Sources (the pages this follows):
+ *   [moshi]  rlx-moshi, src/mlx_dequant.rs: doc comment and body of `dequantize_affine`
+ *            (codes packed LSB-first, code s in bits [s*bits, (s+1)*bits); w = scale*code + bias
+ *            with bias the group minimum; rows independent), and `bf16_to_f32` (widening by a
+ *            16-bit left shift).
+ *   [nuvec]  nuvec_core, quantized.rs: module documentation (codes form one little-endian bit
+ *            stream per row stored as uint32; scales and biases are [.., in/group]), `check_params`
+ *            (group sizes, bit widths), `dequantize` and `quantized_matmul` (x . dequantize(w)^T
+ *            without materialising the dequantized matrix), `gather_indices` (indices as uint32).
+ *   [maya2]  maya2_mlx, quant.py: `mm` (x @ W.T for a quantized weight) and `rows` (an embedding
+ *            lookup that dequantizes only the gathered rows).
+ *   [spark]  spark_runtime, weights/mlx_int8.rs: module documentation (8-bit words hold four bytes,
+ *            low byte = column 0; the affine formula per group of G columns).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_VERSION 1
+
+int orc_version(void) { return ORACLE_VERSION; }
+
+/* ---- bf16 <-> f32 ----------------------------------------------------------------------- */
+
+/* [moshi] bf16_to_f32: the bf16 bit pattern is the upper half of the float32 one. Exact. */
+static float bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* float32 -> bf16, round to nearest, ties to even. The pages round no output themselves (the
+ * moshi helper only truncates exactly representable test values); IEEE RNE is the plain reading
+ * for bf16 outputs. The dropped low half decides: above the midpoint rounds up, below rounds
+ * down, exactly the midpoint rounds to the even neighbour. A carry out of the mantissa steps the
+ * exponent, which is again correct (and turns the largest finite values into infinity). NaN stays
+ * NaN: its quiet bit is set so that dropping the payload's low half cannot turn it into infinity. */
+static uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t hi = u >> 16;
+    uint32_t lo = u & 0xffffu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+        hi += 1;
+    return (uint16_t)hi;
+}
+
+void orc_bf16_to_f32(const uint16_t* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_f32(in[i]);
+}
+
+void orc_f32_to_bf16(const float* in, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
+}
+
+/* ---- codes ------------------------------------------------------------------------------ */
+
+/* [nuvec] module doc, [moshi] doc comment: a row is one little-endian bit stream; code j
+ * occupies stream bits [j*bits, (j+1)*bits), least significant bit first. Stream bit p is bit
+ * (p mod 32) of word (p div 32). Read one bit at a time, so a code that straddles two words
+ * needs no special case. */
+static uint32_t code_at(const uint32_t* row, int64_t j, int bits) {
+    uint32_t code = 0;
+    for (int t = 0; t < bits; ++t) {
+        int64_t p = j * bits + t;
+        uint32_t bit = (row[p / 32] >> (p % 32)) & 1u;
+        code |= bit << t;
+    }
+    return code;
+}
+
+static int valid_stream(int64_t cols, int bits) {
+    return bits >= 1 && bits <= 8 && cols >= 0 && (cols * bits) % 32 == 0;
+}
+
+/* codes [rows, cols] (one byte each) from packed [rows, cols*bits/32]. */
+int orc_unpack_codes(const uint32_t* packed, int64_t rows, int64_t cols, int bits, uint8_t* codes) {
+    if (!valid_stream(cols, bits)) return -1;
+    int64_t words = cols * bits / 32;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j)
+            codes[r * cols + j] = (uint8_t)code_at(packed + r * words, j, bits);
+    return 0;
+}
+
+/* The exact inverse of orc_unpack_codes: writes every stream bit of each code, one by one.
+ * Bits of a code above `bits` are ignored. */
+int orc_pack_codes(const uint8_t* codes, int64_t rows, int64_t cols, int bits, uint32_t* packed) {
+    if (!valid_stream(cols, bits)) return -1;
+    int64_t words = cols * bits / 32;
+    memset(packed, 0, (size_t)(rows * words) * sizeof(uint32_t));
+    for (int64_t r = 0; r < rows; ++r) {
+        uint32_t* row = packed + r * words;
+        for (int64_t j = 0; j < cols; ++j)
+            for (int t = 0; t < bits; ++t) {
+                int64_t p = j * bits + t;
+                if ((codes[r * cols + j] >> t) & 1u) row[p / 32] |= 1u << (p % 32);
+            }
+    }
+    return 0;
+}
+
+/* ---- dequantize ------------------------------------------------------------------------- */
+
+/* [moshi] body of dequantize_affine, [spark] module formula: w = scale * code + bias, where scale
+ * and bias belong to the code's group g = col / G of its row. The product is formed in float32
+ * and then the bias is added in float32 (two roundings as written; with bf16 scales and codes of
+ * at most 8 bits the product is exact, so only the sum rounds). */
+static float dequant_one(const uint32_t* prow, const uint16_t* srow, const uint16_t* brow,
+                         int64_t col, int64_t group, int bits) {
+    uint32_t code = code_at(prow, col, bits);
+    int64_t g = col / group;
+    float s = bf16_to_f32(srow[g]);
+    float b = bf16_to_f32(brow[g]);
+    float p = s * (float)code;
+    float w = p + b;
+    return w;
+}
+
+static void dequant_row(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                        int64_t r, int64_t cols, int64_t group, int bits, float* out_row) {
+    int64_t words = cols * bits / 32, groups = cols / group;
+    const uint32_t* prow = packed + r * words;
+    const uint16_t* srow = scales + r * groups;
+    const uint16_t* brow = biases + r * groups;
+    for (int64_t c = 0; c < cols; ++c)
+        out_row[c] = dequant_one(prow, srow, brow, c, group, bits);
+}
+
+static int valid_params(int64_t cols, int64_t group, int bits) {
+    /* [moshi] argument checks: group > 0 divides cols. Any bit width 1..8 is accepted here (the
+     * oracle is wider than the library on purpose, so the pages' G = 8 example runs as given). */
+    return valid_stream(cols, bits) && group > 0 && cols % group == 0;
+}
+
+/* ---- a tiny row-range thread pool ------------------------------------------------------- */
+
+typedef void (*range_fn)(void* ctx, int64_t begin, int64_t end);
+typedef struct { range_fn fn; void* ctx; int64_t begin, end; } range_job;
+
+static void* range_entry(void* p) {
+    range_job* j = (range_job*)p;
+    j->fn(j->ctx, j->begin, j->end);
+    return NULL;
+}
+
+/* Splits [0, total) into `threads` contiguous ranges and runs fn on each. */
+static void run_ranges(range_fn fn, void* ctx, int64_t total, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > total) threads = (int)(total > 0 ? total : 1);
+    if (threads == 1) { fn(ctx, 0, total); return; }
+    pthread_t* tid = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)threads);
+    range_job* jobs = (range_job*)malloc(sizeof(range_job) * (size_t)threads);
+    for (int t = 0; t < threads; ++t) {
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].begin = total * t / threads;
+        jobs[t].end = total * (t + 1) / threads;
+        pthread_create(&tid[t], NULL, range_entry, &jobs[t]);
+    }
+    for (int t = 0; t < threads; ++t) pthread_join(tid[t], NULL);
+    free(tid);
+    free(jobs);
+}
+
+typedef struct {
+    const uint32_t* packed; const uint16_t* scales; const uint16_t* biases;
+    int64_t cols, group; int bits;
+    const uint32_t* idx; int64_t table_rows;
+    float* out;
+} dq_ctx;
+
+static void dq_range(void* p, int64_t b, int64_t e) {
+    dq_ctx* c = (dq_ctx*)p;
+    for (int64_t r = b; r < e; ++r)
+        dequant_row(c->packed, c->scales, c->biases, r, c->cols, c->group, c->bits, c->out + r * c->cols);
+}
+
+/* out float32 [rows, cols]. Returns 0, or -1 for parameters outside the format. */
+int orc_dequantize(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                   int64_t rows, int64_t cols, int64_t group, int bits, float* out, int threads) {
+    if (rows < 0 || !valid_params(cols, group, bits)) return -1;
+    dq_ctx c = {packed, scales, biases, cols, group, bits, NULL, 0, out};
+    run_ranges(dq_range, &c, rows, threads);
+    return 0;
+}
+
+/* [maya2] rows: dequantize only the gathered rows; [nuvec] gather_indices: indices are uint32.
+ * An index past the table (the pages do not say) gives a row of quiet NaNs. */
+static void rows_range(void* p, int64_t b, int64_t e) {
+    dq_ctx* c = (dq_ctx*)p;
+    uint32_t qnan_bits = 0x7fc00000u;
+    float qnan;
+    memcpy(&qnan, &qnan_bits, sizeof qnan);
+    for (int64_t i = b; i < e; ++i) {
+        float* o = c->out + i * c->cols;
+        int64_t r = (int64_t)c->idx[i];
+        if (r >= c->table_rows) {
+            for (int64_t j = 0; j < c->cols; ++j) o[j] = qnan;
+        } else {
+            dequant_row(c->packed, c->scales, c->biases, r, c->cols, c->group, c->bits, o);
+        }
+    }
+}
+
+int orc_dequant_rows(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                     int64_t table_rows, int64_t cols, int64_t group, int bits,
+                     const uint32_t* idx, int64_t n_idx, float* out, int threads) {
+    if (table_rows < 0 || n_idx < 0 || !valid_params(cols, group, bits)) return -1;
+    dq_ctx c = {packed, scales, biases, cols, group, bits, idx, table_rows, out};
+    run_ranges(rows_range, &c, n_idx, threads);
+    return 0;
+}
+
+/* ---- quantized matmul ------------------------------------------------------------------- */
+
+/* [nuvec] quantized_matmul with transpose (weights stored [out, in]), [maya2] mm:
+ *   y[m, n] = sum over k of x[m, k] * w[n, k],  w = the dequantized weight above.
+ * x is float32, or bf16 widened exactly. Each product and the running sum are in double and the
+ * sum runs over k in order. The result is returned in double; rounding it to the caller's output
+ * type is the comparison's business. */
+typedef struct {
+    const double* xd; int64_t m;
+    const uint32_t* packed; const uint16_t* scales; const uint16_t* biases;
+    int64_t n, k, group; int bits;
+    double* out;
+} qmm_ctx;
+
+static void qmm_range(void* p, int64_t b, int64_t e) {
+    qmm_ctx* c = (qmm_ctx*)p;
+    float* w = (float*)malloc(sizeof(float) * (size_t)(c->k > 0 ? c->k : 1));
+    for (int64_t nn = b; nn < e; ++nn) {
+        dequant_row(c->packed, c->scales, c->biases, nn, c->k, c->group, c->bits, w);
+        for (int64_t mm = 0; mm < c->m; ++mm) {
+            const double* xr = c->xd + mm * c->k;
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < c->k; ++kk) acc += xr[kk] * (double)w[kk];
+            c->out[mm * c->n + nn] = acc;
+        }
+    }
+    free(w);
+}
+
+/* x [m, k] (float32, or bf16 bits when x_is_bf16), packed [n, k*bits/32], scales/biases
+ * [n, k/group] bf16 bits; out double [m, n]. Returns 0, or -1 for parameters outside the format. */
+int orc_qmm(const void* x, int x_is_bf16, int64_t m, const uint32_t* packed, const uint16_t* scales,
+            const uint16_t* biases, int64_t n, int64_t k, int64_t group, int bits, double* out,
+            int threads) {
+    if (m < 0 || n < 0 || !valid_params(k, group, bits)) return -1;
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(m * k > 0 ? m * k : 1));
+    if (!xd) return -2;
+    for (int64_t i = 0; i < m * k; ++i)
+        xd[i] = x_is_bf16 ? (double)bf16_to_f32(((const uint16_t*)x)[i]) : (double)((const float*)x)[i];
+    qmm_ctx c = {xd, m, packed, scales, biases, n, k, group, bits, out};
+    run_ranges(qmm_range, &c, n, threads);
+    free(xd);
+    return 0;
+}

@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle: what the pages print and what mathematics fixes.
+
+The oracle is only trusted as far as these tests pin it. Each check is chosen so that a plausible
+mistake fails it: MSB-first reading, a subtracted bias, swapped scale and bias, a wrong group
+index, a straddling code read from the wrong word, a dropped term or transposed operand in the
+matmul, a wrong rounding of bf16 outputs.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+from quantized_matmul_mlx_amd import workloads as W
+
+
+def _words(tokens):
+    return np.array([int(t, 16) for t in tokens], np.uint32)
+
+
+def _bf16(v):
+    """bf16 bits of a value that bf16 holds exactly (the value's float32 upper half)."""
+    a = np.array([v], np.float32).view(np.uint32) >> 16
+    assert (np.array([v], np.float32).view(np.uint32) & 0xFFFF) == 0, "not exact in bf16"
+    return a.astype(np.uint16)
+
+
+# ---- printed examples ---------------------------------------------------------------------
+
+def test_worked_example_lsb_first_plus_bias(oracle_lib):
+    g = golden("lsb_first_plus_bias.txt")
+    bits, G, cols = int(g["bits"][0]), int(g["group_size"][0]), int(g["cols"][0])
+    packed = _words(g["packed"]).reshape(1, -1)
+    s = _bf16(float(g["scale"][0])).reshape(1, 1)
+    b = _bf16(float(g["bias"][0])).reshape(1, 1)
+    out = oracle_lib.dequantize(packed, s, b, G, bits, cols=cols)
+    expect = np.array([float(t) for t in g["expect"]], np.float32)
+    np.testing.assert_array_equal(out[0], expect)
+    # The readings the page calls wrong: MSB-first codes, or the bias subtracted.
+    msb_first = 2.0 * np.arange(7, -1, -1) - 1.0
+    minus_bias = 2.0 * np.arange(8) + 1.0
+    assert not np.array_equal(out[0], msb_first)
+    assert not np.array_equal(out[0], minus_bias)
+
+
+def test_worked_example_at_group_32(oracle_lib):
+    """The same word repeated over a 32-column group (the smallest group the library takes)."""
+    packed = np.full((1, 4), 0x76543210, np.uint32)
+    out = oracle_lib.dequantize(packed, _bf16(2.0).reshape(1, 1), _bf16(-1.0).reshape(1, 1), 32, 4)
+    np.testing.assert_array_equal(out[0], np.tile(2.0 * np.arange(8) - 1.0, 4).astype(np.float32))
+
+
+def test_identity_shape(oracle_lib):
+    g = golden("identity_shape.txt")
+    bits, G, cols = int(g["bits"][0]), int(g["group_size"][0]), int(g["cols"][0])
+    packed = _words(g["packed"]).reshape(1, -1)
+    out = oracle_lib.dequantize(packed, _bf16(1.0).reshape(1, 1), _bf16(0.0).reshape(1, 1), G, bits,
+                                cols=cols)
+    assert out.shape == (1, cols)
+    np.testing.assert_array_equal(out[0], np.array([float(t) for t in g["expect"]], np.float32))
+
+
+def test_int8_byte_order(oracle_lib):
+    g = golden("int8_byte_order.txt")
+    bits, cols = int(g["bits"][0]), int(g["cols"][0])
+    packed = _words(g["packed"]).reshape(1, -1)
+    codes = oracle_lib.unpack_codes(packed, cols, bits)
+    np.testing.assert_array_equal(codes[0], np.array([int(t) for t in g["codes"]], np.uint8))
+    np.testing.assert_array_equal(oracle_lib.pack_codes(codes, bits), packed)
+
+
+def test_shape_rule(oracle_lib):
+    g = golden("shape_rule.txt")
+    bits, G = int(g["bits"][0]), int(g["group_size"][0])
+    n, k = (int(t) for t in g["w_shape"])
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 2**bits, (n, k), dtype=np.uint8)
+    packed = oracle_lib.pack_codes(codes, bits)
+    assert list(packed.shape) == [int(t) for t in g["packed_shape"]]
+    scales = np.full([int(t) for t in g["scales_shape"]], _bf16(0.5)[0], np.uint16)
+    biases = np.full([int(t) for t in g["scales_shape"]], _bf16(-1.0)[0], np.uint16)
+    assert oracle_lib.dequantize(packed, scales, biases, G, bits).shape == (n, k)
+    x = np.ones([int(t) for t in g["x_shape"]], np.float32)
+    y = oracle_lib.qmm(x, "f32", packed, scales, biases, G, bits)
+    assert list(y.shape) == [int(t) for t in g["y_shape"]]
+
+
+def test_odd_width_3bit_hand_words(oracle_lib):
+    g = golden("odd_width_3bit.txt")
+    bits, cols = int(g["bits"][0]), int(g["cols"][0])
+    words = _words(g["packed"]).reshape(1, -1)
+    codes = np.array([int(t) for t in g["codes"]], np.uint8).reshape(1, -1)
+    np.testing.assert_array_equal(oracle_lib.pack_codes(codes, bits), words)
+    np.testing.assert_array_equal(oracle_lib.unpack_codes(words, cols, bits), codes)
+
+
+# ---- the bit stream, from an independent formulation ----------------------------------------
+
+def _row_int(codes, bits):
+    """A row as one little-endian integer: code j times 2**(bits*j)."""
+    v = 0
+    for j, c in enumerate(codes):
+        v += int(c) << (bits * j)
+    return v
+
+
+def _int_words(v, nwords):
+    return [(v >> (32 * i)) & 0xFFFFFFFF for i in range(nwords)]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_bit_stream_matches_big_integer(oracle_lib, bits):
+    rng = np.random.default_rng(bits)
+    cols = 32 * 5
+    codes = rng.integers(0, 2**bits, (3, cols), dtype=np.uint8)
+    packed = oracle_lib.pack_codes(codes, bits)
+    for r in range(3):
+        assert packed[r].tolist() == _int_words(_row_int(codes[r], bits), cols * bits // 32)
+    # and the other way: random words read as one integer
+    words = rng.integers(0, 2**32, (2, cols * bits // 32), dtype=np.uint32)
+    got = oracle_lib.unpack_codes(words, cols, bits)
+    for r in range(2):
+        v = sum(int(w) << (32 * i) for i, w in enumerate(words[r]))
+        assert got[r].tolist() == [(v >> (bits * j)) & ((1 << bits) - 1) for j in range(cols)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 5, 6])
+def test_straddling_positions(oracle_lib, bits):
+    """A lone code of all ones at each index j sets exactly stream bits [j*bits, (j+1)*bits);
+    the codes that cross a word boundary are exactly those with (j*bits) % 32 + bits > 32."""
+    for j in range(32):
+        codes = np.zeros((1, 32), np.uint8)
+        codes[0, j] = 2**bits - 1
+        v = sum(int(w) << (32 * i) for i, w in enumerate(oracle_lib.pack_codes(codes, bits)[0]))
+        assert v == ((1 << bits) - 1) << (j * bits)
+    straddle = [j for j in range(32) if (j * bits) % 32 + bits > 32]
+    expect = {2: [], 3: [10, 21], 5: [6, 12, 19, 25], 6: [5, 10, 21, 26]}[bits]
+    assert straddle == expect
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+def test_pack_unpack_round_trip(oracle_lib, bits):
+    rng = np.random.default_rng(10 + bits)
+    codes = rng.integers(0, 2**bits, (4, 256), dtype=np.uint8)
+    np.testing.assert_array_equal(oracle_lib.unpack_codes(oracle_lib.pack_codes(codes, bits), 256, bits), codes)
+
+
+# ---- the affine rule -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,G", [(2, 32), (3, 32), (4, 64), (5, 128), (6, 32), (8, 64), (8, 128)])
+def test_dequant_is_one_rounding_of_exact_affine(oracle_lib, bits, G):
+    """Invariant: a bf16 scale (8 significant bits) times a code of at most 8 bits is exact in
+    float32, so scale*code + bias equals the exact value rounded once to float32. The codes are
+    read through the big-integer formulation, the group as column // G."""
+    n, k = 5, 4 * G
+    inp = W.random_inputs(bits, G, n, k, 0, seed=bits * 1000 + G)
+    got = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits)
+    s = W.f32_from_bf16_bits(inp.scales).astype(np.float64)
+    b = W.f32_from_bf16_bits(inp.biases).astype(np.float64)
+    for r in range(n):
+        v = sum(int(w) << (32 * i) for i, w in enumerate(inp.packed[r]))
+        codes = np.array([(v >> (bits * j)) & ((1 << bits) - 1) for j in range(k)], np.float64)
+        grp = np.arange(k) // G
+        exact = s[r, grp] * codes + b[r, grp]   # exact in float64: <= 16-bit product, 8-bit addend
+        np.testing.assert_array_equal(got[r], exact.astype(np.float32))
+
+
+def test_scale_and_bias_not_swapped(oracle_lib):
+    # code 3 with scale 0.5 and bias 4: 0.5*3 + 4 = 5.5; swapped would give 4*3 + 0.5 = 12.5
+    packed = np.array([[0x33333333] * 4], np.uint32)
+    out = oracle_lib.dequantize(packed, _bf16(0.5).reshape(1, 1), _bf16(4.0).reshape(1, 1), 32, 4)
+    np.testing.assert_array_equal(out, np.full((1, 32), 5.5, np.float32))
+
+
+def test_group_index_per_column(oracle_lib):
+    # two groups of 32 with different scales: columns 0..31 use scale 1, 32..63 use scale 3
+    packed = np.full((1, 8), 0x11111111, np.uint32)        # every code 1
+    s = np.concatenate([_bf16(1.0), _bf16(3.0)]).reshape(1, 2)
+    b = np.concatenate([_bf16(0.0), _bf16(0.25)]).reshape(1, 2)
+    out = oracle_lib.dequantize(packed, s, b, 32, 4)
+    np.testing.assert_array_equal(out[0, :32], 1.0)
+    np.testing.assert_array_equal(out[0, 32:], 3.25)
+
+
+def test_rejects_parameters_outside_the_format(oracle_lib):
+    with pytest.raises(ValueError):
+        oracle_lib.dequantize(np.zeros((1, 4), np.uint32), np.zeros((1, 1), np.uint16),
+                              np.zeros((1, 1), np.uint16), 24, 4, cols=32)
+
+
+# ---- bf16 rounding ----------------------------------------------------------------------------
+
+def test_bf16_rne_known_values(oracle_lib):
+    cases = {
+        0x3F800000: 0x3F80,   # 1.0 exact
+        0x3F808000: 0x3F80,   # midpoint, even neighbour below
+        0x3F818000: 0x3F82,   # midpoint, odd below -> up
+        0x3F808001: 0x3F81,   # just above the midpoint
+        0x3F807FFF: 0x3F80,   # just below the midpoint
+        0xBF808001: 0xBF81,   # sign is carried
+        0x80000000: 0x8000,   # -0.0
+        0x7F7FFFFF: 0x7F80,   # largest finite rounds to +inf
+        0x7F800000: 0x7F80,   # +inf
+        0x00000001: 0x0000,   # smallest subnormal rounds to zero
+        0x007FFFFF: 0x0080,   # largest subnormal rounds up to the smallest normal
+    }
+    a = np.array(list(cases), np.uint32).view(np.float32)
+    got = oracle_lib.f32_to_bf16(a)
+    assert [hex(v) for v in got.tolist()] == [hex(v) for v in cases.values()]
+    nan = oracle_lib.f32_to_bf16(np.array([0x7F800001, 0xFFC00000], np.uint32).view(np.float32))
+    assert np.isnan(W.f32_from_bf16_bits(nan)).all()
+
+
+def test_bf16_rne_matches_torch(oracle_lib):
+    rng = np.random.default_rng(3)
+    a = np.concatenate([rng.standard_normal(200000).astype(np.float32),
+                        rng.integers(0, 2**32, 200000, dtype=np.uint32).view(np.float32)])
+    a = a[np.isfinite(a)]
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle_lib.f32_to_bf16(a), ref)
+
+
+def test_bf16_widening_is_exact(oracle_lib):
+    h = np.arange(0, 2**16, dtype=np.uint32).astype(np.uint16)
+    f = oracle_lib.bf16_to_f32(h)
+    ref = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(f.view(np.uint32), ref.view(np.uint32))
+
+
+# ---- the matmul --------------------------------------------------------------------------------
+
+def _exact(v):
+    return Fraction(float(v))
+
+
+@pytest.mark.parametrize("bits,G,k,x_dtype", [(4, 32, 64, "f32"), (3, 32, 32, "bf16"),
+                                              (8, 64, 64, "bf16"), (2, 32, 64, "f32")])
+def test_qmm_brute_force_exact_rationals(oracle_lib, bits, G, k, x_dtype):
+    m, n = 3, 4
+    inp = W.random_inputs(bits, G, n, k, m, x_dtype=x_dtype, seed=7 + bits)
+    w = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits)
+    xf = W.f32_from_bf16_bits(inp.x) if x_dtype == "bf16" else inp.x
+    y = oracle_lib.qmm(inp.x, x_dtype, inp.packed, inp.scales, inp.biases, G, bits)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(_exact(xf[i, t]) * _exact(w[j, t]) for t in range(k))
+            denom = max(abs(exact), Fraction(1, 10**9))
+            assert abs(Fraction(float(y[i, j])) - exact) / denom < Fraction(1, 10**12)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (6, 32), (8, 128)])
+def test_qmm_matches_float64_matmul(oracle_lib, bits, G):
+    inp = W.random_inputs(bits, G, 37, 256, 5, x_dtype="bf16", seed=bits)
+    w = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits).astype(np.float64)
+    x = W.f32_from_bf16_bits(inp.x).astype(np.float64)
+    y = oracle_lib.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases, G, bits)
+    np.testing.assert_allclose(y, x @ w.T, rtol=1e-12, atol=1e-12)
+
+
+def test_qmm_one_hot_selects_a_column(oracle_lib):
+    bits, G, n, k = 4, 64, 9, 128
+    inp = W.random_inputs(bits, G, n, k, 0, seed=5)
+    w = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits)
+    x = np.zeros((3, k), np.float32)
+    cols = [0, 77, 127]
+    for i, c in enumerate(cols):
+        x[i, c] = 1.0
+    y = oracle_lib.qmm(x, "f32", inp.packed, inp.scales, inp.biases, G, bits)
+    for i, c in enumerate(cols):
+        np.testing.assert_array_equal(y[i], w[:, c].astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_qmm_closed_forms(oracle_lib, bits):
+    G, n, k = 32, 6, 128
+    inp = W.random_inputs(bits, G, n, k, 2, x_dtype="f32", seed=11)
+    s = W.f32_from_bf16_bits(inp.scales).astype(np.float64)
+    b = W.f32_from_bf16_bits(inp.biases).astype(np.float64)
+    xg = inp.x.astype(np.float64).reshape(2, k // G, G).sum(-1)        # [m, groups]
+    # every code zero: y = sum_g b_g * sum_{k in g} x_k
+    zeros = np.zeros_like(inp.packed)
+    y0 = oracle_lib.qmm(inp.x, "f32", zeros, inp.scales, inp.biases, G, bits)
+    np.testing.assert_allclose(y0, xg @ b.T, rtol=1e-12, atol=1e-12)
+    # every code at its maximum, x = 1: y = sum_g G * (s_g * (2^bits - 1) + b_g)
+    ones_w = np.full_like(inp.packed, 0xFFFFFFFF)
+    x1 = np.ones((1, k), np.float32)
+    y1 = oracle_lib.qmm(x1, "f32", ones_w, inp.scales, inp.biases, G, bits)
+    w_max = (s * (2**bits - 1) + b).astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(y1[0], G * w_max.sum(-1), rtol=1e-12)
+
+
+def test_qmm_is_linear_in_x(oracle_lib):
+    bits, G = 5, 32
+    inp = W.random_inputs(bits, G, 7, 96, 2, x_dtype="f32", seed=13)
+    y = oracle_lib.qmm(inp.x, "f32", inp.packed, inp.scales, inp.biases, G, bits)
+    x2 = np.ascontiguousarray((inp.x[0:1] + inp.x[1:2]).astype(np.float32))
+    y2 = oracle_lib.qmm(x2, "f32", inp.packed, inp.scales, inp.biases, G, bits)
+    # float32 rounding of x0 + x1 is the only difference; compare loosely
+    np.testing.assert_allclose(y2[0], y[0] + y[1], rtol=1e-5, atol=1e-5)
+
+
+def test_qmm_empty_shapes(oracle_lib):
+    inp = W.random_inputs(4, 32, 3, 64, 0)
+    y = oracle_lib.qmm(np.zeros((0, 64), np.uint16), "bf16", inp.packed, inp.scales, inp.biases, 32, 4)
+    assert y.shape == (0, 3)
+
+
+# ---- gathered rows -----------------------------------------------------------------------------
+
+def test_dequant_rows_identity_and_gather(oracle_lib):
+    bits, G, rows, cols = 4, 64, 40, 256
+    inp = W.random_inputs(bits, G, rows, cols, 0, seed=17)
+    full = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits)
+    same = oracle_lib.dequant_rows(inp.packed, inp.scales, inp.biases, np.arange(rows), G, bits)
+    np.testing.assert_array_equal(same.view(np.uint32), full.view(np.uint32))
+    idx = np.array([39, 0, 5, 5, 17], np.uint32)
+    got = oracle_lib.dequant_rows(inp.packed, inp.scales, inp.biases, idx, G, bits)
+    np.testing.assert_array_equal(got, full[idx])
+    bf = oracle_lib.dequant_rows(inp.packed, inp.scales, inp.biases, idx, G, bits, out="bf16")
+    np.testing.assert_array_equal(bf, oracle_lib.f32_to_bf16(full[idx]))
+
+
+def test_dequant_rows_out_of_range_is_nan_row(oracle_lib):
+    inp = W.random_inputs(4, 32, 4, 64, 0, seed=19)
+    got = oracle_lib.dequant_rows(inp.packed, inp.scales, inp.biases,
+                                  np.array([1, 4, 2**32 - 1], np.uint32), 32, 4)
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all() and not np.isnan(got[0]).any()
+
+
+# ---- the comparison and the generator ----------------------------------------------------------
+
+def test_max_row_rel_err(oracle_lib):
+    ref = np.array([[1.0, -4.0], [0.0, 0.0]])
+    y = np.array([[1.0, -3.9], [0.0, 1e-3]])
+    assert oracle_lib.max_row_rel_err(y, ref) == pytest.approx(max(0.1 / 4.0, 1e-3))
+
+
+def test_generator_is_seeded_and_uniform():
+    wl = W.WORKLOADS["ref_4bit_g64_256x512"]
+    a, b = W.make_inputs(wl, m=4), W.make_inputs(wl, m=4)
+    np.testing.assert_array_equal(a.packed, b.packed)
+    np.testing.assert_array_equal(a.x, b.x)
+    assert a.packed.shape == (256, 64) and a.scales.shape == (256, 8) and a.x.shape == (4, 512)
+    s = W.f32_from_bf16_bits(a.scales)
+    bb = W.f32_from_bf16_bits(a.biases)
+    assert s.min() >= 1e-3 * 0.99 and s.max() <= 5e-2 and bb.min() >= -0.4 and bb.max() <= 0
+    # the M = 1 and M = 4 draws of one workload share their weights
+    wl2 = W.WORKLOADS["decode_4bit_g64_4096x4096"]
+    p1 = W.make_inputs(wl2, m=1, n=64)
+    p4 = W.make_inputs(wl2, m=4, n=64)
+    np.testing.assert_array_equal(p1.packed, p4.packed)
