@@ -1,0 +1,123 @@
+/*
+ * qaff -- grouped affine dequantization and quantized matmul for AMD Instinct MI355X (gfx950).
+ *
+ * Storage format (MLX layout):
+ *   packed  uint32 [rows, cols*bits/32]. Each row is one little-endian bit stream: code j occupies
+ *           stream bits [j*bits, (j+1)*bits), least significant bit first; stream bit p is bit
+ *           p%32 of word p/32, so 3-, 5- and 6-bit codes may straddle two words.
+ *           (nuvec_core quantized.rs, module documentation; rlx-moshi mlx_dequant.rs, doc comment of
+ *           dequantize_affine. For 8 bits this is spark_runtime weights/mlx_int8.rs, module
+ *           documentation: byte c%4 of word c/4 is column c, low byte first.)
+ *   scales  bf16 bit patterns (uint16) [rows, cols/group_size]
+ *   biases  bf16 bit patterns (uint16) [rows, cols/group_size]
+ *   A weight is w[r,c] = scale[r,c/G] * code[r,c] + bias[r,c/G], computed in float32 (the product
+ *   first, then the bias) -- rlx-moshi dequantize_affine; spark_runtime module formula.
+ *
+ * Common rules for every entry point below:
+ *   - All array pointers are DEVICE pointers to row-major, contiguous buffers. The caller owns every
+ *     buffer; the library never allocates, frees or retains them (spark_runtime MlxInt8Weight: the
+ *     consumer owns the device pointers).
+ *   - bits must be 2, 3, 4, 5, 6 or 8 (else QAFF_ERR_UNSUPPORTED); group_size 32, 64 or 128
+ *     (nuvec_core check_params); cols (k) must be a multiple of group_size.
+ *   - Alignment: packed 4 bytes, scales/biases 2 bytes, indices 4 bytes; x, y and out 16 bytes.
+ *   - Every argument is checked on the host before any launch, so a rejected call writes nothing.
+ *   - Calls are asynchronous on `stream` (NULL = the null stream): they return once the kernel is
+ *     enqueued and never synchronize (unless the environment sets QAFF_DEBUG_SYNC=1).
+ *   - A size of zero in any output dimension is a successful no-op.
+ *   - On failure the call returns a non-zero status and qaff_last_error() describes it. A launch
+ *     failure maps to QAFF_ERR_DEVICE; a fault inside a kernel surfaces asynchronously, on a later
+ *     synchronization of the stream.
+ *   - Calls are re-entrant; the only global state is the calling thread's error text.
+ */
+#ifndef QAFF_H
+#define QAFF_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QAFF_ABI_VERSION 1
+
+typedef enum {
+    QAFF_OK = 0,
+    QAFF_ERR_INVALID_ARGUMENT = 1,
+    QAFF_ERR_UNSUPPORTED = 2,
+    QAFF_ERR_DEVICE = 3
+} qaff_status;
+
+typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1 } qaff_dtype;
+
+/* Kernel choice for qaff_qmm_ex. AUTO: float32 x -> the VALU kernel at any m; bf16 x -> the
+ * bandwidth-bound GEMV when m <= qaff_gemv_max_m(), otherwise the bf16-MFMA GEMM. */
+typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2 } qaff_path;
+
+/*
+ * Dense dequantization (rlx-moshi dequantize_affine; spark_runtime dequantize_to; maya2_mlx QW.dense).
+ *   out [rows, cols] in out_dtype: float32 holds w exactly as defined above; bf16 holds w rounded
+ *   to nearest, ties to even.
+ * Errors: INVALID_ARGUMENT for negative sizes, a bad group size, cols % group_size != 0, a bad
+ * dtype, a null or misaligned pointer where the size is non-zero; UNSUPPORTED for a bit width
+ * outside {2,3,4,5,6,8}.
+ */
+qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t rows, int64_t cols, int32_t group_size, int32_t bits,
+                            void* out, qaff_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Quantized matmul y = x . dequantize(W)^T without materialising W (nuvec_core quantized_matmul with
+ * transpose, for weights stored [out, in]; maya2_mlx mm).
+ *   x [m, k] in x_dtype (float32 or bf16); W is packed/scales/biases of shape [n, k];
+ *   y [m, n] in the same dtype as x (x, scales and biases promote to x's type: bf16 scales never
+ *   widen a float32 x, and a bf16 x stays bf16). Sums accumulate in float32; a bf16 y is the float32
+ *   sum rounded to nearest even.
+ * Kernel choice follows QAFF_PATH_AUTO. k == 0 writes zeros.
+ * Errors: as qaff_dequantize, plus INVALID_ARGUMENT for negative m, n or k.
+ */
+qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m,
+                     const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                     int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                     void* y, hipStream_t stream);
+
+/* qaff_qmm with the kernel forced, for tests and benchmarks. QAFF_PATH_GEMM with a float32 x is
+ * UNSUPPORTED (the MFMA path would round x to bf16); an unknown path is INVALID_ARGUMENT. */
+qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
+                        const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                        int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                        void* y, hipStream_t stream, qaff_path path);
+
+/*
+ * Gathered-row dequantization: out[i, :] = dequantize(table)[indices[i], :] (maya2_mlx rows: an
+ * embedding lookup that dequantizes only the gathered rows). Indices are uint32 (nuvec_core
+ * gather_indices casts integer indices to U32); duplicates are allowed. An index >= table_rows
+ * cannot be checked on the host without a synchronization: its output row is filled with quiet
+ * NaNs (0x7FC00000 in float32, 0x7FC0 in bf16).
+ *   packed/scales/biases: the table [table_rows, cols]; out [n_indices, cols] in out_dtype.
+ * Errors: as qaff_dequantize, plus INVALID_ARGUMENT for negative table_rows or n_indices, or a
+ * null/misaligned indices pointer when n_indices > 0.
+ */
+qaff_status qaff_dequant_rows(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                              int64_t table_rows, int64_t cols, int32_t group_size, int32_t bits,
+                              const uint32_t* indices, int64_t n_indices,
+                              void* out, qaff_dtype out_dtype, hipStream_t stream);
+
+/* Text for the last non-OK status returned on the calling thread ("" if none). The pointer stays
+ * valid until the thread's next qaff call. */
+const char* qaff_last_error(void);
+
+/* A constant name for a status code. */
+const char* qaff_status_string(qaff_status status);
+
+/* QAFF_ABI_VERSION of the loaded library. */
+int qaff_abi_version(void);
+
+/* Largest m that QAFF_PATH_AUTO sends to the GEMV for a bf16 x. */
+int qaff_gemv_max_m(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QAFF_H */

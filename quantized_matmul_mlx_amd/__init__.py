@@ -1,0 +1,171 @@
+"""qaff: MLX-layout grouped affine dequantization and quantized matmul on AMD MI355X (gfx950).
+
+Thin binding over the C ABI of ``include/qaff.h`` (``libqaff.so``, hand-written HIP kernels). This
+layer only marshals arguments: it checks devices, dtypes and contiguity, then passes raw device
+pointers and the current HIP stream. Every step of the computation runs in the library's kernels;
+if the library is missing, calls raise.
+
+Weights use the MLX layout: ``packed`` uint32 (or int32) [n, k*bits/32] holding each row as a
+little-endian bit stream of codes; ``scales`` and ``biases`` bf16 [n, k/group_size] (int16/uint16
+bit views are accepted too). A weight is ``scale * code + bias`` of its group.
+
+    y = qmm(x, packed, scales, biases, group_size, bits)   # x . dequantize(W)^T, W never dense
+    w = dequantize(packed, scales, biases, group_size, bits, out_dtype=torch.bfloat16)
+    e = dequant_rows(packed, scales, biases, idx, group_size, bits)   # embedding lookup
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import QaffError
+
+__all__ = ["dequantize", "qmm", "dequant_rows", "QWeight", "QaffError", "gemv_max_m"]
+
+_PACKED_DTYPES = (torch.int32, torch.uint32)
+_BF16_BITS_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+_INDEX_DTYPES = (torch.int32, torch.uint32)
+_OUT_DTYPES = {torch.float32: _lib.QAFF_F32, torch.bfloat16: _lib.QAFF_BF16}
+
+
+def _need(t, name, dtypes, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _weights(packed, scales, biases, group_size, bits):
+    _need(packed, "packed", _PACKED_DTYPES)
+    dev = packed.device
+    _need(scales, "scales", _BF16_BITS_DTYPES, dev)
+    _need(biases, "biases", _BF16_BITS_DTYPES, dev)
+    if packed.dim() != 2 or scales.dim() != 2 or biases.dim() != 2:
+        raise ValueError("packed, scales and biases must be 2-D")
+    rows, words = packed.shape
+    if (words * 32) % bits:
+        raise ValueError(f"packed width {words} is not a whole number of {bits}-bit codes")
+    cols = words * 32 // bits
+    if group_size <= 0 or cols % group_size:
+        raise ValueError(f"{cols} columns are not a multiple of the group size {group_size}")
+    want = (rows, cols // group_size)
+    if tuple(scales.shape) != want or tuple(biases.shape) != want:
+        raise ValueError(f"scales/biases must be {list(want)}, got {list(scales.shape)} and "
+                         f"{list(biases.shape)}")
+    return dev, rows, cols
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+
+
+def gemv_max_m() -> int:
+    """Largest number of x rows the automatic dispatch sends to the GEMV for a bf16 x."""
+    return int(_lib.load().qaff_gemv_max_m())
+
+
+def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=torch.float32,
+               out=None):
+    """Dense ``[rows, cols]`` weights (rlx-moshi ``dequantize_affine``; maya2_mlx ``QW.dense``)."""
+    lib = _lib.load()
+    dev, rows, cols = _weights(packed, scales, biases, group_size, bits)
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    if out is None:
+        out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (out_dtype,), dev)
+        if tuple(out.shape) != (rows, cols):
+            raise ValueError(f"out must be [{rows}, {cols}]")
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_dequantize(_p(packed), _p(scales), _p(biases), rows, cols, group_size,
+                                       bits, _p(out), _OUT_DTYPES[out_dtype], _stream(dev)))
+    return out
+
+
+def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto", out=None):
+    """``x . dequantize(W)^T`` (nuvec_core ``quantized_matmul`` with transpose; maya2_mlx ``mm``).
+
+    x is float32 or bf16 ``[..., k]`` (a 1-D x is one row); the result has x's dtype and shape
+    ``[..., n]``. ``path`` forces a kernel ("gemv" or "gemm") for tests and benchmarks."""
+    lib = _lib.load()
+    dev, n, k = _weights(packed, scales, biases, group_size, bits)
+    _need(x, "x", tuple(_OUT_DTYPES), dev)
+    if x.shape[-1] != k:
+        raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
+    if path not in _lib.PATHS:
+        raise ValueError(f"path must be one of {tuple(_lib.PATHS)}")
+    lead = tuple(x.shape[:-1])
+    m = math.prod(lead)
+    x2 = x.reshape(m, k)
+    if out is None:
+        out = torch.empty(lead + (n,), dtype=x.dtype, device=dev)
+    else:
+        _need(out, "out", (x.dtype,), dev)
+        if tuple(out.shape) != lead + (n,):
+            raise ValueError(f"out must be {list(lead + (n,))}")
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_qmm_ex(_p(x2), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales),
+                                   _p(biases), n, k, group_size, bits, _p(out), _stream(dev),
+                                   _lib.PATHS[path]))
+    return out
+
+
+def dequant_rows(packed, scales, biases, indices, group_size: int, bits: int,
+                 out_dtype=torch.float32, out=None):
+    """Dequantized rows ``indices`` of a quantized table (maya2_mlx ``rows``). Indices are int32
+    or uint32 and are read as uint32; an index past the table gives a row of NaNs."""
+    lib = _lib.load()
+    dev, rows, cols = _weights(packed, scales, biases, group_size, bits)
+    _need(indices, "indices", _INDEX_DTYPES, dev)
+    idx = indices.reshape(-1)
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    shape = tuple(indices.shape) + (cols,)
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (out_dtype,), dev)
+        if tuple(out.shape) != shape:
+            raise ValueError(f"out must be {list(shape)}")
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_dequant_rows(_p(packed), _p(scales), _p(biases), rows, cols, group_size,
+                                         bits, _p(idx), idx.numel(), _p(out),
+                                         _OUT_DTYPES[out_dtype], _stream(dev)))
+    return out
+
+
+class QWeight:
+    """A quantized ``[out, in]`` weight (maya2_mlx ``QW``): packed codes, scales, biases, bits and
+    group size. The caller owns the tensors."""
+
+    __slots__ = ("q", "scales", "biases", "bits", "group_size", "shape")
+
+    def __init__(self, q, scales, biases, bits: int, group_size: int):
+        self.q, self.scales, self.biases = q, scales, biases
+        self.bits, self.group_size = int(bits), int(group_size)
+        _, rows, cols = _weights(q, scales, biases, self.group_size, self.bits)
+        self.shape = (rows, cols)
+
+    def dense(self, dtype=torch.float32):
+        return dequantize(self.q, self.scales, self.biases, self.group_size, self.bits, dtype)
+
+    def mm(self, x, path: str = "auto"):
+        """x @ W.T"""
+        return qmm(x, self.q, self.scales, self.biases, self.group_size, self.bits, path)
+
+    def rows(self, idx, dtype=torch.float32):
+        return dequant_rows(self.q, self.scales, self.biases, idx, self.group_size, self.bits, dtype)

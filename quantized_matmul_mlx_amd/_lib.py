@@ -1,0 +1,69 @@
+"""ctypes loader for libqaff.so (the C ABI of include/qaff.h). Nothing here computes: it finds the
+library, declares the signatures and turns a non-OK status into an exception."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqaff.so")
+
+QAFF_OK = 0
+QAFF_ERR_INVALID_ARGUMENT = 1
+QAFF_ERR_UNSUPPORTED = 2
+QAFF_ERR_DEVICE = 3
+
+QAFF_F32 = 0
+QAFF_BF16 = 1
+
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
+
+EXPORTS = ("qaff_dequantize", "qaff_qmm", "qaff_qmm_ex", "qaff_dequant_rows", "qaff_last_error",
+           "qaff_status_string", "qaff_abi_version", "qaff_gemv_max_m")
+
+ABI_VERSION = 1
+
+
+class QaffError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the in-tree libqaff.so. Raises if it is not built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m quantized_matmul_mlx_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.qaff_dequantize.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_int, vp]
+    lib.qaff_qmm.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+    lib.qaff_qmm_ex.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp,
+                                ctypes.c_int]
+    lib.qaff_dequant_rows.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, ctypes.c_int, vp]
+    for f in (lib.qaff_dequantize, lib.qaff_qmm, lib.qaff_qmm_ex, lib.qaff_dequant_rows):
+        f.restype = ctypes.c_int
+    lib.qaff_last_error.restype = ctypes.c_char_p
+    lib.qaff_last_error.argtypes = []
+    lib.qaff_status_string.restype = ctypes.c_char_p
+    lib.qaff_status_string.argtypes = [ctypes.c_int]
+    lib.qaff_abi_version.restype = ctypes.c_int
+    lib.qaff_gemv_max_m.restype = ctypes.c_int
+    if lib.qaff_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libqaff ABI {lib.qaff_abi_version()} != expected {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != QAFF_OK:
+        lib = load()
+        name = lib.qaff_status_string(status).decode()
+        raise QaffError(status, f"{name}: {lib.qaff_last_error().decode()}")

@@ -1,0 +1,202 @@
+// The C ABI declared in include/qaff.h: argument checks (all on the host, before any HIP call),
+// kernel dispatch and the per-thread error text.
+//
+// The checks follow the pages' own: nuvec_core quantized.rs `check_params` (group sizes 32/64/128;
+// bit widths -- the library implements 2, 3, 4, 5, 6 and 8), rlx-moshi mlx_dequant.rs
+// `dequantize_affine` (the group size divides the columns; the packed width is cols*bits/32) and
+// spark_runtime weights/mlx_int8.rs `MlxInt8Weight::load` (scales and biases are [rows, cols/G]).
+// Shapes are implied by the sizes passed in, so only sizes, pointers and alignment can be checked.
+#include "qaff.h"
+
+#include "launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_error;
+
+qaff_status fail(qaff_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+constexpr int kGemvMaxM = 16;
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* v = std::getenv("QAFF_DEBUG_SYNC");
+        return v && v[0] && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+qaff_status after_launch(const char* op, hipError_t e, hipStream_t stream) {
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(QAFF_ERR_DEVICE, "%s: %s", op, hipGetErrorString(e));
+    return QAFF_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by every entry point: bits, group size, cols and the weight pointers.
+qaff_status check_weight(const char* op, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t rows, int64_t cols, int32_t group_size,
+                         int32_t bits) {
+    if (bits != 2 && bits != 3 && bits != 4 && bits != 5 && bits != 6 && bits != 8)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: %d bits are not supported (2, 3, 4, 5, 6 or 8)", op, bits);
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: group size %d is not supported (32, 64 or 128)", op, group_size);
+    if (rows < 0 || cols < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative size", op);
+    if (cols % group_size != 0)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: %lld columns are not a multiple of the group size %d", op,
+                    (long long)cols, group_size);
+    if (rows > 0 && cols > 0) {
+        if (!packed || !scales || !biases) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null weight pointer", op);
+        if (!aligned(packed, 4)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: packed codes must be 4-byte aligned", op);
+        if (!aligned(scales, 2) || !aligned(biases, 2))
+            return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: scales and biases must be 2-byte aligned", op);
+    }
+    if (rows > 0xffffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: more than 2^32-1 weight rows", op);
+    if (cols / 32 > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: too many columns", op);
+    return QAFF_OK;
+}
+
+bool valid_dtype(qaff_dtype d) { return d == QAFF_F32 || d == QAFF_BF16; }
+
+qaff_status dequant_common(const char* op, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t table_rows, int64_t cols,
+                           int32_t group_size, int32_t bits, const uint32_t* indices,
+                           int64_t out_rows, bool gather, void* out, qaff_dtype out_dtype,
+                           hipStream_t stream) {
+    g_error.clear();
+    qaff_status st = check_weight(op, packed, scales, biases, table_rows, cols, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (!valid_dtype(out_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown output dtype %d", op, (int)out_dtype);
+    if (out_rows < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative number of indices", op);
+    if (out_rows == 0 || cols == 0) return QAFF_OK;
+    if (gather) {
+        if (!indices) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null indices", op);
+        if (!aligned(indices, 4)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: indices must be 4-byte aligned", op);
+        if (table_rows > 0 && (!packed || !scales || !biases))
+            return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null weight pointer", op);
+    }
+    if (!out) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
+    if (!aligned(out, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be 16-byte aligned", op);
+    if (out_rows * (cols / 32) >= (1LL << 31))
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: output of %lld x %lld is too large", op, (long long)out_rows, (long long)cols);
+    hipError_t e = qaff::launch_dequant(packed, scales, biases, gather ? indices : nullptr, table_rows,
+                                        out_rows, cols, group_size, bits, out, out_dtype == QAFF_BF16, stream);
+    return after_launch(op, e, stream);
+}
+
+}  // namespace
+
+namespace qaff {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
+}  // namespace qaff
+
+extern "C" {
+
+qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t rows, int64_t cols, int32_t group_size, int32_t bits, void* out,
+                            qaff_dtype out_dtype, hipStream_t stream) {
+    return dequant_common("qaff_dequantize", packed, scales, biases, rows, cols, group_size, bits,
+                          nullptr, rows, false, out, out_dtype, stream);
+}
+
+qaff_status qaff_dequant_rows(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                              int64_t table_rows, int64_t cols, int32_t group_size, int32_t bits,
+                              const uint32_t* indices, int64_t n_indices, void* out,
+                              qaff_dtype out_dtype, hipStream_t stream) {
+    return dequant_common("qaff_dequant_rows", packed, scales, biases, table_rows, cols, group_size,
+                          bits, indices, n_indices, true, out, out_dtype, stream);
+}
+
+qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        int32_t group_size, int32_t bits, void* y, hipStream_t stream, qaff_path path) {
+    static const char* op = "qaff_qmm";
+    g_error.clear();
+    qaff_status st = check_weight(op, packed, scales, biases, n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
+    if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
+    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMM)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown path %d", op, (int)path);
+    if (x_dtype == QAFF_F32 && path == QAFF_PATH_GEMM)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the MFMA GEMM takes a bf16 x only", op);
+    if (m == 0 || n == 0) return QAFF_OK;
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * esize, stream), stream);
+    if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+
+    bool use_gemm = false;
+    if (x_dtype == QAFF_BF16) use_gemm = path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && m > kGemvMaxM);
+    hipError_t e;
+    if (use_gemm) {
+        e = qaff::launch_gemm(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
+                              bits, static_cast<uint16_t*>(y), stream);
+    } else {
+        e = qaff::launch_gemv(x, x_dtype == QAFF_F32, m, packed, scales, biases, n, k, group_size, bits, y,
+                              stream);
+    }
+    return after_launch(op, e, stream);
+}
+
+qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                     const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                     int32_t group_size, int32_t bits, void* y, hipStream_t stream) {
+    return qaff_qmm_ex(x, x_dtype, m, packed, scales, biases, n, k, group_size, bits, y, stream,
+                       QAFF_PATH_AUTO);
+}
+
+const char* qaff_last_error(void) { return g_error.c_str(); }
+
+const char* qaff_status_string(qaff_status status) {
+    switch (status) {
+        case QAFF_OK: return "QAFF_OK";
+        case QAFF_ERR_INVALID_ARGUMENT: return "QAFF_ERR_INVALID_ARGUMENT";
+        case QAFF_ERR_UNSUPPORTED: return "QAFF_ERR_UNSUPPORTED";
+        case QAFF_ERR_DEVICE: return "QAFF_ERR_DEVICE";
+        default: return "QAFF_ERR_UNKNOWN";
+    }
+}
+
+int qaff_abi_version(void) { return QAFF_ABI_VERSION; }
+
+int qaff_gemv_max_m(void) { return kGemvMaxM; }
+
+}  // extern "C"

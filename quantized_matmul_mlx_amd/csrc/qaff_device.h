@@ -1,0 +1,87 @@
+// Device helpers for the qaff kernels (gfx950 only): bf16 conversions, whole-block loads of packed
+// words, and code extraction from a row's little-endian bit stream.
+//
+// A "block" is 32 consecutive codes of one row. At any bit width b, 32 codes are exactly b words,
+// so a block always starts on a word boundary and never shares a word with another block. Every
+// group size (32, 64, 128) is a whole number of blocks, so a block has exactly one scale and one
+// bias. The kernels all work block by block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qaff {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));        // 16-byte aligned
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern -> float32: the upper half of the float32 pattern (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Two float32 -> two bf16 in one dword (lo in bits 0..15), round to nearest even. The compiler
+// emits v_cvt_pk_bf16_f32 for the pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo;
+    const __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float v) {
+    const __bf16 a = (__bf16)v;
+    return __builtin_bit_cast(uint16_t, a);
+}
+
+// Loads the BITS words of one block. The pointer only needs 4-byte alignment: gfx950 global loads
+// of 2-4 dwords accept any dword-aligned address.
+template <int BITS>
+__device__ __forceinline__ void load_block(const uint32_t* __restrict__ p, uint32_t (&w)[BITS]) {
+    if constexpr (BITS == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else if constexpr (BITS == 3) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z;
+    } else if constexpr (BITS == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (BITS == 5) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; w[4] = p[4];
+    } else if constexpr (BITS == 6) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(p);
+        const u32x3 u = *reinterpret_cast<const u32x3*>(p + 3);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = u.x; w[4] = u.y; w[5] = u.z;
+    } else {
+        static_assert(BITS == 8, "bit width");
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p + 4);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
+    }
+}
+
+// Code j (0..31) of a block. j is a compile-time constant after unrolling, so this folds to one
+// bit-field extract, or for a code that straddles words j*BITS/32 and the next, one funnel shift
+// (v_alignbit_b32) and a mask.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[BITS], int j) {
+    const int bit = j * BITS;
+    const int wi = bit >> 5;
+    const int sh = bit & 31;
+    const uint32_t mask = (1u << BITS) - 1u;
+    if (sh + BITS <= 32) return (w[wi] >> sh) & mask;
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+}
+
+// Full-wave sum of a float (64 lanes), result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace qaff

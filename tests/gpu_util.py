@@ -1,0 +1,43 @@
+"""Helpers for the GPU tests: move seeded numpy inputs to the device and results back. No method
+arithmetic here: bf16 values move as bit patterns."""
+import sys
+
+import numpy as np
+import torch
+
+
+def banner(msg):
+    """Names the case on stdout before a GPU step, so a run that dies still says where."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev_u32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint32).view(np.int32)).cuda()
+
+
+def dev_bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_x(x, x_dtype):
+    if x_dtype == "bf16":
+        return dev_bf16(x)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
+
+
+def dev_weights(inp):
+    return dev_u32(inp.packed), dev_bf16(inp.scales), dev_bf16(inp.biases)
+
+
+def host_bits(t):
+    """bf16 tensor -> uint16 bit patterns; float32 tensor -> float32 array."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def host_f64(t):
+    t = t.detach().cpu()
+    return t.float().numpy().astype(np.float64)

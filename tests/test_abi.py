@@ -1,0 +1,152 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/qaff.h declares, and
+rejects bad arguments on the host (no GPU is touched: every case here fails validation or is a
+no-op that returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_matmul_mlx_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INVALID, UNSUPPORTED = _lib.QAFF_OK, _lib.QAFF_ERR_INVALID_ARGUMENT, _lib.QAFF_ERR_UNSUPPORTED
+F32, BF16 = _lib.QAFF_F32, _lib.QAFF_BF16
+
+# fake, never dereferenced device addresses (validation fails or the call is a no-op first)
+A16 = ctypes.c_void_p(0x10000)
+A4 = ctypes.c_void_p(0x10004)
+A2 = ctypes.c_void_p(0x10002)
+A1 = ctypes.c_void_p(0x10001)
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from quantized_matmul_mlx_amd import build
+        build.build()
+    return _lib.load()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "qaff.h")).read()
+    return sorted(set(re.findall(r"\b(qaff_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} is declared in qaff.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qaff_abi_version() == _lib.ABI_VERSION
+    assert lib.qaff_status_string(OK) == b"QAFF_OK"
+    assert lib.qaff_status_string(INVALID) == b"QAFF_ERR_INVALID_ARGUMENT"
+    assert lib.qaff_status_string(UNSUPPORTED) == b"QAFF_ERR_UNSUPPORTED"
+    assert lib.qaff_status_string(_lib.QAFF_ERR_DEVICE) == b"QAFF_ERR_DEVICE"
+    assert lib.qaff_gemv_max_m() >= 1
+
+
+def dq(lib, rows=4, cols=64, G=32, bits=4, packed=A16, scales=A16, biases=A16, out=A16, dt=F32):
+    return lib.qaff_dequantize(packed, scales, biases, rows, cols, G, bits, out, dt, NULL)
+
+
+def qmm(lib, m=1, n=4, k=64, G=32, bits=4, x=A16, xdt=BF16, packed=A16, scales=A16, biases=A16,
+        y=A16, path=0):
+    return lib.qaff_qmm_ex(x, xdt, m, packed, scales, biases, n, k, G, bits, y, NULL, path)
+
+
+def rows(lib, table_rows=8, cols=64, G=32, bits=4, idx=A16, n_idx=2, out=A16, dt=F32,
+         packed=A16, scales=A16, biases=A16):
+    return lib.qaff_dequant_rows(packed, scales, biases, table_rows, cols, G, bits, idx, n_idx, out,
+                                 dt, NULL)
+
+
+@pytest.mark.parametrize("bits", [0, 1, 7, 9, 16, -4])
+def test_unsupported_bit_widths(lib, bits):
+    assert dq(lib, bits=bits) == UNSUPPORTED
+    assert b"bits" in lib.qaff_last_error()
+    assert qmm(lib, bits=bits) == UNSUPPORTED
+    assert rows(lib, bits=bits) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("G", [0, 8, 16, 48, 256, -32])
+def test_bad_group_sizes(lib, G):
+    assert dq(lib, G=G, cols=256) == INVALID
+    assert b"group size" in lib.qaff_last_error()
+    assert qmm(lib, G=G, k=256) == INVALID
+    assert rows(lib, G=G, cols=256) == INVALID
+
+
+def test_cols_not_multiple_of_group(lib):
+    assert dq(lib, cols=96, G=64) == INVALID
+    assert qmm(lib, k=96, G=64) == INVALID
+    assert rows(lib, cols=160, G=128) == INVALID
+
+
+def test_negative_sizes(lib):
+    assert dq(lib, rows=-1) == INVALID
+    assert dq(lib, cols=-32) == INVALID
+    assert qmm(lib, m=-1) == INVALID
+    assert qmm(lib, n=-1) == INVALID
+    assert qmm(lib, k=-64) == INVALID
+    assert rows(lib, table_rows=-1) == INVALID
+    assert rows(lib, n_idx=-1) == INVALID
+
+
+def test_null_pointers(lib):
+    assert dq(lib, packed=NULL) == INVALID
+    assert dq(lib, scales=NULL) == INVALID
+    assert dq(lib, biases=NULL) == INVALID
+    assert dq(lib, out=NULL) == INVALID
+    assert qmm(lib, x=NULL) == INVALID
+    assert qmm(lib, y=NULL) == INVALID
+    assert qmm(lib, packed=NULL) == INVALID
+    assert rows(lib, idx=NULL) == INVALID
+    assert rows(lib, out=NULL) == INVALID
+
+
+def test_misaligned_pointers(lib):
+    assert dq(lib, packed=A2) == INVALID and b"4-byte" in lib.qaff_last_error()
+    assert dq(lib, scales=A1) == INVALID
+    assert dq(lib, out=A4) == INVALID and b"16-byte" in lib.qaff_last_error()
+    assert qmm(lib, x=A4) == INVALID
+    assert qmm(lib, y=A2) == INVALID
+    assert rows(lib, idx=A2) == INVALID
+
+
+def test_dtype_and_path_checks(lib):
+    assert dq(lib, dt=7) == INVALID
+    assert qmm(lib, xdt=5) == INVALID
+    assert qmm(lib, path=9) == INVALID
+    assert qmm(lib, xdt=F32, path=2) == UNSUPPORTED      # the MFMA GEMM takes bf16 x only
+    assert b"bf16" in lib.qaff_last_error()
+    assert rows(lib, dt=-1) == INVALID
+
+
+def test_empty_outputs_are_no_ops(lib):
+    # nothing to write: OK, even with null buffers, and no HIP call is made
+    assert dq(lib, rows=0, packed=NULL, scales=NULL, biases=NULL, out=NULL) == OK
+    assert dq(lib, cols=0, packed=NULL, scales=NULL, biases=NULL, out=NULL) == OK
+    assert qmm(lib, m=0, x=NULL, y=NULL) == OK
+    assert qmm(lib, n=0, x=NULL, y=NULL, packed=NULL, scales=NULL, biases=NULL) == OK
+    assert rows(lib, n_idx=0, idx=NULL, out=NULL) == OK
+    assert lib.qaff_last_error() == b""
+
+
+def test_error_text_is_per_call(lib):
+    assert dq(lib, bits=7) == UNSUPPORTED
+    assert lib.qaff_last_error() != b""
+    assert qmm(lib, m=0) == OK
+    assert lib.qaff_last_error() == b""
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

@@ -1,0 +1,292 @@
+"""Parity of the HIP path with the CPU oracle, on the GPU, through the C ABI (via the binding).
+
+Bars:
+* dequantize / dequant_rows: bit-exact, float32 and bf16 (both sides form s*c in float32, add the
+  bias in float32, and round bf16 to nearest even).
+* qmm: per-row max relative error (max_n |y - ref| / max_n |ref|) against the float64 oracle of at
+  most 2e-3 for float32 y and 1.6e-2 for bf16 y.
+* A tighter check, derived from each kernel's arithmetic, catches single-code mistakes that the
+  bars above would let through. Its reference is the oracle's own pieces composed the way the kernel
+  computes: the GEMV uses the float32 weights (the oracle as is), the GEMM its weights rounded to
+  bf16 (the oracle's bf16 dequantization, then a float64 matmul). What is left is float32
+  summation order (~1e-6 relative) and, for a bf16 y, one rounding of each output to nearest even:
+  bf16 keeps 8 significant bits, so that rounding moves y by at most 2^-8 = 3.91e-3 of |y| <=
+  max|ref|. Bound: 4e-3 for bf16 y, 1e-4 for float32 y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc_mod
+from gpu_util import banner, dev_weights, dev_x, host_bits, host_f64
+from quantized_matmul_mlx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-3, "bf16": 1.6e-2}
+TIGHT = {"f32": 1e-4, "bf16": 4e-3}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc_mod.build()
+    import quantized_matmul_mlx_amd as q
+    q._lib.load()
+    return orc_mod
+
+
+def qaff():
+    import quantized_matmul_mlx_amd as q
+    return q
+
+
+def run_qmm(inp, m_rows=None, path="auto"):
+    packed, scales, biases = dev_weights(inp)
+    x = dev_x(inp.x, inp.x_dtype)
+    y = qaff().qmm(x, packed, scales, biases, inp.wl.group_size, inp.wl.bits, path=path)
+    torch.cuda.synchronize()
+    return y
+
+
+def kernel_of(inp, path):
+    """Which kernel ran: the GEMM for a forced "gemm", or "auto" with a bf16 x above the GEMV limit."""
+    m = inp.x.shape[0]
+    if inp.x_dtype == "bf16" and (path == "gemm" or (path == "auto" and m > qaff().gemv_max_m())):
+        return "gemm"
+    return "gemv"
+
+
+def bf16_weight_ref(orc, inp, x_rows):
+    """x . bf16(W)^T in float64: the oracle's bf16 dequantization, widened, through numpy matmul."""
+    wl = inp.wl
+    w16 = orc.dequantize(inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, out="bf16")
+    w = orc.bf16_to_f32(w16).astype(np.float64)
+    x = orc.bf16_to_f32(x_rows).astype(np.float64)
+    return x @ w.T
+
+
+def check_qmm(orc, inp, y, rows=None, path="auto"):
+    wl = inp.wl
+    x = inp.x if rows is None else inp.x[rows]
+    ref = orc.qmm(x, inp.x_dtype, inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits)
+    got = host_f64(y) if rows is None else host_f64(y)[rows]
+    assert np.isfinite(got).all()
+    err = orc.max_row_rel_err(got, ref)
+    kind = inp.x_dtype
+    assert err <= TOL[kind], f"max row rel err {err:.3e} > {TOL[kind]}"
+    tight_ref = bf16_weight_ref(orc, inp, x) if kernel_of(inp, path) == "gemm" else ref
+    terr = orc.max_row_rel_err(got, tight_ref)
+    assert terr <= TIGHT[kind], f"{kernel_of(inp, path)}: max row rel err {terr:.3e} against its " \
+                                f"own arithmetic, above {TIGHT[kind]}"
+    return err
+
+
+# ---- the 4-bit g64 [256, 512] reference workload ------------------------------------------------
+
+def test_ref_workload_dequant_bit_exact(orc):
+    wl = W.WORKLOADS["ref_4bit_g64_256x512"]
+    inp = W.make_inputs(wl, m=4)
+    banner("ref dequant")
+    p, s, b = dev_weights(inp)
+    for out in ("f32", "bf16"):
+        got = host_bits(qaff().dequantize(p, s, b, wl.group_size, wl.bits,
+                                          torch.float32 if out == "f32" else torch.bfloat16))
+        ref = orc.dequantize(inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, out=out)
+        np.testing.assert_array_equal(got.view(np.uint32 if out == "f32" else np.uint16),
+                                      ref.view(np.uint32 if out == "f32" else np.uint16))
+
+
+def test_ref_workload_qmm_f32(orc):
+    wl = W.WORKLOADS["ref_4bit_g64_256x512"]
+    inp = W.make_inputs(wl, m=4)
+    banner("ref qmm f32")
+    y = run_qmm(inp)
+    assert y.dtype == torch.float32 and tuple(y.shape) == (4, 256)
+    check_qmm(orc, inp, y)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+def test_ref_workload_qmm_bf16_paths(orc, path):
+    wl = W.WORKLOADS["ref_4bit_g64_256x512"]
+    inp = W.make_inputs(wl, m=4, x_dtype="bf16")
+    banner(f"ref qmm bf16 {path}")
+    y = run_qmm(inp, path=path)
+    assert y.dtype == torch.bfloat16
+    check_qmm(orc, inp, y, path=path)
+
+
+# ---- dequantize at every bit width and group size ----------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_dequant_bit_exact(orc, bits, G):
+    inp = W.random_inputs(bits, G, 67, G * 6, 0, seed=100 + bits * 7 + G)
+    banner(f"dequant bits={bits} G={G}")
+    p, s, b = dev_weights(inp)
+    for out, tdt, view in (("f32", torch.float32, np.uint32), ("bf16", torch.bfloat16, np.uint16)):
+        got = host_bits(qaff().dequantize(p, s, b, G, bits, tdt))
+        ref = orc.dequantize(inp.packed, inp.scales, inp.biases, G, bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
+
+
+# ---- GEMV and GEMM at every bit width, ragged shapes --------------------------------------------
+
+KB_FOR_G = {32: 97, 64: 98, 128: 100}   # blocks per row: > 64 lanes, not a multiple of 64
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("m,x_dtype", [(1, "bf16"), (3, "bf16"), (16, "bf16"), (4, "f32"), (5, "f32")])
+def test_gemv(orc, bits, G, m, x_dtype):
+    k = KB_FOR_G[G] * 32
+    inp = W.random_inputs(bits, G, 150, k, m, x_dtype=x_dtype, seed=bits * 31 + G + m)
+    banner(f"gemv bits={bits} G={G} m={m} x={x_dtype}")
+    y = run_qmm(inp, path="gemv")
+    check_qmm(orc, inp, y, path="gemv")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 128])
+@pytest.mark.parametrize("m,n", [(17, 129), (130, 200), (257, 64)])
+def test_gemm(orc, bits, G, m, n):
+    k = (G // 32) * 7 * 32     # an odd number of 32-code blocks when G = 32: a ragged K tile
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits * 17 + G + m)
+    banner(f"gemm bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemm")
+    check_qmm(orc, inp, y, path="gemm")
+
+
+@pytest.mark.parametrize("m", [15, 16, 17, 18])
+def test_dispatch_boundary_both_paths(orc, m):
+    assert qaff().gemv_max_m() == 16
+    inp = W.random_inputs(4, 64, 96, 1024, m, seed=m)
+    banner(f"dispatch m={m}")
+    ys = {p: run_qmm(inp, path=p) for p in ("auto", "gemv", "gemm")}
+    for p, y in ys.items():
+        check_qmm(orc, inp, y, path=p)
+    auto = "gemv" if m <= 16 else "gemm"
+    assert torch.equal(ys["auto"].view(torch.int16), ys[auto].view(torch.int16))
+
+
+# ---- edge cases ----------------------------------------------------------------------------------
+
+def test_k_zero_writes_zeros(orc):
+    p = torch.zeros((8, 0), dtype=torch.int32, device="cuda")
+    s = torch.zeros((8, 0), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device="cuda")
+    banner("k=0")
+    y = qaff().qmm(x, p, s, s, 32, 4)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (3, 8) and (y == 0).all()
+
+
+def test_empty_m_and_n(orc):
+    inp = W.random_inputs(4, 32, 8, 64, 0)
+    p, s, b = dev_weights(inp)
+    banner("m=0")
+    y = qaff().qmm(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), p, s, b, 32, 4)
+    assert tuple(y.shape) == (0, 8)
+    e = qaff().dequant_rows(p, s, b, torch.zeros((0,), dtype=torch.int32, device="cuda"), 32, 4)
+    assert tuple(e.shape) == (0, 64)
+
+
+def test_one_dimensional_x_is_a_row(orc):
+    inp = W.random_inputs(4, 64, 40, 256, 1, seed=3)
+    p, s, b = dev_weights(inp)
+    x = dev_x(inp.x, "bf16")
+    banner("1-D x")
+    y1 = qaff().qmm(x[0], p, s, b, 64, 4)
+    y2 = qaff().qmm(x, p, s, b, 64, 4)
+    torch.cuda.synchronize()
+    assert tuple(y1.shape) == (40,)
+    assert torch.equal(y1.view(torch.int16), y2[0].view(torch.int16))
+
+
+def test_misaligned_x_is_rejected(orc):
+    inp = W.random_inputs(4, 32, 8, 64, 2)
+    p, s, b = dev_weights(inp)
+    big = torch.zeros(2 * 64 + 1, dtype=torch.bfloat16, device="cuda")
+    x = big[1:].view(2, 64)                      # 2-byte offset: not 16-byte aligned
+    with pytest.raises(qaff().QaffError, match="16-byte"):
+        qaff().qmm(x, p, s, b, 32, 4)
+
+
+def test_repeat_runs_are_bitwise_identical(orc):
+    for path, m in (("gemv", 4), ("gemm", 64)):
+        inp = W.random_inputs(4, 128, 300, 2048, m, seed=5)
+        banner(f"determinism {path}")
+        a = run_qmm(inp, path=path)
+        b = run_qmm(inp, path=path)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---- the full-size workloads -------------------------------------------------------------------
+
+def _full_qmm(orc, name, m, rows=None):
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, m=m)
+    banner(f"full {name} m={m}")
+    y = run_qmm(inp)
+    assert tuple(y.shape) == (m, wl.n)
+    return check_qmm(orc, inp, y, rows=rows)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_full_decode_gemv(orc, m):
+    _full_qmm(orc, "decode_4bit_g64_4096x4096", m)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_full_int8_gemv(orc, m):
+    _full_qmm(orc, "int8_g64_14336x4096", m)
+
+
+@pytest.mark.parametrize("name", ["odd_3bit_g32_11008x4096", "odd_6bit_g32_11008x4096"])
+@pytest.mark.parametrize("m", [1, 16])
+def test_full_odd_widths(orc, name, m):
+    _full_qmm(orc, name, m)
+
+
+def test_full_prefill_gemm_sampled_rows(orc):
+    # every x row computes on the GPU; the oracle checks 24 of them (first, last, spread between)
+    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(2044, 2048), np.arange(7, 2048, 127)]))
+    _full_qmm(orc, "prefill_4bit_g128_4096x14336", 2048, rows=rows)
+
+
+def test_full_decode_dequant_bit_exact(orc):
+    wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
+    inp = W.make_inputs(wl)
+    p, s, b = dev_weights(inp)
+    banner("full dequant 4096x4096")
+    for out, tdt, view in (("f32", torch.float32, np.uint32), ("bf16", torch.bfloat16, np.uint16)):
+        got = host_bits(qaff().dequantize(p, s, b, wl.group_size, wl.bits, tdt))
+        ref = orc.dequantize(inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
+
+
+def test_full_dequant_rows_bit_exact(orc):
+    wl = W.WORKLOADS["rows_4bit_g64_32768x4096"]
+    inp = W.make_inputs(wl)
+    p, s, b = dev_weights(inp)
+    idx = torch.from_numpy(inp.indices.view(np.int32)).cuda()
+    banner("full dequant_rows 32768x4096 / 4096")
+    for out, tdt, view in (("f32", torch.float32, np.uint32), ("bf16", torch.bfloat16, np.uint16)):
+        got = host_bits(qaff().dequant_rows(p, s, b, idx, wl.group_size, wl.bits, tdt))
+        ref = orc.dequant_rows(inp.packed, inp.scales, inp.biases, inp.indices, wl.group_size,
+                               wl.bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
+
+
+def test_dequant_rows_duplicates_and_out_of_range(orc):
+    inp = W.random_inputs(3, 32, 50, 256, 0, seed=23)
+    p, s, b = dev_weights(inp)
+    idx_np = np.array([49, 0, 7, 7, 50, 2**32 - 1, 13], np.uint32)
+    idx = torch.from_numpy(idx_np.view(np.int32)).cuda()
+    banner("dequant_rows oob")
+    for out, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        got = host_bits(qaff().dequant_rows(p, s, b, idx, 32, 3, tdt))
+        ref = orc.dequant_rows(inp.packed, inp.scales, inp.biases, idx_np, 32, 3, out=out)
+        view = np.uint32 if out == "f32" else np.uint16
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
