@@ -2,13 +2,31 @@
 // path of spark_runtime weights/mlx_int8.rs, `gemv`; the product itself is nuvec_core
 // quantized.rs, `quantized_matmul` with transpose). W is never materialised.
 //
-// HBM-bound: every packed word is read exactly once per launch for up to MB rows of x. One wave
-// owns RW rows of W; its 64 lanes split the row's 32-code blocks (lane l takes blocks l, l+64, ...),
-// so each wave-wide load of a block reads contiguous words. Per block the scale and bias are
-// applied once, using the group identity
-//     sum_{k in block} x_k * (s*c_k + b) = s * sum x_k c_k + b * sum x_k,
-// so the inner loop is one multiply-add per code and x-row. The float32 partial sums are reduced
-// across the wave at the end.
+// HBM-bound: every packed word is read once per launch for up to MB rows of x, so the design goal
+// is to have all of a launch's weight bytes in flight as early as possible and to spend few VALU
+// operations per code.
+//
+// bf16 x (the decode path):
+//   * A 256-thread block owns 4 * RPW rows of W (RPW per wave). Lane l of a wave takes the 32-code
+//     blocks l, l + 64, ... of each of its rows, so a wave-wide load of one block per lane reads
+//     contiguous words. Before touching x, each lane issues the loads of every block it needs in
+//     the current pass (RPW rows x P blocks), plus their scales and biases.
+//   * x is staged once per block of threads in LDS, already permuted into the pairing order in
+//     which the codes are unpacked, as bf16 pairs.
+//   * Codes become exact bf16 values with one AND-OR per pair of codes: for codes below 128,
+//     OR-ing the code into the mantissa of bf16 128.0 (0x4300) gives exactly 128 + c. The 4-bit
+//     pairs (c_i, c_{i+4}) of a word are (w >> 4i) & 0x000F000F | 0x43004300; 2-bit pairs
+//     (c_i, c_{i+8}) likewise. 3-, 5- and 6-bit codes are extracted one by one (a bit-field
+//     extract, or a funnel shift for codes that straddle words) and paired in column order. 8-bit
+//     codes go through the byte-to-float converts, exact in bf16 since c <= 255 has 8 bits.
+//   * v_dot2_f32_bf16 multiplies two code pairs by two x pairs and accumulates in float32. Per
+//     block, with d = sum x_k (o + c_k) and xs = sum x_k (o = 128, or 0 for 8-bit codes),
+//         sum_k x_k (s c_k + b) = s * d + (b - o s) * xs,
+//     so the scale, the bias and the offset cost two multiply-adds per block.
+//   * The float32 partial sums are reduced across the wave; lane 0 writes y.
+//
+// float32 x: the straightforward form of the same loop in float32 (codes converted to float, one
+// multiply-add per code and x row), used for float32 inputs at any m.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -20,37 +38,304 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// The 32 x values of block j of x row `row`, as float32.
-template <bool XF32>
-__device__ __forceinline__ void load_x_block(const void* __restrict__ x, uint32_t row, uint32_t k,
-                                             uint32_t j, float (&xv)[32]) {
-    if constexpr (XF32) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + (size_t)row * k + (size_t)j * 32);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
+
+// (a & mask) | orv in one v_and_or_b32 (the compiler otherwise emits an AND and an OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
+    return r;
+}
+
+// ---- per-bit-width unpacking into 16 bf16 pairs per 32-code block ---------------------------
+
+template <int BITS> struct Codes;
+
+// 4-bit: pair 4q + p of block = (c_{8q+p}, c_{8q+p+4}), values 128 + c.
+template <> struct Codes<4> {
+    static constexpr float kOffset = 128.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[4], uint32_t (&pr)[16]) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const f32x4 v = p[q];
-            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
-        }
-    } else {
-        const u32x4a* p = reinterpret_cast<const u32x4a*>(static_cast<const uint16_t*>(x) + (size_t)row * k + (size_t)j * 32);
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) pr[4 * q + p] = and_or(w[q] >> (4 * p), 0x000F000Fu, kMagic);
+    }
+    // x pairs in the same order, from the block's 32 x values as 16 natural-order dwords.
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const u32x4a v = p[q];
-            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t d0 = xn[4 * q], d1 = xn[4 * q + 1], d2 = xn[4 * q + 2], d3 = xn[4 * q + 3];
+            // x_{8q+0..7} = lo(d0) hi(d0) lo(d1) hi(d1) lo(d2) hi(d2) lo(d3) hi(d3)
+            xp[4 * q + 0] = __builtin_amdgcn_perm(d2, d0, 0x05040100u);  // (lo d0, lo d2)
+            xp[4 * q + 1] = __builtin_amdgcn_perm(d2, d0, 0x07060302u);  // (hi d0, hi d2)
+            xp[4 * q + 2] = __builtin_amdgcn_perm(d3, d1, 0x05040100u);  // (lo d1, lo d3)
+            xp[4 * q + 3] = __builtin_amdgcn_perm(d3, d1, 0x07060302u);  // (hi d1, hi d3)
+        }
+    }
+};
+
+// 2-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values 128 + c.
+template <> struct Codes<2> {
+    static constexpr float kOffset = 128.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[2], uint32_t (&pr)[16]) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xv[8 * q + 2 * e] = __uint_as_float(d[e] << 16);
-                xv[8 * q + 2 * e + 1] = __uint_as_float(d[e] & 0xffff0000u);
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) pr[8 * q + p] = and_or(w[q] >> (2 * p), 0x00030003u, kMagic);
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+        // x_{16q+j}: dword 8q + j/2, half j%2. Pair p takes x_{16q+p} and x_{16q+p+8}.
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t a = xn[8 * q + p / 2], b = xn[8 * q + 4 + p / 2];
+                xp[8 * q + p] = (p & 1) ? __builtin_amdgcn_perm(b, a, 0x07060302u)
+                                        : __builtin_amdgcn_perm(b, a, 0x05040100u);
             }
+    }
+};
+
+// 8-bit: pair 2q + h = (c_{4q+2h}, c_{4q+2h+1}), exact values c (offset 0).
+template <> struct Codes<8> {
+    static constexpr float kOffset = 0.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[8], uint32_t (&pr)[16]) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t f0 = __float_as_uint((float)(w[q] & 0xffu));
+            const uint32_t f1 = __float_as_uint((float)((w[q] >> 8) & 0xffu));
+            const uint32_t f2 = __float_as_uint((float)((w[q] >> 16) & 0xffu));
+            const uint32_t f3 = __float_as_uint((float)(w[q] >> 24));
+            // the upper halves of the float32 patterns are the exact bf16 values
+            pr[2 * q] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+            pr[2 * q + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+        }
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xp[i] = xn[i];
+    }
+};
+
+// 3-, 5-, 6-bit: pair i = (c_{2i}, c_{2i+1}) in column order, values 128 + c.
+template <int BITS> struct Codes {
+    static_assert(BITS == 3 || BITS == 5 || BITS == 6, "bit width");
+    static constexpr float kOffset = 128.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[BITS], uint32_t (&pr)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            pr[i] = (code_at<BITS>(w, 2 * i) | (code_at<BITS>(w, 2 * i + 1) << 16)) | kMagic;
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xp[i] = xn[i];
+    }
+};
+
+// ---- bf16 x kernel -----------------------------------------------------------------------------
+
+// Sum over the 64 lanes of a wave with DPP row operations; every lane gets the total.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int moved = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(moved);
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quad sums
+    v = dpp_add<0x141, 0xF>(v);  // row_half_mirror: half-row sums
+    v = dpp_add<0x140, 0xF>(v);  // row_mirror: row sums
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 holds the total
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int BITS, int MB, int RPW, int WAVES, int P>
+__global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
+    const uint16_t* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
+    uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y) {
+    constexpr int kBlockThreads = WAVES * 64;
+    constexpr int kPassBlocks = 64 * P;  // 32-code blocks per row per pass
+    // x of the pass as bf16 pairs in unpack order: [x row][quarter of a block][block] of 16 bytes,
+    // so that lane l reading quarter t of its block reads the 16 bytes after lane l-1's.
+    __shared__ u32x4a xl[MB][4][kPassBlocks];
+    __shared__ float xsl[MB][kPassBlocks][2];  // float32 sums of each half of each block of x
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const uint32_t row0 = (blockIdx.x * WAVES + wave) * RPW;
+    const uint32_t m0 = blockIdx.y * MB;
+    const uint32_t gpr = kb >> gshift;
+
+    float acc[RPW][MB];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[r][i] = 0.f;
+
+    for (uint32_t pass0 = 0; pass0 < kb; pass0 += kPassBlocks) {
+        // 1. Load the pass's x first (one unit = 16 values of one x row), so that it arrives
+        //    ahead of the weights: the wait for it before staging then leaves the weight loads
+        //    in flight, and each block's multiply waits only for its own weight load.
+        constexpr int kUnitsTotal = MB * 2 * kPassBlocks;
+        constexpr int kUnits = (kUnitsTotal + kBlockThreads - 1) / kBlockThreads;
+        u32x4a xg[kUnits][2];
+        bool xvalid[kUnits];
+#pragma unroll
+        for (int t = 0; t < kUnits; ++t) {
+            // clamped so that every load is in bounds and none sits in a branch; values that are
+            // not part of x are zeroed when staged
+            const int u = min(tid + kBlockThreads * t, kUnitsTotal - 1);
+            const int mi = u / (2 * kPassBlocks);
+            const int rem = u - mi * 2 * kPassBlocks;
+            const int h = rem / kPassBlocks;      // which half of the block
+            const int b = rem - h * kPassBlocks;  // block within the pass
+            const uint32_t j = pass0 + b;
+            xvalid[t] = m0 + mi < m && j < kb;
+            const uint32_t xr = min(m0 + mi, m - 1);
+            const uint32_t jc = min(j, kb - 1);
+            const u32x4a* src = reinterpret_cast<const u32x4a*>(x + (size_t)xr * kb * 32 + (size_t)jc * 32 + h * 16);
+            xg[t][0] = src[0];
+            xg[t][1] = src[1];
+        }
+
+        // 2. Issue every weight load of the pass. Rows are wave-uniform, so each row's base
+        //    address is scalar and a lane only adds its own 32-bit offset. Indices are clamped
+        //    into the weight instead of branching around the loads (a branch per load makes the
+        //    compiler wait for each one): a lane past the row's end reads a valid block that it
+        //    never uses, and rows past n are computed but not stored. Scales and biases stay raw
+        //    until use, so no conversion waits on a load here.
+        uint32_t wq[RPW][P][BITS];
+        uint32_t sraw[RPW][P], braw[RPW][P];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const uint32_t row = min(row0 + r, n - 1);
+            const uint32_t* prow = packed + (size_t)row * kb * BITS;
+            const uint16_t* srow = scales + (size_t)row * gpr;
+            const uint16_t* brow = biases + (size_t)row * gpr;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const uint32_t j = min(pass0 + p * 64 + lane, kb - 1);
+                load_block<BITS>(prow + j * BITS, wq[r][p]);
+                sraw[r][p] = srow[j >> gshift];
+                braw[r][p] = brow[j >> gshift];
+            }
+        }
+
+        // 3. Stage x in LDS, paired in unpack order, with the float32 sum of each 16 values.
+        //    Every pairing only mixes values within 16 (2-bit codes) or 8 (the other widths), so
+        //    a unit is paired on its own: it is placed at its position in a block of 32 and the
+        //    block is paired.
+        if (pass0 > 0) __syncthreads();  // the previous pass has finished reading xl and xsl
+#pragma unroll
+        for (int t = 0; t < kUnits; ++t) {
+            const int u = tid + kBlockThreads * t;
+            if (u >= kUnitsTotal) break;
+            const int mi = u / (2 * kPassBlocks);
+            const int rem = u - mi * 2 * kPassBlocks;
+            const int h = rem / kPassBlocks;
+            const int b = rem - h * kPassBlocks;
+            uint32_t xn[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xn[q] = 0u;
+            uint32_t v[8] = {xg[t][0].x, xg[t][0].y, xg[t][0].z, xg[t][0].w,
+                             xg[t][1].x, xg[t][1].y, xg[t][1].z, xg[t][1].w};
+            if (!xvalid[t]) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = 0u;
+            }
+            float hs = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) hs = dot2(v[q], 0x3F803F80u, hs);  // pairs of 1.0
+            xsl[mi][b][h] = hs;
+            uint32_t xp[16];
+            if (h == 0) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xn[q] = v[q];
+                Codes<BITS>::pair_x(xn, xp);
+                xl[mi][0][b] = u32x4a{xp[0], xp[1], xp[2], xp[3]};
+                xl[mi][1][b] = u32x4a{xp[4], xp[5], xp[6], xp[7]};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) xn[8 + q] = v[q];
+                Codes<BITS>::pair_x(xn, xp);
+                xl[mi][2][b] = u32x4a{xp[8], xp[9], xp[10], xp[11]};
+                xl[mi][3][b] = u32x4a{xp[12], xp[13], xp[14], xp[15]};
+            }
+        }
+        __syncthreads();
+
+        // 4. Multiply.
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const uint32_t j = pass0 + p * 64 + lane;
+            if (j >= kb) break;
+            uint32_t xp[MB][16];
+            float xs[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4a v = xl[i][t][p * 64 + lane];
+                    xp[i][4 * t] = v.x; xp[i][4 * t + 1] = v.y; xp[i][4 * t + 2] = v.z; xp[i][4 * t + 3] = v.w;
+                }
+                xs[i] = xsl[i][p * 64 + lane][0] + xsl[i][p * 64 + lane][1];
+            }
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                uint32_t pr[16];
+                Codes<BITS>::unpack(wq[r][p], pr);
+                const float sc = bf16_to_f32(sraw[r][p]);
+                const float boff = bf16_to_f32(braw[r][p]) - Codes<BITS>::kOffset * sc;
+#pragma unroll
+                for (int i = 0; i < MB; ++i) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 16; ++t) d = dot2(pr[t], xp[i][t], d);
+                    acc[r][i] += sc * d + boff * xs[i];
+                }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const uint32_t row = row0 + r;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const float v = wave_sum_dpp(acc[r][i]);
+            if (lane == 0 && row < n && m0 + i < m) y[(size_t)(m0 + i) * n + row] = to_bf16_bits(v);
         }
     }
 }
 
-template <int BITS, bool XF32, int MB, int RW>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(
-    const void* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
+// ---- float32 x kernel ----------------------------------------------------------------------------
+
+template <int MB>
+__device__ __forceinline__ void load_x_f32_block(const float* __restrict__ x, uint32_t row, uint32_t k,
+                                                 uint32_t j, float (&xv)[32]) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(x + (size_t)row * k + (size_t)j * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const f32x4 v = p[q];
+        xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+    }
+}
+
+template <int BITS, int MB, int RW>
+__global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
+    const float* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
-    uint32_t kb, uint32_t gshift, void* __restrict__ y) {
+    uint32_t kb, uint32_t gshift, float* __restrict__ y) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const uint32_t n0 = (blockIdx.x * kWaves + wave) * RW;
@@ -71,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             if (m0 + i < m) {
-                load_x_block<XF32>(x, m0 + i, k, j, xv[i]);
+                load_x_f32_block<MB>(x, m0 + i, k, j, xv[i]);
             } else {
 #pragma unroll
                 for (int c = 0; c < 32; ++c) xv[i][c] = 0.f;
@@ -109,61 +394,99 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             const float v = wave_sum(acc[r][i]);
-            if (lane == 0 && row < n && m0 + i < m) {
-                const size_t o = (size_t)(m0 + i) * n + row;
-                if constexpr (XF32) static_cast<float*>(y)[o] = v;
-                else static_cast<uint16_t*>(y)[o] = to_bf16_bits(v);
-            }
+            if (lane == 0 && row < n && m0 + i < m) y[(size_t)(m0 + i) * n + row] = v;
         }
     }
 }
 
-constexpr int kRowsPerWave = 2;
+// ---- launchers -----------------------------------------------------------------------------------
 
-template <int BITS, bool XF32, int MB>
-hipError_t launch_mb(const void* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                     const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, void* y,
-                     hipStream_t stream) {
-    const int64_t rows_per_block = (int64_t)kWaves * kRowsPerWave;
-    const unsigned gx = (unsigned)((n + rows_per_block - 1) / rows_per_block);
-    const size_t xsize = XF32 ? 4 : 2;
-    // grid.y is limited to 65535 blocks: long x goes in slices of at most 65535 * MB rows.
-    const int64_t max_rows = (int64_t)65535 * MB;
+// grid.y is limited to 65535 blocks: long x goes in slices of at most 65535 * MB rows.
+template <typename Launch>
+hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
+    const int64_t max_rows = (int64_t)65535 * mb;
     for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
         const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
-        const unsigned gy = (unsigned)((mm + MB - 1) / MB);
-        gemv_kernel<BITS, XF32, MB, kRowsPerWave><<<dim3(gx, gy), dim3(kThreads), 0, stream>>>(
-            static_cast<const char*>(x) + (size_t)m_off * kb * 32 * xsize, (uint32_t)mm, packed,
-            scales, biases, (uint32_t)n, (uint32_t)kb, gshift,
-            static_cast<char*>(y) + (size_t)m_off * n * xsize);
+        launch(m_off, mm, (unsigned)((mm + mb - 1) / mb));
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-template <int BITS, bool XF32>
-hipError_t launch_bits(const void* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                       const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, void* y,
+// Rows per wave and waves per block of the bf16 GEMV, per number of x rows handled by one block.
+#ifndef QAFF_GEMV_RPW_1
+#define QAFF_GEMV_RPW_1 1
+#endif
+#ifndef QAFF_GEMV_WAVES_1
+#define QAFF_GEMV_WAVES_1 8
+#endif
+#ifndef QAFF_GEMV_RPW_N
+#define QAFF_GEMV_RPW_N 2
+#endif
+#ifndef QAFF_GEMV_WAVES_N
+#define QAFF_GEMV_WAVES_N 4
+#endif
+
+template <int BITS, int MB, int RPW, int WAVES>
+hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                       const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                        hipStream_t stream) {
-    if (m == 1) return launch_mb<BITS, XF32, 1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-    if (m == 2) return launch_mb<BITS, XF32, 2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-    return launch_mb<BITS, XF32, 4>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    constexpr int P = 2;
+    const int64_t rows_per_block = (int64_t)WAVES * RPW;
+    const unsigned gx = (unsigned)((n + rows_per_block - 1) / rows_per_block);
+    return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
+        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
+            x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
+            (uint32_t)kb, gshift, y + (size_t)m_off * n);
+    });
 }
 
-template <bool XF32>
-hipError_t launch_x(const void* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                    const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, int bits,
-                    void* y, hipStream_t stream) {
-    switch (bits) {
-        case 2: return launch_bits<2, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        case 3: return launch_bits<3, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        case 4: return launch_bits<4, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        case 5: return launch_bits<5, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        case 6: return launch_bits<6, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        case 8: return launch_bits<8, XF32>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-        default: return hipErrorInvalidValue;
-    }
+template <int BITS>
+hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                         hipStream_t stream) {
+    if (m == 1)
+        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    if (m == 2)
+        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    if (m <= 4)
+        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+}
+
+template <int BITS, int MB>
+hipError_t launch_f32(const float* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                      const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, float* y,
+                      hipStream_t stream) {
+    constexpr int RW = 2;
+    const int64_t rows_per_block = (int64_t)kWaves * RW;
+    const unsigned gx = (unsigned)((n + rows_per_block - 1) / rows_per_block);
+    return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
+        gemv_f32_kernel<BITS, MB, RW><<<dim3(gx, gy), dim3(kThreads), 0, stream>>>(
+            x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
+            (uint32_t)kb, gshift, y + (size_t)m_off * n);
+    });
+}
+
+template <int BITS>
+hipError_t launch_f32_m(const float* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, float* y,
+                        hipStream_t stream) {
+    if (m == 1) return launch_f32<BITS, 1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    if (m == 2) return launch_f32<BITS, 2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+    return launch_f32<BITS, 4>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+}
+
+template <int BITS>
+hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* packed,
+                       const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t kb,
+                       uint32_t gshift, void* y, hipStream_t stream) {
+    if (x_f32)
+        return launch_f32_m<BITS>(static_cast<const float*>(x), m, packed, scales, biases, n, kb, gshift,
+                                  static_cast<float*>(y), stream);
+    return launch_bf16_m<BITS>(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, kb, gshift,
+                               static_cast<uint16_t*>(y), stream);
 }
 
 }  // namespace
@@ -173,8 +496,15 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
                        int group_size, int bits, void* y, hipStream_t stream) {
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
-    return x_f32 ? launch_x<true>(x, m, packed, scales, biases, n, kb, gshift, bits, y, stream)
-                 : launch_x<false>(x, m, packed, scales, biases, n, kb, gshift, bits, y, stream);
+    switch (bits) {
+        case 2: return launch_bits<2>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 3: return launch_bits<3>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 4: return launch_bits<4>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 5: return launch_bits<5>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 6: return launch_bits<6>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 8: return launch_bits<8>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qaff
