@@ -149,10 +149,273 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             }
 }
 
+// ---- 256 x 128 tiles for large m --------------------------------------------------------------
+//
+// One 512-thread block (8 waves, 4 along M x 2 along N, 64 x 64 each) owns a 256 x 128 tile of Y
+// and walks K in steps of 64. With about one tile per compute unit at the prefill shape, latency is
+// hidden by prefetching two K-steps ahead into registers: at step t a block stores step t+1 from
+// registers into the free LDS buffer (dequantizing W on the way), issues the global loads of step
+// t+3 into the register set that just emptied, then multiplies step t from the other LDS buffer.
+// LDS rows are 64 bf16 = eight 16-byte chunks; chunk c of row r is stored at position c ^ (r % 8)
+// so that the MFMA operand reads (16 rows at one chunk) and the tile writes spread over the banks.
+// Blocks are ordered so that consecutive tiles along N share one 256-row band of X and each XCD
+// (block index mod 8 on MI355X) gets one band: its 32 compute units then stream the same X rows
+// through their shared L2.
+
+constexpr int BM2 = 256;
+constexpr int BN2 = 128;
+constexpr int kThreads2 = 512;
+constexpr int kLdsA = BM2 * BK;            // bf16 elements of one A buffer
+constexpr int kLdsB = BN2 * BK;            // bf16 elements of one B buffer
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+
+// A thread's share of W per K-step is half a 32-code block: 16 codes. For even widths those are
+// exactly BITS/2 whole words (16 * BITS bits), loaded on their own; for odd widths they straddle a
+// word, so the thread keeps the whole block and picks its half.
+template <int BITS>
+constexpr int kUnitWords = (BITS % 2 == 0) ? BITS / 2 : BITS;
+
+template <int BITS>
+__device__ __forceinline__ void load_unit(const uint32_t* p, uint32_t (&w)[kUnitWords<BITS>]) {
+    constexpr int NW = kUnitWords<BITS>;
+    if constexpr (NW == 1) {
+        w[0] = p[0];
+    } else if constexpr (NW == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        w[0] = v.x; w[1] = v.y;
+    } else if constexpr (NW == 3) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z;
+    } else if constexpr (NW == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+        static_assert(NW == 5, "unit words");
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; w[4] = p[4];
+    }
+}
+
+// Code j of a little-endian stream held in NW words (j compile-time after unrolling).
+template <int BITS, int NW>
+__device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j) {
+    const int bit = j * BITS, wi = bit >> 5, sh = bit & 31;
+    const uint32_t mask = (1u << BITS) - 1u;
+    if (sh + BITS <= 32) return (w[wi] >> sh) & mask;
+    return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+}
+
+// A thread's 16 codes -> 8 dwords of bf16 pairs in column order, w = s*c + b rounded to nearest
+// even (the float32 product is exact, so the fused multiply-add rounds once like mul-then-add).
+template <int BITS>
+__device__ __forceinline__ void dequant16(const uint32_t (&w)[kUnitWords<BITS>], int half, float s, float b,
+                                          uint32_t (&o)[8]) {
+    float v[16];
+    if constexpr (BITS % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = (float)stream_code<BITS, kUnitWords<BITS>>(w, i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] = (float)(half ? stream_code<BITS, BITS>(w, 16 + i) : stream_code<BITS, BITS>(w, i));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = pack_bf16x2(__builtin_fmaf(s, v[2 * i], b), __builtin_fmaf(s, v[2 * i + 1], b));
+}
+
+template <int BITS>
+struct Stage {
+    u32x4a xa[4];                    // 4 chunks of 16 bytes of the X tile
+    uint32_t wq[kUnitWords<BITS>];  // this thread's words of W
+    uint32_t sraw, braw;
+};
+
+template <int BITS>
+// The operand pointers are deliberately not __restrict__: with them the compiler may move the
+// prefetch loads across anything, including the empty asm that keeps them in place.
+__global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint32_t gshift, uint16_t* y,
+    uint32_t tiles_n, uint32_t tiles) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][kLdsA + kLdsB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1;   // 0..3
+    const int wn = wave & 1;    // 0..1
+
+    // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous run of tiles.
+    uint32_t t = blockIdx.x;
+    if ((tiles & 7u) == 0) t = (t & 7u) * (tiles >> 3) + (t >> 3);
+    const uint32_t m0 = (t / tiles_n) * BM2;
+    const uint32_t n0 = (t % tiles_n) * BN2;
+    const uint32_t k = kb * 32;
+    const uint32_t gpr = kb >> gshift;
+    const uint32_t ktiles = (kb + 1) / 2;
+
+    // this thread's W unit: row (0..127) of the tile, block (0..1) of the step, half (0..1)
+    const int wrow = tid >> 2;
+    const int wblk = (tid >> 1) & 1;
+    const int whalf = tid & 1;
+    const uint32_t gn = min(n0 + wrow, n - 1);
+    const uint32_t* wrow_p = packed + (size_t)gn * kb * BITS;
+    const bool wrow_ok = n0 + wrow < n;
+
+    auto load = [&](Stage<BITS>& st, uint32_t kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads2 * i;
+            const int row = c >> 3;
+            const int kc = c & 7;
+            const uint32_t gm = min(m0 + row, m - 1);
+            const uint32_t gk = min(kt * BK + kc * 8, k - 8);
+            st.xa[i] = *reinterpret_cast<const u32x4a*>(x + (size_t)gm * k + gk);
+        }
+        const uint32_t jb = min(kt * 2 + wblk, kb - 1);
+        const uint32_t wofs = (BITS % 2 == 0) ? jb * BITS + whalf * (BITS / 2) : jb * BITS;
+        load_unit<BITS>(wrow_p + wofs, st.wq);
+        // The 4-byte word holding the bf16 scale (bias): a 16-bit load would need a zero-extension
+        // that the compiler places where it waits for the newest loads. The arrays are 4-byte
+        // aligned on this path, so word e/2 holds element e. (Indexing keeps the loads in the
+        // global address space; an integer round trip of the address would turn them into flat
+        // loads, which the compiler can only wait for all at once.)
+        const size_t e = (size_t)gn * gpr + (jb >> gshift);
+        st.sraw = reinterpret_cast<const uint32_t*>(scales)[e >> 1];
+        st.braw = reinterpret_cast<const uint32_t*>(biases)[e >> 1];
+        // Keep the loads here: the operands are read-only, so the compiler would otherwise sink
+        // them towards their first use a whole step later and lose the prefetch distance.
+        asm volatile("" ::: "memory");
+    };
+
+    auto store = [&](const Stage<BITS>& st, uint32_t kt, int buf) {
+        uint16_t* A = lds[buf];
+        uint16_t* B = lds[buf] + kLdsA;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + kThreads2 * i;
+            const int row = c >> 3;
+            const int kc = c & 7;
+            const bool ok = m0 + row < m && kt * BK + kc * 8 < k;
+            u32x4a v = st.xa[i];
+            asm volatile("" : "+v"(v));  // as for W below: keep this step's work from moving up
+            *reinterpret_cast<u32x4a*>(&A[swz(row, kc)]) = ok ? v : u32x4a{0u, 0u, 0u, 0u};
+        }
+        // The empty asm makes this step's W arithmetic start here: the values are otherwise free
+        // to move, and the compiler hoists the next step's dequantization to the top of the loop,
+        // where it has to wait for the newest loads.
+        uint32_t wq[kUnitWords<BITS>];
+#pragma unroll
+        for (int i = 0; i < kUnitWords<BITS>; ++i) {
+            wq[i] = st.wq[i];
+            asm volatile("" : "+v"(wq[i]));
+        }
+        uint32_t sr = st.sraw, br = st.braw;
+        asm volatile("" : "+v"(sr), "+v"(br));
+        const uint32_t odd = (uint32_t)((size_t)gn * gpr + (min(kt * 2 + wblk, kb - 1) >> gshift)) & 1u;  // upper half?
+        sr = odd ? (sr >> 16) : (sr & 0xffffu);
+        br = odd ? (br >> 16) : (br & 0xffffu);
+        uint32_t o[8];
+        dequant16<BITS>(wq, whalf, bf16_to_f32(sr), bf16_to_f32(br), o);
+        const bool ok = wrow_ok && kt * 2 + wblk < kb;
+        const int chunk = wblk * 4 + whalf * 2;
+        *reinterpret_cast<u32x4a*>(&B[swz(wrow, chunk)]) = ok ? u32x4a{o[0], o[1], o[2], o[3]} : u32x4a{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4a*>(&B[swz(wrow, chunk + 1)]) = ok ? u32x4a{o[4], o[5], o[6], o[7]} : u32x4a{0u, 0u, 0u, 0u};
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int fchunk = lane >> 4;
+    auto compute = [&](int buf) {
+        const uint16_t* A = lds[buf];
+        const uint16_t* B = lds[buf] + kLdsA;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8 a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(&A[swz(wm * 64 + i * 16 + frow, kk * 4 + fchunk)]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(&B[swz(wn * 64 + j * 16 + frow, kk * 4 + fchunk)]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // Prologue: step 0 into LDS buffer 0, steps 1 and 2 in flight in the two register sets.
+    // Loads and stores past the last step are not skipped: loads are clamped into the operands and
+    // such stores write zeros into a buffer that no later step reads. A branch around them would
+    // make the compiler wait for every outstanding load instead of only the two-step-old ones.
+    Stage<BITS> s0, s1;
+    load(s0, 0);
+    store(s0, 0, 0);
+    load(s1, 1);
+    load(s0, 2);
+    __syncthreads();
+
+    // Steady state, unrolled by two so each register set has fixed registers:
+    //   even t: s1 holds t+1, s0 holds t+2;  odd t: s0 holds t+1, s1 holds t+2.
+    // The loop always runs whole pairs: with an odd number of steps the last multiply reads a
+    // buffer that was filled with zeros (a step past the end) and adds exact zeros. A branch out of
+    // the middle would again cost the precise waits.
+    for (uint32_t kt = 0; kt < ktiles; kt += 2) {
+        store(s1, kt + 1, 1);
+        load(s1, kt + 3);
+        compute(0);
+        __syncthreads();
+        store(s0, kt + 2, 0);
+        load(s0, kt + 4);
+        compute(1);
+        __syncthreads();
+    }
+
+    const int orow = (lane >> 4) * 4;
+    const int ocol = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint32_t gm = m0 + wm * 64 + i * 16 + orow + v;
+                const uint32_t gc = n0 + wn * 64 + j * 16 + ocol;
+                if (gm < m && gc < n) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][j][v]);
+            }
+}
+
+// m above this uses the 256 x 128 tiles; below, the 128 x 128 tiles waste less on padding.
+constexpr int64_t kBigTileMinM = 256;
+
 template <int BITS>
 hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                        hipStream_t stream) {
+    const bool sb_aligned = (reinterpret_cast<uintptr_t>(scales) % 4 == 0) && (reinterpret_cast<uintptr_t>(biases) % 4 == 0);
+    if (m >= kBigTileMinM && sb_aligned) {
+        const int64_t tiles_n = (n + BN2 - 1) / BN2;
+        // one launch covers at most 2^31 tiles worth of rows; slice m beyond that
+        const int64_t max_rows = (int64_t)(0x7fffffff / tiles_n) * BM2;
+        for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
+            const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
+            const int64_t tiles = ((mm + BM2 - 1) / BM2) * tiles_n;
+            gemm_big_kernel<BITS><<<dim3((unsigned)tiles), dim3(kThreads2), 0, stream>>>(
+                x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
+                (uint32_t)kb, gshift, y + (size_t)m_off * n, (uint32_t)tiles_n, (uint32_t)tiles);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     const unsigned gx = (unsigned)((n + BN - 1) / BN);
     const int64_t max_rows = (int64_t)65535 * BM;
     for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
