@@ -6,15 +6,21 @@ Headline (`value`): the decode GEMV, 4-bit codes in groups of 64, W [4096, 4096]
 effective GB/s of algorithmic bytes
     B = N*K*bits/8 + 4*N*K/G + M*K*2 + M*N*2 = 9,453,568 bytes per step,
 against the 8 TB/s HBM peak. One step is one qmm call; consecutive steps use different copies of
-the weights (about 1 GiB of copies, four times the 256 MB Infinity Cache), so every step reads its
+the operands (about 1 GiB of copies, four times the 256 MB Infinity Cache), so every step reads its
 weights from HBM. The K timed steps are one captured HIP graph (no Python between launches),
 bracketed by synchronizations and timed with events on the stream the kernels run on.
 
-Also measured, in the same JSON line: the prefill GEMM (4-bit g128, x bf16 [2048, 14336],
-W [4096, 14336]) in TFLOP/s against the 2.5 PFLOP/s dense bf16 MFMA peak, and the CPU oracle on
-the host cores (`cpu_baseline`).
+The same JSON line carries:
+  * `prefill_gemm`: the 4-bit g128 prefill GEMM (x bf16 [2048, 14336], W [4096, 14336]) in TFLOP/s
+    against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
+    rows, the 8-bit and the 3-/6-bit GEMVs, the decode GEMV at M = 4), each against its roofline;
+  * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
+    (also given per row).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-prefill] [--no-rows]
+    python bench.py --eager ...           # plain launches, no graph (for profilers)
+    python bench.py --copy-calibration    # a plain copy of known size (counter calibration)
 """
 from __future__ import annotations
 
@@ -28,14 +34,21 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 METRIC = "qmm effective weight GB/s (GEMV, % HBM peak); TFLOP/s (GEMM, % MFMA peak)"
 ROTATE_BYTES = 1 << 30
 
 
-def algorithmic_bytes(m, n, k, bits, group, xsize=2, ysize=2):
+def qmm_bytes(m, n, k, bits, group, xsize=2, ysize=2):
+    """Algorithmic bytes of one qmm: packed codes + bf16 scale and bias per group + x + y."""
     return n * k * bits // 8 + 4 * n * k // group + m * k * xsize + m * n * ysize
+
+
+def dequant_bytes(rows, k, bits, group, osize, indices=False):
+    """Reads the packed codes, scales and biases of `rows` rows (and the uint32 indices), writes
+    rows * k outputs."""
+    return rows * k * bits // 8 + 4 * rows * k // group + (4 * rows if indices else 0) + rows * k * osize
 
 
 def source_hash(*names):
@@ -59,78 +72,220 @@ def read_traffic(kernel_key, sources):
     return rec.get("hbm_bytes_per_launch")
 
 
-def device_inputs(torch, inp, copies):
-    import numpy as np
-    packed = torch.from_numpy(inp.packed.view(np.int32)).cuda()
-    scales = torch.from_numpy(inp.scales.view(np.int16)).cuda().view(torch.bfloat16)
-    biases = torch.from_numpy(inp.biases.view(np.int16)).cuda().view(torch.bfloat16)
-    x = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
-    sets = []
-    for _ in range(copies):
-        sets.append((x.clone(), packed.clone(), scales.clone(), biases.clone()))
-    return sets
+class Timer:
+    """Times `steps` launches of `launch(i)` after `warmup` untimed ones: one captured graph of
+    all steps (default), or plain launches (`eager`, for profilers)."""
 
+    def __init__(self, torch, eager):
+        self.torch = torch
+        self.eager = eager
 
-def time_graph(torch, q, sets, ys, group, bits, steps, warmup):
-    """Runs `warmup` eager steps, then captures `steps` steps in one graph and times one replay."""
-    nsets = len(sets)
-
-    def step(i):
-        x, p, s, b = sets[i % nsets]
-        q.qmm(x, p, s, b, group, bits, out=ys[i % nsets])
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
+    def __call__(self, launch, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            launch(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        if self.eager:
+            torch.cuda.synchronize()
+            start.record()
             for i in range(steps):
-                step(i)
-    torch.cuda.current_stream().wait_stream(side)
-    g.replay()                      # untimed: first replay pays one-time graph upload costs
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps          # ms per step
+                launch(i)
+            end.record()
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / steps
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(steps):
+                    launch(i)
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()                      # untimed: the first replay pays one-time upload costs
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
 
 
-def cpu_baseline_decode(inp, budget_s=10.0, max_runs=50):
-    import oracle
-    threads = oracle.default_threads()
-    wl = inp.wl
+def to_device(torch, inp):
+    import numpy as np
+    d = {
+        "packed": torch.from_numpy(inp.packed.view(np.int32)).cuda(),
+        "scales": torch.from_numpy(inp.scales.view(np.int16)).cuda().view(torch.bfloat16),
+        "biases": torch.from_numpy(inp.biases.view(np.int16)).cuda().view(torch.bfloat16),
+    }
+    if inp.x is not None:
+        d["x"] = torch.from_numpy(inp.x.view(np.int16)).cuda().view(torch.bfloat16)
+    if inp.indices is not None:
+        d["idx"] = torch.from_numpy(inp.indices.view(np.int32)).cuda()
+    return d
+
+
+def copies_for(nbytes, cap=256):
+    return int(max(1, min(cap, -(-ROTATE_BYTES // max(1, nbytes)))))
+
+
+def replicate(torch, d, copies):
+    return [{k: v.clone() for k, v in d.items()} for _ in range(copies)]
+
+
+def cpu_time(fn, budget_s, max_runs):
+    """Runs fn until budget_s seconds or max_runs runs; returns (runs, seconds)."""
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits,
-                   threads=threads)
+        fn()
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= max_runs:
-            break
-    b = algorithmic_bytes(inp.x.shape[0], wl.n, wl.k, wl.bits, wl.group_size)
-    return {"value": round(b * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"the full decode step (M=1, W 4096x4096 4-bit g64) run {runs} times in "
-                      f"{el:.1f} s on {threads} host threads"}
+            return runs, el
 
 
-def cpu_baseline_prefill(inp, rows):
+def hbm_roofline(gbs, traffic=None):
+    return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+# ---- the headline and the rows ------------------------------------------------------------------
+
+def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
+    """One qmm workload at M = m, rotated over ~1 GiB of operand copies."""
     import oracle
-    threads = oracle.default_threads()
-    wl = inp.wl
-    t0 = time.perf_counter()
-    oracle.qmm(inp.x[:rows], "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits,
-               threads=threads)
-    el = time.perf_counter() - t0
-    flop = 2.0 * rows * wl.n * wl.k
-    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "sample": f"{rows} of the 2048 x rows against all of W, {el:.1f} s"}
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, m=m)
+    b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
+    copies = copies_for(b)
+    sets = replicate(torch, to_device(torch, inp), copies)
+    ys = [torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        q.qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del sets, ys
+    torch.cuda.empty_cache()
+    gbs = b / (ms * 1e-3) / 1e9
+    row = {"workload": f"{name} M={m}", "kernel": "gemv" if m <= q.gemv_max_m() else "gemm",
+           "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies,
+           "roofline": hbm_roofline(gbs)}
+    if cpu:
+        threads = oracle.default_threads()
+        runs, el = cpu_time(lambda: oracle.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases,
+                                               wl.group_size, wl.bits, threads=threads), cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(b * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row, gbs, ms, inp
+
+
+def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_budget, gather):
+    import oracle
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl)
+    rows_out = wl.n_indices if gather else wl.n
+    osize = 4 if out_dtype == "f32" else 2
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    b = dequant_bytes(rows_out, wl.k, wl.bits, wl.group_size, osize, indices=gather)
+    d = to_device(torch, inp)
+    if gather:
+        # the table itself is large (75 MB); rotate the indices and outputs, and the table
+        # copies as far as ~1 GiB allows
+        table_bytes = inp.packed.nbytes + inp.scales.nbytes + inp.biases.nbytes
+        copies = copies_for(table_bytes + rows_out * wl.k * osize, cap=16)
+    else:
+        copies = copies_for(b, cap=64)
+    sets = replicate(torch, d, copies)
+    outs = [torch.empty((rows_out, wl.k), dtype=tdt, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        if gather:
+            q.dequant_rows(s["packed"], s["scales"], s["biases"], s["idx"], wl.group_size, wl.bits, tdt,
+                           out=outs[i % copies])
+        else:
+            q.dequantize(s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, tdt,
+                         out=outs[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del sets, outs
+    torch.cuda.empty_cache()
+    gbs = b / (ms * 1e-3) / 1e9
+    kind = "dequant_rows" if gather else "dequantize"
+    row = {"workload": f"{name} {kind} -> {out_dtype}", "kernel": kind, "bytes_per_step": b,
+           "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
+    if cpu:
+        threads = oracle.default_threads()
+        sample = 512
+        if gather:
+            idx = inp.indices[:sample]
+            fn = lambda: oracle.dequant_rows(inp.packed, inp.scales, inp.biases, idx, wl.group_size,
+                                             wl.bits, out=out_dtype, threads=threads)
+        else:
+            fn = lambda: oracle.dequantize(inp.packed[:sample], inp.scales[:sample], inp.biases[:sample],
+                                           wl.group_size, wl.bits, out=out_dtype, threads=threads)
+        runs, el = cpu_time(fn, cpu_budget, 100000)
+        bs = dequant_bytes(sample, wl.k, wl.bits, wl.group_size, osize, indices=gather)
+        row["cpu_baseline"] = {"value": round(bs * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle", "sample": f"{sample} of the {rows_out} rows, {runs} run(s) in {el:.1f} s"}
+    return row
+
+
+def bench_prefill(torch, q, W, timer, steps, cpu):
+    import oracle
+    wl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
+    m = 2048
+    inp = W.make_inputs(wl, m=m)
+    copies = 4
+    sets = replicate(torch, to_device(torch, inp), copies)
+    ys = [torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        q.qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
+
+    ms = timer(launch, steps, 3)
+    del sets, ys
+    torch.cuda.empty_cache()
+    flop = 2.0 * m * wl.n * wl.k
+    tflops = flop / (ms * 1e-3) / 1e12
+    res = {
+        "workload": "prefill GEMM: 4-bit codes, group 128, W [4096, 14336], x bf16 [2048, 14336], "
+                    "y bf16 [2048, 4096]; seed 0",
+        "ms_per_step": round(ms, 5),
+        "tflops": round(tflops, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h"])},
+    }
+    if cpu:
+        threads = oracle.default_threads()
+        rows = 64
+        t0 = time.perf_counter()
+        oracle.qmm(inp.x[:rows], "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits,
+                   threads=threads)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(2.0 * rows * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{rows} of the 2048 x rows against all of W, {el:.1f} s"}
+    return res
+
+
+def copy_calibration(torch):
+    """A plain device copy of 256 MiB, five times: reads and writes exactly 256 MiB each, the
+    reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -139,8 +294,12 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--row-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="plain launches instead of one graph")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -157,23 +316,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     q._lib.load()
+    timer = Timer(torch, args.eager)
+    cpu = not args.no_cpu_baseline
+    log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     # ---- decode GEMV (headline) ----
-    wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
-    m = 1
-    inp = W.make_inputs(wl, m=m)
-    b_step = algorithmic_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
-    copies = max(1, -(-ROTATE_BYTES // b_step))
-    print(f"[bench] decode GEMV: {copies} weight copies, warmup {args.warmup}, steps {args.steps}",
-          file=sys.stderr, flush=True)
-    sets = device_inputs(torch, inp, copies)
-    ys = [torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
-    ms = time_graph(torch, q, sets, ys, wl.group_size, wl.bits, args.steps, args.warmup)
-    gbs = b_step / (ms * 1e-3) / 1e9
-    del sets, ys
-    torch.cuda.empty_cache()
-
+    log(f"decode GEMV M=1: warmup {args.warmup}, steps {args.steps}")
+    row, gbs, ms, inp = bench_qmm(torch, q, W, timer, "decode_4bit_g64_4096x4096", 1, args.steps,
+                                  args.warmup, False, 0)
+    wl = inp.wl
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -190,53 +345,51 @@ def main():
         "config": {
             "workload": "decode GEMV: 4-bit codes, group 64, W [4096, 4096] (uint32 [4096, 512]), "
                         "x bf16 [1, 4096] ~N(0,1), y bf16 [1, 4096]; seed 0",
-            "m": m, "n": wl.n, "k": wl.k, "bits": wl.bits, "group_size": wl.group_size,
-            "algorithmic_bytes_per_step": b_step,
-            "weight_copies": copies,
-            "timing": "one HIP graph of K qmm launches, events on the launch stream",
+            "m": 1, "n": wl.n, "k": wl.k, "bits": wl.bits, "group_size": wl.group_size,
+            "algorithmic_bytes_per_step": row["bytes_per_step"],
+            "weight_copies": row["weight_copies"],
+            "timing": ("plain launches" if args.eager else "one HIP graph of K qmm launches") +
+                      ", events on the launch stream",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(gbs, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic("gemv_4bit_g64_4096x4096_m1", ["gemv.hip", "qaff_device.h"]),
-        },
+        "roofline": hbm_roofline(gbs, read_traffic("gemv_4bit_g64_4096x4096_m1", ["gemv.hip", "qaff_device.h"])),
     }
 
-    # ---- prefill GEMM (second target) ----
+    # ---- prefill GEMM ----
     if not args.no_prefill:
-        pwl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
-        pm = 2048
-        pinp = W.make_inputs(pwl, m=pm)
-        pcopies = 4
-        print(f"[bench] prefill GEMM: {pcopies} copies, steps {args.prefill_steps}", file=sys.stderr, flush=True)
-        psets = device_inputs(torch, pinp, pcopies)
-        pys = [torch.empty((pm, pwl.n), dtype=torch.bfloat16, device="cuda") for _ in range(pcopies)]
-        pms = time_graph(torch, q, psets, pys, pwl.group_size, pwl.bits, args.prefill_steps, 3)
-        flop = 2.0 * pm * pwl.n * pwl.k
-        tflops = flop / (pms * 1e-3) / 1e12
-        result["prefill_gemm"] = {
-            "workload": "prefill GEMM: 4-bit codes, group 128, W [4096, 14336], x bf16 [2048, 14336], "
-                        "y bf16 [2048, 4096]; seed 0",
-            "ms_per_step": round(pms, 5),
-            "tflops": round(tflops, 2),
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h"])},
-        }
-        del psets, pys
-        torch.cuda.empty_cache()
-    else:
-        pinp = None
+        log(f"prefill GEMM: steps {args.prefill_steps}")
+        result["prefill_gemm"] = bench_prefill(torch, q, W, timer, args.prefill_steps, cpu)
 
-    # ---- CPU oracle on the host cores ----
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline_decode(inp)
-        if pinp is not None:
-            result["prefill_gemm"]["cpu_baseline"] = cpu_baseline_prefill(pinp, rows=8)
+    # ---- the other rows of the path ----
+    if not args.no_rows:
+        rows = []
+        rs, rw = args.row_steps, max(10, args.row_steps // 10)
+        for name, m in (("decode_4bit_g64_4096x4096", 4), ("int8_g64_14336x4096", 1),
+                        ("int8_g64_14336x4096", 8), ("odd_3bit_g32_11008x4096", 1),
+                        ("odd_3bit_g32_11008x4096", 16), ("odd_6bit_g32_11008x4096", 1),
+                        ("odd_6bit_g32_11008x4096", 16)):
+            log(f"row: qmm {name} M={m}")
+            rows.append(bench_qmm(torch, q, W, timer, name, m, rs, rw, cpu, 2.0)[0])
+        for out_dtype in ("f32", "bf16"):
+            log(f"row: dequantize decode W -> {out_dtype}")
+            rows.append(bench_dequant(torch, q, W, timer, "decode_4bit_g64_4096x4096", out_dtype, rs, rw,
+                                      cpu, 2.0, gather=False))
+            log(f"row: dequant_rows 4096 of [32768, 4096] -> {out_dtype}")
+            rows.append(bench_dequant(torch, q, W, timer, "rows_4bit_g64_32768x4096", out_dtype, rs, rw,
+                                      cpu, 2.0, gather=True))
+        result["rows"] = rows
+
+    # ---- CPU oracle on the host cores (headline workload) ----
+    if cpu:
+        import oracle
+        log("cpu baseline (oracle)")
+        threads = oracle.default_threads()
+        runs, el = cpu_time(lambda: oracle.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases,
+                                               wl.group_size, wl.bits, threads=threads), 10.0, 100000)
+        result["cpu_baseline"] = {
+            "value": round(row["bytes_per_step"] * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole decode step (M=1, W 4096x4096 4-bit g64) run {runs} times in {el:.1f} s "
+                      f"on {threads} host threads"}
     else:
         result["cpu_baseline"] = None
 
