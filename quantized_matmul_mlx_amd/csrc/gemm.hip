@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 // ---- 256 x 128 tiles for large m --------------------------------------------------------------
 //
-// One 512-thread block (8 waves, 4 along M x 2 along N, 64 x 64 each) owns a 256 x 128 tile of Y
+// One block of WM x WN waves owns a 256 x 128 tile of Y (each wave a (256/WM) x (128/WN) sub-tile)
 // and walks K in steps of 64. With about one tile per compute unit at the prefill shape, latency is
 // hidden by prefetching two K-steps ahead into registers: at step t a block stores step t+1 from
 // registers into the free LDS buffer (dequantizing W on the way), issues the global loads of step
@@ -164,21 +164,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
 constexpr int BM2 = 256;
 constexpr int BN2 = 128;
-constexpr int kThreads2 = 512;
-constexpr int kLdsA = BM2 * BK;            // bf16 elements of one A buffer
-constexpr int kLdsB = BN2 * BK;            // bf16 elements of one B buffer
+constexpr int kLdsA = BM2 * BK;  // bf16 elements of one A buffer
+constexpr int kLdsB = BN2 * BK;  // bf16 elements of one B buffer
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
-// A thread's share of W per K-step is half a 32-code block: 16 codes. For even widths those are
-// exactly BITS/2 whole words (16 * BITS bits), loaded on their own; for odd widths they straddle a
-// word, so the thread keeps the whole block and picks its half.
-template <int BITS>
-constexpr int kUnitWords = (BITS % 2 == 0) ? BITS / 2 : BITS;
+// A thread's share of W per K-step is UC codes (BN2 * BK / threads: 16 or 32). A whole block (32)
+// is BITS words. Half a block is BITS/2 whole words for even widths (16 * BITS bits); for odd
+// widths it straddles a word, so the thread keeps the whole block and picks its half.
+template <int BITS, int UC>
+constexpr int kUnitWords = (UC == 32 || BITS % 2 == 1) ? BITS : BITS / 2;
 
-template <int BITS>
-__device__ __forceinline__ void load_unit(const uint32_t* p, uint32_t (&w)[kUnitWords<BITS>]) {
-    constexpr int NW = kUnitWords<BITS>;
+template <int NW>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
     if constexpr (NW == 1) {
         w[0] = p[0];
     } else if constexpr (NW == 2) {
@@ -190,10 +188,19 @@ __device__ __forceinline__ void load_unit(const uint32_t* p, uint32_t (&w)[kUnit
     } else if constexpr (NW == 4) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(p);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
-        static_assert(NW == 5, "unit words");
+    } else if constexpr (NW == 5) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(p);
         w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w; w[4] = p[4];
+    } else if constexpr (NW == 6) {
+        const u32x3 v = *reinterpret_cast<const u32x3*>(p);
+        const u32x3 u = *reinterpret_cast<const u32x3*>(p + 3);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = u.x; w[4] = u.y; w[5] = u.z;
+    } else {
+        static_assert(NW == 8, "unit words");
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 u = *reinterpret_cast<const u32x4*>(p + 4);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        w[4] = u.x; w[5] = u.y; w[6] = u.z; w[7] = u.w;
     }
 }
 
@@ -206,45 +213,55 @@ __device__ __forceinline__ uint32_t stream_code(const uint32_t (&w)[NW], int j) 
     return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
 }
 
-// A thread's 16 codes -> 8 dwords of bf16 pairs in column order, w = s*c + b rounded to nearest
+// A thread's UC codes -> UC/2 dwords of bf16 pairs in column order, w = s*c + b rounded to nearest
 // even (the float32 product is exact, so the fused multiply-add rounds once like mul-then-add).
-template <int BITS>
-__device__ __forceinline__ void dequant16(const uint32_t (&w)[kUnitWords<BITS>], int half, float s, float b,
-                                          uint32_t (&o)[8]) {
-    float v[16];
-    if constexpr (BITS % 2 == 0) {
+template <int BITS, int UC>
+__device__ __forceinline__ void dequant_unit(const uint32_t (&w)[kUnitWords<BITS, UC>], int half, float s, float b,
+                                             uint32_t (&o)[UC / 2]) {
+    constexpr int NW = kUnitWords<BITS, UC>;
+    float v[UC];
+    if constexpr (UC == 32 || BITS % 2 == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = (float)stream_code<BITS, kUnitWords<BITS>>(w, i);
+        for (int i = 0; i < UC; ++i) v[i] = (float)stream_code<BITS, NW>(w, i);
     } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            v[i] = (float)(half ? stream_code<BITS, BITS>(w, 16 + i) : stream_code<BITS, BITS>(w, i));
+        for (int i = 0; i < UC; ++i)
+            v[i] = (float)(half ? stream_code<BITS, NW>(w, 16 + i) : stream_code<BITS, NW>(w, i));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = pack_bf16x2(__builtin_fmaf(s, v[2 * i], b), __builtin_fmaf(s, v[2 * i + 1], b));
+    for (int i = 0; i < UC / 2; ++i) o[i] = pack_bf16x2(__builtin_fmaf(s, v[2 * i], b), __builtin_fmaf(s, v[2 * i + 1], b));
 }
 
-template <int BITS>
+template <int BITS, int UC, int NCH>
 struct Stage {
-    u32x4a xa[4];                    // 4 chunks of 16 bytes of the X tile
-    uint32_t wq[kUnitWords<BITS>];  // this thread's words of W
-    uint32_t sraw, braw;
+    u32x4a xa[NCH];                      // chunks of 16 bytes of the X tile
+    uint32_t wq[kUnitWords<BITS, UC>];  // this thread's words of W
+    uint32_t sraw, braw;                 // the 4-byte words holding its scale and bias
 };
 
-template <int BITS>
+template <int BITS, int WM, int WN>
 // The operand pointers are deliberately not __restrict__: with them the compiler may move the
 // prefetch loads across anything, including the empty asm that keeps them in place.
-__global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
+__global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
     const uint16_t* biases, uint32_t n, uint32_t kb, uint32_t gshift, uint16_t* y,
     uint32_t tiles_n, uint32_t tiles) {
+    constexpr int kThreadsB = 64 * WM * WN;
+    constexpr int TM = BM2 / WM;              // wave sub-tile rows
+    constexpr int TN = BN2 / WN;              // wave sub-tile columns
+    constexpr int FM = TM / 16, FN = TN / 16;  // 16 x 16 MFMA tiles per wave
+    constexpr int NCH = BM2 * BK / 8 / kThreadsB;  // 16-byte X chunks per thread per step
+    constexpr int UC = BN2 * BK / kThreadsB;       // W codes per thread per step
+    constexpr int UPR = BK / UC;                   // W units per row of the tile
+    constexpr int NW = kUnitWords<BITS, UC>;
+    static_assert(UC == 16 || UC == 32, "W unit");
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][kLdsA + kLdsB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1;   // 0..3
-    const int wn = wave & 1;    // 0..1
+    const int wm = wave / WN;
+    const int wn = wave % WN;
 
     // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous run of tiles.
     uint32_t t = blockIdx.x;
@@ -255,27 +272,28 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
     const uint32_t gpr = kb >> gshift;
     const uint32_t ktiles = (kb + 1) / 2;
 
-    // this thread's W unit: row (0..127) of the tile, block (0..1) of the step, half (0..1)
-    const int wrow = tid >> 2;
-    const int wblk = (tid >> 1) & 1;
-    const int whalf = tid & 1;
+    // this thread's W unit: row of the tile, block (0..1) of the step, half (0..1) when UC = 16
+    const int wrow = tid / UPR;
+    const int wsub = tid % UPR;
+    const int wblk = wsub / (32 / UC);
+    const int whalf = wsub % (32 / UC);
     const uint32_t gn = min(n0 + wrow, n - 1);
     const uint32_t* wrow_p = packed + (size_t)gn * kb * BITS;
     const bool wrow_ok = n0 + wrow < n;
 
-    auto load = [&](Stage<BITS>& st, uint32_t kt) {
+    auto load = [&](Stage<BITS, UC, NCH>& st, uint32_t kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads2 * i;
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + kThreadsB * i;
             const int row = c >> 3;
             const int kc = c & 7;
             const uint32_t gm = min(m0 + row, m - 1);
-            const uint32_t gk = min(kt * BK + kc * 8, k - 8);
+            const uint32_t gk = min(kt * BK + kc * 8, k - 8);  // also clamps steps past the end
             st.xa[i] = *reinterpret_cast<const u32x4a*>(x + (size_t)gm * k + gk);
         }
         const uint32_t jb = min(kt * 2 + wblk, kb - 1);
-        const uint32_t wofs = (BITS % 2 == 0) ? jb * BITS + whalf * (BITS / 2) : jb * BITS;
-        load_unit<BITS>(wrow_p + wofs, st.wq);
+        const uint32_t wofs = (NW == BITS) ? jb * BITS : jb * BITS + whalf * (BITS / 2);
+        load_words<NW>(wrow_p + wofs, st.wq);
         // The 4-byte word holding the bf16 scale (bias): a 16-bit load would need a zero-extension
         // that the compiler places where it waits for the newest loads. The arrays are 4-byte
         // aligned on this path, so word e/2 holds element e. (Indexing keeps the loads in the
@@ -289,12 +307,12 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
         asm volatile("" ::: "memory");
     };
 
-    auto store = [&](const Stage<BITS>& st, uint32_t kt, int buf) {
+    auto store = [&](const Stage<BITS, UC, NCH>& st, uint32_t kt, int buf) {
         uint16_t* A = lds[buf];
         uint16_t* B = lds[buf] + kLdsA;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + kThreads2 * i;
+        for (int i = 0; i < NCH; ++i) {
+            const int c = tid + kThreadsB * i;
             const int row = c >> 3;
             const int kc = c & 7;
             const bool ok = m0 + row < m && kt * BK + kc * 8 < k;
@@ -305,30 +323,32 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
         // The empty asm makes this step's W arithmetic start here: the values are otherwise free
         // to move, and the compiler hoists the next step's dequantization to the top of the loop,
         // where it has to wait for the newest loads.
-        uint32_t wq[kUnitWords<BITS>];
+        uint32_t wq[NW];
 #pragma unroll
-        for (int i = 0; i < kUnitWords<BITS>; ++i) {
+        for (int i = 0; i < NW; ++i) {
             wq[i] = st.wq[i];
             asm volatile("" : "+v"(wq[i]));
         }
         uint32_t sr = st.sraw, br = st.braw;
         asm volatile("" : "+v"(sr), "+v"(br));
-        const uint32_t odd = (uint32_t)((size_t)gn * gpr + (min(kt * 2 + wblk, kb - 1) >> gshift)) & 1u;  // upper half?
+        const uint32_t odd = (uint32_t)((size_t)gn * gpr + (min(kt * 2 + wblk, kb - 1) >> gshift)) & 1u;
         sr = odd ? (sr >> 16) : (sr & 0xffffu);
         br = odd ? (br >> 16) : (br & 0xffffu);
-        uint32_t o[8];
-        dequant16<BITS>(wq, whalf, bf16_to_f32(sr), bf16_to_f32(br), o);
+        uint32_t o[UC / 2];
+        dequant_unit<BITS, UC>(wq, whalf, bf16_to_f32(sr), bf16_to_f32(br), o);
         const bool ok = wrow_ok && kt * 2 + wblk < kb;
         const int chunk = wblk * 4 + whalf * 2;
-        *reinterpret_cast<u32x4a*>(&B[swz(wrow, chunk)]) = ok ? u32x4a{o[0], o[1], o[2], o[3]} : u32x4a{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4a*>(&B[swz(wrow, chunk + 1)]) = ok ? u32x4a{o[4], o[5], o[6], o[7]} : u32x4a{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < UC / 8; ++q)
+            *reinterpret_cast<u32x4a*>(&B[swz(wrow, chunk + q)]) =
+                ok ? u32x4a{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]} : u32x4a{0u, 0u, 0u, 0u};
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int frow = lane & 15;
     const int fchunk = lane >> 4;
@@ -337,17 +357,17 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
         const uint16_t* B = lds[buf] + kLdsA;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 a[4], b[4];
+            bf16x8 a[FM], b[FN];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(&A[swz(wm * 64 + i * 16 + frow, kk * 4 + fchunk)]);
+            for (int i = 0; i < FM; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(&A[swz(wm * TM + i * 16 + frow, kk * 4 + fchunk)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const bf16x8*>(&B[swz(wn * 64 + j * 16 + frow, kk * 4 + fchunk)]);
+            for (int j = 0; j < FN; ++j)
+                b[j] = *reinterpret_cast<const bf16x8*>(&B[swz(wn * TN + j * 16 + frow, kk * 4 + fchunk)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     };
@@ -356,7 +376,7 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
     // Loads and stores past the last step are not skipped: loads are clamped into the operands and
     // such stores write zeros into a buffer that no later step reads. A branch around them would
     // make the compiler wait for every outstanding load instead of only the two-step-old ones.
-    Stage<BITS> s0, s1;
+    Stage<BITS, UC, NCH> s0, s1;
     load(s0, 0);
     store(s0, 0, 0);
     load(s1, 1);
@@ -382,16 +402,24 @@ __global__ __launch_bounds__(kThreads2) void gemm_big_kernel(
     const int orow = (lane >> 4) * 4;
     const int ocol = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const uint32_t gm = m0 + wm * 64 + i * 16 + orow + v;
-                const uint32_t gc = n0 + wn * 64 + j * 16 + ocol;
+                const uint32_t gm = m0 + wm * TM + i * 16 + orow + v;
+                const uint32_t gc = n0 + wn * TN + j * 16 + ocol;
                 if (gm < m && gc < n) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][j][v]);
             }
 }
+
+// Waves of the 256 x 128 tile along M (WN = 2 along N): 2 gives four 128 x 64 wave tiles, 4 gives
+// eight 64 x 64 ones.
+#ifndef QAFF_GEMM_WM
+#define QAFF_GEMM_WM 4
+#endif
+constexpr int kBigWM = QAFF_GEMM_WM;
+constexpr int kBigWN = 2;
 
 // m above this uses the 256 x 128 tiles; below, the 128 x 128 tiles waste less on padding.
 constexpr int64_t kBigTileMinM = 256;
@@ -408,7 +436,7 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
         for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
             const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
             const int64_t tiles = ((mm + BM2 - 1) / BM2) * tiles_n;
-            gemm_big_kernel<BITS><<<dim3((unsigned)tiles), dim3(kThreads2), 0, stream>>>(
+            gemm_big_kernel<BITS, kBigWM, kBigWN><<<dim3((unsigned)tiles), dim3(64 * kBigWM * kBigWN), 0, stream>>>(
                 x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
                 (uint32_t)kb, gshift, y + (size_t)m_off * n, (uint32_t)tiles_n, (uint32_t)tiles);
             const hipError_t e = hipGetLastError();
