@@ -413,6 +413,274 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(
             }
 }
 
+// ---- 128 x 256 tiles for 4-bit codes ------------------------------------------------------------
+//
+// The prefill shape is limited by what the compute units pull through L2, not by HBM: X is re-read
+// once per tile column and W once per tile row. A 128 (M) x 256 (N) tile halves the X traffic of
+// the 256 x 128 tile at the price of twice the dequantization per multiply, and three changes keep
+// the rest of the traffic in whole cache lines and the dequantization cheap:
+//  * W is fetched one 128-byte line per row at a time, i.e. four K-steps (a "super-step") at once:
+//    in load instruction i, the eight lanes of row group g read the eight 16-byte blocks of row
+//    4 g + i, lane (q, b) block 2 ((q + i) & 3) + b. Every lane thereby holds exactly one block of
+//    every K-step of the super-step, in register slot (u - q) & 3 for step u, and picks it with
+//    three selects.
+//  * Scales and biases arrive in windows of 8 groups (16 bytes per row), one window per thread,
+//    and are kept in LDS as float32.
+//  * The multiply uses v_mfma_f32_32x32x16_bf16, which leaves more issue slots for the
+//    dequantization between matrix instructions than the 16x16x32 form, and each step's
+//    dequantization is interleaved with its matrix instructions.
+// Requirements (checked by the launcher): K a multiple of 8 groups and of 64 * kWideBody; W,
+// scales and biases 16-byte aligned. Rows of X beyond m and rows of W beyond n are clamped, not
+// zeroed: they only reach outputs that are not stored.
+//
+// MFMA 32x32x16 (bf16) layout: lane l supplies row l % 32 of A and of W (column of B), each as the
+// 8 consecutive k starting at 8 * (l / 32); result value v of lane l is row 8 (v / 4) + 4 (l / 32)
+// + v % 4, column l % 32. LDS rows are padded to 72 bf16 (144 bytes), which spreads 8 (16) rows
+// read at one chunk over distinct banks and keeps the chunk offsets compile-time immediates.
+
+constexpr int WBM = 128;
+constexpr int WBN = 256;
+constexpr int kWideThreads = 512;
+constexpr int kWideA = WBM * LDK;  // bf16 elements of one A buffer
+constexpr int kWideB = WBN * LDK;  // bf16 elements of one B buffer
+constexpr int kSbPitch = 9;        // floats per row in the scale (bias) window: 8 groups + 1 padding
+constexpr int kWideBody = 16;      // K-steps per loop iteration (windows are 4, 8 or 16 steps)
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_cndmask_b32 with a lane mask: `if_set` in the lanes of `mask`, `if_clear` elsewhere. Written
+// out because the compiler turns chains of lane-dependent selects into divergent branches.
+__device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, uint32_t if_clear) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
+    return r;
+}
+
+template <int GSHIFT>
+__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
+    uint32_t tiles_n) {
+    constexpr int P = (32 << GSHIFT) / 8;  // K-steps per window of 8 groups: 4, 8 or 16
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][kWideA + kWideB];
+    __shared__ float sbl[2][2][WBN * kSbPitch];  // [buffer][scale, bias][row * 9 + group]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2;  // 64-row slice of the tile
+    const int wn = wave & 3;   // 64-column slice
+
+    // Tile order: block b runs on XCD b % 8, so each XCD gets a contiguous run of 32 tiles, laid
+    // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2.
+    const uint32_t tiles = tiles_m * tiles_n;
+    uint32_t t = blockIdx.x;
+    if ((tiles & 7u) == 0) t = (t & 7u) * (tiles >> 3) + (t >> 3);
+    uint32_t tm, tn;
+    if ((tiles_m & 3u) == 0 && (tiles_n & 7u) == 0) {
+        const uint32_t st = t >> 5, w = t & 31u, stn = tiles_n >> 3;
+        tm = (st / stn) * 4 + (w >> 3);
+        tn = (st % stn) * 8 + (w & 7u);
+    } else {
+        tm = t / tiles_n;
+        tn = t % tiles_n;
+    }
+    const uint32_t m0 = tm * WBM;
+    const uint32_t n0 = tn * WBN;
+    const uint32_t k = kb * 32;
+    const uint32_t gpr = kb >> GSHIFT;  // groups per row
+    const uint32_t ktiles = kb >> 1;    // K-steps
+    const uint32_t nsuper = kb >> 3;    // super-steps
+    const uint32_t nwin = gpr >> 3;     // scale windows
+
+    // Per-block bases (uniform) and 32-bit per-lane offsets: a tile spans far less than 4 GiB.
+    const uint16_t* xb = x + (size_t)m0 * k;
+    const uint32_t* wbase = packed + (size_t)n0 * (kb * 4);
+
+    // X: two 16-byte chunks per thread and step, rows xrow and xrow + 64, chunk xkc.
+    const int xrow = tid >> 3;
+    const int xkc = tid & 7;
+    const uint32_t xo0 = (min(m0 + xrow, m - 1) - m0) * k + xkc * 8;
+    const uint32_t xo1 = (min(m0 + xrow + 64, m - 1) - m0) * k + xkc * 8;
+    const int xa0 = xrow * LDK + xkc * 8;
+    const int xa1 = (xrow + 64) * LDK + xkc * 8;
+
+    // W: row group g, lane pair q, block b (see above).
+    const int wg = tid >> 3;
+    const int wq = (tid >> 1) & 3;
+    const int wb = tid & 1;
+    uint32_t wo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        wo[i] = (min(n0 + 4 * wg + i, n - 1) - n0) * (kb * 4) + (((wq + i) & 3) * 2 + wb) * 4;
+
+    // Scale (threads 0..255) or bias (256..511) window of row sb_row.
+    const int sb_arr = tid >> 8;
+    const int sb_row = tid & 255;
+    const uint16_t* sbp = (sb_arr ? biases : scales) + (size_t)min(n0 + sb_row, n - 1) * gpr;
+
+    auto load_x = [&](u32x4a (&xr)[2], uint32_t kt) {
+        const uint16_t* p = xb + min(kt, ktiles - 1) * BK;
+        xr[0] = *reinterpret_cast<const u32x4a*>(p + xo0);
+        xr[1] = *reinterpret_cast<const u32x4a*>(p + xo1);
+    };
+    auto load_w = [&](u32x4a (&wr)[4], uint32_t s) {
+        const uint32_t* p = wbase + min(s, nsuper - 1) * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[i] = *reinterpret_cast<const u32x4a*>(p + wo[i]);
+    };
+    auto load_sb = [&](u32x4a& r, uint32_t win) { r = *reinterpret_cast<const u32x4a*>(sbp + min(win, nwin - 1) * 8); };
+    auto store_sb = [&](const u32x4a& r, int buf) {
+        float* d = &sbl[buf][sb_arr][sb_row * kSbPitch];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            d[2 * e] = __uint_as_float(r[e] << 16);
+            d[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
+        }
+    };
+    auto store_x = [&](const u32x4a (&xr)[2], int buf) {
+        *reinterpret_cast<u32x4a*>(&lds[buf][xa0]) = xr[0];
+        *reinterpret_cast<u32x4a*>(&lds[buf][xa1]) = xr[1];
+    };
+
+    // Lanes whose register slot i (0..2) holds K-step u of a super-step: q == u - i.
+    uint64_t sel[4][3];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 3; ++i) sel[u][i] = __builtin_amdgcn_ballot_w64(wq == ((u - i) & 3));
+
+    // Dequantization of this lane's block of K-step dkt (u = dkt % 4) into B buffer dbuf, split in
+    // four parts (one word, 8 codes, 16 bytes of the tile each) to interleave with the multiply.
+    struct Deq {
+        uint32_t w[4];
+        float s, b;
+        uint16_t* dst;
+    };
+    auto deq_begin = [&](const u32x4a (&wr)[4], uint32_t dkt, int u, int dbuf) {
+        Deq d;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t v = lane_select(sel[u][2], wr[2][c], wr[3][c]);
+            v = lane_select(sel[u][1], wr[1][c], v);
+            d.w[c] = lane_select(sel[u][0], wr[0][c], v);
+        }
+        const int row = 4 * wg + ((u - wq) & 3);
+        const int grp = (int)(((dkt * 2 + wb) >> GSHIFT) & 7u);
+        const int sbuf = (int)((dkt / P) & 1u);
+        d.s = sbl[sbuf][0][row * kSbPitch + grp];
+        d.b = sbl[sbuf][1][row * kSbPitch + grp];
+        d.dst = lds[dbuf] + kWideA + row * LDK + wb * 32;
+        return d;
+    };
+    auto deq_part = [&](const Deq& d, int c) {
+        // even codes in the bytes of lo, odd codes in those of hi; the empty asm keeps the compiler
+        // from turning the byte conversions back into one bit-field extract per code
+        uint32_t lo = d.w[c] & 0x0f0f0f0fu;
+        uint32_t hi = (d.w[c] >> 4) & 0x0f0f0f0fu;
+        asm("" : "+v"(lo), "+v"(hi));
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = pack_bf16x2(__builtin_fmaf(d.s, (float)((lo >> (8 * j)) & 0xffu), d.b),
+                               __builtin_fmaf(d.s, (float)((hi >> (8 * j)) & 0xffu), d.b));
+        *reinterpret_cast<u32x4a*>(d.dst + 8 * c) = u32x4a{o[0], o[1], o[2], o[3]};
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // Operand rows: wm*64 + 32 i + lane % 32 of A, wn*64 + 32 j + lane % 32 of B; chunk 2 kk +
+    // lane / 32 of the step is a constant offset from these.
+    const int aoff = (wm * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
+    const int boff = kWideA + (wn * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
+    auto read_ops = [&](const uint16_t* L, int kk, bf16x8 (&a)[2], bf16x8 (&b)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(L + aoff + 32 * i * LDK + 16 * kk);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(L + boff + 32 * j * LDK + 16 * kk);
+    };
+    // Multiplies step buffer cbuf while dequantizing the next step (d) into the other buffer.
+    auto compute_deq = [&](int cbuf, const Deq& d) {
+        const uint16_t* L = lds[cbuf];
+        bf16x8 a[2][2], b[2][2];
+        read_ops(L, 0, a[0], b[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3) read_ops(L, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
+            deq_part(d, kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Prologue: window 0 in LDS, step 0 in buffer 0, steps 1 and 2 of X in flight, super-steps 0
+    // and 1 of W in registers.
+    u32x4a xr[2][2], wr[2][4], sbr;
+    load_sb(sbr, 0);
+    load_w(wr[0], 0);
+    load_w(wr[1], 1);
+    load_x(xr[0], 0);
+    load_x(xr[1], 1);
+    store_sb(sbr, 0);
+    store_x(xr[0], 0);
+    load_x(xr[0], 2);
+    __syncthreads();
+    {
+        const Deq d = deq_begin(wr[0], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) deq_part(d, c);
+    }
+    __syncthreads();
+
+    // Step kt: store X of step kt+1 into the free buffer and issue the loads of step kt+3 (of
+    // super-step kt/4 + 2 at the end of a super-step; of the next scale window at the start of a
+    // window, stored to LDS two steps before its first use), then multiply step kt while
+    // dequantizing W of step kt+1 into the free buffer. Register sets are fixed by the position in
+    // the unrolled body: X by the step's parity, W by the super-step's.
+    for (uint32_t kt0 = 0; kt0 < ktiles; kt0 += kWideBody) {
+#pragma unroll
+        for (int u = 0; u < kWideBody; ++u) {
+            const uint32_t kt = kt0 + u;
+            const int nb = (u + 1) & 1;
+            const int ws = ((u + 1) >> 2) & 1;  // W set of step kt+1
+            store_x(xr[nb], nb);
+            if (((u + 1) & 3) == 0) load_w(wr[ws ^ 1], (kt + 1) / 4 + 1);
+            load_x(xr[nb], kt + 3);
+            if (u % P == 0) load_sb(sbr, (kt + P) / P);
+            // Keep the loads here: the operands are read-only, so the compiler could otherwise sink
+            // them towards their first use and lose the prefetch distance.
+            asm volatile("" ::: "memory");
+            if (u % P == P - 2) store_sb(sbr, (int)(((kt + 2) / P) & 1u));
+            const Deq d = deq_begin(wr[ws], kt + 1, (u + 1) & 3, nb);
+            compute_deq(u & 1, d);
+            __syncthreads();
+        }
+    }
+
+    const int ocol = lane & 31;
+    const int orow = 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const uint32_t gm = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + orow + (v & 3);
+                const uint32_t gc = n0 + wn * 64 + 32 * j + ocol;
+                if (gm < m && gc < n) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][j][v]);
+            }
+}
+
 // Waves of the 256 x 128 tile along M (WN = 2 along N): 2 gives four 128 x 64 wave tiles, 4 gives
 // eight 64 x 64 ones.
 #ifndef QAFF_GEMM_WM
@@ -465,6 +733,28 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
                        int group_size, int bits, uint16_t* y, hipStream_t stream) {
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    if (bits == 4 && m >= kBigTileMinM && k % (64 * kWideBody) == 0 && k % (8 * (int64_t)group_size) == 0 &&
+        a16(packed) && a16(scales) &&
+        a16(biases)) {
+        const int64_t tiles_n = (n + WBN - 1) / WBN;
+        const int64_t max_rows = (int64_t)(0x7fffffff / tiles_n) * WBM;
+        for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
+            const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
+            const int64_t tiles_m = (mm + WBM - 1) / WBM;
+            const dim3 grid((unsigned)(tiles_m * tiles_n));
+            const uint16_t* xs = x + (size_t)m_off * k;
+            uint16_t* ys = y + (size_t)m_off * n;
+            switch (gshift) {
+                case 0: gemm_wide_kernel<0><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
+                case 1: gemm_wide_kernel<1><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
+                default: gemm_wide_kernel<2><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
+            }
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     switch (bits) {
         case 2: return launch_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 3: return launch_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, stream);

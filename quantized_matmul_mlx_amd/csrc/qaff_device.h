@@ -22,12 +22,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // bf16 bit pattern -> float32: the upper half of the float32 pattern (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Two float32 -> two bf16 in one dword (lo in bits 0..15), round to nearest even. The compiler
-// emits v_cvt_pk_bf16_f32 for the pair.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two float32 -> two bf16 in one dword (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 (two scalar conversions would each be a separate instruction plus a merge).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo;
-    const __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ uint16_t to_bf16_bits(float v) {
