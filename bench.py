@@ -152,6 +152,15 @@ def hbm_roofline(gbs, traffic=None):
 
 # ---- the headline and the rows ------------------------------------------------------------------
 
+def kernel_name(q, m, k):
+    """The kernel the automatic dispatch picks for a bf16 x of m rows (the library's rule)."""
+    if m > q.gemv_max_m():
+        return "gemm"
+    if m >= q.gemv_mfma_min_m() and k % 512 == 0 and k <= 4096:
+        return "gemv_mfma"
+    return "gemv"
+
+
 def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
     """One qmm workload at M = m, rotated over ~1 GiB of operand copies."""
     import oracle
@@ -170,7 +179,7 @@ def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
     del sets, ys
     torch.cuda.empty_cache()
     gbs = b / (ms * 1e-3) / 1e9
-    row = {"workload": f"{name} M={m}", "kernel": "gemv" if m <= q.gemv_max_m() else "gemm",
+    row = {"workload": f"{name} M={m}", "kernel": kernel_name(q, m, wl.k),
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies,
            "roofline": hbm_roofline(gbs)}
     if cpu:

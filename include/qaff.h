@@ -50,9 +50,12 @@ typedef enum {
 
 typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1 } qaff_dtype;
 
-/* Kernel choice for qaff_qmm_ex. AUTO: float32 x -> the VALU kernel at any m; bf16 x -> the
- * bandwidth-bound GEMV when m <= qaff_gemv_max_m(), otherwise the bf16-MFMA GEMM. */
-typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2 } qaff_path;
+/* Kernel choice for qaff_qmm_ex. AUTO: float32 x -> the VALU kernel at any m; bf16 x with
+ * m <= qaff_gemv_max_m() -> the decode path: the VALU GEMV for m below qaff_gemv_mfma_min_m(),
+ * the matrix-core decode kernel (GEMV_MFMA) from there on where it applies (K a multiple of 512
+ * and at most 4096, 4-byte aligned scales and biases), the VALU GEMV otherwise; bf16 x with a
+ * larger m -> the bf16-MFMA GEMM. GEMV_MFMA forced on a shape it does not take is UNSUPPORTED. */
+typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2, QAFF_PATH_GEMV_MFMA = 3 } qaff_path;
 
 /*
  * Dense dequantization (rlx-moshi dequantize_affine; spark_runtime dequantize_to; maya2_mlx QW.dense).
@@ -81,8 +84,10 @@ qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m,
                      int64_t n, int64_t k, int32_t group_size, int32_t bits,
                      void* y, hipStream_t stream);
 
-/* qaff_qmm with the kernel forced, for tests and benchmarks. QAFF_PATH_GEMM with a float32 x is
- * UNSUPPORTED (the MFMA path would round x to bf16); an unknown path is INVALID_ARGUMENT. */
+/* qaff_qmm with the kernel forced, for tests and benchmarks. QAFF_PATH_GEMM or
+ * QAFF_PATH_GEMV_MFMA with a float32 x is UNSUPPORTED (the MFMA paths would round x to bf16), and
+ * so is QAFF_PATH_GEMV_MFMA with m > 16 or a shape it does not take; an unknown path is
+ * INVALID_ARGUMENT. */
 qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
                         const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                         int64_t n, int64_t k, int32_t group_size, int32_t bits,
@@ -113,8 +118,11 @@ const char* qaff_status_string(qaff_status status);
 /* QAFF_ABI_VERSION of the loaded library. */
 int qaff_abi_version(void);
 
-/* Largest m that QAFF_PATH_AUTO sends to the GEMV for a bf16 x. */
+/* Largest m that QAFF_PATH_AUTO sends to the decode path for a bf16 x. */
 int qaff_gemv_max_m(void);
+
+/* Smallest m that QAFF_PATH_AUTO sends to the matrix-core decode kernel (where it applies). */
+int qaff_gemv_mfma_min_m(void);
 
 #ifdef __cplusplus
 }

@@ -73,8 +73,14 @@ def _p(t):
 
 
 def gemv_max_m() -> int:
-    """Largest number of x rows the automatic dispatch sends to the GEMV for a bf16 x."""
+    """Largest number of x rows the automatic dispatch sends to the decode path for a bf16 x."""
     return int(_lib.load().qaff_gemv_max_m())
+
+
+def gemv_mfma_min_m() -> int:
+    """Smallest number of bf16 x rows the automatic dispatch sends to the matrix-core decode
+    kernel (for the shapes it takes)."""
+    return int(_lib.load().qaff_gemv_mfma_min_m())
 
 
 def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=torch.float32,
@@ -100,7 +106,8 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
     """``x . dequantize(W)^T`` (nuvec_core ``quantized_matmul`` with transpose; maya2_mlx ``mm``).
 
     x is float32 or bf16 ``[..., k]`` (a 1-D x is one row); the result has x's dtype and shape
-    ``[..., n]``. ``path`` forces a kernel ("gemv" or "gemm") for tests and benchmarks."""
+    ``[..., n]``. ``path`` forces a kernel ("gemv", "gemv_mfma" or "gemm") for tests and
+    benchmarks."""
     lib = _lib.load()
     dev, n, k = _weights(packed, scales, biases, group_size, bits)
     _need(x, "x", tuple(_OUT_DTYPES), dev)

@@ -16,10 +16,10 @@ QAFF_ERR_DEVICE = 3
 QAFF_F32 = 0
 QAFF_BF16 = 1
 
-PATHS = {"auto": 0, "gemv": 1, "gemm": 2}
+PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "gemv_mfma": 3}
 
 EXPORTS = ("qaff_dequantize", "qaff_qmm", "qaff_qmm_ex", "qaff_dequant_rows", "qaff_last_error",
-           "qaff_status_string", "qaff_abi_version", "qaff_gemv_max_m")
+           "qaff_status_string", "qaff_abi_version", "qaff_gemv_max_m", "qaff_gemv_mfma_min_m")
 
 ABI_VERSION = 1
 
@@ -56,6 +56,7 @@ def load() -> ctypes.CDLL:
     lib.qaff_status_string.argtypes = [ctypes.c_int]
     lib.qaff_abi_version.restype = ctypes.c_int
     lib.qaff_gemv_max_m.restype = ctypes.c_int
+    lib.qaff_gemv_mfma_min_m.restype = ctypes.c_int
     if lib.qaff_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libqaff ABI {lib.qaff_abi_version()} != expected {ABI_VERSION}")
     _lib = lib

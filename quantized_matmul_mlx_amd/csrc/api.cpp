@@ -35,6 +35,10 @@ qaff_status fail(qaff_status st, const char* fmt, ...) {
 }
 
 constexpr int kGemvMaxM = 16;
+#ifndef QAFF_GEMV_MFMA_MIN_M
+#define QAFF_GEMV_MFMA_MIN_M 3
+#endif
+constexpr int kGemvMfmaMinM = QAFF_GEMV_MFMA_MIN_M;
 
 bool debug_sync() {
     static const bool on = [] {
@@ -150,10 +154,16 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint
     if (st != QAFF_OK) return st;
     if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
     if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
-    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMM)
+    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMM && path != QAFF_PATH_GEMV_MFMA)
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown path %d", op, (int)path);
-    if (x_dtype == QAFF_F32 && path == QAFF_PATH_GEMM)
-        return fail(QAFF_ERR_UNSUPPORTED, "%s: the MFMA GEMM takes a bf16 x only", op);
+    if (x_dtype == QAFF_F32 && (path == QAFF_PATH_GEMM || path == QAFF_PATH_GEMV_MFMA))
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the MFMA paths take a bf16 x only", op);
+    // the matrix-core decode kernel: m <= 16, its K range, scale words readable as 4-byte words
+    const bool mfma_ok = x_dtype == QAFF_BF16 && m <= kGemvMaxM && qaff::gemv_mfma_supported(m, k) &&
+                         aligned(scales, 4) && aligned(biases, 4);
+    if (path == QAFF_PATH_GEMV_MFMA && m > 0 && n > 0 && k > 0 && !mfma_ok)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes 1 <= m <= 16, k a multiple "
+                    "of 512 up to 4096 and 4-byte aligned scales and biases", op);
     if (m == 0 || n == 0) return QAFF_OK;
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
     if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
@@ -163,10 +173,16 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint
     if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
     if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
 
-    bool use_gemm = false;
-    if (x_dtype == QAFF_BF16) use_gemm = path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && m > kGemvMaxM);
+    bool use_gemm = false, use_mfma = false;
+    if (x_dtype == QAFF_BF16) {
+        use_gemm = path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && m > kGemvMaxM);
+        use_mfma = path == QAFF_PATH_GEMV_MFMA || (path == QAFF_PATH_AUTO && m >= kGemvMfmaMinM && mfma_ok);
+    }
     hipError_t e;
-    if (use_gemm) {
+    if (use_mfma && !use_gemm) {
+        e = qaff::launch_gemv_mfma(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
+                                   bits, static_cast<uint16_t*>(y), stream);
+    } else if (use_gemm) {
         e = qaff::launch_gemm(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
                               bits, static_cast<uint16_t*>(y), stream);
     } else {
@@ -198,5 +214,7 @@ const char* qaff_status_string(qaff_status status) {
 int qaff_abi_version(void) { return QAFF_ABI_VERSION; }
 
 int qaff_gemv_max_m(void) { return kGemvMaxM; }
+
+int qaff_gemv_mfma_min_m(void) { return kGemvMfmaMinM; }
 
 }  // extern "C"

@@ -1,0 +1,272 @@
+// Quantized decode matmul on the matrix cores: y[m, n] = sum_k x[m, k] * w[n, k] for a few rows
+// of a bf16 x (the decode path of spark_runtime weights/mlx_int8.rs, `gemv`, at m > 1; the
+// product itself is nuvec_core quantized.rs, `quantized_matmul` with transpose). W is never
+// materialised: each code is dequantized once, in registers, straight into an MFMA operand.
+//
+// On the VALU the work per code grows with m (one multiply per code and x row, and the x values
+// through LDS), so from a few rows on the VALU, not HBM, sets the time. Here
+// v_mfma_f32_16x16x32_bf16 takes all (up to 16) x rows at once, and the VALU work per code is
+// the dequantization alone: w = fma(s, c, b) rounded to bf16, as in the prefill GEMM.
+//
+// Layout of the work:
+//  * A block of `kb / 16` waves owns 16 * NT rows of W (NT tiles of 16 rows) and all of K; wave w
+//    takes the K slice [512 w, 512 w + 512): four chunks of 128 codes.
+//  * In chunk c, lane (r, g) = (l % 16, l / 16) of tile t holds the whole 32-code block 4 c + g of
+//    row 16 t + r (BITS words, one load). MFMA j of the chunk takes codes 8 j .. 8 j + 7 of every
+//    lane's block, i.e. K is visited in the order (chunk, j, g, e). The x operand follows the same
+//    order: lane (r, g) supplies x[r][128 c + 32 g + 8 j + e]. The 16x16x32 operand layout: lane l
+//    supplies row l % 16 of A (x) and of W, the 8 values at k-slot l / 16; result value v of lane l
+//    is D[4 (l / 16) + v][l % 16].
+//  * Each wave loads its slice of the x rows (m rounded up to 4, 8 or 16: a compile-time count
+//    keeps the loaded rows in fixed registers) with one contiguous 1 KB load per row and stores
+//    it into its own LDS region, from which the lanes read their operands; no barrier is needed
+//    before the multiply. (LDS-direct copies would skip the registers, but the compiler can only
+//    wait for every outstanding load before reading LDS they wrote.)
+//  * Scales and biases of a tile row come as one window over the slice (16, 8 or 4 groups),
+//    not one load per block: small scattered loads were a third of the time.
+//  * The slices' float32 partial tiles are summed through LDS at the end.
+// Requirements (checked by the launcher): bf16 x, K a multiple of 512 and at most 4096.
+#include "launch.h"
+#include "qaff_device.h"
+
+#include <hip/hip_runtime.h>
+
+namespace qaff {
+namespace {
+
+constexpr int kSlice = 512;                // codes of K per wave
+
+// v_cndmask_b32 with a lane mask: `if_set` in the lanes of `mask`, `if_clear` elsewhere.
+__device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, uint32_t if_clear) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
+    return r;
+}
+
+// Codes 8 j .. 8 j + 7 of a 32-code block, dequantized and rounded to bf16, in k order.
+template <int BITS>
+__device__ __forceinline__ bf16x8 dequant8(const uint32_t (&w)[BITS], int j, float s, float b) {
+    uint32_t o[4];
+    if constexpr (BITS == 4) {
+        // even codes in the bytes of lo, odd codes in those of hi (the empty asm keeps the byte
+        // converts from being turned into one bit-field extract per code)
+        uint32_t lo = w[j] & 0x0f0f0f0fu;
+        uint32_t hi = (w[j] >> 4) & 0x0f0f0f0fu;
+        asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16x2(__builtin_fmaf(s, (float)((lo >> (8 * e)) & 0xffu), b),
+                               __builtin_fmaf(s, (float)((hi >> (8 * e)) & 0xffu), b));
+    } else if constexpr (BITS == 8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t v = w[2 * j + h];
+            o[2 * h] = pack_bf16x2(__builtin_fmaf(s, (float)(v & 0xffu), b), __builtin_fmaf(s, (float)((v >> 8) & 0xffu), b));
+            o[2 * h + 1] = pack_bf16x2(__builtin_fmaf(s, (float)((v >> 16) & 0xffu), b), __builtin_fmaf(s, (float)(v >> 24), b));
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16x2(__builtin_fmaf(s, (float)code_at<BITS>(w, 8 * j + 2 * e), b),
+                               __builtin_fmaf(s, (float)code_at<BITS>(w, 8 * j + 2 * e + 1), b));
+    }
+    return __builtin_bit_cast(bf16x8, u32x4a{o[0], o[1], o[2], o[3]});
+}
+
+constexpr int kXPitch = 2 * kSlice + 16;  // bytes per x row in a wave's LDS region (banks: see below)
+
+// A row's scales (biases) over one slice: 16, 8 or 4 groups, loaded whole (32, 16 or 8 bytes).
+template <int GSHIFT>
+struct SbWindow {
+    static constexpr int kWords = 8 >> GSHIFT;
+    uint32_t w[kWords];
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        if constexpr (kWords == 8) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(p + 8);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w; w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+        } else if constexpr (kWords == 4) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+            w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        } else {
+            const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+            w[0] = a.x; w[1] = a.y;
+        }
+    }
+    // float32 value of the group of block 4 c + g (c compile-time, g = lane / 16)
+    __device__ __forceinline__ float get(int c, int g, uint64_t g_hi) const {
+        uint32_t word, sh;
+        if constexpr (GSHIFT == 0) {         // group 4 c + g: word 2 c + g / 2, half g % 2
+            word = lane_select(g_hi, w[2 * c + 1], w[2 * c]);
+            sh = 16u * (uint32_t)(g & 1);
+        } else if constexpr (GSHIFT == 1) {  // group 2 c + g / 2: word c, half g / 2
+            word = w[c];
+            sh = 16u * (uint32_t)(g >> 1);
+        } else {                             // group c: word c / 2, half c % 2
+            word = w[c >> 1];
+            sh = 16u * (uint32_t)(c & 1);
+        }
+        return __uint_as_float((word >> sh) << 16);
+    }
+};
+
+template <int BITS, int NT, int GSHIFT, int MB>
+__global__ __launch_bounds__(512) void gemv_mfma_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int waves = (int)(kb >> 4);
+    const uint32_t n0 = blockIdx.x * (16 * NT);
+    const uint32_t k = kb * 32;
+    const uint32_t gpr = kb >> GSHIFT;  // groups per row
+    const int lr16 = lane & 15;
+    const int lg = lane >> 4;
+    const uint64_t g_hi = __builtin_amdgcn_ballot_w64(lg >= 2);
+
+    // 1. Loads, oldest first: this wave's slice of every x row (one contiguous 1 KB load per row),
+    //    then per tile the scale and bias windows and, chunk by chunk, the W blocks, so that each
+    //    chunk waits only for what it uses.
+    // MB = m rounded up to 4, 8 or 16; rows past m repeat row m - 1 (their results are not stored)
+    u32x4a xg[MB];
+    const uint16_t* xs = x + (size_t)wave * kSlice + lane * 8;
+#pragma unroll
+    for (int r = 0; r < MB; ++r) xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min((uint32_t)r, m - 1) * k);
+    SbWindow<GSHIFT> sw[NT], bw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
+        const size_t e = (size_t)row * gpr + (size_t)wave * (16 >> GSHIFT);
+        sw[t].load(scales + e);
+        bw[t].load(biases + e);
+    }
+    uint32_t wq[NT][4][BITS];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
+            const uint32_t jb = (uint32_t)wave * 16 + 4 * c + lg;
+            load_block<BITS>(packed + (size_t)row * kb * BITS + (size_t)jb * BITS, wq[t][c]);
+        }
+        asm volatile("" ::: "memory");  // chunk by chunk, in issue order
+    }
+
+    // 2. x into this wave's LDS region: row r at r * 1040 bytes, so the 16 rows that the operand
+    //    read touches at one offset fall on distinct banks (1040 / 4 = 4 mod 64).
+    uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
+#pragma unroll
+    for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
+    const uint8_t* xa = xl + min((uint32_t)lr16, (uint32_t)MB - 1) * kXPitch + lg * 64;
+
+    // 3. Multiply, chunk by chunk. Lane (r, g) of chunk c holds block 4 c + g of its row; MFMA j
+    //    takes codes 8 j .. 8 j + 7 of each lane's block, and x in the same order.
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        // The empty asm makes chunk c's arithmetic start here, after every load is issued and
+        // after chunk c - 1's multiply (its input): the compiler would otherwise hoist the cheap
+        // scale selection of every chunk into the loads and wait for all of them there.
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(wq[t][c][i]) : "v"(acc[0]));
+        bf16x8 wb[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const float sc = sw[t].get(c, lg, g_hi);
+            const float bi = bw[t].get(c, lg, g_hi);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
+        }
+    }
+
+    // 4. Sum the slices' partial tiles through LDS: [wave][tile][v][lane] float32.
+    __syncthreads();  // every wave is done with its x rows
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((wave * NT + t) * 4 + v) * 64 + lane] = acc[t][v];
+    __syncthreads();
+    for (int o = tid; o < 256 * NT; o += (int)blockDim.x) {
+        const int t = o >> 8, mm = (o >> 4) & 15, nn = o & 15;
+        const int l = ((mm >> 2) << 4) | nn, v = mm & 3;
+        float sum = 0.f;
+        for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+        const uint32_t row = n0 + 16 * t + nn;
+        if ((uint32_t)mm < m && row < n) y[(size_t)mm * n + row] = to_bf16_bits(sum);
+    }
+}
+
+template <int BITS, int NT, int GSHIFT, int MB>
+hipError_t launch_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                     const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    const int waves = (int)(kb / 16);
+    size_t lds = (size_t)waves * MB * kXPitch;
+    const size_t red = (size_t)waves * NT * 4 * 64 * sizeof(float);
+    if (red > lds) lds = red;
+    const unsigned blocks = (unsigned)((n + 16 * NT - 1) / (16 * NT));
+    gemv_mfma_kernel<BITS, NT, GSHIFT, MB><<<dim3(blocks), dim3(waves * 64), lds, stream>>>(
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y);
+    return hipGetLastError();
+}
+
+template <int BITS, int GSHIFT, int MB>
+hipError_t launch_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                    const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    // Tiles of 16 rows per block: two for large n, so that each x row serves more rows of W.
+    if (n > 6144) return launch_nt<BITS, 2, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+    return launch_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+}
+
+template <int BITS, int GSHIFT>
+hipError_t launch_mb(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                     const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    if (m <= 4) return launch_g<BITS, GSHIFT, 4>(x, m, packed, scales, biases, n, kb, y, stream);
+    if (m <= 8) return launch_g<BITS, GSHIFT, 8>(x, m, packed, scales, biases, n, kb, y, stream);
+    return launch_g<BITS, GSHIFT, 16>(x, m, packed, scales, biases, n, kb, y, stream);
+}
+
+template <int BITS>
+hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                       const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                       hipStream_t stream) {
+    if (gshift == 0) return launch_mb<BITS, 0>(x, m, packed, scales, biases, n, kb, y, stream);
+    if (gshift == 1) return launch_mb<BITS, 1>(x, m, packed, scales, biases, n, kb, y, stream);
+    return launch_mb<BITS, 2>(x, m, packed, scales, biases, n, kb, y, stream);
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(int64_t m, int64_t k) {
+    return m >= 1 && m <= 16 && k % kSlice == 0 && k <= 8 * kSlice;
+}
+
+hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                            const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
+                            uint16_t* y, hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 2: return launch_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 3: return launch_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 4: return launch_bits<4>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 5: return launch_bits<5>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 6: return launch_bits<6>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        case 8: return launch_bits<8>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qaff

@@ -19,6 +19,14 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                        int group_size, int bits, void* y, hipStream_t stream);
 
+// The decode product on the matrix cores: y[m, n] (bf16) = x (bf16) . dequantize(W)^T for
+// 1 <= m <= 16, with each code dequantized to bf16 in registers. Only for shapes where
+// gemv_mfma_supported(m, k) holds, and scales/biases 4-byte aligned.
+bool gemv_mfma_supported(int64_t m, int64_t k);
+hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed,
+                            const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                            int group_size, int bits, uint16_t* y, hipStream_t stream);
+
 // y[m, n] (bf16) = x (bf16) . dequantize(W)^T with W tiles dequantized to bf16 and bf16 MFMA,
 // float32 accumulation.
 hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,

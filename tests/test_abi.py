@@ -49,6 +49,7 @@ def test_version_and_status_strings(lib):
     assert lib.qaff_status_string(UNSUPPORTED) == b"QAFF_ERR_UNSUPPORTED"
     assert lib.qaff_status_string(_lib.QAFF_ERR_DEVICE) == b"QAFF_ERR_DEVICE"
     assert lib.qaff_gemv_max_m() >= 1
+    assert 1 <= lib.qaff_gemv_mfma_min_m() <= lib.qaff_gemv_max_m()
 
 
 def dq(lib, rows=4, cols=64, G=32, bits=4, packed=A16, scales=A16, biases=A16, out=A16, dt=F32):
@@ -125,6 +126,13 @@ def test_dtype_and_path_checks(lib):
     assert qmm(lib, path=9) == INVALID
     assert qmm(lib, xdt=F32, path=2) == UNSUPPORTED      # the MFMA GEMM takes bf16 x only
     assert b"bf16" in lib.qaff_last_error()
+    assert qmm(lib, xdt=F32, path=3) == UNSUPPORTED      # so does the matrix-core decode kernel
+    # the matrix-core decode kernel: k a multiple of 512 up to 4096, m <= 16, 4-byte scale words
+    assert qmm(lib, k=64, path=3) == UNSUPPORTED
+    assert b"matrix-core decode" in lib.qaff_last_error()
+    assert qmm(lib, k=8192, path=3) == UNSUPPORTED
+    assert qmm(lib, m=17, k=512, path=3) == UNSUPPORTED
+    assert qmm(lib, k=512, scales=A2, path=3) == UNSUPPORTED
     assert rows(lib, dt=-1) == INVALID
 
 

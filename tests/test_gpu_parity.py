@@ -7,8 +7,9 @@ Bars:
   most 2e-3 for float32 y and 1.6e-2 for bf16 y.
 * A tighter check, derived from each kernel's arithmetic, catches single-code mistakes that the
   bars above would let through. Its reference is the oracle's own pieces composed the way the kernel
-  computes: the GEMV uses the float32 weights (the oracle as is), the GEMM its weights rounded to
-  bf16 (the oracle's bf16 dequantization, then a float64 matmul). What is left is float32
+  computes: the VALU GEMV uses the float32 weights (the oracle as is), the two MFMA kernels (GEMM
+  and matrix-core decode) their weights rounded to bf16 (the oracle's bf16 dequantization, then a
+  float64 matmul). What is left is float32
   summation order (~1e-6 relative) and, for a bf16 y, one rounding of each output to nearest even:
   bf16 keeps 8 significant bits, so that rounding moves y by at most 2^-8 = 3.91e-3 of |y| <=
   max|ref|. Bound: 4e-3 for bf16 y, 1e-4 for float32 y.
@@ -50,11 +51,22 @@ def run_qmm(inp, m_rows=None, path="auto"):
     return y
 
 
+def mfma_decode_takes(inp):
+    """Shapes the matrix-core decode kernel takes: 1 <= m <= 16, k a multiple of 512 up to 4096."""
+    m, k = inp.x.shape[0], inp.wl.k
+    return 1 <= m <= 16 and k % 512 == 0 and k <= 4096
+
+
 def kernel_of(inp, path):
-    """Which kernel ran: the GEMM for a forced "gemm", or "auto" with a bf16 x above the GEMV limit."""
+    """Which kernel ran: "gemm" (bf16-MFMA GEMM), "gemv_mfma" (matrix-core decode kernel) or
+    "gemv" (VALU GEMV), as the dispatch in the library picks them."""
     m = inp.x.shape[0]
-    if inp.x_dtype == "bf16" and (path == "gemm" or (path == "auto" and m > qaff().gemv_max_m())):
+    if inp.x_dtype != "bf16":
+        return "gemv"
+    if path == "gemm" or (path == "auto" and m > qaff().gemv_max_m()):
         return "gemm"
+    if path == "gemv_mfma" or (path == "auto" and m >= qaff().gemv_mfma_min_m() and mfma_decode_takes(inp)):
+        return "gemv_mfma"
     return "gemv"
 
 
@@ -76,7 +88,8 @@ def check_qmm(orc, inp, y, rows=None, path="auto"):
     err = orc.max_row_rel_err(got, ref)
     kind = inp.x_dtype
     assert err <= TOL[kind], f"max row rel err {err:.3e} > {TOL[kind]}"
-    tight_ref = bf16_weight_ref(orc, inp, x) if kernel_of(inp, path) == "gemm" else ref
+    # both MFMA kernels multiply bf16-rounded weights
+    tight_ref = bf16_weight_ref(orc, inp, x) if kernel_of(inp, path) != "gemv" else ref
     terr = orc.max_row_rel_err(got, tight_ref)
     assert terr <= TIGHT[kind], f"{kernel_of(inp, path)}: max row rel err {terr:.3e} against its " \
                                 f"own arithmetic, above {TIGHT[kind]}"
@@ -170,16 +183,50 @@ def test_gemm_wide_tiles(orc, G, m, n, k):
     check_qmm(orc, inp, y, path="gemm")
 
 
-@pytest.mark.parametrize("m", [15, 16, 17, 18])
-def test_dispatch_boundary_both_paths(orc, m):
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 15, 16, 17, 18])
+def test_dispatch_boundary_all_paths(orc, m):
     assert qaff().gemv_max_m() == 16
     inp = W.random_inputs(4, 64, 96, 1024, m, seed=m)
     banner(f"dispatch m={m}")
-    ys = {p: run_qmm(inp, path=p) for p in ("auto", "gemv", "gemm")}
+    paths = ("auto", "gemv", "gemm") + (("gemv_mfma",) if m <= 16 else ())
+    ys = {p: run_qmm(inp, path=p) for p in paths}
     for p, y in ys.items():
         check_qmm(orc, inp, y, path=p)
-    auto = "gemv" if m <= 16 else "gemm"
+    auto = kernel_of(inp, "auto")
+    assert auto == ("gemm" if m > 16 else "gemv_mfma" if m >= qaff().gemv_mfma_min_m() else "gemv")
     assert torch.equal(ys["auto"].view(torch.int16), ys[auto].view(torch.int16))
+
+
+# The matrix-core decode kernel: every width and group size, m from 1 to 16, ragged n (not a
+# multiple of 16), K from one to eight 512-code slices, and n large enough for 2 and 4 row tiles
+# per block.
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("m,n,k", [(1, 150, 512), (3, 150, 1536), (8, 77, 4096), (16, 150, 2048)])
+def test_gemv_mfma(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits * 13 + G + m + n)
+    banner(f"gemv_mfma bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
+@pytest.mark.parametrize("n", [4100, 8200])
+def test_gemv_mfma_row_tiles(orc, n):
+    inp = W.random_inputs(4, 64, n, 512, 5, seed=n)
+    banner(f"gemv_mfma row tiles n={n}")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
+def test_gemv_mfma_rejects_other_shapes(orc):
+    inp = W.random_inputs(4, 32, 8, 768, 4, seed=1)   # k not a multiple of 512
+    p, s, b = dev_weights(inp)
+    with pytest.raises(qaff().QaffError, match="matrix-core decode"):
+        qaff().qmm(dev_x(inp.x, "bf16"), p, s, b, 32, 4, path="gemv_mfma")
+    inp = W.random_inputs(4, 32, 8, 512, 17, seed=1)  # m above 16
+    p, s, b = dev_weights(inp)
+    with pytest.raises(qaff().QaffError, match="matrix-core decode"):
+        qaff().qmm(dev_x(inp.x, "bf16"), p, s, b, 32, 4, path="gemv_mfma")
 
 
 # ---- edge cases ----------------------------------------------------------------------------------
