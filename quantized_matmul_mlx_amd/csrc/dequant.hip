@@ -3,8 +3,14 @@
 // maya2_mlx quant.py, rows).
 //
 // HBM-bound and write-dominated: a 4-bit weight reads 0.5 B of codes and writes 4 B (float32) or
-// 2 B (bf16). One thread owns one 32-code block: it loads the block's `bits` words in one or two
-// vector loads, reads the block's single scale and bias, and writes 32 outputs as 16-byte stores.
+// 2 B (bf16), so the stores decide the speed. Each lane produces 4 consecutive outputs at a time
+// (a "unit"), and the lanes of a wave take consecutive units, so that every store instruction
+// writes one contiguous run (1 KB of float32, 512 B of bf16). A unit's 4 codes are 4 * bits
+// consecutive bits of the row: one funnel shift of the (at most two) words they lie in. Its
+// scale and bias are those of its group; the lanes of a group read the same two values.
+// Blocks map to (row segment, row), so a lane finds its row and column without a division;
+// one block covers 256 * kUnits units of one row. The gathered form reads the source row index
+// once per block (a scalar load) and writes quiet NaNs for an index past the table.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -14,51 +20,65 @@ namespace qaff {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnits = 4;  // units per lane: all loads of the four are issued before any store
 
+// The pointers are deliberately not __restrict__: with it, the compiler moves each unit's loads
+// down to its store, one unit at a time, past the empty asm that keeps them together.
 template <int BITS, bool OUT_BF16, bool GATHER>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
-    const uint32_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, const uint32_t* __restrict__ indices, uint32_t table_rows,
-    uint32_t out_rows, uint32_t kb, uint32_t gshift, void* __restrict__ out) {
-#pragma clang fp contract(off)
-    const uint32_t total = out_rows * kb;  // the host guarantees this fits in 32 bits
-    const uint32_t gpr = kb >> gshift;     // groups per row
-    for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b < total; b += gridDim.x * kThreads) {
-        const uint32_t r = b / kb;
-        const uint32_t j = b - r * kb;
-        uint32_t src = r;
-        if constexpr (GATHER) src = indices[r];
-        float v[32];
-        if (GATHER && src >= table_rows) {
+    const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+    const uint32_t* indices, uint32_t table_rows, uint32_t kb, uint32_t gshift, void* out) {
+    const uint32_t r = blockIdx.y;
+    const uint32_t upr = kb * 8;       // 4-code units per row
+    const uint32_t wpr = kb * BITS;    // packed words per row
+    const uint32_t gpr = kb >> gshift;  // groups per row
+    uint32_t src = r;
+    bool ok = true;
+    if constexpr (GATHER) {
+        src = indices[r];  // uniform: a scalar load
+        ok = src < table_rows;
+        if (!ok) src = 0;  // read a valid row; the outputs are NaN
+    }
+    const uint32_t* prow = packed + (size_t)src * wpr;
+    const uint16_t* srow = scales + (size_t)src * gpr;
+    const uint16_t* brow = biases + (size_t)src * gpr;
+    const uint32_t u0 = blockIdx.x * (kThreads * kUnits) + threadIdx.x;
+
+    uint32_t w0[kUnits], w1[kUnits], sh[kUnits];
+    uint16_t sv[kUnits], bv[kUnits];
 #pragma unroll
-            for (int c = 0; c < 32; ++c) v[c] = __uint_as_float(0x7fc00000u);
-        } else {
-            uint32_t w[BITS];
-            load_block<BITS>(packed + (size_t)src * kb * BITS + (size_t)j * BITS, w);
-            const size_t gi = (size_t)src * gpr + (j >> gshift);
-            const float s = bf16_to_f32(scales[gi]);
-            const float bias = bf16_to_f32(biases[gi]);
+    for (int i = 0; i < kUnits; ++i) {
+        const uint32_t p = min(u0 + i * kThreads, upr - 1);  // clamped: loads stay in the row
+        const uint32_t bit = p * 4 * BITS;
+        const uint32_t wi = bit >> 5;
+        sh[i] = bit & 31;
+        w0[i] = prow[wi];
+        w1[i] = prow[min(wi + 1, wpr - 1)];  // only read when the unit straddles two words
+        const uint32_t g = p >> (3 + gshift);
+        sv[i] = srow[g];
+        bv[i] = brow[g];
+    }
+    asm volatile("" ::: "memory");  // every load of the lane before its first store
 #pragma unroll
-            for (int c = 0; c < 32; ++c) {
-                const float p = s * (float)code_at<BITS>(w, c);
-                v[c] = p + bias;
-            }
+    for (int i = 0; i < kUnits; ++i) {
+        const uint32_t p = u0 + i * kThreads;
+        const uint32_t v = __builtin_amdgcn_alignbit(w1[i], w0[i], sh[i]);
+        const float s = bf16_to_f32(sv[i]);
+        const float b = bf16_to_f32(bv[i]);
+        float o[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // s * code is exact in float32, so the fused form rounds once, like s * c then + b
+            o[c] = ok ? __builtin_fmaf(s, (float)((v >> (c * BITS)) & ((1u << BITS) - 1u)), b)
+                      : __uint_as_float(0x7fc00000u);
         }
-        if constexpr (OUT_BF16) {
-            u32x4a* o = reinterpret_cast<u32x4a*>(static_cast<uint16_t*>(out) + ((size_t)r * kb + j) * 32);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x4a d;
-                d.x = pack_bf16x2(v[8 * q + 0], v[8 * q + 1]);
-                d.y = pack_bf16x2(v[8 * q + 2], v[8 * q + 3]);
-                d.z = pack_bf16x2(v[8 * q + 4], v[8 * q + 5]);
-                d.w = pack_bf16x2(v[8 * q + 6], v[8 * q + 7]);
-                o[q] = d;
+        const size_t e = (size_t)r * upr * 4 + (size_t)p * 4;
+        if (p < upr) {
+            if constexpr (OUT_BF16) {
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            } else {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = f32x4{o[0], o[1], o[2], o[3]};
             }
-        } else {
-            f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + ((size_t)r * kb + j) * 32);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) o[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
         }
     }
 }
@@ -67,14 +87,23 @@ template <int BITS, bool OUT_BF16, bool GATHER>
 hipError_t launch_one(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                       const uint32_t* indices, int64_t table_rows, int64_t out_rows, int64_t kb,
                       uint32_t gshift, void* out, hipStream_t stream) {
-    const int64_t total = out_rows * kb;
-    int64_t grid = (total + kThreads - 1) / kThreads;
-    const int64_t cap = (int64_t)device_cu_count() * 16;
-    if (grid > cap) grid = cap;
-    dequant_kernel<BITS, OUT_BF16, GATHER><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-        packed, scales, biases, indices, (uint32_t)table_rows,
-        (uint32_t)out_rows, (uint32_t)kb, gshift, out);
-    return hipGetLastError();
+    const int64_t upr = kb * 8;
+    const unsigned gx = (unsigned)((upr + kThreads * kUnits - 1) / (kThreads * kUnits));
+    const size_t osize = OUT_BF16 ? 2 : 4;
+    // grid.y is limited to 65535 rows per launch
+    for (int64_t r0 = 0; r0 < out_rows; r0 += 65535) {
+        const int64_t rows = out_rows - r0 < 65535 ? out_rows - r0 : 65535;
+        const uint32_t* pk = GATHER ? packed : packed + (size_t)r0 * kb * BITS;
+        const uint16_t* sc = GATHER ? scales : scales + (size_t)r0 * (kb >> gshift);
+        const uint16_t* bi = GATHER ? biases : biases + (size_t)r0 * (kb >> gshift);
+        const uint32_t* ix = GATHER ? indices + r0 : nullptr;
+        void* o = static_cast<char*>(out) + (size_t)r0 * kb * 32 * osize;
+        dequant_kernel<BITS, OUT_BF16, GATHER><<<dim3(gx, (unsigned)rows), dim3(kThreads), 0, stream>>>(
+            pk, sc, bi, ix, (uint32_t)table_rows, (uint32_t)kb, gshift, o);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int BITS>
