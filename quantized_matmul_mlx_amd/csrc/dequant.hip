@@ -3,10 +3,10 @@
 // maya2_mlx quant.py, rows).
 //
 // HBM-bound and write-dominated: a 4-bit weight reads 0.5 B of codes and writes 4 B (float32) or
-// 2 B (bf16), so the stores decide the speed. Each lane produces 4 consecutive outputs at a time
-// (a "unit"), and the lanes of a wave take consecutive units, so that every store instruction
-// writes one contiguous run (1 KB of float32, 512 B of bf16). A unit's 4 codes are 4 * bits
-// consecutive bits of the row: one funnel shift of the (at most two) words they lie in. Its
+// 2 B (bf16), so the stores decide the speed. Each lane produces 16 bytes of consecutive outputs
+// at a time (a "unit": 4 float32, or 8 bf16 for codes up to 4 bits, else 4), and the lanes of a
+// wave take consecutive units, so that every store instruction writes one contiguous run. A
+// unit's codes are consecutive bits of the row: one funnel shift of the two words they lie in. Its
 // scale and bias are those of its group; the lanes of a group read the same two values.
 // Blocks map to (row segment, row), so a lane finds its row and column without a division;
 // one block covers 256 * kUnits units of one row. The gathered form reads the source row index
@@ -20,7 +20,19 @@ namespace qaff {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnits = 4;  // units per lane: all loads of the four are issued before any store
+#ifndef QAFF_DQ_UNITS
+#define QAFF_DQ_UNITS 4
+#endif
+constexpr int kUnits = QAFF_DQ_UNITS;  // units per lane: all their loads are issued before any store
+
+// Codes per unit: 4 (16 bytes of float32), or 8 for bf16 outputs of codes up to 4 bits (16 bytes
+// of bf16, still one funnel shift of two words).
+template <int BITS, bool OUT_BF16>
+#ifdef QAFF_DQ_NARROW
+constexpr int kUnitCodes = 4;
+#else
+constexpr int kUnitCodes = (OUT_BF16 && BITS <= 4) ? 8 : 4;
+#endif
 
 // The pointers are deliberately not __restrict__: with it, the compiler moves each unit's loads
 // down to its store, one unit at a time, past the empty asm that keeps them together.
@@ -28,8 +40,10 @@ template <int BITS, bool OUT_BF16, bool GATHER>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(
     const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
     const uint32_t* indices, uint32_t table_rows, uint32_t kb, uint32_t gshift, void* out) {
+    constexpr int UC = kUnitCodes<BITS, OUT_BF16>;
+    constexpr int LUC = UC == 8 ? 3 : 2;
     const uint32_t r = blockIdx.y;
-    const uint32_t upr = kb * 8;       // 4-code units per row
+    const uint32_t upr = kb * (32 / UC);  // units per row
     const uint32_t wpr = kb * BITS;    // packed words per row
     const uint32_t gpr = kb >> gshift;  // groups per row
     uint32_t src = r;
@@ -49,12 +63,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
 #pragma unroll
     for (int i = 0; i < kUnits; ++i) {
         const uint32_t p = min(u0 + i * kThreads, upr - 1);  // clamped: loads stay in the row
-        const uint32_t bit = p * 4 * BITS;
+        const uint32_t bit = p * UC * BITS;
         const uint32_t wi = bit >> 5;
         sh[i] = bit & 31;
         w0[i] = prow[wi];
         w1[i] = prow[min(wi + 1, wpr - 1)];  // only read when the unit straddles two words
-        const uint32_t g = p >> (3 + gshift);
+        const uint32_t g = p >> (5 + gshift - LUC);
         sv[i] = srow[g];
         bv[i] = brow[g];
     }
@@ -65,16 +79,19 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
         const uint32_t v = __builtin_amdgcn_alignbit(w1[i], w0[i], sh[i]);
         const float s = bf16_to_f32(sv[i]);
         const float b = bf16_to_f32(bv[i]);
-        float o[4];
+        float o[UC];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < UC; ++c) {
             // s * code is exact in float32, so the fused form rounds once, like s * c then + b
             o[c] = ok ? __builtin_fmaf(s, (float)((v >> (c * BITS)) & ((1u << BITS) - 1u)), b)
                       : __uint_as_float(0x7fc00000u);
         }
-        const size_t e = (size_t)r * upr * 4 + (size_t)p * 4;
+        const size_t e = (size_t)r * upr * UC + (size_t)p * UC;
         if (p < upr) {
-            if constexpr (OUT_BF16) {
+            if constexpr (OUT_BF16 && UC == 8) {
+                *reinterpret_cast<u32x4a*>(static_cast<uint16_t*>(out) + e) =
+                    u32x4a{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+            } else if constexpr (OUT_BF16) {
                 *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
             } else {
                 *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = f32x4{o[0], o[1], o[2], o[3]};
@@ -87,7 +104,7 @@ template <int BITS, bool OUT_BF16, bool GATHER>
 hipError_t launch_one(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                       const uint32_t* indices, int64_t table_rows, int64_t out_rows, int64_t kb,
                       uint32_t gshift, void* out, hipStream_t stream) {
-    const int64_t upr = kb * 8;
+    const int64_t upr = kb * (32 / kUnitCodes<BITS, OUT_BF16>);
     const unsigned gx = (unsigned)((upr + kThreads * kUnits - 1) / (kThreads * kUnits));
     const size_t osize = OUT_BF16 ? 2 : 4;
     // grid.y is limited to 65535 rows per launch
