@@ -73,10 +73,13 @@ def _load():
                                      _f32p, _int]
     lib.orc_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
                             _int, _f64p, _int]
+    lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
+    lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
+                                      _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
-                 "orc_qmm"):
+                 "orc_qmm", "orc_silu_gate_qmm"):
         getattr(lib, name).restype = _int
-    for name in ("orc_bf16_to_f32", "orc_f32_to_bf16"):
+    for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -186,6 +189,46 @@ def qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: int,
     out = np.empty((m, n), np.float64)
     _check(_load().orc_qmm(xa.ctypes.data, 1 if x_dtype == "bf16" else 0, m, packed, scales, biases,
                            n, k, group_size, bits, out, threads or default_threads()), "qmm")
+    return out
+
+
+def silu_gate(gate, up) -> np.ndarray:
+    """h = silu(gate) * up in float64 (spark_runtime ``gemv_silu_gate``'s activation); gate and up
+    are bf16 bit patterns of one shape."""
+    gate = _c(gate, np.uint16)
+    up = _c(up, np.uint16)
+    if gate.shape != up.shape:
+        raise ValueError("gate and up differ in shape")
+    out = np.empty(gate.shape, np.float64)
+    _load().orc_silu_gate(gate, up, gate.size, out)
+    return out
+
+
+def silu_gate_qmm(gate, up, resid, packed, scales, biases, group_size: int, bits: int,
+                  threads: int | None = None) -> np.ndarray:
+    """y = (silu(gate) * up) . dequantize(W)^T (+ resid) in float64, shape [m, n]
+    (spark_runtime ``gemv_silu_gate`` / ``gemv_silu_gate_resid``). gate, up [m, k] and resid
+    [m, n] (or None) are bf16 bit patterns."""
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    biases = _c(biases, np.uint16)
+    gate = _c(np.atleast_2d(gate), np.uint16)
+    up = _c(np.atleast_2d(up), np.uint16)
+    if gate.shape != up.shape:
+        raise ValueError("gate and up differ in shape")
+    m, k = gate.shape
+    n = packed.shape[0]
+    if packed.shape[1] * 32 != k * bits:
+        raise ValueError("gate columns do not match the packed width")
+    r = None
+    if resid is not None:
+        r = _c(np.atleast_2d(resid), np.uint16)
+        if r.shape != (m, n):
+            raise ValueError("resid must be [m, n]")
+    out = np.empty((m, n), np.float64)
+    _check(_load().orc_silu_gate_qmm(gate, up, r.ctypes.data if r is not None else None, m, packed, scales,
+                                     biases, n, k, group_size, bits, out, threads or default_threads()),
+           "silu_gate_qmm")
     return out
 
 

@@ -26,7 +26,9 @@
  *   [maya2]  maya2_mlx, quant.py: `mm` (x @ W.T for a quantized weight) and `rows` (an embedding
  *            lookup that dequantizes only the gathered rows).
  *   [spark]  spark_runtime, weights/mlx_int8.rs: module documentation (8-bit words hold four bytes,
- *            low byte = column 0; the affine formula per group of G columns).
+ *            low byte = column 0; the affine formula per group of G columns); the fused decode
+ *            products `gemv_gate_up` (two projections of one x), `gemv_silu_gate`
+ *            (y = W . (silu(gate) * up)) and `gemv_silu_gate_resid` (the same plus a residual).
  */
 #include <math.h>
 #include <pthread.h>
@@ -275,5 +277,36 @@ int orc_qmm(const void* x, int x_is_bf16, int64_t m, const uint32_t* packed, con
     qmm_ctx c = {xd, m, packed, scales, biases, n, k, group, bits, out};
     run_ranges(qmm_range, &c, n, threads);
     free(xd);
+    return 0;
+}
+
+/* ---- fused decode products --------------------------------------------------------------- */
+
+/* silu(v) = v * sigmoid(v) = v / (1 + exp(-v)), in double. */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* [spark] the activation of gemv_silu_gate: h = silu(gate) * up, element by element, with gate and
+ * up bf16 bit patterns widened exactly; h in double. */
+void orc_silu_gate(const uint16_t* gate, const uint16_t* up, int64_t count, double* out) {
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = silu((double)bf16_to_f32(gate[i])) * (double)bf16_to_f32(up[i]);
+}
+
+/* [spark] gemv_silu_gate (resid null) and gemv_silu_gate_resid:
+ *   y[m, n] = sum over k of h[m, k] * w[n, k]  (+ resid[m, n]),  h = silu(gate) * up,
+ * gate and up [m, k] and resid [m, n] bf16 bit patterns; everything after the widening in double,
+ * the sum over k in order. Returns 0, or -1 for parameters outside the format. */
+int orc_silu_gate_qmm(const uint16_t* gate, const uint16_t* up, const uint16_t* resid, int64_t m,
+                      const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                      int64_t n, int64_t k, int64_t group, int bits, double* out, int threads) {
+    if (m < 0 || n < 0 || !valid_params(k, group, bits)) return -1;
+    double* h = (double*)malloc(sizeof(double) * (size_t)(m * k > 0 ? m * k : 1));
+    if (!h) return -2;
+    orc_silu_gate(gate, up, m * k, h);
+    qmm_ctx c = {h, m, packed, scales, biases, n, k, group, bits, out};
+    run_ranges(qmm_range, &c, n, threads);
+    if (resid)
+        for (int64_t i = 0; i < m * n; ++i) out[i] += (double)bf16_to_f32(resid[i]);
+    free(h);
     return 0;
 }

@@ -350,3 +350,68 @@ def test_generator_is_seeded_and_uniform():
     p1 = W.make_inputs(wl2, m=1, n=64)
     p4 = W.make_inputs(wl2, m=4, n=64)
     np.testing.assert_array_equal(p1.packed, p4.packed)
+
+
+# ---- fused decode products (spark_runtime gemv_silu_gate, gemv_silu_gate_resid) ----------------
+
+def _bf16v(vals):
+    return np.concatenate([_bf16(v) for v in vals])
+
+
+def test_silu_known_values(oracle_lib):
+    # logistic(1) = 0.7310585786300049 and logistic(2) = 0.8807970779778823 (tabulated values),
+    # so silu(1), silu(-1) = -(1 - logistic(1)), silu(2) and silu(-2) follow
+    h = oracle_lib.silu_gate(_bf16v([0.0, 1.0, -1.0, 2.0, -2.0]), _bf16v([1.0] * 5))
+    expect = [0.0, 0.7310585786300049, -0.2689414213699951, 2 * 0.8807970779778823,
+              -2 * (1 - 0.8807970779778823)]
+    np.testing.assert_allclose(h, expect, rtol=1e-15, atol=1e-16)
+
+
+def test_silu_odd_part_and_saturation(oracle_lib):
+    # silu(v) - silu(-v) = v for every v (sigmoid(v) + sigmoid(-v) = 1); a sign slip or a dropped
+    # factor breaks it. Far out, silu saturates to v and to 0.
+    rng = np.random.default_rng(3)
+    v = W.bf16_bits_from_f32(rng.uniform(-12, 12, 500).astype(np.float32))
+    neg = v ^ np.uint16(0x8000)
+    one = _bf16v([1.0] * v.size)
+    hv = oracle_lib.silu_gate(v, one)
+    hn = oracle_lib.silu_gate(neg, one)
+    np.testing.assert_allclose(hv - hn, W.f32_from_bf16_bits(v).astype(np.float64), rtol=0, atol=1e-14)
+    far = oracle_lib.silu_gate(_bf16v([64.0, -64.0]), _bf16v([1.0, 1.0]))
+    assert far[0] == 64.0 and -1e-25 < far[1] < 0
+
+
+def test_silu_gate_qmm_reduces_to_qmm(oracle_lib):
+    # gate = 64 makes silu(gate) = 64 exactly in double, so with up = x / 64 (exact in bf16) the
+    # fused product is the plain matmul of x
+    inp = W.random_inputs(4, 64, 9, 256, 3, seed=11)
+    x = W.f32_from_bf16_bits(inp.x)
+    up = W.bf16_bits_from_f32(x / 64)
+    assert np.array_equal(W.f32_from_bf16_bits(up) * 64, x)
+    gate = np.full_like(inp.x, _bf16(64.0)[0])
+    y = oracle_lib.silu_gate_qmm(gate, up, None, inp.packed, inp.scales, inp.biases, 64, 4)
+    ref = oracle_lib.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases, 64, 4)
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_silu_gate_residual_and_linearity(oracle_lib):
+    inp = W.random_inputs(3, 32, 7, 128, 2, seed=12)
+    rng = np.random.default_rng(5)
+    gate = W.bf16_bits_from_f32(rng.standard_normal((2, 128)).astype(np.float32))
+    up = W.bf16_bits_from_f32(rng.standard_normal((2, 128)).astype(np.float32))
+    resid = W.bf16_bits_from_f32(rng.standard_normal((2, 7)).astype(np.float32))
+    # a zero weight (scales and biases 0) leaves exactly the residual
+    zs = np.zeros_like(inp.scales)
+    y0 = oracle_lib.silu_gate_qmm(gate, up, resid, inp.packed, zs, zs, 32, 3)
+    np.testing.assert_array_equal(y0, W.f32_from_bf16_bits(resid).astype(np.float64))
+    # the residual is added, not subtracted or scaled
+    y = oracle_lib.silu_gate_qmm(gate, up, None, inp.packed, inp.scales, inp.biases, 32, 3)
+    yr = oracle_lib.silu_gate_qmm(gate, up, resid, inp.packed, inp.scales, inp.biases, 32, 3)
+    np.testing.assert_allclose(yr - y, W.f32_from_bf16_bits(resid), rtol=0, atol=1e-12)
+    # doubling up (exact in bf16) doubles y: up enters as a factor, gate through silu
+    up2 = W.bf16_bits_from_f32(W.f32_from_bf16_bits(up) * 2)
+    y2 = oracle_lib.silu_gate_qmm(gate, up2, None, inp.packed, inp.scales, inp.biases, 32, 3)
+    np.testing.assert_allclose(y2, 2 * y, rtol=1e-14, atol=1e-14)
+    # up = 0 gives 0 whatever the gate
+    yz = oracle_lib.silu_gate_qmm(gate, np.zeros_like(up), None, inp.packed, inp.scales, inp.biases, 32, 3)
+    assert not yz.any()
