@@ -94,6 +94,36 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
                         void* y, hipStream_t stream, qaff_path path);
 
 /*
+ * Dual decode product (spark_runtime weights/mlx_int8.rs gemv_gate_up): gate_y = x . dequantize(G)^T
+ * and up_y = x . dequantize(U)^T in one launch, x read once. Both weights share n, k, group_size
+ * and bits. x bf16 [m, k] with 1 <= m <= 16; gate_y, up_y bf16 [m, n]; sums in float32, each output
+ * rounded to nearest even. k == 0 writes zeros.
+ * Errors: as qaff_qmm for each weight; UNSUPPORTED for m > 16; INVALID_ARGUMENT for a null or
+ * misaligned (16-byte) x or output.
+ */
+qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_packed,
+                              const uint16_t* gate_scales, const uint16_t* gate_biases,
+                              const uint32_t* up_packed, const uint16_t* up_scales,
+                              const uint16_t* up_biases, int64_t n, int64_t k, int32_t group_size,
+                              int32_t bits, void* gate_y, void* up_y, hipStream_t stream);
+
+/*
+ * Fused activation and decode product (spark_runtime weights/mlx_int8.rs gemv_silu_gate and
+ * gemv_silu_gate_resid): y = h . dequantize(W)^T (+ resid), where h = silu(gate) * up,
+ * silu(v) = v / (1 + exp(-v)). h is formed in float32 and rounded to bf16 (the element type of
+ * gate and up, as the staging buffer that the fusion removes would hold it); the sum is float32;
+ * a residual is added in float32 before y is rounded to nearest even.
+ *   gate, up bf16 [m, k] with 1 <= m <= 16; resid bf16 [m, n] or NULL; y bf16 [m, n].
+ * k == 0 writes resid (or zeros).
+ * Errors: as qaff_qmm for the weight; UNSUPPORTED for m > 16; INVALID_ARGUMENT for a null or
+ * misaligned (16-byte) gate, up or y, or a resid that is not 2-byte aligned.
+ */
+qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, const uint32_t* packed,
+                                const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                int32_t group_size, int32_t bits, const void* resid, void* y,
+                                hipStream_t stream);
+
+/*
  * Gathered-row dequantization: out[i, :] = dequantize(table)[indices[i], :] (maya2_mlx rows: an
  * embedding lookup that dequantizes only the gathered rows). Indices are uint32 (nuvec_core
  * gather_indices casts integer indices to U32); duplicates are allowed. An index >= table_rows

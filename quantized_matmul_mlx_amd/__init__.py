@@ -12,6 +12,8 @@ bit views are accepted too). A weight is ``scale * code + bias`` of its group.
     y = qmm(x, packed, scales, biases, group_size, bits)   # x . dequantize(W)^T, W never dense
     w = dequantize(packed, scales, biases, group_size, bits, out_dtype=torch.bfloat16)
     e = dequant_rows(packed, scales, biases, idx, group_size, bits)   # embedding lookup
+    g, u = gemv_gate_up(x, gate_w, up_w, group_size, bits)           # two projections, x read once
+    y = gemv_silu_gate(g, u, packed, scales, biases, group_size, bits, resid=r)  # W . (silu(g) * u) + r
 """
 from __future__ import annotations
 
@@ -23,7 +25,8 @@ import torch
 from . import _lib
 from ._lib import QaffError
 
-__all__ = ["dequantize", "qmm", "dequant_rows", "QWeight", "QaffError", "gemv_max_m"]
+__all__ = ["dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "QWeight", "QaffError",
+           "gemv_max_m", "gemv_mfma_min_m"]
 
 _PACKED_DTYPES = (torch.int32, torch.uint32)
 _BF16_BITS_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
@@ -176,3 +179,54 @@ class QWeight:
 
     def rows(self, idx, dtype=torch.float32):
         return dequant_rows(self.q, self.scales, self.biases, idx, self.group_size, self.bits, dtype)
+
+
+def _rows_2d(t, name, k, dev):
+    """A bf16 [..., k] decode input as [m, k] (a 1-D input is one row) and its leading shape."""
+    _need(t, name, (torch.bfloat16,), dev)
+    if t.shape[-1] != k:
+        raise ValueError(f"{name} has {t.shape[-1]} columns, the weight {k}")
+    lead = tuple(t.shape[:-1])
+    return t.reshape(math.prod(lead), k), lead
+
+
+def gemv_gate_up(x, gate_w, up_w, group_size: int, bits: int):
+    """Both projections of one bf16 x in one launch (spark_runtime ``gemv_gate_up``): returns
+    ``(x . dequantize(gate)^T, x . dequantize(up)^T)``. ``gate_w`` and ``up_w`` are
+    ``(packed, scales, biases)`` of the same shape; at most 16 rows of x."""
+    lib = _lib.load()
+    dev, n, k = _weights(*gate_w, group_size, bits)
+    dev2, n2, k2 = _weights(*up_w, group_size, bits)
+    if (dev2, n2, k2) != (dev, n, k):
+        raise ValueError("gate and up weights differ in device or shape")
+    x2, lead = _rows_2d(x, "x", k, dev)
+    gy = torch.empty(lead + (n,), dtype=torch.bfloat16, device=dev)
+    uy = torch.empty(lead + (n,), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_gemv_gate_up(_p(x2), x2.shape[0], _p(gate_w[0]), _p(gate_w[1]), _p(gate_w[2]),
+                                         _p(up_w[0]), _p(up_w[1]), _p(up_w[2]), n, k, group_size, bits,
+                                         _p(gy), _p(uy), _stream(dev)))
+    return gy, uy
+
+
+def gemv_silu_gate(gate, up, packed, scales, biases, group_size: int, bits: int, resid=None):
+    """``(silu(gate) * up) . dequantize(W)^T (+ resid)`` in one launch (spark_runtime
+    ``gemv_silu_gate`` / ``gemv_silu_gate_resid``); gate and up bf16 ``[..., k]`` (at most 16
+    rows), resid bf16 ``[..., n]`` or None; the result is bf16 ``[..., n]``."""
+    lib = _lib.load()
+    dev, n, k = _weights(packed, scales, biases, group_size, bits)
+    g2, lead = _rows_2d(gate, "gate", k, dev)
+    u2, lead_u = _rows_2d(up, "up", k, dev)
+    if lead_u != lead:
+        raise ValueError("gate and up differ in shape")
+    r2 = None
+    if resid is not None:
+        _need(resid, "resid", (torch.bfloat16,), dev)
+        if tuple(resid.shape) != lead + (n,):
+            raise ValueError(f"resid must be {list(lead + (n,))}")
+        r2 = resid
+    y = torch.empty(lead + (n,), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_gemv_silu_gate(_p(g2), _p(u2), g2.shape[0], _p(packed), _p(scales), _p(biases),
+                                           n, k, group_size, bits, _p(r2), _p(y), _stream(dev)))
+    return y

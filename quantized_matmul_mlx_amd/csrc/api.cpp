@@ -192,6 +192,71 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint
     return after_launch(op, e, stream);
 }
 
+qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_packed,
+                              const uint16_t* gate_scales, const uint16_t* gate_biases,
+                              const uint32_t* up_packed, const uint16_t* up_scales,
+                              const uint16_t* up_biases, int64_t n, int64_t k, int32_t group_size,
+                              int32_t bits, void* gate_y, void* up_y, hipStream_t stream) {
+    static const char* op = "qaff_gemv_gate_up";
+    g_error.clear();
+    qaff_status st = check_weight(op, gate_packed, gate_scales, gate_biases, n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    st = check_weight(op, up_packed, up_scales, up_biases, n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
+    if (m > kGemvMaxM) return fail(QAFF_ERR_UNSUPPORTED, "%s: a decode product: m <= %d", op, kGemvMaxM);
+    if (m == 0 || n == 0) return QAFF_OK;
+    if (!gate_y || !up_y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
+    if (!aligned(gate_y, 16) || !aligned(up_y, 16))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: outputs must be 16-byte aligned", op);
+    if (k == 0) {
+        hipError_t e = qaff::launch_fill_zero(gate_y, m * n * 2, stream);
+        if (e == hipSuccess) e = qaff::launch_fill_zero(up_y, m * n * 2, stream);
+        return after_launch(op, e, stream);
+    }
+    if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (n > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: n above 2^31-1", op);
+    qaff::GemvFused f{};
+    f.packed2 = up_packed;
+    f.scales2 = up_scales;
+    f.biases2 = up_biases;
+    f.y2 = static_cast<uint16_t*>(up_y);
+    return after_launch(op, qaff::launch_gemv_fused(static_cast<const uint16_t*>(x), m, gate_packed, gate_scales,
+                                                    gate_biases, n, k, group_size, bits,
+                                                    static_cast<uint16_t*>(gate_y), f, stream), stream);
+}
+
+qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, const uint32_t* packed,
+                                const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                int32_t group_size, int32_t bits, const void* resid, void* y,
+                                hipStream_t stream) {
+    static const char* op = "qaff_gemv_silu_gate";
+    g_error.clear();
+    qaff_status st = check_weight(op, packed, scales, biases, n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
+    if (m > kGemvMaxM) return fail(QAFF_ERR_UNSUPPORTED, "%s: a decode product: m <= %d", op, kGemvMaxM);
+    if (m == 0 || n == 0) return QAFF_OK;
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    if (resid && !aligned(resid, 2)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: resid must be 2-byte aligned", op);
+    if (k == 0) {  // y = bf16(0 + resid) = resid, or zeros
+        if (resid) return after_launch(op, hipMemcpyAsync(y, resid, (size_t)(m * n * 2), hipMemcpyDeviceToDevice, stream), stream);
+        return after_launch(op, qaff::launch_fill_zero(y, m * n * 2, stream), stream);
+    }
+    if (!gate || !up) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null gate or up", op);
+    if (!aligned(gate, 16) || !aligned(up, 16))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: gate and up must be 16-byte aligned", op);
+    if (n > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: n above 2^31-1", op);
+    qaff::GemvFused f{};
+    f.up = static_cast<const uint16_t*>(up);
+    f.resid = static_cast<const uint16_t*>(resid);
+    return after_launch(op, qaff::launch_gemv_fused(static_cast<const uint16_t*>(gate), m, packed, scales, biases,
+                                                    n, k, group_size, bits, static_cast<uint16_t*>(y), f, stream),
+                        stream);
+}
+
 qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
                      const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                      int32_t group_size, int32_t bits, void* y, hipStream_t stream) {

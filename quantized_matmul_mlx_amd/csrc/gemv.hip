@@ -157,11 +157,16 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-template <int BITS, int MB, int RPW, int WAVES, int P>
+// silu(v) = v / (1 + exp(-v)) in float32.
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+
+// FUSED adds the decode fusions of `GemvFused` (uniform flags read at run time): the x transform,
+// the residual, and a second weight whose rows follow the first's (rows n .. 2n - 1).
+template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED>
 __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint16_t* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
-    uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y) {
+    uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y, GemvFused fz) {
     constexpr int kBlockThreads = WAVES * 64;
     constexpr int kPassBlocks = 64 * P;  // 32-code blocks per row per pass
     // x of the pass as bf16 pairs in unpack order: [x row][quarter of a block][block] of 16 bytes,
@@ -175,6 +180,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint32_t row0 = (blockIdx.x * WAVES + wave) * RPW;
     const uint32_t m0 = blockIdx.y * MB;
     const uint32_t gpr = kb >> gshift;
+    // rows of the launch: n, or 2n with a second weight (its rows after the first's)
+    const uint32_t nrows = (FUSED && fz.packed2) ? 2 * n : n;
+    const bool silu = FUSED && fz.up != nullptr;
+    const uint16_t* __restrict__ upx = silu ? fz.up : x;  // read either way: no branch around loads
 
     float acc[RPW][MB];
 #pragma unroll
@@ -189,6 +198,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
         constexpr int kUnitsTotal = MB * 2 * kPassBlocks;
         constexpr int kUnits = (kUnitsTotal + kBlockThreads - 1) / kBlockThreads;
         u32x4a xg[kUnits][2];
+        u32x4a ug[FUSED ? kUnits : 1][2];
         bool xvalid[kUnits];
 #pragma unroll
         for (int t = 0; t < kUnits; ++t) {
@@ -203,9 +213,15 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             xvalid[t] = m0 + mi < m && j < kb;
             const uint32_t xr = min(m0 + mi, m - 1);
             const uint32_t jc = min(j, kb - 1);
-            const u32x4a* src = reinterpret_cast<const u32x4a*>(x + (size_t)xr * kb * 32 + (size_t)jc * 32 + h * 16);
+            const size_t xo = (size_t)xr * kb * 32 + (size_t)jc * 32 + h * 16;
+            const u32x4a* src = reinterpret_cast<const u32x4a*>(x + xo);
             xg[t][0] = src[0];
             xg[t][1] = src[1];
+            if constexpr (FUSED) {
+                const u32x4a* usrc = reinterpret_cast<const u32x4a*>(upx + xo);
+                ug[t][0] = usrc[0];
+                ug[t][1] = usrc[1];
+            }
         }
 
         // 2. Issue every weight load of the pass. Rows are wave-uniform, so each row's base
@@ -218,10 +234,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
         uint32_t sraw[RPW][P], braw[RPW][P];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            const uint32_t row = min(row0 + r, n - 1);
-            const uint32_t* prow = packed + (size_t)row * kb * BITS;
-            const uint16_t* srow = scales + (size_t)row * gpr;
-            const uint16_t* brow = biases + (size_t)row * gpr;
+            uint32_t row = min(row0 + r, nrows - 1);
+            const uint32_t* pk = packed;
+            const uint16_t* sc = scales;
+            const uint16_t* bi = biases;
+            if (FUSED && row >= n) {  // wave-uniform: the second weight
+                row -= n;
+                pk = fz.packed2;
+                sc = fz.scales2;
+                bi = fz.biases2;
+            }
+            const uint32_t* prow = pk + (size_t)row * kb * BITS;
+            const uint16_t* srow = sc + (size_t)row * gpr;
+            const uint16_t* brow = bi + (size_t)row * gpr;
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const uint32_t j = min(pass0 + p * 64 + lane, kb - 1);
@@ -249,6 +274,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             for (int q = 0; q < 16; ++q) xn[q] = 0u;
             uint32_t v[8] = {xg[t][0].x, xg[t][0].y, xg[t][0].z, xg[t][0].w,
                              xg[t][1].x, xg[t][1].y, xg[t][1].z, xg[t][1].w};
+            if constexpr (FUSED) {
+                if (silu) {
+                    // h = silu(gate) * up in float32, rounded to bf16: the GEMV's input
+                    const uint32_t uv[8] = {ug[t][0].x, ug[t][0].y, ug[t][0].z, ug[t][0].w,
+                                            ug[t][1].x, ug[t][1].y, ug[t][1].z, ug[t][1].w};
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float g0 = __uint_as_float(v[q] << 16), g1 = __uint_as_float(v[q] & 0xffff0000u);
+                        const float u0 = __uint_as_float(uv[q] << 16), u1 = __uint_as_float(uv[q] & 0xffff0000u);
+                        v[q] = pack_bf16x2(silu_f32(g0) * u0, silu_f32(g1) * u1);
+                    }
+                }
+            }
             if (!xvalid[t]) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) v[q] = 0u;
@@ -301,7 +339,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
                     float d = 0.f;
 #pragma unroll
                     for (int t = 0; t < 16; ++t) d = dot2(pr[t], xp[i][t], d);
-                    acc[r][i] += sc * d + boff * xs[i];
+                    // written as two fused multiply-adds so that every instantiation rounds
+                    // the same way (left to the compiler, the contraction varies with the code)
+                    acc[r][i] = __builtin_fmaf(sc, d, __builtin_fmaf(boff, xs[i], acc[r][i]));
                 }
             }
         }
@@ -309,11 +349,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
 
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-        const uint32_t row = row0 + r;
+        uint32_t row = row0 + r;
+        uint16_t* yo = y;
+        if (FUSED && row >= n) {
+            row -= n;
+            yo = fz.y2;
+        }
+        const bool in_range = row0 + r < nrows;
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const float v = wave_sum_dpp(acc[r][i]);
-            if (lane == 0 && row < n && m0 + i < m) y[(size_t)(m0 + i) * n + row] = to_bf16_bits(v);
+            float v = wave_sum_dpp(acc[r][i]);
+            if (lane == 0 && in_range && m0 + i < m) {
+                const size_t o = (size_t)(m0 + i) * n + row;
+                if (FUSED && fz.resid) v += bf16_to_f32(fz.resid[o]);
+                yo[o] = to_bf16_bits(v);
+            }
         }
     }
 }
@@ -428,31 +478,38 @@ hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
 #define QAFF_GEMV_WAVES_N 4
 #endif
 
-template <int BITS, int MB, int RPW, int WAVES>
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED>
 hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
-                       hipStream_t stream) {
+                       const GemvFused& fz, hipStream_t stream) {
     constexpr int P = 2;
     const int64_t rows_per_block = (int64_t)WAVES * RPW;
-    const unsigned gx = (unsigned)((n + rows_per_block - 1) / rows_per_block);
+    const int64_t nrows = (FUSED && fz.packed2) ? 2 * n : n;
+    const unsigned gx = (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
     return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
-        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
+        GemvFused f = fz;
+        if (FUSED) {
+            if (f.up) f.up += (size_t)m_off * kb * 32;
+            if (f.resid) f.resid += (size_t)m_off * n;
+            if (f.y2) f.y2 += (size_t)m_off * n;
+        }
+        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
             x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
-            (uint32_t)kb, gshift, y + (size_t)m_off * n);
+            (uint32_t)kb, gshift, y + (size_t)m_off * n, f);
     });
 }
 
-template <int BITS>
+template <int BITS, bool FUSED>
 hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
-                         hipStream_t stream) {
+                         const GemvFused& f, hipStream_t stream) {
     if (m == 1)
-        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 2)
-        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m <= 4)
-        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
-    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
+        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
 }
 
 template <int BITS, int MB>
@@ -485,8 +542,8 @@ hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* pac
     if (x_f32)
         return launch_f32_m<BITS>(static_cast<const float*>(x), m, packed, scales, biases, n, kb, gshift,
                                   static_cast<float*>(y), stream);
-    return launch_bf16_m<BITS>(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, kb, gshift,
-                               static_cast<uint16_t*>(y), stream);
+    return launch_bf16_m<BITS, false>(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, kb, gshift,
+                                      static_cast<uint16_t*>(y), GemvFused{}, stream);
 }
 
 }  // namespace
@@ -503,6 +560,22 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
         case 5: return launch_bits<5>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 6: return launch_bits<6>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 8: return launch_bits<8>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_fused(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                             const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
+                             uint16_t* y, const GemvFused& f, hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 2: return launch_bf16_m<2, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 3: return launch_bf16_m<3, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 4: return launch_bf16_m<4, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 5: return launch_bf16_m<5, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 6: return launch_bf16_m<6, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 8: return launch_bf16_m<8, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -19,6 +19,20 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                        int group_size, int bits, void* y, hipStream_t stream);
 
+// Fused decode products on the bf16 GEMV (spark_runtime gemv_gate_up, gemv_silu_gate,
+// gemv_silu_gate_resid). Null members are unused.
+struct GemvFused {
+    const uint16_t* up;       // x is the gate; the product's input is bf16(silu(x) * up)
+    const uint16_t* resid;    // y = bf16(sum + resid[m, n])
+    const uint32_t* packed2;  // a second weight of the same shape (n, k, group, bits) ...
+    const uint16_t* scales2;
+    const uint16_t* biases2;
+    uint16_t* y2;             // ... whose product with the same x goes to y2
+};
+hipError_t launch_gemv_fused(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                             const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
+                             uint16_t* y, const GemvFused& f, hipStream_t stream);
+
 // The decode product on the matrix cores: y[m, n] (bf16) = x (bf16) . dequantize(W)^T for
 // 1 <= m <= 16, with each code dequantized to bf16 in registers. Only for shapes where
 // gemv_mfma_supported(m, k) holds, and scales/biases 4-byte aligned.

@@ -158,3 +158,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def gate_up(lib, m=1, n=4, k=64, G=32, bits=4, x=A16, gy=A16, uy=A16, gp=A16, up=A16):
+    return lib.qaff_gemv_gate_up(x, m, gp, A16, A16, up, A16, A16, n, k, G, bits, gy, uy, NULL)
+
+
+def silu(lib, m=1, n=4, k=64, G=32, bits=4, gate=A16, upv=A16, resid=NULL, y=A16):
+    return lib.qaff_gemv_silu_gate(gate, upv, m, A16, A16, A16, n, k, G, bits, resid, y, NULL)
+
+
+def test_fused_decode_checks(lib):
+    assert gate_up(lib, m=17) == UNSUPPORTED                 # decode products: m <= 16
+    assert b"m <= 16" in lib.qaff_last_error()
+    assert silu(lib, m=17) == UNSUPPORTED
+    assert gate_up(lib, bits=7) == UNSUPPORTED
+    assert silu(lib, G=48) == INVALID
+    assert gate_up(lib, up=NULL) == INVALID                  # the second weight is checked too
+    assert gate_up(lib, uy=NULL) == INVALID
+    assert gate_up(lib, x=A2) == INVALID
+    assert silu(lib, gate=A2) == INVALID
+    assert silu(lib, y=NULL) == INVALID
+    assert silu(lib, resid=A1) == INVALID                    # a residual must be 2-byte aligned
+    assert gate_up(lib, m=-1) == INVALID
+    # nothing to write
+    assert gate_up(lib, m=0, x=NULL, gy=NULL, uy=NULL) == OK
+    assert silu(lib, n=0, gate=NULL, upv=NULL, y=NULL) == OK
