@@ -14,7 +14,9 @@ The same JSON line carries:
   * `prefill_gemm`: the 4-bit g128 prefill GEMM (x bf16 [2048, 14336], W [4096, 14336]) in TFLOP/s
     against the 2.5 PFLOP/s dense bf16 MFMA peak;
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
-    rows, the 8-bit and the 3-/6-bit GEMVs, the decode GEMV at M = 4), each against its roofline;
+    rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
+    product at M = 4, and the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
+    residual), each against its roofline;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
     (also given per row).
 
@@ -190,6 +192,69 @@ def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
                                "kind": "oracle",
                                "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
     return row, gbs, ms, inp
+
+
+def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
+    """The fused decode products at the FFN shapes (4-bit g64, M = 1): "gate_up" (both [14336, 4096]
+    projections of one x) or "silu_gate" (down [4096, 14336] on silu(gate) * up plus the residual)."""
+    import numpy as np
+    import oracle
+    if kind == "gate_up":
+        wa, wb = W.WORKLOADS["ffn_gate_4bit_g64_14336x4096"], W.WORKLOADS["ffn_up_4bit_g64_14336x4096"]
+        a, bb = W.make_inputs(wa, m=1), W.make_inputs(wb, m=1)
+        wbytes = 2 * (qmm_bytes(1, wa.n, wa.k, wa.bits, wa.group_size) - wa.k * 2 - wa.n * 2)
+        nbytes = wbytes + wa.k * 2 + 2 * wa.n * 2
+        copies = copies_for(nbytes)
+        sa = replicate(torch, to_device(torch, a), copies)
+        sb = replicate(torch, to_device(torch, bb), copies)
+
+        def launch(i):
+            x, y = sa[i % copies], sb[i % copies]
+            q.gemv_gate_up(x["x"], (x["packed"], x["scales"], x["biases"]),
+                           (y["packed"], y["scales"], y["biases"]), wa.group_size, wa.bits)
+
+        def cpu_step():
+            oracle.qmm(a.x, "bf16", a.packed, a.scales, a.biases, wa.group_size, wa.bits, threads=threads)
+            oracle.qmm(a.x, "bf16", bb.packed, bb.scales, bb.biases, wa.group_size, wa.bits, threads=threads)
+        label = "gemv_gate_up 2 x [14336, 4096] 4-bit g64 M=1"
+        sets = (sa, sb)
+    else:
+        wd = W.WORKLOADS["ffn_down_4bit_g64_4096x14336"]
+        d = W.make_inputs(wd, m=1)
+        rng = np.random.default_rng(34)
+        gate = W.bf16_bits_from_f32(rng.standard_normal((1, wd.k), dtype=np.float32))
+        up = W.bf16_bits_from_f32(rng.standard_normal((1, wd.k), dtype=np.float32))
+        resid = W.bf16_bits_from_f32(rng.standard_normal((1, wd.n), dtype=np.float32))
+        # weight + gate + up + residual + y
+        nbytes = (qmm_bytes(1, wd.n, wd.k, wd.bits, wd.group_size) - wd.k * 2 - wd.n * 2) + 2 * wd.k * 2 + 2 * wd.n * 2
+        copies = copies_for(nbytes)
+        sd = replicate(torch, to_device(torch, d), copies)
+        g_t = [torch.from_numpy(gate.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(copies)]
+        u_t = [torch.from_numpy(up.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(copies)]
+        r_t = torch.from_numpy(resid.view(np.int16)).cuda().view(torch.bfloat16)
+
+        def launch(i):
+            s = sd[i % copies]
+            q.gemv_silu_gate(g_t[i % copies], u_t[i % copies], s["packed"], s["scales"], s["biases"],
+                             wd.group_size, wd.bits, resid=r_t)
+
+        def cpu_step():
+            oracle.silu_gate_qmm(gate, up, resid, d.packed, d.scales, d.biases, wd.group_size, wd.bits,
+                                 threads=threads)
+        label = "gemv_silu_gate + residual [4096, 14336] 4-bit g64 M=1"
+        sets = (sd, g_t, u_t)
+    threads = oracle.default_threads()
+    ms = timer(launch, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    row = {"workload": label, "kernel": f"gemv_{kind} (fused)", "bytes_per_step": nbytes,
+           "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
+    if cpu:
+        runs, el = cpu_time(cpu_step, cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row
 
 
 def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_budget, gather):
@@ -385,6 +450,9 @@ def main():
             log(f"row: dequant_rows 4096 of [32768, 4096] -> {out_dtype}")
             rows.append(bench_dequant(torch, q, W, timer, "rows_4bit_g64_32768x4096", out_dtype, rs, rw,
                                       cpu, 2.0, gather=True))
+        for kind in ("gate_up", "silu_gate"):
+            log(f"row: fused {kind}")
+            rows.append(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
         result["rows"] = rows
 
     # ---- CPU oracle on the host cores (headline workload) ----

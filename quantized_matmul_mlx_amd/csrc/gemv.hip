@@ -157,8 +157,13 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// silu(v) = v / (1 + exp(-v)) in float32.
-__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + __expf(-v)); }
+// silu(v) = v / (1 + exp(-v)) in float32 from the hardware exp2 and reciprocal (each within a few
+// ulp): h is rounded to bf16 right after, which an error of that size moves only in rare ties.
+// Every block of the GEMV recomputes the activation for its x, so its cost counts.
+__device__ __forceinline__ float silu_f32(float v) {
+    const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);  // exp(-v)
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // FUSED adds the decode fusions of `GemvFused` (uniform flags read at run time): the x transform,
 // the residual, and a second weight whose rows follow the first's (rows n .. 2n - 1).
@@ -478,11 +483,16 @@ hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
 #define QAFF_GEMV_WAVES_N 4
 #endif
 
-template <int BITS, int MB, int RPW, int WAVES, bool FUSED>
-hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                       const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
-                       const GemvFused& fz, hipStream_t stream) {
-    constexpr int P = 2;
+// Blocks per lane and pass: 2 (128 blocks, 4096 codes: one pass at the decode shape). Each pass
+// waits for its own loads, so long rows at small MB take wider passes: 8 (MB = 1) or 4 (MB = 2)
+// blocks per lane, one pass up to 16384 (8192) codes, within the registers and LDS they need.
+template <int MB>
+constexpr int kLongPass = MB == 1 ? 8 : MB == 2 ? 4 : 2;
+
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int P>
+hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                         const GemvFused& fz, hipStream_t stream) {
     const int64_t rows_per_block = (int64_t)WAVES * RPW;
     const int64_t nrows = (FUSED && fz.packed2) ? 2 * n : n;
     const unsigned gx = (unsigned)((nrows + rows_per_block - 1) / rows_per_block);
@@ -499,10 +509,24 @@ hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, con
     });
 }
 
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED>
+hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                       const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                       const GemvFused& fz, hipStream_t stream) {
+    if (kLongPass<MB> > 2 && kb > 128)
+        return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>>(x, m, packed, scales, biases, n, kb,
+                                                                          gshift, y, fz, stream);
+    return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, 2>(x, m, packed, scales, biases, n, kb, gshift, y, fz, stream);
+}
+
 template <int BITS, bool FUSED>
 hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                          const GemvFused& f, hipStream_t stream) {
+    // The fused products recompute their x transform per block: 16 rows per block at M = 1 halve
+    // that work against the plain GEMV's 8.
+    if (m == 1 && FUSED)
+        return launch_bf16<BITS, 1, 2, 8, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 1)
         return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 2)

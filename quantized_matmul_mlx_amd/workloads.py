@@ -70,6 +70,14 @@ WORKLOADS = {
                                         (1e-3, 2e-2), (-0.15, 0.0), ms=(1, 16)),
     "odd_6bit_g32_11008x4096": Workload("odd_6bit_g32_11008x4096", 6, 32, 11008, 4096,
                                         (1e-3, 2e-2), (-0.15, 0.0), ms=(1, 16)),
+    # A decode FFN step at 4-bit g64 (the fused products): gate and up [14336, 4096] on one x row,
+    # then down [4096, 14336] on silu(gate) * up plus the residual.
+    "ffn_gate_4bit_g64_14336x4096": Workload("ffn_gate_4bit_g64_14336x4096", 4, 64, 14336, 4096,
+                                             (1e-3, 2e-2), (-0.15, 0.0), ms=(1,), seed=31),
+    "ffn_up_4bit_g64_14336x4096": Workload("ffn_up_4bit_g64_14336x4096", 4, 64, 14336, 4096,
+                                           (1e-3, 2e-2), (-0.15, 0.0), ms=(1,), seed=32),
+    "ffn_down_4bit_g64_4096x14336": Workload("ffn_down_4bit_g64_4096x14336", 4, 64, 4096, 14336,
+                                             (1e-3, 2e-2), (-0.15, 0.0), ms=(1,), seed=33),
     # Embedding table: 4-bit g64 [32768, 4096], 4096 uniform-random gathered rows.
     "rows_4bit_g64_32768x4096": Workload("rows_4bit_g64_32768x4096", 4, 64, 32768, 4096,
                                          (1e-3, 2e-2), (-0.15, 0.0), n_indices=4096),

@@ -160,6 +160,19 @@ def test_gemv(orc, bits, G, m, x_dtype):
     check_qmm(orc, inp, y, path="gemv")
 
 
+# Long rows at M <= 2 take wider passes (8 or 4 blocks per lane): 300 blocks (one ragged pass) and
+# 520 blocks (more than one pass at M = 1, ragged).
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("m,kb", [(1, 300), (2, 300), (1, 520)])
+def test_gemv_long_rows(orc, bits, G, m, kb):
+    k = kb * 32 // G * G
+    inp = W.random_inputs(bits, G, 70, k, m, seed=bits * 3 + G + m + kb)
+    banner(f"gemv long rows bits={bits} G={G} m={m} k={k}")
+    y = run_qmm(inp, path="gemv")
+    check_qmm(orc, inp, y, path="gemv")
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 128])
 @pytest.mark.parametrize("m,n", [(17, 129), (130, 200), (257, 64)])
