@@ -225,9 +225,23 @@ hipError_t launch_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const
 template <int BITS, int GSHIFT, int MB>
 hipError_t launch_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                     const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
-    // Tiles of 16 rows per block: two for large n, so that each x row serves more rows of W.
-    if (n > 6144) return launch_nt<BITS, 2, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
-    return launch_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+    // The kernel is latency-bound: all blocks should be resident at once. A block's LDS (its x
+    // slices: MB x 1040 bytes per wave) sets how many fit on a compute unit; each block takes as
+    // many 16-row tiles (1 to 4) as needed to cover n in one round of the compute units.
+    const int64_t waves = kb / 16;
+    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch);
+    if (per_cu < 1) per_cu = 1;
+    if (per_cu > 4) per_cu = 4;
+    const int64_t slots = (int64_t)device_cu_count() * per_cu;
+    int64_t nt = (n + 16 * slots - 1) / (16 * slots);
+    // 8-bit codes: more than two tiles of W (64 registers each) crowd out the waves that hide the
+    // latency (measured: 8-bit M = 16 on [14336, 4096] 20 us at two tiles, 25 us at three)
+    constexpr int kMaxNt = BITS == 8 ? 2 : 4;
+    if (nt > kMaxNt) nt = kMaxNt;
+    if (nt <= 1) return launch_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+    if (nt == 2) return launch_nt<BITS, 2, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+    if (nt == 3 || kMaxNt == 3) return launch_nt<BITS, 3, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
+    return launch_nt<BITS, kMaxNt, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
 }
 
 template <int BITS, int GSHIFT>

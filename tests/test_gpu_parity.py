@@ -223,10 +223,12 @@ def test_gemv_mfma(orc, bits, G, m, n, k):
     check_qmm(orc, inp, y, path="gemv_mfma")
 
 
-@pytest.mark.parametrize("n", [4100, 8200])
-def test_gemv_mfma_row_tiles(orc, n):
-    inp = W.random_inputs(4, 64, n, 512, 5, seed=n)
-    banner(f"gemv_mfma row tiles n={n}")
+# Tiles of 16 rows per block: with M = 16 and K = 4096 one block fills a compute unit's LDS, so on
+# 256 compute units n = 4100, 8200 and 12300 take 2, 3 and 4 tiles per block (8-bit codes at most 2).
+@pytest.mark.parametrize("bits,n", [(4, 4100), (4, 8200), (4, 12300), (3, 12300), (8, 12300)])
+def test_gemv_mfma_row_tiles(orc, bits, n):
+    inp = W.random_inputs(bits, 32, n, 4096, 16, seed=n + bits)
+    banner(f"gemv_mfma row tiles bits={bits} n={n}")
     y = run_qmm(inp, path="gemv_mfma")
     check_qmm(orc, inp, y, path="gemv_mfma")
 
