@@ -17,6 +17,10 @@ patterns. What each function computes, and the page passage it follows, is docum
 * ``dequant_rows`` -- the gathered-row lookup (maya2_mlx ``quant.py``, ``rows``).
 * ``qmm`` -- ``x . dequantize(W)^T`` summed in double precision (nuvec_core ``quantized_matmul``;
   maya2_mlx ``mm``).
+* ``gather_qmm`` -- output batch i is ``x[lhs[i]] . dequantize(W[rhs[i]])^T`` (nuvec_core
+  ``gather_qmm`` and ``gather_indices``).
+* ``silu_gate`` / ``silu_gate_qmm`` -- the fused decode products' activation and product
+  (spark_runtime ``gemv_silu_gate``).
 """
 from __future__ import annotations
 
@@ -73,11 +77,13 @@ def _load():
                                      _f32p, _int]
     lib.orc_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
                             _int, _f64p, _int]
+    lib.orc_gather_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
+                                   _i64, _int, ctypes.c_void_p, ctypes.c_void_p, _i64, _f64p, _int]
     lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
     lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
-                 "orc_qmm", "orc_silu_gate_qmm"):
+                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm"):
         getattr(lib, name).restype = _int
     for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate"):
         getattr(lib, name).restype = None
@@ -230,6 +236,56 @@ def silu_gate_qmm(gate, up, resid, packed, scales, biases, group_size: int, bits
                                      biases, n, k, group_size, bits, out, threads or default_threads()),
            "silu_gate_qmm")
     return out
+
+
+def gather_indices(x_batch_shape, w_batch_shape, lhs=None, rhs=None):
+    """nuvec_core ``gather_indices``: the two index arrays as uint32, each defaulting to every batch
+    of its operand in order (shaped like that operand's batch dimensions), broadcast together.
+    Returns (lhs, rhs) flattened, and the broadcast batch shape."""
+    def one(batch_shape, given):
+        if given is None:
+            count = int(np.prod(batch_shape, dtype=np.int64))
+            return np.arange(count, dtype=np.uint32).reshape(batch_shape)
+        given = np.asarray(given)
+        if given.dtype.kind not in "iu":
+            raise ValueError("indices must be integers")
+        return given.astype(np.uint32)
+    lhs_a, rhs_a = one(tuple(x_batch_shape), lhs), one(tuple(w_batch_shape), rhs)
+    shape = np.broadcast_shapes(lhs_a.shape, rhs_a.shape)
+    return (np.ascontiguousarray(np.broadcast_to(lhs_a, shape)).reshape(-1),
+            np.ascontiguousarray(np.broadcast_to(rhs_a, shape)).reshape(-1), shape)
+
+
+def gather_qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: int, lhs=None, rhs=None,
+               threads: int | None = None) -> np.ndarray:
+    """nuvec_core ``gather_qmm`` with the transpose: x is [..., m, k] (float32, or bf16 bit
+    patterns with ``x_dtype="bf16"``), packed [..., n, k*bits/32] and scales, biases [..., n, k/G];
+    output batch i is ``x[lhs[i]] . dequantize(W[rhs[i]])^T`` in float64, shape
+    broadcast(batch) + [m, n]. An index past its operand gives a NaN batch."""
+    if x_dtype == "bf16":
+        xa = _c(x, np.uint16)
+    elif x_dtype == "f32":
+        xa = _c(x, np.float32)
+    else:
+        raise ValueError(x_dtype)
+    packed = _c(packed, np.uint32)
+    scales = _c(scales, np.uint16)
+    biases = _c(biases, np.uint16)
+    if xa.ndim < 2 or packed.ndim < 2 or scales.shape != biases.shape:
+        raise ValueError("x must be [..., m, k] and w [..., n, k*bits/32]")
+    m, k = xa.shape[-2:]
+    n = packed.shape[-2]
+    if packed.shape[-1] * 32 != k * bits:
+        raise ValueError("x columns do not match the packed width")
+    li, ri, shape = gather_indices(xa.shape[:-2], packed.shape[:-2], lhs, rhs)
+    xb = int(np.prod(xa.shape[:-2], dtype=np.int64))
+    wb = int(np.prod(packed.shape[:-2], dtype=np.int64))
+    out = np.empty((li.size, m, n), np.float64)
+    _check(_load().orc_gather_qmm(xa.ctypes.data, 1 if x_dtype == "bf16" else 0, xb, m,
+                                  packed.reshape(-1), scales.reshape(-1), biases.reshape(-1), wb, n, k,
+                                  group_size, bits, li.ctypes.data, ri.ctypes.data, li.size, out,
+                                  threads or default_threads()), "gather_qmm")
+    return out.reshape(tuple(shape) + (m, n))
 
 
 def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:

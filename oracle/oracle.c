@@ -3,6 +3,7 @@
  *   - dequantize:        w[n,k] = scale[n,k/G] * code[n,k] + bias[n,k/G]
  *   - gathered rows:     out[i,:] = dequantize(table)[idx[i], :]
  *   - quantized matmul:  y[m,n] = sum_k x[m,k] * w[n,k]      (y = x . dequantize(W)^T)
+ *   - gathered matmul:   y[i] = x[lhs[i]] . dequantize(W[rhs[i]])^T  (mixture-of-experts batches)
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
  * may load this library. The HIP library never calls it and shares no code, header, table or
@@ -22,7 +23,9 @@
  *   [nuvec]  nuvec_core, quantized.rs: module documentation (codes form one little-endian bit
  *            stream per row stored as uint32; scales and biases are [.., in/group]), `check_params`
  *            (group sizes, bit widths), `dequantize` and `quantized_matmul` (x . dequantize(w)^T
- *            without materialising the dequantized matrix), `gather_indices` (indices as uint32).
+ *            without materialising the dequantized matrix), `gather_indices` (indices as uint32;
+ *            either index array defaults to every batch in order) and `gather_qmm` (output batch i
+ *            is x[lhs[i]] . dequantize(w[rhs[i]])^T over flattened batch dimensions).
  *   [maya2]  maya2_mlx, quant.py: `mm` (x @ W.T for a quantized weight) and `rows` (an embedding
  *            lookup that dequantizes only the gathered rows).
  *   [spark]  spark_runtime, weights/mlx_int8.rs: module documentation (8-bit words hold four bytes,
@@ -308,5 +311,39 @@ int orc_silu_gate_qmm(const uint16_t* gate, const uint16_t* up, const uint16_t* 
     if (resid)
         for (int64_t i = 0; i < m * n; ++i) out[i] += (double)bf16_to_f32(resid[i]);
     free(h);
+    return 0;
+}
+
+/* [nuvec] gather_qmm (transpose form): x is [x_batches, m, k] (bf16 bit patterns or float32), the
+ * weight is w_batches matrices of [n, k] with their scales and biases stacked the same way, and
+ * output batch i (of `batch`) is
+ *     y[i] = x[lhs[i]] . dequantize(W[rhs[i]])^T          ([m, n], double)
+ * computed by orc_qmm on that pair. [nuvec] gather_indices: a null index array stands for
+ * 0, 1, ..., batch - 1. The pages leave an index past its operand undefined; here that output
+ * batch is NaN. `sorted_indices` only promises an order of rhs that lets a kernel walk each weight
+ * batch once: it changes no value, so the oracle has no such argument.
+ * Returns 0, or -1 for parameters outside the format. */
+int orc_gather_qmm(const void* x, int x_is_bf16, int64_t x_batches, int64_t m, const uint32_t* packed,
+                   const uint16_t* scales, const uint16_t* biases, int64_t w_batches, int64_t n, int64_t k,
+                   int64_t group, int bits, const uint32_t* lhs, const uint32_t* rhs, int64_t batch,
+                   double* out, int threads) {
+    if (m < 0 || n < 0 || batch < 0 || x_batches < 0 || w_batches < 0 || !valid_params(k, group, bits))
+        return -1;
+    if ((!lhs && batch > x_batches) || (!rhs && batch > w_batches)) return -1;
+    const int64_t xsize = x_is_bf16 ? 2 : 4;
+    const int64_t words = k * bits / 32; /* packed words per weight row */
+    for (int64_t i = 0; i < batch; ++i) {
+        const int64_t li = lhs ? (int64_t)lhs[i] : i;
+        const int64_t ri = rhs ? (int64_t)rhs[i] : i;
+        double* yi = out + i * m * n;
+        if (li >= x_batches || ri >= w_batches) {
+            for (int64_t t = 0; t < m * n; ++t) yi[t] = NAN;
+            continue;
+        }
+        const void* xi = (const uint8_t*)x + li * m * k * xsize;
+        int rc = orc_qmm(xi, x_is_bf16, m, packed + ri * n * words, scales + ri * n * (k / group),
+                         biases + ri * n * (k / group), n, k, group, bits, yi, threads);
+        if (rc != 0) return rc;
+    }
     return 0;
 }

@@ -415,3 +415,85 @@ def test_silu_gate_residual_and_linearity(oracle_lib):
     # up = 0 gives 0 whatever the gate
     yz = oracle_lib.silu_gate_qmm(gate, np.zeros_like(up), None, inp.packed, inp.scales, inp.biases, 32, 3)
     assert not yz.any()
+
+
+# ---- gathered products (mixture of experts) -----------------------------------------------------
+
+def _experts(oracle_lib, experts, n, k, G, bits, seed):
+    """`experts` random weights of [n, k], stacked: packed [E, n, k*bits/32], scales/biases [E, n, k/G]."""
+    parts = [W.random_inputs(bits, G, n, k, 1, seed=seed + e) for e in range(experts)]
+    return (np.stack([p.packed for p in parts]), np.stack([p.scales for p in parts]),
+            np.stack([p.biases for p in parts]))
+
+
+def test_gather_qmm_worked_example(oracle_lib):
+    g = golden("gather_qmm_two_experts.txt")
+    E, n, k = int(g["experts"][0]), int(g["n"][0]), int(g["k"][0])
+    G, bits = int(g["group_size"][0]), int(g["bits"][0])
+    codes = np.stack([np.full((n, k), int(c), np.uint8) for c in g["codes"]])
+    packed = np.stack([oracle_lib.pack_codes(codes[e], bits) for e in range(E)])
+    sc = np.stack([np.full((n, k // G), _bf16(float(v))[0], np.uint16) for v in g["scale"]])
+    bi = np.stack([np.full((n, k // G), _bf16(float(v))[0], np.uint16) for v in g["bias"]])
+    # the hand-built experts really are all-ones and all-twos
+    for e in range(E):
+        assert np.all(oracle_lib.dequantize(packed[e], sc[e], bi[e], G, bits) == e + 1)
+    x = np.ones((int(g["tokens"][0]), 1, k), np.float32)
+    rhs = np.array([int(v) for v in g["rhs"]], np.uint32)
+    y = oracle_lib.gather_qmm(x, "f32", packed, sc, bi, G, bits, rhs=rhs)
+    assert list(y.shape) == [int(v) for v in g["shape"]]
+    assert list(y.reshape(-1)[:5]) == [float(v) for v in g["expect_first5"]]
+    # the rest follows from the same rule: token i takes expert rhs[i], whose rows sum to 64 (e + 1)
+    np.testing.assert_array_equal(y[:, 0, :], np.repeat((64.0 * (rhs + 1))[:, None], n, axis=1))
+
+
+def test_gather_qmm_default_indices_are_per_batch_qmm(oracle_lib):
+    packed, sc, bi = _experts(oracle_lib, 3, 9, 128, 32, 3, seed=40)
+    x = W.bf16_bits_from_f32(np.random.default_rng(41).standard_normal((3, 2, 128)).astype(np.float32))
+    y = oracle_lib.gather_qmm(x, "bf16", packed, sc, bi, 32, 3)
+    assert y.shape == (3, 2, 9)
+    for b in range(3):
+        np.testing.assert_array_equal(y[b], oracle_lib.qmm(x[b], "bf16", packed[b], sc[b], bi[b], 32, 3))
+
+
+def test_gather_qmm_indices_against_numpy(oracle_lib):
+    # x batches and experts differ in number, so swapped index arrays land out of range; every pair
+    # is checked against a float64 numpy product of the (pinned) dequantized expert
+    E, n, k, G, bits = 5, 7, 128, 64, 4
+    packed, sc, bi = _experts(oracle_lib, E, n, k, G, bits, seed=50)
+    x = np.random.default_rng(51).standard_normal((4, 3, k)).astype(np.float32)
+    lhs = np.array([3, 0, 0, 2, 1, 3], np.uint32)
+    rhs = np.array([4, 4, 1, 0, 2, 3], np.uint32)
+    y = oracle_lib.gather_qmm(x, "f32", packed, sc, bi, G, bits, lhs=lhs, rhs=rhs)
+    assert y.shape == (6, 3, n)
+    for i in range(6):
+        w = oracle_lib.dequantize(packed[rhs[i]], sc[rhs[i]], bi[rhs[i]], G, bits).astype(np.float64)
+        np.testing.assert_allclose(y[i], x[lhs[i]].astype(np.float64) @ w.T, rtol=1e-12, atol=1e-12)
+
+
+def test_gather_qmm_broadcasts_indices(oracle_lib):
+    packed, sc, bi = _experts(oracle_lib, 3, 5, 64, 32, 2, seed=60)
+    x = np.random.default_rng(61).standard_normal((2, 1, 64)).astype(np.float32)
+    lhs = np.array([[1], [0]], np.int64)      # [2, 1]
+    rhs = np.array([2, 0, 1], np.int32)       # [3]  -> batch [2, 3]
+    y = oracle_lib.gather_qmm(x, "f32", packed, sc, bi, 32, 2, lhs=lhs, rhs=rhs)
+    assert y.shape == (2, 3, 1, 5)
+    for a in range(2):
+        for b in range(3):
+            ref = oracle_lib.qmm(x[lhs[a, 0]], "f32", packed[rhs[b]], sc[rhs[b]], bi[rhs[b]], 32, 2)
+            np.testing.assert_array_equal(y[a, b], ref)
+    # an absent lhs defaults to every x batch in order and broadcasts the same way
+    y2 = oracle_lib.gather_qmm(x[:1], "f32", packed, sc, bi, 32, 2, rhs=rhs)
+    np.testing.assert_array_equal(y2, y[1])  # lhs[1] = 0
+    with pytest.raises(ValueError):
+        oracle_lib.gather_qmm(x, "f32", packed, sc, bi, 32, 2, rhs=np.array([0.0, 1.0]))
+    with pytest.raises(ValueError):   # 2 and 3 do not broadcast
+        oracle_lib.gather_qmm(x, "f32", packed, sc, bi, 32, 2, lhs=np.array([0, 1]), rhs=rhs)
+
+
+def test_gather_qmm_out_of_range_is_nan(oracle_lib):
+    packed, sc, bi = _experts(oracle_lib, 2, 4, 64, 64, 8, seed=70)
+    x = np.random.default_rng(71).standard_normal((2, 1, 64)).astype(np.float32)
+    y = oracle_lib.gather_qmm(x, "f32", packed, sc, bi, 64, 8, lhs=np.array([0, 2, 1], np.uint32),
+                              rhs=np.array([1, 0, 2], np.uint32))
+    assert np.isnan(y[1]).all() and np.isnan(y[2]).all()
+    np.testing.assert_array_equal(y[0], oracle_lib.qmm(x[0], "f32", packed[1], sc[1], bi[1], 64, 8))
