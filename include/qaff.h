@@ -124,6 +124,43 @@ qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, con
                                 hipStream_t stream);
 
 /*
+ * Quantized products of gathered batches (nuvec_core quantized.rs gather_qmm with the transpose;
+ * its mixture-of-experts use: one weight batch per expert). Output batch b is
+ *     y[b] = x[lhs_indices[b]] . dequantize(W[rhs_indices[b]])^T.
+ *   x [x_batches, m, k] in x_dtype (float32 or bf16); the weight is w_batches matrices [n, k] stacked:
+ *   packed [w_batches, n, k*bits/32], scales and biases [w_batches, n, k/group_size];
+ *   lhs_indices, rhs_indices: uint32 device arrays of `batch` entries (nuvec_core gather_indices
+ *   casts integer indices to U32), or NULL for 0 .. batch-1 (then batch must not exceed that
+ *   operand's batches). Broadcasting index arrays against each other is left to the caller, who
+ *   passes them expanded to `batch` entries. y [batch, m, n] in x's dtype; sums in float32.
+ *   An index at or past its operand's batches cannot be checked on the host without a
+ *   synchronization: that output batch is filled with quiet NaNs.
+ *   sorted_indices != 0 promises that rhs_indices is non-decreasing (rows grouped by expert). With
+ *   m == 1, lhs_indices NULL and a bf16 x, the matrix-core kernel then walks each expert once over
+ *   all of its rows (rows [#(rhs < e), #(rhs < e + 1)) of expert e). A broken promise leaves rows
+ *   unwritten or computed with another expert. Without the conditions the flag changes nothing.
+ * Kernels (QAFF_PATH_AUTO): the matrix-core decode kernel where it applies (bf16 x, k a multiple of
+ * 512 up to 4096, 4-byte aligned scales and biases) when grouped, or when m >= qaff_gemv_mfma_min_m();
+ * the VALU GEMV otherwise (any m).
+ * Errors: as qaff_qmm, plus INVALID_ARGUMENT for negative batch counts, a NULL index array with
+ * batch above its operand's batches, or misaligned (4-byte) indices.
+ */
+qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                            const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                            const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
+                            int32_t sorted_indices, void* y, hipStream_t stream);
+
+/* qaff_gather_qmm with the kernel forced: QAFF_PATH_GEMV (the VALU GEMV; the sorted promise is not
+ * used) or QAFF_PATH_GEMV_MFMA (UNSUPPORTED where that kernel does not apply). QAFF_PATH_GEMM is
+ * UNSUPPORTED. */
+qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                               const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                               int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                               const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
+                               int32_t sorted_indices, void* y, hipStream_t stream, qaff_path path);
+
+/*
  * Gathered-row dequantization: out[i, :] = dequantize(table)[indices[i], :] (maya2_mlx rows: an
  * embedding lookup that dequantizes only the gathered rows). Indices are uint32 (nuvec_core
  * gather_indices casts integer indices to U32); duplicates are allowed. An index >= table_rows

@@ -14,6 +14,8 @@ bit views are accepted too). A weight is ``scale * code + bias`` of its group.
     e = dequant_rows(packed, scales, biases, idx, group_size, bits)   # embedding lookup
     g, u = gemv_gate_up(x, gate_w, up_w, group_size, bits)           # two projections, x read once
     y = gemv_silu_gate(g, u, packed, scales, biases, group_size, bits, resid=r)  # W . (silu(g) * u) + r
+    y = gather_qmm(x, packed, scales, biases, group_size, bits, rhs_indices=experts,
+                   sorted_indices=True)                     # batch i: x[i] . dequantize(W[experts[i]])^T
 """
 from __future__ import annotations
 
@@ -25,12 +27,13 @@ import torch
 from . import _lib
 from ._lib import QaffError
 
-__all__ = ["dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "QWeight", "QaffError",
-           "gemv_max_m", "gemv_mfma_min_m"]
+__all__ = ["dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "gather_qmm", "QWeight",
+           "QaffError", "gemv_max_m", "gemv_mfma_min_m"]
 
 _PACKED_DTYPES = (torch.int32, torch.uint32)
 _BF16_BITS_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
 _INDEX_DTYPES = (torch.int32, torch.uint32)
+_GATHER_INDEX_DTYPES = (torch.int32, torch.uint32, torch.int64)
 _OUT_DTYPES = {torch.float32: _lib.QAFF_F32, torch.bfloat16: _lib.QAFF_BF16}
 
 
@@ -230,3 +233,79 @@ def gemv_silu_gate(gate, up, packed, scales, biases, group_size: int, bits: int,
         _lib.check(lib.qaff_gemv_silu_gate(_p(g2), _p(u2), g2.shape[0], _p(packed), _p(scales), _p(biases),
                                            n, k, group_size, bits, _p(r2), _p(y), _stream(dev)))
     return y
+
+
+def _batch_indices(given, batch_shape, name, dev):
+    """One operand's indices of a gathered product (nuvec_core ``gather_indices``): the given
+    integer tensor, or every batch of the operand in order (None stands for that while its shape is
+    the broadcast one)."""
+    if given is None:
+        return None, tuple(batch_shape)
+    _need(given, name, _GATHER_INDEX_DTYPES, dev)
+    return given, tuple(given.shape)
+
+
+def _expand_indices(t, own_shape, shape, dev):
+    """Indices as a contiguous int32/uint32 tensor of the broadcast shape (argument marshalling:
+    a default becomes an explicit arange only when it has to broadcast)."""
+    if t is None:
+        if own_shape == shape:
+            return None
+        t = torch.arange(math.prod(own_shape), dtype=torch.int32, device=dev).reshape(own_shape)
+    elif t.dtype == torch.int64:
+        t = t.to(torch.int32)  # the low 32 bits: the same uint32 value as a cast of the integer
+    if tuple(t.shape) != shape:
+        t = t.expand(shape)
+    return t.contiguous()
+
+
+def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indices=None, rhs_indices=None,
+               sorted_indices: bool = False, path: str = "auto", out=None):
+    """Quantized products of gathered batches (nuvec_core ``gather_qmm`` with the transpose):
+    output batch i is ``x[lhs[i]] . dequantize(W[rhs[i]])^T`` over the flattened batch dimensions
+    of x ``[..., m, k]`` (float32 or bf16) and of the weight (packed ``[..., n, k*bits/32]``,
+    scales and biases ``[..., n, k/group_size]``). Indices are integer tensors that broadcast
+    together, each defaulting to every batch of its operand; an index past its operand gives a NaN
+    batch. ``sorted_indices`` promises that ``rhs_indices`` is sorted (rows grouped by expert),
+    which lets the kernel read each expert's weights once. The result has x's dtype and shape
+    ``broadcast(batch) + [m, n]``."""
+    lib = _lib.load()
+    _need(packed, "packed", _PACKED_DTYPES)
+    dev = packed.device
+    if packed.dim() < 2 or scales.dim() < 2 or tuple(scales.shape[:-2]) != tuple(packed.shape[:-2]):
+        raise ValueError("packed must be [..., n, k*bits/32] and scales, biases [..., n, k/group_size]")
+    if tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("scales and biases differ in shape")
+    w_batch = tuple(packed.shape[:-2])
+    wb = math.prod(w_batch)
+    n = packed.shape[-2]
+    _, _, k = _weights(packed.reshape(-1, packed.shape[-1]), scales.reshape(-1, scales.shape[-1]),
+                       biases.reshape(-1, biases.shape[-1]), group_size, bits)
+    _need(x, "x", tuple(_OUT_DTYPES), dev)
+    if x.dim() < 2:
+        raise ValueError("x must be [..., m, k]")
+    m = x.shape[-2]
+    if x.shape[-1] != k:
+        raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
+    if path not in ("auto", "gemv", "gemv_mfma"):
+        raise ValueError("path must be 'auto', 'gemv' or 'gemv_mfma'")
+    x_batch = tuple(x.shape[:-2])
+    lhs, lhs_shape = _batch_indices(lhs_indices, x_batch, "lhs_indices", dev)
+    rhs, rhs_shape = _batch_indices(rhs_indices, w_batch, "rhs_indices", dev)
+    shape = tuple(torch.broadcast_shapes(lhs_shape, rhs_shape))
+    lhs = _expand_indices(lhs, lhs_shape, shape, dev)
+    rhs = _expand_indices(rhs, rhs_shape, shape, dev)
+    batch = math.prod(shape)
+    want = shape + (m, n)
+    if out is None:
+        out = torch.empty(want, dtype=x.dtype, device=dev)
+    else:
+        _need(out, "out", (x.dtype,), dev)
+        if tuple(out.shape) != want:
+            raise ValueError(f"out must be {list(want)}")
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_gather_qmm_ex(_p(x), _OUT_DTYPES[x.dtype], math.prod(x_batch), m, _p(packed),
+                                          _p(scales), _p(biases), wb, n, k, group_size, bits, _p(lhs),
+                                          _p(rhs), batch, 1 if sorted_indices else 0, _p(out), _stream(dev),
+                                          _lib.PATHS[path]))
+    return out

@@ -257,6 +257,86 @@ qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, con
                         stream);
 }
 
+qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                               const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                               int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                               const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
+                               int32_t sorted_indices, void* y, hipStream_t stream, qaff_path path) {
+    static const char* op = "qaff_gather_qmm";
+    g_error.clear();
+    if (x_batches < 0 || w_batches < 0 || batch < 0 || m < 0)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative size", op);
+    // the weight as one matrix of w_batches * n rows
+    qaff_status st = check_weight(op, packed, scales, biases, w_batches * n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
+    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMV_MFMA)
+        return fail(path == QAFF_PATH_GEMM ? QAFF_ERR_UNSUPPORTED : QAFF_ERR_INVALID_ARGUMENT,
+                    "%s: path %d is not available for gathered products", op, (int)path);
+    if (!lhs_indices && batch > x_batches)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: no lhs indices, but %lld batches of %lld x batches", op,
+                    (long long)batch, (long long)x_batches);
+    if (!rhs_indices && batch > w_batches)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: no rhs indices, but %lld batches of %lld weight batches", op,
+                    (long long)batch, (long long)w_batches);
+    if ((lhs_indices && !aligned(lhs_indices, 4)) || (rhs_indices && !aligned(rhs_indices, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: indices must be 4-byte aligned", op);
+    if (x_batches >= 0xffffffffLL || w_batches >= 0xffffffffLL || batch >= 0xffffffffLL)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: 2^32-1 or more batches", op);
+    const bool mfma_ok = x_dtype == QAFF_BF16 && qaff::gemv_mfma_supported(1, k) && aligned(scales, 4) &&
+                         aligned(biases, 4);
+    if (path == QAFF_PATH_GEMV_MFMA && batch > 0 && m > 0 && n > 0 && k > 0 && !mfma_ok)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes a bf16 x, k a multiple of 512 "
+                    "up to 4096 and 4-byte aligned scales and biases", op);
+    if (batch == 0 || m == 0 || n == 0) return QAFF_OK;
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, batch * m * n * esize, stream), stream);
+    if (x_batches > 0 && !x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (x && !aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+
+    qaff::Gather g{};
+    g.lhs = lhs_indices;
+    g.rhs = rhs_indices;
+    g.x_count = (uint32_t)x_batches;
+    g.w_count = (uint32_t)w_batches;
+    g.batch = (uint32_t)batch;
+    g.x_stride = (uint64_t)(m * k);
+    g.w_stride = (uint64_t)(n * (k / 32) * bits);
+    g.sb_stride = (uint64_t)(n * (k / group_size));
+    g.y_stride = (uint64_t)(m * n);
+    // sorted rows, one per output batch, gathered by expert
+    const bool groupable = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices && mfma_ok;
+    bool use_mfma = false;
+    if (path == QAFF_PATH_GEMV_MFMA) {
+        use_mfma = true;
+        g.grouped = groupable;
+    } else if (path == QAFF_PATH_AUTO && mfma_ok) {
+        // grouped once experts average at least one row: each expert's weights are then read once
+        g.grouped = groupable && batch >= w_batches;
+        use_mfma = g.grouped || m >= kGemvMfmaMinM;
+    }
+    hipError_t e;
+    if (use_mfma)
+        e = qaff::launch_gemv_mfma_gather(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
+                                          bits, static_cast<uint16_t*>(y), g, stream);
+    else
+        e = qaff::launch_gemv_gather(x, x_dtype == QAFF_F32, m, packed, scales, biases, n, k, group_size, bits, y, g,
+                                     stream);
+    return after_launch(op, e, stream);
+}
+
+qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                            const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                            const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
+                            int32_t sorted_indices, void* y, hipStream_t stream) {
+    return qaff_gather_qmm_ex(x, x_dtype, x_batches, m, packed, scales, biases, w_batches, n, k, group_size, bits,
+                              lhs_indices, rhs_indices, batch, sorted_indices, y, stream, QAFF_PATH_AUTO);
+}
+
 qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
                      const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                      int32_t group_size, int32_t bits, void* y, hipStream_t stream) {

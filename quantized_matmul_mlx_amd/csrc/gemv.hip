@@ -167,11 +167,39 @@ __device__ __forceinline__ float silu_f32(float v) {
 
 // FUSED adds the decode fusions of `GemvFused` (uniform flags read at run time): the x transform,
 // the residual, and a second weight whose rows follow the first's (rows n .. 2n - 1).
-template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED>
+// The x batch and weight batch of a gathered product's block (grid z = output batch). Returns
+// false, after writing NaN over the block's outputs, when an index is out of range.
+template <int RPW, int MB, typename XP, typename PP, typename SP, typename YP>
+__device__ __forceinline__ bool gather_batch(const Gather& ga, uint32_t row0, uint32_t m0, uint32_t m, uint32_t n,
+                                             int lane, XP& x, PP& packed, SP& scales, SP& biases, YP& y) {
+    const uint32_t b = ga.b0 + blockIdx.z;
+    const uint32_t li = ga.lhs ? ga.lhs[b] : b;
+    const uint32_t ri = ga.rhs ? ga.rhs[b] : b;
+    y += (size_t)b * ga.y_stride;
+    if (li >= ga.x_count || ri >= ga.w_count) {
+        if (lane == 0)
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+                    if (row0 + r < n && m0 + i < m) {
+                        if constexpr (sizeof(*y) == 2) y[(size_t)(m0 + i) * n + row0 + r] = 0x7FC0u;
+                        else y[(size_t)(m0 + i) * n + row0 + r] = __builtin_nanf("");
+                    }
+        return false;
+    }
+    x += (size_t)li * ga.x_stride;
+    packed += (size_t)ri * ga.w_stride;
+    scales += (size_t)ri * ga.sb_stride;
+    biases += (size_t)ri * ga.sb_stride;
+    return true;
+}
+
+template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED, bool GATHER = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint16_t* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
-    uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y, GemvFused fz) {
+    uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y, GemvFused fz, Gather ga) {
     constexpr int kBlockThreads = WAVES * 64;
     constexpr int kPassBlocks = 64 * P;  // 32-code blocks per row per pass
     // x of the pass as bf16 pairs in unpack order: [x row][quarter of a block][block] of 16 bytes,
@@ -185,6 +213,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint32_t row0 = (blockIdx.x * WAVES + wave) * RPW;
     const uint32_t m0 = blockIdx.y * MB;
     const uint32_t gpr = kb >> gshift;
+    if constexpr (GATHER) {  // block-uniform: the whole block returns
+        if (!gather_batch<RPW, MB>(ga, row0, m0, m, n, lane, x, packed, scales, biases, y)) return;
+    }
     // rows of the launch: n, or 2n with a second weight (its rows after the first's)
     const uint32_t nrows = (FUSED && fz.packed2) ? 2 * n : n;
     const bool silu = FUSED && fz.up != nullptr;
@@ -386,16 +417,19 @@ __device__ __forceinline__ void load_x_f32_block(const float* __restrict__ x, ui
     }
 }
 
-template <int BITS, int MB, int RW>
+template <int BITS, int MB, int RW, bool GATHER = false>
 __global__ __launch_bounds__(kThreads) void gemv_f32_kernel(
     const float* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
-    uint32_t kb, uint32_t gshift, float* __restrict__ y) {
+    uint32_t kb, uint32_t gshift, float* __restrict__ y, Gather ga) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const uint32_t n0 = (blockIdx.x * kWaves + wave) * RW;
     if (n0 >= n) return;  // wave-uniform; this kernel has no block-level barrier
     const uint32_t m0 = blockIdx.y * MB;
+    if constexpr (GATHER) {
+        if (!gather_batch<RW, MB>(ga, n0, m0, m, n, lane, x, packed, scales, biases, y)) return;
+    }
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> gshift;
 
@@ -505,7 +539,7 @@ hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, c
         }
         gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
             x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
-            (uint32_t)kb, gshift, y + (size_t)m_off * n, f);
+            (uint32_t)kb, gshift, y + (size_t)m_off * n, f, Gather{});
     });
 }
 
@@ -546,7 +580,7 @@ hipError_t launch_f32(const float* x, int64_t m, const uint32_t* packed, const u
     return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
         gemv_f32_kernel<BITS, MB, RW><<<dim3(gx, gy), dim3(kThreads), 0, stream>>>(
             x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
-            (uint32_t)kb, gshift, y + (size_t)m_off * n);
+            (uint32_t)kb, gshift, y + (size_t)m_off * n, Gather{});
     });
 }
 
@@ -570,7 +604,98 @@ hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* pac
                                       static_cast<uint16_t*>(y), GemvFused{}, stream);
 }
 
+// ---- gathered batches: grid z = output batch, in launches of at most 65535 batches ----------------
+
+template <typename Launch>
+hipError_t over_batches(const Gather& ga, Launch&& launch) {
+    for (uint64_t b0 = 0; b0 < ga.batch; b0 += 65535) {
+        Gather g = ga;
+        g.b0 = (uint32_t)b0;
+        const unsigned gz = (unsigned)(ga.batch - b0 < 65535 ? ga.batch - b0 : 65535);
+        const hipError_t e = launch(g, gz);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int BITS, int MB, int RPW, int WAVES, int P>
+hipError_t launch_bf16_gather_p(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                                const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                                const Gather& ga, hipStream_t stream) {
+    const unsigned gx = (unsigned)((n + WAVES * RPW - 1) / (WAVES * RPW));
+    return over_batches(ga, [&](const Gather& g, unsigned gz) {
+        return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
+            gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, false, true><<<dim3(gx, gy, gz), dim3(WAVES * 64), 0, stream>>>(
+                x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
+                (uint32_t)kb, gshift, y + (size_t)m_off * n, GemvFused{}, g);
+        });
+    });
+}
+
+template <int BITS, int MB, int RPW, int WAVES>
+hipError_t launch_bf16_gather(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                              const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                              const Gather& ga, hipStream_t stream) {
+    if (kLongPass<MB> > 2 && kb > 128)
+        return launch_bf16_gather_p<BITS, MB, RPW, WAVES, kLongPass<MB>>(x, m, packed, scales, biases, n, kb,
+                                                                        gshift, y, ga, stream);
+    return launch_bf16_gather_p<BITS, MB, RPW, WAVES, 2>(x, m, packed, scales, biases, n, kb, gshift, y, ga, stream);
+}
+
+template <int BITS, int MB>
+hipError_t launch_f32_gather(const float* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                             const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, float* y,
+                             const Gather& ga, hipStream_t stream) {
+    constexpr int RW = 2;
+    const unsigned gx = (unsigned)((n + kWaves * RW - 1) / (kWaves * RW));
+    return over_batches(ga, [&](const Gather& g, unsigned gz) {
+        return over_m_slices(m, MB, [&](int64_t m_off, int64_t mm, unsigned gy) {
+            gemv_f32_kernel<BITS, MB, RW, true><<<dim3(gx, gy, gz), dim3(kThreads), 0, stream>>>(
+                x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
+                (uint32_t)kb, gshift, y + (size_t)m_off * n, g);
+        });
+    });
+}
+
+template <int BITS>
+hipError_t launch_gather_bits(const void* x, bool x_f32, int64_t m, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t kb,
+                              uint32_t gshift, void* y, const Gather& g, hipStream_t stream) {
+    if (x_f32) {
+        const float* xf = static_cast<const float*>(x);
+        float* yf = static_cast<float*>(y);
+        if (m == 1) return launch_f32_gather<BITS, 1>(xf, m, packed, scales, biases, n, kb, gshift, yf, g, stream);
+        if (m == 2) return launch_f32_gather<BITS, 2>(xf, m, packed, scales, biases, n, kb, gshift, yf, g, stream);
+        return launch_f32_gather<BITS, 4>(xf, m, packed, scales, biases, n, kb, gshift, yf, g, stream);
+    }
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    uint16_t* yb = static_cast<uint16_t*>(y);
+    if (m == 1)
+        return launch_bf16_gather<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+    if (m == 2)
+        return launch_bf16_gather<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+    if (m <= 4)
+        return launch_bf16_gather<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+    return launch_bf16_gather<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+}
+
 }  // namespace
+
+hipError_t launch_gemv_gather(const void* x, bool x_f32, int64_t m, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                              int group_size, int bits, void* y, const Gather& g, hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 2: return launch_gather_bits<2>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 3: return launch_gather_bits<3>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 4: return launch_gather_bits<4>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 5: return launch_gather_bits<5>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 6: return launch_gather_bits<6>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 8: return launch_gather_bits<8>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,

@@ -261,7 +261,226 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
     return launch_mb<BITS, 2>(x, m, packed, scales, biases, n, kb, y, stream);
 }
 
+// ---- gathered batches ---------------------------------------------------------------------------
+//
+// The same operand layout, with the weight tile dequantized once into registers (16 registers
+// per chunk) and reused for every tile of up to MB x rows: a block owns 16 rows of one weight
+// batch and walks all x rows that use it.
+//  * Batched: grid y = output batch b; x rows 0 .. m - 1 of batch lhs[b] against weight rhs[b].
+//  * Grouped (rhs sorted, m == 1, no lhs): grid y = expert e; the rows of e are
+//    [#(rhs < e), #(rhs < e + 1)), found by a search over rhs, so each expert's weights are read
+//    once however many rows use it. Expert w_count takes the rows past every expert (NaN).
+// An out-of-range index gives a NaN output batch.
+
+// #(idx[i] < v1) and #(idx[i] < v2) over a sorted idx[0 .. len) (len >= 1): a 64-ary search per
+// bound, both in lockstep so that their loads go out together. Each step probes lo + lane * step;
+// the probes below v are a prefix (the array is sorted), and the bound lies after the last one
+// and no later than the next.
+__device__ __forceinline__ void count_below2(const uint32_t* idx, uint32_t len, uint32_t v1, uint32_t v2,
+                                             int lane, uint32_t& c1, uint32_t& c2) {
+    uint32_t lo1 = 0, hi1 = len, lo2 = 0, hi2 = len;
+    while (lo1 < hi1 || lo2 < hi2) {
+        const uint32_t st1 = (hi1 - lo1 + 63) >> 6, st2 = (hi2 - lo2 + 63) >> 6;
+        const uint32_t i1 = lo1 + (uint32_t)lane * st1, i2 = lo2 + (uint32_t)lane * st2;
+        const uint32_t a1 = idx[min(i1, len - 1)];
+        const uint32_t a2 = idx[min(i2, len - 1)];
+        const uint32_t n1 = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i1 < hi1 && a1 < v1));
+        const uint32_t n2 = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i2 < hi2 && a2 < v2));
+        if (lo1 < hi1) {
+            if (n1 == 0) {
+                hi1 = lo1;
+            } else {
+                hi1 = min(lo1 + n1 * st1, hi1);
+                lo1 += (n1 - 1) * st1 + 1;
+            }
+        }
+        if (lo2 < hi2) {
+            if (n2 == 0) {
+                hi2 = lo2;
+            } else {
+                hi2 = min(lo2 + n2 * st2, hi2);
+                lo2 += (n2 - 1) * st2 + 1;
+            }
+        }
+    }
+    c1 = lo1;
+    c2 = lo2;
+}
+
+template <int BITS, int GSHIFT, int MB>
+__global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, Gather ga) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int waves = (int)(kb >> 4);
+    const uint32_t n0 = blockIdx.x * 16;
+    const uint32_t k = kb * 32;
+    const uint32_t gpr = kb >> GSHIFT;
+    const int lr16 = lane & 15;
+    const int lg = lane >> 4;
+    const uint64_t g_hi = __builtin_amdgcn_ballot_w64(lg >= 2);
+    const uint32_t z = ga.b0 + blockIdx.y;
+
+    // 1. This block's x rows [r0, r1) (row r at xb + r k, its output at yb + r n) and weight batch.
+    uint32_t r0, r1, wi;
+    const uint16_t* xb = x;
+    uint16_t* yb = y;
+    bool nan_rows;
+    if (ga.grouped) {
+        uint32_t s, t;
+        count_below2(ga.rhs, ga.batch, z, z + 1, lane, s, t);
+        r0 = s;
+        r1 = z >= ga.w_count ? ga.batch : t;
+        wi = z;
+        nan_rows = z >= ga.w_count;
+    } else {
+        const uint32_t li = ga.lhs ? ga.lhs[z] : z;
+        const uint32_t ri = ga.rhs ? ga.rhs[z] : z;
+        r0 = 0;
+        r1 = m;
+        wi = ri;
+        yb = y + (size_t)z * ga.y_stride;
+        nan_rows = li >= ga.x_count || ri >= ga.w_count;
+        if (!nan_rows) xb = x + (size_t)li * ga.x_stride;
+    }
+    if (r0 >= r1) return;  // the same in every wave: the whole block returns
+    if (nan_rows) {
+        for (uint32_t o = tid; o < (r1 - r0) * 16; o += blockDim.x) {
+            const uint32_t col = n0 + (o & 15);
+            if (col < n) yb[(size_t)(r0 + (o >> 4)) * n + col] = 0x7FC0u;
+        }
+        return;
+    }
+    const uint32_t* pw = packed + (size_t)wi * ga.w_stride;
+    const uint16_t* sp = scales + (size_t)wi * ga.sb_stride;
+    const uint16_t* bp = biases + (size_t)wi * ga.sb_stride;
+
+    // 2. Loads: the first x tile, the tile row's scale and bias windows, then the codes.
+    u32x4a xg[MB];
+    const uint16_t* xs = xb + (size_t)wave * kSlice + lane * 8;
+#pragma unroll
+    for (int r = 0; r < MB; ++r) xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min(r0 + r, r1 - 1) * k);
+    const uint32_t row = min(n0 + lr16, n - 1);
+    SbWindow<GSHIFT> sw, bw;
+    {
+        const size_t e = (size_t)row * gpr + (size_t)wave * (16 >> GSHIFT);
+        sw.load(sp + e);
+        bw.load(bp + e);
+    }
+    uint32_t wq[4][BITS];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const uint32_t jb = (uint32_t)wave * 16 + 4 * c + lg;
+        load_block<BITS>(pw + (size_t)row * kb * BITS + (size_t)jb * BITS, wq[c]);
+    }
+
+    // 3. Dequantize the tile once.
+    bf16x8 wb[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float sc = sw.get(c, lg, g_hi);
+        const float bi = bw.get(c, lg, g_hi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wb[c][j] = dequant8<BITS>(wq[c], j, sc, bi);
+    }
+
+    // 4. Walk the x rows in tiles of MB: x through this wave's LDS region (as in the decode kernel),
+    //    the multiply, and the slices' partial tiles summed through a separate LDS area.
+    uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
+    float* red = reinterpret_cast<float*>(smem + (size_t)waves * (MB * kXPitch));
+    const uint8_t* xa = xl + min(lr16, MB - 1) * kXPitch + lg * 64;
+    for (uint32_t t0 = r0; t0 < r1; t0 += MB) {
+        if (t0 != r0) {
+#pragma unroll
+            for (int r = 0; r < MB; ++r) xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min(t0 + r, r1 - 1) * k);
+        }
+#pragma unroll
+        for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[c][j], acc, 0, 0, 0);
+            }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
+        __syncthreads();
+        for (int o = tid; o < 16 * MB; o += (int)blockDim.x) {  // result rows past MB repeat row MB - 1
+            const int mm = o >> 4, nn = o & 15;
+            const int l = ((mm >> 2) << 4) | nn, v = mm & 3;
+            float sum = 0.f;
+            for (int w = 0; w < waves; ++w) sum += red[(w * 4 + v) * 64 + l];
+            const uint32_t r = t0 + (uint32_t)mm, col = n0 + (uint32_t)nn;
+            if (r < r1 && col < n) yb[(size_t)r * n + col] = to_bf16_bits(sum);
+        }
+        __syncthreads();  // red is written again by the next tile
+    }
+}
+
+template <int BITS, int GSHIFT, int MB>
+hipError_t launch_gather_mb(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                            const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, const Gather& ga,
+                            hipStream_t stream) {
+    const int waves = (int)(kb / 16);
+    const size_t lds = (size_t)waves * MB * kXPitch + (size_t)waves * 4 * 64 * sizeof(float);
+    const unsigned gx = (unsigned)((n + 15) / 16);
+    // grid y: output batches, or experts 0 .. w_count when grouped
+    const uint64_t count = ga.grouped ? (uint64_t)ga.w_count + 1 : ga.batch;
+    for (uint64_t b0 = 0; b0 < count; b0 += 65535) {
+        Gather g = ga;
+        g.b0 = (uint32_t)b0;
+        const unsigned gy = (unsigned)(count - b0 < 65535 ? count - b0 : 65535);
+        gemv_mfma_gather_kernel<BITS, GSHIFT, MB><<<dim3(gx, gy), dim3(waves * 64), lds, stream>>>(
+            x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int BITS, int GSHIFT>
+hipError_t launch_gather_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, const Gather& ga,
+                           hipStream_t stream) {
+    // rows per tile: m, or the mean number of rows per expert when grouped
+    const int64_t rows = ga.grouped ? ((int64_t)ga.batch + ga.w_count - 1) / (ga.w_count ? ga.w_count : 1) : m;
+    if (rows <= 4) return launch_gather_mb<BITS, GSHIFT, 4>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+    if (rows <= 8) return launch_gather_mb<BITS, GSHIFT, 8>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+    return launch_gather_mb<BITS, GSHIFT, 16>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+}
+
+template <int BITS>
+hipError_t launch_gather_bits(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                              const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                              const Gather& ga, hipStream_t stream) {
+    if (gshift == 0) return launch_gather_g<BITS, 0>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+    if (gshift == 1) return launch_gather_g<BITS, 1>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+    return launch_gather_g<BITS, 2>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+}
+
 }  // namespace
+
+hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t* packed,
+                                   const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                   int group_size, int bits, uint16_t* y, const Gather& g,
+                                   hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 2: return launch_gather_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 3: return launch_gather_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 4: return launch_gather_bits<4>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 5: return launch_gather_bits<5>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 6: return launch_gather_bits<6>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        case 8: return launch_gather_bits<8>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 bool gemv_mfma_supported(int64_t m, int64_t k) {
     return m >= 1 && m <= 16 && k % kSlice == 0 && k <= 8 * kSlice;

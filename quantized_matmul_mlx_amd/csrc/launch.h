@@ -33,6 +33,29 @@ hipError_t launch_gemv_fused(const uint16_t* x, int64_t m, const uint32_t* packe
                              const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
                              uint16_t* y, const GemvFused& f, hipStream_t stream);
 
+// A gathered product (nuvec_core quantized.rs, `gather_qmm`): output batch b is
+// x[lhs[b]] . dequantize(W[rhs[b]])^T. Launches index the batch through the grid; `b0` is the
+// first batch (or expert) of a launch, since one grid dimension holds at most 65535 blocks.
+struct Gather {
+    const uint32_t* lhs;  // x batch of output batch b; null: b
+    const uint32_t* rhs;  // weight batch of output batch b; null: b
+    uint32_t x_count;     // batches of x and of the weight; an index at or past its count
+    uint32_t w_count;     // gives a NaN output batch
+    uint32_t batch;       // output batches
+    uint32_t b0;
+    int grouped;          // matrix-core kernel only: rhs is sorted, m == 1 and lhs is null; the grid
+                          // walks experts 0 .. w_count (the last one: rows past every expert)
+    uint64_t x_stride;    // x elements per batch (m * k)
+    uint64_t w_stride;    // packed words per weight batch
+    uint64_t sb_stride;   // scales (biases) per weight batch
+    uint64_t y_stride;    // y elements per batch (m * n)
+};
+
+// The VALU GEMV over gathered batches (any m, x float32 or bf16, y in x's dtype).
+hipError_t launch_gemv_gather(const void* x, bool x_f32, int64_t m, const uint32_t* packed,
+                              const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                              int group_size, int bits, void* y, const Gather& g, hipStream_t stream);
+
 // The decode product on the matrix cores: y[m, n] (bf16) = x (bf16) . dequantize(W)^T for
 // 1 <= m <= 16, with each code dequantized to bf16 in registers. Only for shapes where
 // gemv_mfma_supported(m, k) holds, and scales/biases 4-byte aligned.
@@ -40,6 +63,14 @@ bool gemv_mfma_supported(int64_t m, int64_t k);
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed,
                             const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                             int group_size, int bits, uint16_t* y, hipStream_t stream);
+
+// The matrix-core decode kernel over gathered batches (any m, in tiles of up to 16 rows; bf16), or
+// with g.grouped over the rows of each expert, reading each expert's weights once. Only where
+// gemv_mfma_supported(1, k) holds and scales/biases are 4-byte aligned.
+hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t* packed,
+                                   const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                   int group_size, int bits, uint16_t* y, const Gather& g,
+                                   hipStream_t stream);
 
 // y[m, n] (bf16) = x (bf16) . dequantize(W)^T with W tiles dequantized to bf16 and bf16 MFMA,
 // float32 accumulation.

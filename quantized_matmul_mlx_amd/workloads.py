@@ -19,7 +19,8 @@ Conventions
 
 The configurations are the MLX-layout workloads used for parity and for the benchmark: a small
 4-bit reference case, the 4096x4096 4-bit decode GEMV, an 8-bit 14336x4096 GEMV, the 4-bit
-group-128 prefill GEMM, 3- and 6-bit group-32 odd widths, and a gathered-row embedding table.
+group-128 prefill GEMM, 3- and 6-bit group-32 odd widths, a gathered-row embedding table, a decode
+FFN step and a mixture-of-experts layer.
 """
 from __future__ import annotations
 
@@ -42,6 +43,8 @@ class Workload:
     x_dtype: str = "bf16"       # "bf16" or "f32"
     n_indices: int = 0          # gathered-row lookups (embedding table workloads)
     seed: int = 0
+    experts: int = 0            # weight batches of a gathered (mixture-of-experts) product
+    top_k: int = 0              # experts per token
 
     @property
     def packed_cols(self) -> int:
@@ -81,6 +84,11 @@ WORKLOADS = {
     # Embedding table: 4-bit g64 [32768, 4096], 4096 uniform-random gathered rows.
     "rows_4bit_g64_32768x4096": Workload("rows_4bit_g64_32768x4096", 4, 64, 32768, 4096,
                                          (1e-3, 2e-2), (-0.15, 0.0), n_indices=4096),
+    # Mixture of experts (gathered products): 128 experts of W [768, 2048] at 4-bit g64, 8 experts
+    # per token; 1 token (a single decode step) and 64 tokens (a decode batch), rows sorted by expert.
+    "moe_4bit_g64_e128_768x2048": Workload("moe_4bit_g64_e128_768x2048", 4, 64, 768, 2048,
+                                           (1e-3, 2e-2), (-0.15, 0.0), ms=(1, 64), seed=41,
+                                           experts=128, top_k=8),
 }
 
 
@@ -155,3 +163,43 @@ def random_inputs(bits: int, group_size: int, n: int, k: int, m: int, x_dtype: s
     wl = Workload(f"random_{bits}bit_g{group_size}_{n}x{k}", bits, group_size, n, k,
                   scale_range, bias_range, ms=(m,), x_dtype=x_dtype, seed=seed)
     return make_inputs(wl, m=m)
+
+
+@dataclasses.dataclass
+class MoeInputs:
+    """One draw of a mixture-of-experts workload, rows grouped by expert.
+
+    packed  uint32 [experts, n, k*bits/32];  scales, biases uint16 (bf16 bits) [experts, n, k/G]
+    x       uint16 (bf16 bits) [tokens, k]: the tokens' activations
+    token   uint32 [rows]: the token of each row (rows = tokens * top_k), in expert order
+    expert  uint32 [rows]: the expert of each row, non-decreasing
+    x_rows  uint16 [rows, 1, k]: x[token], the product's input with its rows in expert order
+    """
+    wl: Workload
+    packed: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray
+    x: np.ndarray
+    token: np.ndarray
+    expert: np.ndarray
+    x_rows: np.ndarray
+
+
+def moe_inputs(wl: Workload, tokens: int, experts: Optional[int] = None, n: Optional[int] = None,
+               k: Optional[int] = None, seed: Optional[int] = None) -> MoeInputs:
+    """Experts' weights, token activations and a random routing: each token picks top_k distinct
+    experts uniformly (a stand-in for a router's choice); the (token, expert) rows are then ordered
+    by expert, ties by token, as a layer does before a sorted gathered product."""
+    E = wl.experts if experts is None else experts
+    n = wl.n if n is None else n
+    k = wl.k if k is None else k
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    packed, scales, biases = draw_weights(rng, E * n, k, wl.bits, wl.group_size, wl.scale_range, wl.bias_range)
+    x = draw_x(rng, tokens, k, "bf16")
+    choice = np.argsort(rng.random((tokens, E)), axis=1)[:, :min(wl.top_k, E)]
+    tok = np.repeat(np.arange(tokens, dtype=np.uint32), choice.shape[1])
+    exp = choice.reshape(-1).astype(np.uint32)
+    order = np.lexsort((tok, exp))
+    tok, exp = tok[order], exp[order]
+    return MoeInputs(wl, packed.reshape(E, n, -1), scales.reshape(E, n, -1), biases.reshape(E, n, -1), x,
+                     tok, exp, x[tok][:, None, :])

@@ -184,3 +184,35 @@ def test_fused_decode_checks(lib):
     # nothing to write
     assert gate_up(lib, m=0, x=NULL, gy=NULL, uy=NULL) == OK
     assert silu(lib, n=0, gate=NULL, upv=NULL, y=NULL) == OK
+
+
+def gather(lib, xb=2, m=1, wb=3, n=4, k=512, G=64, bits=4, lhs=NULL, rhs=A16, batch=2, sorted_=0, x=A16,
+           y=A16, dtype=BF16, path=0, packed=A16, scales=A16):
+    return lib.qaff_gather_qmm_ex(x, dtype, xb, m, packed, scales, A16, wb, n, k, G, bits, lhs, rhs, batch,
+                                  sorted_, y, NULL, path)
+
+
+def test_gather_qmm_checks(lib):
+    assert gather(lib, xb=-1) == INVALID
+    assert gather(lib, batch=-1) == INVALID
+    assert gather(lib, bits=7) == UNSUPPORTED
+    assert gather(lib, G=48) == INVALID
+    assert gather(lib, packed=NULL) == INVALID                # the stacked weight is checked
+    assert gather(lib, lhs=NULL, batch=3) == INVALID          # no lhs: batch <= x batches
+    assert b"lhs" in lib.qaff_last_error()
+    assert gather(lib, rhs=NULL, batch=4) == INVALID          # no rhs: batch <= weight batches
+    assert gather(lib, rhs=A2) == INVALID                     # indices are 4-byte aligned
+    assert gather(lib, lhs=A2) == INVALID
+    assert gather(lib, path=2) == UNSUPPORTED                 # no GEMM for gathered products
+    assert gather(lib, path=9) == INVALID
+    assert gather(lib, path=3, dtype=F32) == UNSUPPORTED      # the matrix-core kernel takes bf16
+    assert gather(lib, path=3, k=320, G=64) == UNSUPPORTED    # ... and k a multiple of 512
+    assert gather(lib, path=3, scales=A2) == UNSUPPORTED      # ... and 4-byte aligned scales
+    assert gather(lib, y=NULL) == INVALID
+    assert gather(lib, y=A4) == INVALID
+    assert gather(lib, x=A2) == INVALID
+    assert gather(lib, xb=1 << 32) == UNSUPPORTED
+    # nothing to write
+    assert gather(lib, batch=0, x=NULL, y=NULL) == OK
+    assert gather(lib, m=0, x=NULL, y=NULL) == OK
+    assert gather(lib, n=0, x=NULL, y=NULL) == OK

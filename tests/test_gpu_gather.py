@@ -1,0 +1,245 @@
+"""Gathered quantized products (mixture-of-experts batches) on the GPU against the CPU oracle,
+through the C ABI (via the binding).
+
+Output batch i is x[lhs[i]] . dequantize(W[rhs[i]])^T. The bars are those of the plain product:
+per-row max relative error against the float64 oracle of at most 2e-3 (float32 y) and 1.6e-2
+(bf16 y), and the tighter bound from the kernel's own arithmetic (1e-4 / 4e-3) against the oracle
+composed the way the kernel computes: float32 weights for the VALU GEMV, weights rounded to bf16
+for the matrix-core kernel. An index past its operand gives a NaN batch on both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc_mod
+from gpu_util import banner, dev_bf16, dev_u32, dev_x, host_f64
+from quantized_matmul_mlx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-3, "bf16": 1.6e-2}
+TIGHT = {"f32": 1e-4, "bf16": 4e-3}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc_mod.build()
+    import quantized_matmul_mlx_amd as q
+    q._lib.load()
+    return orc_mod
+
+
+def qaff():
+    import quantized_matmul_mlx_amd as q
+    return q
+
+
+def experts(bits, G, E, n, k, seed):
+    """E random experts [n, k], stacked, with the decode workload's distributions."""
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=seed)
+    return inp.packed.reshape(E, n, -1), inp.scales.reshape(E, n, -1), inp.biases.reshape(E, n, -1)
+
+
+def draw_x(shape, x_dtype, seed):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    return W.bf16_bits_from_f32(x) if x_dtype == "bf16" else x
+
+
+def bf16_weight_gather_ref(orc, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs):
+    """Batch i: x[lhs[i]] . bf16(W[rhs[i]])^T in float64 (NaN past either operand)."""
+    out = []
+    for li, ri in zip(lhs, rhs):
+        if li >= x.shape[0] or ri >= packed.shape[0]:
+            out.append(np.full((x.shape[1], packed.shape[1]), np.nan))
+            continue
+        w = orc.bf16_to_f32(orc.dequantize(packed[ri], scales[ri], biases[ri], G, bits, out="bf16"))
+        xs = orc.bf16_to_f32(x[li]) if x_dtype == "bf16" else x[li]
+        out.append(xs.astype(np.float64) @ w.astype(np.float64).T)
+    return np.stack(out)
+
+
+def run(x, x_dtype, packed, scales, biases, G, bits, lhs=None, rhs=None, sorted_=False, path="auto"):
+    xd = dev_x(x, x_dtype)
+    y = qaff().gather_qmm(xd, dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits,
+                          lhs_indices=None if lhs is None else dev_u32(lhs),
+                          rhs_indices=None if rhs is None else dev_u32(rhs), sorted_indices=sorted_, path=path)
+    torch.cuda.synchronize()
+    return host_f64(y)
+
+
+def check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, kernel):
+    """got [batch, m, n] against the oracle; lhs/rhs are the explicit (expanded) index arrays."""
+    ref = orc.gather_qmm(x, x_dtype, packed, scales, biases, G, bits, lhs=lhs, rhs=rhs)
+    assert got.shape == ref.shape
+    nan = np.isnan(ref).all(axis=(1, 2))
+    assert np.isnan(got[nan]).all(), "out-of-range batches must be NaN"
+    assert np.isfinite(got[~nan]).all()
+    g2 = got[~nan].reshape(-1, got.shape[-1])
+    r2 = ref[~nan].reshape(-1, ref.shape[-1])
+    if g2.size == 0:
+        return
+    err = orc.max_row_rel_err(g2, r2)
+    assert err <= TOL[x_dtype], f"max row rel err {err:.3e} > {TOL[x_dtype]}"
+    if kernel == "gemv_mfma":
+        tref = bf16_weight_gather_ref(orc, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs)
+        tref = tref[~nan].reshape(-1, ref.shape[-1])
+    else:
+        tref = r2
+    terr = orc.max_row_rel_err(g2, tref)
+    assert terr <= TIGHT[x_dtype], f"{kernel}: max row rel err {terr:.3e} against its own arithmetic"
+
+
+# ---- batched: any lhs / rhs ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,G,x_dtype,m", [(4, 64, "bf16", 1), (3, 32, "f32", 3), (8, 128, "bf16", 2),
+                                              (6, 32, "bf16", 5), (2, 64, "f32", 1), (5, 128, "bf16", 17)])
+def test_gather_valu_batched(orc, bits, G, x_dtype, m):
+    E, n, k = 4, 150, 640   # 20 blocks of 32 per row: not a whole pass of the GEMV
+    packed, scales, biases = experts(bits, G, E, n, k, seed=100 + bits)
+    x = draw_x((3, m, k), x_dtype, seed=200 + bits)
+    lhs = np.array([2, 0, 0, 1, 2, 1, 0], np.uint32)
+    rhs = np.array([3, 3, 0, 2, 1, 0, 1], np.uint32)
+    banner(f"gather valu batched bits={bits} G={G} {x_dtype} m={m}")
+    got = run(x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, path="gemv")
+    check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, "gemv")
+
+
+@pytest.mark.parametrize("bits,G,m,k", [(4, 64, 1, 512), (4, 128, 5, 2048), (3, 32, 16, 1024), (8, 64, 20, 512),
+                                        (6, 32, 4, 4096), (2, 128, 9, 1536), (5, 64, 33, 512)])
+def test_gather_mfma_batched(orc, bits, G, m, k):
+    E, n = 5, 150
+    packed, scales, biases = experts(bits, G, E, n, k, seed=300 + bits)
+    x = draw_x((4, m, k), "bf16", seed=400 + m)
+    lhs = np.array([3, 0, 0, 2, 1, 3], np.uint32)
+    rhs = np.array([4, 4, 1, 0, 2, 3], np.uint32)
+    banner(f"gather mfma batched bits={bits} G={G} m={m} k={k}")
+    got = run(x, "bf16", packed, scales, biases, G, bits, lhs, rhs, path="gemv_mfma")
+    check(orc, got, x, "bf16", packed, scales, biases, G, bits, lhs, rhs, "gemv_mfma")
+
+
+# ---- grouped: sorted rhs, one row per batch, each expert's weights read once -----------------------
+
+def sorted_rows(counts):
+    return np.repeat(np.arange(len(counts), dtype=np.uint32), counts)
+
+
+@pytest.mark.parametrize("bits,G,k,counts", [
+    (4, 64, 2048, [0, 3, 20, 1, 0, 16]),         # empty experts, one of several tiles, one of a tile
+    (4, 32, 512, [1, 1, 1, 1, 1, 1, 1, 1]),      # one row each
+    (8, 128, 1024, [40, 0, 0, 2]),               # several tiles of 16
+    (3, 32, 4096, [5, 9, 0, 0, 0, 7]),
+    (6, 64, 1536, [0, 0, 0, 0, 0, 0, 0, 12]),    # only the last expert
+    (2, 64, 512, [33]),
+])
+def test_gather_mfma_grouped(orc, bits, G, k, counts):
+    E, n = len(counts), 100
+    packed, scales, biases = experts(bits, G, E, n, k, seed=500 + bits)
+    rhs = sorted_rows(counts)
+    x = draw_x((rhs.size, 1, k), "bf16", seed=600 + k)
+    banner(f"gather mfma grouped bits={bits} G={G} k={k} counts={counts}")
+    got = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemv_mfma")
+    check(orc, got, x, "bf16", packed, scales, biases, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs,
+          "gemv_mfma")
+    # the grouped walk and the batched kernel compute each row the same way
+    got_b = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=False, path="gemv_mfma")
+    np.testing.assert_array_equal(got, got_b)
+
+
+def test_gather_grouped_rows_past_every_expert_are_nan(orc):
+    E, n, k, G, bits = 3, 40, 512, 64, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=700)
+    rhs = np.array([0, 0, 2, 2, 2, 3, 7, 7], np.uint32)  # the last three are past the experts
+    x = draw_x((rhs.size, 1, k), "bf16", seed=701)
+    banner("gather mfma grouped, rows past every expert")
+    got = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemv_mfma")
+    check(orc, got, x, "bf16", packed, scales, biases, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs,
+          "gemv_mfma")
+    assert np.isnan(got[5:]).all() and np.isfinite(got[:5]).all()
+
+
+@pytest.mark.parametrize("path,x_dtype", [("gemv", "bf16"), ("gemv", "f32"), ("gemv_mfma", "bf16")])
+def test_gather_batched_out_of_range_is_nan(orc, path, x_dtype):
+    E, n, k, G, bits = 2, 70, 512, 32, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=710)
+    x = draw_x((2, 3, k), x_dtype, seed=711)
+    lhs = np.array([0, 2, 1, 1], np.uint32)
+    rhs = np.array([1, 0, 5, 0], np.uint32)
+    banner(f"gather out of range {path} {x_dtype}")
+    got = run(x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, path=path)
+    check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, path)
+    assert np.isnan(got[1]).all() and np.isnan(got[2]).all()
+
+
+def test_gather_auto_picks_a_tested_kernel(orc):
+    E, n, k, G, bits = 8, 96, 1024, 64, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=720)
+    rhs = sorted_rows([2, 1, 0, 3, 1, 1, 0, 2])
+    x = draw_x((rhs.size, 1, k), "bf16", seed=721)
+    banner("gather auto vs forced")
+    # sorted, one row per batch, at least one row per expert on average: the grouped walk
+    auto = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True)
+    forced = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemv_mfma")
+    np.testing.assert_array_equal(auto, forced)
+    # unsorted promise, m = 1: the VALU GEMV
+    auto = run(x, "bf16", packed, scales, biases, G, bits, None, rhs)
+    forced = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, path="gemv")
+    np.testing.assert_array_equal(auto, forced)
+
+
+def test_gather_binding_broadcasts_and_defaults(orc):
+    E, n, k, G, bits = 3, 50, 512, 32, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=730)
+    x = draw_x((2, 2, k), "bf16", seed=731)
+    lhs = np.array([[1], [0]], np.uint32)
+    rhs = np.array([2, 0, 1], np.uint32)
+    banner("gather broadcast")
+    q = qaff()
+    y = q.gather_qmm(dev_x(x, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits,
+                     lhs_indices=dev_u32(lhs), rhs_indices=dev_u32(rhs))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 3, 2, n)
+    ref = orc.gather_qmm(x, "bf16", packed, scales, biases, G, bits, lhs=lhs, rhs=rhs)
+    assert orc.max_row_rel_err(host_f64(y).reshape(-1, n), ref.reshape(-1, n)) <= TOL["bf16"]
+    # both defaults: batch i of x with expert i (three of each)
+    x3 = draw_x((3, 1, k), "bf16", seed=732)
+    y3 = q.gather_qmm(dev_x(x3, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits)
+    torch.cuda.synchronize()
+    ref3 = orc.gather_qmm(x3, "bf16", packed, scales, biases, G, bits)
+    assert orc.max_row_rel_err(host_f64(y3).reshape(-1, n), ref3.reshape(-1, n)) <= TOL["bf16"]
+    # int64 indices are read as their uint32 value
+    y4 = q.gather_qmm(dev_x(x, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits,
+                      lhs_indices=torch.from_numpy(lhs.astype(np.int64)).cuda(),
+                      rhs_indices=torch.from_numpy(rhs.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_f64(y4), host_f64(y))
+
+
+def test_gather_empty(orc):
+    packed, scales, biases = experts(4, 64, 2, 8, 512, seed=740)
+    x = draw_x((1, 1, 512), "bf16", seed=741)   # one x batch: broadcasts against no batches
+    banner("gather empty")
+    y = qaff().gather_qmm(dev_x(x, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), 64, 4,
+                          rhs_indices=torch.zeros(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, 1, 8)
+
+
+# ---- the mixture-of-experts workload at full size -----------------------------------------------
+
+@pytest.mark.parametrize("tokens", W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms)
+def test_gather_moe_workload(orc, tokens):
+    wl = W.WORKLOADS["moe_4bit_g64_e128_768x2048"]
+    mi = W.moe_inputs(wl, tokens)
+    banner(f"gather moe workload tokens={tokens} rows={mi.expert.size}")
+    got = run(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits, None, mi.expert,
+              sorted_=True)
+    grouped = mi.expert.size >= wl.experts
+    check(orc, got, mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits,
+          np.arange(mi.expert.size, dtype=np.uint32), mi.expert, "gemv_mfma" if grouped else "gemv")
+    # the same rows through lhs indices (token of each row) into the unpermuted activations
+    got2 = run(mi.x[:, None, :], "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits, mi.token,
+               mi.expert)
+    check(orc, got2, mi.x[:, None, :], "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits,
+          mi.token, mi.expert, "gemv")
