@@ -15,8 +15,9 @@ The same JSON line carries:
     against the 2.5 PFLOP/s dense bf16 MFMA peak;
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
-    product at M = 4, and the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
-    residual), each against its roofline;
+    product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
+    residual, and the mixture-of-experts gathered product gather_qmm at 1 and 64 tokens), each
+    against its roofline;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
     (also given per row).
 
@@ -257,6 +258,52 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
     return row
 
 
+def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget):
+    """A mixture-of-experts gathered product (gather_qmm): 128 experts of W [768, 2048] at 4-bit
+    g64, 8 experts per token, the tokens' rows sorted by expert (rows = 8 * tokens, x [rows, 1, k]).
+    Algorithmic bytes: the weights of the experts in use, x rows, y rows."""
+    import numpy as np
+    import oracle
+    wl = W.WORKLOADS["moe_4bit_g64_e128_768x2048"]
+    mi = W.moe_inputs(wl, tokens)
+    rows = mi.expert.size
+    used = int(np.unique(mi.expert).size)
+    per_expert = wl.n * wl.k * wl.bits // 8 + 2 * wl.n * (wl.k // wl.group_size) * 2
+    nbytes = used * per_expert + rows * wl.k * 2 + rows * wl.n * 2
+    all_bytes = wl.experts * per_expert  # a copy holds every expert
+    copies = copies_for(all_bytes)
+    dev = [{"packed": torch.from_numpy(mi.packed.view(np.int32)).cuda(),
+            "scales": torch.from_numpy(mi.scales.view(np.int16)).cuda().view(torch.bfloat16),
+            "biases": torch.from_numpy(mi.biases.view(np.int16)).cuda().view(torch.bfloat16),
+            "x": torch.from_numpy(mi.x_rows.view(np.int16)).cuda().view(torch.bfloat16)} for _ in range(copies)]
+    rhs = torch.from_numpy(mi.expert.view(np.int32)).cuda()
+    ys = [torch.empty((rows, 1, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = dev[i % copies]
+        q.gather_qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, rhs_indices=rhs,
+                     sorted_indices=True, out=ys[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del dev, ys
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    grouped = rows >= wl.experts
+    row = {"workload": f"gather_qmm {wl.experts} experts [768, 2048] 4-bit g64, top-{wl.top_k}, {tokens} token(s), "
+                       f"{rows} rows sorted by expert ({used} experts in use)",
+           "kernel": "gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)",
+           "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "weight_copies": copies,
+           "roofline": hbm_roofline(gbs)}
+    if cpu:
+        threads = oracle.default_threads()
+        runs, el = cpu_time(lambda: oracle.gather_qmm(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases,
+                                                      wl.group_size, wl.bits, rhs=mi.expert, threads=threads),
+                            cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row
+
+
 def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_budget, gather):
     import oracle
     wl = W.WORKLOADS[name]
@@ -453,6 +500,9 @@ def main():
         for kind in ("gate_up", "silu_gate"):
             log(f"row: fused {kind}")
             rows.append(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
+        for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:
+            log(f"row: gather_qmm, {tokens} token(s)")
+            rows.append(bench_gather(torch, q, W, timer, tokens, rs, rw, cpu, 2.0))
         result["rows"] = rows
 
     # ---- CPU oracle on the host cores (headline workload) ----

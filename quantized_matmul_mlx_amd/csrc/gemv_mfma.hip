@@ -263,21 +263,57 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
 
 // ---- gathered batches ---------------------------------------------------------------------------
 //
-// The same operand layout, with the weight tile dequantized once into registers (16 registers
-// per chunk) and reused for every tile of up to MB x rows: a block owns 16 rows of one weight
-// batch and walks all x rows that use it.
+// The decode kernel's layout over gathered batches: a block owns 16 * NT rows of one weight batch
+// and walks every x row that uses it, in tiles of MB rows; the codes stay in registers across the
+// tiles (each tile dequantizes them again, chunk by chunk, as the decode kernel does).
 //  * Batched: grid y = output batch b; x rows 0 .. m - 1 of batch lhs[b] against weight rhs[b].
 //  * Grouped (rhs sorted, m == 1, no lhs): grid y = expert e; the rows of e are
-//    [#(rhs < e), #(rhs < e + 1)), found by a search over rhs, so each expert's weights are read
-//    once however many rows use it. Expert w_count takes the rows past every expert (NaN).
+//    [#(rhs < e), #(rhs < e + 1)), so each expert's weights are read once however many rows use
+//    it. Expert w_count takes the rows past every expert (NaN).
 // An out-of-range index gives a NaN output batch.
 
-// #(idx[i] < v1) and #(idx[i] < v2) over a sorted idx[0 .. len) (len >= 1): a 64-ary search per
-// bound, both in lockstep so that their loads go out together. Each step probes lo + lane * step;
-// the probes below v are a prefix (the array is sorted), and the bound lies after the last one
-// and no later than the next.
+// #(idx[i] < v1) and #(idx[i] < v2) over a sorted idx[0 .. len), len >= 1.
+//  * len <= 1024: every lane counts 16 consecutive entries (four 16-byte loads, one round trip);
+//    the wave total of a count below 32 is the sum over its bits of the ballot popcounts.
+//  * longer: a 64-ary search per bound, both in lockstep so that their loads go out together.
+//    Each step probes lo + lane * step; the probes below v are a prefix (the array is sorted), and
+//    the bound lies after the last one and no later than the next.
+constexpr uint32_t kCountMax = 1024;
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t c) {  // 0 <= c < 32 in every lane
+    uint32_t t = 0;
+#pragma unroll
+    for (int b = 0; b < 5; ++b)
+        t += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((c >> b) & 1u)) << b;
+    return t;
+}
+
 __device__ __forceinline__ void count_below2(const uint32_t* idx, uint32_t len, uint32_t v1, uint32_t v2,
                                              int lane, uint32_t& c1, uint32_t& c2) {
+    if (len <= kCountMax) {
+        uint32_t a[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t i0 = min((uint32_t)lane * 16 + 4 * q, len - 1);
+            if (i0 + 4 <= len) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(idx + i0);
+                a[4 * q] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[4 * q + e] = idx[min(i0 + e, len - 1)];
+            }
+        }
+        uint32_t n1 = 0, n2 = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const bool in = (uint32_t)lane * 16 + e < len;
+            n1 += (in && a[e] < v1) ? 1u : 0u;
+            n2 += (in && a[e] < v2) ? 1u : 0u;
+        }
+        c1 = wave_total(n1);
+        c2 = wave_total(n2);
+        return;
+    }
     uint32_t lo1 = 0, hi1 = len, lo2 = 0, hi2 = len;
     while (lo1 < hi1 || lo2 < hi2) {
         const uint32_t st1 = (hi1 - lo1 + 63) >> 6, st2 = (hi2 - lo2 + 63) >> 6;
@@ -307,7 +343,7 @@ __device__ __forceinline__ void count_below2(const uint32_t* idx, uint32_t len, 
     c2 = lo2;
 }
 
-template <int BITS, int GSHIFT, int MB>
+template <int BITS, int NT, int GSHIFT, int MB>
 __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
     const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, Gather ga) {
@@ -316,7 +352,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int waves = (int)(kb >> 4);
-    const uint32_t n0 = blockIdx.x * 16;
+    const uint32_t n0 = blockIdx.x * (16 * NT);
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> GSHIFT;
     const int lr16 = lane & 15;
@@ -348,9 +384,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     }
     if (r0 >= r1) return;  // the same in every wave: the whole block returns
     if (nan_rows) {
-        for (uint32_t o = tid; o < (r1 - r0) * 16; o += blockDim.x) {
-            const uint32_t col = n0 + (o & 15);
-            if (col < n) yb[(size_t)(r0 + (o >> 4)) * n + col] = 0x7FC0u;
+        for (uint32_t o = tid; o < (r1 - r0) * 16 * NT; o += blockDim.x) {
+            const uint32_t col = n0 + o % (16 * NT);
+            if (col < n) yb[(size_t)(r0 + o / (16 * NT)) * n + col] = 0x7FC0u;
         }
         return;
     }
@@ -358,37 +394,34 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     const uint16_t* sp = scales + (size_t)wi * ga.sb_stride;
     const uint16_t* bp = biases + (size_t)wi * ga.sb_stride;
 
-    // 2. Loads: the first x tile, the tile row's scale and bias windows, then the codes.
+    // 2. Loads, oldest first: the first x tile, the scale and bias windows, then the codes chunk
+    //    by chunk (as in the decode kernel).
     u32x4a xg[MB];
     const uint16_t* xs = xb + (size_t)wave * kSlice + lane * 8;
 #pragma unroll
     for (int r = 0; r < MB; ++r) xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min(r0 + r, r1 - 1) * k);
-    const uint32_t row = min(n0 + lr16, n - 1);
-    SbWindow<GSHIFT> sw, bw;
-    {
+    SbWindow<GSHIFT> sw[NT], bw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
         const size_t e = (size_t)row * gpr + (size_t)wave * (16 >> GSHIFT);
-        sw.load(sp + e);
-        bw.load(bp + e);
+        sw[t].load(sp + e);
+        bw[t].load(bp + e);
     }
-    uint32_t wq[4][BITS];
+    uint32_t wq[NT][4][BITS];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const uint32_t jb = (uint32_t)wave * 16 + 4 * c + lg;
-        load_block<BITS>(pw + (size_t)row * kb * BITS + (size_t)jb * BITS, wq[c]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
+            const uint32_t jb = (uint32_t)wave * 16 + 4 * c + lg;
+            load_block<BITS>(pw + (size_t)row * kb * BITS + (size_t)jb * BITS, wq[t][c]);
+        }
+        asm volatile("" ::: "memory");
     }
 
-    // 3. Dequantize the tile once.
-    bf16x8 wb[4][4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const float sc = sw.get(c, lg, g_hi);
-        const float bi = bw.get(c, lg, g_hi);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wb[c][j] = dequant8<BITS>(wq[c], j, sc, bi);
-    }
-
-    // 4. Walk the x rows in tiles of MB: x through this wave's LDS region (as in the decode kernel),
-    //    the multiply, and the slices' partial tiles summed through a separate LDS area.
+    // 3. Walk the x rows in tiles of MB: x through this wave's LDS region, the multiply chunk by
+    //    chunk, and the slices' partial tiles summed through a separate LDS area.
     uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
     float* red = reinterpret_cast<float*>(smem + (size_t)waves * (MB * kXPitch));
     const uint8_t* xa = xl + min(lr16, MB - 1) * kXPitch + lg * 64;
@@ -399,48 +432,92 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
         }
 #pragma unroll
         for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc[NT];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            // chunk c's arithmetic starts after chunk c - 1's multiply (see the decode kernel)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(wq[t][c][i]) : "v"(acc[0]));
+            bf16x8 wb[NT][4];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const float sc = sw[t].get(c, lg, g_hi);
+                const float bi = bw[t].get(c, lg, g_hi);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[c][j], acc, 0, 0, 0);
-            }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[(wave * 4 + v) * 64 + lane] = acc[v];
+                for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[((wave * NT + t) * 4 + v) * 64 + lane] = acc[t][v];
         __syncthreads();
-        for (int o = tid; o < 16 * MB; o += (int)blockDim.x) {  // result rows past MB repeat row MB - 1
-            const int mm = o >> 4, nn = o & 15;
+        // result rows past MB repeat row MB - 1: only the first MB are stored
+        for (int o = tid; o < 16 * MB * NT; o += (int)blockDim.x) {
+            const int t = o / (16 * MB), rem = o % (16 * MB);
+            const int mm = rem >> 4, nn = rem & 15;
             const int l = ((mm >> 2) << 4) | nn, v = mm & 3;
             float sum = 0.f;
-            for (int w = 0; w < waves; ++w) sum += red[(w * 4 + v) * 64 + l];
-            const uint32_t r = t0 + (uint32_t)mm, col = n0 + (uint32_t)nn;
+            for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+            const uint32_t r = t0 + (uint32_t)mm, col = n0 + 16 * t + (uint32_t)nn;
             if (r < r1 && col < n) yb[(size_t)r * n + col] = to_bf16_bits(sum);
         }
         __syncthreads();  // red is written again by the next tile
     }
 }
 
-template <int BITS, int GSHIFT, int MB>
-hipError_t launch_gather_mb(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+template <int BITS, int NT, int GSHIFT, int MB>
+hipError_t launch_gather_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                             const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, const Gather& ga,
                             hipStream_t stream) {
     const int waves = (int)(kb / 16);
-    const size_t lds = (size_t)waves * MB * kXPitch + (size_t)waves * 4 * 64 * sizeof(float);
-    const unsigned gx = (unsigned)((n + 15) / 16);
+    const size_t lds = (size_t)waves * MB * kXPitch + (size_t)waves * NT * 4 * 64 * sizeof(float);
+    const unsigned gx = (unsigned)((n + 16 * NT - 1) / (16 * NT));
     // grid y: output batches, or experts 0 .. w_count when grouped
     const uint64_t count = ga.grouped ? (uint64_t)ga.w_count + 1 : ga.batch;
     for (uint64_t b0 = 0; b0 < count; b0 += 65535) {
         Gather g = ga;
         g.b0 = (uint32_t)b0;
         const unsigned gy = (unsigned)(count - b0 < 65535 ? count - b0 : 65535);
-        gemv_mfma_gather_kernel<BITS, GSHIFT, MB><<<dim3(gx, gy), dim3(waves * 64), lds, stream>>>(
+        gemv_mfma_gather_kernel<BITS, NT, GSHIFT, MB><<<dim3(gx, gy), dim3(waves * 64), lds, stream>>>(
             x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+template <int BITS, int GSHIFT, int MB>
+hipError_t launch_gather_mb(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                            const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, const Gather& ga,
+                            hipStream_t stream) {
+    // Row tiles per block as in the decode kernel: enough that the blocks with work fit in one
+    // round of the compute units (a block's x regions set how many fit on one).
+    const int64_t waves = kb / 16;
+    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch + waves * 4 * 1024);
+    if (per_cu < 1) per_cu = 1;
+    if (per_cu > 4) per_cu = 4;
+    const int64_t slots = (int64_t)device_cu_count() * per_cu;
+    const int64_t batches = ga.grouped ? (ga.batch < ga.w_count ? ga.batch : ga.w_count) : ga.batch;
+    const int64_t tiles = ((n + 15) / 16) * (batches > 0 ? batches : 1);
+    int64_t nt = (tiles + slots - 1) / slots;
+#ifdef QAFF_GATHER_NT
+    nt = QAFF_GATHER_NT;
+#endif
+    // at most two tiles (measured on 128 experts of [768, 2048] 4-bit, 512 and 4096 sorted rows:
+    // two tiles 40 and 86 us, four 43 and 116 us, one 42 and 114 us)
+    if (nt <= 1) return launch_gather_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, ga, stream);
+    return launch_gather_nt<BITS, 2, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, ga, stream);
 }
 
 template <int BITS, int GSHIFT>
