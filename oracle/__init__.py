@@ -21,6 +21,9 @@ patterns. What each function computes, and the page passage it follows, is docum
   ``gather_qmm`` and ``gather_indices``).
 * ``silu_gate`` / ``silu_gate_qmm`` -- the fused decode products' activation and product
   (spark_runtime ``gemv_silu_gate``).
+* ``quantize`` -- w -> packed codes, bf16 scales and biases: bias = group min, scale =
+  (max - min) / (2^bits - 1), code = round((w - bias) / scale) clamped (nuvec_core module
+  documentation and ``quantize``; rlx-moshi: bias = group min).
 """
 from __future__ import annotations
 
@@ -79,11 +82,12 @@ def _load():
                             _int, _f64p, _int]
     lib.orc_gather_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
                                    _i64, _int, ctypes.c_void_p, ctypes.c_void_p, _i64, _f64p, _int]
+    lib.orc_quantize.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, _u16p, _u16p]
     lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
     lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
-                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm"):
+                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize"):
         getattr(lib, name).restype = _int
     for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate"):
         getattr(lib, name).restype = None
@@ -286,6 +290,26 @@ def gather_qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: i
                                   group_size, bits, li.ctypes.data, ri.ctypes.data, li.size, out,
                                   threads or default_threads()), "gather_qmm")
     return out.reshape(tuple(shape) + (m, n))
+
+
+def quantize(w, w_dtype: str, group_size: int, bits: int):
+    """(packed uint32 [rows, cols*bits/32], scales bf16 bits [rows, cols/G], biases bf16 bits) of a
+    [rows, cols] weight given as float32 (``w_dtype="f32"``) or bf16 bit patterns ("bf16")."""
+    if w_dtype == "bf16":
+        wa = _c(np.atleast_2d(w), np.uint16)
+    elif w_dtype == "f32":
+        wa = _c(np.atleast_2d(w), np.float32)
+    else:
+        raise ValueError(w_dtype)
+    rows, cols = wa.shape
+    if group_size <= 0 or cols % group_size or (cols * bits) % 32:
+        raise ValueError("cols must be a multiple of the group size")
+    packed = np.empty((rows, cols * bits // 32), np.uint32)
+    sc = np.empty((rows, cols // group_size), np.uint16)
+    bi = np.empty((rows, cols // group_size), np.uint16)
+    _check(_load().orc_quantize(wa.ctypes.data, 1 if w_dtype == "bf16" else 0, rows, cols, group_size, bits,
+                                packed, sc, bi), "quantize")
+    return packed, sc, bi
 
 
 def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:

@@ -4,6 +4,8 @@
  *   - gathered rows:     out[i,:] = dequantize(table)[idx[i], :]
  *   - quantized matmul:  y[m,n] = sum_k x[m,k] * w[n,k]      (y = x . dequantize(W)^T)
  *   - gathered matmul:   y[i] = x[lhs[i]] . dequantize(W[rhs[i]])^T  (mixture-of-experts batches)
+ *   - quantize:          bias = group min, scale = (max - min) / (2^bits - 1), code =
+ *                        round((w - bias) / scale) clamped to [0, 2^bits - 1]
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's CPU-baseline leg
  * may load this library. The HIP library never calls it and shares no code, header, table or
@@ -25,7 +27,9 @@
  *            (group sizes, bit widths), `dequantize` and `quantized_matmul` (x . dequantize(w)^T
  *            without materialising the dequantized matrix), `gather_indices` (indices as uint32;
  *            either index array defaults to every batch in order) and `gather_qmm` (output batch i
- *            is x[lhs[i]] . dequantize(w[rhs[i]])^T over flattened batch dimensions).
+ *            is x[lhs[i]] . dequantize(w[rhs[i]])^T over flattened batch dimensions), module
+ *            documentation of quantization (a value is stored as round((w - bias) / scale),
+ *            clamped to [0, 2^bits - 1]) and `quantize`.
  *   [maya2]  maya2_mlx, quant.py: `mm` (x @ W.T for a quantized weight) and `rows` (an embedding
  *            lookup that dequantizes only the gathered rows).
  *   [spark]  spark_runtime, weights/mlx_int8.rs: module documentation (8-bit words hold four bytes,
@@ -346,4 +350,56 @@ int orc_gather_qmm(const void* x, int x_is_bf16, int64_t x_batches, int64_t m, c
         if (rc != 0) return rc;
     }
     return 0;
+}
+
+/* [nuvec] quantize with [moshi]'s bias: each group of G values of a row, in the pages' order:
+ *   bias  = the group minimum;
+ *   scale = (max - min) / (2^bits - 1), the smallest step whose codes 0 .. 2^bits - 1 reach the
+ *           group maximum from its minimum (the pages state no formula: this is the reading);
+ *   both stored as bf16 (round to nearest even), the dtype the kernels consume;
+ *   code  = round((w - bias) / scale) with the stored bias and scale, rounded half away from zero
+ *           (the Rust `round` of the page), clamped to [0, 2^bits - 1]; a group whose stored scale
+ *           is 0 (all values equal) takes code 0, so it dequantizes to the bias exactly.
+ * Every step is float32 (w widened exactly from bf16, or as given), as the kernels take the same
+ * decisions. Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
+ * Returns 0, or -1 for parameters outside the format. */
+int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64_t group, int bits,
+                 uint32_t* packed, uint16_t* scales, uint16_t* biases) {
+    if (rows < 0 || bits > 8 || group > 128 || !valid_params(cols, group, bits)) return -1;
+    uint8_t* codes = (uint8_t*)malloc((size_t)(rows * cols > 0 ? rows * cols : 1));
+    if (!codes) return -2;
+    const float top = (float)((1 << bits) - 1);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < cols / group; ++g) {
+            float v[128];
+            for (int64_t j = 0; j < group; ++j) {
+                const int64_t i = r * cols + g * group + j;
+                v[j] = w_is_bf16 ? bf16_to_f32(((const uint16_t*)w)[i]) : ((const float*)w)[i];
+            }
+            float lo = v[0], hi = v[0];
+            for (int64_t j = 1; j < group; ++j) {
+                if (v[j] < lo) lo = v[j];
+                if (v[j] > hi) hi = v[j];
+            }
+            const float range = hi - lo;
+            const uint16_t sb = f32_to_bf16_rne(range / top);
+            const uint16_t bb = f32_to_bf16_rne(lo);
+            scales[r * (cols / group) + g] = sb;
+            biases[r * (cols / group) + g] = bb;
+            const float sc = bf16_to_f32(sb), bi = bf16_to_f32(bb);
+            for (int64_t j = 0; j < group; ++j) {
+                float c = 0.0f;
+                if (sc != 0.0f) {
+                    const float diff = v[j] - bi;
+                    const float q = diff / sc;
+                    c = roundf(q);
+                    if (!(c >= 0.0f)) c = 0.0f; /* also a NaN quotient */
+                    if (c > top) c = top;
+                }
+                codes[r * cols + g * group + j] = (uint8_t)c;
+            }
+        }
+    const int rc = orc_pack_codes(codes, rows, cols, bits, packed);
+    free(codes);
+    return rc;
 }

@@ -497,3 +497,107 @@ def test_gather_qmm_out_of_range_is_nan(oracle_lib):
                               rhs=np.array([1, 0, 2], np.uint32))
     assert np.isnan(y[1]).all() and np.isnan(y[2]).all()
     np.testing.assert_array_equal(y[0], oracle_lib.qmm(x[0], "f32", packed[1], sc[1], bi[1], 64, 8))
+
+
+# ---- quantize -----------------------------------------------------------------------------------
+
+def test_quantize_module_example_shapes(oracle_lib):
+    # nuvec_core module example: w[i] = i / 64 as [4, 64], group 64, 4 bits -> 8 words per row
+    w = (np.arange(256, dtype=np.float32) / 64).reshape(4, 64)
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 64, 4)
+    assert packed.shape == (4, 8) and sc.shape == (4, 1) and bi.shape == (4, 1)
+    restored = oracle_lib.dequantize(packed, sc, bi, 64, 4)
+    assert restored.shape == w.shape
+    # bias = the group minimum (row r starts at r, exact in bf16)
+    assert list(W.f32_from_bf16_bits(bi[:, 0])) == [0.0, 1.0, 2.0, 3.0]
+
+
+def test_quantize_then_gather_qmm_worked_example(oracle_lib):
+    # the page's two-expert example end to end, now with quantize: experts of all ones and all
+    # twos must dequantize exactly for the printed 128 = 64 * 2
+    g = golden("gather_qmm_two_experts.txt")
+    E, n, k = int(g["experts"][0]), int(g["n"][0]), int(g["k"][0])
+    G, bits = int(g["group_size"][0]), int(g["bits"][0])
+    w = np.concatenate([np.full((n, k), e + 1.0, np.float32) for e in range(E)])
+    packed, sc, bi = oracle_lib.quantize(w, "f32", G, bits)
+    assert np.all(oracle_lib.dequantize(packed, sc, bi, G, bits) == w)
+    x = np.ones((int(g["tokens"][0]), 1, k), np.float32)
+    y = oracle_lib.gather_qmm(x, "f32", packed.reshape(E, n, -1), sc.reshape(E, n, -1), bi.reshape(E, n, -1),
+                              G, bits, rhs=np.array([int(v) for v in g["rhs"]], np.uint32))
+    assert list(y.shape) == [int(v) for v in g["shape"]]
+    assert list(y.reshape(-1)[:5]) == [float(v) for v in g["expect_first5"]]
+
+
+@pytest.mark.parametrize("bits,G,step,base", [(4, 32, 0.25, 0.5), (8, 128, 2.0 ** -4, -1.0),
+                                              (3, 64, 0.75, -3.0), (2, 32, 4.0, 8.0), (6, 64, 2.0 ** -6, 0.0)])
+def test_quantize_exact_grid(oracle_lib, bits, G, step, base):
+    # values on the grid base + step * c, with both extreme codes present: quantize must return
+    # exactly that step, that base and those codes (a denominator of 2^bits, a bias other than
+    # the minimum, or another packing order fails here)
+    top = 2 ** bits - 1
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, top + 1, size=(3, 2 * G)).astype(np.uint8)
+    codes[:, 0], codes[:, 1], codes[:, G], codes[:, G + 1] = 0, top, top, 0
+    w = (base + step * codes.astype(np.float64)).astype(np.float32)
+    assert np.all(w.astype(np.float64) == base + step * codes)          # exact in float32
+    wb = W.bf16_bits_from_f32(w)
+    assert np.all(W.f32_from_bf16_bits(wb) == w)                         # and in bf16
+    for dt, wi in (("f32", w), ("bf16", wb)):
+        packed, sc, bi = oracle_lib.quantize(wi, dt, G, bits)
+        assert np.all(W.f32_from_bf16_bits(sc) == step) and np.all(W.f32_from_bf16_bits(bi) == base)
+        np.testing.assert_array_equal(oracle_lib.unpack_codes(packed, 2 * G, bits), codes)
+
+
+def test_quantize_ties_round_away_from_zero(oracle_lib):
+    # min 0, max 15 at 4 bits: scale exactly 1, so each value is its own quotient
+    vals = [0.0, 15.0, 2.5, 3.5, 7.5, 14.5, 0.5, 1.25, 6.75] + [5.0] * 23
+    w = np.array([vals], np.float32)
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 32, 4)
+    assert W.f32_from_bf16_bits(sc)[0, 0] == 1.0 and W.f32_from_bf16_bits(bi)[0, 0] == 0.0
+    codes = oracle_lib.unpack_codes(packed, 32, 4)[0]
+    assert list(codes[:9]) == [0, 15, 3, 4, 8, 15, 1, 1, 7]   # halves go up; ties-to-even would give 2, 4, 8, 14, 0
+
+
+def test_quantize_clamps(oracle_lib):
+    # the stored bias rounds above the minimum (1.005 -> bf16 1.0078125): the minimum's quotient
+    # is negative and clamps to 0; the scale rounds so that the maximum's quotient passes 2^bits - 1
+    w = np.linspace(1.005, 1.9, 32, dtype=np.float32)[None, :]
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 32, 4)
+    b = W.f32_from_bf16_bits(bi)[0, 0]
+    assert b > w.min()
+    codes = oracle_lib.unpack_codes(packed, 32, 4)[0]
+    assert codes[0] == 0 and codes.max() <= 15
+    s = W.f32_from_bf16_bits(sc)[0, 0]
+    if (w.max() - b) / s > 15:
+        assert codes[-1] == 15
+
+
+def test_quantize_constant_and_zero_groups(oracle_lib):
+    w = np.zeros((2, 64), np.float32)
+    w[0, :32] = -0.375
+    w[1, 32:] = 3.0
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 32, 5)
+    assert not sc.any()                                     # every group is constant: scale 0
+    assert not packed.any()                                 # ... and code 0
+    np.testing.assert_array_equal(oracle_lib.dequantize(packed, sc, bi, 32, 5), w)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (2, 64), (5, 32), (6, 128)])
+def test_quantize_round_trip_bound(oracle_lib, bits, G):
+    # |dequantize(quantize(w)) - w| <= scale / 2 plus what storing the bias and scale in bf16
+    # moves the grid by (|bias - min| and (2^bits - 1) |scale - range / (2^bits - 1)|)
+    rng = np.random.default_rng(100 + bits)
+    w = (rng.standard_normal((16, 4 * G)) * 0.02).astype(np.float32)
+    packed, sc, bi = oracle_lib.quantize(w, "f32", G, bits)
+    r = oracle_lib.dequantize(packed, sc, bi, G, bits).astype(np.float64)
+    top = 2 ** bits - 1
+    wg = w.reshape(16, -1, G).astype(np.float64)
+    lo, hi = wg.min(-1), wg.max(-1)
+    s = W.f32_from_bf16_bits(sc).astype(np.float64)
+    b = W.f32_from_bf16_bits(bi).astype(np.float64)
+    bound = s / 2 + np.abs(b - lo) + top * np.abs(s - (hi - lo) / top) + 1e-7
+    err = np.abs(r.reshape(16, -1, G) - wg).max(-1)
+    assert np.all(err <= bound), float((err - bound).max())
+    # codes use the whole range: the minimum's code is 0 and the maximum's is 2^bits - 1 or one below
+    codes = oracle_lib.unpack_codes(packed, 4 * G, bits).reshape(16, -1, G)
+    assert np.all(codes.min(-1) == 0) and np.all(codes.max(-1) >= top - 1)
