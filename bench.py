@@ -16,8 +16,8 @@ The same JSON line carries:
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
     product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
-    residual, and the mixture-of-experts gathered product gather_qmm at 1 and 64 tokens), each
-    against its roofline;
+    residual, quantize of a bf16 [4096, 4096] weight, and the mixture-of-experts gathered product
+    gather_qmm at 1 and 64 tokens), each against its roofline;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
     (also given per row).
 
@@ -304,6 +304,33 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget):
     return row
 
 
+def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
+    """quantize of a dense bf16 weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64. Algorithmic bytes:
+    the weight read, the codes, scales and biases written."""
+    import numpy as np
+    import oracle
+    wl = W.WORKLOADS["quantize_4bit_g64_4096x4096"]
+    w = W.dense_weight(wl.n, wl.k, "bf16", seed=wl.seed)
+    nbytes = wl.n * wl.k * 2 + wl.n * wl.k * wl.bits // 8 + 2 * wl.n * (wl.k // wl.group_size) * 2
+    copies = copies_for(nbytes)
+    ws = [torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(copies)]
+
+    def launch(i):
+        q.quantize(ws[i % copies], wl.group_size, wl.bits)
+
+    ms = timer(launch, steps, warmup)
+    del ws
+    torch.cuda.empty_cache()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    row = {"workload": "quantize bf16 [4096, 4096] -> 4-bit g64", "kernel": "quantize_kernel",
+           "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
+    if cpu:
+        runs, el = cpu_time(lambda: oracle.quantize(w, "bf16", wl.group_size, wl.bits), cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row
+
+
 def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_budget, gather):
     import oracle
     wl = W.WORKLOADS[name]
@@ -500,6 +527,8 @@ def main():
         for kind in ("gate_up", "silu_gate"):
             log(f"row: fused {kind}")
             rows.append(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
+        log("row: quantize")
+        rows.append(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:
             log(f"row: gather_qmm, {tokens} token(s)")
             rows.append(bench_gather(torch, q, W, timer, tokens, rs, rw, cpu, 2.0))

@@ -70,6 +70,26 @@ qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, cons
                             void* out, qaff_dtype out_dtype, hipStream_t stream);
 
 /*
+ * Quantization of a dense weight into this format (nuvec_core quantized.rs: module documentation
+ * and quantize; rlx-moshi mlx_dequant.rs: the bias is the group minimum). Per group of group_size
+ * values of a row:
+ *   bias  = the group minimum; scale = (max - min) / (2^bits - 1); both stored as bf16 (round to
+ *           nearest even), the scales' type every kernel here consumes;
+ *   code  = round((w - bias) / scale) with the stored bias and scale, half away from zero, clamped
+ *           to [0, 2^bits - 1]; a stored scale of 0 (all values of the group equal) gives code 0,
+ *           so such a group dequantizes to its value exactly.
+ * All steps in float32 (w widened exactly from bf16), the division correctly rounded. NaN or
+ * infinite inputs give unspecified (but in-range) codes.
+ *   w [rows, cols] in w_dtype (float32 or bf16); packed uint32 [rows, cols*bits/32]; scales and
+ *   biases bf16 [rows, cols/group_size]. All caller-owned device buffers.
+ * Errors: as qaff_dequantize (the outputs are checked as a weight), plus INVALID_ARGUMENT for a
+ * null or misaligned (16-byte) w where the size is non-zero.
+ */
+qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols,
+                          int32_t group_size, int32_t bits, uint32_t* packed, uint16_t* scales,
+                          uint16_t* biases, hipStream_t stream);
+
+/*
  * Quantized matmul y = x . dequantize(W)^T without materialising W (nuvec_core quantized_matmul with
  * transpose, for weights stored [out, in]; maya2_mlx mm).
  *   x [m, k] in x_dtype (float32 or bf16); W is packed/scales/biases of shape [n, k];

@@ -11,6 +11,7 @@ bit views are accepted too). A weight is ``scale * code + bias`` of its group.
 
     y = qmm(x, packed, scales, biases, group_size, bits)   # x . dequantize(W)^T, W never dense
     w = dequantize(packed, scales, biases, group_size, bits, out_dtype=torch.bfloat16)
+    packed, scales, biases = quantize(w, group_size, bits)   # bias = group min, bf16 scales
     e = dequant_rows(packed, scales, biases, idx, group_size, bits)   # embedding lookup
     g, u = gemv_gate_up(x, gate_w, up_w, group_size, bits)           # two projections, x read once
     y = gemv_silu_gate(g, u, packed, scales, biases, group_size, bits, resid=r)  # W . (silu(g) * u) + r
@@ -27,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import QaffError
 
-__all__ = ["dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "gather_qmm", "QWeight",
+__all__ = ["quantize", "dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "gather_qmm", "QWeight",
            "QaffError", "gemv_max_m", "gemv_mfma_min_m"]
 
 _PACKED_DTYPES = (torch.int32, torch.uint32)
@@ -106,6 +107,29 @@ def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=tor
         _lib.check(lib.qaff_dequantize(_p(packed), _p(scales), _p(biases), rows, cols, group_size,
                                        bits, _p(out), _OUT_DTYPES[out_dtype], _stream(dev)))
     return out
+
+
+def quantize(w, group_size: int, bits: int):
+    """Quantizes the last axis of a float32 or bf16 weight ``[..., cols]`` (nuvec_core ``quantize``):
+    returns packed uint32 ``[..., cols*bits/32]`` (as int32), and bf16 scales and biases
+    ``[..., cols/group_size]``; bias = group minimum, scale = (max - min) / (2^bits - 1)."""
+    lib = _lib.load()
+    _need(w, "w", tuple(_OUT_DTYPES))
+    dev = w.device
+    if w.dim() < 1:
+        raise ValueError("w must have at least one dimension")
+    cols = w.shape[-1]
+    lead = tuple(w.shape[:-1])
+    rows = math.prod(lead)
+    if group_size <= 0 or cols % group_size:
+        raise ValueError(f"{cols} columns are not a multiple of the group size {group_size}")
+    packed = torch.empty(lead + (cols * bits // 32,), dtype=torch.int32, device=dev)
+    scales = torch.empty(lead + (cols // group_size,), dtype=torch.bfloat16, device=dev)
+    biases = torch.empty(lead + (cols // group_size,), dtype=torch.bfloat16, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_quantize(_p(w), _OUT_DTYPES[w.dtype], rows, cols, group_size, bits, _p(packed),
+                                     _p(scales), _p(biases), _stream(dev)))
+    return packed, scales, biases
 
 
 def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto", out=None):

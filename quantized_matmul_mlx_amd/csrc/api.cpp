@@ -337,6 +337,23 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                               lhs_indices, rhs_indices, batch, sorted_indices, y, stream, QAFF_PATH_AUTO);
 }
 
+qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
+                          int32_t bits, uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {
+    static const char* op = "qaff_quantize";
+    g_error.clear();
+    // the outputs are checked as a weight would be
+    qaff_status st = check_weight(op, packed, scales, biases, rows, cols, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (!valid_dtype(w_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown w dtype %d", op, (int)w_dtype);
+    if (rows == 0 || cols == 0) return QAFF_OK;
+    if (!w) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null w", op);
+    if (!aligned(w, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: w must be 16-byte aligned", op);
+    if (rows * (cols / 32) >= (1LL << 38))
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld is too large", op, (long long)rows, (long long)cols);
+    return after_launch(op, qaff::launch_quantize(w, w_dtype == QAFF_BF16, rows, cols, group_size, bits, packed,
+                                                  scales, biases, stream), stream);
+}
+
 qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
                      const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                      int32_t group_size, int32_t bits, void* y, hipStream_t stream) {

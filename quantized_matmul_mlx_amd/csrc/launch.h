@@ -78,6 +78,11 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                        int group_size, int bits, uint16_t* y, hipStream_t stream);
 
+// packed/scales/biases of a dense [rows, cols] weight (float32 or bf16): bias = group min,
+// scale = (max - min) / (2^bits - 1), both bf16; code = round((w - bias) / scale), clamped.
+hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t cols, int group_size, int bits,
+                           uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream);
+
 // Writes `bytes` zero bytes (bytes % 2 == 0, p 2-byte aligned) with a kernel, so that the call
 // also behaves under stream capture.
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t stream);

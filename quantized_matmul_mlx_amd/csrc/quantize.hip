@@ -1,0 +1,161 @@
+// Quantization of a dense [rows, cols] weight into the packed form (nuvec_core quantized.rs:
+// module documentation and `quantize`; the bias is the group minimum, as rlx-moshi's
+// mlx_dequant.rs doc comment says). Per group of G values of a row:
+//   bias  = the group minimum, scale = (max - min) / (2^bits - 1), both stored as bf16 (RNE);
+//   code  = round((w - bias) / scale), half away from zero, with the stored bias and scale,
+//           clamped to [0, 2^bits - 1]; a stored scale of 0 (a constant group) gives code 0.
+// Every step is float32 (the division correctly rounded), so each code is decided the same way
+// as in a plain float32 evaluation of those formulas.
+//
+// One lane per 32-value block: it loads its block, the G/32 lanes of a group (adjacent, since a
+// row holds a whole number of groups) combine their minima and maxima, and each lane writes its
+// block's `bits` words of the bit stream; the group's first lane writes the scale and bias.
+// Float32 HBM-bound work: a bf16 weight reads 64 bytes and writes 4 * bits bytes per lane.
+#include "launch.h"
+#include "qaff_device.h"
+
+#include <hip/hip_runtime.h>
+
+namespace qaff {
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+// The running minimum and maximum of the group, combined in block order: the value from the
+// later block wins only if it is strictly smaller (larger), which keeps the first of equal
+// values (as a sequential scan does, e.g. between -0 and +0).
+template <int LANES>
+__device__ __forceinline__ void group_min_max(float& lo, float& hi, int lane) {
+#pragma unroll
+    for (int d = 1; d < LANES; d <<= 1) {
+        const float olo = __shfl_xor(lo, d, 64);
+        const float ohi = __shfl_xor(hi, d, 64);
+        const bool later = (lane & d) == 0;  // the other lane holds the later blocks
+        if (later) {
+            lo = olo < lo ? olo : lo;
+            hi = ohi > hi ? ohi : hi;
+        } else {
+            lo = lo < olo ? lo : olo;
+            hi = hi > ohi ? hi : ohi;
+        }
+    }
+}
+
+template <int BITS, int GSHIFT, bool IN_BF16>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, uint64_t blocks,
+                                                                 uint32_t* packed, uint16_t* scales,
+                                                                 uint16_t* biases) {
+    constexpr int kLanes = 1 << GSHIFT;  // lanes (32-value blocks) per group
+    constexpr float kTop = (float)((1 << BITS) - 1);
+    const uint64_t idx = (uint64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const bool live = idx < blocks;  // whole groups are live or not: blocks is a multiple of kLanes
+    const uint64_t src = live ? idx : 0;
+
+    float v[32];
+    if constexpr (IN_BF16) {
+        const u32x4a* p = reinterpret_cast<const u32x4a*>(static_cast<const uint16_t*>(w) + src * 32);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4a a = p[q];
+            const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[8 * q + 2 * e] = __uint_as_float(u[e] << 16);
+                v[8 * q + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+            }
+        }
+    } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(w) + src * 32);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const f32x4 a = p[q];
+            v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+        }
+    }
+
+    float lo = v[0], hi = v[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        lo = v[j] < lo ? v[j] : lo;
+        hi = v[j] > hi ? v[j] : hi;
+    }
+    group_min_max<kLanes>(lo, hi, lane);
+
+    const uint16_t sbits = to_bf16_bits((hi - lo) / kTop);
+    const uint16_t bbits = to_bf16_bits(lo);
+    const float sc = bf16_to_f32(sbits), bi = bf16_to_f32(bbits);
+
+    uint32_t words[BITS];
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) words[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        float c = 0.0f;
+        if (sc != 0.0f) {
+            c = __builtin_roundf((v[j] - bi) / sc);
+            c = c >= 0.0f ? c : 0.0f;  // also a NaN quotient
+            c = c > kTop ? kTop : c;
+        }
+        const uint32_t code = (uint32_t)c;
+        const int p = j * BITS;  // bit position in the block's stream (compile-time after unrolling)
+        words[p >> 5] |= code << (p & 31);
+        if ((p & 31) + BITS > 32) words[(p >> 5) + 1] |= code >> (32 - (p & 31));
+    }
+
+    if (!live) return;
+    uint32_t* out = packed + idx * BITS;
+    if constexpr (BITS == 4) {
+        *reinterpret_cast<u32x4*>(out) = u32x4{words[0], words[1], words[2], words[3]};
+    } else if constexpr (BITS == 8) {
+        *reinterpret_cast<u32x4*>(out) = u32x4{words[0], words[1], words[2], words[3]};
+        *reinterpret_cast<u32x4*>(out + 4) = u32x4{words[4], words[5], words[6], words[7]};
+    } else if constexpr (BITS == 2) {
+        *reinterpret_cast<u32x2*>(out) = u32x2{words[0], words[1]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) out[i] = words[i];
+    }
+    if ((idx & (kLanes - 1)) == 0) {
+        scales[idx >> GSHIFT] = sbits;
+        biases[idx >> GSHIFT] = bbits;
+    }
+}
+
+template <int BITS, int GSHIFT>
+hipError_t launch_g(const void* w, bool in_bf16, uint64_t blocks, uint32_t* packed, uint16_t* scales,
+                    uint16_t* biases, hipStream_t stream) {
+    const unsigned grid = (unsigned)((blocks + kQuantThreads - 1) / kQuantThreads);
+    if (in_bf16)
+        quantize_kernel<BITS, GSHIFT, true><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
+    else
+        quantize_kernel<BITS, GSHIFT, false><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const void* w, bool in_bf16, uint64_t blocks, uint32_t gshift, uint32_t* packed,
+                       uint16_t* scales, uint16_t* biases, hipStream_t stream) {
+    if (gshift == 0) return launch_g<BITS, 0>(w, in_bf16, blocks, packed, scales, biases, stream);
+    if (gshift == 1) return launch_g<BITS, 1>(w, in_bf16, blocks, packed, scales, biases, stream);
+    return launch_g<BITS, 2>(w, in_bf16, blocks, packed, scales, biases, stream);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t cols, int group_size, int bits,
+                           uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {
+    const uint64_t blocks = (uint64_t)rows * (uint64_t)(cols / 32);
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 2: return launch_bits<2>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        case 3: return launch_bits<3>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        case 4: return launch_bits<4>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        case 5: return launch_bits<5>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        case 6: return launch_bits<6>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        case 8: return launch_bits<8>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qaff

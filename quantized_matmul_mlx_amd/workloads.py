@@ -84,6 +84,9 @@ WORKLOADS = {
     # Embedding table: 4-bit g64 [32768, 4096], 4096 uniform-random gathered rows.
     "rows_4bit_g64_32768x4096": Workload("rows_4bit_g64_32768x4096", 4, 64, 32768, 4096,
                                          (1e-3, 2e-2), (-0.15, 0.0), n_indices=4096),
+    # Quantization of a dense bf16 weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64 (the decode shape).
+    "quantize_4bit_g64_4096x4096": Workload("quantize_4bit_g64_4096x4096", 4, 64, 4096, 4096,
+                                            (0.0, 0.0), (0.0, 0.0), seed=51),
     # Mixture of experts (gathered products): 128 experts of W [768, 2048] at 4-bit g64, 8 experts
     # per token; 1 token (a single decode step) and 64 tokens (a decode batch), rows sorted by expert.
     "moe_4bit_g64_e128_768x2048": Workload("moe_4bit_g64_e128_768x2048", 4, 64, 768, 2048,
@@ -203,3 +206,9 @@ def moe_inputs(wl: Workload, tokens: int, experts: Optional[int] = None, n: Opti
     tok, exp = tok[order], exp[order]
     return MoeInputs(wl, packed.reshape(E, n, -1), scales.reshape(E, n, -1), biases.reshape(E, n, -1), x,
                      tok, exp, x[tok][:, None, :])
+
+
+def dense_weight(rows: int, cols: int, dtype: str = "bf16", std: float = 0.02, seed: int = 0) -> np.ndarray:
+    """A dense weight ~ N(0, std^2) to quantize: float32, or bf16 bit patterns (truncated draws)."""
+    w = (np.random.default_rng(seed).standard_normal((rows, cols), dtype=np.float32) * np.float32(std))
+    return bf16_bits_from_f32(w) if dtype == "bf16" else w

@@ -216,3 +216,20 @@ def test_gather_qmm_checks(lib):
     assert gather(lib, batch=0, x=NULL, y=NULL) == OK
     assert gather(lib, m=0, x=NULL, y=NULL) == OK
     assert gather(lib, n=0, x=NULL, y=NULL) == OK
+
+
+def quant(lib, rows=2, cols=64, G=32, bits=4, w=A16, packed=A16, scales=A16, biases=A16, dtype=BF16):
+    return lib.qaff_quantize(w, dtype, rows, cols, G, bits, packed, scales, biases, NULL)
+
+
+def test_quantize_checks(lib):
+    assert quant(lib, bits=7) == UNSUPPORTED
+    assert quant(lib, G=48) == INVALID
+    assert quant(lib, cols=48) == INVALID                     # not a multiple of the group size
+    assert quant(lib, rows=-1) == INVALID
+    assert quant(lib, packed=NULL) == INVALID
+    assert quant(lib, scales=A1) == INVALID
+    assert quant(lib, w=NULL) == INVALID
+    assert quant(lib, w=A4) == INVALID                        # w 16-byte aligned
+    assert quant(lib, dtype=7) == INVALID
+    assert quant(lib, rows=0, w=NULL, packed=NULL, scales=NULL, biases=NULL) == OK

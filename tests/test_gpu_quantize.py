@@ -1,0 +1,109 @@
+"""Quantization on the GPU against the CPU oracle, through the C ABI (via the binding).
+
+Codes are integers and scales and biases bf16 values, each decided by float32 arithmetic that both
+sides evaluate the same way (bias = group min, scale = (max - min) / (2^bits - 1) rounded to bf16,
+code = round-half-away((w - bias) / scale) clamped): the bar is bit-exact for all three outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc_mod
+from gpu_util import banner, dev_bf16, dev_u32, dev_x, host_bits
+from quantized_matmul_mlx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc_mod.build()
+    import quantized_matmul_mlx_amd as q
+    q._lib.load()
+    return orc_mod
+
+
+def qaff():
+    import quantized_matmul_mlx_amd as q
+    return q
+
+
+def run(w, dtype, G, bits):
+    wd = dev_x(w, dtype)
+    p, s, b = qaff().quantize(wd, G, bits)
+    torch.cuda.synchronize()
+    return (p.cpu().numpy().view(np.uint32), host_bits(s), host_bits(b))
+
+
+def check(orc, w, dtype, G, bits):
+    got = run(w, dtype, G, bits)
+    ref = orc.quantize(w, dtype, G, bits)
+    for name, g, r in zip(("packed", "scales", "biases"), got, ref):
+        assert g.shape == r.shape, name
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)[:5]
+            raise AssertionError(f"{name} differs at {bad.tolist()}: got {g[tuple(bad[0])]:#x}, "
+                                 f"oracle {r[tuple(bad[0])]:#x}")
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantize_bit_exact(orc, dtype, bits, G):
+    # 37 rows (a ragged last thread block) of 5 groups
+    w = W.dense_weight(37, 5 * G, dtype, seed=bits * 10 + G)
+    banner(f"quantize {dtype} bits={bits} G={G}")
+    check(orc, w, dtype, G, bits)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128)])
+def test_quantize_special_groups(orc, bits, G):
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((6, 4 * G)) * 0.5).astype(np.float32)
+    w[0, :G] = 0.75                               # constant group: scale 0, code 0
+    w[1, :] = 0.0                                 # all zero
+    w[1, G:2 * G:2] = -0.0                        # +0 and -0 mixed: the first of equal minima
+    w[2, :G] = np.round(w[2, :G] * 8) / 8         # many values on a coarse grid: exact ties
+    w[3, G:2 * G] = np.linspace(1.005, 1.9, G)    # the stored bias rounds above the minimum
+    w[4, :G] = np.where(np.arange(G) % 2, 1e30, -1e30)   # a huge range
+    w[5, :G] = np.arange(G) * 2.0 ** -20          # a tiny range
+    banner(f"quantize special groups bits={bits} G={G}")
+    check(orc, w, "f32", G, bits)
+    check(orc, W.bf16_bits_from_f32(w), "bf16", G, bits)
+
+
+def test_quantize_round_trip_through_qmm(orc):
+    # quantize -> qmm on the GPU against the oracle's qmm of the oracle's quantization
+    w = W.dense_weight(300, 1024, "bf16", seed=3)
+    banner("quantize then qmm")
+    q = qaff()
+    p, s, b = q.quantize(dev_bf16(w), 64, 4)
+    x = W.bf16_bits_from_f32(np.random.default_rng(4).standard_normal((4, 1024)).astype(np.float32))
+    y = q.qmm(dev_bf16(x), p, s, b, 64, 4)
+    torch.cuda.synchronize()
+    rp, rs, rb = orc.quantize(w, "bf16", 64, 4)
+    ref = orc.qmm(x, "bf16", rp, rs, rb, 64, 4)
+    assert orc.max_row_rel_err(y.float().cpu().numpy().astype(np.float64), ref) <= 1.6e-2
+
+
+def test_quantize_leading_dims_and_empty(orc):
+    w = W.dense_weight(6, 128, "f32", seed=5).reshape(2, 3, 128)
+    banner("quantize leading dims")
+    p, s, b = qaff().quantize(dev_x(w, "f32"), 32, 4)
+    torch.cuda.synchronize()
+    assert tuple(p.shape) == (2, 3, 16) and tuple(s.shape) == (2, 3, 4)
+    rp, rs, rb = orc.quantize(w.reshape(6, 128), "f32", 32, 4)
+    np.testing.assert_array_equal(p.cpu().numpy().view(np.uint32).reshape(6, 16), rp)
+    np.testing.assert_array_equal(host_bits(s).reshape(6, 4), rs)
+    e = qaff().quantize(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), 64, 4)
+    assert tuple(e[0].shape) == (0, 8)
+
+
+def test_quantize_workload_full_size(orc):
+    wl = W.WORKLOADS["quantize_4bit_g64_4096x4096"]
+    w = W.dense_weight(wl.n, wl.k, "bf16", seed=wl.seed)
+    banner("quantize 4096x4096 bf16 4-bit g64")
+    check(orc, w, "bf16", wl.group_size, wl.bits)
