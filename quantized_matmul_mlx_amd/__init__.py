@@ -137,7 +137,18 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
 
     x is float32 or bf16 ``[..., k]`` (a 1-D x is one row); the result has x's dtype and shape
     ``[..., n]``. ``path`` forces a kernel ("gemv", "gemv_mfma" or "gemm") for tests and
-    benchmarks."""
+    benchmarks.
+
+    A weight with batch dimensions (packed ``[..., n, k*bits/32]``) multiplies x ``[..., m, k]``
+    batch by batch, the batch dimensions of both broadcast together (a 2-D x takes the weight's
+    batch; a 1-D x is a row vector and the result drops that row): the gathered product with
+    its default indices."""
+    if isinstance(packed, torch.Tensor) and packed.dim() > 2:
+        if path == "gemm":
+            raise ValueError("a batched weight runs on the gathered kernels: path 'auto', 'gemv' or 'gemv_mfma'")
+        vector = isinstance(x, torch.Tensor) and x.dim() == 1
+        y = gather_qmm(x[None] if vector else x, packed, scales, biases, group_size, bits, path=path, out=out)
+        return y.squeeze(-2) if vector else y
     lib = _lib.load()
     dev, n, k = _weights(packed, scales, biases, group_size, bits)
     _need(x, "x", tuple(_OUT_DTYPES), dev)

@@ -243,3 +243,30 @@ def test_gather_moe_workload(orc, tokens):
                mi.expert)
     check(orc, got2, mi.x[:, None, :], "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits,
           mi.token, mi.expert, "gemv")
+
+
+def test_qmm_with_a_batched_weight_broadcasts(orc):
+    # nuvec_core quantized_matmul: batch dimensions of x and w broadcast when w has them
+    E, n, k, G, bits = 4, 40, 512, 64, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=750)
+    x = draw_x((2, 1, 3, k), "bf16", seed=751)
+    banner("qmm batched weight")
+    q = qaff()
+    pw, sw, bw = dev_u32(packed), dev_bf16(scales), dev_bf16(biases)
+    y = q.qmm(dev_x(x, "bf16"), pw, sw, bw, G, bits)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, E, 3, n)
+    ref = orc.gather_qmm(x, "bf16", packed, scales, biases, G, bits)   # default indices, broadcast
+    assert ref.shape == (2, E, 3, n)
+    assert orc.max_row_rel_err(host_f64(y).reshape(-1, n), ref.reshape(-1, n)) <= TOL["bf16"]
+    # a 2-D x takes the weight's batch; a 1-D x is a row vector and drops that row
+    x2 = draw_x((3, k), "bf16", seed=752)
+    y2 = q.qmm(dev_x(x2, "bf16"), pw, sw, bw, G, bits)
+    x1 = x2[0]
+    y1 = q.qmm(dev_x(x1, "bf16"), pw, sw, bw, G, bits)
+    torch.cuda.synchronize()
+    assert tuple(y2.shape) == (E, 3, n) and tuple(y1.shape) == (E, n)
+    ref2 = orc.gather_qmm(x2[None], "bf16", packed, scales, biases, G, bits)
+    assert orc.max_row_rel_err(host_f64(y2).reshape(-1, n), ref2.reshape(-1, n)) <= TOL["bf16"]
+    ref1 = orc.gather_qmm(x1[None, None], "bf16", packed, scales, biases, G, bits)[:, 0, :]
+    assert orc.max_row_rel_err(host_f64(y1), ref1) <= TOL["bf16"]
