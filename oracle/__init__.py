@@ -17,6 +17,8 @@ patterns. What each function computes, and the page passage it follows, is docum
 * ``dequant_rows`` -- the gathered-row lookup (maya2_mlx ``quant.py``, ``rows``).
 * ``qmm`` -- ``x . dequantize(W)^T`` summed in double precision (nuvec_core ``quantized_matmul``;
   maya2_mlx ``mm``).
+* ``qmm_nt`` -- ``x . dequantize(W)`` for a weight stored [k, n] (nuvec_core ``quantized_matmul``
+  without the transpose).
 * ``gather_qmm`` -- output batch i is ``x[lhs[i]] . dequantize(W[rhs[i]])^T`` (nuvec_core
   ``gather_qmm`` and ``gather_indices``).
 * ``silu_gate`` / ``silu_gate_qmm`` -- the fused decode products' activation and product
@@ -82,12 +84,13 @@ def _load():
                             _int, _f64p, _int]
     lib.orc_gather_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
                                    _i64, _int, ctypes.c_void_p, ctypes.c_void_p, _i64, _f64p, _int]
+    lib.orc_qmm_nt.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _f64p]
     lib.orc_quantize.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, _u16p, _u16p]
     lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
     lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
-                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize"):
+                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize", "orc_qmm_nt"):
         getattr(lib, name).restype = _int
     for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate"):
         getattr(lib, name).restype = None
@@ -199,6 +202,28 @@ def qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: int,
     out = np.empty((m, n), np.float64)
     _check(_load().orc_qmm(xa.ctypes.data, 1 if x_dtype == "bf16" else 0, m, packed, scales, biases,
                            n, k, group_size, bits, out, threads or default_threads()), "qmm")
+    return out
+
+
+def qmm_nt(x, x_dtype: str, packed, scales, biases, group_size: int, bits: int) -> np.ndarray:
+    """y = x . dequantize(W) in float64, shape [m, n], for W stored [k, n]: packed
+    [k, n*bits/32], scales and biases [k, n/G]."""
+    packed = _c(np.atleast_2d(packed), np.uint32)
+    scales = _c(np.atleast_2d(scales), np.uint16)
+    biases = _c(np.atleast_2d(biases), np.uint16)
+    if x_dtype == "bf16":
+        xa = _c(np.atleast_2d(x), np.uint16)
+    elif x_dtype == "f32":
+        xa = _c(np.atleast_2d(x), np.float32)
+    else:
+        raise ValueError(x_dtype)
+    m, k = xa.shape
+    if packed.shape[0] != k:
+        raise ValueError("x columns do not match the weight's rows")
+    n = packed.shape[1] * 32 // bits
+    out = np.empty((m, n), np.float64)
+    _check(_load().orc_qmm_nt(xa.ctypes.data, 1 if x_dtype == "bf16" else 0, m, packed, scales, biases, k, n,
+                              group_size, bits, out), "qmm_nt")
     return out
 
 

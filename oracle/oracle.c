@@ -3,6 +3,7 @@
  *   - dequantize:        w[n,k] = scale[n,k/G] * code[n,k] + bias[n,k/G]
  *   - gathered rows:     out[i,:] = dequantize(table)[idx[i], :]
  *   - quantized matmul:  y[m,n] = sum_k x[m,k] * w[n,k]      (y = x . dequantize(W)^T)
+ *   - without transpose: y[m,n] = sum_k x[m,k] * w[k,n]      (y = x . dequantize(W), W [k, n])
  *   - gathered matmul:   y[i] = x[lhs[i]] . dequantize(W[rhs[i]])^T  (mixture-of-experts batches)
  *   - quantize:          bias = group min, scale = (max - min) / (2^bits - 1), code =
  *                        round((w - bias) / scale) clamped to [0, 2^bits - 1]
@@ -402,4 +403,30 @@ int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64
     const int rc = orc_pack_codes(codes, rows, cols, bits, packed);
     free(codes);
     return rc;
+}
+
+/* [nuvec] quantized_matmul without the transpose: y = x . dequantize(w), for a weight stored
+ * [k, n] (its rows are the k index, each a bit stream of n codes in groups of G along n):
+ *     y[m, n] = sum over k of x[m, k] * w[k, n]
+ * in double, sequentially in k, with each row of w dequantized as everywhere else. x [m, k]
+ * (float32 or bf16 bits), packed [k, n*bits/32], scales/biases [k, n/group]; out double [m, n].
+ * Returns 0, or -1 for parameters outside the format. */
+int orc_qmm_nt(const void* x, int x_is_bf16, int64_t m, const uint32_t* packed, const uint16_t* scales,
+               const uint16_t* biases, int64_t k, int64_t n, int64_t group, int bits, double* out) {
+    if (m < 0 || k < 0 || !valid_params(n, group, bits)) return -1;
+    float* w = (float*)malloc(sizeof(float) * (size_t)(k * n > 0 ? k * n : 1));
+    if (!w) return -2;
+    for (int64_t kk = 0; kk < k; ++kk) dequant_row(packed, scales, biases, kk, n, group, bits, w + kk * n);
+    for (int64_t mm = 0; mm < m; ++mm)
+        for (int64_t nn = 0; nn < n; ++nn) {
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk) {
+                const int64_t i = mm * k + kk;
+                const double xv = x_is_bf16 ? (double)bf16_to_f32(((const uint16_t*)x)[i]) : (double)((const float*)x)[i];
+                acc += xv * (double)w[kk * n + nn];
+            }
+            out[mm * n + nn] = acc;
+        }
+    free(w);
+    return 0;
 }

@@ -601,3 +601,41 @@ def test_quantize_round_trip_bound(oracle_lib, bits, G):
     # codes use the whole range: the minimum's code is 0 and the maximum's is 2^bits - 1 or one below
     codes = oracle_lib.unpack_codes(packed, 4 * G, bits).reshape(16, -1, G)
     assert np.all(codes.min(-1) == 0) and np.all(codes.max(-1) >= top - 1)
+
+
+# ---- the product without the transpose ----------------------------------------------------------
+
+def test_qmm_nt_one_hot_selects_a_row(oracle_lib):
+    # x = e_k picks row k of the dequantized [k, n] weight, exactly
+    inp = W.random_inputs(3, 32, 12, 96, 0, seed=21)     # a [12, 96] weight read as W [k=12, n=96]
+    w = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, 32, 3)
+    x = np.eye(12, dtype=np.float32)[[0, 7, 11]]
+    y = oracle_lib.qmm_nt(x, "f32", inp.packed, inp.scales, inp.biases, 32, 3)
+    np.testing.assert_array_equal(y, w[[0, 7, 11]].astype(np.float64))
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 32), (2, 128), (5, 32)])
+def test_qmm_nt_matches_float64_matmul(oracle_lib, bits, G):
+    # against numpy's float64 product of the pinned dequantization: x [3, k] . W [k, n]; a
+    # transposed operand (the other form) would not even have these shapes
+    inp = W.random_inputs(bits, G, 40, 2 * G, 0, seed=22 + bits)
+    w = oracle_lib.dequantize(inp.packed, inp.scales, inp.biases, G, bits).astype(np.float64)
+    x = np.random.default_rng(5).standard_normal((3, 40)).astype(np.float32)
+    y = oracle_lib.qmm_nt(x, "f32", inp.packed, inp.scales, inp.biases, G, bits)
+    assert y.shape == (3, 2 * G)
+    np.testing.assert_allclose(y, x.astype(np.float64) @ w, rtol=1e-12, atol=1e-12)
+
+
+def test_qmm_nt_and_qmm_agree_on_a_symmetric_weight(oracle_lib):
+    # a weight with w[i, j] = w[j, i] dequantizes to the same matrix read either way, so the
+    # product with and without the transpose must agree to the bit
+    n = 64
+    codes = np.random.default_rng(8).integers(0, 16, size=(n, n)).astype(np.uint8)
+    codes = np.triu(codes) + np.triu(codes, 1).T
+    packed = oracle_lib.pack_codes(codes, 4)
+    sc = np.full((n, 1), _bf16(0.25)[0], np.uint16)   # one group per row, the same everywhere
+    bi = np.full((n, 1), _bf16(-1.0)[0], np.uint16)
+    x = np.random.default_rng(9).standard_normal((2, n)).astype(np.float32)
+    y_nt = oracle_lib.qmm_nt(x, "f32", packed, sc, bi, 64, 4)
+    y_t = oracle_lib.qmm(x, "f32", packed, sc, bi, 64, 4)
+    np.testing.assert_array_equal(y_nt, y_t)
