@@ -28,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import QaffError
 
-__all__ = ["quantize", "dequantize", "qmm", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "gather_qmm", "QWeight",
+__all__ = ["quantize", "dequantize", "qmm", "qmm_nt", "dequant_rows", "gemv_gate_up", "gemv_silu_gate", "gather_qmm", "QWeight",
            "QaffError", "gemv_max_m", "gemv_mfma_min_m"]
 
 _PACKED_DTYPES = (torch.int32, torch.uint32)
@@ -132,7 +132,34 @@ def quantize(w, group_size: int, bits: int):
     return packed, scales, biases
 
 
-def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto", out=None):
+def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None):
+    """``x . dequantize(W)`` for a weight stored ``[k, n]`` (nuvec_core ``quantized_matmul`` with
+    ``transpose=False``): packed ``[k, n*bits/32]``, scales and biases ``[k, n/group_size]``;
+    x float32 or bf16 ``[..., k]`` (1-D: one row); the result has x's dtype and shape ``[..., n]``.
+    The call's float32 K-chunk partial sums go to a workspace tensor allocated here."""
+    lib = _lib.load()
+    dev, k, n = _weights(packed, scales, biases, group_size, bits)
+    _need(x, "x", tuple(_OUT_DTYPES), dev)
+    if x.shape[-1] != k:
+        raise ValueError(f"x has {x.shape[-1]} columns, the weight {k} rows")
+    lead = tuple(x.shape[:-1])
+    m = math.prod(lead)
+    if out is None:
+        out = torch.empty(lead + (n,), dtype=x.dtype, device=dev)
+    else:
+        _need(out, "out", (x.dtype,), dev)
+        if tuple(out.shape) != lead + (n,):
+            raise ValueError(f"out must be {list(lead + (n,))}")
+    nbytes = int(lib.qaff_qmm_nt_workspace_size(m, k, n))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(lib.qaff_qmm_nt(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k, n,
+                                   group_size, bits, _p(ws), ws.numel(), _p(out), _stream(dev)))
+    return out
+
+
+def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto", out=None,
+        transpose: bool = True):
     """``x . dequantize(W)^T`` (nuvec_core ``quantized_matmul`` with transpose; maya2_mlx ``mm``).
 
     x is float32 or bf16 ``[..., k]`` (a 1-D x is one row); the result has x's dtype and shape
@@ -142,7 +169,14 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
     A weight with batch dimensions (packed ``[..., n, k*bits/32]``) multiplies x ``[..., m, k]``
     batch by batch, the batch dimensions of both broadcast together (a 2-D x takes the weight's
     batch; a 1-D x is a row vector and the result drops that row): the gathered product with
-    its default indices."""
+    its default indices.
+
+    ``transpose=False`` computes ``x . dequantize(W)`` for a weight stored ``[k, n]``
+    (``qmm_nt``)."""
+    if not transpose:
+        if path != "auto":
+            raise ValueError("the product without the transpose has one kernel: path 'auto'")
+        return qmm_nt(x, packed, scales, biases, group_size, bits, out=out)
     if isinstance(packed, torch.Tensor) and packed.dim() > 2:
         if path == "gemm":
             raise ValueError("a batched weight runs on the gathered kernels: path 'auto', 'gemv' or 'gemv_mfma'")

@@ -337,6 +337,43 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                               lhs_indices, rhs_indices, batch, sorted_indices, y, stream, QAFF_PATH_AUTO);
 }
 
+size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n) {
+    if (m <= 0 || k <= 0 || n <= 0) return 0;
+    return qaff::qmm_nt_workspace_bytes(m, k, n);
+}
+
+qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                        const uint16_t* biases, int64_t k, int64_t n, int32_t group_size, int32_t bits,
+                        void* workspace, size_t workspace_bytes, void* y, hipStream_t stream) {
+    static const char* op = "qaff_qmm_nt";
+    g_error.clear();
+    // the weight is [k, n]: k rows of n codes
+    qaff_status st = check_weight(op, packed, scales, biases, k, n, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
+    if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
+    if (m == 0 || n == 0) return QAFF_OK;
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * esize, stream), stream);
+    if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (m * n >= (1LL << 31) || k > 0x7fffffffLL || n > 0x7fffffffLL)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld outputs or k = %lld is too large", op, (long long)m,
+                    (long long)n, (long long)k);
+    int64_t kchunk, chunks;
+    qaff::qmm_nt_plan(k, n, &kchunk, &chunks);
+    if (chunks > 65535) return fail(QAFF_ERR_UNSUPPORTED, "%s: k = %lld is too large", op, (long long)k);
+    const size_t need = qaff::qmm_nt_workspace_bytes(m, k, n);
+    if (!workspace || workspace_bytes < need)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: the workspace needs %zu bytes (qaff_qmm_nt_workspace_size), got %zu",
+                    op, need, workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", op);
+    return after_launch(op, qaff::launch_qmm_nt(x, x_dtype == QAFF_F32, m, packed, scales, biases, k, n, group_size,
+                                                bits, workspace, y, stream), stream);
+}
+
 qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
                           int32_t bits, uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {
     static const char* op = "qaff_quantize";

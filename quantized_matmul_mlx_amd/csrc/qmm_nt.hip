@@ -1,0 +1,203 @@
+// The quantized product without the transpose (nuvec_core quantized.rs, `quantized_matmul` with
+// transpose = false): y[m, n] = sum over k of x[m, k] * w[k, n], for a weight stored [k, n] whose
+// rows (the k index) are bit streams of n codes in groups of G along n.
+//
+// The output runs along the weight's rows, so a lane owns one 32-column block (a whole group
+// part: G >= 32) and walks down k. With w = s c + b of the row's group:
+//     sum_k x[k] w[k, n] = sum_k (x[k] s[k]) c[k, n] + sum_k x[k] b[k]
+// one multiply-add per code and x row, plus one per row for the bias term.
+// There are only n/32 column blocks, so K is split over blocks too: each block writes float32
+// partial sums of its K chunk to a caller-provided workspace, and a second kernel adds the chunks
+// in order (deterministic) and rounds y.
+//  * Block: 256 threads over 16 column blocks (512 columns) x 16 row phases: lane (cb, p) walks
+//    rows k0 + p, k0 + p + 16, ... of its chunk, loading its block's `bits` words per row.
+//  * The chunk's x values (m <= 2 rows per launch) sit in LDS as float32; the 16 phases' partial
+//    sums are added through LDS (rows padded to 33 floats against bank conflicts).
+#include "launch.h"
+#include "qaff_device.h"
+
+#include <hip/hip_runtime.h>
+
+namespace qaff {
+namespace {
+
+constexpr int kNtThreads = 256;
+constexpr int kNtCols = 16;    // column blocks per thread block
+constexpr int kNtPhases = 16;  // row phases per thread block
+constexpr int kNtMaxM = 2;     // x rows per launch
+constexpr int kNtPad = 33;     // floats per (phase, column block, row) in the LDS sums
+constexpr int64_t kNtTargetBlocks = 512;
+
+template <int BITS, int MB, bool XF32>
+__global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
+    const void* x, uint32_t m, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+    uint32_t n, uint32_t k, uint32_t gshift, uint32_t kchunk, float* ws) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                              // [MB][kchunk]
+    float* red = lds + MB * kchunk;               // [phase][column block][MB][kNtPad]
+    const int tid = threadIdx.x;
+    const int cbl = tid & (kNtCols - 1);
+    const int phase = tid >> 4;
+    const uint32_t ncb = n >> 5;
+    const uint32_t cb = blockIdx.x * kNtCols + cbl;
+    const uint32_t cbc = min(cb, ncb - 1);        // loads stay in bounds; stores are skipped
+    const uint32_t k0 = blockIdx.y * kchunk;
+    const uint32_t k1 = min(k0 + kchunk, k);
+    const uint32_t gpr = n >> (5 + gshift);       // groups per weight row
+    const uint32_t g = cbc >> gshift;             // this column block's group
+
+    // 1. The chunk's x as float32 (rows past m repeat row m - 1: they are never stored).
+    for (uint32_t i = tid; i < MB * kchunk; i += kNtThreads) {
+        const uint32_t r = i / kchunk, kk = k0 + i % kchunk;
+        float v = 0.f;
+        if (kk < k1) {
+            const size_t o = (size_t)min(r, m - 1) * k + kk;
+            v = XF32 ? static_cast<const float*>(x)[o] : bf16_to_f32(static_cast<const uint16_t*>(x)[o]);
+        }
+        xs[i] = v;
+    }
+    __syncthreads();
+
+    // 2. Walk the chunk's rows.
+    float acc[MB][32];
+    float bsum[MB];
+#pragma unroll
+    for (int r = 0; r < MB; ++r) {
+        bsum[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) acc[r][c] = 0.f;
+    }
+#pragma unroll 2
+    for (uint32_t kk = k0 + phase; kk < k1; kk += kNtPhases) {
+        uint32_t w[BITS];
+        load_block<BITS>(packed + ((size_t)kk * ncb + cbc) * BITS, w);
+        const float s = bf16_to_f32(scales[(size_t)kk * gpr + g]);
+        const float b = bf16_to_f32(biases[(size_t)kk * gpr + g]);
+        float cf[32];
+#pragma unroll
+        for (int c = 0; c < 32; ++c) cf[c] = (float)code_at<BITS>(w, c);
+#pragma unroll
+        for (int r = 0; r < MB; ++r) {
+            const float xv = xs[r * kchunk + (kk - k0)];
+            const float xsv = xv * s;
+            bsum[r] = __builtin_fmaf(xv, b, bsum[r]);
+#pragma unroll
+            for (int c = 0; c < 32; ++c) acc[r][c] = __builtin_fmaf(xsv, cf[c], acc[r][c]);
+        }
+    }
+
+    // 3. Add the 16 phases through LDS, then write the chunk's partial sums.
+#pragma unroll
+    for (int r = 0; r < MB; ++r)
+#pragma unroll
+        for (int c = 0; c < 32; ++c) red[((phase * kNtCols + cbl) * MB + r) * kNtPad + c] = acc[r][c] + bsum[r];
+    __syncthreads();
+    for (int o = tid; o < kNtCols * MB * 32; o += kNtThreads) {
+        const int c = o & 31, r = (o >> 5) % MB, cl = o / (32 * MB);
+        float sum = 0.f;
+#pragma unroll
+        for (int p = 0; p < kNtPhases; ++p) sum += red[((p * kNtCols + cl) * MB + r) * kNtPad + c];
+        const uint32_t col = (blockIdx.x * kNtCols + cl) * 32 + c;
+        if (col < n && (uint32_t)r < m) ws[((size_t)blockIdx.y * MB + r) * n + col] = sum;
+    }
+}
+
+// y[r, col] = sum over the chunks of ws[chunk][r][col], in chunk order.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void qmm_nt_reduce_kernel(const float* ws, uint32_t chunks, uint32_t mb,
+                                                            uint32_t m, uint32_t n, void* y) {
+    const uint32_t o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= m * n) return;
+    const uint32_t r = o / n, col = o % n;
+    float sum = 0.f;
+    for (uint32_t s = 0; s < chunks; ++s) sum += ws[((size_t)s * mb + r) * n + col];
+    if (OUT_BF16) static_cast<uint16_t*>(y)[o] = to_bf16_bits(sum);
+    else static_cast<float*>(y)[o] = sum;
+}
+
+}  // namespace
+
+// The K chunking: about kNtTargetBlocks blocks, at least 4 rows per lane and phase.
+void qmm_nt_plan(int64_t k, int64_t n, int64_t* kchunk, int64_t* chunks) {
+    const int64_t tiles = ((n / 32) + kNtCols - 1) / kNtCols;
+    int64_t split = (kNtTargetBlocks + tiles - 1) / tiles;
+    const int64_t max_split = (k + 4 * kNtPhases - 1) / (4 * kNtPhases);
+    if (split > max_split) split = max_split;
+    if (split < 1) split = 1;
+    int64_t kc = (k + split - 1) / split;
+    kc = (kc + kNtPhases - 1) / kNtPhases * kNtPhases;
+    if (kc < kNtPhases) kc = kNtPhases;
+    if (kc > 4096) kc = 4096;  // the chunk's x (2 rows of float32) must fit in LDS beside the sums
+    *kchunk = kc;
+    *chunks = (k + kc - 1) / kc;
+}
+
+size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n) {
+    int64_t kc, chunks;
+    qmm_nt_plan(k, n, &kc, &chunks);
+    const int64_t mb = m < kNtMaxM ? m : kNtMaxM;
+    return (size_t)(chunks * mb * n) * sizeof(float);
+}
+
+namespace {
+
+template <int BITS, int MB, bool XF32>
+hipError_t launch_slice(const void* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                        const uint16_t* biases, int64_t k, int64_t n, uint32_t gshift, int64_t kchunk,
+                        int64_t chunks, float* ws, void* y, hipStream_t stream) {
+    const size_t lds = (size_t)(MB * kchunk + kNtPhases * kNtCols * MB * kNtPad) * sizeof(float);
+    const unsigned gx = (unsigned)(((n / 32) + kNtCols - 1) / kNtCols);
+    qmm_nt_partial_kernel<BITS, MB, XF32><<<dim3(gx, (unsigned)chunks), kNtThreads, lds, stream>>>(
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)k, gshift, (uint32_t)kchunk, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned gr = (unsigned)((m * n + 255) / 256);
+    if (XF32)
+        qmm_nt_reduce_kernel<false><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
+    else
+        qmm_nt_reduce_kernel<true><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                       const uint16_t* biases, int64_t k, int64_t n, uint32_t gshift, float* ws, void* y,
+                       hipStream_t stream) {
+    int64_t kchunk, chunks;
+    qmm_nt_plan(k, n, &kchunk, &chunks);
+    const size_t xsize = x_f32 ? 4 : 2;
+    for (int64_t m0 = 0; m0 < m; m0 += kNtMaxM) {
+        const int64_t mm = m - m0 < kNtMaxM ? m - m0 : kNtMaxM;
+        const void* xs = static_cast<const uint8_t*>(x) + (size_t)m0 * k * xsize;
+        void* ys = static_cast<uint8_t*>(y) + (size_t)m0 * n * xsize;
+        hipError_t e;
+        if (mm == 1)
+            e = x_f32 ? launch_slice<BITS, 1, true>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream)
+                      : launch_slice<BITS, 1, false>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream);
+        else
+            e = x_f32 ? launch_slice<BITS, 2, true>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream)
+                      : launch_slice<BITS, 2, false>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
+                         void* y, hipStream_t stream) {
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    float* ws = static_cast<float*>(workspace);
+    switch (bits) {
+        case 2: return launch_bits<2>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 3: return launch_bits<3>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 4: return launch_bits<4>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 5: return launch_bits<5>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 6: return launch_bits<6>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 8: return launch_bits<8>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qaff

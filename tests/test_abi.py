@@ -233,3 +233,22 @@ def test_quantize_checks(lib):
     assert quant(lib, w=A4) == INVALID                        # w 16-byte aligned
     assert quant(lib, dtype=7) == INVALID
     assert quant(lib, rows=0, w=NULL, packed=NULL, scales=NULL, biases=NULL) == OK
+
+
+def qnt(lib, m=1, k=64, n=64, G=32, bits=4, x=A16, y=A16, ws=A16, wsb=1 << 20, dtype=BF16):
+    return lib.qaff_qmm_nt(x, dtype, m, A16, A16, A16, k, n, G, bits, ws, wsb, y, NULL)
+
+
+def test_qmm_nt_checks(lib):
+    assert lib.qaff_qmm_nt_workspace_size(1, 4096, 4096) > 0
+    assert lib.qaff_qmm_nt_workspace_size(0, 4096, 4096) == 0
+    assert qnt(lib, bits=7) == UNSUPPORTED
+    assert qnt(lib, n=48) == INVALID                         # groups run along n
+    assert qnt(lib, m=-1) == INVALID
+    assert qnt(lib, y=NULL) == INVALID
+    assert qnt(lib, x=A2) == INVALID
+    assert qnt(lib, ws=NULL) == INVALID                      # the workspace is required ...
+    assert b"workspace" in lib.qaff_last_error()
+    assert qnt(lib, wsb=4) == INVALID                        # ... and must be large enough
+    assert qnt(lib, ws=A4) == INVALID                        # ... and 16-byte aligned
+    assert qnt(lib, m=0, x=NULL, y=NULL, ws=NULL) == OK
