@@ -16,7 +16,8 @@ The same JSON line carries:
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
     product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
-    residual, quantize of a bf16 [4096, 4096] weight, and the mixture-of-experts gathered product
+    residual, the product without the transpose at the decode shape, quantize of a bf16
+    [4096, 4096] weight, and the mixture-of-experts gathered product
     gather_qmm at 1 and 64 tokens), each against its roofline;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
     (also given per row).
@@ -304,6 +305,37 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget):
     return row
 
 
+def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
+    """The product without the transpose at the decode shape: x bf16 [1, 4096] . dequantize(W) for
+    W stored [4096 (k), 4096 (n)], 4-bit g64 (groups along n). Algorithmic bytes as for qmm."""
+    import numpy as np
+    import oracle
+    wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
+    inp = W.make_inputs(wl, m=1)          # the same draws, read as a [k, n] weight
+    b = qmm_bytes(1, wl.n, wl.k, wl.bits, wl.group_size)
+    copies = copies_for(b)
+    sets = replicate(torch, to_device(torch, inp), copies)
+    ys = [torch.empty((1, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        q.qmm_nt(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del sets, ys
+    torch.cuda.empty_cache()
+    gbs = b / (ms * 1e-3) / 1e9
+    row = {"workload": "qmm without the transpose, W [4096 (k), 4096 (n)] 4-bit g64, x bf16 [1, 4096]",
+           "kernel": "qmm_nt_partial_kernel + qmm_nt_reduce_kernel", "bytes_per_step": b,
+           "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
+    if cpu:
+        runs, el = cpu_time(lambda: oracle.qmm_nt(inp.x, "bf16", inp.packed, inp.scales, inp.biases,
+                                                  wl.group_size, wl.bits), cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(b * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row
+
+
 def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     """quantize of a dense bf16 weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64. Algorithmic bytes:
     the weight read, the codes, scales and biases written."""
@@ -527,6 +559,8 @@ def main():
         for kind in ("gate_up", "silu_gate"):
             log(f"row: fused {kind}")
             rows.append(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
+        log("row: qmm without the transpose")
+        rows.append(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0))
         log("row: quantize")
         rows.append(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:

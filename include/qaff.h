@@ -120,7 +120,7 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
  *   x [m, k] in x_dtype (float32 or bf16); packed uint32 [k, n*bits/32], scales and biases bf16
  *   [k, n/group_size] (groups run along n); y [m, n] in x's dtype; float32 sums.
  *   K is split over thread blocks: float32 partial sums go to `workspace`, a caller-owned device
- *   buffer of at least qaff_qmm_nt_workspace_size(m, k, n) bytes (16-byte aligned), which the
+ *   buffer of at least qaff_qmm_nt_workspace_size(m, k, n, bits) bytes (16-byte aligned), which the
  *   call overwrites; a second kernel adds the chunks in a fixed order, so results are
  *   deterministic. Calls that share a workspace must be ordered (the same stream).
  * k == 0 writes zeros. Errors: as qaff_qmm (the weight checked as [k, n]), plus INVALID_ARGUMENT
@@ -131,8 +131,9 @@ qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint
                         int32_t group_size, int32_t bits, void* workspace, size_t workspace_bytes,
                         void* y, hipStream_t stream);
 
-/* Bytes of workspace qaff_qmm_nt needs for these sizes (0 when there is nothing to compute). */
-size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n);
+/* Bytes of workspace qaff_qmm_nt needs for these sizes and bit width (0 when there is nothing to
+ * compute). */
+size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits);
 
 /*
  * Dual decode product (spark_runtime weights/mlx_int8.rs gemv_gate_up): gate_y = x . dequantize(G)^T

@@ -150,7 +150,7 @@ def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None):
         _need(out, "out", (x.dtype,), dev)
         if tuple(out.shape) != lead + (n,):
             raise ValueError(f"out must be {list(lead + (n,))}")
-    nbytes = int(lib.qaff_qmm_nt_workspace_size(m, k, n))
+    nbytes = int(lib.qaff_qmm_nt_workspace_size(m, k, n, bits))
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
         _lib.check(lib.qaff_qmm_nt(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k, n,

@@ -54,7 +54,7 @@ def load() -> ctypes.CDLL:
     lib.qaff_gemv_silu_gate.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp, vp]
     gather = [vp, ctypes.c_int, i64, i64, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, i64, i32, vp, vp]
     lib.qaff_qmm_nt.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp, vp]
-    lib.qaff_qmm_nt_workspace_size.argtypes = [i64, i64, i64]
+    lib.qaff_qmm_nt_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.qaff_qmm_nt_workspace_size.restype = ctypes.c_size_t
     lib.qaff_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
     lib.qaff_gather_qmm.argtypes = gather

@@ -337,9 +337,9 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                               lhs_indices, rhs_indices, batch, sorted_indices, y, stream, QAFF_PATH_AUTO);
 }
 
-size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n) {
+size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits) {
     if (m <= 0 || k <= 0 || n <= 0) return 0;
-    return qaff::qmm_nt_workspace_bytes(m, k, n);
+    return qaff::qmm_nt_workspace_bytes(m, k, n, bits);
 }
 
 qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const uint16_t* scales,
@@ -363,9 +363,9 @@ qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld outputs or k = %lld is too large", op, (long long)m,
                     (long long)n, (long long)k);
     int64_t kchunk, chunks;
-    qaff::qmm_nt_plan(k, n, &kchunk, &chunks);
+    qaff::qmm_nt_plan(k, n, bits, &kchunk, &chunks);
     if (chunks > 65535) return fail(QAFF_ERR_UNSUPPORTED, "%s: k = %lld is too large", op, (long long)k);
-    const size_t need = qaff::qmm_nt_workspace_bytes(m, k, n);
+    const size_t need = qaff::qmm_nt_workspace_bytes(m, k, n, bits);
     if (!workspace || workspace_bytes < need)
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: the workspace needs %zu bytes (qaff_qmm_nt_workspace_size), got %zu",
                     op, need, workspace ? workspace_bytes : (size_t)0);

@@ -86,8 +86,8 @@ hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t co
 // y[m, n] = x[m, k] . dequantize(W) for W stored [k, n] (groups along n); float32 partial sums
 // of K chunks go to `workspace` (qmm_nt_workspace_bytes(m, k, n) bytes), then a second kernel
 // adds them in order. y in x's dtype.
-void qmm_nt_plan(int64_t k, int64_t n, int64_t* kchunk, int64_t* chunks);
-size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n);
+void qmm_nt_plan(int64_t k, int64_t n, int bits, int64_t* kchunk, int64_t* chunks);
+size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n, int bits);
 hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
                          void* y, hipStream_t stream);

@@ -240,8 +240,8 @@ def qnt(lib, m=1, k=64, n=64, G=32, bits=4, x=A16, y=A16, ws=A16, wsb=1 << 20, d
 
 
 def test_qmm_nt_checks(lib):
-    assert lib.qaff_qmm_nt_workspace_size(1, 4096, 4096) > 0
-    assert lib.qaff_qmm_nt_workspace_size(0, 4096, 4096) == 0
+    assert lib.qaff_qmm_nt_workspace_size(1, 4096, 4096, 4) > 0
+    assert lib.qaff_qmm_nt_workspace_size(0, 4096, 4096, 4) == 0
     assert qnt(lib, bits=7) == UNSUPPORTED
     assert qnt(lib, n=48) == INVALID                         # groups run along n
     assert qnt(lib, m=-1) == INVALID
