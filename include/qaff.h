@@ -17,7 +17,7 @@
  *   - All array pointers are DEVICE pointers to row-major, contiguous buffers. The caller owns every
  *     buffer; the library never allocates, frees or retains them (spark_runtime MlxInt8Weight: the
  *     consumer owns the device pointers).
- *   - bits must be 2, 3, 4, 5, 6 or 8 (else QAFF_ERR_UNSUPPORTED); group_size 32, 64 or 128
+ *   - bits must be 1, 2, 3, 4, 5, 6 or 8 (else QAFF_ERR_UNSUPPORTED); group_size 32, 64 or 128
  *     (nuvec_core check_params); cols (k) must be a multiple of group_size.
  *   - Alignment: packed 4 bytes, scales/biases 2 bytes, indices 4 bytes; x, y and out 16 bytes.
  *   - Every argument is checked on the host before any launch, so a rejected call writes nothing.
@@ -63,7 +63,7 @@ typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2, QAFF_
  *   to nearest, ties to even.
  * Errors: INVALID_ARGUMENT for negative sizes, a bad group size, cols % group_size != 0, a bad
  * dtype, a null or misaligned pointer where the size is non-zero; UNSUPPORTED for a bit width
- * outside {2,3,4,5,6,8}.
+ * outside {1,2,3,4,5,6,8}.
  */
 qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                             int64_t rows, int64_t cols, int32_t group_size, int32_t bits,

@@ -2,7 +2,7 @@
 // kernel dispatch and the per-thread error text.
 //
 // The checks follow the pages' own: nuvec_core quantized.rs `check_params` (group sizes 32/64/128;
-// bit widths -- the library implements 2, 3, 4, 5, 6 and 8), rlx-moshi mlx_dequant.rs
+// bit widths 1-6 and 8), rlx-moshi mlx_dequant.rs
 // `dequantize_affine` (the group size divides the columns; the packed width is cols*bits/32) and
 // spark_runtime weights/mlx_int8.rs `MlxInt8Weight::load` (scales and biases are [rows, cols/G]).
 // Shapes are implied by the sizes passed in, so only sizes, pointers and alignment can be checked.
@@ -60,8 +60,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 qaff_status check_weight(const char* op, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t rows, int64_t cols, int32_t group_size,
                          int32_t bits) {
-    if (bits != 2 && bits != 3 && bits != 4 && bits != 5 && bits != 6 && bits != 8)
-        return fail(QAFF_ERR_UNSUPPORTED, "%s: %d bits are not supported (2, 3, 4, 5, 6 or 8)", op, bits);
+    if (bits < 1 || bits > 8 || bits == 7)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: %d bits are not supported (1, 2, 3, 4, 5, 6 or 8)", op, bits);
     if (group_size != 32 && group_size != 64 && group_size != 128)
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: group size %d is not supported (32, 64 or 128)", op, group_size);
     if (rows < 0 || cols < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative size", op);

@@ -150,6 +150,7 @@ hipError_t launch_dequant(const uint32_t* packed, const uint16_t* scales, const 
     const int64_t kb = cols / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return dispatch_out<1>(packed, scales, biases, indices, table_rows, out_rows, kb, gshift, out, out_bf16, stream);
         case 2: return dispatch_out<2>(packed, scales, biases, indices, table_rows, out_rows, kb, gshift, out, out_bf16, stream);
         case 3: return dispatch_out<3>(packed, scales, biases, indices, table_rows, out_rows, kb, gshift, out, out_bf16, stream);
         case 4: return dispatch_out<4>(packed, scales, biases, indices, table_rows, out_rows, kb, gshift, out, out_bf16, stream);

@@ -756,6 +756,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
         return hipSuccess;
     }
     switch (bits) {
+        case 1: return launch_bits<1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 2: return launch_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 3: return launch_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 4: return launch_bits<4>(x, m, packed, scales, biases, n, kb, gshift, y, stream);

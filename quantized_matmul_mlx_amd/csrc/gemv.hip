@@ -102,6 +102,22 @@ template <> struct Codes<2> {
     }
 };
 
+// 1-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values 128 + c. x is staged in halves of 16, so
+// a pair must stay within a half: swapping the word's middle bytes puts c_{8..15} at bits 16..23
+// and c_{16..23} at bits 8..15, after which bits i and i + 16 are such a pair.
+template <> struct Codes<1> {
+    static constexpr float kOffset = 128.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[1], uint32_t (&pr)[16]) {
+        const uint32_t v = __builtin_amdgcn_perm(w[0], w[0], 0x03010200u);  // bytes b0 b2 b1 b3
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pr[i] = and_or(v >> i, 0x00010001u, kMagic);
+    }
+    // the 2-bit pairing of x: pair 8q + p takes x_{16q+p} and x_{16q+p+8}
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+        Codes<2>::pair_x(xn, xp);
+    }
+};
+
 // 8-bit: pair 2q + h = (c_{4q+2h}, c_{4q+2h+1}), exact values c (offset 0).
 template <> struct Codes<8> {
     static constexpr float kOffset = 0.f;
@@ -687,6 +703,7 @@ hipError_t launch_gemv_gather(const void* x, bool x_f32, int64_t m, const uint32
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_gather_bits<1>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 2: return launch_gather_bits<2>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 3: return launch_gather_bits<3>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 4: return launch_gather_bits<4>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, g, stream);
@@ -703,6 +720,7 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_bits<1>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 2: return launch_bits<2>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 3: return launch_bits<3>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 4: return launch_bits<4>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
@@ -719,6 +737,7 @@ hipError_t launch_gemv_fused(const uint16_t* x, int64_t m, const uint32_t* packe
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_bf16_m<1, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
         case 2: return launch_bf16_m<2, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
         case 3: return launch_bf16_m<3, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
         case 4: return launch_bf16_m<4, true>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);

@@ -554,6 +554,7 @@ hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t*
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_gather_bits<1>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 2: return launch_gather_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 3: return launch_gather_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
         case 4: return launch_gather_bits<4>(x, m, packed, scales, biases, n, kb, gshift, y, g, stream);
@@ -574,6 +575,7 @@ hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_bits<1>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 2: return launch_bits<2>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 3: return launch_bits<3>(x, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 4: return launch_bits<4>(x, m, packed, scales, biases, n, kb, gshift, y, stream);

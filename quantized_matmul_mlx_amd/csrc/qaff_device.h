@@ -40,7 +40,9 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float v) {
 // of 2-4 dwords accept any dword-aligned address.
 template <int BITS>
 __device__ __forceinline__ void load_block(const uint32_t* __restrict__ p, uint32_t (&w)[BITS]) {
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 1) {
+        w[0] = p[0];
+    } else if constexpr (BITS == 2) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(p);
         w[0] = v.x; w[1] = v.y;
     } else if constexpr (BITS == 3) {

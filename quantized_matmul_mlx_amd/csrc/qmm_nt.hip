@@ -206,6 +206,7 @@ hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* p
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     float* ws = static_cast<float*>(workspace);
     switch (bits) {
+        case 1: return launch_bits<1>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
         case 2: return launch_bits<2>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
         case 3: return launch_bits<3>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
         case 4: return launch_bits<4>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);

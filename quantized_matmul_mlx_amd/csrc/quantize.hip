@@ -148,6 +148,7 @@ hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t co
     const uint64_t blocks = (uint64_t)rows * (uint64_t)(cols / 32);
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
+        case 1: return launch_bits<1>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
         case 2: return launch_bits<2>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
         case 3: return launch_bits<3>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);
         case 4: return launch_bits<4>(w, in_bf16, blocks, gshift, packed, scales, biases, stream);

@@ -40,7 +40,7 @@ def bf16_rand(rng, shape, scale=1.0):
     return W.bf16_bits_from_f32((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("m", [1, 3, 16])
 def test_gate_up(orc, bits, G, m):
@@ -62,7 +62,7 @@ def test_gate_up(orc, bits, G, m):
         assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("m,with_resid", [(1, False), (1, True), (3, True), (16, False)])
 def test_silu_gate(orc, bits, G, m, with_resid):

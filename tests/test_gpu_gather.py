@@ -93,7 +93,7 @@ def check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, kerne
 
 # ---- batched: any lhs / rhs ------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits,G,x_dtype,m", [(4, 64, "bf16", 1), (3, 32, "f32", 3), (8, 128, "bf16", 2),
+@pytest.mark.parametrize("bits,G,x_dtype,m", [(4, 64, "bf16", 1), (3, 32, "f32", 3), (8, 128, "bf16", 2), (1, 32, "f32", 2),
                                               (6, 32, "bf16", 5), (2, 64, "f32", 1), (5, 128, "bf16", 17)])
 def test_gather_valu_batched(orc, bits, G, x_dtype, m):
     E, n, k = 4, 150, 640   # 20 blocks of 32 per row: not a whole pass of the GEMV
@@ -106,7 +106,7 @@ def test_gather_valu_batched(orc, bits, G, x_dtype, m):
     check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, "gemv")
 
 
-@pytest.mark.parametrize("bits,G,m,k", [(4, 64, 1, 512), (4, 128, 5, 2048), (3, 32, 16, 1024), (8, 64, 20, 512),
+@pytest.mark.parametrize("bits,G,m,k", [(4, 64, 1, 512), (4, 128, 5, 2048), (3, 32, 16, 1024), (8, 64, 20, 512), (1, 64, 3, 1024),
                                         (6, 32, 4, 4096), (2, 128, 9, 1536), (5, 64, 33, 512)])
 def test_gather_mfma_batched(orc, bits, G, m, k):
     E, n = 5, 150
@@ -132,6 +132,7 @@ def sorted_rows(counts):
     (3, 32, 4096, [5, 9, 0, 0, 0, 7]),
     (6, 64, 1536, [0, 0, 0, 0, 0, 0, 0, 12]),    # only the last expert
     (2, 64, 512, [33]),
+    (1, 128, 2048, [2, 0, 7]),
 ])
 def test_gather_mfma_grouped(orc, bits, G, k, counts):
     E, n = len(counts), 100

@@ -132,7 +132,7 @@ def test_ref_workload_qmm_bf16_paths(orc, path):
 
 # ---- dequantize at every bit width and group size ----------------------------------------------
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_dequant_bit_exact(orc, bits, G):
     inp = W.random_inputs(bits, G, 67, G * 6, 0, seed=100 + bits * 7 + G)
@@ -149,7 +149,7 @@ def test_dequant_bit_exact(orc, bits, G):
 KB_FOR_G = {32: 97, 64: 98, 128: 100}   # blocks per row: > 64 lanes, not a multiple of 64
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("m,x_dtype", [(1, "bf16"), (3, "bf16"), (16, "bf16"), (4, "f32"), (5, "f32")])
 def test_gemv(orc, bits, G, m, x_dtype):
@@ -162,7 +162,7 @@ def test_gemv(orc, bits, G, m, x_dtype):
 
 # Long rows at M <= 2 take wider passes (8 or 4 blocks per lane): 300 blocks (one ragged pass) and
 # 520 blocks (more than one pass at M = 1, ragged).
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("m,kb", [(1, 300), (2, 300), (1, 520)])
 def test_gemv_long_rows(orc, bits, G, m, kb):
@@ -173,7 +173,7 @@ def test_gemv_long_rows(orc, bits, G, m, kb):
     check_qmm(orc, inp, y, path="gemv")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 128])
 @pytest.mark.parametrize("m,n", [(17, 129), (130, 200), (257, 64)])
 def test_gemm(orc, bits, G, m, n):
@@ -213,7 +213,7 @@ def test_dispatch_boundary_all_paths(orc, m):
 # The matrix-core decode kernel: every width and group size, m from 1 to 16, ragged n (not a
 # multiple of 16), K from one to eight 512-code slices, and n large enough for 2 and 4 row tiles
 # per block.
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("m,n,k", [(1, 150, 512), (3, 150, 1536), (8, 77, 4096), (16, 150, 2048)])
 def test_gemv_mfma(orc, bits, G, m, n, k):

@@ -52,7 +52,7 @@ def run_check(orc, bits, G, k, n, m, x_dtype, seed):
 
 
 @pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_qmm_nt(orc, x_dtype, bits, G):
     # k = 100 rows (not a multiple of the 16 row phases), n = 5 G (a ragged column tile), M = 3

@@ -50,7 +50,7 @@ def check(orc, w, dtype, G, bits):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_quantize_bit_exact(orc, dtype, bits, G):
     # 37 rows (a ragged last thread block) of 5 groups
