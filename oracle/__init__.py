@@ -23,6 +23,9 @@ patterns. What each function computes, and the page passage it follows, is docum
   ``gather_qmm`` and ``gather_indices``).
 * ``silu_gate`` / ``silu_gate_qmm`` -- the fused decode products' activation and product
   (spark_runtime ``gemv_silu_gate``).
+* ``dequantize_typed`` / ``qmm_typed`` -- the same with float16, bfloat16 or float32 scales, biases
+  and x (nuvec_core: x, scales and biases promote to one float type); ``f16_to_f32`` /
+  ``f32_to_f16`` -- IEEE binary16 widening and round-to-nearest-even narrowing, by hand.
 * ``quantize`` -- w -> packed codes, bf16 scales and biases: bias = group min, scale =
   (max - min) / (2^bits - 1), code = round((w - bias) / scale) clamped (nuvec_core module
   documentation and ``quantize``; rlx-moshi: bias = group min).
@@ -84,15 +87,21 @@ def _load():
                             _int, _f64p, _int]
     lib.orc_gather_qmm.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64,
                                    _i64, _int, ctypes.c_void_p, ctypes.c_void_p, _i64, _f64p, _int]
+    lib.orc_f16_to_f32.argtypes = [_u16p, _i64, _f32p]
+    lib.orc_f32_to_f16.argtypes = [_f32p, _i64, _u16p]
+    lib.orc_dequantize_typed.argtypes = [_u32p, ctypes.c_void_p, ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _f32p]
+    lib.orc_qmm_typed.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, ctypes.c_void_p, ctypes.c_void_p, _int, _i64, _i64,
+                                  _i64, _int, _f64p]
     lib.orc_qmm_nt.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _f64p]
     lib.orc_quantize.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, _u16p, _u16p]
     lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
     lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
-                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize", "orc_qmm_nt"):
+                 "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize", "orc_qmm_nt",
+                 "orc_dequantize_typed", "orc_qmm_typed"):
         getattr(lib, name).restype = _int
-    for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate"):
+    for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate", "orc_f16_to_f32", "orc_f32_to_f16"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -335,6 +344,59 @@ def quantize(w, w_dtype: str, group_size: int, bits: int):
     _check(_load().orc_quantize(wa.ctypes.data, 1 if w_dtype == "bf16" else 0, rows, cols, group_size, bits,
                                 packed, sc, bi), "quantize")
     return packed, sc, bi
+
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def f16_to_f32(h: np.ndarray) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    _load().orc_f16_to_f32(h.reshape(-1), h.size, out.reshape(-1))
+    return out
+
+
+def f32_to_f16(a: np.ndarray) -> np.ndarray:
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_f32_to_f16(a.reshape(-1), a.size, out.reshape(-1))
+    return out
+
+
+def _typed(a, dtype):
+    """float32 array for "f32", uint16 bit patterns for "bf16" / "f16"."""
+    return _c(a, np.float32 if dtype == "f32" else np.uint16)
+
+
+def dequantize_typed(packed, scales, biases, sb_dtype: str, group_size: int, bits: int, out: str = "f32"):
+    """Dense [rows, cols] from scales and biases of dtype ``sb_dtype`` ("f32", "bf16", "f16"): w = s*c
+    then + b in float32, returned as float32 or rounded to "bf16" / "f16" (bit patterns)."""
+    packed = _c(np.atleast_2d(packed), np.uint32)
+    sc, bi = _typed(np.atleast_2d(scales), sb_dtype), _typed(np.atleast_2d(biases), sb_dtype)
+    rows, cols = packed.shape[0], packed.shape[1] * 32 // bits
+    res = np.empty((rows, cols), np.float32)
+    _check(_load().orc_dequantize_typed(packed, sc.ctypes.data, bi.ctypes.data, DTYPES[sb_dtype], rows, cols,
+                                        group_size, bits, res), "dequantize_typed")
+    if out == "f32":
+        return res
+    if out == "bf16":
+        return f32_to_bf16(res)
+    if out == "f16":
+        return f32_to_f16(res)
+    raise ValueError(out)
+
+
+def qmm_typed(x, x_dtype: str, packed, scales, biases, sb_dtype: str, group_size: int, bits: int) -> np.ndarray:
+    """y = x . dequantize(W)^T in float64 with x and the scales/biases of any of the three types."""
+    xa = _typed(np.atleast_2d(x), x_dtype)
+    packed = _c(packed, np.uint32)
+    sc, bi = _typed(scales, sb_dtype), _typed(biases, sb_dtype)
+    m, k = xa.shape
+    n = packed.shape[0]
+    out = np.empty((m, n), np.float64)
+    _check(_load().orc_qmm_typed(xa.ctypes.data, DTYPES[x_dtype], m, packed, sc.ctypes.data, bi.ctypes.data,
+                                 DTYPES[sb_dtype], n, k, group_size, bits, out), "qmm_typed")
+    return out
 
 
 def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:

@@ -430,3 +430,102 @@ int orc_qmm_nt(const void* x, int x_is_bf16, int64_t m, const uint32_t* packed, 
     free(w);
     return 0;
 }
+
+/* ---- other float types of x, scales and biases -------------------------------------------- */
+
+/* [nuvec] quantized_matmul and dequantize promote x, scales and biases to one float type, and
+ * scales keep the weight's dtype (float16, bfloat16 or float32). dtype codes: 0 float32,
+ * 1 bfloat16 (bits), 2 float16 (bits). */
+
+/* IEEE binary16 -> float32, exact: sign, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is
+ * zero or subnormal (fraction * 2^-24), exponent 31 is infinity or NaN. */
+static float f16_to_f32(uint16_t h) {
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 10) & 31;
+    const int f = h & 1023;
+    float v;
+    if (e == 0) v = ldexpf((float)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexpf((float)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+void orc_f16_to_f32(const uint16_t* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_to_f32(in[i]);
+}
+
+/* float32 -> binary16, round to nearest, ties to even: the value is scaled to an integer count of
+ * the target's units (2^-24 below 2^-14, else 2^(e-10) for its binade), rounded with ties to
+ * even, and re-encoded; a result of 65520 or more (the midpoint above 65504) is infinity. */
+static uint16_t f32_to_f16_rne(float v) {
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (v != v) return (uint16_t)(sign | 0x7e00u);
+    const double a = fabs((double)v);
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+    int e;
+    frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+    int unit_exp = e - 11;            /* 11 significant bits */
+    if (unit_exp < -24) unit_exp = -24; /* subnormal spacing */
+    const double q = ldexp(a, -unit_exp);
+    double r = floor(q);
+    const double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    /* r units of 2^unit_exp; re-encode (r may have carried into the next binade) */
+    const double val = ldexp(r, unit_exp);
+    if (val == 0.0) return sign;
+    int e2;
+    frexp(val, &e2);
+    const int E = e2 - 1 + 15; /* biased exponent of val = 1.f * 2^(e2-1) */
+    if (E <= 0) return (uint16_t)(sign | (uint16_t)ldexp(val, 24)); /* subnormal */
+    const uint16_t frac_bits = (uint16_t)(ldexp(val, -(e2 - 1)) * 1024.0 - 1024.0);
+    return (uint16_t)(sign | (uint16_t)(E << 10) | frac_bits);
+}
+
+void orc_f32_to_f16(const float* in, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_rne(in[i]);
+}
+
+static float widen(const void* p, int64_t i, int dtype) {
+    if (dtype == 1) return bf16_to_f32(((const uint16_t*)p)[i]);
+    if (dtype == 2) return f16_to_f32(((const uint16_t*)p)[i]);
+    return ((const float*)p)[i];
+}
+
+/* [moshi] dequantize_affine with scales and biases of any of the three types: w = s * c, then
+ * + b, both in float32 (two roundings as written: with float32 scales the product is not always
+ * exact). out float32 [rows, cols]. */
+int orc_dequantize_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
+                         int64_t rows, int64_t cols, int64_t group, int bits, float* out) {
+    if (rows < 0 || sb_dtype < 0 || sb_dtype > 2 || !valid_params(cols, group, bits)) return -1;
+    const int64_t words = cols * bits / 32, groups = cols / group;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint32_t code = code_at(packed + r * words, c, bits);
+            const float s = widen(scales, r * groups + c / group, sb_dtype);
+            const float b = widen(biases, r * groups + c / group, sb_dtype);
+            const float prod = s * (float)code;
+            out[r * cols + c] = prod + b;
+        }
+    return 0;
+}
+
+/* [nuvec] quantized_matmul (transpose) with x and the scales and biases of any of the three types:
+ * y[m, n] = sum_k x[m, k] w[n, k] in double, w as orc_dequantize_typed forms it. */
+int orc_qmm_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                  const void* biases, int sb_dtype, int64_t n, int64_t k, int64_t group, int bits, double* out) {
+    if (m < 0 || n < 0 || x_dtype < 0 || x_dtype > 2) return -1;
+    float* w = (float*)malloc(sizeof(float) * (size_t)(n * k > 0 ? n * k : 1));
+    if (!w) return -2;
+    const int rc = orc_dequantize_typed(packed, scales, biases, sb_dtype, n, k, group, bits, w);
+    if (rc != 0) { free(w); return rc; }
+    for (int64_t mm = 0; mm < m; ++mm)
+        for (int64_t nn = 0; nn < n; ++nn) {
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk) acc += (double)widen(x, mm * k + kk, x_dtype) * (double)w[nn * k + kk];
+            out[mm * n + nn] = acc;
+        }
+    free(w);
+    return 0;
+}

@@ -639,3 +639,76 @@ def test_qmm_nt_and_qmm_agree_on_a_symmetric_weight(oracle_lib):
     y_nt = oracle_lib.qmm_nt(x, "f32", packed, sc, bi, 64, 4)
     y_t = oracle_lib.qmm(x, "f32", packed, sc, bi, 64, 4)
     np.testing.assert_array_equal(y_nt, y_t)
+
+
+# ---- float16 and float32 scales, biases and x -----------------------------------------------------
+
+def test_f16_widening_matches_numpy(oracle_lib):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)      # every binary16 pattern
+    got = oracle_lib.f16_to_f32(h)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_f16_narrowing_matches_numpy(oracle_lib):
+    rng = np.random.default_rng(3)
+    a = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * np.float32(10.0) ** rng.integers(-9, 5, 200000),
+        # exact midpoints between neighbours (ties), around subnormals, near the overflow point
+        (np.arange(1, 2048, dtype=np.float32) + 0.5) * np.float32(2.0 ** -24),
+        (np.arange(1024, 2048, dtype=np.float32) + 0.5) * np.float32(2.0 ** -10),
+        np.array([65504.0, 65519.0, 65520.0, 70000.0, -65520.0, 0.0, -0.0, 6e-8, 3e-8, 2.9e-8], np.float32),
+    ]).astype(np.float32)
+    got = oracle_lib.f32_to_f16(a)
+    with np.errstate(over="ignore"):
+        ref = a.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("sb", ["f16", "f32", "bf16"])
+def test_dequantize_typed_is_the_affine_rule(oracle_lib, sb):
+    # w = s * c then + b in float32, with s and b read in their own type: against numpy float32
+    # arithmetic on the same widened values (two roundings, as written)
+    inp = W.random_inputs(5, 32, 6, 128, 0, seed=31)
+    rng = np.random.default_rng(32)
+    s32 = rng.uniform(1e-3, 2e-2, (6, 4)).astype(np.float32)
+    b32 = rng.uniform(-0.15, 0.0, (6, 4)).astype(np.float32)
+    if sb == "f16":
+        sc, bi = s32.astype(np.float16).view(np.uint16), b32.astype(np.float16).view(np.uint16)
+        sw, bw = sc.view(np.float16).astype(np.float32), bi.view(np.float16).astype(np.float32)
+    elif sb == "bf16":
+        sc, bi = W.bf16_bits_from_f32(s32), W.bf16_bits_from_f32(b32)
+        sw, bw = W.f32_from_bf16_bits(sc), W.f32_from_bf16_bits(bi)
+    else:
+        sc, bi, sw, bw = s32, b32, s32, b32
+    codes = oracle_lib.unpack_codes(inp.packed, 128, 5).astype(np.float32)
+    g = np.arange(128) // 32
+    ref = (sw[:, g] * codes).astype(np.float32) + bw[:, g]
+    got = oracle_lib.dequantize_typed(inp.packed, sc, bi, sb, 32, 5)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.astype(np.float32).view(np.uint32))
+    if sb == "bf16":   # the typed form with bf16 scales is the plain dequantization
+        np.testing.assert_array_equal(got, oracle_lib.dequantize(inp.packed, sc, bi, 32, 5))
+
+
+def test_qmm_typed_reduces_to_qmm(oracle_lib):
+    inp = W.random_inputs(4, 64, 9, 256, 3, seed=33)
+    np.testing.assert_array_equal(
+        oracle_lib.qmm_typed(inp.x, "bf16", inp.packed, inp.scales, inp.biases, "bf16", 64, 4),
+        oracle_lib.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases, 64, 4))
+    # a float16 x holding the same values as the bf16 one gives the same product
+    xf = W.f32_from_bf16_bits(inp.x)
+    x16 = xf.astype(np.float16)
+    exact = x16.astype(np.float32) == xf
+    xf = np.where(exact, xf, 0).astype(np.float32)
+    y16 = oracle_lib.qmm_typed(xf.astype(np.float16).view(np.uint16), "f16", inp.packed, inp.scales, inp.biases,
+                               "bf16", 64, 4)
+    y32 = oracle_lib.qmm_typed(xf, "f32", inp.packed, inp.scales, inp.biases, "bf16", 64, 4)
+    np.testing.assert_array_equal(y16, y32)
+    # against numpy float64 over the typed dequantization
+    s16 = W.f32_from_bf16_bits(inp.scales).astype(np.float16).view(np.uint16)
+    b16 = W.f32_from_bf16_bits(inp.biases).astype(np.float16).view(np.uint16)
+    w = oracle_lib.dequantize_typed(inp.packed, s16, b16, "f16", 64, 4).astype(np.float64)
+    y = oracle_lib.qmm_typed(xf, "f32", inp.packed, s16, b16, "f16", 64, 4)
+    np.testing.assert_allclose(y, xf.astype(np.float64) @ w.T, rtol=1e-12, atol=1e-12)
