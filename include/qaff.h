@@ -48,7 +48,7 @@ typedef enum {
     QAFF_ERR_DEVICE = 3
 } qaff_status;
 
-typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1 } qaff_dtype;
+typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1, QAFF_F16 = 2 } qaff_dtype;
 
 /* Kernel choice for qaff_qmm_ex. AUTO: float32 x -> the VALU kernel at any m; bf16 x with
  * m <= qaff_gemv_max_m() -> the decode path: the VALU GEMV for m below qaff_gemv_mfma_min_m(),
@@ -68,6 +68,40 @@ typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2, QAFF_
 qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                             int64_t rows, int64_t cols, int32_t group_size, int32_t bits,
                             void* out, qaff_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Other float types (nuvec_core quantized.rs: quantized_matmul and dequantize promote x, scales and
+ * biases to one float type; scales keep the weight's dtype). QAFF_F16 is accepted only by the
+ * *_typed entry points below; every other entry point takes float32 or bf16 x and bf16 scales.
+ *
+ * qaff_promote_dtype: the common type of two dtypes, as y's dtype: equal types stay, anything
+ * else (float32 with anything, bf16 with float16) is float32.
+ */
+qaff_dtype qaff_promote_dtype(qaff_dtype a, qaff_dtype b);
+
+/*
+ * Dense dequantization with scales and biases of sb_dtype (float32, bf16 or float16):
+ * w = s * c, then + b, in float32 (two roundings as written: with float32 scales the product is not
+ * always exact), stored in out_dtype (float32, bf16 or float16, round to nearest even).
+ *   scales and biases [rows, cols/group_size] of sb_dtype; out [rows, cols] of out_dtype.
+ * bf16 scales with a float32 or bf16 output take qaff_dequantize's kernel (the same values).
+ * Errors: as qaff_dequantize, plus INVALID_ARGUMENT for an unknown dtype or scales and biases not
+ * aligned to their element size.
+ */
+qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, const void* biases,
+                                  qaff_dtype sb_dtype, int64_t rows, int64_t cols, int32_t group_size,
+                                  int32_t bits, void* out, qaff_dtype out_dtype, hipStream_t stream);
+
+/*
+ * y = x . dequantize(W)^T with x of x_dtype and scales and biases of sb_dtype (each float32, bf16 or
+ * float16); y [m, n] of qaff_promote_dtype(x_dtype, sb_dtype); float32 sums.
+ * bf16 scales with a float32 or bf16 x take qaff_qmm's kernels (QAFF_PATH_AUTO); every other
+ * combination runs on a VALU GEMV that reads the types as given (any m, any k).
+ * Errors: as qaff_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.
+ */
+qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                           const void* scales, const void* biases, qaff_dtype sb_dtype, int64_t n,
+                           int64_t k, int32_t group_size, int32_t bits, void* y, hipStream_t stream);
 
 /*
  * Quantization of a dense weight into this format (nuvec_core quantized.rs: module documentation

@@ -36,6 +36,16 @@ _BF16_BITS_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
 _INDEX_DTYPES = (torch.int32, torch.uint32)
 _GATHER_INDEX_DTYPES = (torch.int32, torch.uint32, torch.int64)
 _OUT_DTYPES = {torch.float32: _lib.QAFF_F32, torch.bfloat16: _lib.QAFF_BF16}
+# every float type the typed entry points take (x, scales and biases, outputs)
+_ANY_DTYPES = {torch.float32: _lib.QAFF_F32, torch.bfloat16: _lib.QAFF_BF16, torch.float16: _lib.QAFF_F16}
+_FROM_CODE = {v: k for k, v in _ANY_DTYPES.items()}
+_SCALE_DTYPES = _BF16_BITS_DTYPES + (torch.float16, torch.float32)
+
+
+def _sb_code(scales):
+    """dtype code of the scales: float16 and float32 tensors as such, anything else bf16 bits."""
+    return _ANY_DTYPES.get(scales.dtype, _lib.QAFF_BF16) if scales.dtype in (torch.float16, torch.float32) \
+        else _lib.QAFF_BF16
 
 
 def _need(t, name, dtypes, device=None):
@@ -51,11 +61,18 @@ def _need(t, name, dtypes, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _weights(packed, scales, biases, group_size, bits):
+def _weights(packed, scales, biases, group_size, bits, typed=False):
+    """Checks a weight; returns (device, rows, cols). Only ``typed`` callers (qmm, dequantize) take
+    float16 or float32 scales and biases; the other operations read bf16 ones."""
     _need(packed, "packed", _PACKED_DTYPES)
     dev = packed.device
-    _need(scales, "scales", _BF16_BITS_DTYPES, dev)
-    _need(biases, "biases", _BF16_BITS_DTYPES, dev)
+    _need(scales, "scales", _SCALE_DTYPES, dev)
+    _need(biases, "biases", _SCALE_DTYPES, dev)
+    if _sb_code(scales) != _sb_code(biases):
+        raise TypeError(f"scales ({scales.dtype}) and biases ({biases.dtype}) differ in type")
+    if not typed and _sb_code(scales) != _lib.QAFF_BF16:
+        raise TypeError(f"this operation reads bf16 scales and biases, got {scales.dtype} "
+                        "(float16 and float32 scales are taken by qmm and dequantize)")
     if packed.dim() != 2 or scales.dim() != 2 or biases.dim() != 2:
         raise ValueError("packed, scales and biases must be 2-D")
     rows, words = packed.shape
@@ -92,11 +109,12 @@ def gemv_mfma_min_m() -> int:
 
 def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=torch.float32,
                out=None):
-    """Dense ``[rows, cols]`` weights (rlx-moshi ``dequantize_affine``; maya2_mlx ``QW.dense``)."""
+    """Dense ``[rows, cols]`` weights (rlx-moshi ``dequantize_affine``; maya2_mlx ``QW.dense``).
+    Scales and biases may be bf16, float16 or float32, and the output float32, bf16 or float16."""
     lib = _lib.load()
-    dev, rows, cols = _weights(packed, scales, biases, group_size, bits)
-    if out_dtype not in _OUT_DTYPES:
-        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    dev, rows, cols = _weights(packed, scales, biases, group_size, bits, typed=True)
+    if out_dtype not in _ANY_DTYPES:
+        raise TypeError(f"out_dtype must be float32, bfloat16 or float16, got {out_dtype}")
     if out is None:
         out = torch.empty((rows, cols), dtype=out_dtype, device=dev)
     else:
@@ -104,8 +122,8 @@ def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=tor
         if tuple(out.shape) != (rows, cols):
             raise ValueError(f"out must be [{rows}, {cols}]")
     with torch.cuda.device(dev):
-        _lib.check(lib.qaff_dequantize(_p(packed), _p(scales), _p(biases), rows, cols, group_size,
-                                       bits, _p(out), _OUT_DTYPES[out_dtype], _stream(dev)))
+        _lib.check(lib.qaff_dequantize_typed(_p(packed), _p(scales), _p(biases), _sb_code(scales), rows, cols,
+                                             group_size, bits, _p(out), _ANY_DTYPES[out_dtype], _stream(dev)))
     return out
 
 
@@ -172,7 +190,10 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
     its default indices.
 
     ``transpose=False`` computes ``x . dequantize(W)`` for a weight stored ``[k, n]``
-    (``qmm_nt``)."""
+    (``qmm_nt``).
+
+    x may also be float16, and the scales and biases float16 or float32: x, scales and biases then
+    promote to one type (float32 unless they agree), which is y's type."""
     if not transpose:
         if path != "auto":
             raise ValueError("the product without the transpose has one kernel: path 'auto'")
@@ -184,12 +205,30 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
         y = gather_qmm(x[None] if vector else x, packed, scales, biases, group_size, bits, path=path, out=out)
         return y.squeeze(-2) if vector else y
     lib = _lib.load()
-    dev, n, k = _weights(packed, scales, biases, group_size, bits)
-    _need(x, "x", tuple(_OUT_DTYPES), dev)
+    dev, n, k = _weights(packed, scales, biases, group_size, bits, typed=True)
+    _need(x, "x", tuple(_ANY_DTYPES), dev)
     if x.shape[-1] != k:
         raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
     if path not in _lib.PATHS:
         raise ValueError(f"path must be one of {tuple(_lib.PATHS)}")
+    sb = _sb_code(scales)
+    if sb != _lib.QAFF_BF16 or x.dtype == torch.float16:
+        # x, scales and biases promote to one type (float32 unless they agree); the typed kernel
+        if path != "auto":
+            raise ValueError("float16 x or non-bf16 scales run on one kernel: path 'auto'")
+        lead = tuple(x.shape[:-1])
+        m = math.prod(lead)
+        yt = _FROM_CODE[int(lib.qaff_promote_dtype(_ANY_DTYPES[x.dtype], sb))]
+        if out is None:
+            out = torch.empty(lead + (n,), dtype=yt, device=dev)
+        else:
+            _need(out, "out", (yt,), dev)
+            if tuple(out.shape) != lead + (n,):
+                raise ValueError(f"out must be {list(lead + (n,))}")
+        with torch.cuda.device(dev):
+            _lib.check(lib.qaff_qmm_typed(_p(x), _ANY_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), sb, n,
+                                          k, group_size, bits, _p(out), _stream(dev)))
+        return out
     lead = tuple(x.shape[:-1])
     m = math.prod(lead)
     x2 = x.reshape(m, k)
@@ -239,7 +278,7 @@ class QWeight:
     def __init__(self, q, scales, biases, bits: int, group_size: int):
         self.q, self.scales, self.biases = q, scales, biases
         self.bits, self.group_size = int(bits), int(group_size)
-        _, rows, cols = _weights(q, scales, biases, self.group_size, self.bits)
+        _, rows, cols = _weights(q, scales, biases, self.group_size, self.bits, typed=True)
         self.shape = (rows, cols)
 
     def dense(self, dtype=torch.float32):

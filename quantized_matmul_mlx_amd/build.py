@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqaff.so")
 
-SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip"]
+SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip", "typed.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -80,6 +80,7 @@ qaff_status check_weight(const char* op, const uint32_t* packed, const uint16_t*
 }
 
 bool valid_dtype(qaff_dtype d) { return d == QAFF_F32 || d == QAFF_BF16; }
+bool any_dtype(qaff_dtype d) { return d == QAFF_F32 || d == QAFF_BF16 || d == QAFF_F16; }
 
 qaff_status dequant_common(const char* op, const uint32_t* packed, const uint16_t* scales,
                            const uint16_t* biases, int64_t table_rows, int64_t cols,
@@ -335,6 +336,59 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                             int32_t sorted_indices, void* y, hipStream_t stream) {
     return qaff_gather_qmm_ex(x, x_dtype, x_batches, m, packed, scales, biases, w_batches, n, k, group_size, bits,
                               lhs_indices, rhs_indices, batch, sorted_indices, y, stream, QAFF_PATH_AUTO);
+}
+
+qaff_dtype qaff_promote_dtype(qaff_dtype a, qaff_dtype b) { return a == b ? a : QAFF_F32; }
+
+qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, const void* biases, qaff_dtype sb_dtype,
+                                  int64_t rows, int64_t cols, int32_t group_size, int32_t bits, void* out,
+                                  qaff_dtype out_dtype, hipStream_t stream) {
+    static const char* op = "qaff_dequantize_typed";
+    g_error.clear();
+    if (!any_dtype(sb_dtype) || !any_dtype(out_dtype))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown dtype (%d, %d)", op, (int)sb_dtype, (int)out_dtype);
+    if (sb_dtype == QAFF_BF16 && out_dtype != QAFF_F16)
+        return qaff_dequantize(packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases), rows,
+                               cols, group_size, bits, out, out_dtype, stream);
+    // the weight checks, with the scales' own alignment
+    qaff_status st = check_weight(op, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                                  rows, cols, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (rows == 0 || cols == 0) return QAFF_OK;
+    if (sb_dtype == QAFF_F32 && (!aligned(scales, 4) || !aligned(biases, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
+    if (!out) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
+    if (!aligned(out, 4)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be 4-byte aligned", op);
+    return after_launch(op, qaff::launch_dequant_typed(packed, scales, biases, (int)sb_dtype, rows, cols, group_size,
+                                                       bits, out, (int)out_dtype, stream), stream);
+}
+
+qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                           const void* biases, qaff_dtype sb_dtype, int64_t n, int64_t k, int32_t group_size,
+                           int32_t bits, void* y, hipStream_t stream) {
+    static const char* op = "qaff_qmm_typed";
+    g_error.clear();
+    if (!any_dtype(x_dtype) || !any_dtype(sb_dtype))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown dtype (%d, %d)", op, (int)x_dtype, (int)sb_dtype);
+    if (sb_dtype == QAFF_BF16 && x_dtype != QAFF_F16)
+        return qaff_qmm_ex(x, x_dtype, m, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                           n, k, group_size, bits, y, stream, QAFF_PATH_AUTO);
+    qaff_status st = check_weight(op, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                                  n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
+    if (m == 0 || n == 0) return QAFF_OK;
+    if (sb_dtype == QAFF_F32 && k > 0 && (!aligned(scales, 4) || !aligned(biases, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    const qaff_dtype yt = qaff_promote_dtype(x_dtype, sb_dtype);
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * (yt == QAFF_F32 ? 4 : 2), stream), stream);
+    if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    return after_launch(op, qaff::launch_gemv_typed(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
+                                                    group_size, bits, y, (int)yt, stream), stream);
 }
 
 size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits) {

@@ -92,6 +92,14 @@ hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* p
                          const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
                          void* y, hipStream_t stream);
 
+// Other float types (dtype codes 0 float32, 1 bf16, 2 float16) for scales, biases, x and outputs.
+hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
+                                int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,
+                                hipStream_t stream);
+hipError_t launch_gemv_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                             const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits, void* y,
+                             int y_dtype, hipStream_t stream);
+
 // Writes `bytes` zero bytes (bytes % 2 == 0, p 2-byte aligned) with a kernel, so that the call
 // also behaves under stream capture.
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t stream);

@@ -1,0 +1,192 @@
+// Other float types for x, scales and biases (nuvec_core quantized.rs: `quantized_matmul` and
+// `dequantize` promote x, scales and biases to one float type; scales keep the weight's dtype,
+// float16, bfloat16 or float32). The bf16-scale paths have their own kernels; these take every
+// other combination, with the types as run-time (block-uniform) switches:
+//  * dequant_typed_kernel: w = s * c, then + b, in float32 with two roundings as written (with
+//    float32 scales the product is not always exact, so no fused multiply-add), stored as
+//    float32, bf16 or float16 (round to nearest even).
+//  * gemv_typed_kernel: y = x . dequantize(W)^T on the VALU, float32 sums, x of any of the three
+//    types, y in the promoted type. Per block of 32 codes: s * sum(x c) + b * sum(x).
+#include "launch.h"
+#include "qaff_device.h"
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+
+namespace qaff {
+namespace {
+
+constexpr int kTypedThreads = 256;
+
+// dtype codes: 0 float32, 1 bfloat16, 2 float16
+__device__ __forceinline__ float load_as_f32(const void* p, size_t i, int dtype) {
+    if (dtype == 1) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    if (dtype == 2) return __half2float(__ushort_as_half(static_cast<const uint16_t*>(p)[i]));
+    return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void store_from_f32(void* p, size_t i, int dtype, float v) {
+    if (dtype == 1) static_cast<uint16_t*>(p)[i] = to_bf16_bits(v);
+    else if (dtype == 2) static_cast<uint16_t*>(p)[i] = __half_as_ushort(__float2half_rn(v));
+    else static_cast<float*>(p)[i] = v;
+}
+
+// One thread per 32-code block.
+template <int BITS>
+__global__ __launch_bounds__(kTypedThreads) void dequant_typed_kernel(
+    const uint32_t* packed, const void* scales, const void* biases, int st, uint64_t blocks, uint32_t kb,
+    uint32_t gshift, void* out, int ot) {
+    // two roundings, product then sum: the compiler must not fuse them (device code contracts by
+    // default, and __fmul_rn / __fadd_rn are plain operators)
+#pragma clang fp contract(off)
+    const uint64_t idx = (uint64_t)blockIdx.x * kTypedThreads + threadIdx.x;
+    if (idx >= blocks) return;
+    const uint64_t row = idx / kb;
+    const uint32_t j = (uint32_t)(idx - row * kb);
+    uint32_t w[BITS];
+    load_block<BITS>(packed + idx * BITS, w);
+    const size_t gi = row * (kb >> gshift) + (j >> gshift);
+    const float s = load_as_f32(scales, gi, st);
+    const float b = load_as_f32(biases, gi, st);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+        const float prod = s * (float)code_at<BITS>(w, c);
+        store_from_f32(out, idx * 32 + c, ot, prod + b);
+    }
+}
+
+// A wave owns RW rows of W; lanes take the row's 32-code blocks l, l + 64, ...
+constexpr int kTypedRows = 2;
+
+template <int BITS, int MB>
+__global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
+    const void* x, int xt, uint32_t m, const uint32_t* packed, const void* scales, const void* biases, int st,
+    uint32_t n, uint32_t kb, uint32_t gshift, void* y, int yt) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t n0 = (blockIdx.x * (kTypedThreads / 64) + wave) * kTypedRows;
+    if (n0 >= n) return;  // wave-uniform; no block-level barrier
+    const uint32_t m0 = blockIdx.y * MB;
+    const uint32_t k = kb * 32;
+    const uint32_t gpr = kb >> gshift;
+
+    float acc[kTypedRows][MB];
+#pragma unroll
+    for (int r = 0; r < kTypedRows; ++r)
+#pragma unroll
+        for (int i = 0; i < MB; ++i) acc[r][i] = 0.f;
+
+    for (uint32_t j = lane; j < kb; j += 64) {
+        float xv[MB][32];
+        float xs[MB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const uint32_t xr = min(m0 + i, m - 1);
+            float t = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) {
+                xv[i][c] = m0 + i < m ? load_as_f32(x, (size_t)xr * k + (size_t)j * 32 + c, xt) : 0.f;
+                t += xv[i][c];
+            }
+            xs[i] = t;
+        }
+#pragma unroll
+        for (int r = 0; r < kTypedRows; ++r) {
+            const uint32_t row = n0 + r;
+            if (row >= n) break;
+            uint32_t w[BITS];
+            load_block<BITS>(packed + ((size_t)row * kb + j) * BITS, w);
+            const size_t gi = (size_t)row * gpr + (j >> gshift);
+            const float s = load_as_f32(scales, gi, st);
+            const float b = load_as_f32(biases, gi, st);
+            float cf[32];
+#pragma unroll
+            for (int c = 0; c < 32; ++c) cf[c] = (float)code_at<BITS>(w, c);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                float d = 0.f;
+#pragma unroll
+                for (int c = 0; c < 32; ++c) d = __builtin_fmaf(xv[i][c], cf[c], d);
+                acc[r][i] = __builtin_fmaf(s, d, __builtin_fmaf(b, xs[i], acc[r][i]));
+            }
+        }
+    }
+
+#pragma unroll
+    for (int r = 0; r < kTypedRows; ++r) {
+        const uint32_t row = n0 + r;
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+            const float v = wave_sum(acc[r][i]);
+            if (lane == 0 && row < n && m0 + i < m) store_from_f32(y, (size_t)(m0 + i) * n + row, yt, v);
+        }
+    }
+}
+
+template <int BITS>
+hipError_t launch_dequant_bits(const uint32_t* packed, const void* scales, const void* biases, int st, int64_t rows,
+                               int64_t kb, uint32_t gshift, void* out, int ot, hipStream_t stream) {
+    const uint64_t blocks = (uint64_t)rows * (uint64_t)kb;
+    const unsigned grid = (unsigned)((blocks + kTypedThreads - 1) / kTypedThreads);
+    dequant_typed_kernel<BITS><<<grid, kTypedThreads, 0, stream>>>(packed, scales, biases, st, blocks, (uint32_t)kb,
+                                                                   gshift, out, ot);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
+                            const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
+                            hipStream_t stream) {
+    constexpr int MB = 4;
+    const unsigned gx = (unsigned)((n + (kTypedThreads / 64) * kTypedRows - 1) / ((kTypedThreads / 64) * kTypedRows));
+    const size_t xsize = xt == 0 ? 4 : 2, ysize = yt == 0 ? 4 : 2;
+    const int64_t max_rows = (int64_t)65535 * MB;
+    for (int64_t m0 = 0; m0 < m; m0 += max_rows) {
+        const int64_t mm = m - m0 < max_rows ? m - m0 : max_rows;
+        const unsigned gy = (unsigned)((mm + MB - 1) / MB);
+        gemv_typed_kernel<BITS, MB><<<dim3(gx, gy), kTypedThreads, 0, stream>>>(
+            static_cast<const uint8_t*>(x) + (size_t)m0 * kb * 32 * xsize, xt, (uint32_t)mm, packed, scales, biases, st,
+            (uint32_t)n, (uint32_t)kb, gshift, static_cast<uint8_t*>(y) + (size_t)m0 * n * ysize, yt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
+                                int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,
+                                hipStream_t stream) {
+    const int64_t kb = cols / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 1: return launch_dequant_bits<1>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 2: return launch_dequant_bits<2>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 3: return launch_dequant_bits<3>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 4: return launch_dequant_bits<4>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 5: return launch_dequant_bits<5>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 6: return launch_dequant_bits<6>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 8: return launch_dequant_bits<8>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                             const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits, void* y,
+                             int y_dtype, hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 1: return launch_gemv_bits<1>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 2: return launch_gemv_bits<2>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 3: return launch_gemv_bits<3>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 4: return launch_gemv_bits<4>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 5: return launch_gemv_bits<5>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 6: return launch_gemv_bits<6>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 8: return launch_gemv_bits<8>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qaff

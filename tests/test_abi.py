@@ -252,3 +252,26 @@ def test_qmm_nt_checks(lib):
     assert qnt(lib, wsb=4) == INVALID                        # ... and must be large enough
     assert qnt(lib, ws=A4) == INVALID                        # ... and 16-byte aligned
     assert qnt(lib, m=0, x=NULL, y=NULL, ws=NULL) == OK
+
+
+def test_typed_checks(lib):
+    F16 = _lib.QAFF_F16
+    assert lib.qaff_promote_dtype(F16, F16) == F16
+    assert lib.qaff_promote_dtype(BF16, BF16) == BF16
+    assert lib.qaff_promote_dtype(BF16, F16) == F32
+    assert lib.qaff_promote_dtype(F32, F16) == F32
+    dq_t = lambda sb=F16, out=F32, scales=A16, o=A16, bits=4: lib.qaff_dequantize_typed(
+        A16, scales, A16, sb, 2, 64, 32, bits, o, out, NULL)
+    assert dq_t(sb=7) == INVALID
+    assert dq_t(out=9) == INVALID
+    assert dq_t(bits=7) == UNSUPPORTED
+    assert dq_t(sb=F32, scales=A2) == INVALID               # float32 scales are 4-byte aligned
+    assert dq_t(o=NULL) == INVALID
+    q_t = lambda xt=F16, sb=F16, x=A16, y=A16, scales=A16: lib.qaff_qmm_typed(
+        x, xt, 1, A16, scales, A16, sb, 4, 64, 32, 4, y, NULL)
+    assert q_t(xt=5) == INVALID
+    assert q_t(sb=F32, scales=A2) == INVALID
+    assert q_t(y=NULL) == INVALID
+    assert q_t(x=A2) == INVALID
+    # the old entry points keep their types: float16 is not one of them
+    assert lib.qaff_qmm(A16, F16, 1, A16, A16, A16, 4, 64, 32, 4, A16, NULL) == INVALID

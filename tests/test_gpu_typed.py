@@ -1,0 +1,125 @@
+"""float16 and float32 scales and biases, float16 x (x, scales and biases promote to one float
+type), on the GPU against the CPU oracle through the C ABI (via the binding).
+
+* dequantize: bit-exact (w = s * c, then + b, in float32 on both sides; bf16 and float16 outputs
+  rounded to nearest even on both sides).
+* qmm: per-row max relative error against the float64 oracle: 1e-4 for a float32 y (the kernel
+  sums float32 products, like the VALU GEMV), 1e-3 for a float16 y (one rounding to 11
+  significant bits, 2^-11 = 4.9e-4 of the row's largest value, plus float32 summation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc_mod
+from gpu_util import banner, dev_u32
+from quantized_matmul_mlx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = {torch.float32: 1e-4, torch.float16: 1e-3, torch.bfloat16: 4e-3}
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc_mod.build()
+    import quantized_matmul_mlx_amd as q
+    q._lib.load()
+    return orc_mod
+
+
+def qaff():
+    import quantized_matmul_mlx_amd as q
+    return q
+
+
+def scales_of(inp, sb, seed):
+    """Scales and biases of the workload's ranges as host arrays of type sb (bit patterns for the
+    16-bit types) and as device tensors of that type."""
+    rng = np.random.default_rng(seed)
+    s32 = rng.uniform(1e-3, 2e-2, inp.scales.shape).astype(np.float32)
+    b32 = rng.uniform(-0.15, 0.0, inp.scales.shape).astype(np.float32)
+    if sb == "f32":
+        hs, hb = s32, b32
+    elif sb == "f16":
+        hs, hb = s32.astype(np.float16).view(np.uint16), b32.astype(np.float16).view(np.uint16)
+    else:
+        hs, hb = W.bf16_bits_from_f32(s32), W.bf16_bits_from_f32(b32)
+    return hs, hb, to_dev(hs, sb), to_dev(hb, sb)
+
+
+def to_dev(a, dtype):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).cuda()
+    return t.view(TORCH[dtype])
+
+
+def host(t):
+    t = t.detach().cpu()
+    return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("sb", ["f16", "f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (6, 64)])
+def test_dequantize_typed_bit_exact(orc, sb, out, bits, G):
+    inp = W.random_inputs(bits, G, 37, 3 * G, 0, seed=bits + G)
+    hs, hb, ds, db = scales_of(inp, sb, seed=bits * G)
+    banner(f"dequantize typed sb={sb} out={out} bits={bits} G={G}")
+    got = qaff().dequantize(dev_u32(inp.packed), ds, db, G, bits, out_dtype=TORCH[out])
+    torch.cuda.synchronize()
+    ref = orc.dequantize_typed(inp.packed, hs, hb, sb, G, bits, out=out)
+    np.testing.assert_array_equal(host(got).view(ref.dtype), ref)
+
+
+@pytest.mark.parametrize("xt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("sb", ["f16", "f32"])
+@pytest.mark.parametrize("bits,G", [(4, 64), (5, 32), (8, 128), (2, 64)])
+@pytest.mark.parametrize("m", [1, 5])
+def test_qmm_typed(orc, xt, sb, bits, G, m):
+    n, k = 150, 20 * G // 2 * 2
+    inp = W.random_inputs(bits, G, n, k, 0, seed=bits * 7 + G + m)
+    hs, hb, ds, db = scales_of(inp, sb, seed=bits + G + m)
+    x32 = np.random.default_rng(m + bits).standard_normal((m, k)).astype(np.float32)
+    hx = x32 if xt == "f32" else (x32.astype(np.float16).view(np.uint16) if xt == "f16" else W.bf16_bits_from_f32(x32))
+    banner(f"qmm typed x={xt} sb={sb} bits={bits} G={G} m={m}")
+    y = qaff().qmm(to_dev(hx, xt), dev_u32(inp.packed), ds, db, G, bits)
+    torch.cuda.synchronize()
+    want = torch.float16 if (xt == "f16" and sb == "f16") else torch.float32
+    assert y.dtype == want and tuple(y.shape) == (m, n)
+    ref = orc.qmm_typed(hx, xt, inp.packed, hs, hb, sb, G, bits)
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = orc.max_row_rel_err(got, ref)
+    assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
+
+
+def test_f16_x_with_bf16_scales_promotes_to_f32(orc):
+    inp = W.random_inputs(4, 64, 100, 512, 0, seed=5)
+    x = np.random.default_rng(6).standard_normal((3, 512)).astype(np.float16)
+    banner("qmm f16 x, bf16 scales")
+    y = qaff().qmm(to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed), to_dev(inp.scales, "bf16"),
+                   to_dev(inp.biases, "bf16"), 64, 4)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float32
+    ref = orc.qmm_typed(x.view(np.uint16), "f16", inp.packed, inp.scales, inp.biases, "bf16", 64, 4)
+    assert orc.max_row_rel_err(y.cpu().numpy().astype(np.float64), ref) <= TIGHT[torch.float32]
+
+
+def test_bf16_only_operations_reject_other_scales(orc):
+    inp = W.random_inputs(4, 64, 16, 128, 0, seed=7)
+    hs, hb, ds, db = scales_of(inp, "f16", seed=8)
+    q = qaff()
+    banner("bf16-only operations reject float16 scales")
+    with pytest.raises(TypeError):
+        q.dequant_rows(dev_u32(inp.packed), ds, db, torch.zeros(2, dtype=torch.int32, device="cuda"), 64, 4)
+    with pytest.raises(TypeError):
+        q.gemv_silu_gate(torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda"),
+                         torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda"), dev_u32(inp.packed), ds, db, 64, 4)
+    with pytest.raises(TypeError):   # scales and biases of different types
+        q.qmm(torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda"), dev_u32(inp.packed), ds,
+              to_dev(inp.biases, "bf16"), 64, 4)
