@@ -16,7 +16,8 @@ The same JSON line carries:
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
     product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
-    residual, the product without the transpose at the decode shape, quantize of a bf16
+    residual, the product without the transpose at the decode shape, the decode product with
+    float16 x, scales and biases, quantize of a bf16
     [4096, 4096] weight, and the mixture-of-experts gathered product
     gather_qmm at 1 and 64 tokens), each against its roofline;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
@@ -336,6 +337,42 @@ def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     return row
 
 
+def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
+    """qmm with float16 x, scales and biases (y float16) at the decode shape W [4096, 4096] 4-bit
+    g64, M = 1: the typed VALU GEMV. The scales and biases are the decode workload's, as float16."""
+    import numpy as np
+    import oracle
+    wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
+    inp = W.make_inputs(wl, m=1)
+    s16 = W.f32_from_bf16_bits(inp.scales).astype(np.float16).view(np.uint16)
+    b16 = W.f32_from_bf16_bits(inp.biases).astype(np.float16).view(np.uint16)
+    x16 = W.f32_from_bf16_bits(inp.x).astype(np.float16).view(np.uint16)
+    b = qmm_bytes(1, wl.n, wl.k, wl.bits, wl.group_size)
+    copies = copies_for(b)
+    h = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+    sets = [{"packed": torch.from_numpy(inp.packed.view(np.int32)).cuda(), "scales": h(s16), "biases": h(b16),
+             "x": h(x16)} for _ in range(copies)]
+    ys = [torch.empty((1, wl.n), dtype=torch.float16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        q.qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del sets, ys
+    torch.cuda.empty_cache()
+    gbs = b / (ms * 1e-3) / 1e9
+    row = {"workload": "qmm float16 x, scales and biases, W [4096, 4096] 4-bit g64, M=1", "kernel": "gemv_typed_kernel",
+           "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
+    if cpu:
+        threads = oracle.default_threads()
+        runs, el = cpu_time(lambda: oracle.qmm_typed(x16, "f16", inp.packed, s16, b16, "f16", wl.group_size, wl.bits),
+                            cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(b * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
+    return row
+
+
 def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     """quantize of a dense bf16 weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64. Algorithmic bytes:
     the weight read, the codes, scales and biases written."""
@@ -561,6 +598,8 @@ def main():
             rows.append(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
         log("row: qmm without the transpose")
         rows.append(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0))
+        log("row: typed qmm")
+        rows.append(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0))
         log("row: quantize")
         rows.append(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:

@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kTypedThreads) void dequant_typed_kernel(
     }
 }
 
-// A wave owns RW rows of W; lanes take the row's 32-code blocks l, l + 64, ...
+// A wave owns kTypedRows rows of W; lanes take the row's 32-code blocks l, l + 64, ... (x needs
+// 16-byte alignment: the ABI checks it, and a block of 32 values keeps it)
 constexpr int kTypedRows = 2;
 
 template <int BITS, int MB>
@@ -82,10 +83,36 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
             const uint32_t xr = min(m0 + i, m - 1);
+            const size_t o = (size_t)xr * k + (size_t)j * 32;  // the block's 32 x values, 16-byte loads
+            if (xt == 0) {
+                const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + o);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const f32x4 v = p[q];
+                    xv[i][4 * q] = v.x; xv[i][4 * q + 1] = v.y; xv[i][4 * q + 2] = v.z; xv[i][4 * q + 3] = v.w;
+                }
+            } else {
+                const u32x4a* p = reinterpret_cast<const u32x4a*>(static_cast<const uint16_t*>(x) + o);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4a v = p[q];
+                    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (xt == 1) {
+                            xv[i][8 * q + 2 * e] = __uint_as_float(u[e] << 16);
+                            xv[i][8 * q + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+                        } else {
+                            xv[i][8 * q + 2 * e] = __half2float(__ushort_as_half((uint16_t)(u[e] & 0xffffu)));
+                            xv[i][8 * q + 2 * e + 1] = __half2float(__ushort_as_half((uint16_t)(u[e] >> 16)));
+                        }
+                    }
+                }
+            }
             float t = 0.f;
 #pragma unroll
             for (int c = 0; c < 32; ++c) {
-                xv[i][c] = m0 + i < m ? load_as_f32(x, (size_t)xr * k + (size_t)j * 32 + c, xt) : 0.f;
+                if (m0 + i >= m) xv[i][c] = 0.f;
                 t += xv[i][c];
             }
             xs[i] = t;
@@ -133,11 +160,10 @@ hipError_t launch_dequant_bits(const uint32_t* packed, const void* scales, const
     return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
-                            const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
-                            hipStream_t stream) {
-    constexpr int MB = 4;
+template <int BITS, int MB>
+hipError_t launch_gemv_mb(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
+                          const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
+                          hipStream_t stream) {
     const unsigned gx = (unsigned)((n + (kTypedThreads / 64) * kTypedRows - 1) / ((kTypedThreads / 64) * kTypedRows));
     const size_t xsize = xt == 0 ? 4 : 2, ysize = yt == 0 ? 4 : 2;
     const int64_t max_rows = (int64_t)65535 * MB;
@@ -151,6 +177,15 @@ hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* pa
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// x rows per block: 1 for a single row, else 4
+template <int BITS>
+hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
+                            const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
+                            hipStream_t stream) {
+    if (m == 1) return launch_gemv_mb<BITS, 1>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, stream);
+    return launch_gemv_mb<BITS, 4>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, stream);
 }
 
 }  // namespace
