@@ -66,7 +66,7 @@ def source_hash(*names):
 
 def read_traffic(kernel_key, sources):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    kernel's sources changed since the counters were taken."""
+    kernel's sources or the build flags (build.py) changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_key}.json")
     if not os.path.exists(path):
         return None
@@ -477,7 +477,7 @@ def bench_prefill(torch, q, W, timer, steps, cpu):
         "tflops": round(tflops, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h"])},
+                     "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h", "../build.py"])},
     }
     if cpu:
         threads = oracle.default_threads()
@@ -568,7 +568,7 @@ def main():
             "timing": ("plain launches" if args.eager else "one HIP graph of K qmm launches") +
                       ", events on the launch stream",
         },
-        "roofline": hbm_roofline(gbs, read_traffic("gemv_4bit_g64_4096x4096_m1", ["gemv.hip", "qaff_device.h"])),
+        "roofline": hbm_roofline(gbs, read_traffic("gemv_4bit_g64_4096x4096_m1", ["gemv.hip", "qaff_device.h", "../build.py"])),
     }
 
     # ---- prefill GEMM ----
