@@ -361,8 +361,8 @@ int orc_gather_qmm(const void* x, int x_is_bf16, int64_t x_batches, int64_t m, c
  *   code  = round((w - bias) / scale) with the stored bias and scale, rounded half away from zero
  *           (the Rust `round` of the page), clamped to [0, 2^bits - 1]; a group whose stored scale
  *           is 0 (all values equal) takes code 0, so it dequantizes to the bias exactly.
- * Every step is float32 (w widened exactly from bf16, or as given), as the kernels take the same
- * decisions. Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
+ * The statistics and w - bias are float32 (w widened exactly from bf16, or as given); the division
+ * is the plain quotient, rounded as an exact value (not first rounded to float32). Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
  * Returns 0, or -1 for parameters outside the format. */
 int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64_t group, int bits,
                  uint32_t* packed, uint16_t* scales, uint16_t* biases) {
@@ -389,12 +389,14 @@ int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64
             biases[r * (cols / group) + g] = bb;
             const float sc = bf16_to_f32(sb), bi = bf16_to_f32(bb);
             for (int64_t j = 0; j < group; ++j) {
-                float c = 0.0f;
+                double c = 0.0;
                 if (sc != 0.0f) {
                     const float diff = v[j] - bi;
-                    const float q = diff / sc;
-                    c = roundf(q);
-                    if (!(c >= 0.0f)) c = 0.0f; /* also a NaN quotient */
+                    /* the quotient of two floats in double: it lands on a half-integer only when
+                     * the exact quotient does, so round() decides as on the exact value */
+                    const double q = (double)diff / (double)sc;
+                    c = round(q);
+                    if (!(c >= 0.0)) c = 0.0; /* also a NaN quotient */
                     if (c > top) c = top;
                 }
                 codes[r * cols + g * group + j] = (uint8_t)c;

@@ -439,7 +439,7 @@ qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64
     if (rows == 0 || cols == 0) return QAFF_OK;
     if (!w) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null w", op);
     if (!aligned(w, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: w must be 16-byte aligned", op);
-    if (rows * (cols / 32) >= (1LL << 38))
+    if (rows * (cols / 32) >= (1LL << 37))
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld is too large", op, (long long)rows, (long long)cols);
     return after_launch(op, qaff::launch_quantize(w, w_dtype == QAFF_BF16, rows, cols, group_size, bits, packed,
                                                   scales, biases, stream), stream);

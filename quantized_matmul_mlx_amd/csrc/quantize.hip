@@ -4,8 +4,8 @@
 //   bias  = the group minimum, scale = (max - min) / (2^bits - 1), both stored as bf16 (RNE);
 //   code  = round((w - bias) / scale), half away from zero, with the stored bias and scale,
 //           clamped to [0, 2^bits - 1]; a stored scale of 0 (a constant group) gives code 0.
-// Every step is float32 (the division correctly rounded), so each code is decided the same way
-// as in a plain float32 evaluation of those formulas.
+// w - bias is a float32 difference; the rounding of the quotient is decided exactly (the quotient
+// itself is never rounded to float32 first).
 //
 // One lane per 32-value block: it loads its block, the G/32 lanes of a group (adjacent, since a
 // row holds a whole number of groups) combine their minima and maxima, and each lane writes its
@@ -89,11 +89,20 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     uint32_t words[BITS];
 #pragma unroll
     for (int i = 0; i < BITS; ++i) words[i] = 0u;
+    // code = round((w - bias) / scale), half away from zero, decided exactly: a candidate from the
+    // reciprocal is off by at most one, and the signs of d - (c -+ 1/2) s settle it (each product
+    // has at most 10 + 8 significant bits, exact in float32, so the fused form rounds only the
+    // difference, whose sign is exact).
+    const float rcp = sc != 0.0f ? 1.0f / sc : 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         float c = 0.0f;
         if (sc != 0.0f) {
-            c = __builtin_roundf((v[j] - bi) / sc);
+            const float d = v[j] - bi;
+            const float c0 = __builtin_floorf(__builtin_fmaf(d, rcp, 0.5f));
+            const float hi = __builtin_fmaf(-(c0 + 0.5f), sc, d);  // >= 0: the quotient rounds above c0
+            const float lo = __builtin_fmaf(-(c0 - 0.5f), sc, d);  // <  0: the quotient rounds below c0
+            c = c0 + (hi >= 0.0f ? 1.0f : 0.0f) - (lo < 0.0f ? 1.0f : 0.0f);
             c = c >= 0.0f ? c : 0.0f;  // also a NaN quotient
             c = c > kTop ? kTop : c;
         }
