@@ -211,7 +211,10 @@ __device__ __forceinline__ bool gather_batch(const Gather& ga, uint32_t row0, ui
     return true;
 }
 
-template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED, bool GATHER = false>
+// STAGE_SB (long rows, an even number of groups per row): the pass's scales and biases of each of
+// the wave's rows come in one 16-byte load per lane and row, through a wave-private LDS area,
+// instead of one 2-byte load per lane, block and row.
+template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED, bool GATHER = false, bool STAGE_SB = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint16_t* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
@@ -222,6 +225,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     // so that lane l reading quarter t of its block reads the 16 bytes after lane l-1's.
     __shared__ u32x4a xl[MB][4][kPassBlocks];
     __shared__ float xsl[MB][kPassBlocks][2];  // float32 sums of each half of each block of x
+    __shared__ uint16_t sbl[STAGE_SB ? WAVES : 1][RPW][2][STAGE_SB ? kPassBlocks : 1];  // [wave][row][s, b][group]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -284,6 +288,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
         //    until use, so no conversion waits on a load here.
         uint32_t wq[RPW][P][BITS];
         uint32_t sraw[RPW][P], braw[RPW][P];
+        u32x4 sbw[STAGE_SB ? RPW : 1][2];   // STAGE_SB: 8 scales and 8 biases from group gl
+        const uint32_t g0 = pass0 >> gshift;
+        const uint32_t gl = min(g0 + 8 * (uint32_t)lane, gpr - 8);  // clamped into the row
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             uint32_t row = min(row0 + r, nrows - 1);
@@ -299,12 +306,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             const uint32_t* prow = pk + (size_t)row * kb * BITS;
             const uint16_t* srow = sc + (size_t)row * gpr;
             const uint16_t* brow = bi + (size_t)row * gpr;
+            if constexpr (STAGE_SB) {  // 4-byte aligned: gpr and g0 are even
+                sbw[r][0] = *reinterpret_cast<const u32x4*>(srow + gl);
+                sbw[r][1] = *reinterpret_cast<const u32x4*>(brow + gl);
+            }
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const uint32_t j = min(pass0 + p * 64 + lane, kb - 1);
                 load_block<BITS>(prow + j * BITS, wq[r][p]);
-                sraw[r][p] = srow[j >> gshift];
-                braw[r][p] = brow[j >> gshift];
+                if constexpr (!STAGE_SB) {
+                    sraw[r][p] = srow[j >> gshift];
+                    braw[r][p] = brow[j >> gshift];
+                }
             }
         }
 
@@ -363,6 +376,34 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             }
         }
         __syncthreads();
+
+        // STAGE_SB: each lane stores its chunk's group pairs that fall in the pass at their own
+        // positions (a chunk clamped at the row's end can start before the pass, and overlaps its
+        // neighbour with the same values), then reads its blocks' groups.
+        if constexpr (STAGE_SB) {
+            const uint32_t ng = kPassBlocks >> gshift;  // groups of the pass
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    const u32x4 v = sbw[r][a];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t gd = gl + 2 * d;  // the pair's first group
+                        if (8 * (uint32_t)lane < ng && gd >= g0 && gd - g0 < ng)
+                            *reinterpret_cast<uint32_t*>(&sbl[wave][r][a][gd - g0]) = w4[d];
+                    }
+                }
+#pragma unroll
+            for (int r = 0; r < RPW; ++r)
+#pragma unroll
+                for (int p = 0; p < P; ++p) {
+                    const uint32_t q = min((uint32_t)(p * 64 + lane) >> gshift, ng - 1);
+                    sraw[r][p] = sbl[wave][r][0][q];
+                    braw[r][p] = sbl[wave][r][1][q];
+                }
+        }
 
         // 4. Multiply.
 #pragma unroll
@@ -539,7 +580,7 @@ hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
 template <int MB>
 constexpr int kLongPass = MB == 1 ? 8 : MB == 2 ? 4 : 2;
 
-template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int P>
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int P, bool STAGE_SB = false>
 hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                          const GemvFused& fz, hipStream_t stream) {
@@ -553,7 +594,7 @@ hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, c
             if (f.resid) f.resid += (size_t)m_off * n;
             if (f.y2) f.y2 += (size_t)m_off * n;
         }
-        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
+        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED, false, STAGE_SB><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
             x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
             (uint32_t)kb, gshift, y + (size_t)m_off * n, f, Gather{});
     });
@@ -563,9 +604,15 @@ template <int BITS, int MB, int RPW, int WAVES, bool FUSED>
 hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                        const GemvFused& fz, hipStream_t stream) {
-    if (kLongPass<MB> > 2 && kb > 128)
+    // long rows: the wider pass, and scales and biases through LDS when a row has an even number
+    // of groups (their 16-byte loads need 4-byte alignment)
+    if (kLongPass<MB> > 2 && kb > 128) {
+        if (((kb >> gshift) & 1) == 0)
+            return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, true>(x, m, packed, scales, biases, n,
+                                                                                kb, gshift, y, fz, stream);
         return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>>(x, m, packed, scales, biases, n, kb,
                                                                           gshift, y, fz, stream);
+    }
     return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, 2>(x, m, packed, scales, biases, n, kb, gshift, y, fz, stream);
 }
 
