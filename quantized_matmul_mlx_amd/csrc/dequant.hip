@@ -87,14 +87,17 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(
                       : __uint_as_float(0x7fc00000u);
         }
         const size_t e = (size_t)r * upr * UC + (size_t)p * UC;
+        // non-temporal stores: the output streams past the caches (measured at [4096, 4096] 4-bit:
+        // float32 17.3 -> 12.3 us, bf16 10.3 -> 7.3 us)
         if (p < upr) {
             if constexpr (OUT_BF16 && UC == 8) {
-                *reinterpret_cast<u32x4a*>(static_cast<uint16_t*>(out) + e) =
-                    u32x4a{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+                __builtin_nontemporal_store(u32x4a{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])},
+                                            reinterpret_cast<u32x4a*>(static_cast<uint16_t*>(out) + e));
             } else if constexpr (OUT_BF16) {
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                __builtin_nontemporal_store(u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])},
+                                            reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + e));
             } else {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(out) + e) = f32x4{o[0], o[1], o[2], o[3]};
+                __builtin_nontemporal_store(f32x4{o[0], o[1], o[2], o[3]}, reinterpret_cast<f32x4*>(static_cast<float*>(out) + e));
             }
         }
     }

@@ -313,7 +313,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
 #pragma unroll
             for (int p = 0; p < P; ++p) {
                 const uint32_t j = min(pass0 + p * 64 + lane, kb - 1);
-                load_block<BITS>(prow + j * BITS, wq[r][p]);
+                if constexpr (BITS == 4) {
+                    // non-temporal: each weight is read once (measured: 4-bit decode 3.81 -> 3.73 us,
+                    // gate_up 15.4 -> 14.4 us; the 8-bit GEMV lost 12% with them, so only here)
+                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(prow + j * BITS));
+                    wq[r][p][0] = v.x; wq[r][p][1] = v.y; wq[r][p][2] = v.z; wq[r][p][3] = v.w;
+                } else {
+                    load_block<BITS>(prow + j * BITS, wq[r][p]);
+                }
                 if constexpr (!STAGE_SB) {
                     sraw[r][p] = srow[j >> gshift];
                     braw[r][p] = brow[j >> gshift];
