@@ -1,0 +1,84 @@
+"""Launches that split their grid: one grid dimension holds at most 65535 blocks, so long x (the
+GEMVs' rows of x per block), many output batches (the gathered products) and many experts (the
+grouped walk) go out in several launches. Checked against the CPU oracle at the smallest sizes
+that cross the limit (k small so that the oracle finishes in seconds)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc_mod
+from gpu_util import banner, dev_bf16, dev_u32, dev_weights, dev_x, host_f64
+from quantized_matmul_mlx_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TIGHT = {"f32": 1e-4, "bf16": 4e-3}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    orc_mod.build()
+    import quantized_matmul_mlx_amd as q
+    q._lib.load()
+    return orc_mod
+
+
+def qaff():
+    import quantized_matmul_mlx_amd as q
+    return q
+
+
+@pytest.mark.parametrize("x_dtype,m", [("f32", 65535 * 4 + 7), ("bf16", 65535 * 8 + 9)])
+def test_gemv_over_m_slices(orc, x_dtype, m):
+    # the VALU GEMV takes 4 (float32) or 8 (bf16) x rows per block in grid y
+    inp = W.random_inputs(4, 32, 40, 32, m, x_dtype=x_dtype, seed=m % 97)
+    banner(f"gemv m={m} {x_dtype} (several launches)")
+    p, s, b = dev_weights(inp)
+    y = qaff().qmm(dev_x(inp.x, x_dtype), p, s, b, 32, 4, path="gemv")
+    torch.cuda.synchronize()
+    ref = orc.qmm(inp.x, x_dtype, inp.packed, inp.scales, inp.biases, 32, 4)
+    got = host_f64(y)
+    # every row, and the rows at the launch boundaries in particular
+    assert orc.max_row_rel_err(got, ref) <= TIGHT[x_dtype]
+
+
+def test_gather_over_batch_slices(orc):
+    # the VALU gathered GEMV: grid z = output batch, 65535 per launch
+    E, n, k, G, bits, batch = 3, 40, 64, 32, 4, 65535 + 300
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=5)
+    packed, scales, biases = (inp.packed.reshape(E, n, -1), inp.scales.reshape(E, n, -1),
+                              inp.biases.reshape(E, n, -1))
+    rng = np.random.default_rng(6)
+    x = W.bf16_bits_from_f32(rng.standard_normal((7, 1, k)).astype(np.float32))
+    lhs = rng.integers(0, 7, batch).astype(np.uint32)
+    rhs = rng.integers(0, E, batch).astype(np.uint32)
+    banner(f"gather batch={batch} (several launches)")
+    y = qaff().gather_qmm(dev_x(x, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits,
+                          lhs_indices=dev_u32(lhs), rhs_indices=dev_u32(rhs), path="gemv")
+    torch.cuda.synchronize()
+    # one oracle call per batch: single-threaded, so that no thread pool starts 65835 times
+    ref = orc.gather_qmm(x, "bf16", packed, scales, biases, G, bits, lhs=lhs, rhs=rhs, threads=1)
+    assert orc.max_row_rel_err(host_f64(y).reshape(-1, n), ref.reshape(-1, n)) <= TIGHT["bf16"]
+
+
+def test_grouped_walk_over_expert_slices(orc):
+    # the grouped walk: grid y = experts + 1, 65535 per launch; 70000 experts of [16, 512]
+    E, n, k, G, bits = 70000, 16, 512, 128, 2
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=7)
+    packed, scales, biases = (inp.packed.reshape(E, n, -1), inp.scales.reshape(E, n, -1),
+                              inp.biases.reshape(E, n, -1))
+    rng = np.random.default_rng(8)
+    rhs = np.sort(rng.integers(0, E, 2000)).astype(np.uint32)
+    rhs[-3:] = E - 1                                         # rows for the last expert (the last launch)
+    rhs = np.sort(rhs)
+    x = W.bf16_bits_from_f32(rng.standard_normal((rhs.size, 1, k)).astype(np.float32))
+    banner(f"grouped walk over {E} experts (several launches)")
+    y = qaff().gather_qmm(dev_x(x, "bf16"), dev_u32(packed), dev_bf16(scales), dev_bf16(biases), G, bits,
+                          rhs_indices=dev_u32(rhs), sorted_indices=True, path="gemv_mfma")
+    torch.cuda.synchronize()
+    ref = orc.gather_qmm(x, "bf16", packed, scales, biases, G, bits, rhs=rhs, threads=1)
+    got = host_f64(y).reshape(-1, n)
+    assert np.isfinite(got).all()
+    assert orc.max_row_rel_err(got, ref.reshape(-1, n)) <= 1.6e-2
