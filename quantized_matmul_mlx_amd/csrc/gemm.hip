@@ -413,63 +413,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(
             }
 }
 
-// ---- 128 x 256 tiles for 4-bit codes ------------------------------------------------------------
+// ---- 128 x 256 tiles with W dequantized into registers ------------------------------------------
 //
-// The prefill shape is limited by what the compute units pull through L2, not by HBM: X is re-read
-// once per tile column and W once per tile row. A 128 (M) x 256 (N) tile halves the X traffic of
-// the 256 x 128 tile at the price of twice the dequantization per multiply, and three changes keep
-// the rest of the traffic in whole cache lines and the dequantization cheap:
-//  * W is fetched one 128-byte line per row at a time, i.e. four K-steps (a "super-step") at once:
-//    in load instruction i, the eight lanes of row group g read the eight 16-byte blocks of row
-//    4 g + i, lane (q, b) block 2 ((q + i) & 3) + b. Every lane thereby holds exactly one block of
-//    every K-step of the super-step, in register slot (u - q) & 3 for step u, and picks it with
-//    three selects.
-//  * Scales and biases arrive in windows of 8 groups (16 bytes per row), one window per thread,
-//    and are kept in LDS as float32.
-//  * The multiply uses v_mfma_f32_32x32x16_bf16, which leaves more issue slots for the
-//    dequantization between matrix instructions than the 16x16x32 form, and each step's
-//    dequantization is interleaved with its matrix instructions.
-// Requirements (checked by the launcher): K a multiple of 8 groups and of 64 * kWideBody; W,
+// At the prefill shape the products above are held back by what runs beside the matrix cores --
+// the dequantization on the VALU and the traffic through LDS -- and by the power it all draws, not
+// by HBM. This kernel keeps W out of LDS: each W element is dequantized once, by the one wave that
+// multiplies it, straight into a register operand.
+//  * A 512-thread block owns a 128 (M) x 256 (N) tile of Y. Wave w owns W rows 32 w .. 32 w + 31 of
+//    the tile and all 128 rows of X: four 32 x 32 tiles of Y along M.
+//  * K goes in steps of 64 codes (two 32-code blocks). In a step, lane l = 32 h + r holds block h of
+//    W row r (BITS words, one load), and MFMA kk (0..3) of the step contracts codes 8 kk .. 8 kk + 7
+//    of every lane's block. X follows the same order: lane (r, h) supplies
+//    x[row][64 t + 32 h + 8 kk + e], e = 0..7, from LDS (the MFMA sums over all its k slots, so any
+//    order that X and W share is the same product).
+//  * X tiles go through LDS, double buffered, rows padded to 72 bf16 so that 16 rows read at one
+//    offset fall on distinct banks. X is loaded two steps ahead, W three steps ahead.
+//  * Scales and biases come in windows of 8 groups (16 bytes per row and array), one window ahead.
+// Against dequantizing W tiles into LDS this halves the VALU work per flop and removes the W tile's
+// LDS stores and reads; two waves per SIMD still hide the latencies.
+// Requirements (checked by the launcher): K a multiple of 64 * kDirectBody (so of 8 groups);
 // scales and biases 16-byte aligned. Rows of X beyond m and rows of W beyond n are clamped, not
 // zeroed: they only reach outputs that are not stored.
 //
-// MFMA 32x32x16 (bf16) layout: lane l supplies row l % 32 of A and of W (column of B), each as the
-// 8 consecutive k starting at 8 * (l / 32); result value v of lane l is row 8 (v / 4) + 4 (l / 32)
-// + v % 4, column l % 32. LDS rows are padded to 72 bf16 (144 bytes), which spreads 8 (16) rows
-// read at one chunk over distinct banks and keeps the chunk offsets compile-time immediates.
+// MFMA 32x32x16 (bf16) layout: lane l supplies row l % 32 of A and of W (column of B), each as 8
+// values of k slot l / 32; result value v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
+// l % 32.
 
-constexpr int WBM = 128;
-constexpr int WBN = 256;
-constexpr int kWideThreads = 512;
-constexpr int kWideA = WBM * LDK;  // bf16 elements of one A buffer
-constexpr int kWideB = WBN * LDK;  // bf16 elements of one B buffer
-constexpr int kSbPitch = 9;        // floats per row in the scale (bias) window: 8 groups + 1 padding
-constexpr int kWideBody = 16;      // K-steps per loop iteration (windows are 4, 8 or 16 steps)
+constexpr int DBM = 128;
+constexpr int DBN = 256;
+constexpr int kDirectThreads = 512;
+constexpr int kDirectBody = 16;  // K-steps per loop iteration (scale windows are 4, 8 or 16 steps)
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// v_cndmask_b32 with a lane mask: `if_set` in the lanes of `mask`, `if_clear` elsewhere. Written
-// out because the compiler turns chains of lane-dependent selects into divergent branches.
-__device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, uint32_t if_clear) {
-    uint32_t r;
-    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
-    return r;
-}
-
-template <int GSHIFT>
-__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(
+template <int BITS, int GSHIFT>
+__global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
     const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
     uint32_t tiles_n) {
-    constexpr int P = (32 << GSHIFT) / 8;  // K-steps per window of 8 groups: 4, 8 or 16
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][kWideA + kWideB];
-    __shared__ float sbl[2][2][WBN * kSbPitch];  // [buffer][scale, bias][row * 9 + group]
+    constexpr int P = 4 << GSHIFT;                // K-steps per window of 8 groups
+    constexpr int XPT = DBM * 8 / kDirectThreads;  // 16-byte X chunks per thread and step
+    __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 2;  // 64-row slice of the tile
-    const int wn = wave & 3;   // 64-column slice
+    const int h = lane >> 5;
 
     // Tile order: block b runs on XCD b % 8, so each XCD gets a contiguous run of 32 tiles, laid
     // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2.
@@ -485,200 +474,131 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(
         tm = t / tiles_n;
         tn = t % tiles_n;
     }
-    const uint32_t m0 = tm * WBM;
-    const uint32_t n0 = tn * WBN;
+    const uint32_t m0 = tm * DBM;
+    const uint32_t n0 = tn * DBN;
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> GSHIFT;  // groups per row
     const uint32_t ktiles = kb >> 1;    // K-steps
-    const uint32_t nsuper = kb >> 3;    // super-steps
     const uint32_t nwin = gpr >> 3;     // scale windows
 
-    // Per-block bases (uniform) and 32-bit per-lane offsets: a tile spans far less than 4 GiB.
+    // X: chunk (xkc) of rows xrow + 64 i; 32-bit offsets within the tile's rows.
     const uint16_t* xb = x + (size_t)m0 * k;
-    const uint32_t* wbase = packed + (size_t)n0 * (kb * 4);
-
-    // X: two 16-byte chunks per thread and step, rows xrow and xrow + 64, chunk xkc.
     const int xrow = tid >> 3;
     const int xkc = tid & 7;
-    const uint32_t xo0 = (min(m0 + xrow, m - 1) - m0) * k + xkc * 8;
-    const uint32_t xo1 = (min(m0 + xrow + 64, m - 1) - m0) * k + xkc * 8;
-    const int xa0 = xrow * LDK + xkc * 8;
-    const int xa1 = (xrow + 64) * LDK + xkc * 8;
+    uint32_t xo[XPT];
+    int xa[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+        xo[i] = (min(m0 + xrow + 64 * i, m - 1) - m0) * k + xkc * 8;
+        xa[i] = (xrow + 64 * i) * LDK + xkc * 8;
+    }
+    // W row of this lane, its block h of each step, and its scale and bias windows.
+    const uint32_t wrow = min(n0 + 32 * wave + (lane & 31), n - 1);
+    const uint32_t* wp = packed + (size_t)wrow * kb * BITS + h * BITS;
+    const uint16_t* sp = scales + (size_t)wrow * gpr;
+    const uint16_t* bp = biases + (size_t)wrow * gpr;
 
-    // W: row group g, lane pair q, block b (see above).
-    const int wg = tid >> 3;
-    const int wq = (tid >> 1) & 3;
-    const int wb = tid & 1;
-    uint32_t wo[4];
+    auto load_x = [&](u32x4a (&xr)[XPT], uint32_t kt) {
+        const uint16_t* p = xb + min(kt, ktiles - 1) * 64;
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) xr[i] = *reinterpret_cast<const u32x4a*>(p + xo[i]);
+    };
+    auto store_x = [&](const u32x4a (&xr)[XPT], int buf) {
+#pragma unroll
+        for (int i = 0; i < XPT; ++i) *reinterpret_cast<u32x4a*>(&xl[buf][xa[i]]) = xr[i];
+    };
+    auto load_w = [&](uint32_t (&wr)[BITS], uint32_t kt) { load_block<BITS>(wp + (size_t)min(kt, ktiles - 1) * 2 * BITS, wr); };
+    auto load_sb = [&](u32x4a (&r)[2], uint32_t win) {
+        const uint32_t o = min(win, nwin - 1) * 8;
+        r[0] = *reinterpret_cast<const u32x4a*>(sp + o);
+        r[1] = *reinterpret_cast<const u32x4a*>(bp + o);
+    };
+
+    f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        wo[i] = (min(n0 + 4 * wg + i, n - 1) - n0) * (kb * 4) + (((wq + i) & 3) * 2 + wb) * 4;
-
-    // Scale (threads 0..255) or bias (256..511) window of row sb_row.
-    const int sb_arr = tid >> 8;
-    const int sb_row = tid & 255;
-    const uint16_t* sbp = (sb_arr ? biases : scales) + (size_t)min(n0 + sb_row, n - 1) * gpr;
-
-    auto load_x = [&](u32x4a (&xr)[2], uint32_t kt) {
-        const uint16_t* p = xb + min(kt, ktiles - 1) * BK;
-        xr[0] = *reinterpret_cast<const u32x4a*>(p + xo0);
-        xr[1] = *reinterpret_cast<const u32x4a*>(p + xo1);
-    };
-    auto load_w = [&](u32x4a (&wr)[4], uint32_t s) {
-        const uint32_t* p = wbase + min(s, nsuper - 1) * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wr[i] = *reinterpret_cast<const u32x4a*>(p + wo[i]);
-    };
-    auto load_sb = [&](u32x4a& r, uint32_t win) { r = *reinterpret_cast<const u32x4a*>(sbp + min(win, nwin - 1) * 8); };
-    auto store_sb = [&](const u32x4a& r, int buf) {
-        float* d = &sbl[buf][sb_arr][sb_row * kSbPitch];
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+
+    // X operand of tile i, MFMA kk: row 32 i + lane % 32, k offset 32 h + 8 kk.
+    const int aoff = (lane & 31) * LDK + h * 32;
+    auto read_a = [&](const uint16_t* L, int kk, bf16x8 (&a)[4]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            d[2 * e] = __uint_as_float(r[e] << 16);
-            d[2 * e + 1] = __uint_as_float(r[e] & 0xffff0000u);
-        }
-    };
-    auto store_x = [&](const u32x4a (&xr)[2], int buf) {
-        *reinterpret_cast<u32x4a*>(&lds[buf][xa0]) = xr[0];
-        *reinterpret_cast<u32x4a*>(&lds[buf][xa1]) = xr[1];
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(L + aoff + 32 * i * LDK + 8 * kk);
     };
 
-    // Lanes whose register slot i (0..2) holds K-step u of a super-step: q == u - i.
-    uint64_t sel[4][3];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 3; ++i) sel[u][i] = __builtin_amdgcn_ballot_w64(wq == ((u - i) & 3));
-
-    // Dequantization of this lane's block of K-step dkt (u = dkt % 4) into B buffer dbuf, split in
-    // four parts (one word, 8 codes, 16 bytes of the tile each) to interleave with the multiply.
-    struct Deq {
-        uint32_t w[4];
-        float s, b;
-        uint16_t* dst;
-    };
-    auto deq_begin = [&](const u32x4a (&wr)[4], uint32_t dkt, int u, int dbuf) {
-        Deq d;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            uint32_t v = lane_select(sel[u][2], wr[2][c], wr[3][c]);
-            v = lane_select(sel[u][1], wr[1][c], v);
-            d.w[c] = lane_select(sel[u][0], wr[0][c], v);
-        }
-        const int row = 4 * wg + ((u - wq) & 3);
-        const int grp = (int)(((dkt * 2 + wb) >> GSHIFT) & 7u);
-        const int sbuf = (int)((dkt / P) & 1u);
-        d.s = sbl[sbuf][0][row * kSbPitch + grp];
-        d.b = sbl[sbuf][1][row * kSbPitch + grp];
-        d.dst = lds[dbuf] + kWideA + row * LDK + wb * 32;
-        return d;
-    };
-    auto deq_part = [&](const Deq& d, int c) {
-        // even codes in the bytes of lo, odd codes in those of hi; the empty asm keeps the compiler
-        // from turning the byte conversions back into one bit-field extract per code
-        uint32_t lo = d.w[c] & 0x0f0f0f0fu;
-        uint32_t hi = (d.w[c] >> 4) & 0x0f0f0f0fu;
-        asm("" : "+v"(lo), "+v"(hi));
-        uint32_t o[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            o[j] = pack_bf16x2(__builtin_fmaf(d.s, (float)((lo >> (8 * j)) & 0xffu), d.b),
-                               __builtin_fmaf(d.s, (float)((hi >> (8 * j)) & 0xffu), d.b));
-        *reinterpret_cast<u32x4a*>(d.dst + 8 * c) = u32x4a{o[0], o[1], o[2], o[3]};
-    };
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // Operand rows: wm*64 + 32 i + lane % 32 of A, wn*64 + 32 j + lane % 32 of B; chunk 2 kk +
-    // lane / 32 of the step is a constant offset from these.
-    const int aoff = (wm * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
-    const int boff = kWideA + (wn * 64 + (lane & 31)) * LDK + (lane >> 5) * 8;
-    auto read_ops = [&](const uint16_t* L, int kk, bf16x8 (&a)[2], bf16x8 (&b)[2]) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(L + aoff + 32 * i * LDK + 16 * kk);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const bf16x8*>(L + boff + 32 * j * LDK + 16 * kk);
-    };
-    // Multiplies step buffer cbuf while dequantizing the next step (d) into the other buffer.
-    auto compute_deq = [&](int cbuf, const Deq& d) {
-        const uint16_t* L = lds[cbuf];
-        bf16x8 a[2][2], b[2][2];
-        read_ops(L, 0, a[0], b[0]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) read_ops(L, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], b[kk & 1][j], acc[i][j], 0, 0, 0);
-            deq_part(d, kk);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-
-    // Prologue: window 0 in LDS, step 0 in buffer 0, steps 1 and 2 of X in flight, super-steps 0
-    // and 1 of W in registers.
-    u32x4a xr[2][2], wr[2][4], sbr;
-    load_sb(sbr, 0);
+    // Prologue: X of step 0 in LDS, X of steps 1 and 2 and W of steps 0..2 in flight, the first
+    // scale window in flight.
+    u32x4a xr[2][XPT], sbc[2], sbn[2];
+    uint32_t wr[4][BITS];
+    load_sb(sbn, 0);
     load_w(wr[0], 0);
     load_w(wr[1], 1);
+    load_w(wr[2], 2);
     load_x(xr[0], 0);
     load_x(xr[1], 1);
-    store_sb(sbr, 0);
     store_x(xr[0], 0);
     load_x(xr[0], 2);
     __syncthreads();
-    {
-        const Deq d = deq_begin(wr[0], 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) deq_part(d, c);
-    }
-    __syncthreads();
 
-    // Step kt: store X of step kt+1 into the free buffer and issue the loads of step kt+3 (of
-    // super-step kt/4 + 2 at the end of a super-step; of the next scale window at the start of a
-    // window, stored to LDS two steps before its first use), then multiply step kt while
-    // dequantizing W of step kt+1 into the free buffer. Register sets are fixed by the position in
-    // the unrolled body: X by the step's parity, W by the super-step's.
-    for (uint32_t kt0 = 0; kt0 < ktiles; kt0 += kWideBody) {
+    // Step kt: store X of step kt+1 into the free buffer and issue the loads of X and W of step
+    // kt+3 (and of the next scale window at a window's first step), then multiply step kt. Register
+    // sets are fixed by the position in the unrolled body: X by the step's parity, W by kt % 4.
+    for (uint32_t kt0 = 0; kt0 < ktiles; kt0 += kDirectBody) {
 #pragma unroll
-        for (int u = 0; u < kWideBody; ++u) {
+        for (int u = 0; u < kDirectBody; ++u) {
             const uint32_t kt = kt0 + u;
-            const int nb = (u + 1) & 1;
-            const int ws = ((u + 1) >> 2) & 1;  // W set of step kt+1
-            store_x(xr[nb], nb);
-            if (((u + 1) & 3) == 0) load_w(wr[ws ^ 1], (kt + 1) / 4 + 1);
-            load_x(xr[nb], kt + 3);
-            if (u % P == 0) load_sb(sbr, (kt + P) / P);
+            if (u % P == 0) {
+                sbc[0] = sbn[0];
+                sbc[1] = sbn[1];
+            }
+            store_x(xr[(u + 1) & 1], (u + 1) & 1);
+            load_x(xr[(u + 1) & 1], kt + 3);
+            load_w(wr[(u + 3) & 3], kt + 3);
+            if (u % P == 0) load_sb(sbn, kt / P + 1);
             // Keep the loads here: the operands are read-only, so the compiler could otherwise sink
             // them towards their first use and lose the prefetch distance.
             asm volatile("" ::: "memory");
-            if (u % P == P - 2) store_sb(sbr, (int)(((kt + 2) / P) & 1u));
-            const Deq d = deq_begin(wr[ws], kt + 1, (u + 1) & 3, nb);
-            compute_deq(u & 1, d);
+            // This lane's group in the window: block 2 u + h, i.e. group (2 u + h) >> GSHIFT.
+            uint32_t sw, bw, sh;
+            if constexpr (GSHIFT == 0) {
+                sw = sbc[0][u % P];
+                bw = sbc[1][u % P];
+                sh = 16u * (uint32_t)h;
+            } else {
+                const int gi = (u % P) >> (GSHIFT - 1);
+                sw = sbc[0][gi >> 1];
+                bw = sbc[1][gi >> 1];
+                sh = 16u * (uint32_t)(gi & 1);
+            }
+            const float s = __uint_as_float((sw >> sh) << 16);
+            const float b = __uint_as_float((bw >> sh) << 16);
+            const uint16_t* L = xl[u & 1];
+            bf16x8 a[2][4];
+            read_a(L, 0, a[0]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk < 3) read_a(L, kk + 1, a[(kk + 1) & 1]);
+                const bf16x8 bw8 = dequant8<BITS>(wr[u & 3], kk, s, b);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], bw8, acc[i], 0, 0, 0);
+            }
             __syncthreads();
         }
     }
 
-    const int ocol = lane & 31;
-    const int orow = 4 * (lane >> 5);
+    const uint32_t gc = n0 + 32 * wave + (lane & 31);
+    const int orow = 4 * h;
+    if (gc < n) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const uint32_t gm = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + orow + (v & 3);
-                const uint32_t gc = n0 + wn * 64 + 32 * j + ocol;
-                if (gm < m && gc < n) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][j][v]);
+                const uint32_t gm = m0 + 32 * i + 8 * (v >> 2) + orow + (v & 3);
+                if (gm < m) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][v]);
             }
+    }
 }
 
 // Waves of the 256 x 128 tile along M (WN = 2 along N): 2 gives four 128 x 64 wave tiles, 4 gives
@@ -726,6 +646,39 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
     return hipSuccess;
 }
 
+template <int BITS, int GSHIFT>
+hipError_t launch_direct_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, int64_t tiles_m,
+                           int64_t tiles_n, hipStream_t stream) {
+    gemm_direct_kernel<BITS, GSHIFT><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kDirectThreads), 0, stream>>>(
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m, (uint32_t)tiles_n);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_direct_b(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
+                           int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
+    if (gshift == 0) return launch_direct_g<BITS, 0>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
+    if (gshift == 1) return launch_direct_g<BITS, 1>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
+    return launch_direct_g<BITS, 2>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
+}
+
+hipError_t launch_direct(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t n, int64_t kb, int bits, uint32_t gshift, uint16_t* y,
+                         int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
+    switch (bits) {
+        case 1: return launch_direct_b<1>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 2: return launch_direct_b<2>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 3: return launch_direct_b<3>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 4: return launch_direct_b<4>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 5: return launch_direct_b<5>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 6: return launch_direct_b<6>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 8: return launch_direct_b<8>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
@@ -734,23 +687,14 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
-    if (bits == 4 && m >= kBigTileMinM && k % (64 * kWideBody) == 0 && k % (8 * (int64_t)group_size) == 0 &&
-        a16(packed) && a16(scales) &&
-        a16(biases)) {
-        const int64_t tiles_n = (n + WBN - 1) / WBN;
-        const int64_t max_rows = (int64_t)(0x7fffffff / tiles_n) * WBM;
+    if (m >= kBigTileMinM && k % (64 * kDirectBody) == 0 && a16(scales) && a16(biases)) {
+        const int64_t tiles_n = (n + DBN - 1) / DBN;
+        const int64_t max_rows = (int64_t)(0x7fffffff / tiles_n) * DBM;
         for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
             const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
-            const int64_t tiles_m = (mm + WBM - 1) / WBM;
-            const dim3 grid((unsigned)(tiles_m * tiles_n));
-            const uint16_t* xs = x + (size_t)m_off * k;
-            uint16_t* ys = y + (size_t)m_off * n;
-            switch (gshift) {
-                case 0: gemm_wide_kernel<0><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
-                case 1: gemm_wide_kernel<1><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
-                default: gemm_wide_kernel<2><<<grid, kWideThreads, 0, stream>>>(xs, (uint32_t)mm, packed, scales, biases, (uint32_t)n, (uint32_t)kb, ys, (uint32_t)tiles_m, (uint32_t)tiles_n); break;
-            }
-            const hipError_t e = hipGetLastError();
+            const int64_t tiles_m = (mm + DBM - 1) / DBM;
+            const hipError_t e = launch_direct(x + (size_t)m_off * k, mm, packed, scales, biases, n, kb, bits, gshift,
+                                               y + (size_t)m_off * n, tiles_m, tiles_n, stream);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;

@@ -43,36 +43,6 @@ __device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, 
     return r;
 }
 
-// Codes 8 j .. 8 j + 7 of a 32-code block, dequantized and rounded to bf16, in k order.
-template <int BITS>
-__device__ __forceinline__ bf16x8 dequant8(const uint32_t (&w)[BITS], int j, float s, float b) {
-    uint32_t o[4];
-    if constexpr (BITS == 4) {
-        // even codes in the bytes of lo, odd codes in those of hi (the empty asm keeps the byte
-        // converts from being turned into one bit-field extract per code)
-        uint32_t lo = w[j] & 0x0f0f0f0fu;
-        uint32_t hi = (w[j] >> 4) & 0x0f0f0f0fu;
-        asm("" : "+v"(lo), "+v"(hi));
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf16x2(__builtin_fmaf(s, (float)((lo >> (8 * e)) & 0xffu), b),
-                               __builtin_fmaf(s, (float)((hi >> (8 * e)) & 0xffu), b));
-    } else if constexpr (BITS == 8) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t v = w[2 * j + h];
-            o[2 * h] = pack_bf16x2(__builtin_fmaf(s, (float)(v & 0xffu), b), __builtin_fmaf(s, (float)((v >> 8) & 0xffu), b));
-            o[2 * h + 1] = pack_bf16x2(__builtin_fmaf(s, (float)((v >> 16) & 0xffu), b), __builtin_fmaf(s, (float)(v >> 24), b));
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf16x2(__builtin_fmaf(s, (float)code_at<BITS>(w, 8 * j + 2 * e), b),
-                               __builtin_fmaf(s, (float)code_at<BITS>(w, 8 * j + 2 * e + 1), b));
-    }
-    return __builtin_bit_cast(bf16x8, u32x4a{o[0], o[1], o[2], o[3]});
-}
-
 constexpr int kXPitch = 2 * kSlice + 16;  // bytes per x row in a wave's LDS region (banks: see below)
 
 // A row's scales (biases) over one slice: 16, 8 or 4 groups, loaded whole (32, 16 or 8 bytes).

@@ -184,14 +184,26 @@ def test_gemm(orc, bits, G, m, n):
     check_qmm(orc, inp, y, path="gemm")
 
 
-# 4-bit codes with K a multiple of 1024 take the 128 x 256 tile kernel: every group size, ragged m
-# and n tails, one to three 16-step loop iterations, and grids with and without the 4 x 8 tile
-# blocks per XCD (512 x 2048: 4 x 8 tiles; the others are not multiples of 8 tiles).
+# m >= 256 with K a multiple of 1024 takes the 128 x 256 tile kernel that dequantizes W into
+# registers: every group size, ragged m and n tails, one to three 16-step loop iterations, and grids
+# with and without the 4 x 8 tile blocks per XCD (512 x 2048: 4 x 8 tiles; the others are not
+# multiples of 8 tiles).
 @pytest.mark.parametrize("G,m,n,k", [(32, 256, 256, 1024), (64, 300, 520, 2048), (128, 512, 2048, 1024),
                                      (128, 257, 300, 3072), (32, 384, 1000, 2048)])
-def test_gemm_wide_tiles(orc, G, m, n, k):
+def test_gemm_direct_tiles(orc, G, m, n, k):
     inp = W.random_inputs(4, G, n, k, m, seed=G + m + n)
-    banner(f"gemm wide G={G} m={m} n={n} k={k}")
+    banner(f"gemm direct G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemm")
+    check_qmm(orc, inp, y, path="gemm")
+
+
+# The same kernel at every other bit width (a block of 32 codes is BITS words; 3-, 5- and 6-bit
+# codes straddle words), with a ragged tile in m and in n.
+@pytest.mark.parametrize("bits", [1, 2, 3, 5, 6, 8])
+@pytest.mark.parametrize("G,m,n,k", [(32, 260, 300, 1024), (128, 300, 520, 2048)])
+def test_gemm_direct_widths(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits * 7 + G + m)
+    banner(f"gemm direct bits={bits} G={G} m={m} n={n} k={k}")
     y = run_qmm(inp, path="gemm")
     check_qmm(orc, inp, y, path="gemm")
 
