@@ -20,6 +20,9 @@ The same JSON line carries:
     float16 x, scales and biases, quantize of a bf16
     [4096, 4096] weight, and the mixture-of-experts gathered product
     gather_qmm at 1 and 64 tokens), each against its roofline;
+  * `context`: what the box does on the same sizes without this library, timed the same way: an
+    empty kernel launch, a device copy of the decode step's bytes, a dense bf16 matmul at the
+    prefill shape;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
     (also given per row).
 
@@ -492,6 +495,54 @@ def bench_prefill(torch, q, W, timer, steps, cpu):
     return res
 
 
+def bench_context(torch, timer):
+    """What the same box does on the same sizes without this library, timed the same way: an
+    empty kernel launch, a device copy of the decode step's bytes (it reads them and writes as
+    many), and a dense bf16 matmul at the prefill shape (the vendor BLAS). Context for the two
+    roofline fractions, not a result of the path."""
+    steps = 1000
+    empty_ms = timer(lambda i: torch.cuda._sleep(0), steps, 100)
+
+    nbytes = 9453568                                      # the decode step's algorithmic bytes
+    copies = (1 << 30) // nbytes + 1                     # about 1 GiB: four times the MALL
+    srcs = [torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda") for _ in range(copies)]
+    dsts = [torch.empty_like(t) for t in srcs]
+    copy_ms = timer(lambda i: dsts[i % copies].copy_(srcs[i % copies]), steps, 100)
+    del srcs, dsts
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    xs = torch.randn((2048, 14336), generator=g, device="cuda").to(torch.bfloat16)
+    ws = torch.randn((4096, 14336), generator=g, device="cuda").to(torch.bfloat16)
+    y = torch.empty((2048, 4096), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(xs, ws.t(), out=y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mm_steps = 20
+    start.record()
+    for _ in range(mm_steps):
+        torch.matmul(xs, ws.t(), out=y)
+    end.record()
+    torch.cuda.synchronize()
+    mm_ms = start.elapsed_time(end) / mm_steps
+    del xs, ws, y
+    torch.cuda.empty_cache()
+    flop = 2.0 * 2048 * 4096 * 14336
+    return {
+        "empty_kernel_us_per_launch": round(empty_ms * 1e3, 3),
+        "copy_of_decode_bytes": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                 "us_per_step": round(copy_ms * 1e3, 3),
+                                 "GBps_moved": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+                                 "how": f"device copy of a {nbytes}-byte tensor, {copies} rotated copies, "
+                                        "same timing as the headline"},
+        "dense_bf16_matmul_prefill": {"us_per_step": round(mm_ms * 1e3, 1),
+                                      "tflops": round(flop / (mm_ms * 1e-3) / 1e12, 1),
+                                      "frac": round(flop / (mm_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "how": "torch.matmul x [2048, 14336] . W^T [14336, 4096], bf16 N(0,1), "
+                                             f"{mm_steps} plain launches"},
+    }
+
+
 def copy_calibration(torch):
     """A plain device copy of 256 MiB, five times: reads and writes exactly 256 MiB each, the
     reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
@@ -515,6 +566,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--no-context", action="store_true", help="skip the empty-launch, device-copy and dense-matmul context")
     ap.add_argument("--eager", action="store_true", help="plain launches instead of one graph")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -575,6 +627,11 @@ def main():
     if not args.no_prefill:
         log(f"prefill GEMM: steps {args.prefill_steps}")
         result["prefill_gemm"] = bench_prefill(torch, q, W, timer, args.prefill_steps, cpu)
+
+    # ---- what the box does on the same sizes without this library ----
+    if not args.no_context:
+        log("context: empty launch, device copy, dense bf16 matmul")
+        result["context"] = bench_context(torch, timer)
 
     # ---- the other rows of the path ----
     if not args.no_rows:
