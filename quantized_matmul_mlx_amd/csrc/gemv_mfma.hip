@@ -210,12 +210,24 @@ hipError_t launch_g(const uint16_t* x, int64_t m, const uint32_t* packed, const 
     int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch);
     if (per_cu < 1) per_cu = 1;
     if (per_cu > 4) per_cu = 4;
-    const int64_t slots = (int64_t)device_cu_count() * per_cu;
+    const int64_t cus = device_cu_count();
+    const int64_t slots = cus * per_cu;
     int64_t nt = (n + 16 * slots - 1) / (16 * slots);
     // 8-bit codes: more than two tiles of W (64 registers each) crowd out the waves that hide the
     // latency (measured: 8-bit M = 16 on [14336, 4096] 20 us at two tiles, 25 us at three)
     constexpr int kMaxNt = BITS == 8 ? 2 : 4;
     if (nt > kMaxNt) nt = kMaxNt;
+    // The dequantization keeps the VALU busy, so the compute unit with the most rows sets the
+    // time: among the tile counts that still fit one round, take the one that gives it the fewest
+    // (3-bit [11008, 4096] at m = 8: three tiles, 48 rows per unit, where two tiles put 64 rows on
+    // some units).
+    auto busiest = [&](int64_t t) {
+        const int64_t blocks = (n + 16 * t - 1) / (16 * t);
+        const int64_t per = (blocks + cus - 1) / cus;
+        return per > per_cu ? INT64_MAX : per * 16 * t;
+    };
+    for (int64_t t = 1; t <= kMaxNt; ++t)
+        if (busiest(t) < busiest(nt)) nt = t;
     if (nt <= 1) return launch_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
     if (nt == 2) return launch_nt<BITS, 2, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
     if (nt == 3 || kMaxNt == 3) return launch_nt<BITS, 3, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);

@@ -245,6 +245,16 @@ def test_gemv_mfma_row_tiles(orc, bits, n):
     check_qmm(orc, inp, y, path="gemv_mfma")
 
 
+# At m = 5..8 (x rows rounded to 8) two blocks fit a compute unit; for 8192 < n <= 12288 three
+# tiles per block put at most 48 rows on a unit where two would put 64 on some.
+@pytest.mark.parametrize("bits,n", [(3, 8300), (6, 11008)])
+def test_gemv_mfma_balanced_tiles(orc, bits, n):
+    inp = W.random_inputs(bits, 32, n, 4096, 8, seed=n + bits)
+    banner(f"gemv_mfma balanced tiles bits={bits} n={n} m=8")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
 def test_gemv_mfma_rejects_other_shapes(orc):
     inp = W.random_inputs(4, 32, 8, 768, 4, seed=1)   # k not a multiple of 512
     p, s, b = dev_weights(inp)
