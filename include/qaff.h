@@ -95,8 +95,10 @@ qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, co
 /*
  * y = x . dequantize(W)^T with x of x_dtype and scales and biases of sb_dtype (each float32, bf16 or
  * float16); y [m, n] of qaff_promote_dtype(x_dtype, sb_dtype); float32 sums.
- * bf16 scales with a float32 or bf16 x take qaff_qmm's kernels (QAFF_PATH_AUTO); every other
- * combination runs on a VALU GEMV that reads the types as given (any m, any k).
+ * bf16 scales with a float32 or bf16 x take qaff_qmm's kernels (QAFF_PATH_AUTO); float16 x with
+ * float16 scales and biases take the bf16 GEMV's layout in float16 (codes as the exact values
+ * 1024 + c, v_dot2_f32_f16, float32 sums, y rounded to nearest even); every other combination runs
+ * on a VALU GEMV that reads the types as given (any m, any k).
  * Errors: as qaff_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.
  */
 qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,

@@ -387,6 +387,11 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
     if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
     if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    if (x_dtype == QAFF_F16 && sb_dtype == QAFF_F16)
+        return after_launch(op, qaff::launch_gemv_f16(static_cast<const uint16_t*>(x), m, packed,
+                                                      static_cast<const uint16_t*>(scales),
+                                                      static_cast<const uint16_t*>(biases), n, k, group_size, bits,
+                                                      static_cast<uint16_t*>(y), stream), stream);
     return after_launch(op, qaff::launch_gemv_typed(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
                                                     group_size, bits, y, (int)yt, stream), stream);
 }

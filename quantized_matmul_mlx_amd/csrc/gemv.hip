@@ -44,7 +44,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
-constexpr uint32_t kMagic = 0x43004300u;  // bf16 128.0 in both halves
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit format F of x, scales, biases and y: 0 bf16, 1 float16. Codes become exact values
+// o + c of that format (o = 128 in bf16, whose 8 significant bits hold 128 + c for c < 128; o =
+// 1024 in float16, whose 11 hold 1024 + c for every code up to 8 bits), and v_dot2 of the format
+// multiplies two of them by two x values exactly and adds in float32.
+template <int F> constexpr uint32_t kMagicF = F ? 0x64006400u : 0x43004300u;  // o in both halves
+template <int F> constexpr float kOffsetF = F ? 1024.f : 128.f;
+
+template <int F>
+__device__ __forceinline__ float dot2f(uint32_t a, uint32_t b, float c) {
+    if constexpr (F == 1)
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+    else
+        return dot2(a, b, c);
+}
+
+template <int F>
+__device__ __forceinline__ float widen16(uint32_t h) {  // exact
+    if constexpr (F == 1)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+    else
+        return bf16_to_f32(h);
+}
+
+template <int F>
+__device__ __forceinline__ uint16_t narrow16(float v) {  // round to nearest even
+    if constexpr (F == 1)
+        return __builtin_bit_cast(uint16_t, (_Float16)v);
+    else
+        return to_bf16_bits(v);
+}
 
 // (a & mask) | orv in one v_and_or_b32 (the compiler otherwise emits an AND and an OR).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
@@ -55,16 +86,16 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
 
 // ---- per-bit-width unpacking into 16 bf16 pairs per 32-code block ---------------------------
 
-template <int BITS> struct Codes;
+template <int BITS, int F = 0> struct Codes;
 
-// 4-bit: pair 4q + p of block = (c_{8q+p}, c_{8q+p+4}), values 128 + c.
-template <> struct Codes<4> {
-    static constexpr float kOffset = 128.f;
+// 4-bit: pair 4q + p of block = (c_{8q+p}, c_{8q+p+4}), values o + c.
+template <int F> struct Codes<4, F> {
+    static constexpr float kOffset = kOffsetF<F>;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[4], uint32_t (&pr)[16]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) pr[4 * q + p] = and_or(w[q] >> (4 * p), 0x000F000Fu, kMagic);
+            for (int p = 0; p < 4; ++p) pr[4 * q + p] = and_or(w[q] >> (4 * p), 0x000F000Fu, kMagicF<F>);
     }
     // x pairs in the same order, from the block's 32 x values as 16 natural-order dwords.
     __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
@@ -80,14 +111,14 @@ template <> struct Codes<4> {
     }
 };
 
-// 2-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values 128 + c.
-template <> struct Codes<2> {
-    static constexpr float kOffset = 128.f;
+// 2-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values o + c.
+template <int F> struct Codes<2, F> {
+    static constexpr float kOffset = kOffsetF<F>;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[2], uint32_t (&pr)[16]) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int p = 0; p < 8; ++p) pr[8 * q + p] = and_or(w[q] >> (2 * p), 0x00030003u, kMagic);
+            for (int p = 0; p < 8; ++p) pr[8 * q + p] = and_or(w[q] >> (2 * p), 0x00030003u, kMagicF<F>);
     }
     __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
         // x_{16q+j}: dword 8q + j/2, half j%2. Pair p takes x_{16q+p} and x_{16q+p+8}.
@@ -102,24 +133,24 @@ template <> struct Codes<2> {
     }
 };
 
-// 1-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values 128 + c. x is staged in halves of 16, so
+// 1-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values o + c. x is staged in halves of 16, so
 // a pair must stay within a half: swapping the word's middle bytes puts c_{8..15} at bits 16..23
 // and c_{16..23} at bits 8..15, after which bits i and i + 16 are such a pair.
-template <> struct Codes<1> {
-    static constexpr float kOffset = 128.f;
+template <int F> struct Codes<1, F> {
+    static constexpr float kOffset = kOffsetF<F>;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[1], uint32_t (&pr)[16]) {
         const uint32_t v = __builtin_amdgcn_perm(w[0], w[0], 0x03010200u);  // bytes b0 b2 b1 b3
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pr[i] = and_or(v >> i, 0x00010001u, kMagic);
+        for (int i = 0; i < 16; ++i) pr[i] = and_or(v >> i, 0x00010001u, kMagicF<F>);
     }
     // the 2-bit pairing of x: pair 8q + p takes x_{16q+p} and x_{16q+p+8}
     __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
-        Codes<2>::pair_x(xn, xp);
+        Codes<2, F>::pair_x(xn, xp);
     }
 };
 
 // 8-bit: pair 2q + h = (c_{4q+2h}, c_{4q+2h+1}), exact values c (offset 0).
-template <> struct Codes<8> {
+template <> struct Codes<8, 0> {
     static constexpr float kOffset = 0.f;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[8], uint32_t (&pr)[16]) {
 #pragma unroll
@@ -139,14 +170,31 @@ template <> struct Codes<8> {
     }
 };
 
-// 3-, 5-, 6-bit: pair i = (c_{2i}, c_{2i+1}) in column order, values 128 + c.
-template <int BITS> struct Codes {
+// 8-bit, float16: pair 2q + h = (c_{4q+2h}, c_{4q+2h+1}), values 1024 + c: one byte permute
+// puts two codes under the exponent bytes of 1024.0.
+template <> struct Codes<8, 1> {
+    static constexpr float kOffset = 1024.f;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[8], uint32_t (&pr)[16]) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            pr[2 * q] = __builtin_amdgcn_perm(0x64646464u, w[q], 0x04010400u);      // c0, c1
+            pr[2 * q + 1] = __builtin_amdgcn_perm(0x64646464u, w[q], 0x04030402u);  // c2, c3
+        }
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xp[i] = xn[i];
+    }
+};
+
+// 3-, 5-, 6-bit: pair i = (c_{2i}, c_{2i+1}) in column order, values o + c.
+template <int BITS, int F> struct Codes {
     static_assert(BITS == 3 || BITS == 5 || BITS == 6, "bit width");
-    static constexpr float kOffset = 128.f;
+    static constexpr float kOffset = kOffsetF<F>;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[BITS], uint32_t (&pr)[16]) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            pr[i] = (code_at<BITS>(w, 2 * i) | (code_at<BITS>(w, 2 * i + 1) << 16)) | kMagic;
+            pr[i] = (code_at<BITS>(w, 2 * i) | (code_at<BITS>(w, 2 * i + 1) << 16)) | kMagicF<F>;
     }
     __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
 #pragma unroll
@@ -214,11 +262,12 @@ __device__ __forceinline__ bool gather_batch(const Gather& ga, uint32_t row0, ui
 // STAGE_SB (long rows, an even number of groups per row): the pass's scales and biases of each of
 // the wave's rows come in one 16-byte load per lane and row, through a wave-private LDS area,
 // instead of one 2-byte load per lane, block and row.
-template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED, bool GATHER = false, bool STAGE_SB = false>
+template <int BITS, int MB, int RPW, int WAVES, int P, bool FUSED, bool GATHER = false, bool STAGE_SB = false, int F = 0>
 __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
     const uint16_t* __restrict__ x, uint32_t m, const uint32_t* __restrict__ packed,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ biases, uint32_t n,
     uint32_t kb, uint32_t gshift, uint16_t* __restrict__ y, GemvFused fz, Gather ga) {
+    static_assert(F == 0 || (!FUSED && !GATHER), "float16 operands: the plain product only");
     constexpr int kBlockThreads = WAVES * 64;
     constexpr int kPassBlocks = 64 * P;  // 32-code blocks per row per pass
     // x of the pass as bf16 pairs in unpack order: [x row][quarter of a block][block] of 16 bytes,
@@ -365,19 +414,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             }
             float hs = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) hs = dot2(v[q], 0x3F803F80u, hs);  // pairs of 1.0
+            for (int q = 0; q < 8; ++q) hs = dot2f<F>(v[q], F ? 0x3C003C00u : 0x3F803F80u, hs);  // pairs of 1.0
             xsl[mi][b][h] = hs;
             uint32_t xp[16];
             if (h == 0) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) xn[q] = v[q];
-                Codes<BITS>::pair_x(xn, xp);
+                Codes<BITS, F>::pair_x(xn, xp);
                 xl[mi][0][b] = u32x4a{xp[0], xp[1], xp[2], xp[3]};
                 xl[mi][1][b] = u32x4a{xp[4], xp[5], xp[6], xp[7]};
             } else {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) xn[8 + q] = v[q];
-                Codes<BITS>::pair_x(xn, xp);
+                Codes<BITS, F>::pair_x(xn, xp);
                 xl[mi][2][b] = u32x4a{xp[8], xp[9], xp[10], xp[11]};
                 xl[mi][3][b] = u32x4a{xp[12], xp[13], xp[14], xp[15]};
             }
@@ -431,14 +480,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 uint32_t pr[16];
-                Codes<BITS>::unpack(wq[r][p], pr);
-                const float sc = bf16_to_f32(sraw[r][p]);
-                const float boff = bf16_to_f32(braw[r][p]) - Codes<BITS>::kOffset * sc;
+                Codes<BITS, F>::unpack(wq[r][p], pr);
+                const float sc = widen16<F>(sraw[r][p]);
+                const float boff = widen16<F>(braw[r][p]) - Codes<BITS, F>::kOffset * sc;
 #pragma unroll
                 for (int i = 0; i < MB; ++i) {
                     float d = 0.f;
 #pragma unroll
-                    for (int t = 0; t < 16; ++t) d = dot2(pr[t], xp[i][t], d);
+                    for (int t = 0; t < 16; ++t) d = dot2f<F>(pr[t], xp[i][t], d);
                     // written as two fused multiply-adds so that every instantiation rounds
                     // the same way (left to the compiler, the contraction varies with the code)
                     acc[r][i] = __builtin_fmaf(sc, d, __builtin_fmaf(boff, xs[i], acc[r][i]));
@@ -462,7 +511,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_bf16_kernel(
             if (lane == 0 && in_range && m0 + i < m) {
                 const size_t o = (size_t)(m0 + i) * n + row;
                 if (FUSED && fz.resid) v += bf16_to_f32(fz.resid[o]);
-                yo[o] = to_bf16_bits(v);
+                yo[o] = narrow16<F>(v);
             }
         }
     }
@@ -587,7 +636,7 @@ hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
 template <int MB>
 constexpr int kLongPass = MB == 1 ? 8 : MB == 2 ? 4 : 2;
 
-template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int P, bool STAGE_SB = false>
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int P, bool STAGE_SB = false, int F = 0>
 hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                          const GemvFused& fz, hipStream_t stream) {
@@ -601,13 +650,13 @@ hipError_t launch_bf16_p(const uint16_t* x, int64_t m, const uint32_t* packed, c
             if (f.resid) f.resid += (size_t)m_off * n;
             if (f.y2) f.y2 += (size_t)m_off * n;
         }
-        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED, false, STAGE_SB><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
+        gemv_bf16_kernel<BITS, MB, RPW, WAVES, P, FUSED, false, STAGE_SB, F><<<dim3(gx, gy), dim3(WAVES * 64), 0, stream>>>(
             x + (size_t)m_off * kb * 32, (uint32_t)mm, packed, scales, biases, (uint32_t)n,
             (uint32_t)kb, gshift, y + (size_t)m_off * n, f, Gather{});
     });
 }
 
-template <int BITS, int MB, int RPW, int WAVES, bool FUSED>
+template <int BITS, int MB, int RPW, int WAVES, bool FUSED, int F = 0>
 hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                        const GemvFused& fz, hipStream_t stream) {
@@ -615,15 +664,15 @@ hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, con
     // of groups (their 16-byte loads need 4-byte alignment)
     if (kLongPass<MB> > 2 && kb > 128) {
         if (((kb >> gshift) & 1) == 0)
-            return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, true>(x, m, packed, scales, biases, n,
-                                                                                kb, gshift, y, fz, stream);
-        return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>>(x, m, packed, scales, biases, n, kb,
-                                                                          gshift, y, fz, stream);
+            return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, true, F>(x, m, packed, scales, biases, n,
+                                                                                   kb, gshift, y, fz, stream);
+        return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, false, F>(x, m, packed, scales, biases, n, kb,
+                                                                                   gshift, y, fz, stream);
     }
-    return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, 2>(x, m, packed, scales, biases, n, kb, gshift, y, fz, stream);
+    return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, 2, false, F>(x, m, packed, scales, biases, n, kb, gshift, y, fz, stream);
 }
 
-template <int BITS, bool FUSED>
+template <int BITS, bool FUSED, int F = 0>
 hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                          const GemvFused& f, hipStream_t stream) {
@@ -632,12 +681,12 @@ hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, c
     if (m == 1 && FUSED)
         return launch_bf16<BITS, 1, 2, 8, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 1)
-        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 2)
-        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m <= 4)
-        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
-    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
 }
 
 template <int BITS, int MB>
@@ -781,6 +830,24 @@ hipError_t launch_gemv(const void* x, bool x_f32, int64_t m, const uint32_t* pac
         case 5: return launch_bits<5>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 6: return launch_bits<6>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
         case 8: return launch_bits<8>(x, x_f32, m, packed, scales, biases, n, kb, gshift, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_f16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
+                           hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    const GemvFused f{};
+    switch (bits) {
+        case 1: return launch_bf16_m<1, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 2: return launch_bf16_m<2, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 3: return launch_bf16_m<3, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 4: return launch_bf16_m<4, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 5: return launch_bf16_m<5, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 6: return launch_bf16_m<6, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        case 8: return launch_bf16_m<8, false, 1>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -33,6 +33,12 @@ hipError_t launch_gemv_fused(const uint16_t* x, int64_t m, const uint32_t* packe
                              const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
                              uint16_t* y, const GemvFused& f, hipStream_t stream);
 
+// The same GEMV with float16 x, scales and biases and a float16 y: codes as the exact float16 values
+// 1024 + c, v_dot2_f32_f16, float32 sums.
+hipError_t launch_gemv_f16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
+                           hipStream_t stream);
+
 // A gathered product (nuvec_core quantized.rs, `gather_qmm`): output batch b is
 // x[lhs[b]] . dequantize(W[rhs[b]])^T. Launches index the batch through the grid; `b0` is the
 // first batch (or expert) of a launch, since one grid dimension holds at most 65535 blocks.

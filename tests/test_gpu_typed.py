@@ -98,6 +98,30 @@ def test_qmm_typed(orc, xt, sb, bits, G, m):
     assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
 
 
+# float16 x with float16 scales and biases: the bf16 GEMV's layout in float16 (codes as 1024 + c,
+# v_dot2_f32_f16). Every width; m = 1, 2, 3 and 8 (x-row tiles of 1, 2, 4 and 8 rows); K of one
+# pass, and long rows (more than 4096 codes: the wider pass, with scales and biases through LDS when
+# a row has an even number of groups, 4352 / 128 = 34 and 8192 / 32 = 256, and without at
+# 4224 / 128 = 33).
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G,m,k", [(64, 1, 2048), (32, 2, 1024), (128, 3, 4352), (64, 8, 1024), (32, 1, 8192),
+                                   (128, 1, 4224)])
+def test_qmm_f16_gemv(orc, bits, G, m, k):
+    n = 77
+    inp = W.random_inputs(bits, G, n, k, 0, seed=bits * 11 + G + m + k)
+    hs, hb, ds, db = scales_of(inp, "f16", seed=bits + G + m + k)
+    x = np.random.default_rng(m + bits + k).standard_normal((m, k)).astype(np.float16)
+    banner(f"qmm float16 gemv bits={bits} G={G} m={m} k={k}")
+    y = qaff().qmm(to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed), ds, db, G, bits)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16 and tuple(y.shape) == (m, n)
+    ref = orc.qmm_typed(x.view(np.uint16), "f16", inp.packed, hs, hb, "f16", G, bits)
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = orc.max_row_rel_err(got, ref)
+    assert err <= TIGHT[torch.float16], f"max row rel err {err:.3e} > {TIGHT[torch.float16]}"
+
+
 def test_f16_x_with_bf16_scales_promotes_to_f32(orc):
     inp = W.random_inputs(4, 64, 100, 512, 0, seed=5)
     x = np.random.default_rng(6).standard_normal((3, 512)).astype(np.float16)
