@@ -12,7 +12,9 @@ bracketed by synchronizations and timed with events on the stream the kernels ru
 
 The same JSON line carries:
   * `prefill_gemm`: the 4-bit g128 prefill GEMM (x bf16 [2048, 14336], W [4096, 14336]) in TFLOP/s
-    against the 2.5 PFLOP/s dense bf16 MFMA peak;
+    against the 2.5 PFLOP/s dense bf16 MFMA peak: GEMMs back to back for a few seconds, with the
+    graphics clock and socket power sampled meanwhile (`sustained`; the chip is power-limited and
+    settles after a transient dip), and a short graph of launches (`burst`);
   * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
     product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
@@ -455,7 +457,81 @@ def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_b
     return row
 
 
-def bench_prefill(torch, q, W, timer, steps, cpu):
+class GpuMetrics:
+    """Graphics clock (MHz) and socket power (W) of the GPU from amdsmi's metrics table, or nothing
+    where amdsmi is unavailable. The table refreshes on the order of a second, so only long
+    windows of sustained work read anything meaningful from it."""
+
+    def __init__(self):
+        self.smi, self.h = None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.h = amdsmi.amdsmi_get_processor_handles()[0]
+            self.smi = amdsmi
+        except Exception:
+            self.smi, self.h = None, None
+
+    def read(self):
+        if self.h is None:
+            return None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+        except Exception:
+            return None
+        clk, pw = m.get("current_gfxclk"), m.get("current_socket_power")
+        if isinstance(clk, (int, float)) and isinstance(pw, (int, float)):
+            return float(clk), float(pw)
+        return None
+
+    def close(self):
+        if self.smi is not None:
+            try:
+                self.smi.amdsmi_shut_down()
+            except Exception:
+                pass
+
+
+def sustained(torch, launch, seconds, metrics, flop):
+    """Plain launches back to back for about `seconds`, never more than two batches queued ahead
+    (the queue never runs dry), with the clock and power sampled every 50 ms after the first
+    second. Time per launch over the whole window."""
+    import statistics
+    batch = 16
+    pending = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    n, samples = 0, []
+    t0 = last = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            launch(n)
+            n += 1
+        e = torch.cuda.Event()
+        e.record()
+        pending.append(e)
+        if len(pending) > 2:
+            pending.pop(0).synchronize()
+        now = time.perf_counter()
+        if metrics is not None and now - t0 >= 1.0 and now - last >= 0.05:
+            r = metrics.read()
+            if r is not None:
+                samples.append(r)
+            last = now
+    end.record()
+    end.synchronize()
+    ms = start.elapsed_time(end) / n
+    res = {"seconds": round(time.perf_counter() - t0, 2), "launches": n, "us_per_launch": round(ms * 1e3, 1),
+           "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    if samples:
+        res["gfxclk_mhz_median"] = statistics.median(c for c, _ in samples)
+        res["socket_power_w_median"] = statistics.median(p for _, p in samples)
+        res["samples"] = len(samples)
+    return res
+
+
+def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
     import oracle
     wl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
     m = 2048
@@ -468,20 +544,32 @@ def bench_prefill(torch, q, W, timer, steps, cpu):
         s = sets[i % copies]
         q.qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
 
-    ms = timer(launch, steps, 3)
+    burst_ms = timer(launch, steps, 3)
+    flop = 2.0 * m * wl.n * wl.k
+    held = sustained(torch, launch, sustain_s, metrics, flop) if sustain_s > 0 else None
     del sets, ys
     torch.cuda.empty_cache()
-    flop = 2.0 * m * wl.n * wl.k
+    # The figure is the steady state of back-to-back GEMMs when measured (the power-limited chip
+    # settles after a transient dip that a short burst right after idle falls into), else the burst.
+    ms = held["us_per_launch"] * 1e-3 if held is not None else burst_ms
     tflops = flop / (ms * 1e-3) / 1e12
     res = {
         "workload": "prefill GEMM: 4-bit codes, group 128, W [4096, 14336], x bf16 [2048, 14336], "
                     "y bf16 [2048, 4096]; seed 0",
         "ms_per_step": round(ms, 5),
         "tflops": round(tflops, 2),
+        "timing": (f"{held['launches']} launches back to back over {held['seconds']} s, events on the launch stream"
+                   if held is not None else f"one HIP graph of {steps} launches, events on the launch stream"),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h", "../build.py"])},
     }
+    if held is not None:
+        res["sustained"] = held
+        burst_tf = flop / (burst_ms * 1e-3) / 1e12
+        res["burst"] = {"launches": steps, "ms_per_step": round(burst_ms, 5), "tflops": round(burst_tf, 2),
+                        "frac": round(burst_tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "timing": f"one HIP graph of {steps} launches after the decode rows"}
     if cpu:
         threads = oracle.default_threads()
         rows = 64
@@ -495,7 +583,7 @@ def bench_prefill(torch, q, W, timer, steps, cpu):
     return res
 
 
-def bench_context(torch, timer):
+def bench_context(torch, timer, metrics=None, sustain_s=0.0):
     """What the same box does on the same sizes without this library, timed the same way: an
     empty kernel launch, a device copy of the decode step's bytes (it reads them and writes as
     many), and a dense bf16 matmul at the prefill shape (the vendor BLAS). Context for the two
@@ -525,10 +613,12 @@ def bench_context(torch, timer):
     end.record()
     torch.cuda.synchronize()
     mm_ms = start.elapsed_time(end) / mm_steps
+    flop = 2.0 * 2048 * 4096 * 14336
+    held = (sustained(torch, lambda i: torch.matmul(xs, ws.t(), out=y), sustain_s, metrics, flop)
+            if sustain_s > 0 else None)
     del xs, ws, y
     torch.cuda.empty_cache()
-    flop = 2.0 * 2048 * 4096 * 14336
-    return {
+    res = {
         "empty_kernel_us_per_launch": round(empty_ms * 1e3, 3),
         "copy_of_decode_bytes": {"bytes_read": nbytes, "bytes_written": nbytes,
                                  "us_per_step": round(copy_ms * 1e3, 3),
@@ -541,6 +631,9 @@ def bench_context(torch, timer):
                                       "how": "torch.matmul x [2048, 14336] . W^T [14336, 4096], bf16 N(0,1), "
                                              f"{mm_steps} plain launches"},
     }
+    if held is not None:
+        res["dense_bf16_matmul_prefill"]["sustained"] = held
+    return res
 
 
 def copy_calibration(torch):
@@ -567,6 +660,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--no-context", action="store_true", help="skip the empty-launch, device-copy and dense-matmul context")
+    ap.add_argument("--sustain", type=float, default=3.0,
+                    help="seconds of back-to-back prefill GEMMs (and dense matmuls) with clock and power samples; 0: none")
     ap.add_argument("--eager", action="store_true", help="plain launches instead of one graph")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -590,6 +685,7 @@ def main():
         return
     q._lib.load()
     timer = Timer(torch, args.eager)
+    metrics = GpuMetrics() if args.sustain > 0 else None
     cpu = not args.no_cpu_baseline
     log = lambda msg: print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -626,12 +722,12 @@ def main():
     # ---- prefill GEMM ----
     if not args.no_prefill:
         log(f"prefill GEMM: steps {args.prefill_steps}")
-        result["prefill_gemm"] = bench_prefill(torch, q, W, timer, args.prefill_steps, cpu)
+        result["prefill_gemm"] = bench_prefill(torch, q, W, timer, args.prefill_steps, cpu, metrics, args.sustain)
 
     # ---- what the box does on the same sizes without this library ----
     if not args.no_context:
         log("context: empty launch, device copy, dense bf16 matmul")
-        result["context"] = bench_context(torch, timer)
+        result["context"] = bench_context(torch, timer, metrics, args.sustain)
 
     # ---- the other rows of the path ----
     if not args.no_rows:
@@ -679,6 +775,8 @@ def main():
     else:
         result["cpu_baseline"] = None
 
+    if metrics is not None:
+        metrics.close()
     print(json.dumps(result), flush=True)
 
 
