@@ -184,8 +184,7 @@ def test_gemm(orc, bits, G, m, n):
     check_qmm(orc, inp, y, path="gemm")
 
 
-# m >= 256 with K a multiple of 1024 takes the 128 x 256 tile kernel that dequantizes W into
-# registers: every group size, ragged m and n tails, one to three 16-step loop iterations, and grids
+# K a multiple of 1024 takes the 128 x 256 tile kernel that dequantizes W into registers (at any m): every group size, ragged m and n tails, one to three 16-step loop iterations, and grids
 # with and without the 4 x 8 tile blocks per XCD (512 x 2048: 4 x 8 tiles; the others are not
 # multiples of 8 tiles).
 @pytest.mark.parametrize("G,m,n,k", [(32, 256, 256, 1024), (64, 300, 520, 2048), (128, 512, 2048, 1024),
@@ -193,6 +192,17 @@ def test_gemm(orc, bits, G, m, n):
 def test_gemm_direct_tiles(orc, G, m, n, k):
     inp = W.random_inputs(4, G, n, k, m, seed=G + m + n)
     banner(f"gemm direct G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemm")
+    check_qmm(orc, inp, y, path="gemm")
+
+
+# Fewer than 256 rows of x take the same kernel (one or two rows of tiles, the rest of the tile
+# clamped): m just above the decode range, a ragged single tile row, and one and a half tile rows.
+@pytest.mark.parametrize("bits,G,m,n,k", [(4, 64, 17, 300, 1024), (4, 128, 100, 520, 2048), (3, 32, 200, 264, 1024),
+                                          (8, 128, 33, 256, 2048)])
+def test_gemm_direct_small_m(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + n)
+    banner(f"gemm direct small m bits={bits} G={G} m={m} n={n} k={k}")
     y = run_qmm(inp, path="gemm")
     check_qmm(orc, inp, y, path="gemm")
 
