@@ -150,6 +150,27 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
                         void* y, hipStream_t stream, qaff_path path);
 
 /*
+ * qaff_qmm (QAFF_PATH_AUTO) with a workspace that lets the bf16 GEMM path split K (nuvec_core
+ * quantized_matmul with transpose, as qaff_qmm). Where the GEMM's 128 x 256 tiles are fewer than
+ * the compute units (m up to about 1024 at n = 4096, K a multiple of 1024), K is split into ranges
+ * of whole 1024-code chunks: each range's float32 partial sums go to `workspace`, and a second
+ * kernel adds the ranges in a fixed order (results are deterministic) and rounds y to bf16.
+ *   Arguments as qaff_qmm, plus workspace: a caller-owned device buffer of at least
+ *   qaff_qmm_workspace_size(m, n, k, group_size, bits) bytes, 16-byte aligned, which the call
+ *   overwrites; it may be NULL when that size is 0. Calls that share a workspace must not overlap.
+ * Errors: as qaff_qmm, plus INVALID_ARGUMENT for a missing, short or misaligned workspace where
+ * one is needed.
+ */
+qaff_status qaff_qmm_ws(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        int32_t group_size, int32_t bits, void* workspace, size_t workspace_bytes, void* y,
+                        hipStream_t stream);
+
+/* Bytes of workspace qaff_qmm_ws can use for these sizes with a bf16 x (0 where it would not split
+ * K: m <= 16, enough tiles, or K not a multiple of 1024). */
+size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits);
+
+/*
  * The product without the transpose (nuvec_core quantized.rs quantized_matmul with transpose =
  * false): y = x . dequantize(W) for a weight stored [k, n], i.e. y[m, n] = sum_k x[m, k] w[k, n],
  * without materialising W.

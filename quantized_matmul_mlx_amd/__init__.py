@@ -238,10 +238,18 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
         _need(out, "out", (x.dtype,), dev)
         if tuple(out.shape) != lead + (n,):
             raise ValueError(f"out must be {list(lead + (n,))}")
+    # the automatic path of a bf16 x may split K through a workspace (few tiles of the GEMM)
+    nbytes = int(lib.qaff_qmm_workspace_size(m, n, k, group_size, bits)) if (
+        path == "auto" and x.dtype == torch.bfloat16) else 0
     with torch.cuda.device(dev):
-        _lib.check(lib.qaff_qmm_ex(_p(x2), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales),
-                                   _p(biases), n, k, group_size, bits, _p(out), _stream(dev),
-                                   _lib.PATHS[path]))
+        if nbytes > 0:
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            _lib.check(lib.qaff_qmm_ws(_p(x2), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), n, k,
+                                       group_size, bits, _p(ws), ws.numel(), _p(out), _stream(dev)))
+        else:
+            _lib.check(lib.qaff_qmm_ex(_p(x2), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales),
+                                       _p(biases), n, k, group_size, bits, _p(out), _stream(dev),
+                                       _lib.PATHS[path]))
     return out
 
 

@@ -146,10 +146,14 @@ qaff_status qaff_dequant_rows(const uint32_t* packed, const uint16_t* scales, co
                           bits, indices, n_indices, true, out, out_dtype, stream);
 }
 
-qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
-                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
-                        int32_t group_size, int32_t bits, void* y, hipStream_t stream, qaff_path path) {
-    static const char* op = "qaff_qmm";
+namespace {
+
+// qaff_qmm_ex, and qaff_qmm_ws with a workspace (ws non-null: the call needs ws_need bytes, checked
+// by the caller; the GEMM path may split K into it).
+qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                     const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                     int32_t group_size, int32_t bits, void* y, hipStream_t stream, qaff_path path,
+                     void* ws, size_t ws_bytes) {
     g_error.clear();
     qaff_status st = check_weight(op, packed, scales, biases, n, k, group_size, bits);
     if (st != QAFF_OK) return st;
@@ -185,12 +189,45 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint
                                    bits, static_cast<uint16_t*>(y), stream);
     } else if (use_gemm) {
         e = qaff::launch_gemm(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
-                              bits, static_cast<uint16_t*>(y), stream);
+                              bits, static_cast<uint16_t*>(y), stream, ws, ws_bytes);
     } else {
         e = qaff::launch_gemv(x, x_dtype == QAFF_F32, m, packed, scales, biases, n, k, group_size, bits, y,
                               stream);
     }
     return after_launch(op, e, stream);
+}
+
+}  // namespace
+
+qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        int32_t group_size, int32_t bits, void* y, hipStream_t stream, qaff_path path) {
+    return qmm_impl("qaff_qmm", x, x_dtype, m, packed, scales, biases, n, k, group_size, bits, y, stream, path,
+                    nullptr, 0);
+}
+
+size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits) {
+    (void)group_size;
+    (void)bits;
+    if (m <= kGemvMaxM || n <= 0 || k <= 0) return 0;
+    return qaff::gemm_workspace_bytes(m, n, k);
+}
+
+qaff_status qaff_qmm_ws(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                        int32_t group_size, int32_t bits, void* workspace, size_t workspace_bytes, void* y,
+                        hipStream_t stream) {
+    static const char* op = "qaff_qmm_ws";
+    g_error.clear();
+    const size_t need = qaff_qmm_workspace_size(m, n, k, group_size, bits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: the workspace needs %zu bytes (qaff_qmm_workspace_size), got %zu",
+                        op, need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", op);
+    }
+    return qmm_impl(op, x, x_dtype, m, packed, scales, biases, n, k, group_size, bits, y, stream, QAFF_PATH_AUTO,
+                    need > 0 ? workspace : nullptr, need > 0 ? workspace_bytes : 0);
 }
 
 qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_packed,

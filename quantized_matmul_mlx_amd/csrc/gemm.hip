@@ -434,6 +434,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(
 // Requirements (checked by the launcher): K a multiple of 64 * kDirectBody (so of 8 groups);
 // scales and biases 16-byte aligned. Rows of X beyond m and rows of W beyond n are clamped, not
 // zeroed: they only reach outputs that are not stored.
+// Split K (PARTIAL): with few tiles, grid y splits K into `splits` ranges of whole 1024-code
+// chunks; block (tile, s) sums its range and stores the float32 tile to part[s][m][n], and
+// sum_partials_kernel adds the ranges in order.
 //
 // MFMA 32x32x16 (bf16) layout: lane l supplies row l % 32 of A and of W (column of B), each as 8
 // values of k slot l / 32; result value v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
@@ -446,11 +449,11 @@ constexpr int kDirectBody = 16;  // K-steps per loop iteration (scale windows ar
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BITS, int GSHIFT>
+template <int BITS, int GSHIFT, bool PARTIAL>
 __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
     const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
-    uint32_t tiles_n) {
+    uint32_t tiles_n, float* part, uint32_t splits) {
     constexpr int P = 4 << GSHIFT;                // K-steps per window of 8 groups
     constexpr int XPT = DBM * 8 / kDirectThreads;  // 16-byte X chunks per thread and step
     __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
@@ -478,11 +481,17 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     const uint32_t n0 = tn * DBN;
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> GSHIFT;  // groups per row
-    const uint32_t ktiles = kb >> 1;    // K-steps
-    const uint32_t nwin = gpr >> 3;     // scale windows
+    // This block's K range: 1024-code chunks [c0, c1) of the kb / 32 (all of them unless split).
+    const uint32_t chunks = kb >> 5;
+    const uint32_t split = PARTIAL ? blockIdx.y : 0u;
+    const uint32_t c0 = PARTIAL ? (uint32_t)((uint64_t)split * chunks / splits) : 0u;
+    const uint32_t c1 = PARTIAL ? (uint32_t)((uint64_t)(split + 1) * chunks / splits) : chunks;
+    const uint32_t kt_off = c0 * kDirectBody;               // first K-step
+    const uint32_t ktiles = (c1 - c0) * kDirectBody;        // K-steps of the range
+    const uint32_t nwin = ktiles / P;                       // scale windows of the range
 
     // X: chunk (xkc) of rows xrow + 64 i; 32-bit offsets within the tile's rows.
-    const uint16_t* xb = x + (size_t)m0 * k;
+    const uint16_t* xb = x + (size_t)m0 * k + (size_t)kt_off * 64;
     const int xrow = tid >> 3;
     const int xkc = tid & 7;
     uint32_t xo[XPT];
@@ -494,9 +503,9 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     }
     // W row of this lane, its block h of each step, and its scale and bias windows.
     const uint32_t wrow = min(n0 + 32 * wave + (lane & 31), n - 1);
-    const uint32_t* wp = packed + (size_t)wrow * kb * BITS + h * BITS;
-    const uint16_t* sp = scales + (size_t)wrow * gpr;
-    const uint16_t* bp = biases + (size_t)wrow * gpr;
+    const uint32_t* wp = packed + (size_t)wrow * kb * BITS + h * BITS + (size_t)kt_off * 2 * BITS;
+    const uint16_t* sp = scales + (size_t)wrow * gpr + (kt_off / P) * 8;
+    const uint16_t* bp = biases + (size_t)wrow * gpr + (kt_off / P) * 8;
 
     auto load_x = [&](u32x4a (&xr)[XPT], uint32_t kt) {
         const uint16_t* p = xb + min(kt, ktiles - 1) * 64;
@@ -596,8 +605,34 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const uint32_t gm = m0 + 32 * i + 8 * (v >> 2) + orow + (v & 3);
-                if (gm < m) y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][v]);
+                if (gm < m) {
+                    if constexpr (PARTIAL)
+                        part[((size_t)split * m + gm) * n + gc] = acc[i][v];
+                    else
+                        y[(size_t)gm * n + gc] = to_bf16_bits(acc[i][v]);
+                }
             }
+    }
+}
+
+// y[i] = bf16(part[0][i] + part[1][i] + ... + part[splits - 1][i]), in that order, for i < count.
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, uint64_t count, uint32_t splits,
+                                                           uint16_t* y) {
+    const uint64_t i = ((uint64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= count) return;
+    if (i + 4 <= count && (count & 3) == 0) {
+        f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+        for (uint32_t s = 1; s < splits; ++s) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(part + (size_t)s * count + i);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        *reinterpret_cast<u32x2*>(y + i) = u32x2{pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w)};
+        return;
+    }
+    for (uint64_t j = i; j < i + 4 && j < count; ++j) {
+        float a = part[j];
+        for (uint32_t s = 1; s < splits; ++s) a += part[(size_t)s * count + j];
+        y[j] = to_bf16_bits(a);
     }
 }
 
@@ -649,41 +684,75 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
 template <int BITS, int GSHIFT>
 hipError_t launch_direct_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                            const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, int64_t tiles_m,
-                           int64_t tiles_n, hipStream_t stream) {
-    gemm_direct_kernel<BITS, GSHIFT><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kDirectThreads), 0, stream>>>(
-        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m, (uint32_t)tiles_n);
+                           int64_t tiles_n, float* part, int64_t splits, hipStream_t stream) {
+    if (splits > 1) {
+        gemm_direct_kernel<BITS, GSHIFT, true><<<dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
+                                                 dim3(kDirectThreads), 0, stream>>>(
+            x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m,
+            (uint32_t)tiles_n, part, (uint32_t)splits);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const uint64_t count = (uint64_t)m * (uint64_t)n;
+        sum_partials_kernel<<<dim3((unsigned)((count + 1023) / 1024)), dim3(256), 0, stream>>>(part, count,
+                                                                                            (uint32_t)splits, y);
+        return hipGetLastError();
+    }
+    gemm_direct_kernel<BITS, GSHIFT, false><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kDirectThreads), 0, stream>>>(
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m, (uint32_t)tiles_n,
+        nullptr, 1u);
     return hipGetLastError();
 }
 
 template <int BITS>
 hipError_t launch_direct_b(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                            const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
-                           int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
-    if (gshift == 0) return launch_direct_g<BITS, 0>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
-    if (gshift == 1) return launch_direct_g<BITS, 1>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
-    return launch_direct_g<BITS, 2>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, stream);
+                           int64_t tiles_m, int64_t tiles_n, float* part, int64_t splits, hipStream_t stream) {
+    if (gshift == 0) return launch_direct_g<BITS, 0>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, part, splits, stream);
+    if (gshift == 1) return launch_direct_g<BITS, 1>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, part, splits, stream);
+    return launch_direct_g<BITS, 2>(x, m, packed, scales, biases, n, kb, y, tiles_m, tiles_n, part, splits, stream);
 }
 
 hipError_t launch_direct(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, int bits, uint32_t gshift, uint16_t* y,
-                         int64_t tiles_m, int64_t tiles_n, hipStream_t stream) {
+                         int64_t tiles_m, int64_t tiles_n, float* part, int64_t splits, hipStream_t stream) {
     switch (bits) {
-        case 1: return launch_direct_b<1>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 2: return launch_direct_b<2>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 3: return launch_direct_b<3>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 4: return launch_direct_b<4>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 5: return launch_direct_b<5>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 6: return launch_direct_b<6>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
-        case 8: return launch_direct_b<8>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, stream);
+        case 1: return launch_direct_b<1>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 2: return launch_direct_b<2>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 3: return launch_direct_b<3>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 4: return launch_direct_b<4>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 5: return launch_direct_b<5>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 6: return launch_direct_b<6>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
+        case 8: return launch_direct_b<8>(x, m, packed, scales, biases, n, kb, gshift, y, tiles_m, tiles_n, part, splits, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
+// Splits of K for the 128 x 256 kernel: enough K ranges (whole 1024-code chunks) for about one
+// block per compute unit when the tiles alone are fewer, and only where the product fits one
+// launch (one slice of m).
+int64_t direct_splits(int64_t m, int64_t n, int64_t k) {
+    if (m <= 0 || n <= 0 || k % (64 * kDirectBody) != 0) return 1;
+    const int64_t tiles_n = (n + DBN - 1) / DBN;
+    const int64_t tiles = ((m + DBM - 1) / DBM) * tiles_n;
+    if (tiles > 0x7fffffff / 2) return 1;
+    const int64_t chunks = k / (64 * kDirectBody);
+    int64_t s = (int64_t)device_cu_count() / tiles;
+    if (s > chunks) s = chunks;
+    if (s > 64) s = 64;
+    return s < 1 ? 1 : s;
+}
+
 }  // namespace
+
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    const int64_t s = direct_splits(m, n, k);
+    return s > 1 ? (size_t)s * (size_t)m * (size_t)n * sizeof(float) : 0;
+}
 
 hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
-                       int group_size, int bits, uint16_t* y, hipStream_t stream) {
+                       int group_size, int bits, uint16_t* y, hipStream_t stream, void* workspace,
+                       size_t workspace_bytes) {
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
@@ -693,11 +762,16 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
     if (k % (64 * kDirectBody) == 0 && a16(scales) && a16(biases)) {
         const int64_t tiles_n = (n + DBN - 1) / DBN;
         const int64_t max_rows = (int64_t)(0x7fffffff / tiles_n) * DBM;
+        // split K where the workspace allows it (float32 partials of every split)
+        const int64_t splits = direct_splits(m, n, k);
+        if (splits > 1 && workspace && workspace_bytes >= gemm_workspace_bytes(m, n, k))
+            return launch_direct(x, m, packed, scales, biases, n, kb, bits, gshift, y, (m + DBM - 1) / DBM, tiles_n,
+                                 static_cast<float*>(workspace), splits, stream);
         for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
             const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
             const int64_t tiles_m = (mm + DBM - 1) / DBM;
             const hipError_t e = launch_direct(x + (size_t)m_off * k, mm, packed, scales, biases, n, kb, bits, gshift,
-                                               y + (size_t)m_off * n, tiles_m, tiles_n, stream);
+                                               y + (size_t)m_off * n, tiles_m, tiles_n, nullptr, 1, stream);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;

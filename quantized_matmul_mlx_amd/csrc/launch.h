@@ -78,11 +78,15 @@ hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t*
                                    int group_size, int bits, uint16_t* y, const Gather& g,
                                    hipStream_t stream);
 
-// y[m, n] (bf16) = x (bf16) . dequantize(W)^T with W tiles dequantized to bf16 and bf16 MFMA,
-// float32 accumulation.
+// y[m, n] (bf16) = x (bf16) . dequantize(W)^T with W dequantized to bf16 and bf16 MFMA, float32
+// accumulation. With a workspace of at least gemm_workspace_bytes(m, n, k) bytes (16-byte
+// aligned), few tiles split K: float32 partial sums go to the workspace and a second kernel adds
+// them in order.
 hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
                        const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
-                       int group_size, int bits, uint16_t* y, hipStream_t stream);
+                       int group_size, int bits, uint16_t* y, hipStream_t stream, void* workspace = nullptr,
+                       size_t workspace_bytes = 0);
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // packed/scales/biases of a dense [rows, cols] weight (float32 or bf16): bias = group min,
 // scale = (max - min) / (2^bits - 1), both bf16; code = round((w - bias) / scale), clamped.

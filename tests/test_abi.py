@@ -254,6 +254,25 @@ def test_qmm_nt_checks(lib):
     assert qnt(lib, m=0, x=NULL, y=NULL, ws=NULL) == OK
 
 
+def qws(lib, m=128, n=4096, k=14336, G=128, bits=4, x=A16, y=A16, ws=A16, wsb=1 << 26):
+    return lib.qaff_qmm_ws(x, BF16, m, A16, A16, A16, n, k, G, bits, ws, wsb, y, NULL)
+
+
+def test_qmm_ws_checks(lib):
+    size = lambda m, n=4096, k=14336: lib.qaff_qmm_workspace_size(m, n, k, 128, 4)
+    assert size(16) == 0                                     # the decode path never splits
+    assert size(17) > 0 and size(128) > 0 and size(1024) > 0  # few GEMM tiles: K splits
+    assert size(2048) == 0                                   # a tile per compute unit already
+    assert size(128, k=14336 + 64) == 0                      # K not a multiple of 1024
+    assert size(128, k=1024) == 0                            # a single chunk of K
+    assert qws(lib, ws=NULL) == INVALID                      # a workspace is needed here ...
+    assert b"workspace" in lib.qaff_last_error()
+    assert qws(lib, wsb=4) == INVALID                        # ... large enough
+    assert qws(lib, ws=A4) == INVALID                        # ... and 16-byte aligned
+    assert qws(lib, m=0, x=NULL, y=NULL, ws=NULL) == OK
+    assert qws(lib, bits=7) == UNSUPPORTED
+
+
 def test_typed_checks(lib):
     F16 = _lib.QAFF_F16
     assert lib.qaff_promote_dtype(F16, F16) == F16

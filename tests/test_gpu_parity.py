@@ -207,6 +207,24 @@ def test_gemm_direct_small_m(orc, bits, G, m, n, k):
     check_qmm(orc, inp, y, path="gemm")
 
 
+# The automatic path of a bf16 x with few GEMM tiles splits K through a workspace that the binding
+# allocates (qaff_qmm_ws): 2, 3, 4 and 14 ranges of 1024 codes with ragged m and n, and a shape with
+# a single chunk of K, which cannot split. Against the oracle and against the unsplit kernel.
+@pytest.mark.parametrize("bits,G,m,n,k,splits", [(4, 128, 17, 300, 2048, True), (4, 64, 100, 520, 3072, True),
+                                                 (3, 32, 260, 264, 4096, True), (8, 128, 33, 256, 14336, True),
+                                                 (4, 128, 300, 4096, 1024, False)])
+def test_gemm_split_k(orc, bits, G, m, n, k, splits):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + n + k)
+    lib = qaff()._lib.load()
+    assert (lib.qaff_qmm_workspace_size(m, n, k, G, bits) > 0) == splits
+    banner(f"gemm split K bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="auto")
+    check_qmm(orc, inp, y, path="auto")
+    whole = run_qmm(inp, path="gemm")
+    a, b = host_f64(y), host_f64(whole)
+    assert orc.max_row_rel_err(a, b) <= 1e-2  # two float32 summation orders, each rounded to bf16
+
+
 # The same kernel at every other bit width (a block of 32 codes is BITS words; 3-, 5- and 6-bit
 # codes straddle words), with a ragged tile in m and in n.
 @pytest.mark.parametrize("bits", [1, 2, 3, 5, 6, 8])
