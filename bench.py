@@ -15,7 +15,8 @@ The same JSON line carries:
     against the 2.5 PFLOP/s dense bf16 MFMA peak: GEMMs back to back for a few seconds, with the
     graphics clock and socket power sampled meanwhile (`sustained`; the chip is power-limited and
     settles after a transient dip), and a short graph of launches (`burst`);
-  * `rows`: every other kernel of the path at its workload (standalone dequantization, gathered
+  * `rows`: every other kernel of the path at its workload (the prefill GEMM at a small batch,
+    M = 128, where K is split through a workspace; standalone dequantization, gathered
     rows, the 8-bit and the 3-/6-bit decode products at M = 1 and at their larger M, the decode
     product at M = 4, the fused decode FFN products gemv_gate_up and gemv_silu_gate with a
     residual, the product without the transpose at the decode shape, the decode product with
@@ -583,6 +584,46 @@ def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
     return res
 
 
+def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget):
+    """The prefill GEMM at a small batch (4-bit g128, W [4096, 14336], x bf16 [m, 14336]): few
+    tiles, so the automatic path splits K through a workspace (qaff_qmm_ws). Against the bf16
+    MFMA peak (2·m·n·k flop per step)."""
+    import oracle
+    wl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
+    inp = W.make_inputs(wl, m=m)
+    b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
+    copies = copies_for(b)
+    sets = replicate(torch, to_device(torch, inp), copies)
+    ys = [torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+
+    def launch(i):
+        s = sets[i % copies]
+        q.qmm(s["x"], s["packed"], s["scales"], s["biases"], wl.group_size, wl.bits, out=ys[i % copies])
+
+    ms = timer(launch, steps, warmup)
+    del sets, ys
+    torch.cuda.empty_cache()
+    flop = 2.0 * m * wl.n * wl.k
+    tflops = flop / (ms * 1e-3) / 1e12
+    lib = q._lib.load()
+    row = {"workload": f"prefill_4bit_g128_4096x14336 M={m} (small batch)",
+           "kernel": "gemm, K split through a workspace (qaff_qmm_ws)",
+           "splits_workspace_bytes": int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)),
+           "bytes_per_step": b, "ms_per_step": round(ms, 6), "tflops": round(tflops, 2), "weight_copies": copies,
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
+    if cpu:
+        threads = oracle.default_threads()
+        rows = 64
+        t0 = time.perf_counter()
+        oracle.qmm(inp.x[:rows], "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, threads=threads)
+        el = time.perf_counter() - t0
+        row["cpu_baseline"] = {"value": round(2.0 * rows * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{rows} of the {m} x rows against all of W, {el:.1f} s"}
+    return row
+
+
 def bench_context(torch, timer, metrics=None, sustain_s=0.0):
     """What the same box does on the same sizes without this library, timed the same way: an
     empty kernel launch, a device copy of the decode step's bytes (it reads them and writes as
@@ -733,6 +774,8 @@ def main():
     if not args.no_rows:
         rows = []
         rs, rw = args.row_steps, max(10, args.row_steps // 10)
+        log("row: prefill GEMM at M = 128 (K split)")
+        rows.append(bench_prefill_small(torch, q, W, timer, 128, rs, rw, cpu, 2.0))
         for name, m in (("decode_4bit_g64_4096x4096", 4), ("int8_g64_14336x4096", 1),
                         ("int8_g64_14336x4096", 8), ("odd_3bit_g32_11008x4096", 1),
                         ("odd_3bit_g32_11008x4096", 16), ("odd_6bit_g32_11008x4096", 1),
