@@ -152,7 +152,8 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
 /*
  * qaff_qmm (QAFF_PATH_AUTO) with a workspace that lets the bf16 GEMM path split K (nuvec_core
  * quantized_matmul with transpose, as qaff_qmm). Where the GEMM's 128 x 256 tiles are fewer than
- * the compute units (m up to about 1024 at n = 4096, K a multiple of 1024), K is split into ranges
+ * the compute units (m up to about 1024 at n = 4096, K a multiple of 1024; and 8 <= m <= 16 with K
+ * above 4096, which the decode kernels would otherwise take on the VALU), K is split into ranges
  * of whole 1024-code chunks: each range's float32 partial sums go to `workspace`, and a second
  * kernel adds the ranges in a fixed order (results are deterministic) and rounds y to bf16.
  *   Arguments as qaff_qmm, plus workspace: a caller-owned device buffer of at least
@@ -167,7 +168,8 @@ qaff_status qaff_qmm_ws(const void* x, qaff_dtype x_dtype, int64_t m, const uint
                         hipStream_t stream);
 
 /* Bytes of workspace qaff_qmm_ws can use for these sizes with a bf16 x (0 where it would not split
- * K: m <= 16, enough tiles, or K not a multiple of 1024). */
+ * K: enough tiles, K not a multiple of 1024, or m <= 16 inside the decode kernels' range). From 8
+ * rows on, K above 4096 codes (past the matrix-core decode kernel) also takes the split GEMM. */
 size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits);
 
 /*

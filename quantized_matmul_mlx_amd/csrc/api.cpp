@@ -10,6 +10,10 @@
 
 #include "launch.h"
 
+#ifndef QAFF_SPLIT_MIN_M
+#define QAFF_SPLIT_MIN_M 8
+#endif
+
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -148,6 +152,14 @@ qaff_status qaff_dequant_rows(const uint32_t* packed, const uint16_t* scales, co
 
 namespace {
 
+// Decode-sized m that take the GEMM with K split when a workspace is given: K beyond the
+// matrix-core decode kernel (more than 4096 codes) and a multiple of 1024, from kSplitMinM rows on,
+// where the VALU GEMV's work per code and x row outweighs the GEMM's fixed cost.
+constexpr int64_t kSplitMinM = QAFF_SPLIT_MIN_M;
+bool split_gemv_range(int64_t m, int64_t k) {
+    return m >= kSplitMinM && m <= kGemvMaxM && !qaff::gemv_mfma_supported(m, k) && k % 1024 == 0 && k > 4096;
+}
+
 // qaff_qmm_ex, and qaff_qmm_ws with a workspace (ws non-null: the call needs ws_need bytes, checked
 // by the caller; the GEMM path may split K into it).
 qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
@@ -182,6 +194,11 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
     if (x_dtype == QAFF_BF16) {
         use_gemm = path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && m > kGemvMaxM);
         use_mfma = path == QAFF_PATH_GEMV_MFMA || (path == QAFF_PATH_AUTO && m >= kGemvMfmaMinM && mfma_ok);
+        // with a workspace (qaff_qmm_ws sized it for these m, n, k), a few rows beyond the matrix-core
+        // decode kernel's K range take the GEMM with K split, which beats the VALU GEMV there
+        if (path == QAFF_PATH_AUTO && ws && m <= kGemvMaxM && !mfma_ok && split_gemv_range(m, k) &&
+            aligned(scales, 16) && aligned(biases, 16))
+            use_gemm = true;
     }
     hipError_t e;
     if (use_mfma && !use_gemm) {
@@ -209,7 +226,8 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m, const uint
 size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits) {
     (void)group_size;
     (void)bits;
-    if (m <= kGemvMaxM || n <= 0 || k <= 0) return 0;
+    if (n <= 0 || k <= 0) return 0;
+    if (m <= kGemvMaxM && !split_gemv_range(m, k)) return 0;
     return qaff::gemm_workspace_bytes(m, n, k);
 }
 

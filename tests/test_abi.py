@@ -260,7 +260,8 @@ def qws(lib, m=128, n=4096, k=14336, G=128, bits=4, x=A16, y=A16, ws=A16, wsb=1 
 
 def test_qmm_ws_checks(lib):
     size = lambda m, n=4096, k=14336: lib.qaff_qmm_workspace_size(m, n, k, 128, 4)
-    assert size(16) == 0                                     # the decode path never splits
+    assert size(16, k=4096) == 0                             # the matrix-core decode kernel's range
+    assert size(7) == 0 and size(8) > 0 and size(16) > 0     # past it, from 8 rows: the split GEMM
     assert size(17) > 0 and size(128) > 0 and size(1024) > 0  # few GEMM tiles: K splits
     assert size(2048) == 0                                   # a tile per compute unit already
     assert size(128, k=14336 + 64) == 0                      # K not a multiple of 1024

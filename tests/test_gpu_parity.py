@@ -65,6 +65,11 @@ def kernel_of(inp, path):
         return "gemv"
     if path == "gemm" or (path == "auto" and m > qaff().gemv_max_m()):
         return "gemm"
+    # the binding's automatic path passes a workspace when one is sized: decode-sized m beyond
+    # the matrix-core decode kernel's K range then take the GEMM with K split
+    wl = inp.wl
+    if path == "auto" and qaff()._lib.load().qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits) > 0:
+        return "gemm"
     if path == "gemv_mfma" or (path == "auto" and m >= qaff().gemv_mfma_min_m() and mfma_decode_takes(inp)):
         return "gemv_mfma"
     return "gemv"
@@ -223,6 +228,19 @@ def test_gemm_split_k(orc, bits, G, m, n, k, splits):
     whole = run_qmm(inp, path="gemm")
     a, b = host_f64(y), host_f64(whole)
     assert orc.max_row_rel_err(a, b) <= 1e-2  # two float32 summation orders, each rounded to bf16
+
+
+# Decode-sized m with K past the matrix-core decode kernel's range: from 8 rows on the automatic
+# path takes the split GEMM (faster than the VALU GEMV there); below, the VALU GEMV.
+@pytest.mark.parametrize("bits,G,m,k,gemm", [(4, 128, 8, 5120, True), (4, 64, 16, 6144, True), (6, 32, 12, 5120, True),
+                                             (4, 128, 7, 5120, False)])
+def test_decode_sized_m_split_gemm(orc, bits, G, m, k, gemm):
+    n = 300
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + k)
+    assert (kernel_of(inp, "auto") == "gemm") == gemm
+    banner(f"decode-sized m split gemm bits={bits} G={G} m={m} k={k}")
+    y = run_qmm(inp, path="auto")
+    check_qmm(orc, inp, y, path="auto")
 
 
 # The same kernel at every other bit width (a block of 32 codes is BITS words; 3-, 5- and 6-bit
