@@ -16,9 +16,11 @@
 //   * Codes become exact bf16 values with one AND-OR per pair of codes: for codes below 128,
 //     OR-ing the code into the mantissa of bf16 128.0 (0x4300) gives exactly 128 + c. The 4-bit
 //     pairs (c_i, c_{i+4}) of a word are (w >> 4i) & 0x000F000F | 0x43004300; 2-bit pairs
-//     (c_i, c_{i+8}) likewise. 3-, 5- and 6-bit codes are extracted one by one (a bit-field
-//     extract, or a funnel shift for codes that straddle words) and paired in column order. 8-bit
-//     codes go through the byte-to-float converts, exact in bf16 since c <= 255 has 8 bits.
+//     (c_i, c_{i+8}) likewise. 3-bit pairs (c_i, c_{i+8}) and 6-bit pairs (c_i, c_{i+4}) sit 24
+//     bits apart: one funnel shift, one byte permute and one AND-OR per pair. 5-bit codes are
+//     extracted one by one (a bit-field extract, or a funnel shift for codes that straddle words)
+//     and paired in column order. 8-bit codes go through the byte-to-float converts, exact in bf16
+//     since c <= 255 has 8 bits.
 //   * v_dot2_f32_bf16 multiplies two code pairs by two x pairs and accumulates in float32. Per
 //     block, with d = sum x_k (o + c_k) and xs = sum x_k (o = 128, or 0 for 8-bit codes),
 //         sum_k x_k (s c_k + b) = s * d + (b - o s) * xs,
@@ -187,9 +189,56 @@ template <> struct Codes<8, 1> {
     }
 };
 
-// 3-, 5-, 6-bit: pair i = (c_{2i}, c_{2i+1}) in column order, values o + c.
+// 32 bits of a block's stream from bit `bit` on (compile-time after unrolling): one funnel shift,
+// or a plain shift in the last word (the bits above the block are not used).
+template <int NW>
+__device__ __forceinline__ uint32_t stream_window(const uint32_t (&w)[NW], int bit) {
+    const int wi = bit >> 5, sh = bit & 31;
+    if (wi + 1 < NW) return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+    return w[wi] >> sh;
+}
+
+// 3-bit: pair 8q + p = (c_{16q+p}, c_{16q+p+8}), values o + c. With the stream shifted so that
+// c_i starts at bit 0, c_{i+8} starts at bit 24; one byte permute (bytes 0, 1, 3, 3) moves it to
+// bit 16, and one AND-OR forms the pair. x pairs as for 2-bit codes.
+template <int F> struct Codes<3, F> {
+    static constexpr float kOffset = kOffsetF<F>;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[3], uint32_t (&pr)[16]) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const uint32_t v = stream_window<3>(w, 3 * (16 * q + p));
+                pr[8 * q + p] = and_or(__builtin_amdgcn_perm(v, v, 0x03030100u), 0x00070007u, kMagicF<F>);
+            }
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+        Codes<2, F>::pair_x(xn, xp);
+    }
+};
+
+// 6-bit: pair 4q + p = (c_{8q+p}, c_{8q+p+4}), values o + c: c_{i+4} starts 24 bits after c_i, so
+// the same permute forms the pair. x pairs as for 4-bit codes.
+template <int F> struct Codes<6, F> {
+    static constexpr float kOffset = kOffsetF<F>;
+    __device__ __forceinline__ static void unpack(const uint32_t (&w)[6], uint32_t (&pr)[16]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t v = stream_window<6>(w, 6 * (8 * q + p));
+                pr[4 * q + p] = and_or(__builtin_amdgcn_perm(v, v, 0x03030100u), 0x003F003Fu, kMagicF<F>);
+            }
+    }
+    __device__ __forceinline__ static void pair_x(const uint32_t (&xn)[16], uint32_t (&xp)[16]) {
+        Codes<4, F>::pair_x(xn, xp);
+    }
+};
+
+// 5-bit: pair i = (c_{2i}, c_{2i+1}) in column order, values o + c (no pair of 5-bit codes sits
+// 16 or 24 bits apart within 32).
 template <int BITS, int F> struct Codes {
-    static_assert(BITS == 3 || BITS == 5 || BITS == 6, "bit width");
+    static_assert(BITS == 5, "bit width");
     static constexpr float kOffset = kOffsetF<F>;
     __device__ __forceinline__ static void unpack(const uint32_t (&w)[BITS], uint32_t (&pr)[16]) {
 #pragma unroll
