@@ -79,13 +79,6 @@ __device__ __forceinline__ uint16_t narrow16(float v) {  // round to nearest eve
         return to_bf16_bits(v);
 }
 
-// (a & mask) | orv in one v_and_or_b32 (the compiler otherwise emits an AND and an OR).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(orv));
-    return r;
-}
-
 // ---- per-bit-width unpacking into 16 bf16 pairs per 32-code block ---------------------------
 
 template <int BITS, int F = 0> struct Codes;
