@@ -25,13 +25,6 @@
 //  * Scales and biases of a tile row come as one window over the slice (16, 8 or 4 groups),
 //    not one load per block: small scattered loads were a third of the time.
 //  * The slices' float32 partial tiles are summed through LDS at the end.
-//  * 4-bit codes in groups of 64 or 128 enter the MFMA exactly, as bf16 128 + c (one AND-OR per
-//    pair of codes, pairs (c_i, c_{i+4}), x stored in the same pair order), and every MFMA
-//    contracts codes of one group; each group's float32 sums D and 128 X (one more MFMA against
-//    a constant 128) take the scale and bias: s D + (b / 128 - s) 128 X. Groups of 128: a chunk is
-//    one group. Groups of 64: lane g needs words 2 g and 2 g + 1 of both groups of the chunk,
-//    brought over from the lanes that loaded them by two row swaps (v_permlane16_swap,
-//    v_permlane32_swap) per pair of words.
 // Requirements (checked by the launcher): bf16 x, K a multiple of 512 and at most 4096.
 #include "launch.h"
 #include "qaff_device.h"
@@ -48,15 +41,6 @@ __device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, 
     uint32_t r;
     asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
     return r;
-}
-
-// Rows of 16 lanes: (a, b) = ([a0, a1, a2, a3], [b0, b1, b2, b3]) becomes ([a0, b0, a1, b1],
-// [a2, b2, a3, b3]): v_permlane16_swap exchanges the odd rows of a with the even rows of b, then
-// v_permlane32_swap the upper half of a with the lower half of b (one asm block, two wait states
-// before, between and after the swaps).
-__device__ __forceinline__ void swap_rows(uint32_t& a, uint32_t& b) {
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
-                 : "+v"(a), "+v"(b));
 }
 
 constexpr int kXPitch = 2 * kSlice + 16;  // bytes per x row in a wave's LDS region (banks: see below)
@@ -78,11 +62,6 @@ struct SbWindow {
             const u32x2 a = *reinterpret_cast<const u32x2*>(p);
             w[0] = a.x; w[1] = a.y;
         }
-    }
-    // float32 value of group i of the window (i compile-time)
-    __device__ __forceinline__ float at(int i) const {
-        const uint32_t word = w[i >> 1];
-        return __uint_as_float((i & 1) ? (word & 0xffff0000u) : (word << 16));
     }
     // float32 value of the group of block 4 c + g (c compile-time, g = lane / 16)
     __device__ __forceinline__ float get(int c, int g, uint64_t g_hi) const {
@@ -116,12 +95,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     const int lr16 = lane & 15;
     const int lg = lane >> 4;
     const uint64_t g_hi = __builtin_amdgcn_ballot_w64(lg >= 2);
-    // 4-bit codes in groups of 64 or 128: every MFMA contracts codes of a single group, so the
-    // codes enter exactly (bf16 128 + c) and the scale, bias and offset are applied to each
-    // group's MFMA sums: sum_k x_k (s c_k + b) = s D + (b / 128 - s) 128 X, with
-    // D = sum_k x_k (128 + c_k) and 128 X = sum_k x_k 128 from one more MFMA per group (shared by
-    // the row tiles).
-    constexpr bool kExact = BITS == 4 && GSHIFT >= 1;
 
     // 1. Loads, oldest first: this wave's slice of every x row (one contiguous 1 KB load per row),
     //    then per tile the scale and bias windows and, chunk by chunk, the W blocks, so that each
@@ -162,25 +135,15 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     // 2. x into this wave's LDS region: row r at r * 1040 bytes, so the 16 rows that the operand
     //    read touches at one offset fall on distinct banks (1040 / 4 = 4 mod 64).
     uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
-    //    For exact codes each 8-value unit is stored in the codes' pair order.
 #pragma unroll
-    for (int r = 0; r < MB; ++r)
-        *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = kExact ? pair_order4(xg[r]) : xg[r];
-    // lane g's x: block 4 c + g (64 g bytes into the chunk), or with exact codes in groups of 64
-    // its words 2 g, 2 g + 1 of each group (32 g bytes into the group)
-    const uint8_t* xa = xl + min((uint32_t)lr16, (uint32_t)MB - 1) * kXPitch + lg * (kExact && GSHIFT == 1 ? 32 : 64);
+    for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
+    const uint8_t* xa = xl + min((uint32_t)lr16, (uint32_t)MB - 1) * kXPitch + lg * 64;
 
     // 3. Multiply, chunk by chunk. Lane (r, g) of chunk c holds block 4 c + g of its row; MFMA j
     //    takes codes 8 j .. 8 j + 7 of each lane's block, and x in the same order.
     f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // bf16 128.0 in every element: the second operand of the X sums, held in registers of its own
-    // for the whole loop. Rematerialised per use, the compiler wrote it into the four registers
-    // that the code MFMA issued two instructions earlier took as its operand, and groups of 64
-    // came out wrong (every output row); with the constant kept apart they match the oracle.
-    u32x4a k128w = u32x4a{0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
-    if constexpr (kExact) asm volatile("" : "+v"(k128w));
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         // The empty asm makes chunk c's arithmetic start here, after every load is issued and
@@ -190,75 +153,19 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(wq[t][c][i]) : "v"(acc[0]));
-        if constexpr (kExact) {
-            // groups of 128: the chunk is group c, MFMA j takes word j of each lane's block;
-            // groups of 64: the chunk is groups 2 c and 2 c + 1, MFMA (h, j) takes word 2 h + j
-            constexpr int H = GSHIFT == 1 ? 2 : 1;
-            constexpr int J = 4 / H;
-            const bf16x8 k128 = __builtin_bit_cast(bf16x8, k128w);
-            // The words each lane multiplies. Groups of 64: lane g loaded block 4 c + g (words
-            // 0-1 = half 0, words 2-3 = half 1), and needs words 2 g, 2 g + 1 of group 2 c (half
-            // g % 2 of block 4 c + g / 2) and of group 2 c + 1 (the same of block 4 c + 2 + g / 2).
-            // With rows of 16 lanes holding (half 0, half 1) of blocks 0..3, swapping the odd rows
-            // of the halves 0 with the even rows of the halves 1, then the upper 32 lanes of the
-            // first with the lower 32 lanes of the second, leaves halves (0 of 0, 1 of 0, 0 of 1,
-            // 1 of 1) in the first and those of blocks 2 and 3 in the second.
-            uint32_t wg[NT][4];
+        bf16x8 wb[NT][4];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if constexpr (GSHIFT == 1) {
+        for (int t = 0; t < NT; ++t) {
+            const float sc = sw[t].get(c, lg, g_hi);
+            const float bi = bw[t].get(c, lg, g_hi);
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        uint32_t p0 = wq[t][c][e], p1 = wq[t][c][2 + e];
-                        swap_rows(p0, p1);
-                        wg[t][e] = p0;      // group 2 c, word 2 g + e
-                        wg[t][2 + e] = p1;  // group 2 c + 1, word 2 g + e
-                    }
-                } else {
+            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
+        }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) wg[t][e] = wq[t][c][e];
-                }
-            }
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
 #pragma unroll
-            for (int h = 0; h < H; ++h) {
-                f32x4 dg[NT];
-                f32x4 d128 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < NT; ++t) dg[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 128 * h + 16 * j);
-#pragma unroll
-                    for (int t = 0; t < NT; ++t)
-                        dg[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, codes4_exact(wg[t][J * h + j]), dg[t], 0, 0, 0);
-                    d128 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, k128, d128, 0, 0, 0);
-                }
-                const int grp = GSHIFT == 1 ? 2 * c + h : c;  // group within the slice's window
-#pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    // s D + (b / 128 - s) 128 X
-                    const float sc = sw[t].at(grp);
-                    const float beta = __builtin_fmaf(bw[t].at(grp), 0.0078125f, -sc);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        acc[t][v] = __builtin_fmaf(sc, dg[t][v], __builtin_fmaf(beta, d128[v], acc[t][v]));
-                }
-            }
-        } else {
-            bf16x8 wb[NT][4];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const float sc = sw[t].get(c, lg, g_hi);
-                const float bi = bw[t].get(c, lg, g_hi);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
-            }
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
         }
     }
 

@@ -117,20 +117,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
     return r;
 }
 
-// The eight 4-bit codes of a word as exact bf16 values 128 + c (OR-ing a code below 128 into the
-// mantissa of bf16 128.0 = 0x4300), in the pair order (c0, c4), (c1, c5), (c2, c6), (c3, c7).
-__device__ __forceinline__ bf16x8 codes4_exact(uint32_t w) {
-    const uint32_t o = 0x43004300u;
-    return __builtin_bit_cast(bf16x8, u32x4a{and_or(w, 0x000F000Fu, o), and_or(w >> 4, 0x000F000Fu, o),
-                                             and_or(w >> 8, 0x000F000Fu, o), and_or(w >> 12, 0x000F000Fu, o)});
-}
-
-// Eight bf16 values x0..x7 (four words, natural order) in that pair order: x0 x4 x1 x5 x2 x6 x3 x7.
-__device__ __forceinline__ u32x4a pair_order4(u32x4a v) {
-    return u32x4a{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
-                  __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
-}
-
 // Full-wave sum of a float (64 lanes), result in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -7,10 +7,8 @@ Bars:
   most 2e-3 for float32 y and 1.6e-2 for bf16 y.
 * A tighter check, derived from each kernel's arithmetic, catches single-code mistakes that the
   bars above would let through. Its reference is the oracle's own pieces composed the way the kernel
-  computes: the VALU GEMV uses the float32 weights (the oracle as is), and so does the matrix-core
-  decode kernel for 4-bit codes in groups of 64 or 128 (exact codes, scale and bias applied in
-  float32 to each group's sums); the GEMM and the matrix-core decode kernel at the other widths
-  and groups multiply their weights rounded to bf16 (the oracle's bf16 dequantization, then a
+  computes: the VALU GEMV uses the float32 weights (the oracle as is), the two MFMA kernels (GEMM
+  and matrix-core decode) their weights rounded to bf16 (the oracle's bf16 dequantization, then a
   float64 matmul). What is left is float32
   summation order (~1e-6 relative) and, for a bf16 y, one rounding of each output to nearest even:
   bf16 keeps 8 significant bits, so that rounding moves y by at most 2^-8 = 3.91e-3 of |y| <=
@@ -77,12 +75,6 @@ def kernel_of(inp, path):
     return "gemv"
 
 
-def exact_codes(inp, kernel):
-    """The matrix-core decode kernel takes 4-bit codes in groups of 64 or 128 exactly (bf16 128 + c)
-    and applies scale and bias to each group's float32 sums, as the VALU GEMV does."""
-    return kernel == "gemv" or (kernel == "gemv_mfma" and inp.wl.bits == 4 and inp.wl.group_size >= 64)
-
-
 def bf16_weight_ref(orc, inp, x_rows):
     """x . bf16(W)^T in float64: the oracle's bf16 dequantization, widened, through numpy matmul."""
     wl = inp.wl
@@ -101,8 +93,8 @@ def check_qmm(orc, inp, y, rows=None, path="auto"):
     err = orc.max_row_rel_err(got, ref)
     kind = inp.x_dtype
     assert err <= TOL[kind], f"max row rel err {err:.3e} > {TOL[kind]}"
-    # the MFMA kernels multiply bf16-rounded weights, except where they take the codes exactly
-    tight_ref = ref if exact_codes(inp, kernel_of(inp, path)) else bf16_weight_ref(orc, inp, x)
+    # both MFMA kernels multiply bf16-rounded weights
+    tight_ref = bf16_weight_ref(orc, inp, x) if kernel_of(inp, path) != "gemv" else ref
     terr = orc.max_row_rel_err(got, tight_ref)
     assert terr <= TIGHT[kind], f"{kernel_of(inp, path)}: max row rel err {terr:.3e} against its " \
                                 f"own arithmetic, above {TIGHT[kind]}"
@@ -295,6 +287,16 @@ def test_gemv_mfma(orc, bits, G, m, n, k):
 def test_gemv_mfma_row_tiles(orc, bits, n):
     inp = W.random_inputs(bits, 32, n, 4096, 16, seed=n + bits)
     banner(f"gemv_mfma row tiles bits={bits} n={n}")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
+# The same tile counts at 4 bits with groups of 64 and 128.
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("n", [4100, 8200, 12300])
+def test_gemv_mfma_row_tiles_groups(orc, G, n):
+    inp = W.random_inputs(4, G, n, 4096, 16, seed=n + G)
+    banner(f"gemv_mfma row tiles G={G} n={n}")
     y = run_qmm(inp, path="gemv_mfma")
     check_qmm(orc, inp, y, path="gemv_mfma")
 
