@@ -119,6 +119,23 @@ def test_gather_mfma_batched(orc, bits, G, m, k):
     check(orc, got, x, "bf16", packed, scales, biases, G, bits, lhs, rhs, "gemv_mfma")
 
 
+# Two row tiles per block: 128 output batches of 10 tiles each (n = 160) are more tiles than one
+# round of the compute units holds (at most 4 blocks of this size per unit), so the launcher takes
+# two tiles per block. Every width, M = 4 and 16.
+@pytest.mark.parametrize("bits,G", [(1, 32), (2, 64), (3, 32), (4, 128), (5, 64), (6, 32), (8, 64)])
+@pytest.mark.parametrize("m", [4, 16])
+def test_gather_mfma_batched_two_tiles(orc, bits, G, m):
+    E, n, k, batch = 16, 160, 512, 128
+    packed, scales, biases = experts(bits, G, E, n, k, seed=800 + bits)
+    x = draw_x((8, m, k), "bf16", seed=810 + m)
+    rng = np.random.default_rng(820 + bits)
+    lhs = rng.integers(0, 8, batch).astype(np.uint32)
+    rhs = rng.integers(0, E, batch).astype(np.uint32)
+    banner(f"gather mfma batched two tiles bits={bits} G={G} m={m}")
+    got = run(x, "bf16", packed, scales, biases, G, bits, lhs, rhs, path="gemv_mfma")
+    check(orc, got, x, "bf16", packed, scales, biases, G, bits, lhs, rhs, "gemv_mfma")
+
+
 # ---- grouped: sorted rhs, one row per batch, each expert's weights read once -----------------------
 
 def sorted_rows(counts):
