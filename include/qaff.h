@@ -114,7 +114,9 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
  *   code  = round((w - bias) / scale) with the stored bias and scale, half away from zero, clamped
  *           to [0, 2^bits - 1]; a stored scale of 0 (all values of the group equal) gives code 0,
  *           so such a group dequantizes to its value exactly.
- * All steps in float32 (w widened exactly from bf16), the division correctly rounded. NaN or
+ * The minimum, maximum, max - min and its quotient by 2^bits - 1 are float32 (w widened exactly
+ * from bf16) before the bf16 rounding. The code is the rounding of the exact value of
+ * (w - bias) / scale: neither the difference nor the quotient is rounded to float32 first. NaN or
  * infinite inputs give unspecified (but in-range) codes.
  *   w [rows, cols] in w_dtype (float32 or bf16); packed uint32 [rows, cols*bits/32]; scales and
  *   biases bf16 [rows, cols/group_size]. All caller-owned device buffers.

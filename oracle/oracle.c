@@ -353,17 +353,52 @@ int orc_gather_qmm(const void* x, int x_is_bf16, int64_t x_batches, int64_t m, c
     return 0;
 }
 
+/* Sign (-1, 0, +1) of the exact sum a + b + c of three doubles, by expansion arithmetic
+ * (Shewchuk, "Adaptive precision floating-point arithmetic and fast robust geometric predicates",
+ * 1997: Two-Sum, and Grow-Expansion with its theorem that the result is a nonoverlapping expansion
+ * in increasing order of magnitude, so its sign is that of its largest nonzero component).
+ * Round-to-nearest double arithmetic, no overflow (the arguments are float32-sized). */
+static void two_sum(double a, double b, double* s, double* e) {
+    *s = a + b;
+    const double bv = *s - a;
+    const double av = *s - bv;
+    *e = (a - av) + (b - bv);
+}
+
+static int sign_of_sum3(double a, double b, double c) {
+    double x, ex, q, h1, h2;
+    two_sum(a, b, &x, &ex);  /* a + b = x + ex exactly: the expansion [ex, x] */
+    two_sum(c, ex, &q, &h1); /* grow it by c */
+    two_sum(q, x, &q, &h2);  /* a + b + c = h1 + h2 + q exactly */
+    if (q != 0.0) return q > 0.0 ? 1 : -1; /* a NaN lands here as -1 */
+    if (h2 != 0.0) return h2 > 0.0 ? 1 : -1;
+    return (h1 > 0.0) - (h1 < 0.0);
+}
+
 /* [nuvec] quantize with [moshi]'s bias: each group of G values of a row, in the pages' order:
- *   bias  = the group minimum;
- *   scale = (max - min) / (2^bits - 1), the smallest step whose codes 0 .. 2^bits - 1 reach the
- *           group maximum from its minimum (the pages state no formula: this is the reading);
+ *   bias  = the group minimum; scale = (max - min) / (2^bits - 1): the statistics in float32,
  *   both stored as bf16 (round to nearest even), the dtype the kernels consume;
- *   code  = round((w - bias) / scale) with the stored bias and scale, rounded half away from zero
- *           (the Rust `round` of the page), clamped to [0, 2^bits - 1]; a group whose stored scale
- *           is 0 (all values equal) takes code 0, so it dequantizes to the bias exactly.
- * The statistics and w - bias are float32 (w widened exactly from bf16, or as given); the division
- * is the plain quotient, rounded as an exact value (not first rounded to float32). Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
+ *   code  = round((w - bias) / scale) with the stored bias and scale, the value of the formula
+ *           itself (no intermediate rounding of the difference or the quotient), rounded half away
+ *           from zero (the Rust `round` of the page) and clamped to [0, 2^bits - 1]; a group whose
+ *           stored scale is 0 (all values equal) takes code 0, so it dequantizes to the bias
+ *           exactly.
+ * For a positive scale, code c >= 0 is the rounded quotient exactly when
+ *     (c - 1/2) * scale <= w - bias < (c + 1/2) * scale,
+ * which is decided by the exact sign of w - bias - (c +- 1/2) * scale (each (c +- 1/2) * scale has
+ * at most 9 + 8 significant bits, exact in double). A double estimate is stepped until both hold.
+ * Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
  * Returns 0, or -1 for parameters outside the format. */
+static double quantize_code(float w, float bias, float scale, double top) {
+    if (scale == 0.0f) return 0.0;
+    double c = floor(((double)w - (double)bias) / (double)scale + 0.5);
+    if (!(c >= 0.0)) c = 0.0; /* also a NaN estimate */
+    if (c > top + 1.0) c = top + 1.0;
+    while (c > 0.0 && sign_of_sum3(w, -(double)bias, -(c - 0.5) * (double)scale) < 0) c -= 1.0;
+    while (c <= top && sign_of_sum3(w, -(double)bias, -(c + 0.5) * (double)scale) >= 0) c += 1.0;
+    return c > top ? top : c;
+}
+
 int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64_t group, int bits,
                  uint32_t* packed, uint16_t* scales, uint16_t* biases) {
     if (rows < 0 || bits > 8 || group > 128 || !valid_params(cols, group, bits)) return -1;
@@ -388,19 +423,8 @@ int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64
             scales[r * (cols / group) + g] = sb;
             biases[r * (cols / group) + g] = bb;
             const float sc = bf16_to_f32(sb), bi = bf16_to_f32(bb);
-            for (int64_t j = 0; j < group; ++j) {
-                double c = 0.0;
-                if (sc != 0.0f) {
-                    const float diff = v[j] - bi;
-                    /* the quotient of two floats in double: it lands on a half-integer only when
-                     * the exact quotient does, so round() decides as on the exact value */
-                    const double q = (double)diff / (double)sc;
-                    c = round(q);
-                    if (!(c >= 0.0)) c = 0.0; /* also a NaN quotient */
-                    if (c > top) c = top;
-                }
-                codes[r * cols + g * group + j] = (uint8_t)c;
-            }
+            for (int64_t j = 0; j < group; ++j)
+                codes[r * cols + g * group + j] = (uint8_t)quantize_code(v[j], bi, sc, (double)top);
         }
     const int rc = orc_pack_codes(codes, rows, cols, bits, packed);
     free(codes);

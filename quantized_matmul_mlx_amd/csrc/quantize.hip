@@ -4,8 +4,8 @@
 //   bias  = the group minimum, scale = (max - min) / (2^bits - 1), both stored as bf16 (RNE);
 //   code  = round((w - bias) / scale), half away from zero, with the stored bias and scale,
 //           clamped to [0, 2^bits - 1]; a stored scale of 0 (a constant group) gives code 0.
-// w - bias is a float32 difference; the rounding of the quotient is decided exactly (the quotient
-// itself is never rounded to float32 first).
+// The code is the rounded value of the formula itself: neither w - bias nor the quotient is rounded
+// to float32 before the decision.
 //
 // One lane per 32-value block: it loads its block, the G/32 lanes of a group (adjacent, since a
 // row holds a whole number of groups) combine their minima and maxima, and each lane writes its
@@ -89,20 +89,27 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     uint32_t words[BITS];
 #pragma unroll
     for (int i = 0; i < BITS; ++i) words[i] = 0u;
-    // code = round((w - bias) / scale), half away from zero, decided exactly: a candidate from the
-    // reciprocal is off by at most one, and the signs of d - (c -+ 1/2) s settle it (each product
-    // has at most 10 + 8 significant bits, exact in float32, so the fused form rounds only the
-    // difference, whose sign is exact).
+    // code = round((w - bias) / scale), half away from zero, decided exactly. d = fl(w - bias) and
+    // its rounding error e (Two-Sum: d + e = w - bias exactly). A candidate from the reciprocal is
+    // off by at most one; the signs of (w - bias) - (c0 -+ 1/2) s settle it. Each (c0 -+ 1/2) s has
+    // at most 9 + 8 significant bits, exact in float32, so the fused form rounds only d - p and
+    // keeps its sign. Where d != p, |d - p| is at least one ulp of d (d is on a grid of that ulp,
+    // p on one at least as coarse unless it is far smaller than d), which |e| (half an ulp at most)
+    // cannot overturn; where d == p, the sign is e's.
     const float rcp = sc != 0.0f ? 1.0f / sc : 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         float c = 0.0f;
         if (sc != 0.0f) {
             const float d = v[j] - bi;
+            const float dv = d - v[j];
+            const float e = (v[j] - (d - dv)) + (-bi - dv);
             const float c0 = __builtin_floorf(__builtin_fmaf(d, rcp, 0.5f));
-            const float hi = __builtin_fmaf(-(c0 + 0.5f), sc, d);  // >= 0: the quotient rounds above c0
-            const float lo = __builtin_fmaf(-(c0 - 0.5f), sc, d);  // <  0: the quotient rounds below c0
-            c = c0 + (hi >= 0.0f ? 1.0f : 0.0f) - (lo < 0.0f ? 1.0f : 0.0f);
+            const float rh = __builtin_fmaf(-(c0 + 0.5f), sc, d);
+            const float rl = __builtin_fmaf(-(c0 - 0.5f), sc, d);
+            const bool up = rh > 0.0f || (rh == 0.0f && e >= 0.0f);    // w - bias >= (c0 + 1/2) s
+            const bool down = rl < 0.0f || (rl == 0.0f && e < 0.0f);   // w - bias <  (c0 - 1/2) s
+            c = c0 + (up ? 1.0f : 0.0f) - (down ? 1.0f : 0.0f);
             c = c >= 0.0f ? c : 0.0f;  // also a NaN quotient
             c = c > kTop ? kTop : c;
         }

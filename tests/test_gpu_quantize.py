@@ -1,8 +1,8 @@
 """Quantization on the GPU against the CPU oracle, through the C ABI (via the binding).
 
-Codes are integers and scales and biases bf16 values, each decided by float32 arithmetic that both
-sides evaluate the same way (bias = group min, scale = (max - min) / (2^bits - 1) rounded to bf16,
-code = round-half-away((w - bias) / scale) clamped): the bar is bit-exact for all three outputs.
+Codes are integers and scales and biases bf16 values (bias = group min and scale =
+(max - min) / (2^bits - 1), float32 statistics rounded to bf16; code = round-half-away of the exact
+value of (w - bias) / scale, clamped): the bar is bit-exact for all three outputs.
 """
 import numpy as np
 import pytest
@@ -10,6 +10,7 @@ import torch
 
 import oracle as orc_mod
 from gpu_util import banner, dev_bf16, dev_u32, dev_x, host_bits
+from near_ties import bf16_rne, near_tie_groups, tie_example
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -73,6 +74,24 @@ def test_quantize_special_groups(orc, bits, G):
     banner(f"quantize special groups bits={bits} G={G}")
     check(orc, w, "f32", G, bits)
     check(orc, W.bf16_bits_from_f32(w), "bf16", G, bits)
+
+
+def test_quantize_exact_difference_decides_a_tie(orc):
+    # w - bias is not a float32 here; the exact quotients 3.5 - 2^-96 and 5.5 - 2^-96 round to 3
+    # and 5 (a float32 difference would land on the ties and give 4 and 6)
+    banner("quantize tie decided by the exact difference")
+    got = check(orc, tie_example(), "f32", 32, 4)
+    assert list(orc.unpack_codes(got[0], 32, 4)[0, :4]) == [0, 15, 3, 5]
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (6, 64), (2, 128), (5, 32)])
+def test_quantize_near_ties(orc, bits, G):
+    # values within a few ulps of every boundary bias + (k + 1/2) scale, minima of very different
+    # magnitudes: the exact decision on both sides
+    w = near_tie_groups(40, 3, G, bits, seed=300 + bits)
+    banner(f"quantize near ties bits={bits} G={G}")
+    check(orc, w, "f32", G, bits)
+    check(orc, bf16_rne(w), "bf16", G, bits)
 
 
 def test_quantize_round_trip_through_qmm(orc):

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from conftest import golden
+from near_ties import bf16_rne, near_tie_groups, tie_example
 from quantized_matmul_mlx_amd import workloads as W
 
 
@@ -556,6 +557,84 @@ def test_quantize_ties_round_away_from_zero(oracle_lib):
     assert W.f32_from_bf16_bits(sc)[0, 0] == 1.0 and W.f32_from_bf16_bits(bi)[0, 0] == 0.0
     codes = oracle_lib.unpack_codes(packed, 32, 4)[0]
     assert list(codes[:9]) == [0, 15, 3, 4, 8, 15, 1, 1, 7]   # halves go up; ties-to-even would give 2, 4, 8, 14, 0
+
+
+def _round_half_away(q: Fraction) -> int:
+    # the Rust `round` of the page, on an exact rational
+    return int(q + Fraction(1, 2)) if q >= 0 else -int(-q + Fraction(1, 2))
+
+
+def _exact_codes(w, sc, bi, G, bits):
+    """round((w - bias) / scale) clamped, each quotient an exact rational (Fraction)."""
+    top = 2 ** bits - 1
+    s = W.f32_from_bf16_bits(sc).astype(np.float64)
+    b = W.f32_from_bf16_bits(bi).astype(np.float64)
+    out = np.zeros(w.shape, np.int64)
+    for r in range(w.shape[0]):
+        for j in range(w.shape[1]):
+            sg, bg = s[r, j // G], b[r, j // G]
+            if sg == 0.0:
+                continue
+            c = _round_half_away((Fraction(float(w[r, j])) - Fraction(bg)) / Fraction(sg))
+            out[r, j] = min(max(c, 0), top)
+    return out
+
+
+def test_quantize_exact_difference_decides_a_tie(oracle_lib):
+    # nuvec_core stores round((w - bias) / scale). Here w - bias is not a float32: the group's
+    # minimum (and so its bias) is 2^-100, its maximum 0.9375, so scale = 0.9375 / 15 = 0.0625
+    # exactly, and w = 3.5 * 0.0625 gives the exact quotient 3.5 - 2^-96, which rounds to 3. A
+    # float32 difference would round w - bias onto 3.5 * 0.0625 and the tie up to 4 (the same for
+    # 5.5 * 0.0625: 5, not 6). The expected codes come from exact rationals.
+    w = tie_example()
+    tiny = w[0, 0]
+    assert np.float32(w[0, 2] - tiny) == w[0, 2]                  # the float32 difference rounds
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 32, 4)
+    assert W.f32_from_bf16_bits(sc)[0, 0] == 0.0625 and W.f32_from_bf16_bits(bi)[0, 0] == tiny
+    codes = oracle_lib.unpack_codes(packed, 32, 4)[0]
+    expect = _exact_codes(w, sc, bi, 32, 4)[0]
+    assert list(expect[:5]) == [0, 15, 3, 5, 8]
+    np.testing.assert_array_equal(codes, expect)
+
+
+def test_float32_quotient_of_a_float32_difference_is_exact_at_ties():
+    # Why no pin separates an exact quotient from a float32 one: for a float32 d and a bf16 scale
+    # s, fl32(d / s) is a half-integer only when d / s is (moving d by one ulp moves the quotient
+    # by more than half an ulp). Checked on values within a few ulps of every tie k + 1/2.
+    rng = np.random.default_rng(5)
+    s = W.f32_from_bf16_bits(bf16_rne(rng.uniform(1e-3, 4.0, 20000)))
+    k = rng.integers(0, 256, 20000)
+    p = ((k + 0.5) * s.astype(np.float64)).astype(np.float32)           # exact: 9 + 8 bits
+    d = p.copy()
+    steps = rng.integers(-3, 4, 20000)
+    for i in range(d.size):
+        for _ in range(abs(int(steps[i]))):
+            d[i] = np.nextafter(d[i], np.float32(np.inf if steps[i] > 0 else -np.inf))
+    q32 = d / s
+    on_tie = q32.astype(np.float64) == k + 0.5
+    assert on_tie.sum() > 1000
+    for i in np.flatnonzero(on_tie):
+        assert Fraction(float(d[i])) / Fraction(float(s[i])) == Fraction(2 * int(k[i]) + 1, 2)
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (6, 64)])
+def test_quantize_codes_are_exact_rational_rounding(oracle_lib, bits, G):
+    # groups with values within a few float32 ulps of every kind of tie b + (k + 1/2) s, and
+    # minima of very different magnitudes (so that w - bias often rounds): every code equals the
+    # exact rational rounding of (w - bias) / scale, and the scales and biases are the bf16
+    # roundings of the float32 statistics
+    rows, top = 24, 2 ** bits - 1
+    w = near_tie_groups(rows, 2, G, bits, seed=200 + bits)
+    for dt in ("f32", "bf16"):
+        wi = w if dt == "f32" else bf16_rne(w)
+        wf = w if dt == "f32" else W.f32_from_bf16_bits(wi)
+        packed, sc, bi = oracle_lib.quantize(wi, dt, G, bits)
+        wg = wf.reshape(rows, -1, G)
+        lo, hi = wg.min(-1), wg.max(-1)
+        np.testing.assert_array_equal(sc, bf16_rne((hi - lo) / np.float32(top)))
+        np.testing.assert_array_equal(bi, bf16_rne(lo))
+        codes = oracle_lib.unpack_codes(packed, 2 * G, bits).astype(np.int64)
+        np.testing.assert_array_equal(codes, _exact_codes(wf, sc, bi, G, bits))
 
 
 def test_quantize_clamps(oracle_lib):
