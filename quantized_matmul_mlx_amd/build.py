@@ -1,9 +1,10 @@
-"""Builds libqaff.so (HIP, gfx950 only) in-tree with hipcc.
+"""Builds libqaff.so (HIP, gfx950 only) in-tree with hipcc, and beside it libqaff_bench.so (the
+benchmark's measurement aids, include/qaff_bench.h; not linked into libqaff.so).
 
     python -m quantized_matmul_mlx_amd.build          # or __graft_entry__.build()
 
 Each source compiles to an object under _build/ in parallel, then they link into
-quantized_matmul_mlx_amd/libqaff.so. Always recompiles.
+quantized_matmul_mlx_amd/libqaff.so and libqaff_bench.so. Always recompiles.
 """
 from __future__ import annotations
 
@@ -17,8 +18,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqaff.so")
+BENCH_LIB = os.path.join(PKG, "libqaff_bench.so")
 
 SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip", "typed.hip"]
+BENCH_SOURCES = ["bench_aux.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -52,16 +55,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(lib: str, objs, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link(LIB, [objs[s] for s in SOURCES], verbose)
+    _link(BENCH_LIB, [objs[s] for s in BENCH_SOURCES], verbose)
     return LIB
 
 

@@ -10,10 +10,6 @@
 
 #include "launch.h"
 
-#ifndef QAFF_SPLIT_MIN_M
-#define QAFF_SPLIT_MIN_M 8
-#endif
-
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -39,10 +35,7 @@ qaff_status fail(qaff_status st, const char* fmt, ...) {
 }
 
 constexpr int kGemvMaxM = 16;
-#ifndef QAFF_GEMV_MFMA_MIN_M
-#define QAFF_GEMV_MFMA_MIN_M 3
-#endif
-constexpr int kGemvMfmaMinM = QAFF_GEMV_MFMA_MIN_M;
+constexpr int kGemvMfmaMinM = 3;
 
 bool debug_sync() {
     static const bool on = [] {
@@ -155,7 +148,7 @@ namespace {
 // Decode-sized m that take the GEMM with K split when a workspace is given: K beyond the
 // matrix-core decode kernel (more than 4096 codes) and a multiple of 1024, from kSplitMinM rows on,
 // where the VALU GEMV's work per code and x row outweighs the GEMM's fixed cost.
-constexpr int64_t kSplitMinM = QAFF_SPLIT_MIN_M;
+constexpr int64_t kSplitMinM = 8;
 bool split_gemv_range(int64_t m, int64_t k) {
     return m >= kSplitMinM && m <= kGemvMaxM && !qaff::gemv_mfma_supported(m, k) && k % 1024 == 0 && k > 4096;
 }

@@ -20,19 +20,12 @@ namespace qaff {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef QAFF_DQ_UNITS
-#define QAFF_DQ_UNITS 4
-#endif
-constexpr int kUnits = QAFF_DQ_UNITS;  // units per lane: all their loads are issued before any store
+constexpr int kUnits = 4;  // units per lane: all their loads are issued before any store
 
 // Codes per unit: 4 (16 bytes of float32), or 8 for bf16 outputs of codes up to 4 bits (16 bytes
 // of bf16, still one funnel shift of two words).
 template <int BITS, bool OUT_BF16>
-#ifdef QAFF_DQ_NARROW
-constexpr int kUnitCodes = 4;
-#else
 constexpr int kUnitCodes = (OUT_BF16 && BITS <= 4) ? 8 : 4;
-#endif
 
 // The pointers are deliberately not __restrict__: with it, the compiler moves each unit's loads
 // down to its store, one unit at a time, past the empty asm that keeps them together.

@@ -638,10 +638,7 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, ui
 
 // Waves of the 256 x 128 tile along M (WN = 2 along N): 2 gives four 128 x 64 wave tiles, 4 gives
 // eight 64 x 64 ones.
-#ifndef QAFF_GEMM_WM
-#define QAFF_GEMM_WM 4
-#endif
-constexpr int kBigWM = QAFF_GEMM_WM;
+constexpr int kBigWM = 4;
 constexpr int kBigWN = 2;
 
 // m above this uses the 256 x 128 tiles; below, the 128 x 128 tiles waste less on padding.

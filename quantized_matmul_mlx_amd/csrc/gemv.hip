@@ -659,18 +659,8 @@ hipError_t over_m_slices(int64_t m, int mb, Launch&& launch) {
 }
 
 // Rows per wave and waves per block of the bf16 GEMV, per number of x rows handled by one block.
-#ifndef QAFF_GEMV_RPW_1
-#define QAFF_GEMV_RPW_1 1
-#endif
-#ifndef QAFF_GEMV_WAVES_1
-#define QAFF_GEMV_WAVES_1 8
-#endif
-#ifndef QAFF_GEMV_RPW_N
-#define QAFF_GEMV_RPW_N 2
-#endif
-#ifndef QAFF_GEMV_WAVES_N
-#define QAFF_GEMV_WAVES_N 4
-#endif
+constexpr int kRpw1 = 1, kWaves1 = 8;  // M = 1
+constexpr int kRpwN = 2, kWavesN = 4;  // M >= 2
 
 // Blocks per lane and pass: 2 (128 blocks, 4096 codes: one pass at the decode shape). Each pass
 // waits for its own loads, so long rows at small MB take wider passes: 8 (MB = 1) or 4 (MB = 2)
@@ -703,9 +693,10 @@ hipError_t launch_bf16(const uint16_t* x, int64_t m, const uint32_t* packed, con
                        const uint16_t* biases, int64_t n, int64_t kb, uint32_t gshift, uint16_t* y,
                        const GemvFused& fz, hipStream_t stream) {
     // long rows: the wider pass, and scales and biases through LDS when a row has an even number
-    // of groups (their 16-byte loads need 4-byte alignment)
+    // of groups and the arrays are 4-byte aligned (their 16-byte loads need 4-byte aligned words)
     if (kLongPass<MB> > 2 && kb > 128) {
-        if (((kb >> gshift) & 1) == 0)
+        const bool sb4 = reinterpret_cast<uintptr_t>(scales) % 4 == 0 && reinterpret_cast<uintptr_t>(biases) % 4 == 0;
+        if (((kb >> gshift) & 1) == 0 && sb4)
             return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, true, F>(x, m, packed, scales, biases, n,
                                                                                    kb, gshift, y, fz, stream);
         return launch_bf16_p<BITS, MB, RPW, WAVES, FUSED, kLongPass<MB>, false, F>(x, m, packed, scales, biases, n, kb,
@@ -730,12 +721,12 @@ hipError_t launch_bf16_m(const uint16_t* x, int64_t m, const uint32_t* packed, c
     if (m == 1 && BITS == 3)
         return launch_bf16<BITS, 1, 2, 8, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 1)
-        return launch_bf16<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 1, kRpw1, kWaves1, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m == 2)
-        return launch_bf16<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 2, kRpwN, kWavesN, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
     if (m <= 4)
-        return launch_bf16<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
-    return launch_bf16<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+        return launch_bf16<BITS, 4, kRpwN, kWavesN, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
+    return launch_bf16<BITS, 8, kRpwN, kWavesN, FUSED, F>(x, m, packed, scales, biases, n, kb, gshift, y, f, stream);
 }
 
 template <int BITS, int MB>
@@ -839,12 +830,12 @@ hipError_t launch_gather_bits(const void* x, bool x_f32, int64_t m, const uint32
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     uint16_t* yb = static_cast<uint16_t*>(y);
     if (m == 1)
-        return launch_bf16_gather<BITS, 1, QAFF_GEMV_RPW_1, QAFF_GEMV_WAVES_1>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+        return launch_bf16_gather<BITS, 1, kRpw1, kWaves1>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
     if (m == 2)
-        return launch_bf16_gather<BITS, 2, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+        return launch_bf16_gather<BITS, 2, kRpwN, kWavesN>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
     if (m <= 4)
-        return launch_bf16_gather<BITS, 4, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
-    return launch_bf16_gather<BITS, 8, QAFF_GEMV_RPW_N, QAFF_GEMV_WAVES_N>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+        return launch_bf16_gather<BITS, 4, kRpwN, kWavesN>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
+    return launch_bf16_gather<BITS, 8, kRpwN, kWavesN>(xb, m, packed, scales, biases, n, kb, gshift, yb, g, stream);
 }
 
 }  // namespace

@@ -500,10 +500,7 @@ hipError_t launch_gather_mb(const uint16_t* x, int64_t m, const uint32_t* packed
     const int64_t slots = (int64_t)device_cu_count() * per_cu;
     const int64_t batches = ga.grouped ? (ga.batch < ga.w_count ? ga.batch : ga.w_count) : ga.batch;
     const int64_t tiles = ((n + 15) / 16) * (batches > 0 ? batches : 1);
-    int64_t nt = (tiles + slots - 1) / slots;
-#ifdef QAFF_GATHER_NT
-    nt = QAFF_GATHER_NT;
-#endif
+    const int64_t nt = (tiles + slots - 1) / slots;
     // at most two tiles (measured on 128 experts of [768, 2048] 4-bit, 512 and 4096 sorted rows:
     // two tiles 40 and 86 us, four 43 and 116 us, one 42 and 114 us)
     if (nt <= 1) return launch_gather_nt<BITS, 1, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, ga, stream);
@@ -517,10 +514,7 @@ hipError_t launch_gather_g(const uint16_t* x, int64_t m, const uint32_t* packed,
     // rows per tile: m, or twice the mean number of rows per expert when grouped, so that most
     // experts take one tile (each tile dequantizes the weights again). Measured at 512 rows over
     // 128 experts (mean 4): 4 rows per tile 40 us, 8 rows 37 us, 16 rows 48 us.
-    int64_t rows = ga.grouped ? (2 * (int64_t)ga.batch + ga.w_count - 1) / (ga.w_count ? ga.w_count : 1) : m;
-#ifdef QAFF_GATHER_MB
-    if (ga.grouped) rows = QAFF_GATHER_MB;
-#endif
+    const int64_t rows = ga.grouped ? (2 * (int64_t)ga.batch + ga.w_count - 1) / (ga.w_count ? ga.w_count : 1) : m;
     if (rows <= 4) return launch_gather_mb<BITS, GSHIFT, 4>(x, m, packed, scales, biases, n, kb, y, ga, stream);
     if (rows <= 8) return launch_gather_mb<BITS, GSHIFT, 8>(x, m, packed, scales, biases, n, kb, y, ga, stream);
     return launch_gather_mb<BITS, GSHIFT, 16>(x, m, packed, scales, biases, n, kb, y, ga, stream);

@@ -29,11 +29,8 @@ constexpr int kNtPhases = 16;  // row phases per thread block
 constexpr int kNtMaxM = 2;     // x rows per launch
 constexpr int kNtPad = 33;     // floats per (phase, column block, row) in the LDS sums
 // rows per lane and K chunk (all loaded at once: fewer for the wider codes, within the registers)
-#ifndef QAFF_NT_ROWS
-#define QAFF_NT_ROWS 8
-#endif
 template <int BITS>
-constexpr int kNtRows = BITS >= 6 ? (QAFF_NT_ROWS < 8 ? QAFF_NT_ROWS : 8) : QAFF_NT_ROWS;
+constexpr int kNtRows = 8;
 
 template <int BITS, int MB, bool XF32>
 __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(

@@ -41,3 +41,13 @@ def host_bits(t):
 def host_f64(t):
     t = t.detach().cpu()
     return t.float().numpy().astype(np.float64)
+
+
+def at_offset(t, elements=1):
+    """A contiguous copy of t that starts `elements` elements past a fresh allocation (2 bytes for
+    bf16: not 4- or 16-byte aligned)."""
+    flat = t.reshape(-1)
+    big = torch.empty(flat.numel() + elements, dtype=t.dtype, device=t.device)
+    view = big[elements:]
+    view.copy_(flat)
+    return view.view(t.shape)

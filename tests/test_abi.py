@@ -42,6 +42,30 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"{name} is declared in qaff.h but not exported"
 
 
+def test_bench_aids_export_every_declared_symbol(lib):
+    # the benchmark's measurement aids: include/qaff_bench.h against libqaff_bench.so
+    text = open(os.path.join(ROOT, "include", "qaff_bench.h")).read()
+    declared = sorted(set(re.findall(r"\b(qaff_bench_[a-z_0-9]+)\s*\(", text)))
+    assert declared == ["qaff_bench_read", "qaff_bench_stamp", "qaff_bench_wall_clock_khz"]
+    aux = ctypes.CDLL(os.path.join(ROOT, "quantized_matmul_mlx_amd", "libqaff_bench.so"))
+    for name in declared:
+        assert hasattr(aux, name), f"{name} is declared in qaff_bench.h but not exported"
+    # argument checks on the host (fake addresses, never dereferenced)
+    aux.qaff_bench_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    aux.qaff_bench_read.restype = ctypes.c_int
+    assert aux.qaff_bench_read(A16, 100, 4, 0, 0, A16, NULL) != 0      # not a multiple of 16 bytes
+    assert aux.qaff_bench_read(A4, 64, 4, 0, 0, A16, NULL) != 0        # misaligned source
+    assert aux.qaff_bench_read(A16, 64, 3, 0, 0, A16, NULL) != 0       # unsupported shape
+    assert aux.qaff_bench_read(NULL, 64, 4, 0, 0, A16, NULL) != 0
+
+
+def test_product_library_does_not_link_the_bench_aids(lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    assert "qaff_bench_" not in out
+
+
 def test_version_and_status_strings(lib):
     assert lib.qaff_abi_version() == _lib.ABI_VERSION
     assert lib.qaff_status_string(OK) == b"QAFF_OK"

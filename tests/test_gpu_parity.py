@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import oracle as orc_mod
-from gpu_util import banner, dev_weights, dev_x, host_bits, host_f64
+from gpu_util import at_offset, banner, dev_weights, dev_x, host_bits, host_f64
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -176,6 +176,23 @@ def test_gemv_long_rows(orc, bits, G, m, kb):
     banner(f"gemv long rows bits={bits} G={G} m={m} k={k}")
     y = run_qmm(inp, path="gemv")
     check_qmm(orc, inp, y, path="gemv")
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_long_rows_scales_at_two_byte_offset(orc, m):
+    # k = 14336 at G = 64 (an even number of groups per row): with 4-byte aligned scales the long
+    # pass stages them through LDS in 16-byte loads; at a 2-byte offset it must read them per block
+    inp = W.random_inputs(4, 64, 300, 14336, m, seed=41 + m)
+    p, s, b = dev_weights(inp)
+    s2, b2 = at_offset(s), at_offset(b)
+    assert s2.data_ptr() % 4 == 2 and b2.data_ptr() % 4 == 2
+    x = dev_x(inp.x, "bf16")
+    banner(f"gemv long rows, scales at a 2-byte offset, m={m}")
+    y = qaff().qmm(x, p, s2, b2, 64, 4, path="gemv")
+    torch.cuda.synchronize()
+    check_qmm(orc, inp, y, path="gemv")
+    y_aligned = run_qmm(inp, path="gemv")
+    assert torch.equal(y.view(torch.int16), y_aligned.view(torch.int16))
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
@@ -401,10 +418,10 @@ def test_full_odd_widths(orc, name, m):
     _full_qmm(orc, name, m)
 
 
-def test_full_prefill_gemm_sampled_rows(orc):
-    # every x row computes on the GPU; the oracle checks 24 of them (first, last, spread between)
-    rows = np.unique(np.concatenate([np.arange(0, 4), np.arange(2044, 2048), np.arange(7, 2048, 127)]))
-    _full_qmm(orc, "prefill_4bit_g128_4096x14336", 2048, rows=rows)
+def test_full_prefill_gemm_every_row(orc):
+    # all 2048 x rows against the oracle (every tile, sub-tile and accumulator slot of the launch
+    # the benchmark times)
+    _full_qmm(orc, "prefill_4bit_g128_4096x14336", 2048)
 
 
 def test_full_decode_dequant_bit_exact(orc):
