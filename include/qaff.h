@@ -197,6 +197,27 @@ qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint
 size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits);
 
 /*
+ * qaff_qmm_nt for callers that cannot allocate device memory (code under graph capture, serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same results, bit for bit, with
+ * the float32 partial sums in a scratch array that the library holds in every device's memory
+ * (qaff_qmm_nt_static_max_bytes() bytes per device, from the library's load until the process
+ * ends) instead of a caller workspace. The call allocates and frees nothing.
+ *   Arguments as qaff_qmm_nt without the workspace. The scratch is resolved for the device current
+ *   at the call (once per device).
+ *   Every call on a device shares that device's scratch and leaves its last contents there (no
+ *   state is carried: every partial sum a call reads, it wrote first). Calls that overlap on one
+ *   device race: order them (the same stream, or events between streams).
+ * Errors: as qaff_qmm_nt, plus UNSUPPORTED where the sizes need more partial sums than the scratch
+ * holds (qaff_qmm_nt_workspace_size(m, k, n, bits) > qaff_qmm_nt_static_max_bytes()).
+ */
+qaff_status qaff_qmm_nt_static(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                               const uint16_t* scales, const uint16_t* biases, int64_t k, int64_t n,
+                               int32_t group_size, int32_t bits, void* y, hipStream_t stream);
+
+/* Bytes of the per-device scratch array behind qaff_qmm_nt_static. */
+size_t qaff_qmm_nt_static_max_bytes(void);
+
+/*
  * Dual decode product (spark_runtime weights/mlx_int8.rs gemv_gate_up): gate_y = x . dequantize(G)^T
  * and up_y = x . dequantize(U)^T in one launch, x read once. Both weights share n, k, group_size
  * and bits. x bf16 [m, k] with 1 <= m <= 16; gate_y, up_y bf16 [m, n]; sums in float32, each output

@@ -150,11 +150,13 @@ def quantize(w, group_size: int, bits: int):
     return packed, scales, biases
 
 
-def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None):
+def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None, static_scratch: bool = False):
     """``x . dequantize(W)`` for a weight stored ``[k, n]`` (nuvec_core ``quantized_matmul`` with
     ``transpose=False``): packed ``[k, n*bits/32]``, scales and biases ``[k, n/group_size]``;
     x float32 or bf16 ``[..., k]`` (1-D: one row); the result has x's dtype and shape ``[..., n]``.
-    The call's float32 K-chunk partial sums go to a workspace tensor allocated here."""
+    The call's float32 K-chunk partial sums go to a workspace tensor allocated here, or with
+    ``static_scratch`` (and ``out`` given) to the library's per-device scratch array
+    (``qaff_qmm_nt_static``): the call then allocates nothing."""
     lib = _lib.load()
     dev, k, n = _weights(packed, scales, biases, group_size, bits)
     _need(x, "x", tuple(_OUT_DTYPES), dev)
@@ -168,6 +170,11 @@ def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None):
         _need(out, "out", (x.dtype,), dev)
         if tuple(out.shape) != lead + (n,):
             raise ValueError(f"out must be {list(lead + (n,))}")
+    if static_scratch:
+        with torch.cuda.device(dev):
+            _lib.check(lib.qaff_qmm_nt_static(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k,
+                                              n, group_size, bits, _p(out), _stream(dev)))
+        return out
     nbytes = int(lib.qaff_qmm_nt_workspace_size(m, k, n, bits))
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):

@@ -22,7 +22,8 @@ PATHS = {"auto": 0, "gemv": 1, "gemm": 2, "gemv_mfma": 3}
 EXPORTS = ("qaff_dequantize", "qaff_qmm", "qaff_qmm_ex", "qaff_dequant_rows", "qaff_last_error",
            "qaff_status_string", "qaff_abi_version", "qaff_gemv_max_m", "qaff_gemv_mfma_min_m",
            "qaff_gemv_gate_up", "qaff_gemv_silu_gate", "qaff_gather_qmm", "qaff_gather_qmm_ex",
-           "qaff_quantize", "qaff_qmm_nt", "qaff_qmm_nt_workspace_size", "qaff_qmm_ws", "qaff_qmm_workspace_size",
+           "qaff_quantize", "qaff_qmm_nt", "qaff_qmm_nt_workspace_size", "qaff_qmm_nt_static",
+           "qaff_qmm_nt_static_max_bytes", "qaff_qmm_ws", "qaff_qmm_workspace_size",
            "qaff_promote_dtype",
            "qaff_dequantize_typed", "qaff_qmm_typed")
 
@@ -61,6 +62,9 @@ def load() -> ctypes.CDLL:
     lib.qaff_dequantize_typed.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, vp, ctypes.c_int, vp]
     lib.qaff_qmm_typed.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, vp, vp]
     lib.qaff_qmm_nt.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp, vp]
+    lib.qaff_qmm_nt_static.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+    lib.qaff_qmm_nt_static_max_bytes.argtypes = []
+    lib.qaff_qmm_nt_static_max_bytes.restype = ctypes.c_size_t
     lib.qaff_qmm_nt_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.qaff_qmm_nt_workspace_size.restype = ctypes.c_size_t
     lib.qaff_qmm_ws.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp, vp]
@@ -71,7 +75,7 @@ def load() -> ctypes.CDLL:
     lib.qaff_gather_qmm_ex.argtypes = gather + [ctypes.c_int]
     for f in (lib.qaff_dequantize, lib.qaff_qmm, lib.qaff_qmm_ex, lib.qaff_dequant_rows,
               lib.qaff_gemv_gate_up, lib.qaff_gemv_silu_gate, lib.qaff_gather_qmm, lib.qaff_gather_qmm_ex,
-              lib.qaff_quantize, lib.qaff_qmm_nt, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
+              lib.qaff_quantize, lib.qaff_qmm_nt, lib.qaff_qmm_nt_static, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
         f.restype = ctypes.c_int
     lib.qaff_last_error.restype = ctypes.c_char_p
     lib.qaff_last_error.argtypes = []

@@ -449,10 +449,14 @@ size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits)
     return qaff::qmm_nt_workspace_bytes(m, k, n, bits);
 }
 
-qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                        const uint16_t* biases, int64_t k, int64_t n, int32_t group_size, int32_t bits,
-                        void* workspace, size_t workspace_bytes, void* y, hipStream_t stream) {
-    static const char* op = "qaff_qmm_nt";
+namespace {
+
+// qaff_qmm_nt with the workspace given (ws) or, for qaff_qmm_nt_static (ws null), the library's
+// static scratch array of the current device.
+qaff_status qmm_nt_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                        const uint16_t* scales, const uint16_t* biases, int64_t k, int64_t n, int32_t group_size,
+                        int32_t bits, void* workspace, size_t workspace_bytes, bool use_static, void* y,
+                        hipStream_t stream) {
     g_error.clear();
     // the weight is [k, n]: k rows of n codes
     qaff_status st = check_weight(op, packed, scales, biases, k, n, group_size, bits);
@@ -473,13 +477,40 @@ qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint
     qaff::qmm_nt_plan(k, n, bits, &kchunk, &chunks);
     if (chunks > 65535) return fail(QAFF_ERR_UNSUPPORTED, "%s: k = %lld is too large", op, (long long)k);
     const size_t need = qaff::qmm_nt_workspace_bytes(m, k, n, bits);
-    if (!workspace || workspace_bytes < need)
-        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: the workspace needs %zu bytes (qaff_qmm_nt_workspace_size), got %zu",
-                    op, need, workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", op);
+    if (use_static) {
+        if (need > qaff::kQmmNtStaticScratchBytes)
+            return fail(QAFF_ERR_UNSUPPORTED, "%s: these sizes need %zu bytes of partial sums, more than the static "
+                        "scratch of %zu bytes (qaff_qmm_nt_static_max_bytes); use qaff_qmm_nt with a workspace",
+                        op, need, qaff::kQmmNtStaticScratchBytes);
+        const hipError_t e = qaff::qmm_nt_static_scratch(&workspace);
+        if (e != hipSuccess) return fail(QAFF_ERR_DEVICE, "%s: static scratch: %s", op, hipGetErrorString(e));
+    } else {
+        if (!workspace || workspace_bytes < need)
+            return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: the workspace needs %zu bytes (qaff_qmm_nt_workspace_size), got %zu",
+                        op, need, workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", op);
+    }
     return after_launch(op, qaff::launch_qmm_nt(x, x_dtype == QAFF_F32, m, packed, scales, biases, k, n, group_size,
                                                 bits, workspace, y, stream), stream);
 }
+
+}  // namespace
+
+qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                        const uint16_t* biases, int64_t k, int64_t n, int32_t group_size, int32_t bits,
+                        void* workspace, size_t workspace_bytes, void* y, hipStream_t stream) {
+    return qmm_nt_impl("qaff_qmm_nt", x, x_dtype, m, packed, scales, biases, k, n, group_size, bits, workspace,
+                       workspace_bytes, false, y, stream);
+}
+
+qaff_status qaff_qmm_nt_static(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                               const uint16_t* scales, const uint16_t* biases, int64_t k, int64_t n,
+                               int32_t group_size, int32_t bits, void* y, hipStream_t stream) {
+    return qmm_nt_impl("qaff_qmm_nt_static", x, x_dtype, m, packed, scales, biases, k, n, group_size, bits, nullptr,
+                       0, true, y, stream);
+}
+
+size_t qaff_qmm_nt_static_max_bytes(void) { return qaff::kQmmNtStaticScratchBytes; }
 
 qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
                           int32_t bits, uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {

@@ -102,6 +102,11 @@ hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* p
                          const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
                          void* y, hipStream_t stream);
 
+// The device address of the static scratch array that stands in for qmm_nt's workspace
+// (kQmmNtStaticScratchBytes on every device), resolved once per device with it current.
+constexpr size_t kQmmNtStaticScratchBytes = (size_t)8 << 20;
+hipError_t qmm_nt_static_scratch(void** ptr);
+
 // Other float types (dtype codes 0 float32, 1 bf16, 2 float16) for scales, biases, x and outputs.
 hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
                                 int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,

@@ -20,8 +20,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+#include <vector>
+
 namespace qaff {
 namespace {
+
+// The float32 partial sums of qaff_qmm_nt_static (for callers that cannot allocate): one array per
+// device, held until the process ends. Host code never names it after set-up; it uses the device
+// address that hipGetSymbolAddress returns for the current device (qmm_nt_static_scratch).
+static __device__ __align__(256) uint8_t scratch[kQmmNtStaticScratchBytes];
 
 constexpr int kNtThreads = 256;
 constexpr int kNtCols = 16;    // column blocks per thread block
@@ -196,6 +204,25 @@ hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* pac
 }
 
 }  // namespace
+
+hipError_t qmm_nt_static_scratch(void** ptr) {
+    static std::mutex mu;
+    static std::vector<void*> addr;  // per device; null until resolved
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current: its own copy
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,

@@ -319,3 +319,16 @@ def test_typed_checks(lib):
     assert q_t(x=A2) == INVALID
     # the old entry points keep their types: float16 is not one of them
     assert lib.qaff_qmm(A16, F16, 1, A16, A16, A16, 4, 64, 32, 4, A16, NULL) == INVALID
+
+
+def test_qmm_nt_static_rejects_on_the_host(lib):
+    # past the static scratch (8 MiB of partial sums): UNSUPPORTED, before any device call
+    assert lib.qaff_qmm_nt_static_max_bytes() == 8 << 20
+    m, k, n = 2, 128 * 300, 4096
+    assert lib.qaff_qmm_nt_workspace_size(m, k, n, 4) > lib.qaff_qmm_nt_static_max_bytes()
+    assert lib.qaff_qmm_nt_static(A16, BF16, m, A16, A16, A16, k, n, 64, 4, A16, NULL) == UNSUPPORTED
+    assert b"static scratch" in lib.qaff_last_error()
+    # the workspace entry point's own checks apply
+    assert lib.qaff_qmm_nt_static(A16, BF16, 1, A16, A16, A16, 64, 48, 32, 4, A16, NULL) == INVALID  # n % G
+    assert lib.qaff_qmm_nt_static(A16, BF16, 1, A16, A16, A16, 64, 64, 32, 7, A16, NULL) == UNSUPPORTED
+    assert lib.qaff_qmm_nt_static(A16, BF16, 0, A16, A16, A16, 64, 64, 32, 4, A16, NULL) == OK      # m = 0
