@@ -430,7 +430,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_big_kernel(
 //    offset fall on distinct banks. X is loaded two steps ahead, W three steps ahead.
 //  * Scales and biases come in windows of 8 groups (16 bytes per row and array), one window ahead.
 // Against dequantizing W tiles into LDS this halves the VALU work per flop and removes the W tile's
-// LDS stores and reads; two waves per SIMD still hide the latencies.
+// LDS stores and reads; two waves per SIMD still hide the latencies. 4- and 8-bit codes enter the
+// multiply-add as float16 mantissas (dequant8m): at the prefill shape 234 -> 225 us sustained.
+// (A 256 x 128 tile with one wave per SIMD, which dequantizes each W element for 256 rows of X,
+// measured 257-263 us: at the power limit its clock rose to 2.15-2.28 GHz, but the matrix cores
+// idled more, and it moves half again as many bytes per flop from L2.)
 // Requirements (checked by the launcher): K a multiple of 64 * kDirectBody (so of 8 groups);
 // scales and biases 16-byte aligned. Rows of X beyond m and rows of W beyond n are clamped, not
 // zeroed: they only reach outputs that are not stored.
@@ -580,15 +584,14 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
                 bw = sbc[1][gi >> 1];
                 sh = 16u * (uint32_t)(gi & 1);
             }
-            const float s = __uint_as_float((sw >> sh) << 16);
-            const float b = __uint_as_float((bw >> sh) << 16);
+            const Dq dq = make_dq(__uint_as_float((sw >> sh) << 16), __uint_as_float((bw >> sh) << 16));
             const uint16_t* L = xl[u & 1];
             bf16x8 a[2][4];
             read_a(L, 0, a[0]);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 if (kk < 3) read_a(L, kk + 1, a[(kk + 1) & 1]);
-                const bf16x8 bw8 = dequant8<BITS>(wr[u & 3], kk, s, b);
+                const bf16x8 bw8 = dequant8m<BITS>(wr[u & 3], kk, dq);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], bw8, acc[i], 0, 0, 0);

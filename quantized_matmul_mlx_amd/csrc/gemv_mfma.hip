@@ -6,7 +6,8 @@
 // On the VALU the work per code grows with m (one multiply per code and x row, and the x values
 // through LDS), so from a few rows on the VALU, not HBM, sets the time. Here
 // v_mfma_f32_16x16x32_bf16 takes all (up to 16) x rows at once, and the VALU work per code is
-// the dequantization alone: w = fma(s, c, b) rounded to bf16, as in the prefill GEMM.
+// the dequantization alone: w = s c + b rounded to bf16, as in the prefill GEMM (dequant8m: 4- and
+// 8-bit codes enter a mixed-precision multiply-add as float16 mantissas).
 //
 // Layout of the work:
 //  * A block of `kb / 16` waves owns 16 * NT rows of W (NT tiles of 16 rows) and all of K; wave w
@@ -156,10 +157,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
         bf16x8 wb[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const float sc = sw[t].get(c, lg, g_hi);
-            const float bi = bw[t].get(c, lg, g_hi);
+            const Dq dq = make_dq(sw[t].get(c, lg, g_hi), bw[t].get(c, lg, g_hi));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
+            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8m<BITS>(wq[t][c], j, dq);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -435,10 +435,9 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
             bf16x8 wb[NT][4];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const float sc = sw[t].get(c, lg, g_hi);
-                const float bi = bw[t].get(c, lg, g_hi);
+                const Dq dq = make_dq(sw[t].get(c, lg, g_hi), bw[t].get(c, lg, g_hi));
 #pragma unroll
-                for (int j = 0; j < 4; ++j) wb[t][j] = dequant8<BITS>(wq[t][c], j, sc, bi);
+                for (int j = 0; j < 4; ++j) wb[t][j] = dequant8m<BITS>(wq[t][c], j, dq);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {

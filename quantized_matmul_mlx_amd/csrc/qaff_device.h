@@ -117,6 +117,58 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t o
     return r;
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Per-group constants of dequant8m: the scale, the scale / 16, and the bias less 1024 and 64 scales.
+struct Dq {
+    float s, s16, b, b1024, b64;
+};
+__device__ __forceinline__ Dq make_dq(float s, float b) {
+    return Dq{s, s * 0.0625f, b, __builtin_fmaf(-1024.0f, s, b), __builtin_fmaf(-64.0f, s, b)};
+}
+
+// Codes 8 j .. 8 j + 7 of a 32-code block as bf16 MFMA operands, like dequant8, for the GEMM and
+// the matrix-core decode kernel. For 4- and 8-bit codes each code becomes a float16 value without a
+// conversion: one AND-OR puts two codes (or two codes times 16) into the mantissas of
+// 1024.0 (0x6400), and a mixed-precision fused multiply-add (v_fma_mix_f32, which widens the
+// float16 half exactly) forms s (1024 + c) + (b - 1024 s) = s c + b, or (s / 16)(1024 + 16 c) +
+// (b - 64 s). Wherever b - 1024 s (b - 64 s) is exact in float32 -- a scale and a bias within 2^15
+// of each other in magnitude -- that is s c + b rounded once, exactly dequant8's value; otherwise it
+// differs from it by at most one float32 rounding before the bf16 one. 4-bit: 17 instructions per
+// 8 codes against 23.
+template <int BITS>
+__device__ __forceinline__ bf16x8 dequant8m(const uint32_t (&w)[BITS], int j, const Dq& p) {
+    if constexpr (BITS == 4) {
+        constexpr uint32_t kOne = 0x64006400u;  // float16 1024.0 in both halves
+        const uint32_t v = w[j];
+        const uint32_t v8 = v >> 8;
+        const f16x2 h0 = __builtin_bit_cast(f16x2, and_or(v, 0x000F000Fu, kOne));   // codes 0, 4
+        const f16x2 h1 = __builtin_bit_cast(f16x2, and_or(v, 0x00F000F0u, kOne));   // 16 x codes 1, 5
+        const f16x2 h2 = __builtin_bit_cast(f16x2, and_or(v8, 0x000F000Fu, kOne));  // codes 2, 6
+        const f16x2 h3 = __builtin_bit_cast(f16x2, and_or(v8, 0x00F000F0u, kOne));  // 16 x codes 3, 7
+        const float c0 = __builtin_fmaf(p.s, (float)h0.x, p.b1024), c4 = __builtin_fmaf(p.s, (float)h0.y, p.b1024);
+        const float c1 = __builtin_fmaf(p.s16, (float)h1.x, p.b64), c5 = __builtin_fmaf(p.s16, (float)h1.y, p.b64);
+        const float c2 = __builtin_fmaf(p.s, (float)h2.x, p.b1024), c6 = __builtin_fmaf(p.s, (float)h2.y, p.b1024);
+        const float c3 = __builtin_fmaf(p.s16, (float)h3.x, p.b64), c7 = __builtin_fmaf(p.s16, (float)h3.y, p.b64);
+        return __builtin_bit_cast(bf16x8, u32x4a{pack_bf16x2(c0, c1), pack_bf16x2(c2, c3), pack_bf16x2(c4, c5),
+                                                 pack_bf16x2(c6, c7)});
+    } else if constexpr (BITS == 8) {
+        constexpr uint32_t kOne = 0x64006400u;
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t v = w[2 * j + q];
+            const f16x2 ha = __builtin_bit_cast(f16x2, and_or(v, 0x00FF00FFu, kOne));       // bytes 0, 2
+            const f16x2 hb = __builtin_bit_cast(f16x2, and_or(v >> 8, 0x00FF00FFu, kOne));  // bytes 1, 3
+            o[2 * q] = pack_bf16x2(__builtin_fmaf(p.s, (float)ha.x, p.b1024), __builtin_fmaf(p.s, (float)hb.x, p.b1024));
+            o[2 * q + 1] = pack_bf16x2(__builtin_fmaf(p.s, (float)ha.y, p.b1024), __builtin_fmaf(p.s, (float)hb.y, p.b1024));
+        }
+        return __builtin_bit_cast(bf16x8, u32x4a{o[0], o[1], o[2], o[3]});
+    } else {
+        return dequant8<BITS>(w, j, p.s, p.b);
+    }
+}
+
 // Full-wave sum of a float (64 lanes), result in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
