@@ -19,7 +19,13 @@
  *     consumer owns the device pointers).
  *   - bits must be 1, 2, 3, 4, 5, 6 or 8 (else QAFF_ERR_UNSUPPORTED); group_size 32, 64 or 128
  *     (nuvec_core check_params); cols (k) must be a multiple of group_size.
- *   - Alignment: packed 4 bytes, scales/biases 2 bytes, indices 4 bytes; x, y and out 16 bytes.
+ *   - Alignment: packed 4 bytes, scales/biases their element size (2 bytes; 4 for float32), indices
+ *     4 bytes; x, y, out, w, gate, up and resid their element size (4 bytes for float32, 2 for bf16
+ *     and float16). 16-byte aligned x, y and out take the vector kernels; others (a row slice, an
+ *     odd offset into a buffer) are loaded and stored element by element: dequantize, dequant_rows
+ *     and quantize give the same bits, the products the same float32 arithmetic in another
+ *     summation order (within the same bounds). The MFMA paths, when forced (QAFF_PATH_GEMM,
+ *     QAFF_PATH_GEMV_MFMA), need 16-byte aligned x and y and are UNSUPPORTED otherwise.
  *   - Every argument is checked on the host before any launch, so a rejected call writes nothing.
  *   - Calls are asynchronous on `stream` (NULL = the null stream): they return once the kernel is
  *     enqueued and never synchronize (unless the environment sets QAFF_DEBUG_SYNC=1).
@@ -121,7 +127,7 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
  *   w [rows, cols] in w_dtype (float32 or bf16); packed uint32 [rows, cols*bits/32]; scales and
  *   biases bf16 [rows, cols/group_size]. All caller-owned device buffers.
  * Errors: as qaff_dequantize (the outputs are checked as a weight), plus INVALID_ARGUMENT for a
- * null or misaligned (16-byte) w where the size is non-zero.
+ * null w, or one not aligned to its element size, where the size is non-zero.
  */
 qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols,
                           int32_t group_size, int32_t bits, uint32_t* packed, uint16_t* scales,
@@ -223,7 +229,7 @@ size_t qaff_qmm_nt_static_max_bytes(void);
  * and bits. x bf16 [m, k] with 1 <= m <= 16; gate_y, up_y bf16 [m, n]; sums in float32, each output
  * rounded to nearest even. k == 0 writes zeros.
  * Errors: as qaff_qmm for each weight; UNSUPPORTED for m > 16; INVALID_ARGUMENT for a null or
- * misaligned (16-byte) x or output.
+ * misaligned (2-byte) x or output.
  */
 qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_packed,
                               const uint16_t* gate_scales, const uint16_t* gate_biases,
@@ -240,7 +246,7 @@ qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_pac
  *   gate, up bf16 [m, k] with 1 <= m <= 16; resid bf16 [m, n] or NULL; y bf16 [m, n].
  * k == 0 writes resid (or zeros).
  * Errors: as qaff_qmm for the weight; UNSUPPORTED for m > 16; INVALID_ARGUMENT for a null or
- * misaligned (16-byte) gate, up or y, or a resid that is not 2-byte aligned.
+ * misaligned (2-byte) gate, up or y, or a resid that is not 2-byte aligned.
  */
 qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, const uint32_t* packed,
                                 const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqaff.so")
 BENCH_LIB = os.path.join(PKG, "libqaff_bench.so")
 
-SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip", "typed.hip"]
+SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip", "typed.hip",
+           "unaligned.hip"]
 BENCH_SOURCES = ["bench_aux.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

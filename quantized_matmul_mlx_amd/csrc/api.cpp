@@ -53,6 +53,10 @@ qaff_status after_launch(const char* op, hipError_t e, hipStream_t stream) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Bytes of one element of a dtype (x, y and outputs need this much alignment; 16-byte aligned ones
+// take the vector kernels, the others the element-by-element ones).
+uintptr_t esize_of(qaff_dtype d) { return d == QAFF_F32 ? 4 : 2; }
+
 // Checks shared by every entry point: bits, group size, cols and the weight pointers.
 qaff_status check_weight(const char* op, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t rows, int64_t cols, int32_t group_size,
@@ -97,11 +101,16 @@ qaff_status dequant_common(const char* op, const uint32_t* packed, const uint16_
             return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null weight pointer", op);
     }
     if (!out) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
-    if (!aligned(out, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be 16-byte aligned", op);
+    if (!aligned(out, esize_of(out_dtype)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be aligned to its element size", op);
     if (out_rows * (cols / 32) >= (1LL << 31))
         return fail(QAFF_ERR_UNSUPPORTED, "%s: output of %lld x %lld is too large", op, (long long)out_rows, (long long)cols);
-    hipError_t e = qaff::launch_dequant(packed, scales, biases, gather ? indices : nullptr, table_rows,
-                                        out_rows, cols, group_size, bits, out, out_dtype == QAFF_BF16, stream);
+    // an output that is not 16-byte aligned is stored element by element (the same values)
+    hipError_t e = aligned(out, 16)
+        ? qaff::launch_dequant(packed, scales, biases, gather ? indices : nullptr, table_rows, out_rows, cols,
+                               group_size, bits, out, out_dtype == QAFF_BF16, stream)
+        : qaff::launch_dequant_typed(packed, scales, biases, (int)QAFF_BF16, out_rows, cols, group_size, bits, out,
+                                     (int)out_dtype, stream, gather ? indices : nullptr, table_rows);
     return after_launch(op, e, stream);
 }
 
@@ -175,13 +184,21 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
         return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes 1 <= m <= 16, k a multiple "
                     "of 512 up to 4096 and 4-byte aligned scales and biases", op);
     if (m == 0 || n == 0) return QAFF_OK;
+    const int64_t esize = (int64_t)esize_of(x_dtype);
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
-    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (!aligned(y, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
     if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * esize, stream), stream);
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (!aligned(x, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
     if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    if (!aligned(x, 16) || !aligned(y, 16)) {
+        // x or y not 16-byte aligned: the element-by-element GEMV (any m)
+        if (path == QAFF_PATH_GEMM || path == QAFF_PATH_GEMV_MFMA)
+            return fail(QAFF_ERR_UNSUPPORTED, "%s: the MFMA paths need 16-byte aligned x and y", op);
+        return after_launch(op, qaff::launch_gemv_scalar(x, (int)x_dtype, m, packed, scales, biases, (int)QAFF_BF16, n,
+                                                         k, group_size, bits, y, (int)x_dtype, qaff::ScalarGemv{},
+                                                         stream), stream);
+    }
 
     bool use_gemm = false, use_mfma = false;
     if (x_dtype == QAFF_BF16) {
@@ -256,16 +273,27 @@ qaff_status qaff_gemv_gate_up(const void* x, int64_t m, const uint32_t* gate_pac
     if (m > kGemvMaxM) return fail(QAFF_ERR_UNSUPPORTED, "%s: a decode product: m <= %d", op, kGemvMaxM);
     if (m == 0 || n == 0) return QAFF_OK;
     if (!gate_y || !up_y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
-    if (!aligned(gate_y, 16) || !aligned(up_y, 16))
-        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: outputs must be 16-byte aligned", op);
+    if (!aligned(gate_y, 2) || !aligned(up_y, 2))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: outputs must be 2-byte aligned", op);
     if (k == 0) {
         hipError_t e = qaff::launch_fill_zero(gate_y, m * n * 2, stream);
         if (e == hipSuccess) e = qaff::launch_fill_zero(up_y, m * n * 2, stream);
         return after_launch(op, e, stream);
     }
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (!aligned(x, 2)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 2-byte aligned", op);
     if (n > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: n above 2^31-1", op);
+    if (!aligned(x, 16) || !aligned(gate_y, 16) || !aligned(up_y, 16)) {
+        // element by element: the two products one after the other
+        const qaff::ScalarGemv none{};
+        hipError_t e = qaff::launch_gemv_scalar(x, (int)QAFF_BF16, m, gate_packed, gate_scales, gate_biases,
+                                                (int)QAFF_BF16, n, k, group_size, bits, gate_y, (int)QAFF_BF16, none,
+                                                stream);
+        if (e == hipSuccess)
+            e = qaff::launch_gemv_scalar(x, (int)QAFF_BF16, m, up_packed, up_scales, up_biases, (int)QAFF_BF16, n, k,
+                                         group_size, bits, up_y, (int)QAFF_BF16, none, stream);
+        return after_launch(op, e, stream);
+    }
     qaff::GemvFused f{};
     f.packed2 = up_packed;
     f.scales2 = up_scales;
@@ -288,16 +316,24 @@ qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, con
     if (m > kGemvMaxM) return fail(QAFF_ERR_UNSUPPORTED, "%s: a decode product: m <= %d", op, kGemvMaxM);
     if (m == 0 || n == 0) return QAFF_OK;
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
+    if (!aligned(y, 2)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 2-byte aligned", op);
     if (resid && !aligned(resid, 2)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: resid must be 2-byte aligned", op);
     if (k == 0) {  // y = bf16(0 + resid) = resid, or zeros
         if (resid) return after_launch(op, hipMemcpyAsync(y, resid, (size_t)(m * n * 2), hipMemcpyDeviceToDevice, stream), stream);
         return after_launch(op, qaff::launch_fill_zero(y, m * n * 2, stream), stream);
     }
     if (!gate || !up) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null gate or up", op);
-    if (!aligned(gate, 16) || !aligned(up, 16))
-        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: gate and up must be 16-byte aligned", op);
+    if (!aligned(gate, 2) || !aligned(up, 2))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: gate and up must be 2-byte aligned", op);
     if (n > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: n above 2^31-1", op);
+    if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(y, 16)) {
+        qaff::ScalarGemv opt{};
+        opt.up = static_cast<const uint16_t*>(up);
+        opt.resid = static_cast<const uint16_t*>(resid);
+        return after_launch(op, qaff::launch_gemv_scalar(gate, (int)QAFF_BF16, m, packed, scales, biases,
+                                                         (int)QAFF_BF16, n, k, group_size, bits, y, (int)QAFF_BF16, opt,
+                                                         stream), stream);
+    }
     qaff::GemvFused f{};
     f.up = static_cast<const uint16_t*>(up);
     f.resid = static_cast<const uint16_t*>(resid);
@@ -338,13 +374,16 @@ qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batc
         return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes a bf16 x, k a multiple of 512 "
                     "up to 4096 and 4-byte aligned scales and biases", op);
     if (batch == 0 || m == 0 || n == 0) return QAFF_OK;
+    const int64_t esize = (int64_t)esize_of(x_dtype);
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
-    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (!aligned(y, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
     if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
     if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, batch * m * n * esize, stream), stream);
     if (x_batches > 0 && !x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (x && !aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (x && !aligned(x, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
+    const bool vec = (!x || aligned(x, 16)) && aligned(y, 16);
+    if (!vec && path == QAFF_PATH_GEMV_MFMA)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel needs 16-byte aligned x and y", op);
 
     qaff::Gather g{};
     g.lhs = lhs_indices;
@@ -368,7 +407,13 @@ qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batc
         use_mfma = g.grouped || m >= kGemvMfmaMinM;
     }
     hipError_t e;
-    if (use_mfma)
+    if (!vec) {
+        qaff::ScalarGemv opt{};
+        opt.gather = true;
+        opt.g = g;
+        e = qaff::launch_gemv_scalar(x, (int)x_dtype, m, packed, scales, biases, (int)QAFF_BF16, n, k, group_size, bits,
+                                     y, (int)x_dtype, opt, stream);
+    } else if (use_mfma)
         e = qaff::launch_gemv_mfma_gather(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
                                           bits, static_cast<uint16_t*>(y), g, stream);
     else
@@ -406,7 +451,8 @@ qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, co
     if (sb_dtype == QAFF_F32 && (!aligned(scales, 4) || !aligned(biases, 4)))
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
     if (!out) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null output", op);
-    if (!aligned(out, 4)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be 4-byte aligned", op);
+    if (!aligned(out, esize_of(out_dtype)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: output must be aligned to its element size", op);
     return after_launch(op, qaff::launch_dequant_typed(packed, scales, biases, (int)sb_dtype, rows, cols, group_size,
                                                        bits, out, (int)out_dtype, stream), stream);
 }
@@ -428,13 +474,18 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
     if (m == 0 || n == 0) return QAFF_OK;
     if (sb_dtype == QAFF_F32 && k > 0 && (!aligned(scales, 4) || !aligned(biases, 4)))
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
-    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
     const qaff_dtype yt = qaff_promote_dtype(x_dtype, sb_dtype);
-    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * (yt == QAFF_F32 ? 4 : 2), stream), stream);
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, esize_of(yt))) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * (int64_t)esize_of(yt), stream), stream);
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (!aligned(x, esize_of(x_dtype)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
     if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    if (!aligned(x, 16) || !aligned(y, 16))
+        return after_launch(op, qaff::launch_gemv_scalar(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
+                                                         group_size, bits, y, (int)yt, qaff::ScalarGemv{}, stream),
+                            stream);
     if (x_dtype == QAFF_F16 && sb_dtype == QAFF_F16)
         return after_launch(op, qaff::launch_gemv_f16(static_cast<const uint16_t*>(x), m, packed,
                                                       static_cast<const uint16_t*>(scales),
@@ -464,12 +515,13 @@ qaff_status qmm_nt_impl(const char* op, const void* x, qaff_dtype x_dtype, int64
     if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
     if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
     if (m == 0 || n == 0) return QAFF_OK;
+    // the kernels load x and store y one element at a time: element alignment is enough
+    const int64_t esize = (int64_t)esize_of(x_dtype);
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be 16-byte aligned", op);
-    const int64_t esize = x_dtype == QAFF_F32 ? 4 : 2;
+    if (!aligned(y, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
     if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * esize, stream), stream);
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (!aligned(x, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be 16-byte aligned", op);
+    if (!aligned(x, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
     if (m * n >= (1LL << 31) || k > 0x7fffffffLL || n > 0x7fffffffLL)
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld outputs or k = %lld is too large", op, (long long)m,
                     (long long)n, (long long)k);
@@ -522,7 +574,7 @@ qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64
     if (!valid_dtype(w_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown w dtype %d", op, (int)w_dtype);
     if (rows == 0 || cols == 0) return QAFF_OK;
     if (!w) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null w", op);
-    if (!aligned(w, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: w must be 16-byte aligned", op);
+    if (!aligned(w, esize_of(w_dtype))) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: w must be aligned to its element size", op);
     if (rows * (cols / 32) >= (1LL << 37))
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld is too large", op, (long long)rows, (long long)cols);
     return after_launch(op, qaff::launch_quantize(w, w_dtype == QAFF_BF16, rows, cols, group_size, bits, packed,

@@ -263,13 +263,9 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// silu(v) = v / (1 + exp(-v)) in float32 from the hardware exp2 and reciprocal (each within a few
+// silu (silu_f32 in qaff_device.h: float32 from the hardware exp2 and reciprocal, each within a few
 // ulp): h is rounded to bf16 right after, which an error of that size moves only in rare ties.
 // Every block of the GEMV recomputes the activation for its x, so its cost counts.
-__device__ __forceinline__ float silu_f32(float v) {
-    const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);  // exp(-v)
-    return v * __builtin_amdgcn_rcpf(1.0f + e);
-}
 
 // FUSED adds the decode fusions of `GemvFused` (uniform flags read at run time): the x transform,
 // the residual, and a second weight whose rows follow the first's (rows n .. 2n - 1).

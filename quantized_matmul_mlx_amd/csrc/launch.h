@@ -90,6 +90,7 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 // packed/scales/biases of a dense [rows, cols] weight (float32 or bf16): bias = group min,
 // scale = (max - min) / (2^bits - 1), both bf16; code = round((w - bias) / scale), clamped.
+// w 16-byte aligned: 16-byte loads; otherwise element by element.
 hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t cols, int group_size, int bits,
                            uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream);
 
@@ -108,12 +109,31 @@ constexpr size_t kQmmNtStaticScratchBytes = (size_t)8 << 20;
 hipError_t qmm_nt_static_scratch(void** ptr);
 
 // Other float types (dtype codes 0 float32, 1 bf16, 2 float16) for scales, biases, x and outputs.
+// The dequantization stores element by element (out needs only its element size of alignment); with
+// `indices`, output row r is table row indices[r] (an index >= table_rows gives a NaN row).
 hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
                                 int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,
-                                hipStream_t stream);
+                                hipStream_t stream, const uint32_t* indices = nullptr, int64_t table_rows = 0);
 hipError_t launch_gemv_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
                              const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits, void* y,
                              int y_dtype, hipStream_t stream);
+
+// The element-by-element GEMV behind operands that are not 16-byte aligned: y = x . dequantize(W)^T
+// with x, scales, biases and y of the given dtype codes, each loaded and stored one element at a time
+// (every operand needs only its element size of alignment), float32 sums. Options:
+//  * up: x is the gate and the product's input is bf16(silu(x) * up) (bf16 x and up);
+//  * resid: y = bf16(sum + resid) (bf16 y);
+//  * gather: output batch b is x[lhs[b]] . dequantize(W[rhs[b]])^T (NaN batch for an index out of
+//    range).
+struct ScalarGemv {
+    const uint16_t* up = nullptr;
+    const uint16_t* resid = nullptr;
+    bool gather = false;
+    Gather g{};
+};
+hipError_t launch_gemv_scalar(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                              const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits,
+                              void* y, int y_dtype, const ScalarGemv& opt, hipStream_t stream);
 
 // Writes `bytes` zero bytes (bytes % 2 == 0, p 2-byte aligned) with a kernel, so that the call
 // also behaves under stream capture.

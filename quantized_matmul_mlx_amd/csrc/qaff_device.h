@@ -7,6 +7,7 @@
 // bias. The kernels all work block by block.
 #pragma once
 
+#include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -167,6 +168,27 @@ __device__ __forceinline__ bf16x8 dequant8m(const uint32_t (&w)[BITS], int j, co
     } else {
         return dequant8<BITS>(w, j, p.s, p.b);
     }
+}
+
+// Element i of an array of dtype code `dtype` (0 float32, 1 bf16, 2 float16), widened to float32
+// (exactly), and the store of a float32 into such an array (round to nearest even). One element
+// per access: the array needs only its element size of alignment.
+__device__ __forceinline__ float load_as_f32(const void* p, size_t i, int dtype) {
+    if (dtype == 1) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    if (dtype == 2) return __half2float(__ushort_as_half(static_cast<const uint16_t*>(p)[i]));
+    return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void store_from_f32(void* p, size_t i, int dtype, float v) {
+    if (dtype == 1) static_cast<uint16_t*>(p)[i] = to_bf16_bits(v);
+    else if (dtype == 2) static_cast<uint16_t*>(p)[i] = __half_as_ushort(__float2half_rn(v));
+    else static_cast<float*>(p)[i] = v;
+}
+
+// silu(v) = v / (1 + e^-v) from the hardware exp2 and reciprocal (a few ulp in float32).
+__device__ __forceinline__ float silu_f32(float v) {
+    const float e = __builtin_amdgcn_exp2f(-v * 1.4426950408889634f);  // exp(-v)
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Full-wave sum of a float (64 lanes), result in every lane.

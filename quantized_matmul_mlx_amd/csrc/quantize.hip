@@ -41,7 +41,8 @@ __device__ __forceinline__ void group_min_max(float& lo, float& hi, int lane) {
     }
 }
 
-template <int BITS, int GSHIFT, bool IN_BF16>
+// VEC: w is 16-byte aligned and read in 16-byte loads; otherwise one element at a time.
+template <int BITS, int GSHIFT, bool IN_BF16, bool VEC>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, uint64_t blocks,
                                                                  uint32_t* packed, uint16_t* scales,
                                                                  uint16_t* biases) {
@@ -53,7 +54,12 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     const uint64_t src = live ? idx : 0;
 
     float v[32];
-    if constexpr (IN_BF16) {
+    if constexpr (!VEC) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            v[j] = IN_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(w)[src * 32 + j])
+                           : static_cast<const float*>(w)[src * 32 + j];
+    } else if constexpr (IN_BF16) {
         const u32x4a* p = reinterpret_cast<const u32x4a*>(static_cast<const uint16_t*>(w) + src * 32);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -138,15 +144,23 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     }
 }
 
-template <int BITS, int GSHIFT>
-hipError_t launch_g(const void* w, bool in_bf16, uint64_t blocks, uint32_t* packed, uint16_t* scales,
+template <int BITS, int GSHIFT, bool VEC>
+hipError_t launch_v(const void* w, bool in_bf16, uint64_t blocks, uint32_t* packed, uint16_t* scales,
                     uint16_t* biases, hipStream_t stream) {
     const unsigned grid = (unsigned)((blocks + kQuantThreads - 1) / kQuantThreads);
     if (in_bf16)
-        quantize_kernel<BITS, GSHIFT, true><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
+        quantize_kernel<BITS, GSHIFT, true, VEC><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
     else
-        quantize_kernel<BITS, GSHIFT, false><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
+        quantize_kernel<BITS, GSHIFT, false, VEC><<<grid, kQuantThreads, 0, stream>>>(w, blocks, packed, scales, biases);
     return hipGetLastError();
+}
+
+template <int BITS, int GSHIFT>
+hipError_t launch_g(const void* w, bool in_bf16, uint64_t blocks, uint32_t* packed, uint16_t* scales,
+                    uint16_t* biases, hipStream_t stream) {
+    if (reinterpret_cast<uintptr_t>(w) % 16 == 0)
+        return launch_v<BITS, GSHIFT, true>(w, in_bf16, blocks, packed, scales, biases, stream);
+    return launch_v<BITS, GSHIFT, false>(w, in_bf16, blocks, packed, scales, biases, stream);
 }
 
 template <int BITS>

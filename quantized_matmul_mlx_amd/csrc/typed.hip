@@ -18,33 +18,28 @@ namespace {
 
 constexpr int kTypedThreads = 256;
 
-// dtype codes: 0 float32, 1 bfloat16, 2 float16
-__device__ __forceinline__ float load_as_f32(const void* p, size_t i, int dtype) {
-    if (dtype == 1) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-    if (dtype == 2) return __half2float(__ushort_as_half(static_cast<const uint16_t*>(p)[i]));
-    return static_cast<const float*>(p)[i];
-}
-
-__device__ __forceinline__ void store_from_f32(void* p, size_t i, int dtype, float v) {
-    if (dtype == 1) static_cast<uint16_t*>(p)[i] = to_bf16_bits(v);
-    else if (dtype == 2) static_cast<uint16_t*>(p)[i] = __half_as_ushort(__float2half_rn(v));
-    else static_cast<float*>(p)[i] = v;
-}
-
-// One thread per 32-code block.
+// One thread per 32-code block of the output, stored element by element (so `out` needs only its
+// element size of alignment). With `indices`, output row r is table row indices[r], and an index
+// at or past table_rows gives a row of quiet NaNs.
 template <int BITS>
 __global__ __launch_bounds__(kTypedThreads) void dequant_typed_kernel(
     const uint32_t* packed, const void* scales, const void* biases, int st, uint64_t blocks, uint32_t kb,
-    uint32_t gshift, void* out, int ot) {
+    uint32_t gshift, void* out, int ot, const uint32_t* indices, uint32_t table_rows) {
     // two roundings, product then sum: the compiler must not fuse them (device code contracts by
     // default, and __fmul_rn / __fadd_rn are plain operators)
 #pragma clang fp contract(off)
     const uint64_t idx = (uint64_t)blockIdx.x * kTypedThreads + threadIdx.x;
     if (idx >= blocks) return;
-    const uint64_t row = idx / kb;
-    const uint32_t j = (uint32_t)(idx - row * kb);
+    const uint64_t orow = idx / kb;
+    const uint32_t j = (uint32_t)(idx - orow * kb);
+    const uint64_t row = indices ? (uint64_t)indices[orow] : orow;
+    if (indices && row >= table_rows) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) store_from_f32(out, idx * 32 + c, ot, __uint_as_float(0x7fc00000u));
+        return;
+    }
     uint32_t w[BITS];
-    load_block<BITS>(packed + idx * BITS, w);
+    load_block<BITS>(packed + (row * kb + j) * BITS, w);
     const size_t gi = row * (kb >> gshift) + (j >> gshift);
     const float s = load_as_f32(scales, gi, st);
     const float b = load_as_f32(biases, gi, st);
@@ -152,11 +147,12 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
 
 template <int BITS>
 hipError_t launch_dequant_bits(const uint32_t* packed, const void* scales, const void* biases, int st, int64_t rows,
-                               int64_t kb, uint32_t gshift, void* out, int ot, hipStream_t stream) {
+                               int64_t kb, uint32_t gshift, void* out, int ot, const uint32_t* indices,
+                               int64_t table_rows, hipStream_t stream) {
     const uint64_t blocks = (uint64_t)rows * (uint64_t)kb;
     const unsigned grid = (unsigned)((blocks + kTypedThreads - 1) / kTypedThreads);
     dequant_typed_kernel<BITS><<<grid, kTypedThreads, 0, stream>>>(packed, scales, biases, st, blocks, (uint32_t)kb,
-                                                                   gshift, out, ot);
+                                                                   gshift, out, ot, indices, (uint32_t)table_rows);
     return hipGetLastError();
 }
 
@@ -192,17 +188,17 @@ hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* pa
 
 hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
                                 int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,
-                                hipStream_t stream) {
+                                hipStream_t stream, const uint32_t* indices, int64_t table_rows) {
     const int64_t kb = cols / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
-        case 1: return launch_dequant_bits<1>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 2: return launch_dequant_bits<2>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 3: return launch_dequant_bits<3>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 4: return launch_dequant_bits<4>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 5: return launch_dequant_bits<5>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 6: return launch_dequant_bits<6>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
-        case 8: return launch_dequant_bits<8>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, stream);
+        case 1: return launch_dequant_bits<1>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 2: return launch_dequant_bits<2>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 3: return launch_dequant_bits<3>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 4: return launch_dequant_bits<4>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 5: return launch_dequant_bits<5>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 6: return launch_dequant_bits<6>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
+        case 8: return launch_dequant_bits<8>(packed, scales, biases, sb_dtype, rows, kb, gshift, out, out_dtype, indices, table_rows, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -70,10 +70,12 @@ hipError_t launch_qmm_nt(const void*, bool, int64_t, const uint32_t*, const uint
 static uint8_t fake_scratch[64];
 hipError_t qmm_nt_static_scratch(void** ptr) { *ptr = fake_scratch; return rec("static_scratch"); }
 hipError_t launch_dequant_typed(const uint32_t*, const void*, const void*, int, int64_t, int64_t, int, int, void*, int,
-                                hipStream_t) { return rec("dequant_typed"); }
+                                hipStream_t, const uint32_t*, int64_t) { return rec("dequant_typed"); }
 hipError_t launch_gemv_typed(const void*, int, int64_t, const uint32_t*, const void*, const void*, int, int64_t,
                              int64_t, int, int, void*, int, hipStream_t) { return rec("gemv_typed"); }
 hipError_t launch_fill_zero(void*, int64_t, hipStream_t) { return rec("fill_zero"); }
+hipError_t launch_gemv_scalar(const void*, int, int64_t, const uint32_t*, const void*, const void*, int, int64_t,
+                              int64_t, int, int, void*, int, const ScalarGemv&, hipStream_t) { return rec("gemv_scalar"); }
 }  // namespace qaff
 
 // fake device addresses: never dereferenced
@@ -126,6 +128,20 @@ int main() {
     EXPECT(OK, "", qaff_qmm(A16, QAFF_BF16, 0, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(INV, "", qaff_qmm(A16, QAFF_BF16, -1, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(INV, "", qaff_qmm(nullptr, QAFF_BF16, 2, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
+    // operands that are not 16-byte aligned: the element-by-element kernel, or UNSUPPORTED when forced
+    EXPECT(OK, "gemv_scalar", qaff_qmm(A2, QAFF_BF16, 4, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_qmm(A16, QAFF_BF16, 300, P16, S16, B16, 64, 4096, 64, 4, A2, nullptr));
+    EXPECT(UNS, "", qaff_qmm_ex(A2, QAFF_BF16, 300, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr, QAFF_PATH_GEMM));
+    EXPECT(INV, "", qaff_qmm(A1, QAFF_BF16, 4, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "dequant_typed", qaff_dequantize(P16, S16, B16, 4, 64, 32, 4, A2, QAFF_BF16, nullptr));
+    EXPECT(OK, "dequant_typed", qaff_dequant_rows(P16, S16, B16, 10, 64, 32, 4, I16, 5, A2, QAFF_BF16, nullptr));
+    EXPECT(INV, "", qaff_dequantize(P16, S16, B16, 4, 64, 32, 4, A2, QAFF_F32, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_gemv_gate_up(A2, 1, P16, S16, B16, P16, S16, B16, 64, 4096, 64, 4, A16, A16, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_gemv_silu_gate(A16, A16, 1, P16, S16, B16, 64, 4096, 64, 4, A2, A2, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_gather_qmm(A2, QAFF_BF16, 2, 1, P16, S16, B16, 4, 64, 4096, 64, 4, I16, I16, 3, 0,
+                                              A16, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_qmm_typed(A2, QAFF_F16, 1, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "qmm_nt", qaff_qmm_nt(A2, QAFF_BF16, 2, P16, S16, B16, 4096, 4096, 64, 4, A16, 1 << 20, A2, nullptr));
     // qmm with a workspace: the split GEMM where the size calls for one, a short workspace refused
     const size_t need = qaff_qmm_workspace_size(128, 64, 4096, 64, 4);
     CHECK(need > 0);
@@ -151,7 +167,9 @@ int main() {
     // quantize
     EXPECT(OK, "quantize", qaff_quantize(A16, QAFF_BF16, 4, 128, 64, 4, const_cast<uint32_t*>(P16),
                                          const_cast<uint16_t*>(S16), const_cast<uint16_t*>(B16), nullptr));
-    EXPECT(INV, "", qaff_quantize(A2, QAFF_BF16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), const_cast<uint16_t*>(S16),
+    EXPECT(OK, "quantize", qaff_quantize(A2, QAFF_BF16, 4, 128, 64, 4, const_cast<uint32_t*>(P16),
+                                         const_cast<uint16_t*>(S16), const_cast<uint16_t*>(B16), nullptr));
+    EXPECT(INV, "", qaff_quantize(A1, QAFF_BF16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), const_cast<uint16_t*>(S16),
                                   const_cast<uint16_t*>(B16), nullptr));
     // the product without the transpose, with a workspace and with the static scratch
     const size_t nt = qaff_qmm_nt_workspace_size(2, 4096, 4096, 4);

@@ -138,9 +138,15 @@ def test_null_pointers(lib):
 def test_misaligned_pointers(lib):
     assert dq(lib, packed=A2) == INVALID and b"4-byte" in lib.qaff_last_error()
     assert dq(lib, scales=A1) == INVALID
-    assert dq(lib, out=A4) == INVALID and b"16-byte" in lib.qaff_last_error()
-    assert qmm(lib, x=A4) == INVALID
-    assert qmm(lib, y=A2) == INVALID
+    assert dq(lib, out=A2) == INVALID and b"element size" in lib.qaff_last_error()   # float32 out at 2 bytes
+    assert dq(lib, out=A1, dt=BF16) == INVALID
+    assert qmm(lib, y=A1) == INVALID
+    assert qmm(lib, x=A1) == INVALID
+    assert qmm(lib, xdt=F32, x=A2) == INVALID                 # a float32 x at 2 bytes
+    # an element-aligned x that is not 16-byte aligned takes the element-by-element kernel, which
+    # the MFMA paths do not have
+    assert qmm(lib, x=A2, k=512, path=3) == UNSUPPORTED and b"16-byte" in lib.qaff_last_error()
+    assert qmm(lib, x=A2, m=20, path=2) == UNSUPPORTED
     assert rows(lib, idx=A2) == INVALID
 
 
@@ -200,8 +206,10 @@ def test_fused_decode_checks(lib):
     assert silu(lib, G=48) == INVALID
     assert gate_up(lib, up=NULL) == INVALID                  # the second weight is checked too
     assert gate_up(lib, uy=NULL) == INVALID
-    assert gate_up(lib, x=A2) == INVALID
-    assert silu(lib, gate=A2) == INVALID
+    assert gate_up(lib, x=A1) == INVALID
+    assert gate_up(lib, gy=A1) == INVALID
+    assert silu(lib, gate=A1) == INVALID
+    assert silu(lib, y=A1) == INVALID
     assert silu(lib, y=NULL) == INVALID
     assert silu(lib, resid=A1) == INVALID                    # a residual must be 2-byte aligned
     assert gate_up(lib, m=-1) == INVALID
@@ -233,8 +241,9 @@ def test_gather_qmm_checks(lib):
     assert gather(lib, path=3, k=320, G=64) == UNSUPPORTED    # ... and k a multiple of 512
     assert gather(lib, path=3, scales=A2) == UNSUPPORTED      # ... and 4-byte aligned scales
     assert gather(lib, y=NULL) == INVALID
-    assert gather(lib, y=A4) == INVALID
-    assert gather(lib, x=A2) == INVALID
+    assert gather(lib, y=A1) == INVALID
+    assert gather(lib, x=A1) == INVALID
+    assert gather(lib, x=A2, path=3) == UNSUPPORTED            # the matrix-core kernel: 16-byte x
     assert gather(lib, xb=1 << 32) == UNSUPPORTED
     # nothing to write
     assert gather(lib, batch=0, x=NULL, y=NULL) == OK
@@ -254,7 +263,8 @@ def test_quantize_checks(lib):
     assert quant(lib, packed=NULL) == INVALID
     assert quant(lib, scales=A1) == INVALID
     assert quant(lib, w=NULL) == INVALID
-    assert quant(lib, w=A4) == INVALID                        # w 16-byte aligned
+    assert quant(lib, w=A1) == INVALID                        # w aligned to its element size
+    assert quant(lib, w=A2, dtype=F32) == INVALID
     assert quant(lib, dtype=7) == INVALID
     assert quant(lib, rows=0, w=NULL, packed=NULL, scales=NULL, biases=NULL) == OK
 
@@ -270,7 +280,8 @@ def test_qmm_nt_checks(lib):
     assert qnt(lib, n=48) == INVALID                         # groups run along n
     assert qnt(lib, m=-1) == INVALID
     assert qnt(lib, y=NULL) == INVALID
-    assert qnt(lib, x=A2) == INVALID
+    assert qnt(lib, x=A1) == INVALID
+    assert qnt(lib, y=A2, dtype=F32) == INVALID
     assert qnt(lib, ws=NULL) == INVALID                      # the workspace is required ...
     assert b"workspace" in lib.qaff_last_error()
     assert qnt(lib, wsb=4) == INVALID                        # ... and must be large enough
@@ -316,7 +327,9 @@ def test_typed_checks(lib):
     assert q_t(xt=5) == INVALID
     assert q_t(sb=F32, scales=A2) == INVALID
     assert q_t(y=NULL) == INVALID
-    assert q_t(x=A2) == INVALID
+    assert q_t(x=A1) == INVALID
+    assert q_t(xt=F32, x=A2) == INVALID
+    assert dq_t(o=A2) == INVALID                              # a float32 output at 2 bytes
     # the old entry points keep their types: float16 is not one of them
     assert lib.qaff_qmm(A16, F16, 1, A16, A16, A16, 4, 64, 32, 4, A16, NULL) == INVALID
 

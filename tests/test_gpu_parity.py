@@ -373,15 +373,6 @@ def test_one_dimensional_x_is_a_row(orc):
     assert torch.equal(y1.view(torch.int16), y2[0].view(torch.int16))
 
 
-def test_misaligned_x_is_rejected(orc):
-    inp = W.random_inputs(4, 32, 8, 64, 2)
-    p, s, b = dev_weights(inp)
-    big = torch.zeros(2 * 64 + 1, dtype=torch.bfloat16, device="cuda")
-    x = big[1:].view(2, 64)                      # 2-byte offset: not 16-byte aligned
-    with pytest.raises(qaff().QaffError, match="16-byte"):
-        qaff().qmm(x, p, s, b, 32, 4)
-
-
 def test_repeat_runs_are_bitwise_identical(orc):
     for path, m in (("gemv", 4), ("gemm", 64)):
         inp = W.random_inputs(4, 128, 300, 2048, m, seed=5)
