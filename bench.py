@@ -341,13 +341,14 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
     return row
 
 
-def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget):
+def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, name="moe_4bit_g64_e128_768x2048"):
     """A mixture-of-experts gathered product (gather_qmm): 128 experts of W [768, 2048] at 4-bit
     g64, 8 experts per token, the tokens' rows sorted by expert (rows = 8 * tokens, x [rows, 1, k]).
-    Algorithmic bytes: the weights of the experts in use, x rows, y rows."""
+    Algorithmic bytes: the weights of the experts in use, x rows, y rows. At prefill size (experts
+    averaging 32 rows or more: the grouped GEMM) the row is in TFLOP/s against the bf16 MFMA peak."""
     import numpy as np
     import oracle
-    wl = W.WORKLOADS["moe_4bit_g64_e128_768x2048"]
+    wl = W.WORKLOADS[name]
     mi = W.moe_inputs(wl, tokens)
     rows = mi.expert.size
     used = int(np.unique(mi.expert).size)
@@ -372,12 +373,31 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget):
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
     grouped = rows >= wl.experts
+    gemm = rows >= 32 * wl.experts
     row = {"workload": f"gather_qmm {wl.experts} experts [768, 2048] 4-bit g64, top-{wl.top_k}, {tokens} token(s), "
                        f"{rows} rows sorted by expert ({used} experts in use)",
-           "kernel": "gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)",
+           "kernel": "gemm_grouped" if gemm else ("gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)"),
            "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "weight_copies": copies,
            "roofline": hbm_roofline(gbs)}
-    if cpu:
+    if gemm:
+        flop = 2.0 * rows * wl.n * wl.k
+        tflops = flop / (ms * 1e-3) / 1e12
+        row["tflops"] = round(tflops, 2)
+        row["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    if cpu and gemm:
+        # a sample: the rows of the first expert through the oracle's product
+        threads = oracle.default_threads()
+        sel = np.flatnonzero(mi.expert == mi.expert[0])
+        xs = np.ascontiguousarray(mi.x_rows[sel, 0, :])
+        e0 = int(mi.expert[0])
+        t0 = time.perf_counter()
+        oracle.qmm(xs, "bf16", mi.packed[e0], mi.scales[e0], mi.biases[e0], wl.group_size, wl.bits, threads=threads)
+        el = time.perf_counter() - t0
+        row["cpu_baseline"] = {"value": round(2.0 * sel.size * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"the {sel.size} rows of one expert, {el:.2f} s"}
+    elif cpu:
         threads = oracle.default_threads()
         runs, el = cpu_time(lambda: oracle.gather_qmm(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases,
                                                       wl.group_size, wl.bits, rhs=mi.expert, threads=threads),
@@ -931,6 +951,8 @@ def main():
         add(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:
             add(bench_gather(torch, q, W, timer, tokens, rs, rw, cpu, 2.0))
+        wl_p = W.WORKLOADS["moe_prefill_4bit_g64_e128_768x2048"]
+        add(bench_gather(torch, q, W, timer, wl_p.ms[0], max(20, rs // 10), 5, cpu, 2.0, name=wl_p.name))
         full["rows"] = rows
         result["rows"] = len(rows)
 

@@ -269,9 +269,12 @@ qaff_status qaff_gemv_silu_gate(const void* gate, const void* up, int64_t m, con
  *   m == 1, lhs_indices NULL and a bf16 x, the matrix-core kernel then walks each expert once over
  *   all of its rows (rows [#(rhs < e), #(rhs < e + 1)) of expert e). A broken promise leaves rows
  *   unwritten or computed with another expert. Without the conditions the flag changes nothing.
- * Kernels (QAFF_PATH_AUTO): the matrix-core decode kernel where it applies (bf16 x, k a multiple of
+ * Kernels (QAFF_PATH_AUTO): with the sorted promise kept as above, once the experts average 32 rows
+ * or more (batch >= 32 * w_batches), k a multiple of 1024 and every weight batch's scales and biases
+ * 16-byte aligned, a bf16-MFMA GEMM over each expert's rows (each expert's weights dequantized once
+ * per 128 rows); otherwise the matrix-core decode kernel where it applies (bf16 x, k a multiple of
  * 512 up to 4096, 4-byte aligned scales and biases) when grouped, or when m >= qaff_gemv_mfma_min_m();
- * the VALU GEMV otherwise (any m).
+ * the VALU GEMV otherwise (any m). x or y not 16-byte aligned: the element-by-element GEMV.
  * Errors: as qaff_qmm, plus INVALID_ARGUMENT for negative batch counts, a NULL index array with
  * batch above its operand's batches, or misaligned (4-byte) indices.
  */
@@ -282,8 +285,9 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                             int32_t sorted_indices, void* y, hipStream_t stream);
 
 /* qaff_gather_qmm with the kernel forced: QAFF_PATH_GEMV (the VALU GEMV; the sorted promise is not
- * used) or QAFF_PATH_GEMV_MFMA (UNSUPPORTED where that kernel does not apply). QAFF_PATH_GEMM is
- * UNSUPPORTED. */
+ * used), QAFF_PATH_GEMV_MFMA (UNSUPPORTED where that kernel does not apply) or QAFF_PATH_GEMM (the
+ * GEMM over each expert's rows; UNSUPPORTED unless the sorted promise holds with m == 1, no lhs and
+ * a bf16 x, k is a multiple of 1024 and scales and biases are 16-byte aligned per weight batch). */
 qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
                                const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
                                int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,

@@ -410,8 +410,8 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
     m = x.shape[-2]
     if x.shape[-1] != k:
         raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
-    if path not in ("auto", "gemv", "gemv_mfma"):
-        raise ValueError("path must be 'auto', 'gemv' or 'gemv_mfma'")
+    if path not in ("auto", "gemv", "gemv_mfma", "gemm"):
+        raise ValueError("path must be 'auto', 'gemv', 'gemv_mfma' or 'gemm'")
     x_batch = tuple(x.shape[:-2])
     lhs, lhs_shape = _batch_indices(lhs_indices, x_batch, "lhs_indices", dev)
     rhs, rhs_shape = _batch_indices(rhs_indices, w_batch, "rhs_indices", dev)

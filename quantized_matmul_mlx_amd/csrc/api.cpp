@@ -36,6 +36,9 @@ qaff_status fail(qaff_status st, const char* fmt, ...) {
 
 constexpr int kGemvMaxM = 16;
 constexpr int kGemvMfmaMinM = 3;
+// Gathered products grouped by expert take the GEMM over each expert's rows once the experts
+// average this many rows (below, the matrix-core decode kernel's 16-row tiles).
+constexpr int64_t kGroupedGemmRows = 32;
 
 bool debug_sync() {
     static const bool on = [] {
@@ -355,9 +358,8 @@ qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batc
     qaff_status st = check_weight(op, packed, scales, biases, w_batches * n, k, group_size, bits);
     if (st != QAFF_OK) return st;
     if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
-    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMV_MFMA)
-        return fail(path == QAFF_PATH_GEMM ? QAFF_ERR_UNSUPPORTED : QAFF_ERR_INVALID_ARGUMENT,
-                    "%s: path %d is not available for gathered products", op, (int)path);
+    if (path != QAFF_PATH_AUTO && path != QAFF_PATH_GEMV && path != QAFF_PATH_GEMV_MFMA && path != QAFF_PATH_GEMM)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown path %d", op, (int)path);
     if (!lhs_indices && batch > x_batches)
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: no lhs indices, but %lld batches of %lld x batches", op,
                     (long long)batch, (long long)x_batches);
@@ -396,7 +398,18 @@ qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batc
     g.sb_stride = (uint64_t)(n * (k / group_size));
     g.y_stride = (uint64_t)(m * n);
     // sorted rows, one per output batch, gathered by expert
-    const bool groupable = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices && mfma_ok;
+    const bool sorted_rows = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices && x_dtype == QAFF_BF16;
+    const bool groupable = sorted_rows && mfma_ok;
+    // the GEMM over each expert's rows: forced, or once experts average kGroupedGemmRows rows
+    const bool gemm_ok = sorted_rows && vec && qaff::gemm_grouped_supported(k, scales, biases, g.sb_stride) &&
+                         (w_batches + 1) * ((n + 255) / 256) * 3 < (1LL << 31) - 8;  // its grid fits
+    if (path == QAFF_PATH_GEMM && !gemm_ok)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: the grouped GEMM takes sorted rhs with one bf16 x row per batch and no "
+                    "lhs, k a multiple of 1024 and 16-byte aligned scales and biases of every weight batch", op);
+    if (gemm_ok && (path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && batch >= kGroupedGemmRows * w_batches)))
+        return after_launch(op, qaff::launch_gemm_grouped(static_cast<const uint16_t*>(x), packed, scales, biases, n, k,
+                                                          group_size, bits, static_cast<uint16_t*>(y), rhs_indices,
+                                                          batch, w_batches, g.w_stride, g.sb_stride, stream), stream);
     bool use_mfma = false;
     if (path == QAFF_PATH_GEMV_MFMA) {
         use_mfma = true;

@@ -453,41 +453,30 @@ constexpr int kDirectBody = 16;  // K-steps per loop iteration (scale windows ar
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BITS, int GSHIFT, bool PARTIAL>
-__global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
-    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
-    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
-    uint32_t tiles_n, float* part, uint32_t splits) {
+// One (32 SUB) x 256 tile of Y (SUB = 4: 128 rows; 2: 64 rows): rows m0 .. m0 + 32 SUB - 1 of
+// x [m, k] (rows past m clamped, not stored) against W rows n0 .. n0 + 255 of [n, k], over the K-steps of split `split` of `splits` (all of K
+// when not PARTIAL), stored as bf16 into y [m, n] or as float32 into part[split][m][n]. `xl` is the
+// block's LDS for the X tiles; the call opens with a barrier so that the block can run tiles back
+// to back.
+template <int BITS, int GSHIFT, bool PARTIAL, int SUB = 4>
+__device__ __forceinline__ void direct_tile(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+    uint32_t n, uint32_t kb, uint16_t* y, uint32_t m0, uint32_t n0, float* part, uint32_t split, uint32_t splits,
+    uint16_t (&xl)[2][DBM * LDK]) {
+    constexpr int TM = 32 * SUB;                  // tile rows
     constexpr int P = 4 << GSHIFT;                // K-steps per window of 8 groups
-    constexpr int XPT = DBM * 8 / kDirectThreads;  // 16-byte X chunks per thread and step
-    __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
+    constexpr int XPT = TM * 8 / kDirectThreads;   // 16-byte X chunks per thread and step
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
+    __syncthreads();  // the previous tile's reads of xl are done
 
-    // Tile order: block b runs on XCD b % 8, so each XCD gets a contiguous run of 32 tiles, laid
-    // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2.
-    const uint32_t tiles = tiles_m * tiles_n;
-    uint32_t t = blockIdx.x;
-    if ((tiles & 7u) == 0) t = (t & 7u) * (tiles >> 3) + (t >> 3);
-    uint32_t tm, tn;
-    if ((tiles_m & 3u) == 0 && (tiles_n & 7u) == 0) {
-        const uint32_t st = t >> 5, w = t & 31u, stn = tiles_n >> 3;
-        tm = (st / stn) * 4 + (w >> 3);
-        tn = (st % stn) * 8 + (w & 7u);
-    } else {
-        tm = t / tiles_n;
-        tn = t % tiles_n;
-    }
-    const uint32_t m0 = tm * DBM;
-    const uint32_t n0 = tn * DBN;
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> GSHIFT;  // groups per row
     // This block's K range: 1024-code chunks [c0, c1) of the kb / 32 (all of them unless split).
     const uint32_t chunks = kb >> 5;
-    const uint32_t split = PARTIAL ? blockIdx.y : 0u;
     const uint32_t c0 = PARTIAL ? (uint32_t)((uint64_t)split * chunks / splits) : 0u;
     const uint32_t c1 = PARTIAL ? (uint32_t)((uint64_t)(split + 1) * chunks / splits) : chunks;
     const uint32_t kt_off = c0 * kDirectBody;               // first K-step
@@ -527,17 +516,17 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
         r[1] = *reinterpret_cast<const u32x4a*>(bp + o);
     };
 
-    f32x16 acc[4];
+    f32x16 acc[SUB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < SUB; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
 
     // X operand of tile i, MFMA kk: row 32 i + lane % 32, k offset 32 h + 8 kk.
     const int aoff = (lane & 31) * LDK + h * 32;
-    auto read_a = [&](const uint16_t* L, int kk, bf16x8 (&a)[4]) {
+    auto read_a = [&](const uint16_t* L, int kk, bf16x8 (&a)[SUB]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(L + aoff + 32 * i * LDK + 8 * kk);
+        for (int i = 0; i < SUB; ++i) a[i] = *reinterpret_cast<const bf16x8*>(L + aoff + 32 * i * LDK + 8 * kk);
     };
 
     // Prologue: X of step 0 in LDS, X of steps 1 and 2 and W of steps 0..2 in flight, the first
@@ -586,14 +575,14 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
             }
             const Dq dq = make_dq(__uint_as_float((sw >> sh) << 16), __uint_as_float((bw >> sh) << 16));
             const uint16_t* L = xl[u & 1];
-            bf16x8 a[2][4];
+            bf16x8 a[2][SUB];
             read_a(L, 0, a[0]);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 if (kk < 3) read_a(L, kk + 1, a[(kk + 1) & 1]);
                 const bf16x8 bw8 = dequant8m<BITS>(wr[u & 3], kk, dq);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < SUB; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][i], bw8, acc[i], 0, 0, 0);
             }
             __syncthreads();
@@ -604,7 +593,7 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     const int orow = 4 * h;
     if (gc < n) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < SUB; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const uint32_t gm = m0 + 32 * i + 8 * (v >> 2) + orow + (v & 3);
@@ -616,6 +605,75 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
                 }
             }
     }
+}
+
+template <int BITS, int GSHIFT, bool PARTIAL>
+__global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
+    uint32_t tiles_n, float* part, uint32_t splits) {
+    __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
+    // Tile order: block b runs on XCD b % 8, so each XCD gets a contiguous run of 32 tiles, laid
+    // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2.
+    const uint32_t tiles = tiles_m * tiles_n;
+    uint32_t t = blockIdx.x;
+    if ((tiles & 7u) == 0) t = (t & 7u) * (tiles >> 3) + (t >> 3);
+    uint32_t tm, tn;
+    if ((tiles_m & 3u) == 0 && (tiles_n & 7u) == 0) {
+        const uint32_t st = t >> 5, w = t & 31u, stn = tiles_n >> 3;
+        tm = (st / stn) * 4 + (w >> 3);
+        tn = (st % stn) * 8 + (w & 7u);
+    } else {
+        tm = t / tiles_n;
+        tn = t % tiles_n;
+    }
+    direct_tile<BITS, GSHIFT, PARTIAL>(x, m, packed, scales, biases, n, kb, y, tm * DBM, tn * DBN, part,
+                                       PARTIAL ? blockIdx.y : 0u, splits, xl);
+}
+
+// ---- gathered batches grouped by expert (nuvec_core quantized.rs, gather_qmm with sorted rhs) --
+//
+// Output batch r (one row of x each, no lhs) is x[r] . dequantize(W[rhs[r]])^T with rhs sorted,
+// so the rows of expert e are [#(rhs < e), #(rhs < e + 1)): a plain GEMM of those rows against
+// W[e]. Block (e, tile column, s) finds that range in the sorted indices and runs the expert's
+// row tiles s, s + kGroupedSplit, ..., each with W[e] dequantized into registers as above. Experts
+// of a few hundred rows take 64-row tiles (SUB = 2): less padding in each expert's last tile and
+// more, smaller tiles to spread over the compute units, for twice the dequantization per flop.
+// Expert w_count stands for the rows past every expert (an index out of range): they get NaN.
+constexpr uint32_t kGroupedSplit = 3;  // blocks per expert and tile column
+
+template <int BITS, int GSHIFT, int SUB>
+__global__ __launch_bounds__(kDirectThreads) void gemm_grouped_kernel(
+    const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases, uint32_t n,
+    uint32_t kb, uint16_t* y, const uint32_t* rhs, uint32_t batch, uint32_t w_count, uint32_t tiles_n,
+    uint64_t w_stride, uint64_t sb_stride) {
+    constexpr uint32_t TM = 32 * SUB;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
+    // Block b runs on XCD b % 8 (the grid is a multiple of 8): consecutive logical blocks -- those of
+    // one expert -- go to one XCD, so that its L2 holds the expert's weights and rows for all of them.
+    const uint32_t t = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (t >= (w_count + 1) * tiles_n * kGroupedSplit) return;
+    const uint32_t e = t / (tiles_n * kGroupedSplit);
+    const uint32_t rem = t - e * tiles_n * kGroupedSplit;
+    const uint32_t tn = rem / kGroupedSplit, s = rem % kGroupedSplit;
+    const int lane = threadIdx.x & 63;
+    uint32_t lo, hi;
+    count_below2(rhs, batch, e, e + 1, lane, lo, hi);  // the same in every wave
+    if (e == w_count) hi = batch;                       // rows past every expert
+    if (lo >= hi) return;                               // block-uniform
+    const uint32_t rows = hi - lo;
+    if (e >= w_count) {
+        // an index out of range: NaN over these rows' columns of this tile column
+        const uint32_t cols = min(n - tn * DBN, (uint32_t)DBN);
+        for (uint32_t o = s * kDirectThreads + threadIdx.x; o < rows * cols; o += kGroupedSplit * kDirectThreads)
+            y[(size_t)(lo + o / cols) * n + tn * DBN + o % cols] = 0x7fc0u;
+        return;
+    }
+    const uint32_t k = kb * 32;
+    for (uint32_t t = s; t * TM < rows; t += kGroupedSplit)
+        direct_tile<BITS, GSHIFT, false, SUB>(x + (size_t)lo * k, rows, packed + e * w_stride,
+                                              scales + e * sb_stride, biases + e * sb_stride, n, kb,
+                                              y + (size_t)lo * n, t * TM, tn * DBN, nullptr, 0u, 1u, xl);
 }
 
 // y[i] = bf16(part[0][i] + part[1][i] + ... + part[splits - 1][i]), in that order, for i < count.
@@ -742,7 +800,59 @@ int64_t direct_splits(int64_t m, int64_t n, int64_t k) {
     return s < 1 ? 1 : s;
 }
 
+template <int BITS, int GSHIFT>
+hipError_t launch_grouped_g(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t n, int64_t kb, uint16_t* y, const uint32_t* rhs, int64_t batch, int64_t w_count,
+                            uint64_t w_stride, uint64_t sb_stride, hipStream_t stream) {
+    const int64_t tiles_n = (n + DBN - 1) / DBN;
+    const unsigned blocks = (unsigned)(((w_count + 1) * tiles_n * kGroupedSplit + 7) / 8 * 8);
+    // 64-row tiles while the experts average up to 256 rows
+    if (batch <= 256 * w_count)
+        gemm_grouped_kernel<BITS, GSHIFT, 2><<<dim3(blocks), dim3(kDirectThreads), 0, stream>>>(
+            x, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, rhs, (uint32_t)batch, (uint32_t)w_count,
+            (uint32_t)tiles_n, w_stride, sb_stride);
+    else
+        gemm_grouped_kernel<BITS, GSHIFT, 4><<<dim3(blocks), dim3(kDirectThreads), 0, stream>>>(
+            x, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, rhs, (uint32_t)batch, (uint32_t)w_count,
+            (uint32_t)tiles_n, w_stride, sb_stride);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_grouped_b(const uint16_t* x, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                            int64_t n, int64_t kb, uint32_t gshift, uint16_t* y, const uint32_t* rhs, int64_t batch,
+                            int64_t w_count, uint64_t w_stride, uint64_t sb_stride, hipStream_t stream) {
+    if (gshift == 0)
+        return launch_grouped_g<BITS, 0>(x, packed, scales, biases, n, kb, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+    if (gshift == 1)
+        return launch_grouped_g<BITS, 1>(x, packed, scales, biases, n, kb, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+    return launch_grouped_g<BITS, 2>(x, packed, scales, biases, n, kb, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+}
+
 }  // namespace
+
+bool gemm_grouped_supported(int64_t k, const uint16_t* scales, const uint16_t* biases, uint64_t sb_stride) {
+    auto a16 = [](const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+    return k > 0 && k % (64 * kDirectBody) == 0 && a16(scales) && a16(biases) && (sb_stride * 2) % 16 == 0;
+}
+
+hipError_t launch_gemm_grouped(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
+                               const uint32_t* rhs, int64_t batch, int64_t w_count, uint64_t w_stride,
+                               uint64_t sb_stride, hipStream_t stream) {
+    const int64_t kb = k / 32;
+    const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
+    switch (bits) {
+        case 1: return launch_grouped_b<1>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 2: return launch_grouped_b<2>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 3: return launch_grouped_b<3>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 4: return launch_grouped_b<4>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 5: return launch_grouped_b<5>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 6: return launch_grouped_b<6>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        case 8: return launch_grouped_b<8>(x, packed, scales, biases, n, kb, gshift, y, rhs, batch, w_count, w_stride, sb_stride, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     const int64_t s = direct_splits(m, n, k);

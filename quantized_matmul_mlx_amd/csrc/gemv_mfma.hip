@@ -262,77 +262,6 @@ hipError_t launch_bits(const uint16_t* x, int64_t m, const uint32_t* packed, con
 //    it. Expert w_count takes the rows past every expert (NaN).
 // An out-of-range index gives a NaN output batch.
 
-// #(idx[i] < v1) and #(idx[i] < v2) over a sorted idx[0 .. len), len >= 1.
-//  * len <= 1024: every lane counts 16 consecutive entries (four 16-byte loads, one round trip);
-//    the wave total of a count below 32 is the sum over its bits of the ballot popcounts.
-//  * longer: a 64-ary search per bound, both in lockstep so that their loads go out together.
-//    Each step probes lo + lane * step; the probes below v are a prefix (the array is sorted), and
-//    the bound lies after the last one and no later than the next.
-constexpr uint32_t kCountMax = 1024;
-
-__device__ __forceinline__ uint32_t wave_total(uint32_t c) {  // 0 <= c < 32 in every lane
-    uint32_t t = 0;
-#pragma unroll
-    for (int b = 0; b < 5; ++b)
-        t += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((c >> b) & 1u)) << b;
-    return t;
-}
-
-__device__ __forceinline__ void count_below2(const uint32_t* idx, uint32_t len, uint32_t v1, uint32_t v2,
-                                             int lane, uint32_t& c1, uint32_t& c2) {
-    if (len <= kCountMax) {
-        uint32_t a[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint32_t i0 = min((uint32_t)lane * 16 + 4 * q, len - 1);
-            if (i0 + 4 <= len) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(idx + i0);
-                a[4 * q] = v.x; a[4 * q + 1] = v.y; a[4 * q + 2] = v.z; a[4 * q + 3] = v.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a[4 * q + e] = idx[min(i0 + e, len - 1)];
-            }
-        }
-        uint32_t n1 = 0, n2 = 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const bool in = (uint32_t)lane * 16 + e < len;
-            n1 += (in && a[e] < v1) ? 1u : 0u;
-            n2 += (in && a[e] < v2) ? 1u : 0u;
-        }
-        c1 = wave_total(n1);
-        c2 = wave_total(n2);
-        return;
-    }
-    uint32_t lo1 = 0, hi1 = len, lo2 = 0, hi2 = len;
-    while (lo1 < hi1 || lo2 < hi2) {
-        const uint32_t st1 = (hi1 - lo1 + 63) >> 6, st2 = (hi2 - lo2 + 63) >> 6;
-        const uint32_t i1 = lo1 + (uint32_t)lane * st1, i2 = lo2 + (uint32_t)lane * st2;
-        const uint32_t a1 = idx[min(i1, len - 1)];
-        const uint32_t a2 = idx[min(i2, len - 1)];
-        const uint32_t n1 = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i1 < hi1 && a1 < v1));
-        const uint32_t n2 = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(i2 < hi2 && a2 < v2));
-        if (lo1 < hi1) {
-            if (n1 == 0) {
-                hi1 = lo1;
-            } else {
-                hi1 = min(lo1 + n1 * st1, hi1);
-                lo1 += (n1 - 1) * st1 + 1;
-            }
-        }
-        if (lo2 < hi2) {
-            if (n2 == 0) {
-                hi2 = lo2;
-            } else {
-                hi2 = min(lo2 + n2 * st2, hi2);
-                lo2 += (n2 - 1) * st2 + 1;
-            }
-        }
-    }
-    c1 = lo1;
-    c2 = lo2;
-}
-
 template <int BITS, int NT, int GSHIFT, int MB>
 __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,

@@ -88,6 +88,17 @@ hipError_t launch_gemm(const uint16_t* x, int64_t m, const uint32_t* packed,
                        size_t workspace_bytes = 0);
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
+// The GEMM above over gathered batches grouped by expert: output row r (one x row per batch, no lhs)
+// is x[r] . dequantize(W[rhs[r]])^T with rhs sorted (non-decreasing); each expert's rows form a plain
+// GEMM against its weight batch. Rows whose index is at or past w_count get NaN. Supported where
+// gemm_grouped_supported holds (K a multiple of 1024, 16-byte aligned scales and biases of every
+// weight batch).
+bool gemm_grouped_supported(int64_t k, const uint16_t* scales, const uint16_t* biases, uint64_t sb_stride);
+hipError_t launch_gemm_grouped(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                               const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
+                               const uint32_t* rhs, int64_t batch, int64_t w_count, uint64_t w_stride,
+                               uint64_t sb_stride, hipStream_t stream);
+
 // packed/scales/biases of a dense [rows, cols] weight (float32 or bf16): bias = group min,
 // scale = (max - min) / (2^bits - 1), both bf16; code = round((w - bias) / scale), clamped.
 // w 16-byte aligned: 16-byte loads; otherwise element by element.

@@ -92,6 +92,10 @@ WORKLOADS = {
     "moe_4bit_g64_e128_768x2048": Workload("moe_4bit_g64_e128_768x2048", 4, 64, 768, 2048,
                                            (1e-3, 2e-2), (-0.15, 0.0), ms=(1, 64), seed=41,
                                            experts=128, top_k=8),
+    # The same layer at prefill: 2048 tokens (16384 rows, about 128 per expert).
+    "moe_prefill_4bit_g64_e128_768x2048": Workload("moe_prefill_4bit_g64_e128_768x2048", 4, 64, 768, 2048,
+                                                   (1e-3, 2e-2), (-0.15, 0.0), ms=(2048,), seed=42,
+                                                   experts=128, top_k=8),
 }
 
 

@@ -56,6 +56,10 @@ hipError_t launch_gemv_mfma_gather(const uint16_t*, int64_t, const uint32_t*, co
 }
 hipError_t launch_gemm(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
                        int, int, uint16_t*, hipStream_t, void* ws, size_t) { return rec(ws ? "gemm_split" : "gemm"); }
+bool gemm_grouped_supported(int64_t k, const uint16_t*, const uint16_t*, uint64_t) { return k % 1024 == 0; }
+hipError_t launch_gemm_grouped(const uint16_t*, const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
+                               int, int, uint16_t*, const uint32_t*, int64_t, int64_t, uint64_t, uint64_t,
+                               hipStream_t) { return rec("gemm_grouped"); }
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     return (m <= 256 && k % 1024 == 0) ? (size_t)(m * n * 4 * 2) : 0;
 }
@@ -162,6 +166,13 @@ int main() {
                                                            nullptr, I16, 8, 1, A16, nullptr));
     EXPECT(INV, "", qaff_gather_qmm(A16, QAFF_BF16, 2, 1, P16, S16, B16, 4, 64, 4096, 64, 4, nullptr, I16, 3, 0, A16,
                                     nullptr));
+    // sorted rows averaging 32 or more per expert: the grouped GEMM (forced or automatic)
+    EXPECT(OK, "gemm_grouped", qaff_gather_qmm(A16, QAFF_BF16, 512, 1, P16, S16, B16, 16, 64, 4096, 64, 4, nullptr, I16,
+                                               512, 1, A16, nullptr));
+    EXPECT(OK, "gemv_mfma_gather_grouped", qaff_gather_qmm(A16, QAFF_BF16, 500, 1, P16, S16, B16, 16, 64, 4096, 64, 4,
+                                                           nullptr, I16, 500, 1, A16, nullptr));
+    EXPECT(OK, "gemm_grouped", qaff_gather_qmm_ex(A16, QAFF_BF16, 20, 1, P16, S16, B16, 16, 64, 4096, 64, 4, nullptr,
+                                                  I16, 20, 1, A16, nullptr, QAFF_PATH_GEMM));
     EXPECT(UNS, "", qaff_gather_qmm_ex(A16, QAFF_BF16, 2, 1, P16, S16, B16, 4, 64, 4096, 64, 4, I16, I16, 2, 0, A16,
                                        nullptr, QAFF_PATH_GEMM));
     // quantize

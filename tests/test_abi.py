@@ -235,7 +235,7 @@ def test_gather_qmm_checks(lib):
     assert gather(lib, rhs=NULL, batch=4) == INVALID          # no rhs: batch <= weight batches
     assert gather(lib, rhs=A2) == INVALID                     # indices are 4-byte aligned
     assert gather(lib, lhs=A2) == INVALID
-    assert gather(lib, path=2) == UNSUPPORTED                 # no GEMM for gathered products
+    assert gather(lib, path=2) == UNSUPPORTED                 # the grouped GEMM needs sorted rows
     assert gather(lib, path=9) == INVALID
     assert gather(lib, path=3, dtype=F32) == UNSUPPORTED      # the matrix-core kernel takes bf16
     assert gather(lib, path=3, k=320, G=64) == UNSUPPORTED    # ... and k a multiple of 512

@@ -177,6 +177,78 @@ def test_gather_grouped_rows_past_every_expert_are_nan(orc):
     assert np.isnan(got[5:]).all() and np.isfinite(got[:5]).all()
 
 
+# ---- grouped: the GEMM over each expert's rows (hundreds of rows per expert) ------------------------
+
+def grouped_refs(orc, x, packed, scales, biases, G, bits, rhs):
+    """Row r against expert rhs[r], each expert's rows at once: the oracle's product (gather_qmm's
+    definition: the plain product per batch) and x . bf16(W)^T in float64 (the kernel's own
+    arithmetic: weights rounded to bf16); NaN for rows past the experts."""
+    E, n = packed.shape[0], packed.shape[1]
+    xr = x.reshape(rhs.size, -1)
+    ref = np.full((rhs.size, 1, n), np.nan)
+    tight = np.full((rhs.size, 1, n), np.nan)
+    xf = orc.bf16_to_f32(xr).astype(np.float64)
+    for e in np.unique(rhs):
+        if e >= E:
+            continue
+        rows = np.flatnonzero(rhs == e)
+        ref[rows, 0, :] = orc.qmm(np.ascontiguousarray(xr[rows]), "bf16", packed[e], scales[e], biases[e], G, bits)
+        w = orc.bf16_to_f32(orc.dequantize(packed[e], scales[e], biases[e], G, bits, out="bf16")).astype(np.float64)
+        tight[rows, 0, :] = xf[rows] @ w.T
+    return ref, tight
+
+
+def check_grouped(orc, got, x, packed, scales, biases, G, bits, rhs):
+    ref, tight = grouped_refs(orc, x, packed, scales, biases, G, bits, rhs)
+    nan = rhs >= packed.shape[0]
+    assert np.isnan(got[nan]).all(), "rows past every expert must be NaN"
+    assert np.isfinite(got[~nan]).all()
+    g2, r2, t2 = (a[~nan].reshape(-1, a.shape[-1]) for a in (got, ref, tight))
+    if g2.size:
+        assert orc.max_row_rel_err(g2, r2) <= TOL["bf16"]
+        assert orc.max_row_rel_err(g2, t2) <= TIGHT["bf16"]
+
+
+# Experts of several 128-row tiles (odd and even counts, so both blocks of an expert's tile column
+# take tiles), of one row, empty ones, a ragged tile column (n = 300 of 256-column tiles), and rows
+# past every expert; every width.
+@pytest.mark.parametrize("bits,G,counts,past", [
+    (4, 64, [0, 200, 129, 1, 300, 50], 3),
+    (3, 32, [130, 0, 5], 0),
+    (8, 128, [257], 2),
+    (2, 64, [64, 64, 64, 64], 0),
+    (5, 32, [10, 300], 1),
+    (6, 128, [0, 0, 140], 0),
+    (1, 32, [100, 30], 5),
+])
+def test_gather_grouped_gemm(orc, bits, G, counts, past):
+    E, n, k = len(counts), 300, 1024
+    packed, scales, biases = experts(bits, G, E, n, k, seed=900 + bits)
+    rhs = np.concatenate([sorted_rows(counts), np.full(past, E + 2, np.uint32)]).astype(np.uint32)
+    x = draw_x((rhs.size, 1, k), "bf16", seed=910 + bits)
+    banner(f"gather grouped gemm bits={bits} G={G} counts={counts} past={past}")
+    got = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemm")
+    check_grouped(orc, got, x, packed, scales, biases, G, bits, rhs)
+
+
+def test_gather_grouped_gemm_dispatch(orc):
+    # experts averaging 32 rows or more: AUTO takes the grouped GEMM (the same bits as forced);
+    # fewer: the matrix-core decode kernel's grouped walk
+    E, n, k, G, bits = 4, 256, 2048, 64, 4
+    packed, scales, biases = experts(bits, G, E, n, k, seed=930)
+    for counts, kernel in (([40, 30, 50, 8], "gemm"), ([10, 30, 20, 8], "gemv_mfma")):
+        rhs = sorted_rows(counts)
+        x = draw_x((rhs.size, 1, k), "bf16", seed=931)
+        banner(f"gather grouped dispatch counts={counts}")
+        auto = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True)
+        forced = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path=kernel)
+        np.testing.assert_array_equal(auto, forced)
+        check_grouped(orc, auto, x, packed, scales, biases, G, bits, rhs)
+    # the GEMM needs the sorted promise with one row per batch
+    with pytest.raises(qaff().QaffError, match="grouped GEMM"):
+        run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=False, path="gemm")
+
+
 @pytest.mark.parametrize("path,x_dtype", [("gemv", "bf16"), ("gemv", "f32"), ("gemv_mfma", "bf16")])
 def test_gather_batched_out_of_range_is_nan(orc, path, x_dtype):
     E, n, k, G, bits = 2, 70, 512, 32, 4
@@ -288,3 +360,14 @@ def test_qmm_with_a_batched_weight_broadcasts(orc):
     assert orc.max_row_rel_err(host_f64(y2).reshape(-1, n), ref2.reshape(-1, n)) <= TOL["bf16"]
     ref1 = orc.gather_qmm(x1[None, None], "bf16", packed, scales, biases, G, bits)[:, 0, :]
     assert orc.max_row_rel_err(host_f64(y1), ref1) <= TOL["bf16"]
+
+
+def test_gather_moe_prefill_workload(orc):
+    # 2048 tokens, top-8 of 128 experts [768, 2048] (about 128 rows per expert): the grouped GEMM
+    wl = W.WORKLOADS["moe_prefill_4bit_g64_e128_768x2048"]
+    mi = W.moe_inputs(wl, wl.ms[0])
+    lib = qaff()._lib.load()
+    banner(f"gather moe prefill workload rows={mi.expert.size}")
+    got = run(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits, None, mi.expert,
+              sorted_=True)
+    check_grouped(orc, got, mi.x_rows, mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits, mi.expert)
