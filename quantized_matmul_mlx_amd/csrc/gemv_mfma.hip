@@ -26,6 +26,14 @@
 //  * Scales and biases of a tile row come as one window over the slice (16, 8 or 4 groups),
 //    not one load per block: small scattered loads were a third of the time.
 //  * The slices' float32 partial tiles are summed through LDS at the end.
+//  * Exact 4-bit codes (x rows rounded to 4 with any group size, to 8 with groups of 64 or 128,
+//    to 16 with groups of 128): a chunk's 4 >> log2(G / 32) groups each get a band of MB of the 16
+//    operand rows, in which only the lanes whose k-slot lies in that group read x (the others read
+//    a zeroed LDS area). Each result lane then holds the sums of a single group, so the codes can
+//    enter unscaled, as bf16 128 + c (one AND-OR per pair of codes), and the group's scale and bias
+//    are applied to the sums: s D + (b / 128 - s) X, with X = sum x 128 from one more MFMA per
+//    step against a constant 128 (shared by the tiles). The bands are added in the final sum.
+//    The weights are then not rounded to bf16: the result is the float32 product of the oracle.
 // Requirements (checked by the launcher): bf16 x, K a multiple of 512 and at most 4096.
 #include "launch.h"
 #include "qaff_device.h"
@@ -81,6 +89,116 @@ struct SbWindow {
     }
 };
 
+// ---- exact 4-bit codes ---------------------------------------------------------------------------
+
+// Whether the codes enter exactly: every group of a chunk (4 >> GSHIFT of them) needs a band of MB
+// of the 16 operand rows.
+template <int BITS, int GSHIFT, int MB>
+constexpr bool kExactCodes = BITS == 4 && (4 >> GSHIFT) * MB <= 16;
+
+// The constants of the exact operands: the code mask in a scalar register and bf16 128.0 (both
+// halves) in a vector register, for one v_and_or_b32 per pair of codes, and the all-128 operand.
+struct ExactConsts {
+    uint32_t mask, base;
+    bf16x8 k128;
+};
+__device__ __forceinline__ ExactConsts make_exact_consts() {
+    uint32_t base = 0x43004300u;
+    asm volatile("" : "+v"(base));  // kept in a register: the AND-OR takes it as its third operand
+    return ExactConsts{(uint32_t)__builtin_amdgcn_readfirstlane(0x000F000F), base,
+                       __builtin_bit_cast(bf16x8, u32x4a{0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u})};
+}
+
+// The eight 4-bit codes of a word as exact bf16 values 128 + c in the pair order (c0, c4), (c1, c5),
+// (c2, c6), (c3, c7): the codes go into the mantissas of 128.0. Plain C on purpose: this value is
+// an MFMA operand, and the compiler keeps the wait states that a matrix instruction needs after a
+// VALU write of its operand only behind instructions it emitted itself, not behind inline asm (a
+// v_xor_b32 in asm got one wait state before the MFMA reading its result, the same instruction
+// compiled from C two).
+__device__ __forceinline__ bf16x8 codes4_exact(uint32_t w, const ExactConsts& e) {
+    return __builtin_bit_cast(bf16x8, u32x4a{(w & e.mask) | e.base, ((w >> 4) & e.mask) | e.base,
+                                             ((w >> 8) & e.mask) | e.base, ((w >> 12) & e.mask) | e.base});
+}
+
+// Eight bf16 values x0..x7 (four words, natural order) in that pair order: x0 x4 x1 x5 x2 x6 x3 x7.
+__device__ __forceinline__ u32x4a pair_order4(u32x4a v) {
+    return u32x4a{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                  __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+}
+
+// Lane (r, g)'s x operand: row min(r, MB - 1) of its wave's LDS region at k-slot g; with exact
+// codes, row r % MB of band r / MB, which reads x only where the band is the group of the lane's
+// k-slot (g >> GSHIFT) and the zeroed area elsewhere.
+template <int GSHIFT, int MB, bool EXACT>
+__device__ __forceinline__ const uint8_t* x_operand(const uint8_t* xl, const uint8_t* zero, int lr16, int lg) {
+    if constexpr (!EXACT) {
+        return xl + min(lr16, MB - 1) * kXPitch + lg * 64;
+    } else {
+        const int band = lr16 / MB, r = lr16 % MB;
+        return band == (lg >> GSHIFT) ? xl + r * kXPitch + lg * 64 : zero + lg * 64;
+    }
+}
+
+// The window selector of the group whose scale and bias a result lane takes: the lane's own block
+// (lane / 16) for dequantized codes; with exact codes, the band of its result rows 4 (lane / 16) ..
+// + 3, as a block index of that group (bands past the chunk's groups hold zeros: any group will do).
+template <int GSHIFT, int MB, bool EXACT>
+__device__ __forceinline__ int fold_selector(int lg) {
+    if constexpr (!EXACT) return lg;
+    const int band = (4 * lg) / MB;
+    return (band & ((4 >> GSHIFT) - 1)) << GSHIFT;
+}
+
+// Chunk c of the multiply: acc[t] += x_chunk . w_chunk(tile t)^T, from the codes wq[t][c] of each
+// tile, its scale and bias windows and the x operand at xa (see x_operand), dequantized (scale and
+// bias per lane) or exact (scale and bias per band, on the MFMA sums).
+template <int BITS, int NT, int GSHIFT, int MB>
+__device__ __forceinline__ void chunk_product(int c, const uint32_t (&wq)[NT][4][BITS], const SbWindow<GSHIFT> (&sw)[NT],
+                                              const SbWindow<GSHIFT> (&bw)[NT], const uint8_t* xa, int sel,
+                                              uint64_t sel_hi, const ExactConsts& ec, f32x4 (&acc)[NT]) {
+    if constexpr (kExactCodes<BITS, GSHIFT, MB>) {
+        f32x4 d[NT];
+        f32x4 dx = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) d[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, codes4_exact(wq[t][c][j], ec), d[t], 0, 0, 0);
+            dx = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ec.k128, dx, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            // sum x (s c + b) = s sum x (128 + c) + (b / 128 - s) sum x 128
+            const float s = sw[t].get(c, sel, sel_hi);
+            const float beta = __builtin_fmaf(bw[t].get(c, sel, sel_hi), 0.0078125f, -s);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(s, d[t][v], __builtin_fmaf(beta, dx[v], acc[t][v]));
+        }
+    } else {
+        bf16x8 wb[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const Dq dq = make_dq(sw[t].get(c, sel, sel_hi), bw[t].get(c, sel, sel_hi));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8m<BITS>(wq[t][c], j, dq);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
+        }
+    }
+}
+
+// Extra LDS of the exact-code kernels: the zeroed x area (1 KB: k-slot offsets up to 64 * 3 plus
+// a chunk's 1 KB of steps).
+template <int BITS, int GSHIFT, int MB>
+constexpr size_t kZeroBytes = kExactCodes<BITS, GSHIFT, MB> ? 1024 : 0;
+
 template <int BITS, int NT, int GSHIFT, int MB>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
@@ -95,7 +213,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     const uint32_t gpr = kb >> GSHIFT;  // groups per row
     const int lr16 = lane & 15;
     const int lg = lane >> 4;
-    const uint64_t g_hi = __builtin_amdgcn_ballot_w64(lg >= 2);
 
     // 1. Loads, oldest first: this wave's slice of every x row (one contiguous 1 KB load per row),
     //    then per tile the scale and bias windows and, chunk by chunk, the W blocks, so that each
@@ -134,11 +251,20 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     }
 
     // 2. x into this wave's LDS region: row r at r * 1040 bytes, so the 16 rows that the operand
-    //    read touches at one offset fall on distinct banks (1040 / 4 = 4 mod 64).
+    //    read touches at one offset fall on distinct banks (1040 / 4 = 4 mod 64). Exact codes: each
+    //    8-value unit in the codes' pair order, and the zeroed area after the regions (every wave
+    //    writes the same zeros there before reading it).
+    constexpr bool kExact = kExactCodes<BITS, GSHIFT, MB>;
     uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
+    uint8_t* zero = smem + (size_t)waves * (MB * kXPitch);
 #pragma unroll
-    for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
-    const uint8_t* xa = xl + min((uint32_t)lr16, (uint32_t)MB - 1) * kXPitch + lg * 64;
+    for (int r = 0; r < MB; ++r)
+        *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = kExact ? pair_order4(xg[r]) : xg[r];
+    if constexpr (kExact) *reinterpret_cast<u32x4a*>(zero + lane * 16) = u32x4a{0u, 0u, 0u, 0u};
+    const uint8_t* xa = x_operand<GSHIFT, MB, kExact>(xl, zero, lr16, lg);
+    const int sel = fold_selector<GSHIFT, MB, kExact>(lg);
+    const uint64_t sel_hi = __builtin_amdgcn_ballot_w64(sel >= 2);
+    const ExactConsts ec = make_exact_consts();
 
     // 3. Multiply, chunk by chunk. Lane (r, g) of chunk c holds block 4 c + g of its row; MFMA j
     //    takes codes 8 j .. 8 j + 7 of each lane's block, and x in the same order.
@@ -154,22 +280,12 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(wq[t][c][i]) : "v"(acc[0]));
-        bf16x8 wb[NT][4];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const Dq dq = make_dq(sw[t].get(c, lg, g_hi), bw[t].get(c, lg, g_hi));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wb[t][j] = dequant8m<BITS>(wq[t][c], j, dq);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
-        }
+        chunk_product<BITS, NT, GSHIFT, MB>(c, wq, sw, bw, xa, sel, sel_hi, ec, acc);
     }
 
-    // 4. Sum the slices' partial tiles through LDS: [wave][tile][v][lane] float32.
+    // 4. Sum the slices' partial tiles (and the bands of exact codes) through LDS:
+    //    [wave][tile][v][lane] float32.
+    constexpr int kBands = kExact ? (4 >> GSHIFT) : 1;
     __syncthreads();  // every wave is done with its x rows
     float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -177,11 +293,16 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[((wave * NT + t) * 4 + v) * 64 + lane] = acc[t][v];
     __syncthreads();
-    for (int o = tid; o < 256 * NT; o += (int)blockDim.x) {
-        const int t = o >> 8, mm = (o >> 4) & 15, nn = o & 15;
-        const int l = ((mm >> 2) << 4) | nn, v = mm & 3;
+    for (int o = tid; o < 16 * MB * NT; o += (int)blockDim.x) {
+        const int t = o / (16 * MB), rem = o % (16 * MB);
+        const int mm = rem >> 4, nn = rem & 15;
         float sum = 0.f;
-        for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+#pragma unroll
+        for (int p = 0; p < kBands; ++p) {
+            const int rr = p * MB + mm;
+            const int l = ((rr >> 2) << 4) | nn, v = rr & 3;
+            for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+        }
         const uint32_t row = n0 + 16 * t + nn;
         if ((uint32_t)mm < m && row < n) y[(size_t)mm * n + row] = to_bf16_bits(sum);
     }
@@ -191,7 +312,7 @@ template <int BITS, int NT, int GSHIFT, int MB>
 hipError_t launch_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                      const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
     const int waves = (int)(kb / 16);
-    size_t lds = (size_t)waves * MB * kXPitch;
+    size_t lds = (size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>;
     const size_t red = (size_t)waves * NT * 4 * 64 * sizeof(float);
     if (red > lds) lds = red;
     const unsigned blocks = (unsigned)((n + 16 * NT - 1) / (16 * NT));
@@ -207,7 +328,7 @@ hipError_t launch_g(const uint16_t* x, int64_t m, const uint32_t* packed, const 
     // slices: MB x 1040 bytes per wave) sets how many fit on a compute unit; each block takes as
     // many 16-row tiles (1 to 4) as needed to cover n in one round of the compute units.
     const int64_t waves = kb / 16;
-    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch);
+    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch + (int64_t)kZeroBytes<BITS, GSHIFT, MB>);
     if (per_cu < 1) per_cu = 1;
     if (per_cu > 4) per_cu = 4;
     const int64_t cus = device_cu_count();
@@ -276,7 +397,6 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     const uint32_t gpr = kb >> GSHIFT;
     const int lr16 = lane & 15;
     const int lg = lane >> 4;
-    const uint64_t g_hi = __builtin_amdgcn_ballot_w64(lg >= 2);
     const uint32_t z = ga.b0 + blockIdx.y;
 
     // 1. This block's x rows [r0, r1) (row r at xb + r k, its output at yb + r n) and weight batch.
@@ -340,17 +460,27 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
     }
 
     // 3. Walk the x rows in tiles of MB: x through this wave's LDS region, the multiply chunk by
-    //    chunk, and the slices' partial tiles summed through a separate LDS area.
+    //    chunk, and the slices' partial tiles (and the bands of exact codes) summed through a
+    //    separate LDS area. Exact codes: x in the codes' pair order, and the zeroed area after the
+    //    x regions (see the decode kernel).
+    constexpr bool kExact = kExactCodes<BITS, GSHIFT, MB>;
+    constexpr int kBands = kExact ? (4 >> GSHIFT) : 1;
     uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
-    float* red = reinterpret_cast<float*>(smem + (size_t)waves * (MB * kXPitch));
-    const uint8_t* xa = xl + min(lr16, MB - 1) * kXPitch + lg * 64;
+    uint8_t* zero = smem + (size_t)waves * (MB * kXPitch);
+    float* red = reinterpret_cast<float*>(zero + kZeroBytes<BITS, GSHIFT, MB>);
+    if constexpr (kExact) *reinterpret_cast<u32x4a*>(zero + lane * 16) = u32x4a{0u, 0u, 0u, 0u};
+    const uint8_t* xa = x_operand<GSHIFT, MB, kExact>(xl, zero, lr16, lg);
+    const int sel = fold_selector<GSHIFT, MB, kExact>(lg);
+    const uint64_t sel_hi = __builtin_amdgcn_ballot_w64(sel >= 2);
+    const ExactConsts ec = make_exact_consts();
     for (uint32_t t0 = r0; t0 < r1; t0 += MB) {
         if (t0 != r0) {
 #pragma unroll
             for (int r = 0; r < MB; ++r) xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min(t0 + r, r1 - 1) * k);
         }
 #pragma unroll
-        for (int r = 0; r < MB; ++r) *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = xg[r];
+        for (int r = 0; r < MB; ++r)
+            *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = kExact ? pair_order4(xg[r]) : xg[r];
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -361,19 +491,7 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(wq[t][c][i]) : "v"(acc[0]));
-            bf16x8 wb[NT][4];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const Dq dq = make_dq(sw[t].get(c, lg, g_hi), bw[t].get(c, lg, g_hi));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) wb[t][j] = dequant8m<BITS>(wq[t][c], j, dq);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(xa + 256 * c + 16 * j);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wb[t][j], acc[t], 0, 0, 0);
-            }
+            chunk_product<BITS, NT, GSHIFT, MB>(c, wq, sw, bw, xa, sel, sel_hi, ec, acc);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -384,9 +502,13 @@ __global__ __launch_bounds__(512) void gemv_mfma_gather_kernel(
         for (int o = tid; o < 16 * MB * NT; o += (int)blockDim.x) {
             const int t = o / (16 * MB), rem = o % (16 * MB);
             const int mm = rem >> 4, nn = rem & 15;
-            const int l = ((mm >> 2) << 4) | nn, v = mm & 3;
             float sum = 0.f;
-            for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+#pragma unroll
+            for (int p = 0; p < kBands; ++p) {
+                const int rr = p * MB + mm;
+                const int l = ((rr >> 2) << 4) | nn, v = rr & 3;
+                for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+            }
             const uint32_t r = t0 + (uint32_t)mm, col = n0 + 16 * t + (uint32_t)nn;
             if (r < r1 && col < n) yb[(size_t)r * n + col] = to_bf16_bits(sum);
         }
@@ -399,7 +521,8 @@ hipError_t launch_gather_nt(const uint16_t* x, int64_t m, const uint32_t* packed
                             const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, const Gather& ga,
                             hipStream_t stream) {
     const int waves = (int)(kb / 16);
-    const size_t lds = (size_t)waves * MB * kXPitch + (size_t)waves * NT * 4 * 64 * sizeof(float);
+    const size_t lds = (size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB> +
+                       (size_t)waves * NT * 4 * 64 * sizeof(float);
     const unsigned gx = (unsigned)((n + 16 * NT - 1) / (16 * NT));
     // grid y: output batches, or experts 0 .. w_count when grouped
     const uint64_t count = ga.grouped ? (uint64_t)ga.w_count + 1 : ga.batch;
@@ -422,7 +545,7 @@ hipError_t launch_gather_mb(const uint16_t* x, int64_t m, const uint32_t* packed
     // Row tiles per block as in the decode kernel: enough that the blocks with work fit in one
     // round of the compute units (a block's x regions set how many fit on one).
     const int64_t waves = kb / 16;
-    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch + waves * 4 * 1024);
+    int64_t per_cu = (int64_t)(160 * 1024) / (waves * MB * kXPitch + (int64_t)kZeroBytes<BITS, GSHIFT, MB> + waves * 4 * 1024);
     if (per_cu < 1) per_cu = 1;
     if (per_cu > 4) per_cu = 4;
     const int64_t slots = (int64_t)device_cu_count() * per_cu;

@@ -51,3 +51,20 @@ def at_offset(t, elements=1):
     view = big[elements:]
     view.copy_(flat)
     return view.view(t.shape)
+
+
+def mfma_rows_per_tile(rows):
+    """x rows per tile of the matrix-core decode and gathered kernels: rows rounded up to 4, 8 or 16."""
+    return 4 if rows <= 4 else 8 if rows <= 8 else 16
+
+
+def mfma_exact_codes(bits, G, rows):
+    """Whether those kernels multiply 4-bit codes exactly (scale and bias applied to each group's
+    sums, weights never rounded to bf16): a chunk's 4 >> log2(G / 32) groups each take a band of
+    the tile's rows among the 16 operand rows. Their own arithmetic is then the float32 oracle."""
+    return bits == 4 and (4 >> {32: 0, 64: 1, 128: 2}[G]) * mfma_rows_per_tile(rows) <= 16
+
+
+def grouped_rows_per_tile(batch, experts):
+    """The grouped walk's rows per tile: twice the mean rows per expert, rounded up."""
+    return (2 * batch + experts - 1) // max(experts, 1)

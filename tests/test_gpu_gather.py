@@ -4,15 +4,16 @@ through the C ABI (via the binding).
 Output batch i is x[lhs[i]] . dequantize(W[rhs[i]])^T. The bars are those of the plain product:
 per-row max relative error against the float64 oracle of at most 2e-3 (float32 y) and 1.6e-2
 (bf16 y), and the tighter bound from the kernel's own arithmetic (1e-4 / 4e-3) against the oracle
-composed the way the kernel computes: float32 weights for the VALU GEMV, weights rounded to bf16
-for the matrix-core kernel. An index past its operand gives a NaN batch on both sides.
+composed the way the kernel computes: float32 weights for the VALU GEMV and for the matrix-core
+kernel where it takes 4-bit codes exactly, weights rounded to bf16 for the matrix-core kernel
+otherwise and for the grouped GEMM. An index past its operand gives a NaN batch on both sides.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle as orc_mod
-from gpu_util import banner, dev_bf16, dev_u32, dev_x, host_f64
+from gpu_util import banner, dev_bf16, dev_u32, dev_x, grouped_rows_per_tile, host_f64, mfma_exact_codes
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -69,8 +70,9 @@ def run(x, x_dtype, packed, scales, biases, G, bits, lhs=None, rhs=None, sorted_
     return host_f64(y)
 
 
-def check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, kernel):
-    """got [batch, m, n] against the oracle; lhs/rhs are the explicit (expanded) index arrays."""
+def check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, kernel, grouped=False):
+    """got [batch, m, n] against the oracle; lhs/rhs are the explicit (expanded) index arrays;
+    grouped: the matrix-core kernel walked sorted rows by expert (rows per tile from the mean count)."""
     ref = orc.gather_qmm(x, x_dtype, packed, scales, biases, G, bits, lhs=lhs, rhs=rhs)
     assert got.shape == ref.shape
     nan = np.isnan(ref).all(axis=(1, 2))
@@ -82,7 +84,8 @@ def check(orc, got, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs, kerne
         return
     err = orc.max_row_rel_err(g2, r2)
     assert err <= TOL[x_dtype], f"max row rel err {err:.3e} > {TOL[x_dtype]}"
-    if kernel == "gemv_mfma":
+    rows = grouped_rows_per_tile(got.shape[0], packed.shape[0]) if grouped else got.shape[1]
+    if kernel == "gemv_mfma" and not mfma_exact_codes(bits, G, rows):
         tref = bf16_weight_gather_ref(orc, x, x_dtype, packed, scales, biases, G, bits, lhs, rhs)
         tref = tref[~nan].reshape(-1, ref.shape[-1])
     else:
@@ -159,10 +162,15 @@ def test_gather_mfma_grouped(orc, bits, G, k, counts):
     banner(f"gather mfma grouped bits={bits} G={G} k={k} counts={counts}")
     got = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemv_mfma")
     check(orc, got, x, "bf16", packed, scales, biases, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs,
-          "gemv_mfma")
-    # the grouped walk and the batched kernel compute each row the same way
+          "gemv_mfma", grouped=True)
     got_b = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=False, path="gemv_mfma")
-    np.testing.assert_array_equal(got, got_b)
+    if mfma_exact_codes(bits, G, grouped_rows_per_tile(rhs.size, E)) == mfma_exact_codes(bits, G, 1):
+        # the grouped walk and the batched kernel compute each row the same way
+        np.testing.assert_array_equal(got, got_b)
+    else:
+        # the batched kernel (one row per tile) takes the codes exactly, the grouped walk does not
+        check(orc, got_b, x, "bf16", packed, scales, biases, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs,
+              "gemv_mfma")
 
 
 def test_gather_grouped_rows_past_every_expert_are_nan(orc):
@@ -173,7 +181,7 @@ def test_gather_grouped_rows_past_every_expert_are_nan(orc):
     banner("gather mfma grouped, rows past every expert")
     got = run(x, "bf16", packed, scales, biases, G, bits, None, rhs, sorted_=True, path="gemv_mfma")
     check(orc, got, x, "bf16", packed, scales, biases, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs,
-          "gemv_mfma")
+          "gemv_mfma", grouped=True)
     assert np.isnan(got[5:]).all() and np.isfinite(got[:5]).all()
 
 
@@ -327,7 +335,7 @@ def test_gather_moe_workload(orc, tokens):
               sorted_=True)
     grouped = mi.expert.size >= wl.experts
     check(orc, got, mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits,
-          np.arange(mi.expert.size, dtype=np.uint32), mi.expert, "gemv_mfma" if grouped else "gemv")
+          np.arange(mi.expert.size, dtype=np.uint32), mi.expert, "gemv_mfma" if grouped else "gemv", grouped=grouped)
     # the same rows through lhs indices (token of each row) into the unpermuted activations
     got2 = run(mi.x[:, None, :], "bf16", mi.packed, mi.scales, mi.biases, wl.group_size, wl.bits, mi.token,
                mi.expert)

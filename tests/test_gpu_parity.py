@@ -9,7 +9,8 @@ Bars:
   bars above would let through. Its reference is the oracle's own pieces composed the way the kernel
   computes: the VALU GEMV uses the float32 weights (the oracle as is), the two MFMA kernels (GEMM
   and matrix-core decode) their weights rounded to bf16 (the oracle's bf16 dequantization, then a
-  float64 matmul). What is left is float32
+  float64 matmul), except where the matrix-core decode kernel takes 4-bit codes exactly (scale and
+  bias applied to each group's sums: the oracle as is). What is left is float32
   summation order (~1e-6 relative) and, for a bf16 y, one rounding of each output to nearest even:
   bf16 keeps 8 significant bits, so that rounding moves y by at most 2^-8 = 3.91e-3 of |y| <=
   max|ref|. Bound: 4e-3 for bf16 y, 1e-4 for float32 y.
@@ -19,7 +20,7 @@ import pytest
 import torch
 
 import oracle as orc_mod
-from gpu_util import at_offset, banner, dev_weights, dev_x, host_bits, host_f64
+from gpu_util import at_offset, banner, dev_weights, dev_x, host_bits, host_f64, mfma_exact_codes
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -93,8 +94,11 @@ def check_qmm(orc, inp, y, rows=None, path="auto"):
     err = orc.max_row_rel_err(got, ref)
     kind = inp.x_dtype
     assert err <= TOL[kind], f"max row rel err {err:.3e} > {TOL[kind]}"
-    # both MFMA kernels multiply bf16-rounded weights
-    tight_ref = bf16_weight_ref(orc, inp, x) if kernel_of(inp, path) != "gemv" else ref
+    # both MFMA kernels multiply bf16-rounded weights, except the matrix-core decode kernel with
+    # exact 4-bit codes
+    kernel = kernel_of(inp, path)
+    exact = kernel == "gemv_mfma" and mfma_exact_codes(wl.bits, wl.group_size, inp.x.shape[0])
+    tight_ref = ref if kernel == "gemv" or exact else bf16_weight_ref(orc, inp, x)
     terr = orc.max_row_rel_err(got, tight_ref)
     assert terr <= TIGHT[kind], f"{kernel_of(inp, path)}: max row rel err {terr:.3e} against its " \
                                 f"own arithmetic, above {TIGHT[kind]}"
@@ -314,6 +318,19 @@ def test_gemv_mfma_row_tiles(orc, bits, n):
 def test_gemv_mfma_row_tiles_groups(orc, G, n):
     inp = W.random_inputs(4, G, n, 4096, 16, seed=n + G)
     banner(f"gemv_mfma row tiles G={G} n={n}")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
+# Exact 4-bit codes in bands of the operand rows, at 2, 3 and 4 tiles per block: with K = 4096 a
+# block of 4 x rows (34 KB of LDS) fits 4 times on a compute unit and one of 8 rows (67 KB) twice,
+# so on 256 compute units these n take 2, 3, 4 (m = 4) and 2, 3, 4 (m = 8) tiles.
+@pytest.mark.parametrize("G,m,n", [(32, 4, 16400), (32, 4, 33000), (64, 4, 49200),
+                                   (64, 8, 8200), (64, 8, 16400), (128, 8, 24600)])
+def test_gemv_mfma_exact_codes_row_tiles(orc, G, m, n):
+    assert mfma_exact_codes(4, G, m)
+    inp = W.random_inputs(4, G, n, 4096, m, seed=n + G + m)
+    banner(f"gemv_mfma exact codes G={G} m={m} n={n}")
     y = run_qmm(inp, path="gemv_mfma")
     check_qmm(orc, inp, y, path="gemv_mfma")
 
