@@ -94,12 +94,17 @@ def _load():
                                   _i64, _int, _f64p]
     lib.orc_qmm_nt.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _f64p]
     lib.orc_quantize.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, _u16p, _u16p]
+    lib.orc_quantize_typed.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, ctypes.c_void_p,
+                                       ctypes.c_void_p, _int]
+    lib.orc_gather_qmm_typed.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _u32p, ctypes.c_void_p, ctypes.c_void_p,
+                                         _int, _i64, _i64, _i64, _i64, _int, ctypes.c_void_p, ctypes.c_void_p, _i64,
+                                         _f64p]
     lib.orc_silu_gate.argtypes = [_u16p, _u16p, _i64, _f64p]
     lib.orc_silu_gate_qmm.argtypes = [_u16p, _u16p, ctypes.c_void_p, _i64, _u32p, _u16p, _u16p, _i64,
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
                  "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize", "orc_qmm_nt",
-                 "orc_dequantize_typed", "orc_qmm_typed"):
+                 "orc_dequantize_typed", "orc_qmm_typed", "orc_quantize_typed", "orc_gather_qmm_typed"):
         getattr(lib, name).restype = _int
     for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate", "orc_f16_to_f32", "orc_f32_to_f16"):
         getattr(lib, name).restype = None
@@ -326,23 +331,23 @@ def gather_qmm(x, x_dtype: str, packed, scales, biases, group_size: int, bits: i
     return out.reshape(tuple(shape) + (m, n))
 
 
-def quantize(w, w_dtype: str, group_size: int, bits: int):
-    """(packed uint32 [rows, cols*bits/32], scales bf16 bits [rows, cols/G], biases bf16 bits) of a
-    [rows, cols] weight given as float32 (``w_dtype="f32"``) or bf16 bit patterns ("bf16")."""
-    if w_dtype == "bf16":
-        wa = _c(np.atleast_2d(w), np.uint16)
-    elif w_dtype == "f32":
-        wa = _c(np.atleast_2d(w), np.float32)
-    else:
-        raise ValueError(w_dtype)
+def quantize(w, w_dtype: str, group_size: int, bits: int, sb_dtype: str = "bf16"):
+    """(packed uint32 [rows, cols*bits/32], scales [rows, cols/G], biases [rows, cols/G]) of a
+    [rows, cols] weight given as float32 (``w_dtype="f32"``) or bf16 / float16 bit patterns
+    ("bf16", "f16"); scales and biases in ``sb_dtype`` (float32, or bf16 / float16 bit patterns;
+    nuvec_core's rule is w's own dtype)."""
+    wa = _typed(np.atleast_2d(w), w_dtype)
+    if w_dtype not in DTYPES or sb_dtype not in DTYPES:
+        raise ValueError((w_dtype, sb_dtype))
     rows, cols = wa.shape
     if group_size <= 0 or cols % group_size or (cols * bits) % 32:
         raise ValueError("cols must be a multiple of the group size")
     packed = np.empty((rows, cols * bits // 32), np.uint32)
-    sc = np.empty((rows, cols // group_size), np.uint16)
-    bi = np.empty((rows, cols // group_size), np.uint16)
-    _check(_load().orc_quantize(wa.ctypes.data, 1 if w_dtype == "bf16" else 0, rows, cols, group_size, bits,
-                                packed, sc, bi), "quantize")
+    sbt = np.float32 if sb_dtype == "f32" else np.uint16
+    sc = np.empty((rows, cols // group_size), sbt)
+    bi = np.empty((rows, cols // group_size), sbt)
+    _check(_load().orc_quantize_typed(wa.ctypes.data, DTYPES[w_dtype], rows, cols, group_size, bits, packed,
+                                      sc.ctypes.data, bi.ctypes.data, DTYPES[sb_dtype]), "quantize")
     return packed, sc, bi
 
 
@@ -397,6 +402,30 @@ def qmm_typed(x, x_dtype: str, packed, scales, biases, sb_dtype: str, group_size
     _check(_load().orc_qmm_typed(xa.ctypes.data, DTYPES[x_dtype], m, packed, sc.ctypes.data, bi.ctypes.data,
                                  DTYPES[sb_dtype], n, k, group_size, bits, out), "qmm_typed")
     return out
+
+
+def gather_qmm_typed(x, x_dtype: str, packed, scales, biases, sb_dtype: str, group_size: int, bits: int,
+                     lhs=None, rhs=None) -> np.ndarray:
+    """gather_qmm with x and the scales/biases of any of the three types: output batch i is
+    qmm_typed of x batch lhs[i] against weight batch rhs[i] in float64 (NaN past either operand),
+    shape broadcast(batch) + [m, n]."""
+    xa = _typed(x, x_dtype)
+    packed = _c(packed, np.uint32)
+    sc, bi = _typed(scales, sb_dtype), _typed(biases, sb_dtype)
+    if xa.ndim < 2 or packed.ndim < 2 or sc.shape != bi.shape:
+        raise ValueError("x must be [..., m, k] and w [..., n, k*bits/32]")
+    m, k = xa.shape[-2:]
+    n = packed.shape[-2]
+    if packed.shape[-1] * 32 != k * bits:
+        raise ValueError("x columns do not match the packed width")
+    li, ri, shape = gather_indices(xa.shape[:-2], packed.shape[:-2], lhs, rhs)
+    xb = int(np.prod(xa.shape[:-2], dtype=np.int64))
+    wb = int(np.prod(packed.shape[:-2], dtype=np.int64))
+    out = np.empty((li.size, m, n), np.float64)
+    _check(_load().orc_gather_qmm_typed(xa.ctypes.data, DTYPES[x_dtype], xb, m, packed.reshape(-1), sc.ctypes.data,
+                                        bi.ctypes.data, DTYPES[sb_dtype], wb, n, k, group_size, bits, li.ctypes.data,
+                                        ri.ctypes.data, li.size, out), "gather_qmm_typed")
+    return out.reshape(tuple(shape) + (m, n))
 
 
 def max_row_rel_err(y: np.ndarray, ref: np.ndarray) -> float:

@@ -375,62 +375,6 @@ static int sign_of_sum3(double a, double b, double c) {
     return (h1 > 0.0) - (h1 < 0.0);
 }
 
-/* [nuvec] quantize with [moshi]'s bias: each group of G values of a row, in the pages' order:
- *   bias  = the group minimum; scale = (max - min) / (2^bits - 1): the statistics in float32,
- *   both stored as bf16 (round to nearest even), the dtype the kernels consume;
- *   code  = round((w - bias) / scale) with the stored bias and scale, the value of the formula
- *           itself (no intermediate rounding of the difference or the quotient), rounded half away
- *           from zero (the Rust `round` of the page) and clamped to [0, 2^bits - 1]; a group whose
- *           stored scale is 0 (all values equal) takes code 0, so it dequantizes to the bias
- *           exactly.
- * For a positive scale, code c >= 0 is the rounded quotient exactly when
- *     (c - 1/2) * scale <= w - bias < (c + 1/2) * scale,
- * which is decided by the exact sign of w - bias - (c +- 1/2) * scale (each (c +- 1/2) * scale has
- * at most 9 + 8 significant bits, exact in double). A double estimate is stepped until both hold.
- * Codes are packed into the row's bit stream one bit at a time (orc_pack_codes).
- * Returns 0, or -1 for parameters outside the format. */
-static double quantize_code(float w, float bias, float scale, double top) {
-    if (scale == 0.0f) return 0.0;
-    double c = floor(((double)w - (double)bias) / (double)scale + 0.5);
-    if (!(c >= 0.0)) c = 0.0; /* also a NaN estimate */
-    if (c > top + 1.0) c = top + 1.0;
-    while (c > 0.0 && sign_of_sum3(w, -(double)bias, -(c - 0.5) * (double)scale) < 0) c -= 1.0;
-    while (c <= top && sign_of_sum3(w, -(double)bias, -(c + 0.5) * (double)scale) >= 0) c += 1.0;
-    return c > top ? top : c;
-}
-
-int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64_t group, int bits,
-                 uint32_t* packed, uint16_t* scales, uint16_t* biases) {
-    if (rows < 0 || bits > 8 || group > 128 || !valid_params(cols, group, bits)) return -1;
-    uint8_t* codes = (uint8_t*)malloc((size_t)(rows * cols > 0 ? rows * cols : 1));
-    if (!codes) return -2;
-    const float top = (float)((1 << bits) - 1);
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t g = 0; g < cols / group; ++g) {
-            float v[128];
-            for (int64_t j = 0; j < group; ++j) {
-                const int64_t i = r * cols + g * group + j;
-                v[j] = w_is_bf16 ? bf16_to_f32(((const uint16_t*)w)[i]) : ((const float*)w)[i];
-            }
-            float lo = v[0], hi = v[0];
-            for (int64_t j = 1; j < group; ++j) {
-                if (v[j] < lo) lo = v[j];
-                if (v[j] > hi) hi = v[j];
-            }
-            const float range = hi - lo;
-            const uint16_t sb = f32_to_bf16_rne(range / top);
-            const uint16_t bb = f32_to_bf16_rne(lo);
-            scales[r * (cols / group) + g] = sb;
-            biases[r * (cols / group) + g] = bb;
-            const float sc = bf16_to_f32(sb), bi = bf16_to_f32(bb);
-            for (int64_t j = 0; j < group; ++j)
-                codes[r * cols + g * group + j] = (uint8_t)quantize_code(v[j], bi, sc, (double)top);
-        }
-    const int rc = orc_pack_codes(codes, rows, cols, bits, packed);
-    free(codes);
-    return rc;
-}
-
 /* [nuvec] quantized_matmul without the transpose: y = x . dequantize(w), for a weight stored
  * [k, n] (its rows are the k index, each a bit stream of n codes in groups of G along n):
  *     y[m, n] = sum over k of x[m, k] * w[k, n]
@@ -553,5 +497,110 @@ int orc_qmm_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed,
             out[mm * n + nn] = acc;
         }
     free(w);
+    return 0;
+}
+
+/* [nuvec] quantize (module documentation and `quantize`: float16, bfloat16 or float32 w; scales and
+ * biases in w's dtype) with [moshi]'s bias: each group of G values of a row, in the pages' order:
+ *   bias  = the group minimum; scale = (max - min) / (2^bits - 1): the statistics in float32 (w
+ *           widened exactly), both stored in sb_dtype (float32 as is; bf16 or float16 rounded to
+ *           nearest even). nuvec_core's rule is sb_dtype = w's dtype; orc_quantize stores bf16, the
+ *           type every kernel here consumes;
+ *   code  = round((w - bias) / scale) with the stored bias and scale, the value of the formula
+ *           itself (no intermediate rounding of the difference or the quotient), rounded half away
+ *           from zero (the Rust `round` of the page) and clamped to [0, 2^bits - 1]; a group whose
+ *           stored scale is 0 (all values equal, or a range below the narrower type's least value)
+ *           takes code 0, so it dequantizes to the bias.
+ * For a positive scale, code c >= 0 is the rounded quotient exactly when
+ *     (c - 1/2) * scale <= w - bias < (c + 1/2) * scale,
+ * which is decided by the exact sign of w - bias - (c +- 1/2) * scale (each (c +- 1/2) * scale has
+ * at most 9 + 24 significant bits, exact in double). A double estimate is stepped until both hold.
+ * A stored scale or bias that is not finite (an input that is not, or a statistic past the
+ * narrower type's range) leaves the codes unspecified. Codes are packed into the row's bit stream
+ * one bit at a time (orc_pack_codes). Returns 0, or -1 for parameters outside the format. */
+static double quantize_code(float w, float bias, float scale, double top) {
+    if (scale == 0.0f) return 0.0;
+    double c = floor(((double)w - (double)bias) / (double)scale + 0.5);
+    if (!(c >= 0.0)) c = 0.0; /* also a NaN estimate */
+    if (c > top + 1.0) c = top + 1.0;
+    while (c > 0.0 && sign_of_sum3(w, -(double)bias, -(c - 0.5) * (double)scale) < 0) c -= 1.0;
+    while (c <= top && sign_of_sum3(w, -(double)bias, -(c + 0.5) * (double)scale) >= 0) c += 1.0;
+    return c > top ? top : c;
+}
+
+/* v stored as dtype (float32 as is, bf16 / float16 rounded to nearest even) and read back. */
+static float store_typed(void* p, int64_t i, int dtype, float v) {
+    if (dtype == 1) {
+        ((uint16_t*)p)[i] = f32_to_bf16_rne(v);
+        return bf16_to_f32(((uint16_t*)p)[i]);
+    }
+    if (dtype == 2) {
+        ((uint16_t*)p)[i] = f32_to_f16_rne(v);
+        return f16_to_f32(((uint16_t*)p)[i]);
+    }
+    ((float*)p)[i] = v;
+    return v;
+}
+
+int orc_quantize_typed(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t group, int bits,
+                       uint32_t* packed, void* scales, void* biases, int sb_dtype) {
+    if (rows < 0 || bits > 8 || group > 128 || !valid_params(cols, group, bits)) return -1;
+    if (w_dtype < 0 || w_dtype > 2 || sb_dtype < 0 || sb_dtype > 2) return -1;
+    uint8_t* codes = (uint8_t*)malloc((size_t)(rows * cols > 0 ? rows * cols : 1));
+    if (!codes) return -2;
+    const float top = (float)((1 << bits) - 1);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < cols / group; ++g) {
+            float v[128];
+            for (int64_t j = 0; j < group; ++j) v[j] = widen(w, r * cols + g * group + j, w_dtype);
+            float lo = v[0], hi = v[0];
+            for (int64_t j = 1; j < group; ++j) {
+                if (v[j] < lo) lo = v[j];
+                if (v[j] > hi) hi = v[j];
+            }
+            const float range = hi - lo;
+            const int64_t gi = r * (cols / group) + g;
+            const float sc = store_typed(scales, gi, sb_dtype, range / top);
+            const float bi = store_typed(biases, gi, sb_dtype, lo);
+            for (int64_t j = 0; j < group; ++j)
+                codes[r * cols + g * group + j] = (uint8_t)quantize_code(v[j], bi, sc, (double)top);
+        }
+    const int rc = orc_pack_codes(codes, rows, cols, bits, packed);
+    free(codes);
+    return rc;
+}
+
+/* orc_quantize_typed with float32 or bf16 w and bf16 scales and biases. */
+int orc_quantize(const void* w, int w_is_bf16, int64_t rows, int64_t cols, int64_t group, int bits,
+                 uint32_t* packed, uint16_t* scales, uint16_t* biases) {
+    return orc_quantize_typed(w, w_is_bf16 ? 1 : 0, rows, cols, group, bits, packed, scales, biases, 1);
+}
+
+/* [nuvec] gather_qmm (transpose form) with x and the scales and biases of any of the three types:
+ * output batch i is orc_qmm_typed of x batch lhs[i] against weight batch rhs[i] (each defaulting
+ * to i when null); an index past its operand gives a NaN batch. x [x_batches, m, k], packed
+ * [w_batches, n, k*bits/32], scales/biases [w_batches, n, k/group]; out double [batch, m, n]. */
+int orc_gather_qmm_typed(const void* x, int x_dtype, int64_t x_batches, int64_t m, const uint32_t* packed,
+                         const void* scales, const void* biases, int sb_dtype, int64_t w_batches, int64_t n,
+                         int64_t k, int64_t group, int bits, const uint32_t* lhs, const uint32_t* rhs,
+                         int64_t batch, double* out) {
+    if (batch < 0 || m < 0 || n < 0 || x_dtype < 0 || x_dtype > 2 || sb_dtype < 0 || sb_dtype > 2) return -1;
+    if (!valid_params(k, group, bits)) return -1;
+    const int64_t xsize = x_dtype == 0 ? 4 : 2, sbsize = sb_dtype == 0 ? 4 : 2;
+    const int64_t words = k * bits / 32, groups = k / group;
+    for (int64_t i = 0; i < batch; ++i) {
+        const int64_t li = lhs ? (int64_t)lhs[i] : i;
+        const int64_t ri = rhs ? (int64_t)rhs[i] : i;
+        double* yi = out + i * m * n;
+        if (li >= x_batches || ri >= w_batches) {
+            for (int64_t t = 0; t < m * n; ++t) yi[t] = NAN;
+            continue;
+        }
+        const int rc = orc_qmm_typed((const uint8_t*)x + li * m * k * xsize, x_dtype, m, packed + ri * n * words,
+                                     (const uint8_t*)scales + ri * n * groups * sbsize,
+                                     (const uint8_t*)biases + ri * n * groups * sbsize, sb_dtype, n, k, group,
+                                     bits, yi);
+        if (rc != 0) return rc;
+    }
     return 0;
 }

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from conftest import golden
-from near_ties import bf16_rne, near_tie_groups, tie_example
+from near_ties import bf16_rne, bf16_value, f16_value, f32_value, near_tie_groups, tie_example
 from quantized_matmul_mlx_amd import workloads as W
 
 
@@ -791,3 +791,151 @@ def test_qmm_typed_reduces_to_qmm(oracle_lib):
     w = oracle_lib.dequantize_typed(inp.packed, s16, b16, "f16", 64, 4).astype(np.float64)
     y = oracle_lib.qmm_typed(xf, "f32", inp.packed, s16, b16, "f16", 64, 4)
     np.testing.assert_allclose(y, xf.astype(np.float64) @ w.T, rtol=1e-12, atol=1e-12)
+
+
+# ---- quantize with float16 / float32 weights, scales and biases ----------------------------------
+
+_TYPE = {"f32": np.float32, "bf16": None, "f16": np.float16}
+
+
+def _as_type(w32, dt):
+    """float32 values (exact in dt) as the oracle's input for dtype dt."""
+    if dt == "f32":
+        return w32.astype(np.float32)
+    if dt == "f16":
+        return w32.astype(np.float16).view(np.uint16)
+    return W.bf16_bits_from_f32(w32)
+
+
+def _widen(a, dt):
+    """An oracle array of dtype dt as float64, widened by numpy and torch (not the oracle)."""
+    if dt == "f32":
+        return a.astype(np.float64)
+    if dt == "f16":
+        return a.view(np.float16).astype(np.float64)
+    return W.f32_from_bf16_bits(a).astype(np.float64)
+
+
+def _exact_codes_f(w64, s64, b64, G, bits):
+    """round((w - bias) / scale) clamped, each quotient an exact rational (Fraction)."""
+    top = 2 ** bits - 1
+    out = np.zeros(w64.shape, np.int64)
+    for r in range(w64.shape[0]):
+        for j in range(w64.shape[1]):
+            sg, bg = s64[r, j // G], b64[r, j // G]
+            if sg == 0.0:
+                continue
+            c = _round_half_away((Fraction(float(w64[r, j])) - Fraction(float(bg))) / Fraction(float(sg)))
+            out[r, j] = min(max(c, 0), top)
+    return out
+
+
+@pytest.mark.parametrize("w_dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("sb_dt", ["f32", "bf16", "f16"])
+def test_quantize_typed_exact_grid(oracle_lib, w_dt, sb_dt):
+    # values base + step * c, exact in every type, both extreme codes present: the scale is step and
+    # the bias base in the scales' own type, and the codes come back (nuvec_core: scales and biases
+    # in w's dtype; any of the three here)
+    G, bits, step, base = 32, 4, 0.125, -1.5
+    rng = np.random.default_rng(41)
+    codes = rng.integers(0, 16, size=(3, 2 * G)).astype(np.uint8)
+    codes[:, 0], codes[:, 1], codes[:, G], codes[:, G + 1] = 0, 15, 15, 0
+    w32 = (base + step * codes.astype(np.float64)).astype(np.float32)
+    packed, sc, bi = oracle_lib.quantize(_as_type(w32, w_dt), w_dt, G, bits, sb_dt)
+    assert sc.dtype == (np.float32 if sb_dt == "f32" else np.uint16)
+    assert np.all(_widen(sc, sb_dt) == step) and np.all(_widen(bi, sb_dt) == base)
+    np.testing.assert_array_equal(oracle_lib.unpack_codes(packed, 2 * G, bits), codes)
+
+
+@pytest.mark.parametrize("w_dt,sb_dt", [("f32", "f32"), ("f16", "f16"), ("f32", "f16"), ("bf16", "f16"),
+                                        ("f16", "f32"), ("f16", "bf16")])
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128)])
+def test_quantize_typed_codes_are_exact_rational_rounding(oracle_lib, w_dt, sb_dt, bits, G):
+    # values within a few ulps of the boundaries of the stored scale and bias: every code is the
+    # exact rational rounding of (w - bias) / scale, and the scales and biases are the roundings of
+    # the float32 statistics to their type (numpy's float16 conversion, torch's bf16 one)
+    rows = 12
+    stored = {"f32": f32_value, "bf16": bf16_value, "f16": f16_value}[sb_dt]
+    w_type = np.float16 if w_dt == "f16" else np.float32
+    w = near_tie_groups(rows, 2, G, bits, seed=300 + bits, w_type=w_type, stored=stored)
+    wf = w.astype(np.float32)
+    if w_dt == "bf16":
+        wi = bf16_rne(wf)
+        wf = W.f32_from_bf16_bits(wi)
+    else:
+        wi = w if w_dt == "f32" else w.view(np.uint16)
+    packed, sc, bi = oracle_lib.quantize(wi, w_dt, G, bits, sb_dt)
+    wg = wf.reshape(rows, -1, G)
+    lo, hi = wg.min(-1), wg.max(-1)
+    q = (hi - lo) / np.float32(2 ** bits - 1)
+    np.testing.assert_array_equal(_widen(sc, sb_dt), stored(q).astype(np.float64))
+    np.testing.assert_array_equal(_widen(bi, sb_dt), stored(lo).astype(np.float64))
+    codes = oracle_lib.unpack_codes(packed, 2 * G, bits).astype(np.int64)
+    np.testing.assert_array_equal(codes, _exact_codes_f(wf.astype(np.float64), _widen(sc, sb_dt),
+                                                        _widen(bi, sb_dt), G, bits))
+
+
+def test_quantize_float32_scale_exact_quotient_below_a_tie(oracle_lib):
+    # With a float32 scale, (k + 1/2) * scale needs more than 24 bits, so a float32 value can sit
+    # just below it while its float32 quotient lands on the tie: scale 1 + 2^-20 (min 0, max 15 *
+    # scale, exact in float32), w = fl32((k + 1/2) * scale) rounded down. The exact quotient is
+    # below k + 1/2 and rounds to k; rounding the float32 quotient would give k + 1.
+    s = np.float32(1.0 + 2.0 ** -20)
+    lo, hi = np.float32(0.0), np.float32(15.0 * (1.0 + 2.0 ** -20))
+    assert float(hi) == 15.0 * (1.0 + 2.0 ** -20) and np.float32(hi / np.float32(15)) == s
+    picks = []
+    for k in range(15):
+        exact = Fraction(2 * k + 1, 2) * Fraction(float(s))
+        v = np.float32(float(exact))
+        if Fraction(float(v)) > exact:
+            v = np.nextafter(v, np.float32(-np.inf))
+        assert Fraction(float(v)) < exact
+        if float(np.float32(v / s)) == k + 0.5:
+            picks.append((k, v))
+    assert len(picks) >= 3
+    w = np.full((1, 32), lo, np.float32)
+    w[0, 1] = hi
+    for i, (k, v) in enumerate(picks[:8]):
+        w[0, 2 + i] = v
+    packed, sc, bi = oracle_lib.quantize(w, "f32", 32, 4, "f32")
+    assert sc[0, 0] == s and bi[0, 0] == 0.0
+    codes = oracle_lib.unpack_codes(packed, 32, 4)[0]
+    assert [int(codes[2 + i]) for i in range(len(picks[:8]))] == [k for k, _ in picks[:8]]
+
+
+# ---- gathered products with float16 / float32 x, scales and biases -------------------------------
+
+def test_gather_qmm_typed_against_numpy(oracle_lib):
+    # batch i: x[lhs[i]] . dequantize_typed(W[rhs[i]])^T (the typed dequantization is pinned above)
+    # in numpy float64, NaN past either operand, for a float16 x and float32 / float16 scales
+    E, n, k, G, bits, m = 3, 10, 128, 32, 5, 2
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=51)
+    packed = inp.packed.reshape(E, n, -1)
+    rng = np.random.default_rng(52)
+    x32 = rng.standard_normal((4, m, k)).astype(np.float16).astype(np.float32)
+    lhs = np.array([0, 3, 2, 4, 1], np.uint32)
+    rhs = np.array([2, 0, 1, 1, 5], np.uint32)
+    s32 = rng.uniform(1e-3, 2e-2, (E, n, k // G)).astype(np.float32)
+    b32 = rng.uniform(-0.2, 0.0, (E, n, k // G)).astype(np.float32)
+    for x_dt, sb_dt in (("f16", "f32"), ("f16", "f16"), ("f32", "f16"), ("bf16", "f32")):
+        sc, bi = _as_type(s32, sb_dt), _as_type(b32, sb_dt)
+        xi = _as_type(x32, x_dt)
+        got = oracle_lib.gather_qmm_typed(xi, x_dt, packed, sc, bi, sb_dt, G, bits, lhs=lhs, rhs=rhs)
+        assert got.shape == (5, m, n)
+        for i, (li, ri) in enumerate(zip(lhs, rhs)):
+            if li >= 4 or ri >= E:
+                assert np.isnan(got[i]).all()
+                continue
+            w = oracle_lib.dequantize_typed(packed[ri], sc[ri], bi[ri], sb_dt, G, bits).astype(np.float64)
+            np.testing.assert_allclose(got[i], _widen(xi[li], x_dt) @ w.T, rtol=1e-12, atol=1e-12)
+
+
+def test_gather_qmm_typed_reduces_to_gather_qmm(oracle_lib):
+    # bf16 scales and a float32 or bf16 x: the plain gathered product
+    E, n, k, G, bits = 4, 12, 256, 64, 4
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=53)
+    p, sc, bi = (a.reshape(E, n, -1) for a in (inp.packed, inp.scales, inp.biases))
+    x = W.bf16_bits_from_f32(np.random.default_rng(54).standard_normal((3, 2, k)).astype(np.float32))
+    lhs, rhs = np.array([2, 0, 1, 2], np.uint32), np.array([3, 3, 0, 1], np.uint32)
+    np.testing.assert_array_equal(oracle_lib.gather_qmm_typed(x, "bf16", p, sc, bi, "bf16", G, bits, lhs, rhs),
+                                  oracle_lib.gather_qmm(x, "bf16", p, sc, bi, G, bits, lhs=lhs, rhs=rhs))
