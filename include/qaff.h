@@ -78,7 +78,8 @@ qaff_status qaff_dequantize(const uint32_t* packed, const uint16_t* scales, cons
 /*
  * Other float types (nuvec_core quantized.rs: quantized_matmul and dequantize promote x, scales and
  * biases to one float type; scales keep the weight's dtype). QAFF_F16 is accepted only by the
- * *_typed entry points below; every other entry point takes float32 or bf16 x and bf16 scales.
+ * *_typed entry points and as qaff_quantize's w; every other entry point takes float32 or bf16 x
+ * and bf16 scales.
  *
  * qaff_promote_dtype: the common type of two dtypes, as y's dtype: equal types stay, anything
  * else (float32 with anything, bf16 with float16) is float32.
@@ -116,22 +117,35 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
  * and quantize; rlx-moshi mlx_dequant.rs: the bias is the group minimum). Per group of group_size
  * values of a row:
  *   bias  = the group minimum; scale = (max - min) / (2^bits - 1); both stored as bf16 (round to
- *           nearest even), the scales' type every kernel here consumes;
+ *           nearest even), the scales' type every kernel here consumes (qaff_quantize_typed stores
+ *           them in another type);
  *   code  = round((w - bias) / scale) with the stored bias and scale, half away from zero, clamped
  *           to [0, 2^bits - 1]; a stored scale of 0 (all values of the group equal) gives code 0,
  *           so such a group dequantizes to its value exactly.
- * The minimum, maximum, max - min and its quotient by 2^bits - 1 are float32 (w widened exactly
- * from bf16) before the bf16 rounding. The code is the rounding of the exact value of
- * (w - bias) / scale: neither the difference nor the quotient is rounded to float32 first. NaN or
- * infinite inputs give unspecified (but in-range) codes.
- *   w [rows, cols] in w_dtype (float32 or bf16); packed uint32 [rows, cols*bits/32]; scales and
- *   biases bf16 [rows, cols/group_size]. All caller-owned device buffers.
+ * The minimum, maximum, max - min and its quotient by 2^bits - 1 are float32 (w widened exactly)
+ * before the rounding to the stored type. The code is the rounding of the exact value of
+ * (w - bias) / scale: neither the difference nor the quotient is rounded first. NaN or infinite
+ * inputs, or a stored scale or bias that is not finite (past the stored type's range), give
+ * unspecified (but in-range) codes.
+ *   w [rows, cols] in w_dtype (float32, bf16 or float16); packed uint32 [rows, cols*bits/32];
+ *   scales and biases bf16 [rows, cols/group_size]. All caller-owned device buffers.
  * Errors: as qaff_dequantize (the outputs are checked as a weight), plus INVALID_ARGUMENT for a
  * null w, or one not aligned to its element size, where the size is non-zero.
  */
 qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols,
                           int32_t group_size, int32_t bits, uint32_t* packed, uint16_t* scales,
                           uint16_t* biases, hipStream_t stream);
+
+/*
+ * qaff_quantize with the scales and biases stored as sb_dtype (float32 as is, bf16 or float16
+ * rounded to nearest even): nuvec_core quantized.rs, quantize, returns them in w's own dtype
+ * (sb_dtype = w_dtype). The codes follow the same rule with the values so stored.
+ *   scales and biases [rows, cols/group_size] of sb_dtype, aligned to its element size.
+ * Errors: as qaff_quantize, plus INVALID_ARGUMENT for an unknown dtype.
+ */
+qaff_status qaff_quantize_typed(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols,
+                                int32_t group_size, int32_t bits, uint32_t* packed, void* scales,
+                                void* biases, qaff_dtype sb_dtype, hipStream_t stream);
 
 /*
  * Quantized matmul y = x . dequantize(W)^T without materialising W (nuvec_core quantized_matmul with
@@ -283,6 +297,24 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
                             int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
                             const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
                             int32_t sorted_indices, void* y, hipStream_t stream);
+
+/*
+ * qaff_gather_qmm with x and the scales and biases of any of the three types (nuvec_core
+ * quantized.rs, gather_qmm: x, scales and biases promote to one float type): y [batch, m, n] of
+ * qaff_promote_dtype(x_dtype, sb_dtype); float32 sums.
+ *   scales and biases [w_batches, n, k/group_size] of sb_dtype (float32 4-byte aligned); the other
+ *   arguments as qaff_gather_qmm. bf16 scales with a float32 or bf16 x take qaff_gather_qmm itself
+ *   (the same kernels and results); every other combination runs on the typed VALU GEMV with grid z
+ *   over the output batches (x 16-byte aligned; otherwise element by element). The sorted promise
+ *   is used only by qaff_gather_qmm's kernels.
+ * Errors: as qaff_gather_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.
+ */
+qaff_status qaff_gather_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                                  const uint32_t* packed, const void* scales, const void* biases,
+                                  qaff_dtype sb_dtype, int64_t w_batches, int64_t n, int64_t k,
+                                  int32_t group_size, int32_t bits, const uint32_t* lhs_indices,
+                                  const uint32_t* rhs_indices, int64_t batch, int32_t sorted_indices,
+                                  void* y, hipStream_t stream);
 
 /* qaff_gather_qmm with the kernel forced: QAFF_PATH_GEMV (the VALU GEMV; the sorted promise is not
  * used), QAFF_PATH_GEMV_MFMA (UNSUPPORTED where that kernel does not apply) or QAFF_PATH_GEMM (the

@@ -62,8 +62,8 @@ def _need(t, name, dtypes, device=None):
 
 
 def _weights(packed, scales, biases, group_size, bits, typed=False):
-    """Checks a weight; returns (device, rows, cols). Only ``typed`` callers (qmm, dequantize) take
-    float16 or float32 scales and biases; the other operations read bf16 ones."""
+    """Checks a weight; returns (device, rows, cols). Only ``typed`` callers (qmm, gather_qmm,
+    dequantize) take float16 or float32 scales and biases; the other operations read bf16 ones."""
     _need(packed, "packed", _PACKED_DTYPES)
     dev = packed.device
     _need(scales, "scales", _SCALE_DTYPES, dev)
@@ -127,12 +127,17 @@ def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=tor
     return out
 
 
-def quantize(w, group_size: int, bits: int):
-    """Quantizes the last axis of a float32 or bf16 weight ``[..., cols]`` (nuvec_core ``quantize``):
-    returns packed uint32 ``[..., cols*bits/32]`` (as int32), and bf16 scales and biases
-    ``[..., cols/group_size]``; bias = group minimum, scale = (max - min) / (2^bits - 1)."""
+def quantize(w, group_size: int, bits: int, scales_dtype=None):
+    """Quantizes the last axis of a float32, bf16 or float16 weight ``[..., cols]`` (nuvec_core
+    ``quantize``): returns packed uint32 ``[..., cols*bits/32]`` (as int32), and scales and biases
+    ``[..., cols/group_size]`` in ``scales_dtype`` (default: w's dtype, nuvec_core's rule; bf16 is
+    what the products other than the ``*_typed`` ones read); bias = group minimum, scale =
+    (max - min) / (2^bits - 1)."""
     lib = _lib.load()
-    _need(w, "w", tuple(_OUT_DTYPES))
+    _need(w, "w", tuple(_ANY_DTYPES))
+    sdt = w.dtype if scales_dtype is None else scales_dtype
+    if sdt not in _ANY_DTYPES:
+        raise TypeError(f"scales_dtype must be float32, bfloat16 or float16, got {sdt}")
     dev = w.device
     if w.dim() < 1:
         raise ValueError("w must have at least one dimension")
@@ -142,11 +147,11 @@ def quantize(w, group_size: int, bits: int):
     if group_size <= 0 or cols % group_size:
         raise ValueError(f"{cols} columns are not a multiple of the group size {group_size}")
     packed = torch.empty(lead + (cols * bits // 32,), dtype=torch.int32, device=dev)
-    scales = torch.empty(lead + (cols // group_size,), dtype=torch.bfloat16, device=dev)
-    biases = torch.empty(lead + (cols // group_size,), dtype=torch.bfloat16, device=dev)
+    scales = torch.empty(lead + (cols // group_size,), dtype=sdt, device=dev)
+    biases = torch.empty(lead + (cols // group_size,), dtype=sdt, device=dev)
     with torch.cuda.device(dev):
-        _lib.check(lib.qaff_quantize(_p(w), _OUT_DTYPES[w.dtype], rows, cols, group_size, bits, _p(packed),
-                                     _p(scales), _p(biases), _stream(dev)))
+        _lib.check(lib.qaff_quantize_typed(_p(w), _ANY_DTYPES[w.dtype], rows, cols, group_size, bits, _p(packed),
+                                           _p(scales), _p(biases), _ANY_DTYPES[sdt], _stream(dev)))
     return packed, scales, biases
 
 
@@ -386,12 +391,15 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
                sorted_indices: bool = False, path: str = "auto", out=None):
     """Quantized products of gathered batches (nuvec_core ``gather_qmm`` with the transpose):
     output batch i is ``x[lhs[i]] . dequantize(W[rhs[i]])^T`` over the flattened batch dimensions
-    of x ``[..., m, k]`` (float32 or bf16) and of the weight (packed ``[..., n, k*bits/32]``,
-    scales and biases ``[..., n, k/group_size]``). Indices are integer tensors that broadcast
-    together, each defaulting to every batch of its operand; an index past its operand gives a NaN
-    batch. ``sorted_indices`` promises that ``rhs_indices`` is sorted (rows grouped by expert),
-    which lets the kernel read each expert's weights once. The result has x's dtype and shape
-    ``broadcast(batch) + [m, n]``."""
+    of x ``[..., m, k]`` and of the weight (packed ``[..., n, k*bits/32]``, scales and biases
+    ``[..., n, k/group_size]``). Indices are integer tensors that broadcast together, each
+    defaulting to every batch of its operand; an index past its operand gives a NaN batch.
+    ``sorted_indices`` promises that ``rhs_indices`` is sorted (rows grouped by expert), which lets
+    the kernel read each expert's weights once. The result has shape ``broadcast(batch) + [m, n]``.
+
+    x is float32, bf16 or float16 and the scales and biases bf16, float16 or float32: they promote
+    to one type (float32 unless they agree), which is the result's type. A float16 x or scales
+    other than bf16 run on the typed VALU kernel (path 'auto' or 'gemv')."""
     lib = _lib.load()
     _need(packed, "packed", _PACKED_DTYPES)
     dev = packed.device
@@ -403,8 +411,11 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
     wb = math.prod(w_batch)
     n = packed.shape[-2]
     _, _, k = _weights(packed.reshape(-1, packed.shape[-1]), scales.reshape(-1, scales.shape[-1]),
-                       biases.reshape(-1, biases.shape[-1]), group_size, bits)
-    _need(x, "x", tuple(_OUT_DTYPES), dev)
+                       biases.reshape(-1, biases.shape[-1]), group_size, bits, typed=True)
+    _need(x, "x", tuple(_ANY_DTYPES), dev)
+    sb = _sb_code(scales)
+    typed = sb != _lib.QAFF_BF16 or x.dtype == torch.float16
+    yt = _FROM_CODE[int(lib.qaff_promote_dtype(_ANY_DTYPES[x.dtype], sb))]
     if x.dim() < 2:
         raise ValueError("x must be [..., m, k]")
     m = x.shape[-2]
@@ -412,6 +423,8 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
         raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
     if path not in ("auto", "gemv", "gemv_mfma", "gemm"):
         raise ValueError("path must be 'auto', 'gemv', 'gemv_mfma' or 'gemm'")
+    if typed and path not in ("auto", "gemv"):
+        raise ValueError("float16 x or non-bf16 scales run on the typed VALU kernel: path 'auto' or 'gemv'")
     x_batch = tuple(x.shape[:-2])
     lhs, lhs_shape = _batch_indices(lhs_indices, x_batch, "lhs_indices", dev)
     rhs, rhs_shape = _batch_indices(rhs_indices, w_batch, "rhs_indices", dev)
@@ -421,14 +434,19 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
     batch = math.prod(shape)
     want = shape + (m, n)
     if out is None:
-        out = torch.empty(want, dtype=x.dtype, device=dev)
+        out = torch.empty(want, dtype=yt, device=dev)
     else:
-        _need(out, "out", (x.dtype,), dev)
+        _need(out, "out", (yt,), dev)
         if tuple(out.shape) != want:
             raise ValueError(f"out must be {list(want)}")
     with torch.cuda.device(dev):
-        _lib.check(lib.qaff_gather_qmm_ex(_p(x), _OUT_DTYPES[x.dtype], math.prod(x_batch), m, _p(packed),
-                                          _p(scales), _p(biases), wb, n, k, group_size, bits, _p(lhs),
-                                          _p(rhs), batch, 1 if sorted_indices else 0, _p(out), _stream(dev),
-                                          _lib.PATHS[path]))
+        if typed:
+            _lib.check(lib.qaff_gather_qmm_typed(_p(x), _ANY_DTYPES[x.dtype], math.prod(x_batch), m, _p(packed),
+                                                 _p(scales), _p(biases), sb, wb, n, k, group_size, bits, _p(lhs),
+                                                 _p(rhs), batch, 1 if sorted_indices else 0, _p(out), _stream(dev)))
+        else:
+            _lib.check(lib.qaff_gather_qmm_ex(_p(x), _OUT_DTYPES[x.dtype], math.prod(x_batch), m, _p(packed),
+                                              _p(scales), _p(biases), wb, n, k, group_size, bits, _p(lhs),
+                                              _p(rhs), batch, 1 if sorted_indices else 0, _p(out), _stream(dev),
+                                              _lib.PATHS[path]))
     return out

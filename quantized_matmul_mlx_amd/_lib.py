@@ -25,7 +25,7 @@ EXPORTS = ("qaff_dequantize", "qaff_qmm", "qaff_qmm_ex", "qaff_dequant_rows", "q
            "qaff_quantize", "qaff_qmm_nt", "qaff_qmm_nt_workspace_size", "qaff_qmm_nt_static",
            "qaff_qmm_nt_static_max_bytes", "qaff_qmm_ws", "qaff_qmm_workspace_size",
            "qaff_promote_dtype",
-           "qaff_dequantize_typed", "qaff_qmm_typed")
+           "qaff_dequantize_typed", "qaff_qmm_typed", "qaff_quantize_typed", "qaff_gather_qmm_typed")
 
 ABI_VERSION = 1
 
@@ -71,11 +71,15 @@ def load() -> ctypes.CDLL:
     lib.qaff_qmm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     lib.qaff_qmm_workspace_size.restype = ctypes.c_size_t
     lib.qaff_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, vp]
+    lib.qaff_quantize_typed.argtypes = [vp, ctypes.c_int, i64, i64, i32, i32, vp, vp, vp, ctypes.c_int, vp]
     lib.qaff_gather_qmm.argtypes = gather
     lib.qaff_gather_qmm_ex.argtypes = gather + [ctypes.c_int]
+    lib.qaff_gather_qmm_typed.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, vp, ctypes.c_int, i64, i64, i64, i32,
+                                          i32, vp, vp, i64, i32, vp, vp]
     for f in (lib.qaff_dequantize, lib.qaff_qmm, lib.qaff_qmm_ex, lib.qaff_dequant_rows,
               lib.qaff_gemv_gate_up, lib.qaff_gemv_silu_gate, lib.qaff_gather_qmm, lib.qaff_gather_qmm_ex,
-              lib.qaff_quantize, lib.qaff_qmm_nt, lib.qaff_qmm_nt_static, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
+              lib.qaff_gather_qmm_typed,
+              lib.qaff_quantize, lib.qaff_quantize_typed, lib.qaff_qmm_nt, lib.qaff_qmm_nt_static, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
         f.restype = ctypes.c_int
     lib.qaff_last_error.restype = ctypes.c_char_p
     lib.qaff_last_error.argtypes = []

@@ -446,6 +446,67 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
 
 qaff_dtype qaff_promote_dtype(qaff_dtype a, qaff_dtype b) { return a == b ? a : QAFF_F32; }
 
+qaff_status qaff_gather_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,
+                                  const uint32_t* packed, const void* scales, const void* biases, qaff_dtype sb_dtype,
+                                  int64_t w_batches, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                                  const uint32_t* lhs_indices, const uint32_t* rhs_indices, int64_t batch,
+                                  int32_t sorted_indices, void* y, hipStream_t stream) {
+    static const char* op = "qaff_gather_qmm_typed";
+    g_error.clear();
+    if (!any_dtype(x_dtype) || !any_dtype(sb_dtype))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown dtype (x %d, scales %d)", op, (int)x_dtype, (int)sb_dtype);
+    // bf16 scales with a float32 or bf16 x: the plain gathered product (y in x's dtype, the promoted one)
+    if (sb_dtype == QAFF_BF16 && x_dtype != QAFF_F16)
+        return qaff_gather_qmm(x, x_dtype, x_batches, m, packed, static_cast<const uint16_t*>(scales),
+                               static_cast<const uint16_t*>(biases), w_batches, n, k, group_size, bits, lhs_indices,
+                               rhs_indices, batch, sorted_indices, y, stream);
+    if (x_batches < 0 || w_batches < 0 || batch < 0 || m < 0)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative size", op);
+    qaff_status st = check_weight(op, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                                  w_batches * n, k, group_size, bits);
+    if (st != QAFF_OK) return st;
+    if (!lhs_indices && batch > x_batches)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: no lhs indices, but %lld batches of %lld x batches", op,
+                    (long long)batch, (long long)x_batches);
+    if (!rhs_indices && batch > w_batches)
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: no rhs indices, but %lld batches of %lld weight batches", op,
+                    (long long)batch, (long long)w_batches);
+    if ((lhs_indices && !aligned(lhs_indices, 4)) || (rhs_indices && !aligned(rhs_indices, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: indices must be 4-byte aligned", op);
+    if (x_batches >= 0xffffffffLL || w_batches >= 0xffffffffLL || batch >= 0xffffffffLL)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: 2^32-1 or more batches", op);
+    const qaff_dtype y_dtype = qaff_promote_dtype(x_dtype, sb_dtype);
+    if (batch == 0 || m == 0 || n == 0) return QAFF_OK;
+    if (sb_dtype == QAFF_F32 && (!aligned(scales, 4) || !aligned(biases, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
+    if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
+    if (!aligned(y, esize_of(y_dtype))) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
+    if (n > 0x7fffffffLL || m > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: m or n above 2^31-1", op);
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, batch * m * n * (int64_t)esize_of(y_dtype), stream), stream);
+    if (x_batches > 0 && !x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
+    if (x && !aligned(x, esize_of(x_dtype)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
+    qaff::Gather g{};
+    g.lhs = lhs_indices;
+    g.rhs = rhs_indices;
+    g.x_count = (uint32_t)x_batches;
+    g.w_count = (uint32_t)w_batches;
+    g.batch = (uint32_t)batch;
+    g.x_stride = (uint64_t)(m * k);
+    g.w_stride = (uint64_t)(n * (k / 32) * bits);
+    g.sb_stride = (uint64_t)(n * (k / group_size));
+    g.y_stride = (uint64_t)(m * n);
+    if ((x && !aligned(x, 16)) || !aligned(y, 16)) {  // the typed GEMV reads x in 16-byte loads
+        qaff::ScalarGemv opt{};
+        opt.gather = true;
+        opt.g = g;
+        return after_launch(op, qaff::launch_gemv_scalar(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
+                                                         group_size, bits, y, (int)y_dtype, opt, stream), stream);
+    }
+    return after_launch(op, qaff::launch_gemv_typed(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
+                                                    group_size, bits, y, (int)y_dtype, stream, &g), stream);
+}
+
 qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, const void* biases, qaff_dtype sb_dtype,
                                   int64_t rows, int64_t cols, int32_t group_size, int32_t bits, void* out,
                                   qaff_dtype out_dtype, hipStream_t stream) {
@@ -577,21 +638,42 @@ qaff_status qaff_qmm_nt_static(const void* x, qaff_dtype x_dtype, int64_t m, con
 
 size_t qaff_qmm_nt_static_max_bytes(void) { return qaff::kQmmNtStaticScratchBytes; }
 
-qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
-                          int32_t bits, uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {
-    static const char* op = "qaff_quantize";
+namespace {
+
+qaff_status quantize_impl(const char* op, const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols,
+                          int32_t group_size, int32_t bits, uint32_t* packed, void* scales, void* biases,
+                          qaff_dtype sb_dtype, hipStream_t stream) {
     g_error.clear();
-    // the outputs are checked as a weight would be
-    qaff_status st = check_weight(op, packed, scales, biases, rows, cols, group_size, bits);
+    if (!any_dtype(w_dtype) || !any_dtype(sb_dtype))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown dtype (w %d, scales %d)", op, (int)w_dtype, (int)sb_dtype);
+    // the outputs are checked as a weight would be, with the scales' own alignment
+    qaff_status st = check_weight(op, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                                  rows, cols, group_size, bits);
     if (st != QAFF_OK) return st;
-    if (!valid_dtype(w_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown w dtype %d", op, (int)w_dtype);
     if (rows == 0 || cols == 0) return QAFF_OK;
+    if (sb_dtype == QAFF_F32 && (!aligned(scales, 4) || !aligned(biases, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
     if (!w) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null w", op);
     if (!aligned(w, esize_of(w_dtype))) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: w must be aligned to its element size", op);
     if (rows * (cols / 32) >= (1LL << 37))
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld is too large", op, (long long)rows, (long long)cols);
-    return after_launch(op, qaff::launch_quantize(w, w_dtype == QAFF_BF16, rows, cols, group_size, bits, packed,
-                                                  scales, biases, stream), stream);
+    return after_launch(op, qaff::launch_quantize(w, (int)w_dtype, rows, cols, group_size, bits, packed, scales, biases,
+                                                  (int)sb_dtype, stream), stream);
+}
+
+}  // namespace
+
+qaff_status qaff_quantize(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
+                          int32_t bits, uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream) {
+    return quantize_impl("qaff_quantize", w, w_dtype, rows, cols, group_size, bits, packed, scales, biases, QAFF_BF16,
+                         stream);
+}
+
+qaff_status qaff_quantize_typed(const void* w, qaff_dtype w_dtype, int64_t rows, int64_t cols, int32_t group_size,
+                                int32_t bits, uint32_t* packed, void* scales, void* biases, qaff_dtype sb_dtype,
+                                hipStream_t stream) {
+    return quantize_impl("qaff_quantize_typed", w, w_dtype, rows, cols, group_size, bits, packed, scales, biases,
+                         sb_dtype, stream);
 }
 
 qaff_status qaff_qmm(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,

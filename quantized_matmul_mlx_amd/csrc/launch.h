@@ -99,11 +99,11 @@ hipError_t launch_gemm_grouped(const uint16_t* x, const uint32_t* packed, const 
                                const uint32_t* rhs, int64_t batch, int64_t w_count, uint64_t w_stride,
                                uint64_t sb_stride, hipStream_t stream);
 
-// packed/scales/biases of a dense [rows, cols] weight (float32 or bf16): bias = group min,
-// scale = (max - min) / (2^bits - 1), both bf16; code = round((w - bias) / scale), clamped.
-// w 16-byte aligned: 16-byte loads; otherwise element by element.
-hipError_t launch_quantize(const void* w, bool in_bf16, int64_t rows, int64_t cols, int group_size, int bits,
-                           uint32_t* packed, uint16_t* scales, uint16_t* biases, hipStream_t stream);
+// packed/scales/biases of a dense [rows, cols] weight of dtype code w_dtype (0 float32, 1 bf16,
+// 2 float16): bias = group min, scale = (max - min) / (2^bits - 1), both stored as sb_dtype; code =
+// round((w - bias) / scale), clamped. w 16-byte aligned: 16-byte loads; otherwise element by element.
+hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t cols, int group_size, int bits,
+                           uint32_t* packed, void* scales, void* biases, int sb_dtype, hipStream_t stream);
 
 // y[m, n] = x[m, k] . dequantize(W) for W stored [k, n] (groups along n); float32 partial sums
 // of K chunks go to `workspace` (qmm_nt_workspace_bytes(m, k, n) bytes), then a second kernel
@@ -125,9 +125,11 @@ hipError_t qmm_nt_static_scratch(void** ptr);
 hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, const void* biases, int sb_dtype,
                                 int64_t rows, int64_t cols, int group_size, int bits, void* out, int out_dtype,
                                 hipStream_t stream, const uint32_t* indices = nullptr, int64_t table_rows = 0);
+// With `gather`, the product over its output batches (x batch lhs[b] against weight batch rhs[b],
+// strides in elements of each operand's own type; NaN batches past either operand).
 hipError_t launch_gemv_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
                              const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits, void* y,
-                             int y_dtype, hipStream_t stream);
+                             int y_dtype, hipStream_t stream, const Gather* gather = nullptr);
 
 // The element-by-element GEMV behind operands that are not 16-byte aligned: y = x . dequantize(W)^T
 // with x, scales, biases and y of the given dtype codes, each loaded and stored one element at a time

@@ -6,7 +6,9 @@
 //    float32 scales the product is not always exact, so no fused multiply-add), stored as
 //    float32, bf16 or float16 (round to nearest even).
 //  * gemv_typed_kernel: y = x . dequantize(W)^T on the VALU, float32 sums, x of any of the three
-//    types, y in the promoted type. Per block of 32 codes: s * sum(x c) + b * sum(x).
+//    types, y in the promoted type. Per block of 32 codes: s * sum(x c) + b * sum(x). Gathered
+//    (nuvec_core quantized.rs, `gather_qmm`): grid z is the output batch, x batch lhs[z] against
+//    weight batch rhs[z]; an index past its operand gives a NaN batch.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -57,7 +59,7 @@ constexpr int kTypedRows = 2;
 template <int BITS, int MB>
 __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
     const void* x, int xt, uint32_t m, const uint32_t* packed, const void* scales, const void* biases, int st,
-    uint32_t n, uint32_t kb, uint32_t gshift, void* y, int yt) {
+    uint32_t n, uint32_t kb, uint32_t gshift, void* y, int yt, Gather ga, int gathered) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const uint32_t n0 = (blockIdx.x * (kTypedThreads / 64) + wave) * kTypedRows;
@@ -65,6 +67,25 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
     const uint32_t m0 = blockIdx.y * MB;
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> gshift;
+    if (gathered) {
+        // this output batch's x, weight and y (element sizes: 4 for float32, else 2)
+        const uint32_t z = ga.b0 + blockIdx.z;
+        const uint32_t li = ga.lhs ? ga.lhs[z] : z;
+        const uint32_t ri = ga.rhs ? ga.rhs[z] : z;
+        y = static_cast<uint8_t*>(y) + (size_t)z * ga.y_stride * (yt == 0 ? 4 : 2);
+        if (li >= ga.x_count || ri >= ga.w_count) {
+            if (lane < kTypedRows * MB) {
+                const uint32_t row = n0 + (uint32_t)lane / MB, i = m0 + (uint32_t)lane % MB;
+                if (row < n && i < m) store_from_f32(y, (size_t)i * n + row, yt, __builtin_nanf(""));
+            }
+            return;
+        }
+        x = static_cast<const uint8_t*>(x) + (size_t)li * ga.x_stride * (xt == 0 ? 4 : 2);
+        packed += (size_t)ri * ga.w_stride;
+        const size_t sb = (size_t)ri * ga.sb_stride * (st == 0 ? 4 : 2);
+        scales = static_cast<const uint8_t*>(scales) + sb;
+        biases = static_cast<const uint8_t*>(biases) + sb;
+    }
 
     float acc[kTypedRows][MB];
 #pragma unroll
@@ -156,21 +177,30 @@ hipError_t launch_dequant_bits(const uint32_t* packed, const void* scales, const
     return hipGetLastError();
 }
 
+// Grid: x = row groups of W, y = x rows in tiles of MB (at most 65535 per launch), z = output
+// batches when gathered (at most 65535 per launch).
 template <int BITS, int MB>
 hipError_t launch_gemv_mb(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
                           const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
-                          hipStream_t stream) {
+                          const Gather* ga, hipStream_t stream) {
     const unsigned gx = (unsigned)((n + (kTypedThreads / 64) * kTypedRows - 1) / ((kTypedThreads / 64) * kTypedRows));
     const size_t xsize = xt == 0 ? 4 : 2, ysize = yt == 0 ? 4 : 2;
     const int64_t max_rows = (int64_t)65535 * MB;
-    for (int64_t m0 = 0; m0 < m; m0 += max_rows) {
-        const int64_t mm = m - m0 < max_rows ? m - m0 : max_rows;
-        const unsigned gy = (unsigned)((mm + MB - 1) / MB);
-        gemv_typed_kernel<BITS, MB><<<dim3(gx, gy), kTypedThreads, 0, stream>>>(
-            static_cast<const uint8_t*>(x) + (size_t)m0 * kb * 32 * xsize, xt, (uint32_t)mm, packed, scales, biases, st,
-            (uint32_t)n, (uint32_t)kb, gshift, static_cast<uint8_t*>(y) + (size_t)m0 * n * ysize, yt);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    const int64_t batches = ga ? ga->batch : 1;
+    for (int64_t b0 = 0; b0 < batches; b0 += 65535) {
+        Gather g = ga ? *ga : Gather{};
+        g.b0 = (uint32_t)b0;
+        const unsigned gz = (unsigned)(batches - b0 < 65535 ? batches - b0 : 65535);
+        for (int64_t m0 = 0; m0 < m; m0 += max_rows) {
+            const int64_t mm = m - m0 < max_rows ? m - m0 : max_rows;
+            const unsigned gy = (unsigned)((mm + MB - 1) / MB);
+            gemv_typed_kernel<BITS, MB><<<dim3(gx, gy, gz), kTypedThreads, 0, stream>>>(
+                static_cast<const uint8_t*>(x) + (size_t)m0 * kb * 32 * xsize, xt, (uint32_t)mm, packed, scales, biases,
+                st, (uint32_t)n, (uint32_t)kb, gshift, static_cast<uint8_t*>(y) + (size_t)m0 * n * ysize, yt, g,
+                ga ? 1 : 0);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
@@ -179,9 +209,9 @@ hipError_t launch_gemv_mb(const void* x, int xt, int64_t m, const uint32_t* pack
 template <int BITS>
 hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
                             const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
-                            hipStream_t stream) {
-    if (m == 1) return launch_gemv_mb<BITS, 1>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, stream);
-    return launch_gemv_mb<BITS, 4>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, stream);
+                            const Gather* ga, hipStream_t stream) {
+    if (m == 1) return launch_gemv_mb<BITS, 1>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, ga, stream);
+    return launch_gemv_mb<BITS, 4>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, ga, stream);
 }
 
 }  // namespace
@@ -205,17 +235,17 @@ hipError_t launch_dequant_typed(const uint32_t* packed, const void* scales, cons
 
 hipError_t launch_gemv_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
                              const void* biases, int sb_dtype, int64_t n, int64_t k, int group_size, int bits, void* y,
-                             int y_dtype, hipStream_t stream) {
+                             int y_dtype, hipStream_t stream, const Gather* gather) {
     const int64_t kb = k / 32;
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     switch (bits) {
-        case 1: return launch_gemv_bits<1>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 2: return launch_gemv_bits<2>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 3: return launch_gemv_bits<3>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 4: return launch_gemv_bits<4>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 5: return launch_gemv_bits<5>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 6: return launch_gemv_bits<6>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
-        case 8: return launch_gemv_bits<8>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, stream);
+        case 1: return launch_gemv_bits<1>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 2: return launch_gemv_bits<2>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 3: return launch_gemv_bits<3>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 4: return launch_gemv_bits<4>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 5: return launch_gemv_bits<5>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 6: return launch_gemv_bits<6>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
+        case 8: return launch_gemv_bits<8>(x, x_dtype, m, packed, scales, biases, sb_dtype, n, kb, gshift, y, y_dtype, gather, stream);
         default: return hipErrorInvalidValue;
     }
 }

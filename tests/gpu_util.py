@@ -23,6 +23,8 @@ def dev_bf16(a):
 def dev_x(x, x_dtype):
     if x_dtype == "bf16":
         return dev_bf16(x)
+    if x_dtype == "f16":   # float16 bit patterns
+        return torch.from_numpy(np.ascontiguousarray(x, np.uint16).view(np.int16)).cuda().view(torch.float16)
     return torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda()
 
 
@@ -31,9 +33,9 @@ def dev_weights(inp):
 
 
 def host_bits(t):
-    """bf16 tensor -> uint16 bit patterns; float32 tensor -> float32 array."""
+    """bf16 or float16 tensor -> uint16 bit patterns; float32 tensor -> float32 array."""
     t = t.detach().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
 

@@ -63,7 +63,7 @@ hipError_t launch_gemm_grouped(const uint16_t*, const uint32_t*, const uint16_t*
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
     return (m <= 256 && k % 1024 == 0) ? (size_t)(m * n * 4 * 2) : 0;
 }
-hipError_t launch_quantize(const void*, bool, int64_t, int64_t, int, int, uint32_t*, uint16_t*, uint16_t*,
+hipError_t launch_quantize(const void*, int, int64_t, int64_t, int, int, uint32_t*, void*, void*, int,
                            hipStream_t) { return rec("quantize"); }
 void qmm_nt_plan(int64_t k, int64_t, int, int64_t* kchunk, int64_t* chunks) { *kchunk = 128; *chunks = (k + 127) / 128; }
 size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n, int) {
@@ -76,7 +76,7 @@ hipError_t qmm_nt_static_scratch(void** ptr) { *ptr = fake_scratch; return rec("
 hipError_t launch_dequant_typed(const uint32_t*, const void*, const void*, int, int64_t, int64_t, int, int, void*, int,
                                 hipStream_t, const uint32_t*, int64_t) { return rec("dequant_typed"); }
 hipError_t launch_gemv_typed(const void*, int, int64_t, const uint32_t*, const void*, const void*, int, int64_t,
-                             int64_t, int, int, void*, int, hipStream_t) { return rec("gemv_typed"); }
+                             int64_t, int, int, void*, int, hipStream_t, const Gather*) { return rec("gemv_typed"); }
 hipError_t launch_fill_zero(void*, int64_t, hipStream_t) { return rec("fill_zero"); }
 hipError_t launch_gemv_scalar(const void*, int, int64_t, const uint32_t*, const void*, const void*, int, int64_t,
                               int64_t, int, int, void*, int, const ScalarGemv&, hipStream_t) { return rec("gemv_scalar"); }
@@ -182,6 +182,12 @@ int main() {
                                          const_cast<uint16_t*>(S16), const_cast<uint16_t*>(B16), nullptr));
     EXPECT(INV, "", qaff_quantize(A1, QAFF_BF16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), const_cast<uint16_t*>(S16),
                                   const_cast<uint16_t*>(B16), nullptr));
+    EXPECT(OK, "quantize", qaff_quantize_typed(A2, QAFF_F16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), A16, A16,
+                                               QAFF_F32, nullptr));
+    EXPECT(INV, "", qaff_quantize_typed(A16, QAFF_F16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), A2, A16, QAFF_F32,
+                                        nullptr));  // float32 scales need 4-byte alignment
+    EXPECT(INV, "", qaff_quantize_typed(A16, QAFF_F16, 4, 128, 64, 4, const_cast<uint32_t*>(P16), A16, A16,
+                                        (qaff_dtype)3, nullptr));
     // the product without the transpose, with a workspace and with the static scratch
     const size_t nt = qaff_qmm_nt_workspace_size(2, 4096, 4096, 4);
     CHECK(nt > 0);
@@ -196,6 +202,16 @@ int main() {
     EXPECT(OK, "gemv_typed", qaff_qmm_typed(A16, QAFF_F32, 1, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(INV, "", qaff_qmm_typed(A16, (qaff_dtype)5, 1, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
     CHECK(qaff_promote_dtype(QAFF_BF16, QAFF_F16) == QAFF_F32);
+    EXPECT(OK, "gemv_typed", qaff_gather_qmm_typed(A16, QAFF_F16, 2, 1, P16, A16, A16, QAFF_F32, 4, 64, 4096, 64, 4,
+                                                   I16, I16, 3, 0, A16, nullptr));
+    EXPECT(OK, "gemv_scalar", qaff_gather_qmm_typed(A2, QAFF_F16, 2, 1, P16, A16, A16, QAFF_F16, 4, 64, 4096, 64, 4,
+                                                    I16, I16, 3, 0, A16, nullptr));
+    EXPECT(OK, "gemv_gather", qaff_gather_qmm_typed(A16, QAFF_BF16, 2, 1, P16, A16, A16, QAFF_BF16, 4, 64, 4096, 64,
+                                                    4, I16, I16, 3, 0, A16, nullptr));  // the plain gathered product
+    EXPECT(INV, "", qaff_gather_qmm_typed(A16, QAFF_F16, 2, 1, P16, A2, A16, QAFF_F32, 4, 64, 4096, 64, 4, I16, I16, 3,
+                                          0, A16, nullptr));
+    EXPECT(INV, "", qaff_gather_qmm_typed(A16, QAFF_F16, 2, 1, P16, A16, A16, QAFF_F32, 4, 64, 4096, 64, 4, nullptr,
+                                          I16, 3, 0, A16, nullptr));  // 3 batches of 2 x batches without lhs
     // the error text of a failure, then cleared by the next call
     qaff_dequantize(P16, S16, B16, 4, 64, 32, 7, A16, QAFF_F32, nullptr);
     CHECK(std::strstr(qaff_last_error(), "bits") != nullptr);

@@ -82,3 +82,29 @@ def test_grouped_walk_over_expert_slices(orc):
     got = host_f64(y).reshape(-1, n)
     assert np.isfinite(got).all()
     assert orc.max_row_rel_err(got, ref.reshape(-1, n)) <= 1.6e-2
+
+
+def test_typed_gather_over_batch_slices(orc):
+    # the typed gathered GEMV: grid z = output batch, 65535 per launch (float16 x, float32 scales)
+    E, n, k, G, bits, batch = 3, 40, 64, 32, 4, 65535 + 300
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=9)
+    packed = inp.packed.reshape(E, n, -1)
+    rng = np.random.default_rng(10)
+    sc = rng.uniform(1e-3, 2e-2, (E, n, k // G)).astype(np.float32)
+    bi = rng.uniform(-0.15, 0.0, (E, n, k // G)).astype(np.float32)
+    x = rng.standard_normal((7, 1, k)).astype(np.float16)
+    lhs = rng.integers(0, 7, batch).astype(np.uint32)
+    rhs = rng.integers(0, E, batch).astype(np.uint32)
+    rhs[-5:] = E + 2                                          # NaN batches in the last launch
+    banner(f"typed gather batch={batch} (several launches)")
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16)
+    y = qaff().gather_qmm(xd, dev_u32(packed), torch.from_numpy(sc).cuda(), torch.from_numpy(bi).cuda(), G, bits,
+                          lhs_indices=dev_u32(lhs), rhs_indices=dev_u32(rhs))
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float32
+    ref = orc.gather_qmm_typed(x.view(np.uint16), "f16", packed, sc, bi, "f32", G, bits, lhs=lhs, rhs=rhs)
+    got = host_f64(y).reshape(-1, n)
+    ref = ref.reshape(-1, n)
+    nan = np.isnan(ref).all(axis=1)
+    assert nan.sum() == 5 and np.isnan(got[nan]).all()
+    assert orc.max_row_rel_err(got[~nan], ref[~nan]) <= TIGHT["f32"]

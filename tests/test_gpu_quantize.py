@@ -1,8 +1,9 @@
 """Quantization on the GPU against the CPU oracle, through the C ABI (via the binding).
 
-Codes are integers and scales and biases bf16 values (bias = group min and scale =
-(max - min) / (2^bits - 1), float32 statistics rounded to bf16; code = round-half-away of the exact
-value of (w - bias) / scale, clamped): the bar is bit-exact for all three outputs.
+Codes are integers and scales and biases values of their stored type (bias = group min and scale =
+(max - min) / (2^bits - 1), float32 statistics stored as bf16, float16 or float32; code =
+round-half-away of the exact value of (w - bias) / scale, clamped): the bar is bit-exact for all
+three outputs, for float32, bf16 and float16 weights.
 """
 import numpy as np
 import pytest
@@ -10,7 +11,7 @@ import torch
 
 import oracle as orc_mod
 from gpu_util import banner, dev_bf16, dev_u32, dev_x, host_bits
-from near_ties import bf16_rne, near_tie_groups, tie_example
+from near_ties import bf16_rne, bf16_value, f16_value, f32_value, near_tie_groups, tie_example
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -31,18 +32,23 @@ def qaff():
     return q
 
 
-def run(w, dtype, G, bits):
+TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def run(w, dtype, G, bits, sb="bf16"):
     wd = dev_x(w, dtype)
-    p, s, b = qaff().quantize(wd, G, bits)
+    p, s, b = qaff().quantize(wd, G, bits, scales_dtype=TORCH[sb])
     torch.cuda.synchronize()
     return (p.cpu().numpy().view(np.uint32), host_bits(s), host_bits(b))
 
 
-def check(orc, w, dtype, G, bits):
-    got = run(w, dtype, G, bits)
-    ref = orc.quantize(w, dtype, G, bits)
+def check(orc, w, dtype, G, bits, sb="bf16"):
+    got = run(w, dtype, G, bits, sb)
+    ref = orc.quantize(w, dtype, G, bits, sb)
     for name, g, r in zip(("packed", "scales", "biases"), got, ref):
         assert g.shape == r.shape, name
+        if g.dtype == np.float32:   # float32 scales: compare the bit patterns
+            g, r = g.view(np.uint32), r.view(np.uint32)
         if not np.array_equal(g, r):
             bad = np.argwhere(g != r)[:5]
             raise AssertionError(f"{name} differs at {bad.tolist()}: got {g[tuple(bad[0])]:#x}, "
@@ -111,7 +117,7 @@ def test_quantize_round_trip_through_qmm(orc):
 def test_quantize_leading_dims_and_empty(orc):
     w = W.dense_weight(6, 128, "f32", seed=5).reshape(2, 3, 128)
     banner("quantize leading dims")
-    p, s, b = qaff().quantize(dev_x(w, "f32"), 32, 4)
+    p, s, b = qaff().quantize(dev_x(w, "f32"), 32, 4, scales_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert tuple(p.shape) == (2, 3, 16) and tuple(s.shape) == (2, 3, 4)
     rp, rs, rb = orc.quantize(w.reshape(6, 128), "f32", 32, 4)
@@ -126,3 +132,64 @@ def test_quantize_workload_full_size(orc):
     w = W.dense_weight(wl.n, wl.k, "bf16", seed=wl.seed)
     banner("quantize 4096x4096 bf16 4-bit g64")
     check(orc, w, "bf16", wl.group_size, wl.bits)
+
+
+# ---- float16 weights, and scales and biases in float32 or float16 ----------------------------------
+
+def f16_bits(w32):
+    return np.asarray(w32, np.float32).astype(np.float16).view(np.uint16)
+
+
+def as_input(w32, dtype):
+    return {"f32": lambda a: np.asarray(a, np.float32), "bf16": W.bf16_bits_from_f32, "f16": f16_bits}[dtype](w32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("sb", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (6, 128)])
+def test_quantize_typed_bit_exact(orc, dtype, sb, bits, G):
+    # 37 rows of 5 groups; scales and biases stored as sb
+    w = as_input(W.dense_weight(37, 5 * G, "f32", seed=bits * 10 + G), dtype)
+    banner(f"quantize {dtype} -> scales {sb} bits={bits} G={G}")
+    check(orc, w, dtype, G, bits, sb)
+
+
+@pytest.mark.parametrize("dtype,sb", [("f32", "f32"), ("f16", "f16"), ("f32", "f16"), ("bf16", "f16"),
+                                      ("f16", "f32"), ("f16", "bf16")])
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (5, 32)])
+def test_quantize_typed_near_ties(orc, dtype, sb, bits, G):
+    # values within a few ulps of the boundaries of the stored scale and bias
+    stored = {"f32": f32_value, "bf16": bf16_value, "f16": f16_value}[sb]
+    w = near_tie_groups(40, 3, G, bits, seed=400 + bits, w_type=np.float16 if dtype == "f16" else np.float32,
+                        stored=stored)
+    wi = {"f32": w, "f16": w.view(np.uint16) if w.dtype == np.float16 else w, "bf16": bf16_rne(w)}[dtype]
+    banner(f"quantize near ties {dtype} -> scales {sb} bits={bits} G={G}")
+    check(orc, wi, dtype, G, bits, sb)
+
+
+def test_quantize_float32_scale_exact_quotient_below_a_tie(orc):
+    # scale 1 + 2^-20 (min 0, max 15 scale): values just below (k + 1/2) scale whose float32
+    # quotient lands on the tie round down (see the oracle pin of the same case)
+    s = np.float32(1.0 + 2.0 ** -20)
+    w = np.zeros((1, 32), np.float32)
+    w[0, 1] = np.float32(15.0 * (1.0 + 2.0 ** -20))
+    for i, k in enumerate(range(1, 15)):
+        v = np.float32((k + 0.5) * float(s))
+        if np.float64(v) >= (k + 0.5) * float(s):
+            v = np.nextafter(v, np.float32(-np.inf))
+        w[0, 2 + i] = v
+    banner("quantize float32 scale near a tie")
+    got = check(orc, w, "f32", 32, 4, "f32")
+    assert got[1][0, 0] == s
+
+
+def test_quantize_default_scales_dtype_is_w_dtype(orc):
+    w = W.dense_weight(4, 128, "f32", seed=9)
+    q = qaff()
+    for dtype, tdt in (("f32", torch.float32), ("bf16", torch.bfloat16), ("f16", torch.float16)):
+        banner(f"quantize default scales dtype {dtype}")
+        p, s, b = q.quantize(dev_x(as_input(w, dtype), dtype), 64, 4)
+        torch.cuda.synchronize()
+        assert s.dtype == tdt and b.dtype == tdt
+        rp, rs, rb = orc.quantize(as_input(w, dtype), dtype, 64, 4, dtype)
+        np.testing.assert_array_equal(p.cpu().numpy().view(np.uint32), rp)

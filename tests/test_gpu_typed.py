@@ -147,3 +147,70 @@ def test_bf16_only_operations_reject_other_scales(orc):
     with pytest.raises(TypeError):   # scales and biases of different types
         q.qmm(torch.zeros((1, 128), dtype=torch.bfloat16, device="cuda"), dev_u32(inp.packed), ds,
               to_dev(inp.biases, "bf16"), 64, 4)
+
+
+# ---- gathered products (nuvec_core gather_qmm: x, scales and biases promote to one type) ----------
+
+def promoted(xt, sb):
+    return TORCH[xt] if xt == sb else torch.float32
+
+
+def typed_experts(bits, G, E, n, k, sb, seed):
+    inp = W.random_inputs(bits, G, E * n, k, 0, seed=seed)
+    hs, hb, ds, db = scales_of(inp, sb, seed=seed + 1)
+    return (inp.packed.reshape(E, n, -1), hs.reshape(E, n, -1), hb.reshape(E, n, -1),
+            ds.reshape(E, n, -1), db.reshape(E, n, -1))
+
+
+def check_gather(orc, y, hx, xt, packed, hs, hb, sb, G, bits, lhs, rhs):
+    want = promoted(xt, sb)
+    assert y.dtype == want
+    ref = orc.gather_qmm_typed(hx, xt, packed, hs, hb, sb, G, bits, lhs=lhs, rhs=rhs)
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert got.shape == ref.shape
+    nan = np.isnan(ref).all(axis=(1, 2))
+    assert np.isnan(got[nan]).all() and np.isfinite(got[~nan]).all()
+    err = orc.max_row_rel_err(got[~nan].reshape(-1, got.shape[-1]), ref[~nan].reshape(-1, ref.shape[-1]))
+    assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
+
+
+@pytest.mark.parametrize("xt,sb", [("f16", "f16"), ("f16", "f32"), ("f32", "f16"), ("bf16", "f32"), ("f16", "bf16"),
+                                   ("f32", "f32")])
+@pytest.mark.parametrize("bits,G,m", [(4, 64, 1), (3, 32, 3), (8, 128, 2), (5, 64, 6)])
+def test_gather_qmm_typed(orc, xt, sb, bits, G, m):
+    # 5 experts of [150, 640]; batches past x (lhs 7) and past the experts (rhs 9) are NaN
+    E, n, k = 5, 150, 640
+    packed, hs, hb, ds, db = typed_experts(bits, G, E, n, k, sb, seed=60 + bits + G)
+    x32 = np.random.default_rng(m + bits).standard_normal((4, m, k)).astype(np.float32)
+    hx = x32 if xt == "f32" else (x32.astype(np.float16).view(np.uint16) if xt == "f16" else W.bf16_bits_from_f32(x32))
+    lhs = np.array([3, 0, 0, 2, 1, 7, 3], np.uint32)
+    rhs = np.array([4, 4, 1, 0, 9, 2, 3], np.uint32)
+    banner(f"gather_qmm typed x={xt} sb={sb} bits={bits} G={G} m={m}")
+    y = qaff().gather_qmm(to_dev(hx, xt), dev_u32(packed), ds, db, G, bits, lhs_indices=dev_u32(lhs),
+                          rhs_indices=dev_u32(rhs))
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, xt, packed, hs, hb, sb, G, bits, lhs, rhs)
+
+
+def test_gather_qmm_typed_unaligned_x_and_sorted_rows(orc):
+    # x at a 2-byte offset takes the element-by-element kernel; sorted rows (one per batch, the
+    # mixture-of-experts form) with float16 scales, the typed kernel
+    from gpu_util import at_offset
+    E, n, k, G, bits = 4, 96, 512, 64, 4
+    packed, hs, hb, ds, db = typed_experts(bits, G, E, n, k, "f16", seed=70)
+    rhs = np.repeat(np.arange(E, dtype=np.uint32), [3, 0, 5, 2])
+    x = np.random.default_rng(71).standard_normal((rhs.size, 1, k)).astype(np.float16)
+    hx = x.view(np.uint16)
+    banner("gather_qmm typed, float16 x at an offset, sorted rows")
+    xd = at_offset(to_dev(hx, "f16"))
+    assert xd.data_ptr() % 16 != 0
+    y = qaff().gather_qmm(xd, dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs), sorted_indices=True)
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, "f16", packed, hs, hb, "f16", G, bits, np.arange(rhs.size, dtype=np.uint32), rhs)
+    y2 = qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
+                           sorted_indices=True)
+    torch.cuda.synchronize()
+    check_gather(orc, y2, hx, "f16", packed, hs, hb, "f16", G, bits, np.arange(rhs.size, dtype=np.uint32), rhs)
+    with pytest.raises(ValueError, match="typed VALU kernel"):
+        qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
+                          path="gemv_mfma")
