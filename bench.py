@@ -341,11 +341,14 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
     return row
 
 
-def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, name="moe_4bit_g64_e128_768x2048"):
+def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, name="moe_4bit_g64_e128_768x2048",
+                 f16=False):
     """A mixture-of-experts gathered product (gather_qmm): 128 experts of W [768, 2048] at 4-bit
     g64, 8 experts per token, the tokens' rows sorted by expert (rows = 8 * tokens, x [rows, 1, k]).
     Algorithmic bytes: the weights of the experts in use, x rows, y rows. At prefill size (experts
-    averaging 32 rows or more: the grouped GEMM) the row is in TFLOP/s against the bf16 MFMA peak."""
+    averaging 32 rows or more: the grouped GEMM) the row is in TFLOP/s against the bf16 MFMA peak.
+    f16: x, scales and biases as float16 (the workload's values converted; y float16): the typed
+    gathered GEMV."""
     import numpy as np
     import oracle
     wl = W.WORKLOADS[name]
@@ -356,12 +359,19 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     nbytes = used * per_expert + rows * wl.k * 2 + rows * wl.n * 2
     all_bytes = wl.experts * per_expert  # a copy holds every expert
     copies = copies_for(all_bytes)
+    if f16:
+        to16 = lambda a: W.f32_from_bf16_bits(a).astype(np.float16).view(np.uint16)
+        hs, hb, hx = to16(mi.scales), to16(mi.biases), to16(mi.x_rows)
+        tdt = torch.float16
+    else:
+        hs, hb, hx = mi.scales, mi.biases, mi.x_rows
+        tdt = torch.bfloat16
     dev = [{"packed": torch.from_numpy(mi.packed.view(np.int32)).cuda(),
-            "scales": torch.from_numpy(mi.scales.view(np.int16)).cuda().view(torch.bfloat16),
-            "biases": torch.from_numpy(mi.biases.view(np.int16)).cuda().view(torch.bfloat16),
-            "x": torch.from_numpy(mi.x_rows.view(np.int16)).cuda().view(torch.bfloat16)} for _ in range(copies)]
+            "scales": torch.from_numpy(hs.view(np.int16)).cuda().view(tdt),
+            "biases": torch.from_numpy(hb.view(np.int16)).cuda().view(tdt),
+            "x": torch.from_numpy(hx.view(np.int16)).cuda().view(tdt)} for _ in range(copies)]
     rhs = torch.from_numpy(mi.expert.view(np.int32)).cuda()
-    ys = [torch.empty((rows, 1, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    ys = [torch.empty((rows, 1, wl.n), dtype=tdt, device="cuda") for _ in range(copies)]
 
     def launch(i):
         s = dev[i % copies]
@@ -372,11 +382,13 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     del dev, ys
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    grouped = rows >= wl.experts
-    gemm = rows >= 32 * wl.experts
+    grouped = rows >= wl.experts and not f16
+    gemm = rows >= 32 * wl.experts and not f16
+    kernel = "gemm_grouped" if gemm else ("gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)")
     row = {"workload": f"gather_qmm {wl.experts} experts [768, 2048] 4-bit g64, top-{wl.top_k}, {tokens} token(s), "
-                       f"{rows} rows sorted by expert ({used} experts in use)",
-           "kernel": "gemm_grouped" if gemm else ("gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)"),
+                       f"{rows} rows sorted by expert ({used} experts in use)" +
+                       (", float16 x, scales and biases" if f16 else ""),
+           "kernel": "gemv_typed_kernel (gathered)" if f16 else kernel,
            "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "weight_copies": copies,
            "roofline": hbm_roofline(gbs)}
     if gemm:
@@ -397,6 +409,11 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
         row["cpu_baseline"] = {"value": round(2.0 * sel.size * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
                                "cores": threads, "kind": "oracle",
                                "sample": f"the {sel.size} rows of one expert, {el:.2f} s"}
+    elif cpu and f16:
+        runs, el = cpu_time(lambda: oracle.gather_qmm_typed(hx, "f16", mi.packed, hs, hb, "f16", wl.group_size,
+                                                            wl.bits, rhs=mi.expert), cpu_budget, 100000)
+        row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
     elif cpu:
         threads = oracle.default_threads()
         runs, el = cpu_time(lambda: oracle.gather_qmm(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases,
@@ -474,16 +491,21 @@ def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     return row
 
 
-def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
-    """quantize of a dense bf16 weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64. Algorithmic bytes:
-    the weight read, the codes, scales and biases written."""
+def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget, dtype="bf16"):
+    """quantize of a dense weight [4096, 4096] ~ N(0, 0.02^2) to 4-bit g64, bf16 (or, with dtype
+    "f16", float16: the same draws converted), scales and biases in the weight's dtype. Algorithmic
+    bytes: the weight read, the codes, scales and biases written."""
     import numpy as np
     import oracle
     wl = W.WORKLOADS["quantize_4bit_g64_4096x4096"]
     w = W.dense_weight(wl.n, wl.k, "bf16", seed=wl.seed)
+    tdt = torch.bfloat16
+    if dtype == "f16":
+        w = W.f32_from_bf16_bits(w).astype(np.float16).view(np.uint16)
+        tdt = torch.float16
     nbytes = wl.n * wl.k * 2 + wl.n * wl.k * wl.bits // 8 + 2 * wl.n * (wl.k // wl.group_size) * 2
     copies = copies_for(nbytes)
-    ws = [torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16) for _ in range(copies)]
+    ws = [torch.from_numpy(w.view(np.int16)).cuda().view(tdt) for _ in range(copies)]
 
     def launch(i):
         q.quantize(ws[i % copies], wl.group_size, wl.bits)
@@ -492,10 +514,12 @@ def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     del ws
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    row = {"workload": "quantize bf16 [4096, 4096] -> 4-bit g64", "kernel": "quantize_kernel",
-           "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
+    name = {"bf16": "bf16", "f16": "float16"}[dtype]
+    row = {"workload": f"quantize {name} [4096, 4096] -> 4-bit g64, {name} scales and biases",
+           "kernel": "quantize_kernel", "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "copies": copies,
+           "roofline": hbm_roofline(gbs)}
     if cpu:
-        runs, el = cpu_time(lambda: oracle.quantize(w, "bf16", wl.group_size, wl.bits), cpu_budget, 100000)
+        runs, el = cpu_time(lambda: oracle.quantize(w, dtype, wl.group_size, wl.bits, dtype), cpu_budget, 100000)
         row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
     return row
@@ -949,8 +973,11 @@ def main():
         add(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0))
         add(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0))
         add(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
+        add(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0, dtype="f16"))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:
             add(bench_gather(torch, q, W, timer, tokens, rs, rw, cpu, 2.0))
+        add(bench_gather(torch, q, W, timer, W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms[-1], rs, rw, cpu, 2.0,
+                         f16=True))
         wl_p = W.WORKLOADS["moe_prefill_4bit_g64_e128_768x2048"]
         add(bench_gather(torch, q, W, timer, wl_p.ms[0], max(20, rs // 10), 5, cpu, 2.0, name=wl_p.name))
         full["rows"] = rows
