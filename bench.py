@@ -95,8 +95,10 @@ class Aux:
         lib = ctypes.CDLL(path)
         vp = ctypes.c_void_p
         lib.qaff_bench_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, vp]
+        lib.qaff_bench_read_store.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, vp, ctypes.c_uint32, vp]
         lib.qaff_bench_stamp.argtypes = [vp, vp]
         lib.qaff_bench_read.restype = lib.qaff_bench_stamp.restype = ctypes.c_int
+        lib.qaff_bench_read_store.restype = ctypes.c_int
         lib.qaff_bench_wall_clock_khz.restype = ctypes.c_int
         self.lib = lib
 
@@ -105,9 +107,14 @@ class Aux:
         if rc != 0:
             raise RuntimeError(f"qaff_bench_stamp: hip error {rc}")
 
-    def read(self, torch, src, per_thread, nt, sink):
-        rc = self.lib.qaff_bench_read(src.data_ptr(), src.numel() * src.element_size(), per_thread, nt,
-                                      0xFFFFFFFF, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    def read(self, torch, src, per_thread, nt, sink, out=None):
+        stream = torch.cuda.current_stream().cuda_stream
+        if out is None:
+            rc = self.lib.qaff_bench_read(src.data_ptr(), src.numel() * src.element_size(), per_thread, nt,
+                                          0xFFFFFFFF, sink.data_ptr(), stream)
+        else:
+            rc = self.lib.qaff_bench_read_store(src.data_ptr(), src.numel() * src.element_size(), per_thread, nt,
+                                                out.data_ptr(), out.numel(), stream)
         if rc != 0:
             raise RuntimeError(f"qaff_bench_read: hip error {rc}")
 
@@ -743,20 +750,24 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget):
     return row
 
 
-def plain_read(torch, timer, aux, nbytes, steps, warmup):
+def plain_read(torch, timer, aux, nbytes, steps, warmup, store=0):
     """The ceiling of a kernel that must read `nbytes` bytes once: a plain streaming read
     (qaff_bench_read) of that many bytes, rotated over about 1 GiB of copies like the product rows
     and timed the same way; the best of its eight launch shapes (1, 2, 4 or 8 16-byte loads per
-    thread, with and without the non-temporal bit)."""
+    thread, with and without the non-temporal bit). With `store` (an element count), every wave
+    also writes one dependent 2-byte result into an array of that many elements
+    (qaff_bench_read_store): the ceiling of a kernel that reads the bytes and writes its output."""
     copies = (1 << 30) // nbytes + 1
     srcs = [torch.randint(0, 1 << 30, (nbytes // 4,), dtype=torch.int32, device="cuda") for _ in range(copies)]
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    outs = [torch.zeros(store, dtype=torch.int16, device="cuda") for _ in range(copies)] if store else None
     shapes = {}
     for per_thread in (1, 2, 4, 8):
         for nt in (0, 1):
-            ms = timer(lambda i: aux.read(torch, srcs[i % copies], per_thread, nt, sink), steps, warmup)
+            ms = timer(lambda i: aux.read(torch, srcs[i % copies], per_thread, nt, sink,
+                                          outs[i % copies] if outs else None), steps, warmup)
             shapes[f"{per_thread}{'nt' if nt else ''}"] = round(ms * 1e3, 3)
-    del srcs
+    del srcs, outs
     torch.cuda.empty_cache()
     best = min(shapes, key=shapes.get)
     us = shapes[best]
@@ -768,12 +779,15 @@ def plain_read(torch, timer, aux, nbytes, steps, warmup):
 def bench_context(torch, timer, aux, metrics=None, sustain_s=0.0):
     """What the same box does on the same sizes without this library, timed the same way: an
     empty kernel launch, a plain streaming read of the decode step's bytes and of the 8-bit step's
-    (the ceiling of any kernel that reads them), a device copy of the decode step's bytes, and a
+    (the ceiling of any kernel that reads them), the decode step's read with one dependent 2-byte
+    store per wave into 4096 elements (the ceiling of a kernel that also writes y), a device copy
+    of the decode step's bytes, and a
     dense bf16 matmul at the prefill shape (the vendor BLAS). Context for the roofline fractions,
     not a result of the path."""
     steps = 1000
     empty_ms = timer(lambda i: torch.cuda._sleep(0), steps, 100)
     read_decode = plain_read(torch, timer, aux, 9453568, steps, 100)
+    read_store_decode = plain_read(torch, timer, aux, 9453568, steps, 100, store=4096)
     read_int8 = plain_read(torch, timer, aux, 62427136, 200, 20)
 
     nbytes = 9453568                                      # the decode step's algorithmic bytes
@@ -806,6 +820,7 @@ def bench_context(torch, timer, aux, metrics=None, sustain_s=0.0):
     res = {
         "empty_kernel_us_per_launch": round(empty_ms * 1e3, 3),
         "plain_read_decode_bytes": read_decode,
+        "plain_read_store_decode_bytes": read_store_decode,
         "plain_read_int8_bytes": read_int8,
         "copy_of_decode_bytes": {"bytes_read": nbytes, "bytes_written": nbytes,
                                  "us_per_step": round(copy_ms * 1e3, 3),
@@ -938,8 +953,10 @@ def main():
         ctx = bench_context(torch, timer, aux, metrics, args.sustain)
         full["context"] = ctx
         rd = ctx["plain_read_decode_bytes"]
+        rw = ctx["plain_read_store_decode_bytes"]
         result["ceiling"] = {"plain_read_us": rd["us_per_step"], "plain_read_frac": rd["frac"],
                              "headline_over_plain_read": round(ms * 1e3 / rd["us_per_step"], 3),
+                             "read_store_us": rw["us_per_step"], "read_store_frac": rw["frac"],
                              "empty_launch_us": ctx["empty_kernel_us_per_launch"],
                              "int8_plain_read_frac": ctx["plain_read_int8_bytes"]["frac"]}
         dm = ctx["dense_bf16_matmul_prefill"]

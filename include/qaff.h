@@ -305,8 +305,10 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
  *   scales and biases [w_batches, n, k/group_size] of sb_dtype (float32 4-byte aligned); the other
  *   arguments as qaff_gather_qmm. bf16 scales with a float32 or bf16 x take qaff_gather_qmm itself
  *   (the same kernels and results); every other combination runs on the typed VALU GEMV with grid z
- *   over the output batches (x 16-byte aligned; otherwise element by element). The sorted promise
- *   is used only by qaff_gather_qmm's kernels.
+ *   over the output batches (x 16-byte aligned; otherwise element by element), or, with the sorted
+ *   promise, one x row per batch, no lhs and at least 16 rows per weight batch on average, over the
+ *   experts, each walking its rows [#(rhs < e), #(rhs < e + 1)) and reading its weights once (as
+ *   with qaff_gather_qmm, unsorted rhs under the promise leaves results undefined).
  * Errors: as qaff_gather_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.
  */
 qaff_status qaff_gather_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t x_batches, int64_t m,

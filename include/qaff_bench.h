@@ -30,6 +30,14 @@ extern "C" {
 hipError_t qaff_bench_read(const void* src, size_t bytes, int chunks_per_thread, int nontemporal,
                            uint32_t magic, uint32_t* sink, hipStream_t stream);
 
+/* qaff_bench_read that also writes what a product writes: every wave folds its 64 lanes' loaded
+ * words together and its first lane stores the low 16 bits to out[wave % out_count] (`out`: uint16,
+ * out_count > 0 elements, 2-byte aligned; which wave's value an element keeps is unspecified).
+ * The ceiling of a kernel that reads the bytes once and then writes one dependent result per
+ * wave. hipErrorInvalidValue for other arguments. */
+hipError_t qaff_bench_read_store(const void* src, size_t bytes, int chunks_per_thread, int nontemporal,
+                                 uint16_t* out, uint32_t out_count, hipStream_t stream);
+
 /* Writes the device wall clock (ticks at qaff_bench_wall_clock_khz() kHz) to *slot. */
 hipError_t qaff_bench_stamp(uint64_t* slot, hipStream_t stream);
 

@@ -496,7 +496,13 @@ qaff_status qaff_gather_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t x_b
     g.w_stride = (uint64_t)(n * (k / 32) * bits);
     g.sb_stride = (uint64_t)(n * (k / group_size));
     g.y_stride = (uint64_t)(m * n);
+    // sorted rows, one per output batch, gathered by expert: the grouped walk once experts average
+    // 16 rows or more (each expert's weights are then read once; measured with float16 operands on
+    // 128 experts of [768, 2048]: 4 rows per expert 279 against 204 us batched, 32 rows 1385
+    // against 1506 us, 128 rows 5229 against 5957 us)
+    g.grouped = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices && batch >= 16 * w_batches;
     if ((x && !aligned(x, 16)) || !aligned(y, 16)) {  // the typed GEMV reads x in 16-byte loads
+        g.grouped = 0;
         qaff::ScalarGemv opt{};
         opt.gather = true;
         opt.g = g;

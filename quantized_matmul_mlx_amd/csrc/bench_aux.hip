@@ -10,9 +10,11 @@ typedef uint32_t u32x4a __attribute__((ext_vector_type(4)));
 
 // Block b reads chunks [b * 256 * U, (b + 1) * 256 * U), thread t those t + 256 u: every wave
 // instruction covers 1 KiB of consecutive bytes. All U loads are issued before any is used.
+// With `out`, every wave also folds its lanes' words together and its first lane stores the low
+// 16 bits to out[wave % out_count]: one dependent 2-byte result per wave, as a product writes.
 template <int U, bool NT>
 __global__ __launch_bounds__(256) void read_kernel(const u32x4a* __restrict__ src, uint64_t chunks, uint32_t magic,
-                                                   uint32_t* sink) {
+                                                   uint32_t* sink, uint16_t* out, uint32_t out_count) {
     const uint64_t base = (uint64_t)blockIdx.x * (256 * U) + threadIdx.x;
     u32x4a v[U];
 #pragma unroll
@@ -24,23 +26,43 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4a* __restrict__ sr
     uint32_t acc = 0u;
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    if (acc == magic) sink[0] = acc;
+    if (out) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, d, 64);
+        const uint64_t wave = ((uint64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+        if ((threadIdx.x & 63) == 0) out[wave % out_count] = (uint16_t)acc;
+    } else if (acc == magic) {
+        sink[0] = acc;
+    }
 }
 
 __global__ void stamp_kernel(uint64_t* slot) { *slot = (uint64_t)wall_clock64(); }
 
 template <int U>
-hipError_t launch_read(const void* src, uint64_t chunks, bool nt, uint32_t magic, uint32_t* sink, hipStream_t stream) {
+hipError_t launch_read(const void* src, uint64_t chunks, bool nt, uint32_t magic, uint32_t* sink, uint16_t* out,
+                       uint32_t out_count, hipStream_t stream) {
     const uint64_t blocks = (chunks + 256 * U - 1) / (256 * U);
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffULL) return hipErrorInvalidValue;
     if (nt)
         read_kernel<U, true><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<const u32x4a*>(src), chunks,
-                                                                               magic, sink);
+                                                                               magic, sink, out, out_count);
     else
         read_kernel<U, false><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<const u32x4a*>(src), chunks,
-                                                                                magic, sink);
+                                                                                magic, sink, out, out_count);
     return hipGetLastError();
+}
+
+hipError_t read_any(const void* src, size_t bytes, int chunks_per_thread, int nontemporal, uint32_t magic,
+                    uint32_t* sink, uint16_t* out, uint32_t out_count, hipStream_t stream) {
+    const uint64_t chunks = bytes / 16;
+    switch (chunks_per_thread) {
+        case 1: return launch_read<1>(src, chunks, nontemporal != 0, magic, sink, out, out_count, stream);
+        case 2: return launch_read<2>(src, chunks, nontemporal != 0, magic, sink, out, out_count, stream);
+        case 4: return launch_read<4>(src, chunks, nontemporal != 0, magic, sink, out, out_count, stream);
+        case 8: return launch_read<8>(src, chunks, nontemporal != 0, magic, sink, out, out_count, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -52,14 +74,15 @@ hipError_t qaff_bench_read(const void* src, size_t bytes, int chunks_per_thread,
     if (!src || !sink || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
         reinterpret_cast<uintptr_t>(sink) % 4 != 0)
         return hipErrorInvalidValue;
-    const uint64_t chunks = bytes / 16;
-    switch (chunks_per_thread) {
-        case 1: return launch_read<1>(src, chunks, nontemporal != 0, magic, sink, stream);
-        case 2: return launch_read<2>(src, chunks, nontemporal != 0, magic, sink, stream);
-        case 4: return launch_read<4>(src, chunks, nontemporal != 0, magic, sink, stream);
-        case 8: return launch_read<8>(src, chunks, nontemporal != 0, magic, sink, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return read_any(src, bytes, chunks_per_thread, nontemporal, magic, sink, nullptr, 1, stream);
+}
+
+hipError_t qaff_bench_read_store(const void* src, size_t bytes, int chunks_per_thread, int nontemporal,
+                                 uint16_t* out, uint32_t out_count, hipStream_t stream) {
+    if (!src || !out || out_count == 0 || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(src) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(out) % 2 != 0)
+        return hipErrorInvalidValue;
+    return read_any(src, bytes, chunks_per_thread, nontemporal, 0u, nullptr, out, out_count, stream);
 }
 
 hipError_t qaff_bench_stamp(uint64_t* slot, hipStream_t stream) {

@@ -8,7 +8,10 @@
 //  * gemv_typed_kernel: y = x . dequantize(W)^T on the VALU, float32 sums, x of any of the three
 //    types, y in the promoted type. Per block of 32 codes: s * sum(x c) + b * sum(x). Gathered
 //    (nuvec_core quantized.rs, `gather_qmm`): grid z is the output batch, x batch lhs[z] against
-//    weight batch rhs[z]; an index past its operand gives a NaN batch.
+//    weight batch rhs[z]; an index past its operand gives a NaN batch. Grouped (sorted rhs, one
+//    row per batch, no lhs): grid z is the expert e, whose rows [#(rhs < e), #(rhs < e + 1)) the
+//    block walks in tiles of MB, reading e's weights once for all of them; expert w_count takes
+//    the rows past every expert (NaN).
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -64,10 +67,31 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
     const int wave = threadIdx.x >> 6;
     const uint32_t n0 = (blockIdx.x * (kTypedThreads / 64) + wave) * kTypedRows;
     if (n0 >= n) return;  // wave-uniform; no block-level barrier
-    const uint32_t m0 = blockIdx.y * MB;
     const uint32_t k = kb * 32;
     const uint32_t gpr = kb >> gshift;
-    if (gathered) {
+    // x rows [t0, t1) in tiles of MB from t0, rows below m: one tile (grid y), or an expert's rows
+    uint32_t t0 = blockIdx.y * MB, t1 = t0 + 1;
+    if (gathered && ga.grouped) {
+        const uint32_t e = ga.b0 + blockIdx.z;
+        uint32_t r0, r1;
+        count_below2(ga.rhs, ga.batch, e, e + 1, lane, r0, r1);
+        if (e >= ga.w_count) {  // rows past every expert
+            for (uint32_t o = lane; o < (ga.batch - r0) * kTypedRows; o += 64) {
+                const uint32_t row = n0 + o % kTypedRows, i = r0 + o / kTypedRows;
+                if (row < n) store_from_f32(y, (size_t)i * n + row, yt, __builtin_nanf(""));
+            }
+            return;
+        }
+        if (r0 >= r1) return;
+        packed += (size_t)e * ga.w_stride;
+        const size_t sb = (size_t)e * ga.sb_stride * (st == 0 ? 4 : 2);
+        scales = static_cast<const uint8_t*>(scales) + sb;
+        biases = static_cast<const uint8_t*>(biases) + sb;
+        t0 = r0;
+        t1 = r1;
+        m = r1;  // the expert's last row bounds the tiles
+    } else if (gathered) {
+        const uint32_t m0 = t0;
         // this output batch's x, weight and y (element sizes: 4 for float32, else 2)
         const uint32_t z = ga.b0 + blockIdx.z;
         const uint32_t li = ga.lhs ? ga.lhs[z] : z;
@@ -87,6 +111,7 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
         biases = static_cast<const uint8_t*>(biases) + sb;
     }
 
+    for (uint32_t m0 = t0; m0 < t1; m0 += MB) {
     float acc[kTypedRows][MB];
 #pragma unroll
     for (int r = 0; r < kTypedRows; ++r)
@@ -164,6 +189,7 @@ __global__ __launch_bounds__(kTypedThreads) void gemv_typed_kernel(
             if (lane == 0 && row < n && m0 + i < m) store_from_f32(y, (size_t)(m0 + i) * n + row, yt, v);
         }
     }
+    }
 }
 
 template <int BITS>
@@ -186,7 +212,9 @@ hipError_t launch_gemv_mb(const void* x, int xt, int64_t m, const uint32_t* pack
     const unsigned gx = (unsigned)((n + (kTypedThreads / 64) * kTypedRows - 1) / ((kTypedThreads / 64) * kTypedRows));
     const size_t xsize = xt == 0 ? 4 : 2, ysize = yt == 0 ? 4 : 2;
     const int64_t max_rows = (int64_t)65535 * MB;
-    const int64_t batches = ga ? ga->batch : 1;
+    // grid z: output batches, or experts 0 .. w_count when grouped (then one grid row walks all x rows)
+    const int64_t batches = ga ? (ga->grouped ? (int64_t)ga->w_count + 1 : ga->batch) : 1;
+    if (ga && ga->grouped) m = 1;
     for (int64_t b0 = 0; b0 < batches; b0 += 65535) {
         Gather g = ga ? *ga : Gather{};
         g.b0 = (uint32_t)b0;
@@ -205,12 +233,12 @@ hipError_t launch_gemv_mb(const void* x, int xt, int64_t m, const uint32_t* pack
     return hipSuccess;
 }
 
-// x rows per block: 1 for a single row, else 4
+// x rows per block: 1 for a single row, else 4 (also for the grouped walk over an expert's rows)
 template <int BITS>
 hipError_t launch_gemv_bits(const void* x, int xt, int64_t m, const uint32_t* packed, const void* scales,
                             const void* biases, int st, int64_t n, int64_t kb, uint32_t gshift, void* y, int yt,
                             const Gather* ga, hipStream_t stream) {
-    if (m == 1) return launch_gemv_mb<BITS, 1>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, ga, stream);
+    if (m == 1 && !(ga && ga->grouped)) return launch_gemv_mb<BITS, 1>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, ga, stream);
     return launch_gemv_mb<BITS, 4>(x, xt, m, packed, scales, biases, st, n, kb, gshift, y, yt, ga, stream);
 }
 

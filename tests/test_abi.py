@@ -46,7 +46,7 @@ def test_bench_aids_export_every_declared_symbol(lib):
     # the benchmark's measurement aids: include/qaff_bench.h against libqaff_bench.so
     text = open(os.path.join(ROOT, "include", "qaff_bench.h")).read()
     declared = sorted(set(re.findall(r"\b(qaff_bench_[a-z_0-9]+)\s*\(", text)))
-    assert declared == ["qaff_bench_read", "qaff_bench_stamp", "qaff_bench_wall_clock_khz"]
+    assert declared == ["qaff_bench_read", "qaff_bench_read_store", "qaff_bench_stamp", "qaff_bench_wall_clock_khz"]
     aux = ctypes.CDLL(os.path.join(ROOT, "quantized_matmul_mlx_amd", "libqaff_bench.so"))
     for name in declared:
         assert hasattr(aux, name), f"{name} is declared in qaff_bench.h but not exported"
@@ -58,6 +58,12 @@ def test_bench_aids_export_every_declared_symbol(lib):
     assert aux.qaff_bench_read(A4, 64, 4, 0, 0, A16, NULL) != 0        # misaligned source
     assert aux.qaff_bench_read(A16, 64, 3, 0, 0, A16, NULL) != 0       # unsupported shape
     assert aux.qaff_bench_read(NULL, 64, 4, 0, 0, A16, NULL) != 0
+    aux.qaff_bench_read_store.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    aux.qaff_bench_read_store.restype = ctypes.c_int
+    assert aux.qaff_bench_read_store(A16, 64, 4, 0, A16, 0, NULL) != 0   # no output elements
+    assert aux.qaff_bench_read_store(A16, 64, 4, 0, A1, 8, NULL) != 0    # misaligned output
+    assert aux.qaff_bench_read_store(A16, 64, 5, 0, A16, 8, NULL) != 0   # unsupported shape
 
 
 def test_product_library_does_not_link_the_bench_aids(lib):

@@ -214,3 +214,44 @@ def test_gather_qmm_typed_unaligned_x_and_sorted_rows(orc):
     with pytest.raises(ValueError, match="typed VALU kernel"):
         qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
                           path="gemv_mfma")
+
+
+# The grouped walk (16 rows or more per expert on average): experts of several row tiles, empty
+# ones, one row, rows past every expert, and more than 1024 rows (the counting's search).
+@pytest.mark.parametrize("xt,sb,counts,past", [
+    ("f16", "f16", [39, 0, 1, 26, 14], 0),
+    ("f16", "f32", [23, 33, 0, 0, 22], 3),
+    ("f32", "f16", [130] * 8 + [0] * 8 + [7], 5),
+])
+def test_gather_qmm_typed_grouped(orc, xt, sb, counts, past):
+    E, n, k, G, bits = len(counts), 70, 256, 64, 4
+    packed, hs, hb, ds, db = typed_experts(bits, G, E, n, k, sb, seed=80 + E)
+    rhs = np.concatenate([np.repeat(np.arange(E, dtype=np.uint32), counts),
+                          np.full(past, E + 2, np.uint32)]).astype(np.uint32)
+    x32 = np.random.default_rng(81).standard_normal((rhs.size, 1, k)).astype(np.float32)
+    hx = x32 if xt == "f32" else x32.astype(np.float16).view(np.uint16)
+    banner(f"gather_qmm typed grouped x={xt} sb={sb} rows={rhs.size} past={past}")
+    y = qaff().gather_qmm(to_dev(hx, xt), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
+                          sorted_indices=True)
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, xt, packed, hs, hb, sb, G, bits, np.arange(rhs.size, dtype=np.uint32), rhs)
+    # the batched walk (no promise) computes every row the same way
+    y_b = qaff().gather_qmm(to_dev(hx, xt), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs))
+    torch.cuda.synchronize()
+    a, b = host(y), host(y_b)
+    np.testing.assert_array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                                  b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
+def test_gather_qmm_typed_moe_workload(orc):
+    # the 64-token mixture-of-experts layer with float16 x, scales and biases
+    wl = W.WORKLOADS["moe_4bit_g64_e128_768x2048"]
+    mi = W.moe_inputs(wl, 64)
+    to16 = lambda a: W.f32_from_bf16_bits(a).astype(np.float16).view(np.uint16)
+    hs, hb, hx = to16(mi.scales), to16(mi.biases), to16(mi.x_rows)
+    banner("gather_qmm typed moe 64 tokens")
+    y = qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(mi.packed), to_dev(hs, "f16"), to_dev(hb, "f16"),
+                          wl.group_size, wl.bits, rhs_indices=dev_u32(mi.expert), sorted_indices=True)
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, "f16", mi.packed, hs, hb, "f16", wl.group_size, wl.bits,
+                 np.arange(mi.expert.size, dtype=np.uint32), mi.expert)
