@@ -710,12 +710,12 @@ def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
     return res
 
 
-def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget):
-    """The prefill GEMM at a small batch (4-bit g128, W [4096, 14336], x bf16 [m, 14336]): few
-    tiles, so the automatic path splits K through a workspace (qaff_qmm_ws). Against the bf16
-    MFMA peak (2·m·n·k flop per step)."""
+def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, name="prefill_4bit_g128_4096x14336"):
+    """A prefill GEMM on the automatic path: by default the prefill weight at a small batch
+    (4-bit g128, W [4096, 14336], x bf16 [m, 14336]), whose few tiles split K through a workspace
+    (qaff_qmm_ws); or another GEMM workload. Against the bf16 MFMA peak (2·m·n·k flop per step)."""
     import oracle
-    wl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
+    wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, m=m)
     b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
     copies = copies_for(b)
@@ -732,8 +732,10 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget):
     flop = 2.0 * m * wl.n * wl.k
     tflops = flop / (ms * 1e-3) / 1e12
     lib = q._lib.load()
-    row = {"workload": f"prefill_4bit_g128_4096x14336 M={m} (small batch)",
-           "kernel": "gemm, K split through a workspace (qaff_qmm_ws)",
+    splits = int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)) > 0
+    kernel = "gemm_direct_kernel" + (" (general: K with a tail)" if wl.k % 1024 else "")
+    row = {"workload": f"{name} M={m}" + (" (small batch)" if splits else ""),
+           "kernel": kernel + (", K split through a workspace (qaff_qmm_ws)" if splits else ""),
            "splits_workspace_bytes": int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)),
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "tflops": round(tflops, 2), "weight_copies": copies,
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
@@ -975,6 +977,8 @@ def main():
             log("row: " + json.dumps(r))
         log("row: prefill GEMM at M = 128 (K split)")
         add(bench_prefill_small(torch, q, W, timer, 128, rs, rw, cpu, 2.0))
+        add(bench_prefill_small(torch, q, W, timer, 2048, max(20, rs // 10), 5, cpu, 2.0,
+                                name="prefill_4bit_g128_4096x11008"))
         for name, m in (("decode_4bit_g64_4096x4096", 4), ("int8_g64_14336x4096", 1),
                         ("int8_g64_14336x4096", 8), ("odd_3bit_g32_11008x4096", 1),
                         ("odd_3bit_g32_11008x4096", 16), ("odd_6bit_g32_11008x4096", 1),

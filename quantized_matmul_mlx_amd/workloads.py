@@ -68,6 +68,10 @@ WORKLOADS = {
     # Prefill GEMM: 4-bit g128, W [4096, 14336], bf16 x [2048, 14336].
     "prefill_4bit_g128_4096x14336": Workload("prefill_4bit_g128_4096x14336", 4, 128, 4096, 14336,
                                              (1e-3, 2e-2), (-0.15, 0.0), ms=(2048,)),
+    # A prefill GEMM whose K is not a whole number of 1024 codes: a down projection of an FFN with
+    # 11008 hidden units, 4-bit g128, W [4096, 11008], bf16 x [2048, 11008].
+    "prefill_4bit_g128_4096x11008": Workload("prefill_4bit_g128_4096x11008", 4, 128, 4096, 11008,
+                                             (1e-3, 2e-2), (-0.15, 0.0), ms=(2048,), seed=61),
     # Odd widths g32: codes straddle uint32 boundaries. W [11008, 4096], M = 1 and M = 16.
     "odd_3bit_g32_11008x4096": Workload("odd_3bit_g32_11008x4096", 3, 32, 11008, 4096,
                                         (1e-3, 2e-2), (-0.15, 0.0), ms=(1, 16)),

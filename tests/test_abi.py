@@ -305,8 +305,10 @@ def test_qmm_ws_checks(lib):
     assert size(7) == 0 and size(8) > 0 and size(16) > 0     # past it, from 8 rows: the split GEMM
     assert size(17) > 0 and size(128) > 0 and size(1024) > 0  # few GEMM tiles: K splits
     assert size(2048) == 0                                   # a tile per compute unit already
-    assert size(128, k=14336 + 64) == 0                      # K not a multiple of 1024
+    assert size(128, k=14336 + 64) > 0                       # K with a tail splits its whole chunks too
     assert size(128, k=1024) == 0                            # a single chunk of K
+    assert size(128, k=1024 + 64) == 0                       # ... also with a tail
+    assert size(128, k=960) == 0                             # no whole chunk
     assert qws(lib, ws=NULL) == INVALID                      # a workspace is needed here ...
     assert b"workspace" in lib.qaff_last_error()
     assert qws(lib, wsb=4) == INVALID                        # ... large enough

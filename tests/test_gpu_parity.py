@@ -275,6 +275,43 @@ def test_gemm_direct_widths(orc, bits, G, m, n, k):
     check_qmm(orc, inp, y, path="gemm")
 
 
+# K that is not a whole number of 1024-code chunks: the kernel's general variant walks the whole
+# chunks as usual and the remaining 64-code steps one at a time. K = 11008 (10 chunks and 12 steps),
+# 4160 (65 groups of 64 per row: scale rows only 2-byte aligned), 1056 at G = 32 (33 blocks: half a
+# step), 2176 and 3136 (short tails), and K below one chunk (only the tail).
+@pytest.mark.parametrize("bits,G,m,n,k", [(4, 128, 300, 300, 11008), (4, 64, 257, 264, 4160), (3, 32, 130, 200, 1056),
+                                          (8, 128, 64, 256, 2176), (5, 64, 200, 300, 3136), (6, 32, 140, 72, 800)])
+def test_gemm_general_k_tails(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + k)
+    banner(f"gemm K tail bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemm")
+    check_qmm(orc, inp, y, path="gemm")
+
+
+# The same with K split through the workspace (the last split also takes the tail).
+@pytest.mark.parametrize("bits,G,m,n,k", [(4, 128, 64, 300, 11008), (4, 64, 17, 520, 4160)])
+def test_gemm_general_split_k(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + k + 1)
+    assert qaff()._lib.load().qaff_qmm_workspace_size(m, n, k, G, bits) > 0
+    banner(f"gemm K tail, split K, bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="auto")
+    check_qmm(orc, inp, y, path="auto")
+
+
+# Scales and biases at a 2-byte offset with whole chunks of K: the general variant's element loads
+# of the scale windows, the same arithmetic as the aligned kernel (equal bits).
+def test_gemm_scales_at_two_byte_offset(orc):
+    inp = W.random_inputs(4, 64, 300, 2048, 300, seed=97)
+    p, s, b = dev_weights(inp)
+    s2, b2 = at_offset(s), at_offset(b)
+    assert s2.data_ptr() % 16 == 2 and b2.data_ptr() % 16 == 2
+    banner("gemm, scales at a 2-byte offset")
+    y = qaff().qmm(dev_x(inp.x, "bf16"), p, s2, b2, 64, 4, path="gemm")
+    torch.cuda.synchronize()
+    check_qmm(orc, inp, y, path="gemm")
+    assert torch.equal(y.view(torch.int16), run_qmm(inp, path="gemm").view(torch.int16))
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 15, 16, 17, 18])
 def test_dispatch_boundary_all_paths(orc, m):
     assert qaff().gemv_max_m() == 16
@@ -430,6 +467,11 @@ def test_full_prefill_gemm_every_row(orc):
     # all 2048 x rows against the oracle (every tile, sub-tile and accumulator slot of the launch
     # the benchmark times)
     _full_qmm(orc, "prefill_4bit_g128_4096x14336", 2048)
+
+
+def test_full_prefill_k_tail_gemm_every_row(orc):
+    # K = 11008 (ten whole chunks and a tail of twelve steps) at the batch the benchmark times
+    _full_qmm(orc, "prefill_4bit_g128_4096x11008", 2048)
 
 
 def test_full_decode_dequant_bit_exact(orc):
