@@ -40,6 +40,29 @@ constexpr int kNtPad = 33;     // floats per (phase, column block, row) in the L
 template <int BITS>
 constexpr int kNtRows = 8;
 
+// The 32 codes of a block as float32. 4-bit codes: the even and odd nibbles of each word go to the
+// bytes of two words (one AND, one shift-AND), whose bytes convert directly (v_cvt_f32_ubyte0..3);
+// the empty asm keeps the compiler from turning them back into one bit-field extract per code.
+template <int BITS>
+__device__ __forceinline__ void codes_f32(const uint32_t (&w)[BITS], float (&cf)[32]) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t lo = w[q] & 0x0f0f0f0fu;
+            uint32_t hi = (w[q] >> 4) & 0x0f0f0f0fu;
+            asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                cf[8 * q + 2 * e] = (float)((lo >> (8 * e)) & 0xffu);
+                cf[8 * q + 2 * e + 1] = (float)((hi >> (8 * e)) & 0xffu);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) cf[c] = (float)code_at<BITS>(w, c);
+    }
+}
+
 template <int BITS, int MB, bool XF32>
 __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     const void* x, uint32_t m, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
@@ -90,8 +113,7 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
         const float s = bf16_to_f32(sraw[i]);
         const float b = bf16_to_f32(braw[i]);
         float cf[32];
-#pragma unroll
-        for (int c = 0; c < 32; ++c) cf[c] = (float)code_at<BITS>(w[i], c);
+        codes_f32<BITS>(w[i], cf);
 #pragma unroll
         for (int r = 0; r < MB; ++r) {
             const float xsv = xv[i][r] * s;
@@ -124,17 +146,17 @@ __global__ __launch_bounds__(256) void qmm_nt_reduce_kernel(const float* ws, uin
     const uint32_t o = blockIdx.x * 256 + threadIdx.x;
     if (o >= m * n) return;
     const uint32_t r = o / n, col = o % n;
-    // in chunk order, eight loads in flight at a time
+    // in chunk order, 32 loads in flight at a time (indices past the last chunk re-read it and
+    // are not added)
     float sum = 0.f;
-    uint32_t s = 0;
-    for (; s + 8 <= chunks; s += 8) {
-        float v[8];
+    for (uint32_t s = 0; s < chunks; s += 32) {
+        float v[32];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = ws[((size_t)(s + j) * mb + r) * n + col];
+        for (int j = 0; j < 32; ++j) v[j] = ws[((size_t)min(s + j, chunks - 1) * mb + r) * n + col];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum += v[j];
+        for (int j = 0; j < 32; ++j)
+            if (s + j < chunks) sum += v[j];
     }
-    for (; s < chunks; ++s) sum += ws[((size_t)s * mb + r) * n + col];
     if (OUT_BF16) static_cast<uint16_t*>(y)[o] = to_bf16_bits(sum);
     else static_cast<float*>(y)[o] = sum;
 }
