@@ -249,7 +249,7 @@ def kernel_name(q, m, k):
     """The kernel the automatic dispatch picks for a bf16 x of m rows (the library's rule)."""
     if m > q.gemv_max_m():
         return "gemm"
-    if m >= q.gemv_mfma_min_m() and k % 512 == 0 and k <= 4096:
+    if m >= q.gemv_mfma_min_m(k) and k % 512 == 0 and k <= 32768:
         return "gemv_mfma"
     return "gemv"
 
@@ -982,7 +982,7 @@ def main():
         for name, m in (("decode_4bit_g64_4096x4096", 4), ("int8_g64_14336x4096", 1),
                         ("int8_g64_14336x4096", 8), ("odd_3bit_g32_11008x4096", 1),
                         ("odd_3bit_g32_11008x4096", 16), ("odd_6bit_g32_11008x4096", 1),
-                        ("odd_6bit_g32_11008x4096", 16)):
+                        ("odd_6bit_g32_11008x4096", 16), ("ffn_down_4bit_g64_4096x14336", 4)):
             add(bench_qmm(torch, q, W, timer, name, m, rs, rw, cpu, 2.0)[0])
         for out_dtype in ("f32", "bf16"):
             add(bench_dequant(torch, q, W, timer, "decode_4bit_g64_4096x4096", out_dtype, rs, rw,

@@ -57,10 +57,11 @@ typedef enum {
 typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1, QAFF_F16 = 2 } qaff_dtype;
 
 /* Kernel choice for qaff_qmm_ex. AUTO: float32 x -> the VALU kernel at any m; bf16 x with
- * m <= qaff_gemv_max_m() -> the decode path: the VALU GEMV for m below qaff_gemv_mfma_min_m(),
- * the matrix-core decode kernel (GEMV_MFMA) from there on where it applies (K a multiple of 512
- * and at most 4096, 4-byte aligned scales and biases), the VALU GEMV otherwise; bf16 x with a
- * larger m -> the bf16-MFMA GEMM. GEMV_MFMA forced on a shape it does not take is UNSUPPORTED. */
+ * m <= qaff_gemv_max_m() -> the decode path: the VALU GEMV for m below qaff_gemv_mfma_min_m()
+ * (below 2 where K exceeds 4096), the matrix-core decode kernel (GEMV_MFMA) from there on where it
+ * applies (K a multiple of 512 and at most 32768, 4-byte aligned scales and biases), the VALU GEMV
+ * otherwise; bf16 x with a larger m -> the bf16-MFMA GEMM. GEMV_MFMA forced on a shape it does not
+ * take is UNSUPPORTED. */
 typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2, QAFF_PATH_GEMV_MFMA = 3 } qaff_path;
 
 /*
@@ -175,7 +176,7 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
  * qaff_qmm (QAFF_PATH_AUTO) with a workspace that lets the bf16 GEMM path split K (nuvec_core
  * quantized_matmul with transpose, as qaff_qmm). Where the GEMM's 128 x 256 tiles are fewer than
  * the compute units (m up to about 1024 at n = 4096, K a multiple of 1024; and 8 <= m <= 16 with K
- * above 4096, which the decode kernels would otherwise take on the VALU), K is split into ranges
+ * above 32768, which the decode kernels would otherwise take on the VALU), K is split into ranges
  * of whole 1024-code chunks: each range's float32 partial sums go to `workspace`, and a second
  * kernel adds the ranges in a fixed order (results are deterministic) and rounds y to bf16.
  *   Arguments as qaff_qmm, plus workspace: a caller-owned device buffer of at least
@@ -191,7 +192,7 @@ qaff_status qaff_qmm_ws(const void* x, qaff_dtype x_dtype, int64_t m, const uint
 
 /* Bytes of workspace qaff_qmm_ws can use for these sizes with a bf16 x (0 where it would not split
  * K: enough tiles, K not a multiple of 1024, or m <= 16 inside the decode kernels' range). From 8
- * rows on, K above 4096 codes (past the matrix-core decode kernel) also takes the split GEMM. */
+ * rows on, K above 32768 codes (past the matrix-core decode kernel) also takes the split GEMM. */
 size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits);
 
 /*
@@ -356,7 +357,8 @@ int qaff_abi_version(void);
 /* Largest m that QAFF_PATH_AUTO sends to the decode path for a bf16 x. */
 int qaff_gemv_max_m(void);
 
-/* Smallest m that QAFF_PATH_AUTO sends to the matrix-core decode kernel (where it applies). */
+/* Smallest m that QAFF_PATH_AUTO sends to the matrix-core decode kernel (where it applies) for K
+ * up to 4096; above 4096 it is 2. */
 int qaff_gemv_mfma_min_m(void);
 
 #ifdef __cplusplus

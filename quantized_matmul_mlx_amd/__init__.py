@@ -101,10 +101,11 @@ def gemv_max_m() -> int:
     return int(_lib.load().qaff_gemv_max_m())
 
 
-def gemv_mfma_min_m() -> int:
+def gemv_mfma_min_m(k: int = 0) -> int:
     """Smallest number of bf16 x rows the automatic dispatch sends to the matrix-core decode
-    kernel (for the shapes it takes)."""
-    return int(_lib.load().qaff_gemv_mfma_min_m())
+    kernel (for the shapes it takes) at a K of k codes: the library's figure up to 4096, 2 above
+    (the rule qaff.h states for qaff_gemv_mfma_min_m)."""
+    return 2 if k > 4096 else int(_lib.load().qaff_gemv_mfma_min_m())
 
 
 def dequantize(packed, scales, biases, group_size: int, bits: int, out_dtype=torch.float32,

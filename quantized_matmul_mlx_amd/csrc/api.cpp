@@ -36,6 +36,9 @@ qaff_status fail(qaff_status st, const char* fmt, ...) {
 
 constexpr int kGemvMaxM = 16;
 constexpr int kGemvMfmaMinM = 3;
+// Past 4096 codes the VALU GEMV's long rows cost more: the matrix-core decode kernel wins from 2
+// rows there ([4096, 14336] 4-bit at m = 2: 11.2 against 12.4 us with groups of 64).
+int64_t gemv_mfma_min_m(int64_t k) { return k > 4096 ? 2 : kGemvMfmaMinM; }
 // Gathered products grouped by expert take the GEMM over each expert's rows once the experts
 // average this many rows (below, the matrix-core decode kernel's 16-row tiles).
 constexpr int64_t kGroupedGemmRows = 32;
@@ -158,7 +161,7 @@ qaff_status qaff_dequant_rows(const uint32_t* packed, const uint16_t* scales, co
 namespace {
 
 // Decode-sized m that take the GEMM with K split when a workspace is given: K beyond the
-// matrix-core decode kernel (more than 4096 codes) and a multiple of 1024, from kSplitMinM rows on,
+// matrix-core decode kernel (more than 32768 codes) and a multiple of 1024, from kSplitMinM rows on,
 // where the VALU GEMV's work per code and x row outweighs the GEMM's fixed cost.
 constexpr int64_t kSplitMinM = 8;
 bool split_gemv_range(int64_t m, int64_t k) {
@@ -185,7 +188,7 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
                          aligned(scales, 4) && aligned(biases, 4);
     if (path == QAFF_PATH_GEMV_MFMA && m > 0 && n > 0 && k > 0 && !mfma_ok)
         return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes 1 <= m <= 16, k a multiple "
-                    "of 512 up to 4096 and 4-byte aligned scales and biases", op);
+                    "of 512 up to 32768 and 4-byte aligned scales and biases", op);
     if (m == 0 || n == 0) return QAFF_OK;
     const int64_t esize = (int64_t)esize_of(x_dtype);
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
@@ -206,7 +209,7 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
     bool use_gemm = false, use_mfma = false;
     if (x_dtype == QAFF_BF16) {
         use_gemm = path == QAFF_PATH_GEMM || (path == QAFF_PATH_AUTO && m > kGemvMaxM);
-        use_mfma = path == QAFF_PATH_GEMV_MFMA || (path == QAFF_PATH_AUTO && m >= kGemvMfmaMinM && mfma_ok);
+        use_mfma = path == QAFF_PATH_GEMV_MFMA || (path == QAFF_PATH_AUTO && m >= gemv_mfma_min_m(k) && mfma_ok);
         // with a workspace (qaff_qmm_ws sized it for these m, n, k), a few rows beyond the matrix-core
         // decode kernel's K range take the GEMM with K split, which beats the VALU GEMV there
         if (path == QAFF_PATH_AUTO && ws && m <= kGemvMaxM && !mfma_ok && split_gemv_range(m, k) &&
@@ -370,7 +373,7 @@ qaff_status qaff_gather_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t x_batc
         return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: indices must be 4-byte aligned", op);
     if (x_batches >= 0xffffffffLL || w_batches >= 0xffffffffLL || batch >= 0xffffffffLL)
         return fail(QAFF_ERR_UNSUPPORTED, "%s: 2^32-1 or more batches", op);
-    const bool mfma_ok = x_dtype == QAFF_BF16 && qaff::gemv_mfma_supported(1, k) && aligned(scales, 4) &&
+    const bool mfma_ok = x_dtype == QAFF_BF16 && qaff::gemv_mfma_gather_supported(k) && aligned(scales, 4) &&
                          aligned(biases, 4);
     if (path == QAFF_PATH_GEMV_MFMA && batch > 0 && m > 0 && n > 0 && k > 0 && !mfma_ok)
         return fail(QAFF_ERR_UNSUPPORTED, "%s: the matrix-core decode kernel takes a bf16 x, k a multiple of 512 "

@@ -34,7 +34,8 @@
 //    are applied to the sums: s D + (b / 128 - s) X, with X = sum x 128 from one more MFMA per
 //    step against a constant 128 (shared by the tiles). The bands are added in the final sum.
 //    The weights are then not rounded to bf16: the result is the float32 product of the oracle.
-// Requirements (checked by the launcher): bf16 x, K a multiple of 512 and at most 4096.
+//  * Past 4096 codes, each wave takes several slices in turn (gemv_mfma_long_kernel).
+// Requirements (checked by the caller): bf16 x, K a multiple of 512 and at most 32768.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -43,7 +44,8 @@
 namespace qaff {
 namespace {
 
-constexpr int kSlice = 512;                // codes of K per wave
+constexpr int kSlice = 512;                // codes of K per wave (per slice past 4096 codes)
+constexpr int64_t kMaxK = 64 * kSlice;       // longest K taken: 8 waves of 8 slices (the narrow blocks)
 
 // v_cndmask_b32 with a lane mask: `if_set` in the lanes of `mask`, `if_clear` elsewhere.
 __device__ __forceinline__ uint32_t lane_select(uint64_t mask, uint32_t if_set, uint32_t if_clear) {
@@ -321,9 +323,193 @@ hipError_t launch_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const
     return hipGetLastError();
 }
 
+// ---- K past 4096 ---------------------------------------------------------------------------------
+//
+// The same tiles and slices over a longer K (the down projection's 14336 codes): a block of up to 16
+// waves owns 16 * NT rows (NT = 1 is launched), and wave w takes the slices [w S, min(w S + S,
+// K / 512)) one after another. While it multiplies one slice, the loads of the next (x rows, scale
+// and bias windows, codes) are in flight, in a second set of registers: the loop is unrolled by two
+// so that the two sets swap roles without copies. Each slice's x rows go through the wave's LDS region as in the
+// kernel above (LDS operations of one wave complete in order, so the next slice's stores follow
+// the reads of the last one without a wait).
+
+template <int BITS, int NT, int GSHIFT, int MB>
+struct SliceLoads {
+    u32x4a xg[MB];
+    SbWindow<GSHIFT> sw[NT], bw[NT];
+    uint32_t wq[NT][4][BITS];
+};
+
+// Issue the loads of slice s, oldest first: the x rows (rows past m repeat row m - 1), the scale
+// and bias windows of each tile, then the codes chunk by chunk. A slice that is not `real` (past
+// the wave's last) issues the same loads at harmless addresses whose results go unused: x rows of
+// slice s_last, codes and windows from the start of x (32 bytes per lane; x holds more than 8 KB
+// here). The loop below then has the same loads outstanding on every path.
+template <int BITS, int NT, int GSHIFT, int MB>
+__device__ __forceinline__ void load_slice(SliceLoads<BITS, NT, GSHIFT, MB>& L, const uint16_t* x, uint32_t m,
+                                           const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
+                                           uint32_t n, uint32_t n0, uint32_t kb, int s, int s_last, int lane) {
+    const bool real = s <= s_last;
+    const uint32_t k = kb * 32, gpr = kb >> GSHIFT;
+    const int lr16 = lane & 15, lg = lane >> 4;
+    const uint16_t* xs = x + (size_t)(real ? s : s_last) * kSlice + lane * 8;
+#pragma unroll
+    for (int r = 0; r < MB; ++r) L.xg[r] = *reinterpret_cast<const u32x4a*>(xs + (size_t)min((uint32_t)r, m - 1) * k);
+    const uint16_t* dummy = x + lane * 16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
+        const size_t e = (size_t)row * gpr + (size_t)s * (16 >> GSHIFT);
+        L.sw[t].load(real ? scales + e : dummy);
+        L.bw[t].load(real ? biases + e : dummy);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t row = min(n0 + 16 * t + lr16, n - 1);
+            const uint32_t jb = (uint32_t)s * 16 + 4 * c + lg;
+            const uint32_t* src = real ? packed + (size_t)row * kb * BITS + (size_t)jb * BITS
+                                       : reinterpret_cast<const uint32_t*>(dummy);
+            if constexpr (BITS == 4) {
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+                L.wq[t][c][0] = v.x; L.wq[t][c][1] = v.y; L.wq[t][c][2] = v.z; L.wq[t][c][3] = v.w;
+            } else {
+                load_block<BITS>(src, L.wq[t][c]);
+            }
+        }
+        asm volatile("" ::: "memory");
+    }
+}
+
+// The multiply of one loaded slice: its x rows into the wave's LDS region (exact codes: in the
+// codes' pair order), then the four chunks.
+template <int BITS, int NT, int GSHIFT, int MB>
+__device__ __forceinline__ void slice_product(SliceLoads<BITS, NT, GSHIFT, MB>& L, uint8_t* xl, const uint8_t* xa,
+                                              int sel, uint64_t sel_hi, const ExactConsts& ec, f32x4 (&acc)[NT],
+                                              int lane) {
+    constexpr bool kExact = kExactCodes<BITS, GSHIFT, MB>;
+#pragma unroll
+    for (int r = 0; r < MB; ++r)
+        *reinterpret_cast<u32x4a*>(xl + r * kXPitch + lane * 16) = kExact ? pair_order4(L.xg[r]) : L.xg[r];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        // chunk c's arithmetic starts after chunk c - 1's multiply (see the kernel above)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(L.wq[t][c][i]) : "v"(acc[0]));
+        chunk_product<BITS, NT, GSHIFT, MB>(c, L.wq, L.sw, L.bw, xa, sel, sel_hi, ec, acc);
+    }
+}
+
+// Whether a block may take 16 waves (1024 threads, hence at most 128 registers per lane): where the
+// two register sets fit in them without spills (from the compiler's register reports). Twice the
+// waves keep twice the loads in flight on a compute unit; the others take 8.
+template <int BITS, int GSHIFT, int MB>
+constexpr bool kWideBlock = MB == 4   ? !(BITS == 8 && GSHIFT == 0)
+                            : MB == 8 ? (BITS <= 2 || ((BITS == 3 || BITS == 4) && GSHIFT >= 1))
+                                      : false;
+
+template <int BITS, int NT, int GSHIFT, int MB, int S>
+__global__ __launch_bounds__((kWideBlock<BITS, GSHIFT, MB> ? 1024 : 512)) void gemv_mfma_long_kernel(
+    const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int waves = (int)(blockDim.x >> 6);
+    const uint32_t n0 = blockIdx.x * (16 * NT);
+    const int lr16 = lane & 15;
+    const int lg = lane >> 4;
+    // every wave has at least one slice: the launcher takes waves = ceil(slices / S)
+    const int s0 = wave * S;
+    const int s1 = min(s0 + S, (int)(kb >> 4));
+
+    constexpr bool kExact = kExactCodes<BITS, GSHIFT, MB>;
+    uint8_t* xl = smem + (size_t)wave * (MB * kXPitch);
+    uint8_t* zero = smem + (size_t)waves * (MB * kXPitch);
+    if constexpr (kExact) *reinterpret_cast<u32x4a*>(zero + lane * 16) = u32x4a{0u, 0u, 0u, 0u};
+    const uint8_t* xa = x_operand<GSHIFT, MB, kExact>(xl, zero, lr16, lg);
+    const int sel = fold_selector<GSHIFT, MB, kExact>(lg);
+    const uint64_t sel_hi = __builtin_amdgcn_ballot_w64(sel >= 2);
+    const ExactConsts ec = make_exact_consts();
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Two register sets in turn: while one slice is multiplied, the next one's loads are in flight
+    // (past the wave's last slice, loads that go unused: see load_slice). Unrolled in full: the
+    // compiler's waits before each multiply then cover that slice's loads alone (around a loop
+    // back-edge it also waited for the other set's).
+    SliceLoads<BITS, NT, GSHIFT, MB> a, b;
+    const int last = s1 - 1;
+    load_slice(a, x, m, packed, scales, biases, n, n0, kb, s0, last, lane);
+#pragma unroll
+    for (int i = 0; i < S; i += 2) {
+        if (i + 1 < S) load_slice(b, x, m, packed, scales, biases, n, n0, kb, s0 + i + 1, last, lane);
+        if (s0 + i <= last) slice_product(a, xl, xa, sel, sel_hi, ec, acc, lane);
+        if (i + 1 < S) {
+            if (i + 2 < S) load_slice(a, x, m, packed, scales, biases, n, n0, kb, s0 + i + 2, last, lane);
+            if (s0 + i + 1 <= last) slice_product(b, xl, xa, sel, sel_hi, ec, acc, lane);
+        }
+    }
+
+    // the waves' partial tiles (and the bands of exact codes) summed through LDS, as above
+    constexpr int kBands = kExact ? (4 >> GSHIFT) : 1;
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((wave * NT + t) * 4 + v) * 64 + lane] = acc[t][v];
+    __syncthreads();
+    for (int o = tid; o < 16 * MB * NT; o += (int)blockDim.x) {
+        const int t = o / (16 * MB), rem = o % (16 * MB);
+        const int mm = rem >> 4, nn = rem & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int p = 0; p < kBands; ++p) {
+            const int rr = p * MB + mm;
+            const int l = ((rr >> 2) << 4) | nn, v = rr & 3;
+            for (int w = 0; w < waves; ++w) sum += red[((w * NT + t) * 4 + v) * 64 + l];
+        }
+        const uint32_t row = n0 + 16 * t + nn;
+        if ((uint32_t)mm < m && row < n) y[(size_t)mm * n + row] = to_bf16_bits(sum);
+    }
+}
+
+template <int BITS, int GSHIFT, int MB, int S>
+hipError_t launch_long_s(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                         const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    const int64_t waves = (kb / 16 + S - 1) / S;
+    size_t lds = (size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>;
+    const size_t red = (size_t)waves * 4 * 64 * sizeof(float);
+    if (red > lds) lds = red;
+    gemv_mfma_long_kernel<BITS, 1, GSHIFT, MB, S><<<dim3((unsigned)((n + 15) / 16)), dim3((unsigned)waves * 64), lds,
+                                                    stream>>>(x, (uint32_t)m, packed, scales, biases, (uint32_t)n,
+                                                              (uint32_t)kb, y);
+    return hipGetLastError();
+}
+
+template <int BITS, int GSHIFT, int MB>
+hipError_t launch_long(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                       const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    // S slices per wave (2, 4 or 8), as few as the block's waves (16 or 8) allow, then as few waves
+    // as S needs. One row tile per block: with two, the two register sets no longer fit without
+    // spills, and n = 4096 already gives one block per compute unit.
+    constexpr int64_t kWaves = kWideBlock<BITS, GSHIFT, MB> ? 16 : 8;
+    const int64_t slices = kb / 16;
+    if (slices <= 2 * kWaves) return launch_long_s<BITS, GSHIFT, MB, 2>(x, m, packed, scales, biases, n, kb, y, stream);
+    if (slices <= 4 * kWaves) return launch_long_s<BITS, GSHIFT, MB, 4>(x, m, packed, scales, biases, n, kb, y, stream);
+    return launch_long_s<BITS, GSHIFT, MB, 8>(x, m, packed, scales, biases, n, kb, y, stream);
+}
+
 template <int BITS, int GSHIFT, int MB>
 hipError_t launch_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                     const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
+    if (kb > 8 * (kSlice / 32)) return launch_long<BITS, GSHIFT, MB>(x, m, packed, scales, biases, n, kb, y, stream);
     // The kernel is latency-bound: all blocks should be resident at once. A block's LDS (its x
     // slices: MB x 1040 bytes per wave) sets how many fit on a compute unit; each block takes as
     // many 16-row tiles (1 to 4) as needed to cover n in one round of the compute units.
@@ -601,8 +787,11 @@ hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t*
 }
 
 bool gemv_mfma_supported(int64_t m, int64_t k) {
-    return m >= 1 && m <= 16 && k % kSlice == 0 && k <= 8 * kSlice;
+    return m >= 1 && m <= 16 && k % kSlice == 0 && k > 0 && k <= kMaxK;
 }
+
+// the gathered kernel: one slice per wave, at most 8 waves
+bool gemv_mfma_gather_supported(int64_t k) { return k % kSlice == 0 && k > 0 && k <= 8 * kSlice; }
 
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                             const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,

@@ -64,7 +64,8 @@ hipError_t launch_gemv_gather(const void* x, bool x_f32, int64_t m, const uint32
 
 // The decode product on the matrix cores: y[m, n] (bf16) = x (bf16) . dequantize(W)^T for
 // 1 <= m <= 16, with each code dequantized to bf16 in registers. Only for shapes where
-// gemv_mfma_supported(m, k) holds, and scales/biases 4-byte aligned.
+// gemv_mfma_supported(m, k) holds (k a multiple of 512 up to 32768), and scales/biases 4-byte
+// aligned.
 bool gemv_mfma_supported(int64_t m, int64_t k);
 hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed,
                             const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
@@ -72,7 +73,9 @@ hipError_t launch_gemv_mfma(const uint16_t* x, int64_t m, const uint32_t* packed
 
 // The matrix-core decode kernel over gathered batches (any m, in tiles of up to 16 rows; bf16), or
 // with g.grouped over the rows of each expert, reading each expert's weights once. Only where
-// gemv_mfma_supported(1, k) holds and scales/biases are 4-byte aligned.
+// gemv_mfma_gather_supported(k) holds (k a multiple of 512 up to 4096) and scales/biases are
+// 4-byte aligned.
+bool gemv_mfma_gather_supported(int64_t k);
 hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t* packed,
                                    const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
                                    int group_size, int bits, uint16_t* y, const Gather& g,

@@ -47,7 +47,8 @@ hipError_t launch_gemv_f16(const uint16_t*, int64_t, const uint32_t*, const uint
                            int64_t, int, int, uint16_t*, hipStream_t) { return rec("gemv_f16"); }
 hipError_t launch_gemv_gather(const void*, bool, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
                               int64_t, int, int, void*, const Gather&, hipStream_t) { return rec("gemv_gather"); }
-bool gemv_mfma_supported(int64_t m, int64_t k) { return m >= 1 && m <= 16 && k % 512 == 0 && k > 0 && k <= 4096; }
+bool gemv_mfma_supported(int64_t m, int64_t k) { return m >= 1 && m <= 16 && k % 512 == 0 && k > 0 && k <= 32768; }
+bool gemv_mfma_gather_supported(int64_t k) { return k % 512 == 0 && k > 0 && k <= 4096; }
 hipError_t launch_gemv_mfma(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
                             int64_t, int, int, uint16_t*, hipStream_t) { return rec("gemv_mfma"); }
 hipError_t launch_gemv_mfma_gather(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
@@ -123,7 +124,9 @@ int main() {
     // qmm: dispatch by m and dtype, forced paths, k = 0
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 1, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 4, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
-    EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 4, P16, S16, B16, 64, 4096 + 512 * 2, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 2, P16, S16, B16, 64, 4096 + 512 * 2, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 1, P16, S16, B16, 64, 4096 + 512 * 2, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 4, P16, S16, B16, 64, 32768 + 1024, 64, 4, A16, nullptr));
     EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 17, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_F32, 300, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(UNS, "", qaff_qmm_ex(A16, QAFF_F32, 300, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr, QAFF_PATH_GEMM));

@@ -163,10 +163,10 @@ def test_dtype_and_path_checks(lib):
     assert qmm(lib, xdt=F32, path=2) == UNSUPPORTED      # the MFMA GEMM takes bf16 x only
     assert b"bf16" in lib.qaff_last_error()
     assert qmm(lib, xdt=F32, path=3) == UNSUPPORTED      # so does the matrix-core decode kernel
-    # the matrix-core decode kernel: k a multiple of 512 up to 4096, m <= 16, 4-byte scale words
+    # the matrix-core decode kernel: k a multiple of 512 up to 32768, m <= 16, 4-byte scale words
     assert qmm(lib, k=64, path=3) == UNSUPPORTED
     assert b"matrix-core decode" in lib.qaff_last_error()
-    assert qmm(lib, k=8192, path=3) == UNSUPPORTED
+    assert qmm(lib, k=32768 + 512, path=3) == UNSUPPORTED
     assert qmm(lib, m=17, k=512, path=3) == UNSUPPORTED
     assert qmm(lib, k=512, scales=A2, path=3) == UNSUPPORTED
     assert rows(lib, dt=-1) == INVALID
@@ -301,8 +301,9 @@ def qws(lib, m=128, n=4096, k=14336, G=128, bits=4, x=A16, y=A16, ws=A16, wsb=1 
 
 def test_qmm_ws_checks(lib):
     size = lambda m, n=4096, k=14336: lib.qaff_qmm_workspace_size(m, n, k, 128, 4)
-    assert size(16, k=4096) == 0                             # the matrix-core decode kernel's range
-    assert size(7) == 0 and size(8) > 0 and size(16) > 0     # past it, from 8 rows: the split GEMM
+    assert size(16, k=4096) == 0 and size(16) == 0           # the matrix-core decode kernel's range
+    far = 33792                                              # past it (above 32768), from 8 rows:
+    assert size(7, k=far) == 0 and size(8, k=far) > 0 and size(16, k=far) > 0  # the split GEMM
     assert size(17) > 0 and size(128) > 0 and size(1024) > 0  # few GEMM tiles: K splits
     assert size(2048) == 0                                   # a tile per compute unit already
     assert size(128, k=14336 + 64) > 0                       # K with a tail splits its whole chunks too

@@ -53,9 +53,9 @@ def run_qmm(inp, m_rows=None, path="auto"):
 
 
 def mfma_decode_takes(inp):
-    """Shapes the matrix-core decode kernel takes: 1 <= m <= 16, k a multiple of 512 up to 4096."""
+    """Shapes the matrix-core decode kernel takes: 1 <= m <= 16, k a multiple of 512 up to 32768."""
     m, k = inp.x.shape[0], inp.wl.k
-    return 1 <= m <= 16 and k % 512 == 0 and k <= 4096
+    return 1 <= m <= 16 and k % 512 == 0 and k <= 32768
 
 
 def kernel_of(inp, path):
@@ -71,7 +71,7 @@ def kernel_of(inp, path):
     wl = inp.wl
     if path == "auto" and qaff()._lib.load().qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits) > 0:
         return "gemm"
-    if path == "gemv_mfma" or (path == "auto" and m >= qaff().gemv_mfma_min_m() and mfma_decode_takes(inp)):
+    if path == "gemv_mfma" or (path == "auto" and m >= qaff().gemv_mfma_min_m(wl.k) and mfma_decode_takes(inp)):
         return "gemv_mfma"
     return "gemv"
 
@@ -251,10 +251,10 @@ def test_gemm_split_k(orc, bits, G, m, n, k, splits):
     assert orc.max_row_rel_err(a, b) <= 1e-2  # two float32 summation orders, each rounded to bf16
 
 
-# Decode-sized m with K past the matrix-core decode kernel's range: from 8 rows on the automatic
-# path takes the split GEMM (faster than the VALU GEMV there); below, the VALU GEMV.
-@pytest.mark.parametrize("bits,G,m,k,gemm", [(4, 128, 8, 5120, True), (4, 64, 16, 6144, True), (6, 32, 12, 5120, True),
-                                             (4, 128, 7, 5120, False)])
+# Decode-sized m with K past the matrix-core decode kernel's range (32768 codes): from 8 rows on the
+# automatic path takes the split GEMM (faster than the VALU GEMV there); below, the VALU GEMV.
+@pytest.mark.parametrize("bits,G,m,k,gemm", [(4, 128, 8, 33792, True), (4, 64, 16, 34816, True),
+                                             (6, 32, 12, 33792, True), (4, 128, 7, 33792, False)])
 def test_decode_sized_m_split_gemm(orc, bits, G, m, k, gemm):
     n = 300
     inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + k)
@@ -382,8 +382,41 @@ def test_gemv_mfma_balanced_tiles(orc, bits, n):
     check_qmm(orc, inp, y, path="gemv_mfma")
 
 
+# K past 4096: each wave takes S slices of 512 codes in turn (S = 2, 4 or 8, blocks of up to 16
+# waves where two register sets fit 128 registers, else 8). 4608 codes (9 slices) leave the last
+# wave one slice (its second set loads unused data, its second multiply is skipped); 14336 takes
+# 14 waves of 2 (or 7 of 4); 16896 (33 slices) 9 waves of 4 (or 5 of 8), the last with one; 32768
+# 16 waves of 4 (or 8 of 8). Ragged n, every width and group size, m from 1 to 16.
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("m,n,k", [(1, 40, 4608), (4, 150, 14336), (8, 77, 16896), (16, 40, 32768),
+                                   (3, 150, 8192), (12, 33, 14336)])
+def test_gemv_mfma_long_k(orc, bits, G, m, n, k):
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits * 7 + G + m + n + k)
+    banner(f"gemv_mfma long k bits={bits} G={G} m={m} n={n} k={k}")
+    y = run_qmm(inp, path="gemv_mfma")
+    check_qmm(orc, inp, y, path="gemv_mfma")
+
+
+# The automatic path at K past 4096 takes the matrix-core decode kernel from 2 rows on, and its
+# results are those of the forced path.
+@pytest.mark.parametrize("m", [1, 2, 5, 16])
+def test_long_k_dispatch(orc, m):
+    inp = W.random_inputs(4, 64, 96, 5120, m, seed=m + 5)
+    banner(f"long k dispatch m={m}")
+    y = run_qmm(inp)
+    check_qmm(orc, inp, y)
+    assert kernel_of(inp, "auto") == ("gemv_mfma" if m >= 2 else "gemv")
+    want = run_qmm(inp, path=kernel_of(inp, "auto"))
+    assert torch.equal(y.view(torch.int16), want.view(torch.int16))
+
+
 def test_gemv_mfma_rejects_other_shapes(orc):
     inp = W.random_inputs(4, 32, 8, 768, 4, seed=1)   # k not a multiple of 512
+    p, s, b = dev_weights(inp)
+    with pytest.raises(qaff().QaffError, match="matrix-core decode"):
+        qaff().qmm(dev_x(inp.x, "bf16"), p, s, b, 32, 4, path="gemv_mfma")
+    inp = W.random_inputs(4, 32, 8, 33280, 4, seed=1)  # k above 32768
     p, s, b = dev_weights(inp)
     with pytest.raises(qaff().QaffError, match="matrix-core decode"):
         qaff().qmm(dev_x(inp.x, "bf16"), p, s, b, 32, 4, path="gemv_mfma")
@@ -472,6 +505,12 @@ def test_full_prefill_gemm_every_row(orc):
 def test_full_prefill_k_tail_gemm_every_row(orc):
     # K = 11008 (ten whole chunks and a tail of twelve steps) at the batch the benchmark times
     _full_qmm(orc, "prefill_4bit_g128_4096x11008", 2048)
+
+
+@pytest.mark.parametrize("m", [4, 16])
+def test_full_down_projection_long_k(orc, m):
+    # [4096, 14336] 4-bit g64: the long-K matrix-core decode kernel, every row against the oracle
+    _full_qmm(orc, "ffn_down_4bit_g64_4096x14336", m)
 
 
 def test_full_decode_dequant_bit_exact(orc):
