@@ -354,8 +354,8 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     g64, 8 experts per token, the tokens' rows sorted by expert (rows = 8 * tokens, x [rows, 1, k]).
     Algorithmic bytes: the weights of the experts in use, x rows, y rows. At prefill size (experts
     averaging 32 rows or more: the grouped GEMM) the row is in TFLOP/s against the bf16 MFMA peak.
-    f16: x, scales and biases as float16 (the workload's values converted; y float16): the typed
-    gathered GEMV."""
+    f16: x, scales and biases as float16 (the workload's values converted; y float16): the float16
+    forms of the same kernels."""
     import numpy as np
     import oracle
     wl = W.WORKLOADS[name]
@@ -389,13 +389,15 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     del dev, ys
     torch.cuda.empty_cache()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    grouped = rows >= wl.experts and not f16
-    gemm = rows >= 32 * wl.experts and not f16
+    grouped = rows >= wl.experts
+    gemm = rows >= 32 * wl.experts
     kernel = "gemm_grouped" if gemm else ("gemv_mfma_gather (grouped)" if grouped else "gemv_gather (batched)")
+    if f16:
+        kernel = kernel.replace("gemv_gather (batched)", "gemv_typed_kernel (gathered)") + (", float16" if grouped else "")
     row = {"workload": f"gather_qmm {wl.experts} experts [768, 2048] 4-bit g64, top-{wl.top_k}, {tokens} token(s), "
                        f"{rows} rows sorted by expert ({used} experts in use)" +
                        (", float16 x, scales and biases" if f16 else ""),
-           "kernel": "gemv_typed_kernel (gathered)" if f16 else kernel,
+           "kernel": kernel,
            "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "weight_copies": copies,
            "roofline": hbm_roofline(gbs)}
     if gemm:
@@ -405,13 +407,17 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
         row["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
     if cpu and gemm:
-        # a sample: the rows of the first expert through the oracle's product
-        threads = oracle.default_threads()
+        # a sample: the rows of the first expert through the oracle's product (the typed one on one
+        # thread)
+        threads = 1 if f16 else oracle.default_threads()
         sel = np.flatnonzero(mi.expert == mi.expert[0])
-        xs = np.ascontiguousarray(mi.x_rows[sel, 0, :])
+        xs = np.ascontiguousarray((hx if f16 else mi.x_rows)[sel, 0, :])
         e0 = int(mi.expert[0])
         t0 = time.perf_counter()
-        oracle.qmm(xs, "bf16", mi.packed[e0], mi.scales[e0], mi.biases[e0], wl.group_size, wl.bits, threads=threads)
+        if f16:
+            oracle.qmm_typed(xs, "f16", mi.packed[e0], hs[e0], hb[e0], "f16", wl.group_size, wl.bits)
+        else:
+            oracle.qmm(xs, "bf16", mi.packed[e0], mi.scales[e0], mi.biases[e0], wl.group_size, wl.bits, threads=threads)
         el = time.perf_counter() - t0
         row["cpu_baseline"] = {"value": round(2.0 * sel.size * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
                                "cores": threads, "kind": "oracle",
@@ -462,22 +468,23 @@ def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     return row
 
 
-def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
+def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget, m=1):
     """qmm with float16 x, scales and biases (y float16) at the decode shape W [4096, 4096] 4-bit
-    g64, M = 1: the typed VALU GEMV. The scales and biases are the decode workload's, as float16."""
+    g64: at M = 1 the GEMV in float16, at M = 4 the matrix-core decode kernel in float16. The scales,
+    biases and x are the decode workload's, as float16."""
     import numpy as np
     import oracle
     wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
-    inp = W.make_inputs(wl, m=1)
+    inp = W.make_inputs(wl, m=m)
     s16 = W.f32_from_bf16_bits(inp.scales).astype(np.float16).view(np.uint16)
     b16 = W.f32_from_bf16_bits(inp.biases).astype(np.float16).view(np.uint16)
     x16 = W.f32_from_bf16_bits(inp.x).astype(np.float16).view(np.uint16)
-    b = qmm_bytes(1, wl.n, wl.k, wl.bits, wl.group_size)
+    b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
     copies = copies_for(b)
     h = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
     sets = [{"packed": torch.from_numpy(inp.packed.view(np.int32)).cuda(), "scales": h(s16), "biases": h(b16),
              "x": h(x16)} for _ in range(copies)]
-    ys = [torch.empty((1, wl.n), dtype=torch.float16, device="cuda") for _ in range(copies)]
+    ys = [torch.empty((m, wl.n), dtype=torch.float16, device="cuda") for _ in range(copies)]
 
     def launch(i):
         s = sets[i % copies]
@@ -487,7 +494,8 @@ def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     del sets, ys
     torch.cuda.empty_cache()
     gbs = b / (ms * 1e-3) / 1e9
-    row = {"workload": "qmm float16 x, scales and biases, W [4096, 4096] 4-bit g64, M=1", "kernel": "gemv_typed_kernel",
+    kernel = "gemv_mfma_kernel, float16" if m >= q.gemv_mfma_min_m(wl.k) else "gemv_bf16_kernel, float16 format"
+    row = {"workload": f"qmm float16 x, scales and biases, W [4096, 4096] 4-bit g64, M={m}", "kernel": kernel,
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
         threads = oracle.default_threads()
@@ -710,17 +718,28 @@ def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
     return res
 
 
-def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, name="prefill_4bit_g128_4096x14336"):
+def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, name="prefill_4bit_g128_4096x14336",
+                        f16=False):
     """A prefill GEMM on the automatic path: by default the prefill weight at a small batch
     (4-bit g128, W [4096, 14336], x bf16 [m, 14336]), whose few tiles split K through a workspace
-    (qaff_qmm_ws); or another GEMM workload. Against the bf16 MFMA peak (2·m·n·k flop per step)."""
+    (qaff_qmm_ws); or another GEMM workload. Against the 16-bit MFMA peak (2·m·n·k flop per step;
+    bf16 and float16 have the same). f16: x, scales and biases as float16 (the workload's values
+    converted), the GEMM in float16."""
+    import numpy as np
     import oracle
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, m=m)
     b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
     copies = copies_for(b)
-    sets = replicate(torch, to_device(torch, inp), copies)
-    ys = [torch.empty((m, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    if f16:
+        to16 = lambda a: W.f32_from_bf16_bits(a).astype(np.float16).view(np.uint16)
+        h16 = {"x": to16(inp.x), "scales": to16(inp.scales), "biases": to16(inp.biases)}
+        h = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+        sets = [{"packed": torch.from_numpy(inp.packed.view(np.int32)).cuda(), "scales": h(h16["scales"]),
+                 "biases": h(h16["biases"]), "x": h(h16["x"])} for _ in range(copies)]
+    else:
+        sets = replicate(torch, to_device(torch, inp), copies)
+    ys = [torch.empty((m, wl.n), dtype=torch.float16 if f16 else torch.bfloat16, device="cuda") for _ in range(copies)]
 
     def launch(i):
         s = sets[i % copies]
@@ -732,11 +751,11 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, n
     flop = 2.0 * m * wl.n * wl.k
     tflops = flop / (ms * 1e-3) / 1e12
     lib = q._lib.load()
-    splits = int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)) > 0
-    kernel = "gemm_direct_kernel" + (" (general: K with a tail)" if wl.k % 1024 else "")
-    row = {"workload": f"{name} M={m}" + (" (small batch)" if splits else ""),
+    splits = int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)) > 0 and not f16
+    kernel = "gemm_direct_kernel" + (" (general: K with a tail)" if wl.k % 1024 else "") + (", float16" if f16 else "")
+    row = {"workload": f"{name} M={m}" + (" (small batch)" if splits else "") + (", float16 x, scales and biases" if f16 else ""),
            "kernel": kernel + (", K split through a workspace (qaff_qmm_ws)" if splits else ""),
-           "splits_workspace_bytes": int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)),
+           "splits_workspace_bytes": int(lib.qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits)) if splits else 0,
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "tflops": round(tflops, 2), "weight_copies": copies,
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
@@ -744,7 +763,12 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, n
         threads = oracle.default_threads()
         rows = 64
         t0 = time.perf_counter()
-        oracle.qmm(inp.x[:rows], "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, threads=threads)
+        if f16:  # the typed oracle runs on one thread
+            rows, threads = 8, 1
+            oracle.qmm_typed(h16["x"][:rows], "f16", inp.packed, h16["scales"], h16["biases"], "f16", wl.group_size,
+                             wl.bits)
+        else:
+            oracle.qmm(inp.x[:rows], "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits, threads=threads)
         el = time.perf_counter() - t0
         row["cpu_baseline"] = {"value": round(2.0 * rows * wl.n * wl.k / el / 1e12, 6), "unit": "TFLOP/s",
                                "cores": threads, "kind": "oracle",
@@ -993,6 +1017,8 @@ def main():
             add(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
         add(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0))
         add(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0))
+        add(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0, m=4))
+        add(bench_prefill_small(torch, q, W, timer, 2048, max(20, rs // 10), 5, cpu, 2.0, f16=True))
         add(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0))
         add(bench_quantize(torch, q, W, timer, rs, rw, cpu, 2.0, dtype="f16"))
         for tokens in W.WORKLOADS["moe_4bit_g64_e128_768x2048"].ms:
@@ -1001,6 +1027,7 @@ def main():
                          f16=True))
         wl_p = W.WORKLOADS["moe_prefill_4bit_g64_e128_768x2048"]
         add(bench_gather(torch, q, W, timer, wl_p.ms[0], max(20, rs // 10), 5, cpu, 2.0, name=wl_p.name))
+        add(bench_gather(torch, q, W, timer, wl_p.ms[0], max(20, rs // 10), 5, cpu, 2.0, name=wl_p.name, f16=True))
         full["rows"] = rows
         result["rows"] = len(rows)
 

@@ -104,9 +104,12 @@ qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, co
  * y = x . dequantize(W)^T with x of x_dtype and scales and biases of sb_dtype (each float32, bf16 or
  * float16); y [m, n] of qaff_promote_dtype(x_dtype, sb_dtype); float32 sums.
  * bf16 scales with a float32 or bf16 x take qaff_qmm's kernels (QAFF_PATH_AUTO); float16 x with
- * float16 scales and biases take the bf16 GEMV's layout in float16 (codes as the exact values
- * 1024 + c, v_dot2_f32_f16, float32 sums, y rounded to nearest even); every other combination runs
- * on a VALU GEMV that reads the types as given (any m, any k).
+ * float16 scales and biases take their float16 forms under the same rules, without the K split:
+ * below the matrix-core rows the GEMV in float16 (codes as the exact values 1024 + c,
+ * v_dot2_f32_f16), then the matrix-core decode kernel (exact 4-bit codes 1024 + c where they apply,
+ * else weights rounded to float16; float16 MFMA), past 16 rows the GEMM (weights rounded to
+ * float16, float16 MFMA); float32 sums, y rounded to nearest even. Every other combination runs on
+ * a VALU GEMV that reads the types as given (any m, any k).
  * Errors: as qaff_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.
  */
 qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
@@ -305,7 +308,10 @@ qaff_status qaff_gather_qmm(const void* x, qaff_dtype x_dtype, int64_t x_batches
  * qaff_promote_dtype(x_dtype, sb_dtype); float32 sums.
  *   scales and biases [w_batches, n, k/group_size] of sb_dtype (float32 4-byte aligned); the other
  *   arguments as qaff_gather_qmm. bf16 scales with a float32 or bf16 x take qaff_gather_qmm itself
- *   (the same kernels and results); every other combination runs on the typed VALU GEMV with grid z
+ *   (the same kernels and results); float16 x, scales and biases take the float16 forms of its
+ *   matrix-core kernels under its rules (the grouped GEMM, the grouped or batched decode kernel;
+ *   x and y 16-byte aligned) and otherwise the typed GEMV below; every other combination runs on
+ *   the typed VALU GEMV with grid z
  *   over the output batches (x 16-byte aligned; otherwise element by element), or, with the sorted
  *   promise, one x row per batch, no lhs and at least 16 rows per weight batch on average, over the
  *   experts, each walking its rows [#(rhs < e), #(rhs < e + 1)) and reading its weights once (as

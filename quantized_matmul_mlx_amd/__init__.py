@@ -206,7 +206,9 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
     (``qmm_nt``).
 
     x may also be float16, and the scales and biases float16 or float32: x, scales and biases then
-    promote to one type (float32 unless they agree), which is y's type."""
+    promote to one type (float32 unless they agree), which is y's type. A float16 x with float16
+    scales and biases runs on the float16 forms of the kernels above, chosen as for bf16; other
+    mixes on a typed VALU kernel. Either way the library picks the kernel (path 'auto')."""
     if not transpose:
         if path != "auto":
             raise ValueError("the product without the transpose has one kernel: path 'auto'")
@@ -226,9 +228,10 @@ def qmm(x, packed, scales, biases, group_size: int, bits: int, path: str = "auto
         raise ValueError(f"path must be one of {tuple(_lib.PATHS)}")
     sb = _sb_code(scales)
     if sb != _lib.QAFF_BF16 or x.dtype == torch.float16:
-        # x, scales and biases promote to one type (float32 unless they agree); the typed kernel
+        # x, scales and biases promote to one type (float32 unless they agree); the library picks
+        # the kernel
         if path != "auto":
-            raise ValueError("float16 x or non-bf16 scales run on one kernel: path 'auto'")
+            raise ValueError("float16 x or non-bf16 scales take the automatic path: path 'auto'")
         lead = tuple(x.shape[:-1])
         m = math.prod(lead)
         yt = _FROM_CODE[int(lib.qaff_promote_dtype(_ANY_DTYPES[x.dtype], sb))]
@@ -400,7 +403,8 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
 
     x is float32, bf16 or float16 and the scales and biases bf16, float16 or float32: they promote
     to one type (float32 unless they agree), which is the result's type. A float16 x or scales
-    other than bf16 run on the typed VALU kernel (path 'auto' or 'gemv')."""
+    other than bf16 take the automatic path: the float16 forms of the bf16 kernels where x, scales
+    and biases are all float16, a typed VALU kernel otherwise (path 'auto')."""
     lib = _lib.load()
     _need(packed, "packed", _PACKED_DTYPES)
     dev = packed.device
@@ -424,8 +428,8 @@ def gather_qmm(x, packed, scales, biases, group_size: int, bits: int, lhs_indice
         raise ValueError(f"x has {x.shape[-1]} columns, the weight {k}")
     if path not in ("auto", "gemv", "gemv_mfma", "gemm"):
         raise ValueError("path must be 'auto', 'gemv', 'gemv_mfma' or 'gemm'")
-    if typed and path not in ("auto", "gemv"):
-        raise ValueError("float16 x or non-bf16 scales run on the typed VALU kernel: path 'auto' or 'gemv'")
+    if typed and path != "auto":
+        raise ValueError("float16 x or non-bf16 scales take the automatic path: path 'auto'")
     x_batch = tuple(x.shape[:-2])
     lhs, lhs_shape = _batch_indices(lhs_indices, x_batch, "lhs_indices", dev)
     rhs, rhs_shape = _batch_indices(rhs_indices, w_batch, "rhs_indices", dev)

@@ -20,9 +20,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqaff.so")
 BENCH_LIB = os.path.join(PKG, "libqaff_bench.so")
 
-SOURCES = ["api.cpp", "dequant.hip", "gemv.hip", "gemv_mfma.hip", "gemm.hip", "quantize.hip", "qmm_nt.hip", "typed.hip",
-           "unaligned.hip"]
+# every .hip and .cpp file under csrc/ goes into libqaff.so, except the benchmark's aids
 BENCH_SOURCES = ["bench_aux.hip"]
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")) and f not in BENCH_SOURCES)
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

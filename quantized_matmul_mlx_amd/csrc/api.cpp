@@ -499,12 +499,34 @@ qaff_status qaff_gather_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t x_b
     g.w_stride = (uint64_t)(n * (k / 32) * bits);
     g.sb_stride = (uint64_t)(n * (k / group_size));
     g.y_stride = (uint64_t)(m * n);
+    const bool vec = (!x || aligned(x, 16)) && aligned(y, 16);
+    // float16 x, scales and biases: the matrix-core kernels of qaff_gather_qmm in float16, under
+    // its rules (the grouped GEMM once experts average kGroupedGemmRows rows, the grouped decode
+    // kernel once they average one, the batched one from kGemvMfmaMinM rows)
+    if (x_dtype == QAFF_F16 && sb_dtype == QAFF_F16 && vec) {
+        const uint16_t* s16 = static_cast<const uint16_t*>(scales);
+        const uint16_t* b16 = static_cast<const uint16_t*>(biases);
+        const bool sorted_rows = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices;
+        if (sorted_rows && batch >= kGroupedGemmRows * w_batches && qaff::gemm_grouped_supported(k, s16, b16, g.sb_stride) &&
+            (w_batches + 1) * ((n + 255) / 256) * 3 < (1LL << 31) - 8)
+            return after_launch(op, qaff::launch_gemm_grouped_f16(static_cast<const uint16_t*>(x), packed, s16, b16, n, k,
+                                                                  group_size, bits, static_cast<uint16_t*>(y),
+                                                                  rhs_indices, batch, w_batches, g.w_stride,
+                                                                  g.sb_stride, stream), stream);
+        if (qaff::gemv_mfma_gather_supported(k) && aligned(scales, 4) && aligned(biases, 4)) {
+            g.grouped = sorted_rows && batch >= w_batches;
+            if (g.grouped || m >= kGemvMfmaMinM)
+                return after_launch(op, qaff::launch_gemv_mfma_gather_f16(static_cast<const uint16_t*>(x), m, packed, s16,
+                                                                          b16, n, k, group_size, bits,
+                                                                          static_cast<uint16_t*>(y), g, stream), stream);
+        }
+    }
     // sorted rows, one per output batch, gathered by expert: the grouped walk once experts average
     // 16 rows or more (each expert's weights are then read once; measured with float16 operands on
     // 128 experts of [768, 2048]: 4 rows per expert 279 against 204 us batched, 32 rows 1385
     // against 1506 us, 128 rows 5229 against 5957 us)
     g.grouped = sorted_indices != 0 && m == 1 && !lhs_indices && rhs_indices && batch >= 16 * w_batches;
-    if ((x && !aligned(x, 16)) || !aligned(y, 16)) {  // the typed GEMV reads x in 16-byte loads
+    if (!vec) {  // the typed GEMV reads x in 16-byte loads
         g.grouped = 0;
         qaff::ScalarGemv opt{};
         opt.gather = true;
@@ -569,11 +591,22 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
         return after_launch(op, qaff::launch_gemv_scalar(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
                                                          group_size, bits, y, (int)yt, qaff::ScalarGemv{}, stream),
                             stream);
-    if (x_dtype == QAFF_F16 && sb_dtype == QAFF_F16)
-        return after_launch(op, qaff::launch_gemv_f16(static_cast<const uint16_t*>(x), m, packed,
-                                                      static_cast<const uint16_t*>(scales),
-                                                      static_cast<const uint16_t*>(biases), n, k, group_size, bits,
-                                                      static_cast<uint16_t*>(y), stream), stream);
+    if (x_dtype == QAFF_F16 && sb_dtype == QAFF_F16) {
+        // qaff_qmm's kernels in float16, under its rules: the GEMM past kGemvMaxM rows, the
+        // matrix-core decode kernel from gemv_mfma_min_m(k) rows where it applies, else the GEMV
+        const uint16_t* x16 = static_cast<const uint16_t*>(x);
+        const uint16_t* s16 = static_cast<const uint16_t*>(scales);
+        const uint16_t* b16 = static_cast<const uint16_t*>(biases);
+        uint16_t* y16 = static_cast<uint16_t*>(y);
+        hipError_t e;
+        if (m > kGemvMaxM)
+            e = qaff::launch_gemm_f16(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);
+        else if (m >= gemv_mfma_min_m(k) && qaff::gemv_mfma_supported(m, k) && aligned(scales, 4) && aligned(biases, 4))
+            e = qaff::launch_gemv_mfma_f16(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);
+        else
+            e = qaff::launch_gemv_f16(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);
+        return after_launch(op, e, stream);
+    }
     return after_launch(op, qaff::launch_gemv_typed(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, n, k,
                                                     group_size, bits, y, (int)yt, stream), stream);
 }

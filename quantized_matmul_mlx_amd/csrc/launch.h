@@ -81,6 +81,15 @@ hipError_t launch_gemv_mfma_gather(const uint16_t* x, int64_t m, const uint32_t*
                                    int group_size, int bits, uint16_t* y, const Gather& g,
                                    hipStream_t stream);
 
+// The same two in float16 (x, scales, biases and y float16), for the same shapes.
+hipError_t launch_gemv_mfma_f16(const uint16_t* x, int64_t m, const uint32_t* packed,
+                                const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                int group_size, int bits, uint16_t* y, hipStream_t stream);
+hipError_t launch_gemv_mfma_gather_f16(const uint16_t* x, int64_t m, const uint32_t* packed,
+                                       const uint16_t* scales, const uint16_t* biases, int64_t n, int64_t k,
+                                       int group_size, int bits, uint16_t* y, const Gather& g,
+                                       hipStream_t stream);
+
 // y[m, n] (bf16) = x (bf16) . dequantize(W)^T with W dequantized to bf16 and bf16 MFMA, float32
 // accumulation. With a workspace of at least gemm_workspace_bytes(m, n, k) bytes (16-byte
 // aligned), few tiles split K: float32 partial sums go to the workspace and a second kernel adds
@@ -101,6 +110,16 @@ hipError_t launch_gemm_grouped(const uint16_t* x, const uint32_t* packed, const 
                                const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
                                const uint32_t* rhs, int64_t batch, int64_t w_count, uint64_t w_stride,
                                uint64_t sb_stride, hipStream_t stream);
+
+// The same two in float16 (x, scales, biases and y float16, W rounded to float16), without the
+// K split, for the same shapes.
+hipError_t launch_gemm_f16(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                           const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits, uint16_t* y,
+                           hipStream_t stream);
+hipError_t launch_gemm_grouped_f16(const uint16_t* x, const uint32_t* packed, const uint16_t* scales,
+                                   const uint16_t* biases, int64_t n, int64_t k, int group_size, int bits,
+                                   uint16_t* y, const uint32_t* rhs, int64_t batch, int64_t w_count,
+                                   uint64_t w_stride, uint64_t sb_stride, hipStream_t stream);
 
 // packed/scales/biases of a dense [rows, cols] weight of dtype code w_dtype (0 float32, 1 bf16,
 // 2 float16): bias = group min, scale = (max - min) / (2^bits - 1), both stored as sb_dtype; code =

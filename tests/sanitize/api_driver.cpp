@@ -51,6 +51,17 @@ bool gemv_mfma_supported(int64_t m, int64_t k) { return m >= 1 && m <= 16 && k %
 bool gemv_mfma_gather_supported(int64_t k) { return k % 512 == 0 && k > 0 && k <= 4096; }
 hipError_t launch_gemv_mfma(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
                             int64_t, int, int, uint16_t*, hipStream_t) { return rec("gemv_mfma"); }
+hipError_t launch_gemv_mfma_f16(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
+                                int64_t, int, int, uint16_t*, hipStream_t) { return rec("gemv_mfma_f16"); }
+hipError_t launch_gemv_mfma_gather_f16(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*,
+                                       int64_t, int64_t, int, int, uint16_t*, const Gather& g, hipStream_t) {
+    return rec(g.grouped ? "gemv_mfma_gather_f16_grouped" : "gemv_mfma_gather_f16");
+}
+hipError_t launch_gemm_f16(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
+                           int, int, uint16_t*, hipStream_t) { return rec("gemm_f16"); }
+hipError_t launch_gemm_grouped_f16(const uint16_t*, const uint32_t*, const uint16_t*, const uint16_t*, int64_t, int64_t,
+                                   int, int, uint16_t*, const uint32_t*, int64_t, int64_t, uint64_t, uint64_t,
+                                   hipStream_t) { return rec("gemm_grouped_f16"); }
 hipError_t launch_gemv_mfma_gather(const uint16_t*, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
                                    int64_t, int, int, uint16_t*, const Gather& g, hipStream_t) {
     return rec(g.grouped ? "gemv_mfma_gather_grouped" : "gemv_mfma_gather");
@@ -90,6 +101,7 @@ static void* const A1 = reinterpret_cast<void*>(0x10001);
 static const uint32_t* const P16 = reinterpret_cast<const uint32_t*>(0x20000);
 static const uint16_t* const S16 = reinterpret_cast<const uint16_t*>(0x30000);
 static const uint16_t* const B16 = reinterpret_cast<const uint16_t*>(0x40000);
+static const uint16_t* const B2 = reinterpret_cast<const uint16_t*>(0x40002);  // 2-byte aligned biases
 static const uint32_t* const I16 = reinterpret_cast<const uint32_t*>(0x50000);
 
 // Runs a call and checks its status and what it launched ("" = nothing).
@@ -148,6 +160,22 @@ int main() {
     EXPECT(OK, "gemv_scalar", qaff_gather_qmm(A2, QAFF_BF16, 2, 1, P16, S16, B16, 4, 64, 4096, 64, 4, I16, I16, 3, 0,
                                               A16, nullptr));
     EXPECT(OK, "gemv_scalar", qaff_qmm_typed(A2, QAFF_F16, 1, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    // float16 x, scales and biases: qaff_qmm's kernels in float16
+    EXPECT(OK, "gemv_f16", qaff_qmm_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_mfma_f16", qaff_qmm_typed(A16, QAFF_F16, 3, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_mfma_f16", qaff_qmm_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_F16, 64, 5120, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_f16", qaff_qmm_typed(A16, QAFF_F16, 3, P16, S16, B2, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemm_f16", qaff_qmm_typed(A16, QAFF_F16, 17, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_typed", qaff_qmm_typed(A16, QAFF_F16, 17, P16, S16, B16, QAFF_F32, 64, 4096, 64, 4, A16, nullptr));
+    // ... and qaff_gather_qmm's: grouped GEMM, grouped and batched decode kernels, else the typed GEMV
+    EXPECT(OK, "gemm_grouped_f16", qaff_gather_qmm_typed(A16, QAFF_F16, 256, 1, P16, S16, B16, QAFF_F16, 4, 64, 4096, 64,
+                                                         4, nullptr, I16, 256, 1, A16, nullptr));
+    EXPECT(OK, "gemv_mfma_gather_f16_grouped", qaff_gather_qmm_typed(A16, QAFF_F16, 8, 1, P16, S16, B16, QAFF_F16, 4, 64,
+                                                                     4096, 64, 4, nullptr, I16, 8, 1, A16, nullptr));
+    EXPECT(OK, "gemv_mfma_gather_f16", qaff_gather_qmm_typed(A16, QAFF_F16, 2, 3, P16, S16, B16, QAFF_F16, 4, 64, 4096,
+                                                             64, 4, I16, I16, 3, 0, A16, nullptr));
+    EXPECT(OK, "gemv_typed", qaff_gather_qmm_typed(A16, QAFF_F16, 2, 1, P16, S16, B16, QAFF_F16, 4, 64, 4096, 64, 4,
+                                                   I16, I16, 3, 0, A16, nullptr));
     EXPECT(OK, "qmm_nt", qaff_qmm_nt(A2, QAFF_BF16, 2, P16, S16, B16, 4096, 4096, 64, 4, A16, 1 << 20, A2, nullptr));
     // qmm with a workspace: the split GEMM where the size calls for one, a short workspace refused
     const size_t need = qaff_qmm_workspace_size(128, 64, 4096, 64, 4);

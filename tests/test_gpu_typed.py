@@ -211,7 +211,7 @@ def test_gather_qmm_typed_unaligned_x_and_sorted_rows(orc):
                            sorted_indices=True)
     torch.cuda.synchronize()
     check_gather(orc, y2, hx, "f16", packed, hs, hb, "f16", G, bits, np.arange(rhs.size, dtype=np.uint32), rhs)
-    with pytest.raises(ValueError, match="typed VALU kernel"):
+    with pytest.raises(ValueError, match="automatic path"):
         qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
                           path="gemv_mfma")
 
@@ -255,3 +255,85 @@ def test_gather_qmm_typed_moe_workload(orc):
     torch.cuda.synchronize()
     check_gather(orc, y, hx, "f16", mi.packed, hs, hb, "f16", wl.group_size, wl.bits,
                  np.arange(mi.expert.size, dtype=np.uint32), mi.expert)
+
+
+# ---- float16 on the matrix cores ------------------------------------------------------------------
+#
+# A float16 x with float16 scales and biases takes the float16 forms of qaff_qmm's kernels under its
+# rules: the matrix-core decode kernel from 3 rows (2 past 4096 codes), with exact 4-bit codes
+# 1024 + c in bands of the operand rows where they apply and otherwise the weights rounded to
+# float16; the GEMM past 16 rows, W rounded to float16. Against the float64 oracle at the float16
+# bound above.
+
+def f16_case(bits, G, n, k, m, seed):
+    inp = W.random_inputs(bits, G, n, k, 0, seed=seed)
+    hs, hb, ds, db = scales_of(inp, "f16", seed=seed + 1)
+    x = np.random.default_rng(seed + 2).standard_normal((m, k)).astype(np.float16)
+    return inp, hs, hb, ds, db, x
+
+
+def check_f16_qmm(orc, y, x, inp, hs, hb, G, bits):
+    assert y.dtype == torch.float16 and tuple(y.shape) == (x.shape[0], inp.wl.n)
+    ref = orc.qmm_typed(x.view(np.uint16), "f16", inp.packed, hs, hb, "f16", G, bits)
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = orc.max_row_rel_err(got, ref)
+    assert err <= TIGHT[torch.float16], f"max row rel err {err:.3e} > {TIGHT[torch.float16]}"
+
+
+# The decode kernel: K of one slice (512), several (1536, 2048, 4096), past 4096 (5120: 2 rows;
+# 14336: several slices per wave); x rows rounded to 4, 8 and 16; ragged n.
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("m,n,k", [(3, 150, 512), (4, 77, 4096), (8, 150, 2048), (16, 40, 1536), (2, 40, 5120),
+                                   (12, 33, 14336)])
+def test_qmm_f16_matrix_core_decode(orc, bits, G, m, n, k):
+    inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 5 + G + m + n + k)
+    banner(f"qmm float16 matrix-core decode bits={bits} G={G} m={m} n={n} k={k}")
+    y = qaff().qmm(to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed), ds, db, G, bits)
+    torch.cuda.synchronize()
+    check_f16_qmm(orc, y, x, inp, hs, hb, G, bits)
+
+
+# The GEMM: ragged tiles in m and n, K of whole 1024-code chunks and K with a tail (1056 codes: the
+# general variant).
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("G,m,n,k", [(64, 17, 300, 1024), (128, 300, 520, 2048), (32, 130, 260, 1056)])
+def test_qmm_f16_gemm(orc, bits, G, m, n, k):
+    inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 3 + G + m + k)
+    banner(f"qmm float16 gemm bits={bits} G={G} m={m} n={n} k={k}")
+    y = qaff().qmm(to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed), ds, db, G, bits)
+    torch.cuda.synchronize()
+    check_f16_qmm(orc, y, x, inp, hs, hb, G, bits)
+
+
+# Gathered float16 products on the matrix cores: batched (x rows of 4 per batch; batches past x
+# and past the experts are NaN), grouped by expert (sorted rows, one per batch, at least one per
+# expert on average), and the grouped GEMM (32 or more per expert), with rows past every expert.
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (4, 128)])
+def test_gather_qmm_f16_batched_matrix_cores(orc, bits, G):
+    E, n, k, m = 5, 150, 1024, 4
+    packed, hs, hb, ds, db = typed_experts(bits, G, E, n, k, "f16", seed=90 + bits + G)
+    hx = np.random.default_rng(bits + G).standard_normal((4, m, k)).astype(np.float16).view(np.uint16)
+    lhs = np.array([3, 0, 0, 2, 1, 7, 3], np.uint32)
+    rhs = np.array([4, 4, 1, 0, 9, 2, 3], np.uint32)
+    banner(f"gather_qmm float16 batched matrix cores bits={bits} G={G}")
+    y = qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, lhs_indices=dev_u32(lhs),
+                          rhs_indices=dev_u32(rhs))
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, "f16", packed, hs, hb, "f16", G, bits, lhs, rhs)
+
+
+@pytest.mark.parametrize("bits,G,counts,past", [(4, 64, [3, 0, 1, 7, 5], 2), (3, 32, [2, 9, 0, 4], 0),
+                                                (4, 64, [40, 40, 40, 0, 90], 3), (8, 128, [70, 0, 33, 61], 1)])
+def test_gather_qmm_f16_grouped_matrix_cores(orc, bits, G, counts, past):
+    E, n, k = len(counts), 70, 1024
+    packed, hs, hb, ds, db = typed_experts(bits, G, E, n, k, "f16", seed=95 + E + bits)
+    rhs = np.concatenate([np.repeat(np.arange(E, dtype=np.uint32), counts),
+                          np.full(past, E + 2, np.uint32)]).astype(np.uint32)
+    hx = np.random.default_rng(96 + bits).standard_normal((rhs.size, 1, k)).astype(np.float16).view(np.uint16)
+    banner(f"gather_qmm float16 grouped matrix cores bits={bits} G={G} rows={rhs.size} past={past}")
+    y = qaff().gather_qmm(to_dev(hx, "f16"), dev_u32(packed), ds, db, G, bits, rhs_indices=dev_u32(rhs),
+                          sorted_indices=True)
+    torch.cuda.synchronize()
+    check_gather(orc, y, hx, "f16", packed, hs, hb, "f16", G, bits, np.arange(rhs.size, dtype=np.uint32), rhs)
