@@ -697,7 +697,7 @@ def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
                    if held is not None else f"one HIP graph of {steps} launches, events on the launch stream"),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm.hip", "qaff_device.h", "../build.py"])},
+                     "traffic": read_traffic("gemm_4bit_g128_prefill", ["gemm_impl.h", "mfma16.h", "qaff_device.h", "../build.py"])},
     }
     if held is not None:
         res["sustained"] = held
