@@ -227,3 +227,36 @@ def test_typed(lib):
     assert orc_mod.max_row_rel_err(y.float().cpu().numpy().astype(np.float64), ref) <= 1e-3
     dref = orc_mod.dequantize_typed(inp.packed, s16, b16, "f16", 64, 4, out="f16")
     np.testing.assert_array_equal(o.cpu().view(torch.int16).numpy().view(np.uint16), dref)
+
+
+# Scales and biases at a 2-byte offset (their element size of alignment) on every decode and GEMM
+# route: the long-row VALU GEMV (its staged scale windows need 4-byte words, so it takes the
+# per-block loads), the matrix-core decode kernels (4-byte words: the VALU GEMV instead), and the
+# GEMM (its general variant's element loads); bf16 through qaff_qmm and float16 through
+# qaff_qmm_typed.
+@pytest.mark.parametrize("m,k", [(1, 14336), (4, 4096), (4, 14336), (40, 2048)])
+def test_scales_at_two_byte_offset(lib, m, k):
+    G, bits, n = 64, 4, 96
+    inp = W.random_inputs(bits, G, n, k, m, seed=m + k)
+    p, s, b = dev_weights(inp)
+    so, bo = off(s), off(b)
+    banner(f"scales at a 2-byte offset m={m} k={k}")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    xb = dev_x(inp.x, "bf16")
+    _lib.check(lib.qaff_qmm(P(xb), BF16, m, P(p), P(so), P(bo), n, k, G, bits, P(y), S()))
+    torch.cuda.synchronize()
+    ref = orc_mod.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases, G, bits)
+    # the GEMM multiplies bf16-rounded weights: the parity bound against the float32 weights
+    assert orc_mod.max_row_rel_err(host_f64(y), ref) <= (1.6e-2 if m > 16 else TIGHT["bf16"])
+    # float16 x, scales and biases
+    to16 = lambda a: W.f32_from_bf16_bits(a).astype(np.float16).view(np.uint16)
+    s16, b16, x16 = to16(inp.scales), to16(inp.biases), to16(inp.x)
+    h = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.float16)
+    y16 = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    # every operand held in a variable for the call (a temporary's memory would go back to the
+    # allocator as soon as its address is taken, and the next one could reuse it)
+    xd, sd, bd = h(x16), off(h(s16)), off(h(b16))
+    _lib.check(lib.qaff_qmm_typed(P(xd), F16, m, P(p), P(sd), P(bd), F16, n, k, G, bits, P(y16), S()))
+    torch.cuda.synchronize()
+    ref16 = orc_mod.qmm_typed(x16, "f16", inp.packed, s16, b16, "f16", G, bits)
+    assert orc_mod.max_row_rel_err(y16.float().cpu().numpy().astype(np.float64), ref16) <= 1e-3
