@@ -218,7 +218,7 @@ constexpr size_t kZeroBytes = kExactCodes<BITS, GSHIFT, MB> ? 1024 : 0;
 template <int BITS, int NT, int GSHIFT, int MB, bool F16>
 __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
-    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y) {
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t red_off) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -300,10 +300,12 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     }
 
     // 4. Sum the slices' partial tiles (and the bands of exact codes) through LDS:
-    //    [wave][tile][v][lane] float32.
+    //    [wave][tile][v][lane] float32, at byte red_off: past the x regions where the launcher gave
+    //    the block that much LDS (no wave then waits for the others to finish with x before writing
+    //    its tile), else over them (red_off = 0).
     constexpr int kBands = kExact ? (4 >> GSHIFT) : 1;
-    __syncthreads();  // every wave is done with its x rows
-    float* red = reinterpret_cast<float*>(smem);
+    if (red_off == 0) __syncthreads();  // every wave is done with its x rows
+    float* red = reinterpret_cast<float*>(smem + red_off);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -324,16 +326,34 @@ __global__ __launch_bounds__(512) void gemv_mfma_kernel(
     }
 }
 
+// Blocks of `bytes` of LDS that fit on a compute unit (at most 4: the kernels' launches assume no
+// more).
+inline int64_t blocks_per_cu(size_t bytes) {
+    const int64_t b = (int64_t)(160 * 1024) / (int64_t)bytes;
+    return b < 1 ? 1 : (b > 4 ? 4 : b);
+}
+
+// LDS of a block and the offset of its reduction area: past the x regions when the sum fits a
+// block's LDS and keeps as many blocks on a compute unit, else over them (offset 0).
+inline size_t reduction_layout(size_t regions, size_t red, uint32_t* red_off) {
+    if (regions + red <= (size_t)(160 * 1024) && blocks_per_cu(regions + red) >= blocks_per_cu(regions)) {
+        *red_off = (uint32_t)regions;
+        return regions + red;
+    }
+    *red_off = 0;
+    return regions > red ? regions : red;
+}
+
 template <int BITS, int NT, int GSHIFT, int MB, bool F16>
 hipError_t launch_nt(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                      const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
     const int waves = (int)(kb / 16);
-    size_t lds = (size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>;
-    const size_t red = (size_t)waves * NT * 4 * 64 * sizeof(float);
-    if (red > lds) lds = red;
+    uint32_t red_off;
+    const size_t lds = reduction_layout((size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>,
+                                        (size_t)waves * NT * 4 * 64 * sizeof(float), &red_off);
     const unsigned blocks = (unsigned)((n + 16 * NT - 1) / (16 * NT));
     gemv_mfma_kernel<BITS, NT, GSHIFT, MB, F16><<<dim3(blocks), dim3(waves * 64), lds, stream>>>(
-        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y);
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, red_off);
     return hipGetLastError();
 }
 
@@ -428,7 +448,7 @@ constexpr bool kWideBlock = MB == 4   ? !(BITS == 8 && GSHIFT == 0)
 template <int BITS, int NT, int GSHIFT, int MB, int S, bool F16>
 __global__ __launch_bounds__((kWideBlock<BITS, GSHIFT, MB> ? 1024 : 512)) void gemv_mfma_long_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
-    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y) {
+    const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t red_off) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -472,8 +492,8 @@ __global__ __launch_bounds__((kWideBlock<BITS, GSHIFT, MB> ? 1024 : 512)) void g
 
     // the waves' partial tiles (and the bands of exact codes) summed through LDS, as above
     constexpr int kBands = kExact ? (4 >> GSHIFT) : 1;
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(smem);
+    if (red_off == 0) __syncthreads();  // every wave is done with its x rows
+    float* red = reinterpret_cast<float*>(smem + red_off);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -498,12 +518,12 @@ template <int BITS, int GSHIFT, int MB, int S, bool F16>
 hipError_t launch_long_s(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                          const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, hipStream_t stream) {
     const int64_t waves = (kb / 16 + S - 1) / S;
-    size_t lds = (size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>;
-    const size_t red = (size_t)waves * 4 * 64 * sizeof(float);
-    if (red > lds) lds = red;
+    uint32_t red_off;
+    const size_t lds = reduction_layout((size_t)waves * MB * kXPitch + kZeroBytes<BITS, GSHIFT, MB>,
+                                        (size_t)waves * 4 * 64 * sizeof(float), &red_off);
     gemv_mfma_long_kernel<BITS, 1, GSHIFT, MB, S, F16><<<dim3((unsigned)((n + 15) / 16)), dim3((unsigned)waves * 64), lds,
                                                     stream>>>(x, (uint32_t)m, packed, scales, biases, (uint32_t)n,
-                                                              (uint32_t)kb, y);
+                                                              (uint32_t)kb, y, red_off);
     return hipGetLastError();
 }
 
