@@ -93,6 +93,8 @@ def _load():
     lib.orc_qmm_typed.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, ctypes.c_void_p, ctypes.c_void_p, _int, _i64, _i64,
                                   _i64, _int, _f64p]
     lib.orc_qmm_nt.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, _u16p, _u16p, _i64, _i64, _i64, _int, _f64p]
+    lib.orc_qmm_nt_typed.argtypes = [ctypes.c_void_p, _int, _i64, _u32p, ctypes.c_void_p, ctypes.c_void_p, _int, _i64,
+                                     _i64, _i64, _int, _f64p]
     lib.orc_quantize.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, _u16p, _u16p]
     lib.orc_quantize_typed.argtypes = [ctypes.c_void_p, _int, _i64, _i64, _i64, _int, _u32p, ctypes.c_void_p,
                                        ctypes.c_void_p, _int]
@@ -104,7 +106,8 @@ def _load():
                                       _i64, _i64, _int, _f64p, _int]
     for name in ("orc_unpack_codes", "orc_pack_codes", "orc_dequantize", "orc_dequant_rows",
                  "orc_qmm", "orc_silu_gate_qmm", "orc_gather_qmm", "orc_quantize", "orc_qmm_nt",
-                 "orc_dequantize_typed", "orc_qmm_typed", "orc_quantize_typed", "orc_gather_qmm_typed"):
+                 "orc_dequantize_typed", "orc_qmm_typed", "orc_quantize_typed", "orc_gather_qmm_typed",
+                 "orc_qmm_nt_typed"):
         getattr(lib, name).restype = _int
     for name in ("orc_bf16_to_f32", "orc_f32_to_bf16", "orc_silu_gate", "orc_f16_to_f32", "orc_f32_to_f16"):
         getattr(lib, name).restype = None
@@ -401,6 +404,22 @@ def qmm_typed(x, x_dtype: str, packed, scales, biases, sb_dtype: str, group_size
     out = np.empty((m, n), np.float64)
     _check(_load().orc_qmm_typed(xa.ctypes.data, DTYPES[x_dtype], m, packed, sc.ctypes.data, bi.ctypes.data,
                                  DTYPES[sb_dtype], n, k, group_size, bits, out), "qmm_typed")
+    return out
+
+
+def qmm_nt_typed(x, x_dtype: str, packed, scales, biases, sb_dtype: str, group_size: int, bits: int) -> np.ndarray:
+    """y = x . dequantize(W) in float64 for W stored [k, n] (packed [k, n*bits/32], scales and biases
+    [k, n/G]), with x and the scales/biases of any of the three types."""
+    xa = _typed(np.atleast_2d(x), x_dtype)
+    packed = _c(np.atleast_2d(packed), np.uint32)
+    sc, bi = _typed(np.atleast_2d(scales), sb_dtype), _typed(np.atleast_2d(biases), sb_dtype)
+    m, k = xa.shape
+    if packed.shape[0] != k:
+        raise ValueError("x columns do not match the weight's rows")
+    n = packed.shape[1] * 32 // bits
+    out = np.empty((m, n), np.float64)
+    _check(_load().orc_qmm_nt_typed(xa.ctypes.data, DTYPES[x_dtype], m, packed, sc.ctypes.data, bi.ctypes.data,
+                                    DTYPES[sb_dtype], k, n, group_size, bits, out), "qmm_nt_typed")
     return out
 
 

@@ -500,6 +500,26 @@ int orc_qmm_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed,
     return 0;
 }
 
+/* [nuvec] quantized_matmul without the transpose, x and the scales and biases of any of the three
+ * types: y[m, n] = sum over k of x[m, k] * w[k, n] in double, sequentially in k, for a weight stored
+ * [k, n] whose rows orc_dequantize_typed forms (k rows of n values). */
+int orc_qmm_nt_typed(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                     const void* biases, int sb_dtype, int64_t k, int64_t n, int64_t group, int bits, double* out) {
+    if (m < 0 || k < 0 || x_dtype < 0 || x_dtype > 2) return -1;
+    float* w = (float*)malloc(sizeof(float) * (size_t)(k * n > 0 ? k * n : 1));
+    if (!w) return -2;
+    const int rc = orc_dequantize_typed(packed, scales, biases, sb_dtype, k, n, group, bits, w);
+    if (rc != 0) { free(w); return rc; }
+    for (int64_t mm = 0; mm < m; ++mm)
+        for (int64_t nn = 0; nn < n; ++nn) {
+            double acc = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk) acc += (double)widen(x, mm * k + kk, x_dtype) * (double)w[kk * n + nn];
+            out[mm * n + nn] = acc;
+        }
+    free(w);
+    return 0;
+}
+
 /* [nuvec] quantize (module documentation and `quantize`: float16, bfloat16 or float32 w; scales and
  * biases in w's dtype) with [moshi]'s bias: each group of G values of a row, in the pages' order:
  *   bias  = the group minimum; scale = (max - min) / (2^bits - 1): the statistics in float32 (w

@@ -793,6 +793,52 @@ def test_qmm_typed_reduces_to_qmm(oracle_lib):
     np.testing.assert_allclose(y, xf.astype(np.float64) @ w.T, rtol=1e-12, atol=1e-12)
 
 
+def test_qmm_nt_typed_reduces_to_qmm_nt(oracle_lib):
+    # bf16 scales: the typed form is the plain product without the transpose, for bf16 and f32 x
+    inp = W.random_inputs(4, 64, 24, 128, 0, seed=34)         # W [k=24, n=128]
+    xb = W.random_inputs(4, 64, 8, 64, 3, seed=35).x[:, :24].copy()
+    for x, dt in ((xb, "bf16"), (W.f32_from_bf16_bits(xb), "f32")):
+        np.testing.assert_array_equal(
+            oracle_lib.qmm_nt_typed(x, dt, inp.packed, inp.scales, inp.biases, "bf16", 64, 4),
+            oracle_lib.qmm_nt(x, dt, inp.packed, inp.scales, inp.biases, 64, 4))
+
+
+@pytest.mark.parametrize("x_dt,sb_dt", [("f16", "f16"), ("f32", "f16"), ("bf16", "f32"), ("f16", "bf16")])
+def test_qmm_nt_typed_against_numpy(oracle_lib, x_dt, sb_dt):
+    # numpy's float64 product of the pinned typed dequantization, x [3, k] . W [k, n]; x holds
+    # multiples of 1/64 below 4 in magnitude, which all three types represent exactly
+    bits, G = 5, 32
+    inp = W.random_inputs(bits, G, 40, 96, 0, seed=36)
+    conv = {"f16": lambda a: a.astype(np.float16).view(np.uint16), "f32": lambda a: a.astype(np.float32),
+            "bf16": lambda a: W.bf16_bits_from_f32(a.astype(np.float32))}
+    sf = W.f32_from_bf16_bits(inp.scales)
+    bf = W.f32_from_bf16_bits(inp.biases)
+    sc, bi = conv[sb_dt](sf), conv[sb_dt](bf)
+    w = oracle_lib.dequantize_typed(inp.packed, sc, bi, sb_dt, G, bits).astype(np.float64)
+    xf = (np.random.default_rng(6).integers(-255, 256, size=(3, 40)) / 64).astype(np.float32)
+    x = conv[x_dt](xf)
+    y = oracle_lib.qmm_nt_typed(x, x_dt, inp.packed, sc, bi, sb_dt, G, bits)
+    assert y.shape == (3, 96)
+    np.testing.assert_allclose(y, xf.astype(np.float64) @ w, rtol=1e-12, atol=1e-12)
+    # x = e_k picks row k of the typed dequantization, exactly
+    e = conv[x_dt](np.eye(40, dtype=np.float32)[[0, 13, 39]])
+    np.testing.assert_array_equal(oracle_lib.qmm_nt_typed(e, x_dt, inp.packed, sc, bi, sb_dt, G, bits),
+                                  w[[0, 13, 39]])
+
+
+def test_qmm_nt_typed_and_qmm_typed_agree_on_a_symmetric_weight(oracle_lib):
+    # float16 scales on a symmetric weight: the product with and without the transpose agree to the bit
+    n = 64
+    codes = np.random.default_rng(18).integers(0, 16, size=(n, n)).astype(np.uint8)
+    codes = np.triu(codes) + np.triu(codes, 1).T
+    packed = oracle_lib.pack_codes(codes, 4)
+    sc = np.full((n, 1), np.float16(0.3).view(np.uint16), np.uint16)
+    bi = np.full((n, 1), np.float16(-1.1).view(np.uint16), np.uint16)
+    x = np.random.default_rng(19).standard_normal((2, n)).astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(oracle_lib.qmm_nt_typed(x, "f16", packed, sc, bi, "f16", 64, 4),
+                                  oracle_lib.qmm_typed(x, "f16", packed, sc, bi, "f16", 64, 4))
+
+
 # ---- quantize with float16 / float32 weights, scales and biases ----------------------------------
 
 _TYPE = {"f32": np.float32, "bf16": None, "f16": np.float16}
