@@ -437,17 +437,27 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     return row
 
 
-def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
+def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget, f16=False):
     """The product without the transpose at the decode shape: x bf16 [1, 4096] . dequantize(W) for
-    W stored [4096 (k), 4096 (n)], 4-bit g64 (groups along n). Algorithmic bytes as for qmm."""
+    W stored [4096 (k), 4096 (n)], 4-bit g64 (groups along n). Algorithmic bytes as for qmm. With
+    f16, x, scales and biases are float16 (the same draws converted) and so is y."""
     import numpy as np
     import oracle
     wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
     inp = W.make_inputs(wl, m=1)          # the same draws, read as a [k, n] weight
     b = qmm_bytes(1, wl.n, wl.k, wl.bits, wl.group_size)
     copies = copies_for(b)
-    sets = replicate(torch, to_device(torch, inp), copies)
-    ys = [torch.empty((1, wl.n), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    if f16:
+        s16 = W.f32_from_bf16_bits(inp.scales).astype(np.float16).view(np.uint16)
+        b16 = W.f32_from_bf16_bits(inp.biases).astype(np.float16).view(np.uint16)
+        x16 = W.f32_from_bf16_bits(inp.x).astype(np.float16).view(np.uint16)
+        h = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.float16)
+        sets = [{"packed": torch.from_numpy(inp.packed.view(np.int32)).cuda(), "scales": h(s16), "biases": h(b16),
+                 "x": h(x16)} for _ in range(copies)]
+    else:
+        sets = replicate(torch, to_device(torch, inp), copies)
+    ydt = torch.float16 if f16 else torch.bfloat16
+    ys = [torch.empty((1, wl.n), dtype=ydt, device="cuda") for _ in range(copies)]
 
     def launch(i):
         s = sets[i % copies]
@@ -457,12 +467,16 @@ def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget):
     del sets, ys
     torch.cuda.empty_cache()
     gbs = b / (ms * 1e-3) / 1e9
-    row = {"workload": "qmm without the transpose, W [4096 (k), 4096 (n)] 4-bit g64, x bf16 [1, 4096]",
-           "kernel": "qmm_nt_partial_kernel + qmm_nt_reduce_kernel", "bytes_per_step": b,
-           "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
+    what = "x, scales and biases float16" if f16 else "x bf16"
+    row = {"workload": f"qmm without the transpose, W [4096 (k), 4096 (n)] 4-bit g64, {what} [1, 4096]",
+           "kernel": "qmm_nt_partial_kernel + qmm_nt_reduce_kernel" + (", typed form" if f16 else ""),
+           "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
-        runs, el = cpu_time(lambda: oracle.qmm_nt(inp.x, "bf16", inp.packed, inp.scales, inp.biases,
-                                                  wl.group_size, wl.bits), cpu_budget, 100000)
+        if f16:
+            fn = lambda: oracle.qmm_nt_typed(x16, "f16", inp.packed, s16, b16, "f16", wl.group_size, wl.bits)
+        else:
+            fn = lambda: oracle.qmm_nt(inp.x, "bf16", inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits)
+        runs, el = cpu_time(fn, cpu_budget, 100000)
         row["cpu_baseline"] = {"value": round(b * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
     return row
@@ -1016,6 +1030,7 @@ def main():
         for kind in ("gate_up", "silu_gate"):
             add(bench_fused(torch, q, W, timer, kind, rs, rw, cpu, 2.0))
         add(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0))
+        add(bench_qmm_nt(torch, q, W, timer, rs, rw, cpu, 2.0, f16=True))
         add(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0))
         add(bench_typed(torch, q, W, timer, rs, rw, cpu, 2.0, m=4))
         add(bench_prefill_small(torch, q, W, timer, 2048, max(20, rs // 10), 5, cpu, 2.0, f16=True))

@@ -216,8 +216,23 @@ qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint
                         int32_t group_size, int32_t bits, void* workspace, size_t workspace_bytes,
                         void* y, hipStream_t stream);
 
-/* Bytes of workspace qaff_qmm_nt needs for these sizes and bit width (0 when there is nothing to
- * compute). */
+/*
+ * qaff_qmm_nt with x of x_dtype and scales and biases of sb_dtype (each float32, bf16 or float16;
+ * nuvec_core quantized.rs: quantized_matmul promotes x, scales and biases to one float type):
+ * y [m, n] of qaff_promote_dtype(x_dtype, sb_dtype), float32 sums, the same kernels and K split
+ * (every operand widened to float32 exactly as it is loaded; y rounded to nearest even). The
+ * workspace is qaff_qmm_nt's: qaff_qmm_nt_workspace_size(m, k, n, bits) bytes.
+ * bf16 scales with a float32 or bf16 x give qaff_qmm_nt's results, bit for bit.
+ * Errors: as qaff_qmm_nt, plus INVALID_ARGUMENT for an unknown dtype, float32 scales and biases not
+ * 4-byte aligned, or x or y not aligned to their element size.
+ */
+qaff_status qaff_qmm_nt_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
+                              const void* scales, const void* biases, qaff_dtype sb_dtype, int64_t k,
+                              int64_t n, int32_t group_size, int32_t bits, void* workspace,
+                              size_t workspace_bytes, void* y, hipStream_t stream);
+
+/* Bytes of workspace qaff_qmm_nt and qaff_qmm_nt_typed need for these sizes and bit width (0 when
+ * there is nothing to compute). */
 size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits);
 
 /*

@@ -62,8 +62,9 @@ def _need(t, name, dtypes, device=None):
 
 
 def _weights(packed, scales, biases, group_size, bits, typed=False):
-    """Checks a weight; returns (device, rows, cols). Only ``typed`` callers (qmm, gather_qmm,
-    dequantize) take float16 or float32 scales and biases; the other operations read bf16 ones."""
+    """Checks a weight; returns (device, rows, cols). Only ``typed`` callers (qmm, qmm_nt,
+    gather_qmm, dequantize) take float16 or float32 scales and biases; the other operations read
+    bf16 ones."""
     _need(packed, "packed", _PACKED_DTYPES)
     dev = packed.device
     _need(scales, "scales", _SCALE_DTYPES, dev)
@@ -72,7 +73,7 @@ def _weights(packed, scales, biases, group_size, bits, typed=False):
         raise TypeError(f"scales ({scales.dtype}) and biases ({biases.dtype}) differ in type")
     if not typed and _sb_code(scales) != _lib.QAFF_BF16:
         raise TypeError(f"this operation reads bf16 scales and biases, got {scales.dtype} "
-                        "(float16 and float32 scales are taken by qmm and dequantize)")
+                        "(float16 and float32 scales are taken by qmm, qmm_nt, gather_qmm and dequantize)")
     if packed.dim() != 2 or scales.dim() != 2 or biases.dim() != 2:
         raise ValueError("packed, scales and biases must be 2-D")
     rows, words = packed.shape
@@ -159,24 +160,32 @@ def quantize(w, group_size: int, bits: int, scales_dtype=None):
 def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None, static_scratch: bool = False):
     """``x . dequantize(W)`` for a weight stored ``[k, n]`` (nuvec_core ``quantized_matmul`` with
     ``transpose=False``): packed ``[k, n*bits/32]``, scales and biases ``[k, n/group_size]``;
-    x float32 or bf16 ``[..., k]`` (1-D: one row); the result has x's dtype and shape ``[..., n]``.
+    x ``[..., k]`` (1-D: one row); the result has shape ``[..., n]``.
+    x float32 or bf16 with bf16 scales: the result has x's dtype. x may also be float16 and the
+    scales and biases float16 or float32 (``qaff_qmm_nt_typed``): x, scales and biases then promote
+    to one type (float32 unless they agree), which is the result's type.
     The call's float32 K-chunk partial sums go to a workspace tensor allocated here, or with
-    ``static_scratch`` (and ``out`` given) to the library's per-device scratch array
-    (``qaff_qmm_nt_static``): the call then allocates nothing."""
+    ``static_scratch`` (and ``out`` given; float32 or bf16 x, bf16 scales) to the library's
+    per-device scratch array (``qaff_qmm_nt_static``): the call then allocates nothing."""
     lib = _lib.load()
-    dev, k, n = _weights(packed, scales, biases, group_size, bits)
-    _need(x, "x", tuple(_OUT_DTYPES), dev)
+    dev, k, n = _weights(packed, scales, biases, group_size, bits, typed=True)
+    _need(x, "x", tuple(_ANY_DTYPES), dev)
     if x.shape[-1] != k:
         raise ValueError(f"x has {x.shape[-1]} columns, the weight {k} rows")
+    sb = _sb_code(scales)
+    typed = sb != _lib.QAFF_BF16 or x.dtype == torch.float16
+    yt = _FROM_CODE[int(lib.qaff_promote_dtype(_ANY_DTYPES[x.dtype], sb))]
     lead = tuple(x.shape[:-1])
     m = math.prod(lead)
     if out is None:
-        out = torch.empty(lead + (n,), dtype=x.dtype, device=dev)
+        out = torch.empty(lead + (n,), dtype=yt, device=dev)
     else:
-        _need(out, "out", (x.dtype,), dev)
+        _need(out, "out", (yt,), dev)
         if tuple(out.shape) != lead + (n,):
             raise ValueError(f"out must be {list(lead + (n,))}")
     if static_scratch:
+        if typed:
+            raise TypeError("the static scratch takes float32 or bf16 x with bf16 scales and biases")
         with torch.cuda.device(dev):
             _lib.check(lib.qaff_qmm_nt_static(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k,
                                               n, group_size, bits, _p(out), _stream(dev)))
@@ -184,8 +193,12 @@ def qmm_nt(x, packed, scales, biases, group_size: int, bits: int, out=None, stat
     nbytes = int(lib.qaff_qmm_nt_workspace_size(m, k, n, bits))
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
     with torch.cuda.device(dev):
-        _lib.check(lib.qaff_qmm_nt(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k, n,
-                                   group_size, bits, _p(ws), ws.numel(), _p(out), _stream(dev)))
+        if typed:
+            _lib.check(lib.qaff_qmm_nt_typed(_p(x), _ANY_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), sb,
+                                             k, n, group_size, bits, _p(ws), ws.numel(), _p(out), _stream(dev)))
+        else:
+            _lib.check(lib.qaff_qmm_nt(_p(x), _OUT_DTYPES[x.dtype], m, _p(packed), _p(scales), _p(biases), k, n,
+                                       group_size, bits, _p(ws), ws.numel(), _p(out), _stream(dev)))
     return out
 
 

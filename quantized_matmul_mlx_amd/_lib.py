@@ -25,7 +25,8 @@ EXPORTS = ("qaff_dequantize", "qaff_qmm", "qaff_qmm_ex", "qaff_dequant_rows", "q
            "qaff_quantize", "qaff_qmm_nt", "qaff_qmm_nt_workspace_size", "qaff_qmm_nt_static",
            "qaff_qmm_nt_static_max_bytes", "qaff_qmm_ws", "qaff_qmm_workspace_size",
            "qaff_promote_dtype",
-           "qaff_dequantize_typed", "qaff_qmm_typed", "qaff_quantize_typed", "qaff_gather_qmm_typed")
+           "qaff_dequantize_typed", "qaff_qmm_typed", "qaff_quantize_typed", "qaff_gather_qmm_typed",
+           "qaff_qmm_nt_typed")
 
 ABI_VERSION = 1
 
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.qaff_qmm_typed.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, vp, vp]
     lib.qaff_qmm_nt.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, ctypes.c_size_t, vp, vp]
     lib.qaff_qmm_nt_static.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+    lib.qaff_qmm_nt_typed.argtypes = [vp, ctypes.c_int, i64, vp, vp, vp, ctypes.c_int, i64, i64, i32, i32, vp,
+                                      ctypes.c_size_t, vp, vp]
     lib.qaff_qmm_nt_static_max_bytes.argtypes = []
     lib.qaff_qmm_nt_static_max_bytes.restype = ctypes.c_size_t
     lib.qaff_qmm_nt_workspace_size.argtypes = [i64, i64, i64, i32]
@@ -79,7 +82,8 @@ def load() -> ctypes.CDLL:
     for f in (lib.qaff_dequantize, lib.qaff_qmm, lib.qaff_qmm_ex, lib.qaff_dequant_rows,
               lib.qaff_gemv_gate_up, lib.qaff_gemv_silu_gate, lib.qaff_gather_qmm, lib.qaff_gather_qmm_ex,
               lib.qaff_gather_qmm_typed,
-              lib.qaff_quantize, lib.qaff_quantize_typed, lib.qaff_qmm_nt, lib.qaff_qmm_nt_static, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
+              lib.qaff_quantize, lib.qaff_quantize_typed, lib.qaff_qmm_nt, lib.qaff_qmm_nt_static,
+              lib.qaff_qmm_nt_typed, lib.qaff_dequantize_typed, lib.qaff_qmm_typed, lib.qaff_qmm_ws):
         f.restype = ctypes.c_int
     lib.qaff_last_error.restype = ctypes.c_char_p
     lib.qaff_last_error.argtypes = []

@@ -618,26 +618,32 @@ size_t qaff_qmm_nt_workspace_size(int64_t m, int64_t k, int64_t n, int32_t bits)
 
 namespace {
 
-// qaff_qmm_nt with the workspace given (ws) or, for qaff_qmm_nt_static (ws null), the library's
-// static scratch array of the current device.
+// qaff_qmm_nt (bf16 scales, typed = false) and qaff_qmm_nt_typed with the workspace given (ws) or,
+// for qaff_qmm_nt_static (ws null), the library's static scratch array of the current device.
 qaff_status qmm_nt_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
-                        const uint16_t* scales, const uint16_t* biases, int64_t k, int64_t n, int32_t group_size,
-                        int32_t bits, void* workspace, size_t workspace_bytes, bool use_static, void* y,
-                        hipStream_t stream) {
+                        const void* scales, const void* biases, qaff_dtype sb_dtype, bool typed, int64_t k,
+                        int64_t n, int32_t group_size, int32_t bits, void* workspace, size_t workspace_bytes,
+                        bool use_static, void* y, hipStream_t stream) {
     g_error.clear();
+    if (typed ? !any_dtype(x_dtype) || !any_dtype(sb_dtype) : !valid_dtype(x_dtype))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown dtype (x %d, scales %d)", op, (int)x_dtype, (int)sb_dtype);
     // the weight is [k, n]: k rows of n codes
-    qaff_status st = check_weight(op, packed, scales, biases, k, n, group_size, bits);
+    qaff_status st = check_weight(op, packed, static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(biases),
+                                  k, n, group_size, bits);
     if (st != QAFF_OK) return st;
     if (m < 0) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: negative m", op);
-    if (!valid_dtype(x_dtype)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: unknown x dtype %d", op, (int)x_dtype);
     if (m == 0 || n == 0) return QAFF_OK;
+    if (sb_dtype == QAFF_F32 && k > 0 && (!aligned(scales, 4) || !aligned(biases, 4)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: float32 scales and biases must be 4-byte aligned", op);
     // the kernels load x and store y one element at a time: element alignment is enough
-    const int64_t esize = (int64_t)esize_of(x_dtype);
+    const qaff_dtype y_dtype = qaff_promote_dtype(x_dtype, sb_dtype);
+    const int64_t ysize = (int64_t)esize_of(y_dtype);
     if (!y) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null y", op);
-    if (!aligned(y, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
-    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * esize, stream), stream);
+    if (!aligned(y, ysize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: y must be aligned to its element size", op);
+    if (k == 0) return after_launch(op, qaff::launch_fill_zero(y, m * n * ysize, stream), stream);
     if (!x) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: null x", op);
-    if (!aligned(x, esize)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
+    if (!aligned(x, esize_of(x_dtype)))
+        return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: x must be aligned to its element size", op);
     if (m * n >= (1LL << 31) || k > 0x7fffffffLL || n > 0x7fffffffLL)
         return fail(QAFF_ERR_UNSUPPORTED, "%s: %lld x %lld outputs or k = %lld is too large", op, (long long)m,
                     (long long)n, (long long)k);
@@ -658,8 +664,8 @@ qaff_status qmm_nt_impl(const char* op, const void* x, qaff_dtype x_dtype, int64
                         op, need, workspace ? workspace_bytes : (size_t)0);
         if (!aligned(workspace, 16)) return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", op);
     }
-    return after_launch(op, qaff::launch_qmm_nt(x, x_dtype == QAFF_F32, m, packed, scales, biases, k, n, group_size,
-                                                bits, workspace, y, stream), stream);
+    return after_launch(op, qaff::launch_qmm_nt(x, (int)x_dtype, m, packed, scales, biases, (int)sb_dtype, k, n,
+                                                group_size, bits, workspace, y, (int)y_dtype, stream), stream);
 }
 
 }  // namespace
@@ -667,15 +673,22 @@ qaff_status qmm_nt_impl(const char* op, const void* x, qaff_dtype x_dtype, int64
 qaff_status qaff_qmm_nt(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const uint16_t* scales,
                         const uint16_t* biases, int64_t k, int64_t n, int32_t group_size, int32_t bits,
                         void* workspace, size_t workspace_bytes, void* y, hipStream_t stream) {
-    return qmm_nt_impl("qaff_qmm_nt", x, x_dtype, m, packed, scales, biases, k, n, group_size, bits, workspace,
-                       workspace_bytes, false, y, stream);
+    return qmm_nt_impl("qaff_qmm_nt", x, x_dtype, m, packed, scales, biases, QAFF_BF16, false, k, n, group_size, bits,
+                       workspace, workspace_bytes, false, y, stream);
+}
+
+qaff_status qaff_qmm_nt_typed(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                              const void* biases, qaff_dtype sb_dtype, int64_t k, int64_t n, int32_t group_size,
+                              int32_t bits, void* workspace, size_t workspace_bytes, void* y, hipStream_t stream) {
+    return qmm_nt_impl("qaff_qmm_nt_typed", x, x_dtype, m, packed, scales, biases, sb_dtype, true, k, n, group_size,
+                       bits, workspace, workspace_bytes, false, y, stream);
 }
 
 qaff_status qaff_qmm_nt_static(const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
                                const uint16_t* scales, const uint16_t* biases, int64_t k, int64_t n,
                                int32_t group_size, int32_t bits, void* y, hipStream_t stream) {
-    return qmm_nt_impl("qaff_qmm_nt_static", x, x_dtype, m, packed, scales, biases, k, n, group_size, bits, nullptr,
-                       0, true, y, stream);
+    return qmm_nt_impl("qaff_qmm_nt_static", x, x_dtype, m, packed, scales, biases, QAFF_BF16, false, k, n, group_size,
+                       bits, nullptr, 0, true, y, stream);
 }
 
 size_t qaff_qmm_nt_static_max_bytes(void) { return qaff::kQmmNtStaticScratchBytes; }

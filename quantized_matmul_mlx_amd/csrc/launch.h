@@ -129,12 +129,12 @@ hipError_t launch_quantize(const void* w, int w_dtype, int64_t rows, int64_t col
 
 // y[m, n] = x[m, k] . dequantize(W) for W stored [k, n] (groups along n); float32 partial sums
 // of K chunks go to `workspace` (qmm_nt_workspace_bytes(m, k, n) bytes), then a second kernel
-// adds them in order. y in x's dtype.
+// adds them in order. Dtype codes 0 float32, 1 bf16, 2 float16 for x, the scales and biases, and y.
 void qmm_nt_plan(int64_t k, int64_t n, int bits, int64_t* kchunk, int64_t* chunks);
 size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n, int bits);
-hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                         const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
-                         void* y, hipStream_t stream);
+hipError_t launch_qmm_nt(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                         const void* biases, int sb_dtype, int64_t k, int64_t n, int group_size, int bits,
+                         void* workspace, void* y, int y_dtype, hipStream_t stream);
 
 // The device address of the static scratch array that stands in for qmm_nt's workspace
 // (kQmmNtStaticScratchBytes on every device), resolved once per device with it current.

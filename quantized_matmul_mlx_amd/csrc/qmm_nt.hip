@@ -15,6 +15,10 @@
 //    (Measured at [4096, 4096] 4-bit, M = 1: 8 rows per lane 9.8 us, 16 rows 10.5, 4 rows 11.4.)
 //  * The 16 phases' partial sums are added through LDS (rows padded to 33 floats against bank
 //    conflicts).
+// x and the scales and biases come in three forms (XK): bf16 x with bf16 scales, float32 x with
+// bf16 scales, or each of float32, bf16 or float16 as the launch says (the module's promotion of x,
+// scales and biases to one float type); every value is widened to float32 exactly, so the sums are
+// the same arithmetic in all three.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -63,10 +67,12 @@ __device__ __forceinline__ void codes_f32(const uint32_t (&w)[BITS], float (&cf)
     }
 }
 
-template <int BITS, int MB, bool XF32>
+// XK: 0 bf16 x and bf16 scales, 1 float32 x and bf16 scales, 2 x of dtype code xd and scales and
+// biases of sbd (0 float32, 1 bf16, 2 float16).
+template <int BITS, int MB, int XK>
 __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
-    const void* x, uint32_t m, const uint32_t* packed, const uint16_t* scales, const uint16_t* biases,
-    uint32_t n, uint32_t k, uint32_t gshift, float* ws) {
+    const void* x, uint32_t m, const uint32_t* packed, const void* scales, const void* biases,
+    uint32_t n, uint32_t k, uint32_t gshift, int xd, int sbd, float* ws) {
     __shared__ float red[kNtPhases * kNtCols * MB * kNtPad];  // [phase][column block][MB][kNtPad]
     const int tid = threadIdx.x;
     const int cbl = tid & (kNtCols - 1);
@@ -82,19 +88,28 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     // 1. Every load first: the lane's kRows rows (k0 + phase + 16 i) of codes, scale, bias and x.
     //    Rows past k are clamped and get x = 0, so they add nothing.
     uint32_t w[kRows][BITS];
-    uint32_t sraw[kRows], braw[kRows];
+    uint32_t sraw[kRows], braw[kRows];  // XK 0, 1: the bf16 bits
+    float sv[kRows], bv[kRows];         // XK 2: widened at the load
     float xv[kRows][MB];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         const uint32_t kk = k0 + phase + kNtPhases * i;
         const uint32_t kc = min(kk, k - 1);
         load_block<BITS>(packed + ((size_t)kc * ncb + cbc) * BITS, w[i]);
-        sraw[i] = scales[(size_t)kc * gpr + g];
-        braw[i] = biases[(size_t)kc * gpr + g];
+        const size_t si = (size_t)kc * gpr + g;
+        if constexpr (XK == 2) {
+            sv[i] = load_as_f32(scales, si, sbd);
+            bv[i] = load_as_f32(biases, si, sbd);
+        } else {
+            sraw[i] = static_cast<const uint16_t*>(scales)[si];
+            braw[i] = static_cast<const uint16_t*>(biases)[si];
+        }
 #pragma unroll
         for (int r = 0; r < MB; ++r) {
             const size_t o = (size_t)min((uint32_t)r, m - 1) * k + kc;
-            const float v = XF32 ? static_cast<const float*>(x)[o] : bf16_to_f32(static_cast<const uint16_t*>(x)[o]);
+            const float v = XK == 2 ? load_as_f32(x, o, xd)
+                          : XK == 1 ? static_cast<const float*>(x)[o]
+                                    : bf16_to_f32(static_cast<const uint16_t*>(x)[o]);
             xv[i][r] = kk < k ? v : 0.f;
         }
     }
@@ -110,8 +125,8 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        const float s = bf16_to_f32(sraw[i]);
-        const float b = bf16_to_f32(braw[i]);
+        const float s = XK == 2 ? sv[i] : bf16_to_f32(sraw[i]);
+        const float b = XK == 2 ? bv[i] : bf16_to_f32(braw[i]);
         float cf[32];
         codes_f32<BITS>(w[i], cf);
 #pragma unroll
@@ -139,8 +154,9 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     }
 }
 
-// y[r, col] = sum over the chunks of ws[chunk][r][col], in chunk order.
-template <bool OUT_BF16>
+// y[r, col] = sum over the chunks of ws[chunk][r][col], in chunk order, stored as dtype code OUT
+// (0 float32, 1 bf16, 2 float16; round to nearest even).
+template <int OUT>
 __global__ __launch_bounds__(256) void qmm_nt_reduce_kernel(const float* ws, uint32_t chunks, uint32_t mb,
                                                             uint32_t m, uint32_t n, void* y) {
     const uint32_t o = blockIdx.x * 256 + threadIdx.x;
@@ -157,8 +173,7 @@ __global__ __launch_bounds__(256) void qmm_nt_reduce_kernel(const float* ws, uin
         for (int j = 0; j < 32; ++j)
             if (s + j < chunks) sum += v[j];
     }
-    if (OUT_BF16) static_cast<uint16_t*>(y)[o] = to_bf16_bits(sum);
-    else static_cast<float*>(y)[o] = sum;
+    store_from_f32(y, o, OUT, sum);
 }
 
 }  // namespace
@@ -184,42 +199,55 @@ size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n, int bits) {
 
 namespace {
 
-template <int BITS, int MB, bool XF32>
-hipError_t launch_slice(const void* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                        const uint16_t* biases, int64_t k, int64_t n, uint32_t gshift, int64_t kchunk,
-                        int64_t chunks, float* ws, void* y, hipStream_t stream) {
-    (void)kchunk;
+// The operand types of one launch: x and scales/biases dtype codes, y's, and the kernel form.
+struct NtTypes {
+    int xd, sbd, yd, xk;
+};
+
+template <int BITS, int MB, int XK>
+hipError_t launch_slice(const void* x, int64_t m, const uint32_t* packed, const void* scales, const void* biases,
+                        int64_t k, int64_t n, uint32_t gshift, int64_t chunks, const NtTypes& t, float* ws, void* y,
+                        hipStream_t stream) {
     const unsigned gx = (unsigned)(((n / 32) + kNtCols - 1) / kNtCols);
-    qmm_nt_partial_kernel<BITS, MB, XF32><<<dim3(gx, (unsigned)chunks), kNtThreads, 0, stream>>>(
-        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)k, gshift, ws);
+    qmm_nt_partial_kernel<BITS, MB, XK><<<dim3(gx, (unsigned)chunks), kNtThreads, 0, stream>>>(
+        x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)k, gshift, t.xd, t.sbd, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned gr = (unsigned)((m * n + 255) / 256);
-    if (XF32)
-        qmm_nt_reduce_kernel<false><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
+    if (t.yd == 1)
+        qmm_nt_reduce_kernel<1><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
+    else if (t.yd == 2)
+        qmm_nt_reduce_kernel<2><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
     else
-        qmm_nt_reduce_kernel<true><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
+        qmm_nt_reduce_kernel<0><<<gr, 256, 0, stream>>>(ws, (uint32_t)chunks, MB, (uint32_t)m, (uint32_t)n, y);
     return hipGetLastError();
 }
 
+template <int BITS, int MB>
+hipError_t launch_form(const void* x, int64_t m, const uint32_t* packed, const void* scales, const void* biases,
+                       int64_t k, int64_t n, uint32_t gshift, int64_t chunks, const NtTypes& t, float* ws, void* y,
+                       hipStream_t stream) {
+    switch (t.xk) {
+        case 0: return launch_slice<BITS, MB, 0>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
+        case 1: return launch_slice<BITS, MB, 1>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
+        default: return launch_slice<BITS, MB, 2>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
+    }
+}
+
 template <int BITS>
-hipError_t launch_bits(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                       const uint16_t* biases, int64_t k, int64_t n, uint32_t gshift, float* ws, void* y,
+hipError_t launch_bits(const void* x, int64_t m, const uint32_t* packed, const void* scales, const void* biases,
+                       int64_t k, int64_t n, uint32_t gshift, const NtTypes& t, float* ws, void* y,
                        hipStream_t stream) {
     int64_t kchunk, chunks;
     qmm_nt_plan(k, n, BITS, &kchunk, &chunks);
-    const size_t xsize = x_f32 ? 4 : 2;
+    const size_t xsize = t.xd == 0 ? 4 : 2, ysize = t.yd == 0 ? 4 : 2;
     for (int64_t m0 = 0; m0 < m; m0 += kNtMaxM) {
         const int64_t mm = m - m0 < kNtMaxM ? m - m0 : kNtMaxM;
         const void* xs = static_cast<const uint8_t*>(x) + (size_t)m0 * k * xsize;
-        void* ys = static_cast<uint8_t*>(y) + (size_t)m0 * n * xsize;
-        hipError_t e;
-        if (mm == 1)
-            e = x_f32 ? launch_slice<BITS, 1, true>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream)
-                      : launch_slice<BITS, 1, false>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream);
-        else
-            e = x_f32 ? launch_slice<BITS, 2, true>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream)
-                      : launch_slice<BITS, 2, false>(xs, mm, packed, scales, biases, k, n, gshift, kchunk, chunks, ws, ys, stream);
+        void* ys = static_cast<uint8_t*>(y) + (size_t)m0 * n * ysize;
+        const hipError_t e =
+            mm == 1 ? launch_form<BITS, 1>(xs, mm, packed, scales, biases, k, n, gshift, chunks, t, ws, ys, stream)
+                    : launch_form<BITS, 2>(xs, mm, packed, scales, biases, k, n, gshift, chunks, t, ws, ys, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -246,19 +274,23 @@ hipError_t qmm_nt_static_scratch(void** ptr) {
     return hipSuccess;
 }
 
-hipError_t launch_qmm_nt(const void* x, bool x_f32, int64_t m, const uint32_t* packed, const uint16_t* scales,
-                         const uint16_t* biases, int64_t k, int64_t n, int group_size, int bits, void* workspace,
-                         void* y, hipStream_t stream) {
+hipError_t launch_qmm_nt(const void* x, int x_dtype, int64_t m, const uint32_t* packed, const void* scales,
+                         const void* biases, int sb_dtype, int64_t k, int64_t n, int group_size, int bits,
+                         void* workspace, void* y, int y_dtype, hipStream_t stream) {
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     float* ws = static_cast<float*>(workspace);
+    // bf16 scales with a bf16 or float32 x (and y of x's type) keep their fixed-type kernels
+    const int xk = sb_dtype == 1 && x_dtype == 1 && y_dtype == 1 ? 0
+                 : sb_dtype == 1 && x_dtype == 0 && y_dtype == 0 ? 1 : 2;
+    const NtTypes t{x_dtype, sb_dtype, y_dtype, xk};
     switch (bits) {
-        case 1: return launch_bits<1>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 2: return launch_bits<2>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 3: return launch_bits<3>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 4: return launch_bits<4>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 5: return launch_bits<5>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 6: return launch_bits<6>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
-        case 8: return launch_bits<8>(x, x_f32, m, packed, scales, biases, k, n, gshift, ws, y, stream);
+        case 1: return launch_bits<1>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 2: return launch_bits<2>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 3: return launch_bits<3>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 4: return launch_bits<4>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 5: return launch_bits<5>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 6: return launch_bits<6>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
+        case 8: return launch_bits<8>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -81,8 +81,8 @@ void qmm_nt_plan(int64_t k, int64_t, int, int64_t* kchunk, int64_t* chunks) { *k
 size_t qmm_nt_workspace_bytes(int64_t m, int64_t k, int64_t n, int) {
     return (size_t)(((k + 127) / 128) * (m < 2 ? m : 2) * n) * 4;
 }
-hipError_t launch_qmm_nt(const void*, bool, int64_t, const uint32_t*, const uint16_t*, const uint16_t*, int64_t,
-                         int64_t, int, int, void* ws, void*, hipStream_t) { return rec(ws ? "qmm_nt" : "qmm_nt_null_ws"); }
+hipError_t launch_qmm_nt(const void*, int, int64_t, const uint32_t*, const void*, const void*, int, int64_t,
+                         int64_t, int, int, void* ws, void*, int, hipStream_t) { return rec(ws ? "qmm_nt" : "qmm_nt_null_ws"); }
 static uint8_t fake_scratch[64];
 hipError_t qmm_nt_static_scratch(void** ptr) { *ptr = fake_scratch; return rec("static_scratch"); }
 hipError_t launch_dequant_typed(const uint32_t*, const void*, const void*, int, int64_t, int64_t, int, int, void*, int,
@@ -226,6 +226,19 @@ int main() {
     EXPECT(INV, "", qaff_qmm_nt(A16, QAFF_BF16, 2, P16, S16, B16, 4096, 4096, 64, 4, A16, nt - 4, A16, nullptr));
     EXPECT(OK, "qmm_nt", qaff_qmm_nt_static(A16, QAFF_BF16, 2, P16, S16, B16, 4096, 4096, 64, 4, A16, nullptr));
     EXPECT(UNS, "", qaff_qmm_nt_static(A16, QAFF_BF16, 2, P16, S16, B16, 128 * 300, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "qmm_nt", qaff_qmm_nt_typed(A2, QAFF_F16, 2, P16, S16, B16, QAFF_F16, 4096, 4096, 64, 4, A16, nt,
+                                                 A2, nullptr));
+    EXPECT(OK, "qmm_nt", qaff_qmm_nt_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_BF16, 4096, 4096, 64, 4, A16, nt, A16,
+                                           nullptr));  // float32 y
+    EXPECT(INV, "", qaff_qmm_nt_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_BF16, 4096, 4096, 64, 4, A16, nt, A2,
+                                      nullptr));  // the float32 y needs 4-byte alignment
+    EXPECT(INV, "", qaff_qmm_nt_typed(A16, QAFF_F16, 2, P16, reinterpret_cast<const uint16_t*>(A2), B16, QAFF_F32, 4096,
+                                      4096, 64, 4, A16, nt, A16, nullptr));  // float32 scales need 4-byte alignment
+    EXPECT(INV, "", qaff_qmm_nt_typed(A16, (qaff_dtype)3, 2, P16, S16, B16, QAFF_F16, 4096, 4096, 64, 4, A16, nt, A16,
+                                      nullptr));
+    EXPECT(INV, "", qaff_qmm_nt(A16, QAFF_F16, 2, P16, S16, B16, 4096, 4096, 64, 4, A16, nt, A16, nullptr));
+    EXPECT(INV, "", qaff_qmm_nt_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_F16, 4096, 4096, 64, 4, A16, nt - 4, A16,
+                                      nullptr));
     // other float types
     EXPECT(OK, "dequant_typed", qaff_dequantize_typed(P16, S16, B16, QAFF_F16, 4, 64, 32, 4, A16, QAFF_F32, nullptr));
     EXPECT(OK, "dequant", qaff_dequantize_typed(P16, S16, B16, QAFF_BF16, 4, 64, 32, 4, A16, QAFF_F32, nullptr));

@@ -295,6 +295,23 @@ def test_qmm_nt_checks(lib):
     assert qnt(lib, m=0, x=NULL, y=NULL, ws=NULL) == OK
 
 
+def test_qmm_nt_typed_checks(lib):
+    F16 = _lib.QAFF_F16
+    q = lambda xt=F16, sb=F16, m=1, x=A16, y=A16, scales=A16, ws=A16, wsb=1 << 20, bits=4: lib.qaff_qmm_nt_typed(
+        x, xt, m, A16, scales, A16, sb, 64, 64, 32, bits, ws, wsb, y, NULL)
+    assert q(xt=5) == INVALID and q(sb=3) == INVALID
+    assert q(bits=7) == UNSUPPORTED
+    assert q(sb=F32, scales=A2) == INVALID                   # float32 scales are 4-byte aligned
+    assert q(sb=BF16, y=A2) == INVALID                       # float16 x with bf16 scales: float32 y
+    assert q(xt=F32, x=A2) == INVALID
+    assert q(y=NULL) == INVALID
+    assert q(ws=NULL) == INVALID and b"workspace" in lib.qaff_last_error()
+    assert q(wsb=4) == INVALID
+    assert q(m=0, x=NULL, y=NULL, ws=NULL) == OK
+    # the plain entry point keeps its types: float16 x is not one of them
+    assert qnt(lib, dtype=F16) == INVALID
+
+
 def qws(lib, m=128, n=4096, k=14336, G=128, bits=4, x=A16, y=A16, ws=A16, wsb=1 << 26):
     return lib.qaff_qmm_ws(x, BF16, m, A16, A16, A16, n, k, G, bits, ws, wsb, y, NULL)
 

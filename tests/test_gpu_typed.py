@@ -149,6 +149,79 @@ def test_bf16_only_operations_reject_other_scales(orc):
               to_dev(inp.biases, "bf16"), 64, 4)
 
 
+# ---- the product without the transpose (W stored [k, n]), typed ----------------------------------
+
+def typed_x(x32, xt):
+    return x32 if xt == "f32" else (x32.astype(np.float16).view(np.uint16) if xt == "f16" else W.bf16_bits_from_f32(x32))
+
+
+@pytest.mark.parametrize("xt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("sb", ["f16", "f32", "bf16"])
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128), (1, 32), (6, 64)])
+def test_qmm_nt_typed(orc, xt, sb, bits, G):
+    # k = 100 rows (not a multiple of the 16 row phases), n = 5 G (a ragged column tile), m = 3 (a
+    # slice of 2 x rows and one of 1)
+    k, n, m = 100, 5 * G, 3
+    inp = W.random_inputs(bits, G, k, n, 0, seed=bits * 11 + G)      # a [k, n] weight: groups along n
+    hs, hb, ds, db = scales_of(inp, sb, seed=bits + 3 * G)
+    hx = typed_x(np.random.default_rng(bits + G).standard_normal((m, k)).astype(np.float32), xt)
+    banner(f"qmm_nt typed x={xt} sb={sb} bits={bits} G={G}")
+    y = qaff().qmm(to_dev(hx, xt), dev_u32(inp.packed), ds, db, G, bits, transpose=False)
+    torch.cuda.synchronize()
+    want = promoted(xt, sb)
+    assert y.dtype == want and tuple(y.shape) == (m, n)
+    ref = orc.qmm_nt_typed(hx, xt, inp.packed, hs, hb, sb, G, bits)
+    got = y.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = orc.max_row_rel_err(got, ref)
+    assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
+
+
+@pytest.mark.parametrize("sb", ["f16", "f32"])
+def test_qmm_nt_typed_full_size(orc, sb):
+    # a [4096, 4096] 4-bit g64 weight, x [2, 4096] float16: 32 K chunks per column tile
+    k = n = 4096
+    inp = W.random_inputs(4, 64, k, n, 0, seed=123)
+    hs, hb, ds, db = scales_of(inp, sb, seed=124)
+    hx = typed_x(np.random.default_rng(125).standard_normal((2, k)).astype(np.float32), "f16")
+    banner(f"qmm_nt typed full size sb={sb}")
+    y = qaff().qmm_nt(to_dev(hx, "f16"), dev_u32(inp.packed), ds, db, 64, 4)
+    torch.cuda.synchronize()
+    want = promoted("f16", sb)
+    ref = orc.qmm_nt_typed(hx, "f16", inp.packed, hs, hb, sb, 64, 4)
+    err = orc.max_row_rel_err(y.float().cpu().numpy().astype(np.float64), ref)
+    assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
+
+
+def test_qmm_nt_typed_float16_x_is_its_float32_copy(orc):
+    # every operand is widened to float32 exactly as it is loaded, so a float16 x (the run-time
+    # typed kernel) and the float32 x of the same values (the float32 kernel) give the same y, bit
+    # for bit, with bf16 scales; a 1-D x is one row
+    k, n = 700, 320
+    inp = W.random_inputs(5, 32, k, n, 0, seed=130)
+    x16 = np.random.default_rng(131).standard_normal((3, k)).astype(np.float16)
+    p, s, b = dev_u32(inp.packed), to_dev(inp.scales, "bf16"), to_dev(inp.biases, "bf16")
+    banner("qmm_nt typed float16 x against its float32 copy")
+    y16 = qaff().qmm_nt(to_dev(x16.view(np.uint16), "f16"), p, s, b, 32, 5)
+    y32 = qaff().qmm_nt(to_dev(x16.astype(np.float32), "f32"), p, s, b, 32, 5)
+    y1 = qaff().qmm_nt(to_dev(x16[1].view(np.uint16), "f16"), p, s, b, 32, 5)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.float32 and tuple(y1.shape) == (n,)
+    assert torch.equal(y16, y32) and torch.equal(y1, y32[1])
+    ref = orc.qmm_nt_typed(x16.view(np.uint16), "f16", inp.packed, inp.scales, inp.biases, "bf16", 32, 5)
+    assert orc.max_row_rel_err(host(y16).astype(np.float64), ref) <= TIGHT[torch.float32]
+
+
+def test_qmm_nt_typed_rejects_the_static_scratch(orc):
+    inp = W.random_inputs(4, 64, 64, 128, 0, seed=140)
+    hs, hb, ds, db = scales_of(inp, "f16", seed=141)
+    x = torch.zeros((1, 64), dtype=torch.float16, device="cuda")
+    banner("qmm_nt typed rejects the static scratch")
+    with pytest.raises(TypeError):
+        qaff().qmm_nt(x, dev_u32(inp.packed), ds, db, 64, 4, out=torch.empty((1, 128), dtype=torch.float16,
+                                                                          device="cuda"), static_scratch=True)
+
+
 # ---- gathered products (nuvec_core gather_qmm: x, scales and biases promote to one type) ----------
 
 def promoted(xt, sb):
