@@ -81,3 +81,10 @@ def test_qmm_nt_one_dim_x_and_k_zero(orc):
     y2 = qaff().qmm(dev_x(x, "bf16"), p, s, b, 64, 4, transpose=False)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 5000, 2048), (4, 4096, 14336), (3, 4097, 3072), (1, 1, 2048)])
+def test_qmm_nt_wide_shapes(orc, m, k, n):
+    # wide outputs, K with a ragged last chunk, a single row of K
+    banner(f"qmm_nt wide m={m} k={k} n={n}")
+    run_check(orc, 4, 64, k, n, m, "bf16", seed=m + k + n + 1)

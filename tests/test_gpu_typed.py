@@ -193,15 +193,17 @@ def test_qmm_nt_typed_full_size(orc, sb):
     assert err <= TIGHT[want], f"max row rel err {err:.3e} > {TIGHT[want]}"
 
 
-def test_qmm_nt_typed_float16_x_is_its_float32_copy(orc):
+@pytest.mark.parametrize("n", [320, 2048])
+def test_qmm_nt_typed_float16_x_is_its_float32_copy(orc, n):
     # every operand is widened to float32 exactly as it is loaded, so a float16 x (the run-time
     # typed kernel) and the float32 x of the same values (the float32 kernel) give the same y, bit
-    # for bit, with bf16 scales; a 1-D x is one row
-    k, n = 700, 320
+    # for bit, with bf16 scales; a 1-D x is one row. n = 320 splits K, n = 2048 takes one thread
+    # block per column block.
+    k = 700
     inp = W.random_inputs(5, 32, k, n, 0, seed=130)
     x16 = np.random.default_rng(131).standard_normal((3, k)).astype(np.float16)
     p, s, b = dev_u32(inp.packed), to_dev(inp.scales, "bf16"), to_dev(inp.biases, "bf16")
-    banner("qmm_nt typed float16 x against its float32 copy")
+    banner(f"qmm_nt typed float16 x against its float32 copy n={n}")
     y16 = qaff().qmm_nt(to_dev(x16.view(np.uint16), "f16"), p, s, b, 32, 5)
     y32 = qaff().qmm_nt(to_dev(x16.astype(np.float32), "f32"), p, s, b, 32, 5)
     y1 = qaff().qmm_nt(to_dev(x16[1].view(np.uint16), "f16"), p, s, b, 32, 5)
