@@ -15,10 +15,12 @@
 //    (Measured at [4096, 4096] 4-bit, M = 1: 8 rows per lane 9.8 us, 16 rows 10.5, 4 rows 11.4.)
 //  * The 16 phases' partial sums are added through LDS (rows padded to 33 floats against bank
 //    conflicts).
-// x and the scales and biases come in three forms (XK): bf16 x with bf16 scales, float32 x with
-// bf16 scales, or each of float32, bf16 or float16 as the launch says (the module's promotion of x,
-// scales and biases to one float type); every value is widened to float32 exactly, so the sums are
-// the same arithmetic in all three.
+// x and the scales and biases come in four forms (XK): bf16 x with bf16 scales, float32 x with
+// bf16 scales, float16 x with float16 scales, or each of float32, bf16 or float16 as the launch
+// says (the module's promotion of x, scales and biases to one float type); every value is widened
+// to float32 exactly, so the sums are the same arithmetic in all four. The fixed-type forms issue
+// a lane's loads back to back; the run-time form's per-load type switches take about twice as
+// long at the decode shape.
 #include "launch.h"
 #include "qaff_device.h"
 
@@ -67,8 +69,8 @@ __device__ __forceinline__ void codes_f32(const uint32_t (&w)[BITS], float (&cf)
     }
 }
 
-// XK: 0 bf16 x and bf16 scales, 1 float32 x and bf16 scales, 2 x of dtype code xd and scales and
-// biases of sbd (0 float32, 1 bf16, 2 float16).
+// XK: 0 bf16 x and bf16 scales, 1 float32 x and bf16 scales, 3 float16 x and float16 scales, 2 x
+// of dtype code xd and scales and biases of sbd (0 float32, 1 bf16, 2 float16).
 template <int BITS, int MB, int XK>
 __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     const void* x, uint32_t m, const uint32_t* packed, const void* scales, const void* biases,
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     // 1. Every load first: the lane's kRows rows (k0 + phase + 16 i) of codes, scale, bias and x.
     //    Rows past k are clamped and get x = 0, so they add nothing.
     uint32_t w[kRows][BITS];
-    uint32_t sraw[kRows], braw[kRows];  // XK 0, 1: the bf16 bits
+    uint32_t sraw[kRows], braw[kRows];  // XK 0, 1, 3: the 16-bit patterns
     float sv[kRows], bv[kRows];         // XK 2: widened at the load
     float xv[kRows][MB];
 #pragma unroll
@@ -109,6 +111,7 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
             const size_t o = (size_t)min((uint32_t)r, m - 1) * k + kc;
             const float v = XK == 2 ? load_as_f32(x, o, xd)
                           : XK == 1 ? static_cast<const float*>(x)[o]
+                          : XK == 3 ? __half2float(__ushort_as_half(static_cast<const uint16_t*>(x)[o]))
                                     : bf16_to_f32(static_cast<const uint16_t*>(x)[o]);
             xv[i][r] = kk < k ? v : 0.f;
         }
@@ -125,8 +128,10 @@ __global__ __launch_bounds__(kNtThreads) void qmm_nt_partial_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        const float s = XK == 2 ? sv[i] : bf16_to_f32(sraw[i]);
-        const float b = XK == 2 ? bv[i] : bf16_to_f32(braw[i]);
+        const float s = XK == 2 ? sv[i]
+                      : XK == 3 ? __half2float(__ushort_as_half((uint16_t)sraw[i])) : bf16_to_f32(sraw[i]);
+        const float b = XK == 2 ? bv[i]
+                      : XK == 3 ? __half2float(__ushort_as_half((uint16_t)braw[i])) : bf16_to_f32(braw[i]);
         float cf[32];
         codes_f32<BITS>(w[i], cf);
 #pragma unroll
@@ -230,6 +235,7 @@ hipError_t launch_form(const void* x, int64_t m, const uint32_t* packed, const v
     switch (t.xk) {
         case 0: return launch_slice<BITS, MB, 0>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
         case 1: return launch_slice<BITS, MB, 1>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
+        case 3: return launch_slice<BITS, MB, 3>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
         default: return launch_slice<BITS, MB, 2>(x, m, packed, scales, biases, k, n, gshift, chunks, t, ws, y, stream);
     }
 }
@@ -279,9 +285,11 @@ hipError_t launch_qmm_nt(const void* x, int x_dtype, int64_t m, const uint32_t* 
                          void* workspace, void* y, int y_dtype, hipStream_t stream) {
     const uint32_t gshift = group_size == 32 ? 0u : group_size == 64 ? 1u : 2u;
     float* ws = static_cast<float*>(workspace);
-    // bf16 scales with a bf16 or float32 x (and y of x's type) keep their fixed-type kernels
+    // bf16 scales with a bf16 or float32 x (and y of x's type), and all-float16 operands, take the
+    // fixed-type forms
     const int xk = sb_dtype == 1 && x_dtype == 1 && y_dtype == 1 ? 0
-                 : sb_dtype == 1 && x_dtype == 0 && y_dtype == 0 ? 1 : 2;
+                 : sb_dtype == 1 && x_dtype == 0 && y_dtype == 0 ? 1
+                 : sb_dtype == 2 && x_dtype == 2 && y_dtype == 2 ? 3 : 2;
     const NtTypes t{x_dtype, sb_dtype, y_dtype, xk};
     switch (bits) {
         case 1: return launch_bits<1>(x, m, packed, scales, biases, k, n, gshift, t, ws, y, stream);

@@ -214,6 +214,24 @@ def test_qmm_nt_typed_float16_x_is_its_float32_copy(orc, n):
     assert orc.max_row_rel_err(host(y16).astype(np.float64), ref) <= TIGHT[torch.float32]
 
 
+@pytest.mark.parametrize("bits,G", [(4, 64), (3, 32), (8, 128)])
+def test_qmm_nt_float16_form_is_the_float32_one_rounded(orc, bits, G):
+    # float16 x, scales and biases (the fixed float16 form, y float16) against float32 copies of the
+    # same values (the run-time typed form, y float32): the same float32 sums, so y16 is y32
+    # rounded to nearest even, bit for bit
+    k, n, m = 700, 5 * G, 3
+    inp = W.random_inputs(bits, G, k, n, 0, seed=150 + bits)
+    hs, hb, ds, db = scales_of(inp, "f16", seed=151 + bits)
+    x16 = np.random.default_rng(152 + bits).standard_normal((m, k)).astype(np.float16)
+    p = dev_u32(inp.packed)
+    banner(f"qmm_nt float16 form against float32 copies bits={bits} G={G}")
+    y16 = qaff().qmm_nt(to_dev(x16.view(np.uint16), "f16"), p, ds, db, G, bits)
+    y32 = qaff().qmm_nt(to_dev(x16.astype(np.float32), "f32"), p, ds.float(), db.float(), G, bits)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.float16 and y32.dtype == torch.float32
+    assert torch.equal(y16, y32.half())
+
+
 def test_qmm_nt_typed_rejects_the_static_scratch(orc):
     inp = W.random_inputs(4, 64, 64, 128, 0, seed=140)
     hs, hb, ds, db = scales_of(inp, "f16", seed=141)
