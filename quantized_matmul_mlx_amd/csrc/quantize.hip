@@ -145,24 +145,35 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     // which |e| (half an ulp at most) cannot overturn; where d == p, the sign is e's.
     // float32 scales: (c0 -+ 1/2) s has up to 9 + 24 bits, exact only in double, and the sign comes
     // from residual_sign.
+    // Most values need none of that: t = fma(d, 1/s, 1/2) lies within 3u|q| + u/2 (u = 2^-24) of
+    // q + 1/2, q the exact quotient, so for |q| <= 2^9 (every code not settled by the clamps) t is
+    // off by less than 2^-14, and where t's fraction is at least 2^-12 from an integer, floor(t) is
+    // already the decision. Only the other values (about one in two thousand) take the exact test,
+    // in a branch the wave skips when none of its lanes needs it (an empty exec mask). Past |q| = 2^9 the clamp gives
+    // the same code either way.
     const float rcp = sc != 0.0f ? 1.0f / sc : 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         float c = 0.0f;
         if (sc != 0.0f) {
             const float d = v[j] - bi;
-            const float c0 = __builtin_floorf(__builtin_fmaf(d, rcp, 0.5f));
-            bool up, down;
-            if (st != 0) {
-                const float dv = d - v[j];
-                const float e = (v[j] - (d - dv)) + (-bi - dv);
-                const float rh = __builtin_fmaf(-(c0 + 0.5f), sc, d);
-                const float rl = __builtin_fmaf(-(c0 - 0.5f), sc, d);
-                up = rh > 0.0f || (rh == 0.0f && e >= 0.0f);    // w - bias >= (c0 + 1/2) s
-                down = rl < 0.0f || (rl == 0.0f && e < 0.0f);   // w - bias <  (c0 - 1/2) s
-            } else {
-                up = residual_sign(v[j], bi, ((double)c0 + 0.5) * (double)sc) >= 0;
-                down = residual_sign(v[j], bi, ((double)c0 - 0.5) * (double)sc) < 0;
+            const float t = __builtin_fmaf(d, rcp, 0.5f);
+            const float c0 = __builtin_floorf(t);
+            const float fr = t - c0;  // exact; NaN for a NaN quotient
+            const bool near = !(fr > 0x1p-12f && fr < 1.0f - 0x1p-12f);
+            bool up = false, down = false;
+            if (near) {
+                if (st != 0) {
+                    const float dv = d - v[j];
+                    const float e = (v[j] - (d - dv)) + (-bi - dv);
+                    const float rh = __builtin_fmaf(-(c0 + 0.5f), sc, d);
+                    const float rl = __builtin_fmaf(-(c0 - 0.5f), sc, d);
+                    up = rh > 0.0f || (rh == 0.0f && e >= 0.0f);    // w - bias >= (c0 + 1/2) s
+                    down = rl < 0.0f || (rl == 0.0f && e < 0.0f);   // w - bias <  (c0 - 1/2) s
+                } else {
+                    up = residual_sign(v[j], bi, ((double)c0 + 0.5) * (double)sc) >= 0;
+                    down = residual_sign(v[j], bi, ((double)c0 - 0.5) * (double)sc) < 0;
+                }
             }
             c = c0 + (up ? 1.0f : 0.0f) - (down ? 1.0f : 0.0f);
             c = c >= 0.0f ? c : 0.0f;  // also a NaN quotient
