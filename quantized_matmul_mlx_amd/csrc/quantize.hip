@@ -151,38 +151,43 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const void* w, 
     // already the decision. Only the other values (about one in two thousand) take the exact test,
     // in a branch the wave skips when none of its lanes needs it (an empty exec mask). Past |q| = 2^9 the clamp gives
     // the same code either way.
+    // A scale of 0 (a constant group) gives code 0 everywhere: the loop runs with a reciprocal of
+    // 0 (t = 1/2, or NaN for a non-finite d, which takes the exact test) and its words are
+    // cleared after it, instead of a branch per value.
     const float rcp = sc != 0.0f ? 1.0f / sc : 0.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-        float c = 0.0f;
-        if (sc != 0.0f) {
-            const float d = v[j] - bi;
-            const float t = __builtin_fmaf(d, rcp, 0.5f);
-            const float c0 = __builtin_floorf(t);
-            const float fr = t - c0;  // exact; NaN for a NaN quotient
-            const bool near = !(fr > 0x1p-12f && fr < 1.0f - 0x1p-12f);
-            bool up = false, down = false;
-            if (near) {
-                if (st != 0) {
-                    const float dv = d - v[j];
-                    const float e = (v[j] - (d - dv)) + (-bi - dv);
-                    const float rh = __builtin_fmaf(-(c0 + 0.5f), sc, d);
-                    const float rl = __builtin_fmaf(-(c0 - 0.5f), sc, d);
-                    up = rh > 0.0f || (rh == 0.0f && e >= 0.0f);    // w - bias >= (c0 + 1/2) s
-                    down = rl < 0.0f || (rl == 0.0f && e < 0.0f);   // w - bias <  (c0 - 1/2) s
-                } else {
-                    up = residual_sign(v[j], bi, ((double)c0 + 0.5) * (double)sc) >= 0;
-                    down = residual_sign(v[j], bi, ((double)c0 - 0.5) * (double)sc) < 0;
-                }
+        const float d = v[j] - bi;
+        const float t = __builtin_fmaf(d, rcp, 0.5f);
+        const float c0 = __builtin_floorf(t);
+        // near a tie: t's fraction within 2^-12 of 0 or 1, or NaN (the comparison is then false)
+        const bool near = !(__builtin_fabsf((t - c0) - 0.5f) < 0.5f - 0x1p-12f);
+        float adj = 0.0f;  // the exact test's correction of c0: +1, 0 or -1
+        if (near) {
+            bool up, down;
+            if (st != 0) {
+                const float dv = d - v[j];
+                const float e = (v[j] - (d - dv)) + (-bi - dv);
+                const float rh = __builtin_fmaf(-(c0 + 0.5f), sc, d);
+                const float rl = __builtin_fmaf(-(c0 - 0.5f), sc, d);
+                up = rh > 0.0f || (rh == 0.0f && e >= 0.0f);    // w - bias >= (c0 + 1/2) s
+                down = rl < 0.0f || (rl == 0.0f && e < 0.0f);   // w - bias <  (c0 - 1/2) s
+            } else {
+                up = residual_sign(v[j], bi, ((double)c0 + 0.5) * (double)sc) >= 0;
+                down = residual_sign(v[j], bi, ((double)c0 - 0.5) * (double)sc) < 0;
             }
-            c = c0 + (up ? 1.0f : 0.0f) - (down ? 1.0f : 0.0f);
-            c = c >= 0.0f ? c : 0.0f;  // also a NaN quotient
-            c = c > kTop ? kTop : c;
+            adj = (up ? 1.0f : 0.0f) - (down ? 1.0f : 0.0f);
         }
+        float c = c0 + adj;
+        c = __builtin_fminf(__builtin_fmaxf(c, 0.0f), kTop);  // a NaN quotient gives 0
         const uint32_t code = (uint32_t)c;
         const int p = j * BITS;  // bit position in the block's stream (compile-time after unrolling)
         words[p >> 5] |= code << (p & 31);
         if ((p & 31) + BITS > 32) words[(p >> 5) + 1] |= code >> (32 - (p & 31));
+    }
+    if (sc == 0.0f) {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) words[i] = 0u;
     }
 
     if (!live) return;
