@@ -177,11 +177,12 @@ qaff_status qaff_qmm_ex(const void* x, qaff_dtype x_dtype, int64_t m,
 
 /*
  * qaff_qmm (QAFF_PATH_AUTO) with a workspace that lets the bf16 GEMM path split K (nuvec_core
- * quantized_matmul with transpose, as qaff_qmm). Where the GEMM's 128 x 256 tiles are fewer than
- * the compute units (m up to about 1024 at n = 4096, K a multiple of 1024; and 8 <= m <= 16 with K
- * above 32768, which the decode kernels would otherwise take on the VALU), K is split into ranges
- * of whole 1024-code chunks: each range's float32 partial sums go to `workspace`, and a second
- * kernel adds the ranges in a fixed order (results are deterministic) and rounds y to bf16.
+ * quantized_matmul with transpose, as qaff_qmm). Where the GEMM's tiles (64 x 256 up to 128 rows
+ * of x, 128 x 256 above) are fewer than the compute units (m up to about 1024 at n = 4096, K a
+ * multiple of 1024; and 8 <= m <= 16 with K above 32768, which the decode kernels would otherwise
+ * take on the VALU), K is split into ranges of whole 1024-code chunks: each range's float32
+ * partial sums go to `workspace`, and a second kernel adds the ranges in a fixed order (results
+ * are deterministic) and rounds y to bf16.
  *   Arguments as qaff_qmm, plus workspace: a caller-owned device buffer of at least
  *   qaff_qmm_workspace_size(m, n, k, group_size, bits) bytes, 16-byte aligned, which the call
  *   overwrites; it may be NULL when that size is 0. Calls that share a workspace must not overlap.

@@ -291,14 +291,18 @@ __device__ __forceinline__ void direct_tile(
     }
 }
 
-template <int BITS, int GSHIFT, bool PARTIAL, bool GENERAL, bool F16>
+// SUB: 32-row sub-tiles per tile (4: 128-row tiles; 2: 64-row tiles, for split K at few rows).
+template <int BITS, int GSHIFT, bool PARTIAL, bool GENERAL, bool F16, int SUB>
 __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
     const uint16_t* x, uint32_t m, const uint32_t* packed, const uint16_t* scales,
     const uint16_t* biases, uint32_t n, uint32_t kb, uint16_t* y, uint32_t tiles_m,
     uint32_t tiles_n, float* part, uint32_t splits) {
     __shared__ __attribute__((aligned(16))) uint16_t xl[2][DBM * LDK];
     // Tile order: block b runs on XCD b % 8, so each XCD gets a contiguous run of 32 tiles, laid
-    // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2.
+    // out as 4 tile rows x 8 tile columns where the grid allows, to share X and W in its L2. With
+    // one or two tile rows the run goes down the columns instead, so that each XCD fetches whole W
+    // tile columns (for both rows) and no W column is fetched by two XCDs (x [128, 14336] on
+    // [4096, 14336] in 64-row tiles: about 60 MB against 77 MB across the L2s).
     const uint32_t tiles = tiles_m * tiles_n;
     uint32_t t = blockIdx.x;
     if ((tiles & 7u) == 0) t = (t & 7u) * (tiles >> 3) + (t >> 3);
@@ -307,12 +311,15 @@ __global__ __launch_bounds__(kDirectThreads) void gemm_direct_kernel(
         const uint32_t st = t >> 5, w = t & 31u, stn = tiles_n >> 3;
         tm = (st / stn) * 4 + (w >> 3);
         tn = (st % stn) * 8 + (w & 7u);
+    } else if (tiles_m <= 2) {
+        tm = t % tiles_m;
+        tn = t / tiles_m;
     } else {
         tm = t / tiles_n;
         tn = t % tiles_n;
     }
-    direct_tile<BITS, GSHIFT, PARTIAL, 4, GENERAL, F16>(x, m, packed, scales, biases, n, kb, y, tm * DBM, tn * DBN,
-                                                        part, PARTIAL ? blockIdx.y : 0u, splits, xl);
+    direct_tile<BITS, GSHIFT, PARTIAL, SUB, GENERAL, F16>(x, m, packed, scales, biases, n, kb, y, tm * (32 * SUB),
+                                                          tn * DBN, part, PARTIAL ? blockIdx.y : 0u, splits, xl);
 }
 
 // ---- gathered batches grouped by expert (nuvec_core quantized.rs, gather_qmm with sorted rhs) --
@@ -382,15 +389,25 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, ui
     }
 }
 
+// Tile rows of the split-K GEMM: 64-row tiles up to 128 rows of x (their partial sums are half
+// those of a 14-way split of 128-row tiles: at x [128, 14336] on [4096, 14336], 27.9 against
+// 29.9 us), 128-row tiles above.
+inline int64_t split_tile_rows(int64_t m) { return m <= 128 ? 64 : DBM; }
+
 template <int BITS, int GSHIFT, bool GENERAL, bool F16>
 hipError_t launch_direct_g(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
                            const uint16_t* biases, int64_t n, int64_t kb, uint16_t* y, int64_t tiles_m,
                            int64_t tiles_n, float* part, int64_t splits, hipStream_t stream) {
     if (splits > 1) {
-        gemm_direct_kernel<BITS, GSHIFT, true, GENERAL, F16><<<dim3((unsigned)(tiles_m * tiles_n), (unsigned)splits),
-                                                          dim3(kDirectThreads), 0, stream>>>(
-            x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m,
-            (uint32_t)tiles_n, part, (uint32_t)splits);
+        const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits);
+        if (split_tile_rows(m) == 64)
+            gemm_direct_kernel<BITS, GSHIFT, true, GENERAL, F16, 2><<<grid, dim3(kDirectThreads), 0, stream>>>(
+                x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m,
+                (uint32_t)tiles_n, part, (uint32_t)splits);
+        else
+            gemm_direct_kernel<BITS, GSHIFT, true, GENERAL, F16, 4><<<grid, dim3(kDirectThreads), 0, stream>>>(
+                x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m,
+                (uint32_t)tiles_n, part, (uint32_t)splits);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const uint64_t count = (uint64_t)m * (uint64_t)n;
@@ -398,8 +415,8 @@ hipError_t launch_direct_g(const uint16_t* x, int64_t m, const uint32_t* packed,
                                                                                             (uint32_t)splits, y);
         return hipGetLastError();
     }
-    gemm_direct_kernel<BITS, GSHIFT, false, GENERAL, F16><<<dim3((unsigned)(tiles_m * tiles_n)), dim3(kDirectThreads), 0,
-                                                       stream>>>(
+    gemm_direct_kernel<BITS, GSHIFT, false, GENERAL, F16, 4><<<dim3((unsigned)(tiles_m * tiles_n)),
+                                                          dim3(kDirectThreads), 0, stream>>>(
         x, (uint32_t)m, packed, scales, biases, (uint32_t)n, (uint32_t)kb, y, (uint32_t)tiles_m, (uint32_t)tiles_n,
         nullptr, 1u);
     return hipGetLastError();
@@ -442,17 +459,22 @@ hipError_t launch_direct(const uint16_t* x, int64_t m, const uint32_t* packed, c
                                   splits, stream);
 }
 
-// K splits of whole 1024-code chunks (the last split also takes a K tail).
+// K splits of whole 1024-code chunks (the last split also takes a K tail): at most one block
+// per compute unit, then the fewest splits that keep the longest range as short (14 chunks over
+// at most 8 splits: 7 ranges of two, so fewer partial sums for the same critical path).
 int64_t direct_splits(int64_t m, int64_t n, int64_t k) {
     if (m <= 0 || n <= 0 || k < 64 * kDirectBody) return 1;
     const int64_t tiles_n = (n + DBN - 1) / DBN;
-    const int64_t tiles = ((m + DBM - 1) / DBM) * tiles_n;
+    const int64_t rows = split_tile_rows(m);
+    const int64_t tiles = ((m + rows - 1) / rows) * tiles_n;
     if (tiles > 0x7fffffff / 2) return 1;
     const int64_t chunks = k / (64 * kDirectBody);
     int64_t s = (int64_t)device_cu_count() / tiles;
     if (s > chunks) s = chunks;
     if (s > 64) s = 64;
-    return s < 1 ? 1 : s;
+    if (s <= 1) return 1;
+    const int64_t longest = (chunks + s - 1) / s;
+    return (chunks + longest - 1) / longest;
 }
 
 template <int BITS, int GSHIFT, bool F16>
@@ -517,7 +539,8 @@ hipError_t gemm_run(const uint16_t* x, int64_t m, const uint32_t* packed, const 
     // split K where the workspace allows it (float32 partials of every split)
     const int64_t splits = direct_splits(m, n, k);
     if (splits > 1 && workspace && workspace_bytes >= (size_t)splits * (size_t)m * (size_t)n * sizeof(float))
-        return launch_direct<F16>(x, m, packed, scales, biases, n, kb, bits, gshift, y, (m + DBM - 1) / DBM, tiles_n,
+        return launch_direct<F16>(x, m, packed, scales, biases, n, kb, bits, gshift, y,
+                                  (m + split_tile_rows(m) - 1) / split_tile_rows(m), tiles_n,
                                   static_cast<float*>(workspace), splits, general, stream);
     for (int64_t m_off = 0; m_off < m; m_off += max_rows) {
         const int64_t mm = (m - m_off < max_rows) ? (m - m_off) : max_rows;
