@@ -168,6 +168,47 @@ bool split_gemv_range(int64_t m, int64_t k) {
     return m >= kSplitMinM && m <= kGemvMaxM && !qaff::gemv_mfma_supported(m, k) && k % 1024 == 0 && k > 4096;
 }
 
+// A few rows past the decode range, without K split through a workspace: 16-row slices through the
+// decode kernels (each reads all of W) instead of one GEMM whose few tiles leave most compute units
+// idle. Measured on [4096 | 11008 | 14336, 4096 | 14336] weights, 3 to 8 bits, against the
+// unsplit GEMM: up to 3 slices win everywhere (17 rows of [4096, 14336] 4-bit: 24 against
+// 171 us), 4 slices win where n <= 8192 and lose by up to a fifth above it.
+bool decode_slices(int64_t m, int64_t n, int64_t k) {
+    if (m <= kGemvMaxM || m > 4 * kGemvMaxM || !qaff::gemv_mfma_supported(kGemvMaxM, k)) return false;
+    return (m + kGemvMaxM - 1) / kGemvMaxM <= 3 || n <= 8192;
+}
+
+extern "C++" {
+// The rows [m0, m0 + mm) of a decode-sized product (mm <= 16), as qaff_qmm's automatic path would
+// run them alone: the matrix-core decode kernel from gemv_mfma_min_m(k) rows, else the VALU GEMV.
+// F16: float16 x, scales, biases and y.
+template <bool F16>
+hipError_t decode_slice(const uint16_t* x, int64_t mm, const uint32_t* packed, const uint16_t* scales,
+                        const uint16_t* biases, int64_t n, int64_t k, int32_t group_size, int32_t bits, uint16_t* y,
+                        hipStream_t stream) {
+    if (mm >= gemv_mfma_min_m(k)) {
+        return F16 ? qaff::launch_gemv_mfma_f16(x, mm, packed, scales, biases, n, k, group_size, bits, y, stream)
+                   : qaff::launch_gemv_mfma(x, mm, packed, scales, biases, n, k, group_size, bits, y, stream);
+    }
+    return F16 ? qaff::launch_gemv_f16(x, mm, packed, scales, biases, n, k, group_size, bits, y, stream)
+               : qaff::launch_gemv(x, false, mm, packed, scales, biases, n, k, group_size, bits, y, stream);
+}
+
+template <bool F16>
+hipError_t launch_decode_slices(const uint16_t* x, int64_t m, const uint32_t* packed, const uint16_t* scales,
+                                const uint16_t* biases, int64_t n, int64_t k, int32_t group_size, int32_t bits,
+                                uint16_t* y, hipStream_t stream) {
+    for (int64_t m0 = 0; m0 < m; m0 += kGemvMaxM) {
+        const int64_t mm = m - m0 < kGemvMaxM ? m - m0 : kGemvMaxM;
+        // x and y offsets are multiples of 16 rows: still 16-byte aligned
+        const hipError_t e = decode_slice<F16>(x + (size_t)m0 * k, mm, packed, scales, biases, n, k, group_size, bits,
+                                               y + (size_t)m0 * n, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // extern "C++"
+
 // qaff_qmm_ex, and qaff_qmm_ws with a workspace (ws non-null: the call needs ws_need bytes, checked
 // by the caller; the GEMM path may split K into it).
 qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t m, const uint32_t* packed,
@@ -216,6 +257,13 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
             aligned(scales, 16) && aligned(biases, 16))
             use_gemm = true;
     }
+    // a GEMM with few tiles and no K split: 16-row slices through the decode kernels instead
+    const bool gemm_splits = ws && qaff::gemm_workspace_bytes(m, n, k) > 0 && ws_bytes >= qaff::gemm_workspace_bytes(m, n, k);
+    if (x_dtype == QAFF_BF16 && path == QAFF_PATH_AUTO && use_gemm && m > kGemvMaxM && !gemm_splits &&
+        decode_slices(m, n, k) && aligned(scales, 4) && aligned(biases, 4))
+        return after_launch(op, launch_decode_slices<false>(static_cast<const uint16_t*>(x), m, packed, scales, biases,
+                                                            n, k, group_size, bits, static_cast<uint16_t*>(y), stream),
+                            stream);
     hipError_t e;
     if (use_mfma && !use_gemm) {
         e = qaff::launch_gemv_mfma(static_cast<const uint16_t*>(x), m, packed, scales, biases, n, k, group_size,
@@ -599,7 +647,9 @@ qaff_status qaff_qmm_typed(const void* x, qaff_dtype x_dtype, int64_t m, const u
         const uint16_t* b16 = static_cast<const uint16_t*>(biases);
         uint16_t* y16 = static_cast<uint16_t*>(y);
         hipError_t e;
-        if (m > kGemvMaxM)
+        if (m > kGemvMaxM && decode_slices(m, n, k) && aligned(scales, 4) && aligned(biases, 4))
+            e = launch_decode_slices<true>(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);
+        else if (m > kGemvMaxM)
             e = qaff::launch_gemm_f16(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);
         else if (m >= gemv_mfma_min_m(k) && qaff::gemv_mfma_supported(m, k) && aligned(scales, 4) && aligned(biases, 4))
             e = qaff::launch_gemv_mfma_f16(x16, m, packed, s16, b16, n, k, group_size, bits, y16, stream);

@@ -64,6 +64,10 @@ def kernel_of(inp, path):
     m = inp.x.shape[0]
     if inp.x_dtype != "bf16":
         return "gemv"
+    wl = inp.wl
+    if path == "auto" and decode_slices(m, wl.n, wl.k) and \
+            qaff()._lib.load().qaff_qmm_workspace_size(m, wl.n, wl.k, wl.group_size, wl.bits) == 0:
+        return "slices"
     if path == "gemm" or (path == "auto" and m > qaff().gemv_max_m()):
         return "gemm"
     # the binding's automatic path passes a workspace when one is sized: decode-sized m beyond
@@ -76,6 +80,23 @@ def kernel_of(inp, path):
     return "gemv"
 
 
+def decode_slices(m, n, k):
+    """Where the automatic path runs 17 to 64 rows as 16-row slices of the decode path (with no K
+    split): the matrix-core decode kernel takes K, and up to 3 slices at any n, 4 where n <= 8192."""
+    return 16 < m <= 64 and k % 512 == 0 and 0 < k <= 32768 and ((m + 15) // 16 <= 3 or n <= 8192)
+
+
+def slices_of(inp, path="auto"):
+    """The automatic path's result row slice by slice: each 16-row slice as a call of its own."""
+    packed, scales, biases = dev_weights(inp)
+    x = dev_x(inp.x, inp.x_dtype)
+    m = inp.x.shape[0]
+    ys = [qaff().qmm(x[m0:m0 + 16], packed, scales, biases, inp.wl.group_size, inp.wl.bits, path=path)
+          for m0 in range(0, m, 16)]
+    torch.cuda.synchronize()
+    return torch.cat(ys)
+
+
 def bf16_weight_ref(orc, inp, x_rows):
     """x . bf16(W)^T in float64: the oracle's bf16 dequantization, widened, through numpy matmul."""
     wl = inp.wl
@@ -85,7 +106,7 @@ def bf16_weight_ref(orc, inp, x_rows):
     return x @ w.T
 
 
-def check_qmm(orc, inp, y, rows=None, path="auto"):
+def check_qmm(orc, inp, y, rows=None, path="auto", kernel=None):
     wl = inp.wl
     x = inp.x if rows is None else inp.x[rows]
     ref = orc.qmm(x, inp.x_dtype, inp.packed, inp.scales, inp.biases, wl.group_size, wl.bits)
@@ -96,11 +117,20 @@ def check_qmm(orc, inp, y, rows=None, path="auto"):
     assert err <= TOL[kind], f"max row rel err {err:.3e} > {TOL[kind]}"
     # both MFMA kernels multiply bf16-rounded weights, except the matrix-core decode kernel with
     # exact 4-bit codes
-    kernel = kernel_of(inp, path)
+    kernel = kernel or kernel_of(inp, path)
     exact = kernel == "gemv_mfma" and mfma_exact_codes(wl.bits, wl.group_size, inp.x.shape[0])
     tight_ref = ref if kernel == "gemv" or exact else bf16_weight_ref(orc, inp, x)
+    if kernel == "slices":   # each slice against the arithmetic of the kernel that ran it
+        wref = bf16_weight_ref(orc, inp, x)
+        tight_ref = ref.copy()
+        m = inp.x.shape[0]
+        for m0 in range(0, m, 16):
+            mm = min(16, m - m0)
+            on_mfma = mm >= qaff().gemv_mfma_min_m(wl.k)
+            if on_mfma and not mfma_exact_codes(wl.bits, wl.group_size, mm):
+                tight_ref[m0:m0 + mm] = wref[m0:m0 + mm]
     terr = orc.max_row_rel_err(got, tight_ref)
-    assert terr <= TIGHT[kind], f"{kernel_of(inp, path)}: max row rel err {terr:.3e} against its " \
+    assert terr <= TIGHT[kind], f"{kernel}: max row rel err {terr:.3e} against its " \
                                 f"own arithmetic, above {TIGHT[kind]}"
     return err
 
@@ -322,8 +352,36 @@ def test_dispatch_boundary_all_paths(orc, m):
     for p, y in ys.items():
         check_qmm(orc, inp, y, path=p)
     auto = kernel_of(inp, "auto")
-    assert auto == ("gemm" if m > 16 else "gemv_mfma" if m >= qaff().gemv_mfma_min_m() else "gemv")
-    assert torch.equal(ys["auto"].view(torch.int16), ys[auto].view(torch.int16))
+    assert auto == ("slices" if m > 16 else "gemv_mfma" if m >= qaff().gemv_mfma_min_m() else "gemv")
+    want = slices_of(inp) if auto == "slices" else ys[auto]
+    assert torch.equal(ys["auto"].view(torch.int16), want.view(torch.int16))
+
+
+# 17 to 64 rows through qaff_qmm (no workspace, so no K split): 16-row slices of the decode path,
+# each equal to the slice run as a call of its own (bit for bit) and within the kernels' bars;
+# n = 8192 against 8200 at 64 rows (the slices and the GEMM), K past 4096 (two-row decode slices on
+# the matrix cores), 3-bit codes, and K that the decode kernel does not take (the GEMM).
+@pytest.mark.parametrize("bits,G,m,n,k", [(4, 64, 17, 150, 2048), (3, 32, 33, 300, 4096), (8, 128, 48, 96, 5120),
+                                          (4, 64, 64, 8192, 1024), (4, 64, 64, 8200, 1024), (6, 32, 50, 150, 1536),
+                                          (4, 128, 18, 96, 8192), (4, 32, 20, 96, 1056)])
+def test_decode_slices(orc, bits, G, m, n, k):
+    import ctypes
+    from quantized_matmul_mlx_amd import _lib
+    inp = W.random_inputs(bits, G, n, k, m, seed=bits + G + m + n + k)
+    packed, scales, biases = dev_weights(inp)
+    x = dev_x(inp.x, "bf16")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    banner(f"decode slices bits={bits} G={G} m={m} n={n} k={k}")
+    _lib.check(_lib.load().qaff_qmm(P(x), _lib.QAFF_BF16, m, P(packed), P(scales), P(biases), n, k, G, bits, P(y),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    torch.cuda.synchronize()
+    slices = decode_slices(m, n, k)
+    check_qmm(orc, inp, y, kernel="slices" if slices else "gemm")
+    if slices:
+        assert torch.equal(y.view(torch.int16), slices_of(inp).view(torch.int16))
+    else:
+        assert torch.equal(y.view(torch.int16), run_qmm(inp, path="gemm").view(torch.int16))
 
 
 # The matrix-core decode kernel: every width and group size, m from 1 to 16, ragged n (not a

@@ -389,15 +389,31 @@ def test_qmm_f16_matrix_core_decode(orc, bits, G, m, n, k):
 
 
 # The GEMM: ragged tiles in m and n, K of whole 1024-code chunks and K with a tail (1056 codes: the
-# general variant).
+# general variant). (Up to 64 rows where the decode kernel takes K run as 16-row slices instead.)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
-@pytest.mark.parametrize("G,m,n,k", [(64, 17, 300, 1024), (128, 300, 520, 2048), (32, 130, 260, 1056)])
+@pytest.mark.parametrize("G,m,n,k", [(64, 70, 300, 1024), (128, 300, 520, 2048), (32, 130, 260, 1056),
+                                     (32, 17, 300, 1056)])
 def test_qmm_f16_gemm(orc, bits, G, m, n, k):
     inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 3 + G + m + k)
     banner(f"qmm float16 gemm bits={bits} G={G} m={m} n={n} k={k}")
     y = qaff().qmm(to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed), ds, db, G, bits)
     torch.cuda.synchronize()
     check_f16_qmm(orc, y, x, inp, hs, hb, G, bits)
+
+
+# 17 to 64 float16 rows: 16-row slices of the float16 decode path, each equal to the slice run as a
+# call of its own, bit for bit.
+@pytest.mark.parametrize("bits,G,m,n,k", [(4, 64, 17, 300, 1024), (3, 32, 40, 150, 4096), (8, 128, 64, 96, 2048),
+                                          (4, 64, 33, 150, 8192)])
+def test_qmm_f16_decode_slices(orc, bits, G, m, n, k):
+    inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 5 + G + m + k)
+    banner(f"qmm float16 decode slices bits={bits} G={G} m={m} n={n} k={k}")
+    xd, p = to_dev(x.view(np.uint16), "f16"), dev_u32(inp.packed)
+    y = qaff().qmm(xd, p, ds, db, G, bits)
+    parts = [qaff().qmm(xd[m0:m0 + 16], p, ds, db, G, bits) for m0 in range(0, m, 16)]
+    torch.cuda.synchronize()
+    check_f16_qmm(orc, y, x, inp, hs, hb, G, bits)
+    assert torch.equal(y.view(torch.int16), torch.cat(parts).view(torch.int16))
 
 
 # Gathered float16 products on the matrix cores: batched (x rows of 4 per batch; batches past x
