@@ -199,8 +199,10 @@ qaff_status qaff_qmm_ws(const void* x, qaff_dtype x_dtype, int64_t m, const uint
                         hipStream_t stream);
 
 /* Bytes of workspace qaff_qmm_ws can use for these sizes with a bf16 x (0 where it would not split
- * K: enough tiles, K not a multiple of 1024, or m <= 16 inside the decode kernels' range). From 8
- * rows on, K above 32768 codes (past the matrix-core decode kernel) also takes the split GEMM. */
+ * K: enough tiles, K not a multiple of 1024, m <= 16 inside the decode kernels' range, or up to 32
+ * rows of a weight with n and k at most 4096, whose 16-row slices of the decode path beat the
+ * split). From 8 rows on, K above 32768 codes (past the matrix-core decode kernel) also takes the
+ * split GEMM. */
 size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_size, int32_t bits);
 
 /*

@@ -178,6 +178,13 @@ bool decode_slices(int64_t m, int64_t n, int64_t k) {
     return (m + kGemvMaxM - 1) / kGemvMaxM <= 3 || n <= 8192;
 }
 
+// Where the slices also beat the GEMM with K split through a workspace, which then needs none:
+// small weights at up to 2 slices ([4096, 4096] at 17 rows: 8.1 against 14.3 us for the split;
+// wider or longer weights favour the split).
+bool slices_over_split(int64_t m, int64_t n, int64_t k) {
+    return decode_slices(m, n, k) && m <= 2 * kGemvMaxM && n <= 4096 && k <= 4096;
+}
+
 extern "C++" {
 // The rows [m0, m0 + mm) of a decode-sized product (mm <= 16), as qaff_qmm's automatic path would
 // run them alone: the matrix-core decode kernel from gemv_mfma_min_m(k) rows, else the VALU GEMV.
@@ -258,7 +265,8 @@ qaff_status qmm_impl(const char* op, const void* x, qaff_dtype x_dtype, int64_t 
             use_gemm = true;
     }
     // a GEMM with few tiles and no K split: 16-row slices through the decode kernels instead
-    const bool gemm_splits = ws && qaff::gemm_workspace_bytes(m, n, k) > 0 && ws_bytes >= qaff::gemm_workspace_bytes(m, n, k);
+    const bool gemm_splits = ws && !slices_over_split(m, n, k) && qaff::gemm_workspace_bytes(m, n, k) > 0 &&
+                             ws_bytes >= qaff::gemm_workspace_bytes(m, n, k);
     if (x_dtype == QAFF_BF16 && path == QAFF_PATH_AUTO && use_gemm && m > kGemvMaxM && !gemm_splits &&
         decode_slices(m, n, k) && aligned(scales, 4) && aligned(biases, 4))
         return after_launch(op, launch_decode_slices<false>(static_cast<const uint16_t*>(x), m, packed, scales, biases,
@@ -292,6 +300,7 @@ size_t qaff_qmm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t group_si
     (void)bits;
     if (n <= 0 || k <= 0) return 0;
     if (m <= kGemvMaxM && !split_gemv_range(m, k)) return 0;
+    if (slices_over_split(m, n, k)) return 0;
     return qaff::gemm_workspace_bytes(m, n, k);
 }
 

@@ -322,6 +322,8 @@ def test_qmm_ws_checks(lib):
     far = 33792                                              # past it (above 32768), from 8 rows:
     assert size(7, k=far) == 0 and size(8, k=far) > 0 and size(16, k=far) > 0  # the split GEMM
     assert size(17) > 0 and size(128) > 0 and size(1024) > 0  # few GEMM tiles: K splits
+    assert size(17, k=4096) == 0 and size(32, k=4096) == 0      # ... except small weights at up to 32
+    assert size(33, k=4096) > 0 and size(17, n=8192, k=4096) > 0  # rows: 16-row decode slices there
     assert size(2048) == 0                                   # a tile per compute unit already
     assert size(128, k=14336 + 64) > 0                       # K with a tail splits its whole chunks too
     assert size(128, k=1024) == 0                            # a single chunk of K

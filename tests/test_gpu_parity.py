@@ -264,9 +264,9 @@ def test_gemm_direct_small_m(orc, bits, G, m, n, k):
 
 
 # The automatic path of a bf16 x with few GEMM tiles splits K through a workspace that the binding
-# allocates (qaff_qmm_ws): 2, 3, 4 and 14 ranges of 1024 codes with ragged m and n, and a shape with
+# allocates (qaff_qmm_ws): 8, 3, 4 and 14 ranges of 1024 codes with ragged m and n, and a shape with
 # a single chunk of K, which cannot split. Against the oracle and against the unsplit kernel.
-@pytest.mark.parametrize("bits,G,m,n,k,splits", [(4, 128, 17, 300, 2048, True), (4, 64, 100, 520, 3072, True),
+@pytest.mark.parametrize("bits,G,m,n,k,splits", [(4, 128, 17, 300, 8192, True), (4, 64, 100, 520, 3072, True),
                                                  (3, 32, 260, 264, 4096, True), (8, 128, 33, 256, 14336, True),
                                                  (4, 128, 300, 4096, 1024, False)])
 def test_gemm_split_k(orc, bits, G, m, n, k, splits):
