@@ -60,11 +60,11 @@ typedef enum { QAFF_F32 = 0, QAFF_BF16 = 1, QAFF_F16 = 2 } qaff_dtype;
  * m <= qaff_gemv_max_m() -> the decode path: the VALU GEMV for m below qaff_gemv_mfma_min_m()
  * (below 2 where K exceeds 4096), the matrix-core decode kernel (GEMV_MFMA) from there on where it
  * applies (K a multiple of 512 and at most 32768, 4-byte aligned scales and biases), the VALU GEMV
- * otherwise; bf16 x with a larger m -> the bf16-MFMA GEMM, except that up to 64 rows with no K
+ * otherwise; bf16 x with a larger m -> the bf16-MFMA GEMM, except that up to 128 rows with no K
  * split (no workspace, or one qaff_qmm_ws does not use) run as 16-row slices, each as the decode
  * path would run it alone, where the matrix-core decode kernel takes K and 4-byte aligned scales
- * (up to 48 rows at any n, 64 where n <= 8192: a GEMM with that few tiles leaves most of the chip
- * idle). GEMV_MFMA forced on a shape it does not take is UNSUPPORTED. */
+ * (up to 48 rows at any n, 96 where n <= 8192, 128 where n <= 4096: a GEMM with that few tiles
+ * leaves most of the chip idle). GEMV_MFMA forced on a shape it does not take is UNSUPPORTED. */
 typedef enum { QAFF_PATH_AUTO = 0, QAFF_PATH_GEMV = 1, QAFF_PATH_GEMM = 2, QAFF_PATH_GEMV_MFMA = 3 } qaff_path;
 
 /*
@@ -111,7 +111,7 @@ qaff_status qaff_dequantize_typed(const uint32_t* packed, const void* scales, co
  * below the matrix-core rows the GEMV in float16 (codes as the exact values 1024 + c,
  * v_dot2_f32_f16), then the matrix-core decode kernel (exact 4-bit codes 1024 + c where they apply,
  * else weights rounded to float16; float16 MFMA), past 16 rows the GEMM (weights rounded to
- * float16, float16 MFMA) or, for up to 64 rows, the 16-row slices of QAFF_PATH_AUTO; float32 sums,
+ * float16, float16 MFMA) or, for up to 128 rows, the 16-row slices of QAFF_PATH_AUTO; float32 sums,
  * y rounded to nearest even. Every other combination runs on
  * a VALU GEMV that reads the types as given (any m, any k).
  * Errors: as qaff_qmm, plus INVALID_ARGUMENT for an unknown dtype or misaligned scales.

@@ -170,12 +170,14 @@ bool split_gemv_range(int64_t m, int64_t k) {
 
 // A few rows past the decode range, without K split through a workspace: 16-row slices through the
 // decode kernels (each reads all of W) instead of one GEMM whose few tiles leave most compute units
-// idle. Measured on [4096 | 11008 | 14336, 4096 | 14336] weights, 3 to 8 bits, against the
-// unsplit GEMM: up to 3 slices win everywhere (17 rows of [4096, 14336] 4-bit: 24 against
-// 171 us), 4 slices win where n <= 8192 and lose by up to a fifth above it.
+// idle. Measured on [2048 | 4096 | 8192 | 11008 | 14336, 4096 | 8192 | 14336] weights, 3 to 8
+// bits, against the unsplit GEMM: up to 3 slices win everywhere (17 rows of [4096, 14336] 4-bit:
+// 24 against 171 us), up to 6 where n <= 8192 and up to 8 where n <= 4096 (128 rows of
+// [4096, 14336] 4-bit: 134 against 171 us); past those they lose by up to a fifth.
 bool decode_slices(int64_t m, int64_t n, int64_t k) {
-    if (m <= kGemvMaxM || m > 4 * kGemvMaxM || !qaff::gemv_mfma_supported(kGemvMaxM, k)) return false;
-    return (m + kGemvMaxM - 1) / kGemvMaxM <= 3 || n <= 8192;
+    const int64_t slices = (m + kGemvMaxM - 1) / kGemvMaxM;
+    if (m <= kGemvMaxM || slices > 8 || !qaff::gemv_mfma_supported(kGemvMaxM, k)) return false;
+    return slices <= 3 || (slices <= 6 && n <= 8192) || n <= 4096;
 }
 
 // Where the slices also beat the GEMM with K split through a workspace, which then needs none:

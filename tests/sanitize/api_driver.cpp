@@ -139,12 +139,16 @@ int main() {
     EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 2, P16, S16, B16, 64, 4096 + 512 * 2, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 1, P16, S16, B16, 64, 4096 + 512 * 2, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 4, P16, S16, B16, 64, 32768 + 1024, 64, 4, A16, nullptr));
-    // 17 to 64 rows without a K split: 16-row slices (the last slice's rows decide the last launch)
+    // 17 to 128 rows without a K split: 16-row slices (the last slice's rows decide the last launch)
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 17, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 48, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 64, P16, S16, B16, 8192, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 64, P16, S16, B16, 8256, 4096, 64, 4, A16, nullptr));
-    EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 65, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_BF16, 65, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 96, P16, S16, B16, 8192, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 97, P16, S16, B16, 8192, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemv_mfma", qaff_qmm(A16, QAFF_BF16, 128, P16, S16, B16, 4096, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 129, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemm", qaff_qmm(A16, QAFF_BF16, 17, P16, S16, B16, 64, 4096 + 64, 64, 4, A16, nullptr));  // K % 512
     EXPECT(OK, "gemm", qaff_qmm_ex(A16, QAFF_BF16, 17, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr, QAFF_PATH_GEMM));
     EXPECT(OK, "gemv", qaff_qmm(A16, QAFF_F32, 300, P16, S16, B16, 64, 4096, 64, 4, A16, nullptr));
@@ -173,7 +177,7 @@ int main() {
     EXPECT(OK, "gemv_mfma_f16", qaff_qmm_typed(A16, QAFF_F16, 2, P16, S16, B16, QAFF_F16, 64, 5120, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_f16", qaff_qmm_typed(A16, QAFF_F16, 3, P16, S16, B2, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_f16", qaff_qmm_typed(A16, QAFF_F16, 17, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
-    EXPECT(OK, "gemm_f16", qaff_qmm_typed(A16, QAFF_F16, 65, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
+    EXPECT(OK, "gemm_f16", qaff_qmm_typed(A16, QAFF_F16, 129, P16, S16, B16, QAFF_F16, 64, 4096, 64, 4, A16, nullptr));
     EXPECT(OK, "gemv_typed", qaff_qmm_typed(A16, QAFF_F16, 17, P16, S16, B16, QAFF_F32, 64, 4096, 64, 4, A16, nullptr));
     // ... and qaff_gather_qmm's: grouped GEMM, grouped and batched decode kernels, else the typed GEMV
     EXPECT(OK, "gemm_grouped_f16", qaff_gather_qmm_typed(A16, QAFF_F16, 256, 1, P16, S16, B16, QAFF_F16, 4, 64, 4096, 64,

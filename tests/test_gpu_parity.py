@@ -81,9 +81,11 @@ def kernel_of(inp, path):
 
 
 def decode_slices(m, n, k):
-    """Where the automatic path runs 17 to 64 rows as 16-row slices of the decode path (with no K
-    split): the matrix-core decode kernel takes K, and up to 3 slices at any n, 4 where n <= 8192."""
-    return 16 < m <= 64 and k % 512 == 0 and 0 < k <= 32768 and ((m + 15) // 16 <= 3 or n <= 8192)
+    """Where the automatic path runs 17 to 128 rows as 16-row slices of the decode path (with no K
+    split): the matrix-core decode kernel takes K, and up to 3 slices at any n, 6 where n <= 8192,
+    8 where n <= 4096."""
+    s = (m + 15) // 16
+    return 16 < m <= 128 and k % 512 == 0 and 0 < k <= 32768 and (s <= 3 or (s <= 6 and n <= 8192) or n <= 4096)
 
 
 def slices_of(inp, path="auto"):
@@ -357,13 +359,15 @@ def test_dispatch_boundary_all_paths(orc, m):
     assert torch.equal(ys["auto"].view(torch.int16), want.view(torch.int16))
 
 
-# 17 to 64 rows through qaff_qmm (no workspace, so no K split): 16-row slices of the decode path,
+# 17 to 128 rows through qaff_qmm (no workspace, so no K split): 16-row slices of the decode path,
 # each equal to the slice run as a call of its own (bit for bit) and within the kernels' bars;
-# n = 8192 against 8200 at 64 rows (the slices and the GEMM), K past 4096 (two-row decode slices on
-# the matrix cores), 3-bit codes, and K that the decode kernel does not take (the GEMM).
+# the edges of the rule (n = 8192 at 64 and 96 rows against 100 rows, n = 4096 at 128 rows, n =
+# 8200 at 64 rows), K past 4096 (two-row decode slices on the matrix cores), 3- and 5-bit codes,
+# and K that the decode kernel does not take (the GEMM).
 @pytest.mark.parametrize("bits,G,m,n,k", [(4, 64, 17, 150, 2048), (3, 32, 33, 300, 4096), (8, 128, 48, 96, 5120),
-                                          (4, 64, 64, 8192, 1024), (4, 64, 64, 8200, 1024), (6, 32, 50, 150, 1536),
-                                          (4, 128, 18, 96, 8192), (4, 32, 20, 96, 1056)])
+                                          (4, 64, 64, 8192, 1024), (4, 64, 96, 8192, 1024), (4, 64, 100, 8192, 1024),
+                                          (4, 64, 128, 4096, 1024), (4, 64, 64, 8200, 1024), (6, 32, 50, 150, 1536),
+                                          (5, 32, 113, 300, 2048), (4, 128, 18, 96, 8192), (4, 32, 20, 96, 1056)])
 def test_decode_slices(orc, bits, G, m, n, k):
     import ctypes
     from quantized_matmul_mlx_amd import _lib

@@ -389,9 +389,9 @@ def test_qmm_f16_matrix_core_decode(orc, bits, G, m, n, k):
 
 
 # The GEMM: ragged tiles in m and n, K of whole 1024-code chunks and K with a tail (1056 codes: the
-# general variant). (Up to 64 rows where the decode kernel takes K run as 16-row slices instead.)
+# general variant). (Up to 128 rows where the decode kernel takes K run as 16-row slices instead.)
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
-@pytest.mark.parametrize("G,m,n,k", [(64, 70, 300, 1024), (128, 300, 520, 2048), (32, 130, 260, 1056),
+@pytest.mark.parametrize("G,m,n,k", [(64, 140, 300, 1024), (128, 300, 520, 2048), (32, 130, 260, 1056),
                                      (32, 17, 300, 1056)])
 def test_qmm_f16_gemm(orc, bits, G, m, n, k):
     inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 3 + G + m + k)
@@ -401,10 +401,10 @@ def test_qmm_f16_gemm(orc, bits, G, m, n, k):
     check_f16_qmm(orc, y, x, inp, hs, hb, G, bits)
 
 
-# 17 to 64 float16 rows: 16-row slices of the float16 decode path, each equal to the slice run as a
+# 17 to 128 float16 rows: 16-row slices of the float16 decode path, each equal to the slice run as a
 # call of its own, bit for bit.
 @pytest.mark.parametrize("bits,G,m,n,k", [(4, 64, 17, 300, 1024), (3, 32, 40, 150, 4096), (8, 128, 64, 96, 2048),
-                                          (4, 64, 33, 150, 8192)])
+                                          (4, 64, 33, 150, 8192), (4, 64, 120, 300, 2048)])
 def test_qmm_f16_decode_slices(orc, bits, G, m, n, k):
     inp, hs, hb, ds, db, x = f16_case(bits, G, n, k, m, seed=bits * 5 + G + m + k)
     banner(f"qmm float16 decode slices bits={bits} G={G} m={m} n={n} k={k}")
