@@ -23,7 +23,7 @@ The same JSON line carries:
     float16 x, scales and biases, quantize of a bf16
     [4096, 4096] weight, and the mixture-of-experts gathered product
     gather_qmm at 1 and 64 tokens), each against its roofline;
-  * `context`: what the box does on the same sizes without this library, timed the same way: an
+  * `context`: what the GPU does on the same sizes without this library, timed the same way: an
     empty kernel launch, a device copy of the decode step's bytes, a dense bf16 matmul at the
     prefill shape;
   * `cpu_baseline`: the CPU oracle on the host cores, on a bounded sample of the same workload
@@ -987,7 +987,7 @@ def main():
         result["prefill_gemm"] = summ
         log("prefill: " + json.dumps(summ))
 
-    # ---- what the box does on the same sizes without this library ----
+    # ---- what the GPU does on the same sizes without this library ----
     if not args.no_context:
         log("context: empty launch, plain reads, device copy, dense bf16 matmul")
         ctx = bench_context(torch, timer, aux, metrics, args.sustain)
