@@ -256,7 +256,6 @@ def kernel_name(q, m, k):
 
 def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
     """One qmm workload at M = m, rotated over ~1 GiB of operand copies."""
-    import oracle
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, m=m)
     b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
@@ -276,6 +275,7 @@ def bench_qmm(torch, q, W, timer, name, m, steps, warmup, cpu, cpu_budget):
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies,
            "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
         threads = oracle.default_threads()
         runs, el = cpu_time(lambda: oracle.qmm(inp.x, "bf16", inp.packed, inp.scales, inp.biases,
                                                wl.group_size, wl.bits, threads=threads), cpu_budget, 100000)
@@ -289,7 +289,6 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
     """The fused decode products at the FFN shapes (4-bit g64, M = 1): "gate_up" (both [14336, 4096]
     projections of one x) or "silu_gate" (down [4096, 14336] on silu(gate) * up plus the residual)."""
     import numpy as np
-    import oracle
     if kind == "gate_up":
         wa, wb = W.WORKLOADS["ffn_gate_4bit_g64_14336x4096"], W.WORKLOADS["ffn_up_4bit_g64_14336x4096"]
         a, bb = W.make_inputs(wa, m=1), W.make_inputs(wb, m=1)
@@ -334,7 +333,6 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
                                  threads=threads)
         label = "gemv_silu_gate + residual [4096, 14336] 4-bit g64 M=1"
         sets = (sd, g_t, u_t)
-    threads = oracle.default_threads()
     ms = timer(launch, steps, warmup)
     del sets
     torch.cuda.empty_cache()
@@ -342,6 +340,8 @@ def bench_fused(torch, q, W, timer, kind, steps, warmup, cpu, cpu_budget):
     row = {"workload": label, "kernel": f"gemv_{kind} (fused)", "bytes_per_step": nbytes,
            "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
+        threads = oracle.default_threads()
         runs, el = cpu_time(cpu_step, cpu_budget, 100000)
         row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": threads,
                                "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
@@ -357,7 +357,6 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
     f16: x, scales and biases as float16 (the workload's values converted; y float16): the float16
     forms of the same kernels."""
     import numpy as np
-    import oracle
     wl = W.WORKLOADS[name]
     mi = W.moe_inputs(wl, tokens)
     rows = mi.expert.size
@@ -407,6 +406,7 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
         row["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
     if cpu and gemm:
+        import oracle
         # a sample: the rows of the first expert through the oracle's product (the typed one on one
         # thread)
         threads = 1 if f16 else oracle.default_threads()
@@ -423,11 +423,13 @@ def bench_gather(torch, q, W, timer, tokens, steps, warmup, cpu, cpu_budget, nam
                                "cores": threads, "kind": "oracle",
                                "sample": f"the {sel.size} rows of one expert, {el:.2f} s"}
     elif cpu and f16:
+        import oracle
         runs, el = cpu_time(lambda: oracle.gather_qmm_typed(hx, "f16", mi.packed, hs, hb, "f16", wl.group_size,
                                                             wl.bits, rhs=mi.expert), cpu_budget, 100000)
         row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
     elif cpu:
+        import oracle
         threads = oracle.default_threads()
         runs, el = cpu_time(lambda: oracle.gather_qmm(mi.x_rows, "bf16", mi.packed, mi.scales, mi.biases,
                                                       wl.group_size, wl.bits, rhs=mi.expert, threads=threads),
@@ -442,7 +444,6 @@ def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget, f16=False):
     W stored [4096 (k), 4096 (n)], 4-bit g64 (groups along n). Algorithmic bytes as for qmm. With
     f16, x, scales and biases are float16 (the same draws converted) and so is y."""
     import numpy as np
-    import oracle
     wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
     inp = W.make_inputs(wl, m=1)          # the same draws, read as a [k, n] weight
     b = qmm_bytes(1, wl.n, wl.k, wl.bits, wl.group_size)
@@ -472,6 +473,7 @@ def bench_qmm_nt(torch, q, W, timer, steps, warmup, cpu, cpu_budget, f16=False):
            "kernel": "qmm_nt_partial_kernel + qmm_nt_reduce_kernel" + (", typed form" if f16 else ""),
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
         if f16:
             fn = lambda: oracle.qmm_nt_typed(x16, "f16", inp.packed, s16, b16, "f16", wl.group_size, wl.bits)
         else:
@@ -487,7 +489,6 @@ def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget, m=1):
     g64: at M = 1 the GEMV in float16, at M = 4 the matrix-core decode kernel in float16. The scales,
     biases and x are the decode workload's, as float16."""
     import numpy as np
-    import oracle
     wl = W.WORKLOADS["decode_4bit_g64_4096x4096"]
     inp = W.make_inputs(wl, m=m)
     s16 = W.f32_from_bf16_bits(inp.scales).astype(np.float16).view(np.uint16)
@@ -512,6 +513,7 @@ def bench_typed(torch, q, W, timer, steps, warmup, cpu, cpu_budget, m=1):
     row = {"workload": f"qmm float16 x, scales and biases, W [4096, 4096] 4-bit g64, M={m}", "kernel": kernel,
            "bytes_per_step": b, "ms_per_step": round(ms, 6), "weight_copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
         threads = oracle.default_threads()
         runs, el = cpu_time(lambda: oracle.qmm_typed(x16, "f16", inp.packed, s16, b16, "f16", wl.group_size, wl.bits),
                             cpu_budget, 100000)
@@ -525,7 +527,6 @@ def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget, dtype="bf
     "f16", float16: the same draws converted), scales and biases in the weight's dtype. Algorithmic
     bytes: the weight read, the codes, scales and biases written."""
     import numpy as np
-    import oracle
     wl = W.WORKLOADS["quantize_4bit_g64_4096x4096"]
     w = W.dense_weight(wl.n, wl.k, "bf16", seed=wl.seed)
     tdt = torch.bfloat16
@@ -548,6 +549,7 @@ def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget, dtype="bf
            "kernel": "quantize_kernel", "bytes_per_step": nbytes, "ms_per_step": round(ms, 6), "copies": copies,
            "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
         runs, el = cpu_time(lambda: oracle.quantize(w, dtype, wl.group_size, wl.bits, dtype), cpu_budget, 100000)
         row["cpu_baseline"] = {"value": round(nbytes * runs / el / 1e9, 4), "unit": "GB/s", "cores": 1,
                                "kind": "oracle", "sample": f"the whole step, {runs} run(s) in {el:.1f} s"}
@@ -555,7 +557,6 @@ def bench_quantize(torch, q, W, timer, steps, warmup, cpu, cpu_budget, dtype="bf
 
 
 def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_budget, gather):
-    import oracle
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl)
     rows_out = wl.n_indices if gather else wl.n
@@ -590,6 +591,7 @@ def bench_dequant(torch, q, W, timer, name, out_dtype, steps, warmup, cpu, cpu_b
     row = {"workload": f"{name} {kind} -> {out_dtype}", "kernel": kind, "bytes_per_step": b,
            "ms_per_step": round(ms, 6), "copies": copies, "roofline": hbm_roofline(gbs)}
     if cpu:
+        import oracle
         threads = oracle.default_threads()
         sample = 512
         if gather:
@@ -681,7 +683,6 @@ def sustained(torch, launch, seconds, metrics, flop):
 
 
 def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
-    import oracle
     wl = W.WORKLOADS["prefill_4bit_g128_4096x14336"]
     m = 2048
     inp = W.make_inputs(wl, m=m)
@@ -720,6 +721,7 @@ def bench_prefill(torch, q, W, timer, steps, cpu, metrics=None, sustain_s=0.0):
                         "frac": round(burst_tf / BF16_MFMA_PEAK_TFLOPS, 4),
                         "timing": f"one HIP graph of {steps} launches after the decode rows"}
     if cpu:
+        import oracle
         threads = oracle.default_threads()
         rows = 64
         t0 = time.perf_counter()
@@ -740,7 +742,6 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, n
     bf16 and float16 have the same). f16: x, scales and biases as float16 (the workload's values
     converted), the GEMM in float16."""
     import numpy as np
-    import oracle
     wl = W.WORKLOADS[name]
     inp = W.make_inputs(wl, m=m)
     b = qmm_bytes(m, wl.n, wl.k, wl.bits, wl.group_size)
@@ -774,6 +775,7 @@ def bench_prefill_small(torch, q, W, timer, m, steps, warmup, cpu, cpu_budget, n
            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}}
     if cpu:
+        import oracle
         threads = oracle.default_threads()
         rows = 64
         t0 = time.perf_counter()
