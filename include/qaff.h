@@ -19,6 +19,8 @@
  *     consumer owns the device pointers).
  *   - bits must be 1, 2, 3, 4, 5, 6 or 8 (else QAFF_ERR_UNSUPPORTED); group_size 32, 64 or 128
  *     (nuvec_core check_params); cols (k) must be a multiple of group_size.
+ *   - A weight has at most 2^32 - 1 rows, and a row's code stream, cols * bits bits, stays below
+ *     2^32 bits (the kernels address within a row in 32 bits); larger is QAFF_ERR_UNSUPPORTED.
  *   - Alignment: packed 4 bytes, scales/biases their element size (2 bytes; 4 for float32), indices
  *     4 bytes; x, y, out, w, gate, up and resid their element size (4 bytes for float32, 2 for bf16
  *     and float16). 16-byte aligned x, y and out take the vector kernels; others (a row slice, an

@@ -82,7 +82,10 @@ qaff_status check_weight(const char* op, const uint32_t* packed, const uint16_t*
             return fail(QAFF_ERR_INVALID_ARGUMENT, "%s: scales and biases must be 2-byte aligned", op);
     }
     if (rows > 0xffffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: more than 2^32-1 weight rows", op);
-    if (cols / 32 > 0x7fffffffLL) return fail(QAFF_ERR_UNSUPPORTED, "%s: too many columns", op);
+    // the kernels address within a row's code stream (cols * bits bits) in 32 bits
+    if (cols > 0xffffffffLL / bits)
+        return fail(QAFF_ERR_UNSUPPORTED, "%s: a row of %lld %d-bit codes is 2^32 bits or longer", op, (long long)cols,
+                    bits);
     return QAFF_OK;
 }
 

@@ -129,6 +129,21 @@ def test_negative_sizes(lib):
     assert rows(lib, n_idx=-1) == INVALID
 
 
+def test_rows_of_2_pow_32_bits_or_more(lib):
+    # the kernels address within a row's code stream in 32 bits: cols * bits must stay below 2^32
+    for bits in (1, 3, 4, 8):
+        top = (2**32 - 1) // bits // 128 * 128          # the longest row that fits, in whole groups
+        over = top + 128
+        assert dq(lib, cols=over, G=128, bits=bits) == UNSUPPORTED
+        assert b"2^32 bits" in lib.qaff_last_error()
+        assert qmm(lib, k=over, G=128, bits=bits) == UNSUPPORTED
+        assert rows(lib, cols=over, G=128, bits=bits) == UNSUPPORTED
+        # at the limit the weight itself passes; this call then stops at its null output
+        assert dq(lib, cols=top, G=128, bits=bits, out=NULL) == INVALID
+        assert b"null output" in lib.qaff_last_error()
+    assert dq(lib, cols=2**40, G=128) == UNSUPPORTED      # no overflow in the check itself
+
+
 def test_null_pointers(lib):
     assert dq(lib, packed=NULL) == INVALID
     assert dq(lib, scales=NULL) == INVALID

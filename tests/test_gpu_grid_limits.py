@@ -1,13 +1,13 @@
 """Launches that split their grid: one grid dimension holds at most 65535 blocks, so long x (the
-GEMVs' rows of x per block), many output batches (the gathered products) and many experts (the
-grouped walk) go out in several launches. Checked against the CPU oracle at the smallest sizes
+GEMVs' rows of x per block), many output batches (the gathered products), many experts (the
+grouped walk) and many output rows (dequantize, dequant_rows) go out in several launches. Checked against the CPU oracle at the smallest sizes
 that cross the limit (k small so that the oracle finishes in seconds)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as orc_mod
-from gpu_util import banner, dev_bf16, dev_u32, dev_weights, dev_x, host_f64
+from gpu_util import banner, dev_bf16, dev_u32, dev_weights, dev_x, host_bits, host_f64
 from quantized_matmul_mlx_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -108,3 +108,61 @@ def test_typed_gather_over_batch_slices(orc):
     nan = np.isnan(ref).all(axis=1)
     assert nan.sum() == 5 and np.isnan(got[nan]).all()
     assert orc.max_row_rel_err(got[~nan], ref[~nan]) <= TIGHT["f32"]
+
+
+OUTS = (("f32", torch.float32, np.uint32), ("bf16", torch.bfloat16, np.uint16))
+
+
+def test_dequantize_over_row_slices(orc):
+    # grid y = output rows, 65535 per launch; 3-bit codes straddle words
+    rows, cols, G, bits = 65535 + 37, 96, 32, 3
+    inp = W.random_inputs(bits, G, rows, cols, 0, seed=8)
+    p, s, b = dev_weights(inp)
+    for out, tdt, view in OUTS:
+        banner(f"dequantize rows={rows} -> {out} (several launches)")
+        got = host_bits(qaff().dequantize(p, s, b, G, bits, tdt))
+        ref = orc.dequantize(inp.packed, inp.scales, inp.biases, G, bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
+
+
+def test_dequant_rows_over_index_slices(orc):
+    # grid y = indices, 65535 per launch; some indices past the table (rows of NaN)
+    table, cols, G, bits = 300, 64, 32, 4
+    inp = W.random_inputs(bits, G, table, cols, 0, seed=9)
+    idx = np.random.default_rng(10).integers(0, table, 65535 + 41).astype(np.uint32)
+    idx[[5, 65534, 65535, 65560]] = [table, 2**32 - 1, table + 7, 0]
+    p, s, b = dev_weights(inp)
+    it = torch.from_numpy(idx.view(np.int32)).cuda()
+    for out, tdt, view in OUTS:
+        banner(f"dequant_rows {idx.size} indices -> {out} (several launches)")
+        got = host_bits(qaff().dequant_rows(p, s, b, it, G, bits, tdt))
+        ref = orc.dequant_rows(inp.packed, inp.scales, inp.biases, idx, G, bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
+
+
+def test_dequantize_past_2_pow_31_elements_per_launch(orc):
+    # 65535 + 17 rows of 65536 codes: the first launch covers 2^32 - 2^16 outputs, so element
+    # offsets pass 2^31 inside one launch, and the float32 output (17.2 GB) passes 2^34 bytes.
+    # Inputs drawn on the device from a seeded generator (any words are valid codes); the output
+    # starts as NaN, so that every element must be written, and whole rows on both sides of each
+    # boundary are compared with the oracle to the bit.
+    rows, cols, G, bits = 65535 + 17, 65536, 64, 4
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    p = torch.randint(-2**31, 2**31 - 1, (rows, cols * bits // 32), dtype=torch.int32, device="cuda",
+                      generator=gen)
+    s = torch.empty((rows, cols // G), device="cuda").uniform_(1e-3, 2e-2, generator=gen).to(torch.bfloat16)
+    b = torch.empty((rows, cols // G), device="cuda").uniform_(-0.15, 0.0, generator=gen).to(torch.bfloat16)
+    sel = np.array([0, 1, 32767, 32768, 65534, 65535, 65536, rows - 1])
+    st = torch.from_numpy(sel).cuda()
+    hp = p[st].cpu().numpy().view(np.uint32)
+    hs, hb = (host_bits(t[st]) for t in (s, b))
+    for out, tdt, view in OUTS:
+        banner(f"dequantize {rows}x{cols} -> {out} (past 2^31 elements per launch)")
+        buf = torch.full((rows, cols), float("nan"), dtype=tdt, device="cuda")
+        qaff().dequantize(p, s, b, G, bits, tdt, out=buf)
+        assert not bool(torch.isnan(buf).any())
+        got = host_bits(buf[st])
+        del buf
+        torch.cuda.empty_cache()
+        ref = orc.dequantize(hp, hs, hb, G, bits, out=out)
+        np.testing.assert_array_equal(got.view(view), ref.view(view))
